@@ -1,0 +1,243 @@
+"""CPU oracle for the paged-KV pre-attention path -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its binding) never imports it, and it imports nothing from the product path.
+
+The arithmetic lives in ``pkv_oracle.c`` (plain C, IEEE binary64, one rounding
+per output); this module only loads ``liboracle.so`` with ctypes and passes
+numpy arrays to it.  Every function works on host arrays and mirrors one entry
+point of the method:
+
+* :func:`mla_rope_rmsnorm_quant` -- page "mla_fused_rope_rmsnorm_quantization"
+  (summary, Args) and the fused_rope_rmsnorm_quantization_kernel entry of the
+  "mla_graph" module page;
+* :func:`qk_rope_paged_ragged` -- page "generic_fused_qk_rope_bshd_paged_ragged";
+* :func:`rms_norm_kv_cache_paged` -- page "rms_norm_kv_cache_ragged_paged";
+* the bf16 and FP8 E4M3FN codecs and the RoPE / RMSNorm row steps, exposed so
+  that tests can pin each step on its own.
+
+Parity status of each function: pinned by ``tests/test_oracle_*.py`` against
+closed forms, invariants, brute force and library special cases (no page
+prints a worked example).  ``rms_norm_kv_cache_paged`` with
+``multiply_before_cast=0`` is pinned only through the bf16 codec and the
+RMSNorm row step it is built from.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+_c_u16p = ctypes.POINTER(ctypes.c_uint16)
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+
+SCALE_PER_TENSOR = 1
+SCALE_PER_TOKEN = 2
+CACHE_FP8 = 0
+CACHE_BF16 = 1
+
+
+def build() -> str:
+    """Compile liboracle.so with the oracle's own Makefile (gcc, binary64)."""
+    subprocess.run(["make", "-s", "-C", _HERE], check=True)
+    return LIB_PATH
+
+
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load an oracle library (the default one, or a test-built variant)."""
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        build()
+    lib = ctypes.CDLL(path)
+    lib.oracle_bf16_decode.restype = ctypes.c_double
+    lib.oracle_bf16_decode.argtypes = [ctypes.c_uint16]
+    lib.oracle_bf16_encode.restype = ctypes.c_uint16
+    lib.oracle_bf16_encode.argtypes = [ctypes.c_double]
+    lib.oracle_e4m3fn_decode.restype = ctypes.c_double
+    lib.oracle_e4m3fn_decode.argtypes = [ctypes.c_uint8]
+    lib.oracle_e4m3fn_encode_sat.restype = ctypes.c_uint8
+    lib.oracle_e4m3fn_encode_sat.argtypes = [ctypes.c_double]
+    lib.oracle_rope_row.restype = None
+    lib.oracle_rope_row.argtypes = [_vp, _vp, _i64, _vp, ctypes.c_int]
+    lib.oracle_inv_rms.restype = ctypes.c_double
+    lib.oracle_inv_rms.argtypes = [_vp, _i64, ctypes.c_double]
+    lib.oracle_rmsnorm_row.restype = None
+    lib.oracle_rmsnorm_row.argtypes = [_vp, _vp, _i64, _vp, ctypes.c_double]
+    lib.oracle_mla_rope_rmsnorm_quant.restype = ctypes.c_int
+    lib.oracle_mla_rope_rmsnorm_quant.argtypes = [
+        _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
+        ctypes.c_float, _i64, _i64, _i64, _vp, ctypes.c_int, _i64, _i64, _i64,
+        _i64, ctypes.c_int, ctypes.c_float, _vp]
+    lib.oracle_qk_rope_paged_ragged.restype = ctypes.c_int
+    lib.oracle_qk_rope_paged_ragged.argtypes = [
+        _vp, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64,
+        _i64, _i64, _vp, _i64, _vp, ctypes.c_int, _vp, _i64, ctypes.c_float]
+    lib.oracle_rms_norm_kv_cache_paged.restype = ctypes.c_int
+    lib.oracle_rms_norm_kv_cache_paged.argtypes = [
+        _vp, _i64, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _i64,
+        _vp, _i64, ctypes.c_float, ctypes.c_float, _i64, ctypes.c_int]
+    return lib
+
+
+def _ptr(a: np.ndarray | None, dtype) -> int | None:
+    if a is None:
+        return None
+    if a.dtype != np.dtype(dtype) or not a.flags["C_CONTIGUOUS"]:
+        raise TypeError(f"oracle wants a C-contiguous {np.dtype(dtype)} array, got "
+                        f"{a.dtype} contiguous={a.flags['C_CONTIGUOUS']}")
+    return a.ctypes.data
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        raise OracleError(f"{what}: oracle precondition failed (code {rc})")
+
+
+class Oracle:
+    """One loaded oracle library; methods take and fill numpy arrays."""
+
+    def __init__(self, path: str | None = None):
+        self.path = path or LIB_PATH
+        self.lib = load(self.path)
+
+    # -- codecs and row steps --------------------------------------------------
+    def bf16_decode(self, bits: int) -> float:
+        return self.lib.oracle_bf16_decode(int(bits))
+
+    def bf16_encode(self, v: float) -> int:
+        return self.lib.oracle_bf16_encode(float(v))
+
+    def e4m3fn_decode(self, code: int) -> float:
+        return self.lib.oracle_e4m3fn_decode(int(code))
+
+    def e4m3fn_encode(self, v: float) -> int:
+        return self.lib.oracle_e4m3fn_encode_sat(float(v))
+
+    def bf16_encode_array(self, v) -> np.ndarray:
+        f = self.lib.oracle_bf16_encode
+        v = np.asarray(v, np.float64)
+        return np.fromiter((f(float(x)) for x in v.ravel()), np.uint16,
+                           count=v.size).reshape(v.shape)
+
+    def e4m3fn_encode_array(self, v) -> np.ndarray:
+        f = self.lib.oracle_e4m3fn_encode_sat
+        v = np.asarray(v, np.float64)
+        return np.fromiter((f(float(x)) for x in v.ravel()), np.uint8,
+                           count=v.size).reshape(v.shape)
+
+    def rope_row(self, x, freqs_row, interleaved: bool) -> np.ndarray:
+        x = np.ascontiguousarray(x, np.float64)
+        fr = np.ascontiguousarray(freqs_row, np.float32)
+        if fr.size < x.size:
+            raise ValueError("freqs row narrower than the rotated row")
+        out = np.empty_like(x)
+        self.lib.oracle_rope_row(x.ctypes.data, out.ctypes.data, x.size,
+                                 fr.ctypes.data, int(bool(interleaved)))
+        return out
+
+    def inv_rms(self, x, eps: float) -> float:
+        x = np.ascontiguousarray(x, np.float64)
+        return self.lib.oracle_inv_rms(x.ctypes.data, x.size, float(eps))
+
+    def rmsnorm_row(self, x, g, eps: float) -> np.ndarray:
+        x = np.ascontiguousarray(x, np.float64)
+        g = np.ascontiguousarray(g, np.float64)
+        y = np.empty_like(x)
+        self.lib.oracle_rmsnorm_row(x.ctypes.data, y.ctypes.data, x.size,
+                                    g.ctypes.data, float(eps))
+        return y
+
+    # -- entry points ----------------------------------------------------------
+    def mla_rope_rmsnorm_quant(self, q_out, q_in, latent, row_offsets,
+                               cache_lengths, page_table, freqs, gamma, epsilon,
+                               cache, layer_idx, scale_mode, tensor_scale=1.0,
+                               token_scales=None):
+        """Fill ``q_out`` and the new rows of ``cache`` (and ``token_scales``).
+
+        Shapes: q [T,H,R] u16; latent [T,Dn+R] u16; row_offsets [B+1] u32;
+        cache_lengths [B] u32; page_table [B,stride] u32; freqs [max_seq,R]
+        f32; gamma [Dn] u16; cache [L,P,S,1,Dn+R] u8 (fp8) or u16 (bf16);
+        token_scales [L,P,S,1] f32.  ``scale_mode``: "per_tensor" |
+        "per_token" (ignored for a bf16 cache).
+        """
+        T, H, R = q_in.shape
+        W = latent.shape[1]
+        Dn = W - R
+        L, P, S = cache.shape[:3]
+        if (cache.shape[3:] != (1, W) or q_out.shape != q_in.shape
+                or latent.shape[0] != T):
+            raise ValueError("inconsistent MLA shapes")
+        B = row_offsets.size - 1
+        cache_type = CACHE_BF16 if cache.dtype == np.uint16 else CACHE_FP8
+        mode = {"per_tensor": SCALE_PER_TENSOR, "per_token": SCALE_PER_TOKEN,
+                "none": 0}[scale_mode]
+        rc = self.lib.oracle_mla_rope_rmsnorm_quant(
+            _ptr(q_out, np.uint16), _ptr(q_in, np.uint16), _ptr(latent, np.uint16),
+            _ptr(row_offsets, np.uint32), _ptr(cache_lengths, np.uint32), B,
+            _ptr(page_table, np.uint32), page_table.shape[1],
+            _ptr(freqs, np.float32), freqs.shape[0], _ptr(gamma, np.uint16),
+            float(epsilon), H, R, Dn, _ptr(cache, cache.dtype), cache_type, L, P, S,
+            int(layer_idx), mode, float(tensor_scale),
+            _ptr(token_scales, np.float32))
+        _check(rc, "mla_rope_rmsnorm_quant")
+
+    def qk_rope_paged_ragged(self, q_out, q_in, row_offsets, cache_lengths,
+                             page_table, k_cache, layer_idx, freqs, position_ids,
+                             interleaved, k_gamma=None, epsilon=1e-6):
+        """Fill ``q_out``; rotate (and optionally K-normalise) ``k_cache``.
+
+        Shapes: q [T,Hq,D] u16; k_cache [L,P,S,Hkv,D] u16; freqs [max_seq,D]
+        f32; position_ids [T] u32 or None; k_gamma [C] u16 or None.
+        """
+        T, Hq, D = q_in.shape
+        L, P, S, Hkv, Dk = k_cache.shape
+        if Dk != D or q_out.shape != q_in.shape:
+            raise ValueError("inconsistent QK shapes")
+        B = row_offsets.size - 1
+        rc = self.lib.oracle_qk_rope_paged_ragged(
+            _ptr(q_out, np.uint16), _ptr(q_in, np.uint16), Hq, D,
+            _ptr(row_offsets, np.uint32), _ptr(cache_lengths, np.uint32), B,
+            _ptr(page_table, np.uint32), page_table.shape[1],
+            _ptr(k_cache, np.uint16), L, P, S, Hkv, int(layer_idx),
+            _ptr(freqs, np.float32), freqs.shape[0], _ptr(position_ids, np.uint32),
+            int(bool(interleaved)), _ptr(k_gamma, np.uint16),
+            0 if k_gamma is None else k_gamma.size, float(epsilon))
+        _check(rc, "qk_rope_paged_ragged")
+
+    def rms_norm_kv_cache_paged(self, k_cache, layer_idx, row_offsets,
+                                cache_lengths, page_table, gamma, epsilon,
+                                weight_offset, total_seq_len,
+                                multiply_before_cast=True):
+        """Normalise the new K rows of ``k_cache`` in place (per-head form)."""
+        L, P, S, Hkv, D = k_cache.shape
+        B = row_offsets.size - 1
+        rc = self.lib.oracle_rms_norm_kv_cache_paged(
+            _ptr(k_cache, np.uint16), L, P, S, Hkv, D, int(layer_idx),
+            _ptr(row_offsets, np.uint32), _ptr(cache_lengths, np.uint32), B,
+            _ptr(page_table, np.uint32), page_table.shape[1],
+            _ptr(gamma, np.uint16), gamma.size, float(epsilon),
+            float(weight_offset), int(total_seq_len),
+            int(bool(multiply_before_cast)))
+        _check(rc, "rms_norm_kv_cache_paged")
+
+
+_DEFAULT: Oracle | None = None
+
+
+def default() -> Oracle:
+    """The oracle built from the committed source."""
+    global _DEFAULT
+    if _DEFAULT is None:
+        _DEFAULT = Oracle()
+    return _DEFAULT

@@ -1,0 +1,403 @@
+/*
+ * pkv_oracle.c -- CPU oracle for the paged-KV pre-attention path.
+ *
+ * TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only the test-suite, the smoke check
+ * and the CPU-baseline leg of the benchmark load this library.  It shares no
+ * source, header, table or helper with the HIP library; it includes nothing but
+ * the C standard library.
+ *
+ * Style: plain scalar loops, every intermediate in IEEE binary64 (built with
+ * -ffp-contract=off, no fast-math), and exactly one rounding into each output
+ * type.  A bf16 value times an fp32 value is exact in binary64 (8 + 24
+ * significant bits), so every output below is the correctly rounded value of
+ * the plain definition, apart from measure-zero ties.
+ *
+ * Sources (Modular MAX / Mojo API reference pages):
+ *   [MLA]   "mla_fused_rope_rmsnorm_quantization" -- summary, Parameters, Args
+ *   [QK]    "generic_fused_qk_rope_bshd_paged_ragged" -- summary, Parameters, Args
+ *   [GRAPH] "mla_graph" module page -- Functions list
+ *   [NORM]  "rms_norm_kv_cache_ragged_paged" -- description paragraphs
+ *   FP8 E4M3FN follows the OCP 8-bit floating point specification (v1.0),
+ *   the public format the name "E4M3FN" in [GRAPH] refers to.
+ *
+ * Readings taken where the pages are silent (each is also tested):
+ *   - freqs_cis row p holds (cos, sin) adjacent: column 2i = cos of pair i,
+ *     column 2i+1 = sin of pair i ("cis" = cos + i sin).
+ *   - Rotation: x' = x cos - y sin, y' = y cos + x sin.
+ *   - MLA rope style is rotate-half: pair (i, i + R/2).  In [QK], interleaved
+ *     means the pair (2i, 2i+1); either way pair i uses frequency column i.
+ *   - Latent row = [kv_norm_dim non-rope values | rope_dim rope values]; gamma
+ *     covers the first kv_norm_dim values.
+ *   - Token t of request b (t = o[b] + j) sits at position and cache slot
+ *     c[b] + j, where c[b] is the request's cache length before this step;
+ *     slot s lives in page page_table[b][s / page_size] at offset
+ *     s mod page_size.
+ *   - RMSNorm: r = 1 / sqrt(mean(x^2) + eps), mean over the normalised
+ *     columns only, eps inside the root, gamma applied before any cast.
+ *   - FP8: value = y / scale (scale is the dequantisation multiplier),
+ *     saturating to +-448, round-to-nearest-even, subnormals and -0 kept.
+ *     Per-token scale = fp32(amax / 448) over the whole row; an all-zero row
+ *     gets scale 0 and codes +-0.
+ *   - In [QK] with a K norm, the norm runs before the rotation and the K row
+ *     is rounded to bf16 once, after both.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <string.h>
+
+/* Return codes: 0 = done; negative = a precondition on the data does not hold
+ * (nothing is guaranteed about the outputs then). */
+#define ORACLE_OK 0
+#define ORACLE_BAD_ARG (-1)
+#define ORACLE_BAD_POSITION (-2)
+#define ORACLE_BAD_PAGE (-3)
+
+/* ------------------------------------------------------------------------- */
+/* Number formats                                                             */
+/* ------------------------------------------------------------------------- */
+
+/* bfloat16: the upper 16 bits of an IEEE binary32. */
+double oracle_bf16_decode(uint16_t bits) {
+  uint32_t u = (uint32_t)bits << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+/* Nearest bfloat16 to v, ties to the even significand, in a single step from
+ * binary64 (no intermediate binary32 rounding).  A bf16 value has 8
+ * significant bits; its smallest quantum (subnormals) is 2^-133. */
+uint16_t oracle_bf16_encode(double v) {
+  uint16_t sign = signbit(v) ? 0x8000u : 0u;
+  if (isnan(v)) return 0x7FC0u;
+  double a = fabs(v);
+  if (a == 0.0) return sign;
+  if (isinf(a)) return (uint16_t)(sign | 0x7F80u);
+  int e;
+  frexp(a, &e);                 /* a = f * 2^e with 0.5 <= f < 1 */
+  int qexp = e - 8;             /* keep 8 significant bits */
+  if (qexp < -133) qexp = -133; /* subnormal range: fixed quantum */
+  double n = nearbyint(ldexp(a, -qexp)); /* default mode: ties to even */
+  double r = ldexp(n, qexp);
+  if (r >= ldexp(1.0, 128)) return (uint16_t)(sign | 0x7F80u); /* overflow */
+  float f = (float)r;           /* exact: r has at most 9 significant bits */
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  return (uint16_t)(sign | (uint16_t)(u >> 16));
+}
+
+/* FP8 E4M3FN (OCP): 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits,
+ * no infinities, S.1111.111 is NaN, largest finite 0x7E = 448, exponent field
+ * 0 holds subnormals m * 2^-9. */
+double oracle_e4m3fn_decode(uint8_t code) {
+  int sign = (code >> 7) & 1;
+  int ef = (code >> 3) & 0xF;
+  int m = code & 7;
+  double mag;
+  if (ef == 0xF && m == 7) return NAN;
+  if (ef == 0)
+    mag = ldexp((double)m, -9);
+  else
+    mag = ldexp(1.0 + m / 8.0, ef - 7);
+  return sign ? -mag : mag;
+}
+
+/* Saturating round-to-nearest-even encode of a binary64 value.  Magnitudes
+ * above 448 become 448 (saturation, never NaN); -0 keeps its sign.  A NaN
+ * input is outside the method's domain and maps to the NaN code. */
+uint8_t oracle_e4m3fn_encode_sat(double v) {
+  uint8_t sign = signbit(v) ? 0x80u : 0u;
+  if (isnan(v)) return (uint8_t)(sign | 0x7Fu);
+  double a = fabs(v);
+  if (a > 448.0) a = 448.0;
+  if (a == 0.0) return sign;
+  int e;
+  frexp(a, &e);                 /* a = f * 2^e with 0.5 <= f < 1 */
+  int qexp = e - 4;             /* 4 significant bits for normals */
+  if (qexp < -9) qexp = -9;     /* subnormal quantum 2^-9 */
+  double n = nearbyint(ldexp(a, -qexp));
+  double r = ldexp(n, qexp);    /* rounded magnitude, <= 448 */
+  if (r == 0.0) return sign;
+  if (r < ldexp(1.0, -6)) {     /* subnormal: r = m * 2^-9, m in 1..7 */
+    int m = (int)ldexp(r, 9);
+    return (uint8_t)(sign | m);
+  }
+  int er;
+  frexp(r, &er);
+  int E = er - 1;               /* r = 1.mmm * 2^E, -6 <= E <= 8 */
+  int m = (int)((ldexp(r, -E) - 1.0) * 8.0);
+  return (uint8_t)(sign | ((E + 7) << 3) | m);
+}
+
+/* ------------------------------------------------------------------------- */
+/* Steps of the method, in binary64                                           */
+/* ------------------------------------------------------------------------- */
+
+/* RoPE over one row of `dim` values with one freqs_cis row ([MLA] Args:
+ * freqs_cis holds per position the cosine/sine values, dim columns).  Pair i
+ * is (i, i + dim/2) for rotate-half and (2i, 2i+1) when interleaved ([QK]
+ * Parameters: interleaved); it is rotated by the angle whose cos/sin sit in
+ * columns 2i and 2i+1.  x and out must not alias. */
+void oracle_rope_row(const double* x, double* out, int64_t dim,
+                     const float* freqs_row, int interleaved) {
+  int64_t half = dim / 2;
+  for (int64_t i = 0; i < half; ++i) {
+    double cs = (double)freqs_row[2 * i];
+    double sn = (double)freqs_row[2 * i + 1];
+    int64_t ia = interleaved ? 2 * i : i;
+    int64_t ib = interleaved ? 2 * i + 1 : i + half;
+    double a = x[ia];
+    double b = x[ib];
+    out[ia] = a * cs - b * sn;
+    out[ib] = b * cs + a * sn;
+  }
+}
+
+/* Inverse RMS of the first n values: 1 / sqrt(sum(x^2)/n + eps). */
+double oracle_inv_rms(const double* x, int64_t n, double eps) {
+  double ss = 0.0;
+  for (int64_t k = 0; k < n; ++k) ss += x[k] * x[k];
+  return 1.0 / sqrt(ss / (double)n + eps);
+}
+
+/* RMSNorm of the first n values, y_k = x_k * r * g_k ([MLA] summary: RMSNorm
+ * on the non-rope part, with gamma; [NORM]: gamma plus weight_offset). */
+void oracle_rmsnorm_row(const double* x, double* y, int64_t n, const double* g,
+                        double eps) {
+  double r = oracle_inv_rms(x, n, eps);
+  for (int64_t k = 0; k < n; ++k) y[k] = x[k] * r * g[k];
+}
+
+/* ------------------------------------------------------------------------- */
+/* Ragged and paged addressing                                                */
+/* ------------------------------------------------------------------------- */
+
+/* Physical page holding cache slot `slot` of request b, or -1 when the page
+ * table entry is missing or out of range. */
+static int64_t page_of(const uint32_t* page_table, int64_t pt_stride,
+                       int64_t num_pages, int64_t page_size, int64_t b,
+                       int64_t slot) {
+  int64_t col = slot / page_size;
+  if (col >= pt_stride) return -1;
+  uint32_t p = page_table[b * pt_stride + col];
+  if ((int64_t)p >= num_pages) return -1;
+  return (int64_t)p;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Entry points                                                               */
+/* ------------------------------------------------------------------------- */
+
+/* Scale modes of the latent cache. */
+#define ORACLE_SCALE_PER_TENSOR 1
+#define ORACLE_SCALE_PER_TOKEN 2
+/* Latent cache element types. */
+#define ORACLE_CACHE_FP8 0
+#define ORACLE_CACHE_BF16 1
+
+/*
+ * Fused MLA pre-attention step ([MLA] summary and Args; [GRAPH] entry
+ * fused_rope_rmsnorm_quantization_kernel: read the latent from a buffer,
+ * quantise at the end, write into the cache).
+ *
+ * Host arrays, all dense and row-major:
+ *   q_out, q_in   bf16 bits [T][H][R]            (q_rope_output, q_rope)
+ *   latent        bf16 bits [T][Dn + R]          (the KV latent input)
+ *   row_offsets   u32 [B + 1]                    (input_row_offsets)
+ *   cache_lengths u32 [B]  length of each request's cache before this step
+ *   page_table    u32 [B][pt_stride]
+ *   freqs         f32 [max_seq_len][R]           (freqs_cis)
+ *   gamma         bf16 bits [Dn]
+ *   cache         [L][P][S][Dn + R] of u8 (fp8 codes) or u16 (bf16 bits)
+ *   token_scales  f32 [L][P][S]  (written in per-token mode only)
+ * Only layer `layer_idx` and only the new tokens' slots are written.
+ */
+int oracle_mla_rope_rmsnorm_quant(
+    uint16_t* q_out, const uint16_t* q_in, const uint16_t* latent,
+    const uint32_t* row_offsets, const uint32_t* cache_lengths, int64_t B,
+    const uint32_t* page_table, int64_t pt_stride, const float* freqs,
+    int64_t max_seq_len, const uint16_t* gamma, float epsilon, int64_t H,
+    int64_t R, int64_t Dn, void* cache, int cache_type, int64_t num_layers,
+    int64_t num_pages, int64_t page_size, int64_t layer_idx, int scale_mode,
+    float tensor_scale, float* token_scales) {
+  if (R <= 0 || R % 2 || Dn <= 0 || H < 0 || B < 0 || layer_idx < 0 ||
+      layer_idx >= num_layers || page_size <= 0)
+    return ORACLE_BAD_ARG;
+  const int64_t W = Dn + R; /* latent row width */
+  double x[4096], y[4096], g[4096], qa[1024], qb[1024];
+  if (W > 4096 || R > 1024) return ORACLE_BAD_ARG;
+  for (int64_t k = 0; k < Dn; ++k) g[k] = oracle_bf16_decode(gamma[k]);
+  const double eps = (double)epsilon; /* the fp32 value, widened exactly */
+  int status = ORACLE_OK;
+
+  for (int64_t b = 0; b < B; ++b) {
+    for (int64_t t = row_offsets[b]; t < (int64_t)row_offsets[b + 1]; ++t) {
+      const int64_t j = t - (int64_t)row_offsets[b];
+      const int64_t pos = (int64_t)cache_lengths[b] + j;
+      const int64_t slot = pos;
+      if (pos >= max_seq_len) { status = ORACLE_BAD_POSITION; continue; }
+      const int64_t page = page_of(page_table, pt_stride, num_pages,
+                                   page_size, b, slot);
+      if (page < 0) { status = ORACLE_BAD_PAGE; continue; }
+      const int64_t off = slot % page_size;
+      const float* fr = freqs + pos * R;
+
+      /* q: RoPE on every head, one bf16 rounding per value. */
+      for (int64_t h = 0; h < H; ++h) {
+        const uint16_t* src = q_in + (t * H + h) * R;
+        uint16_t* dst = q_out + (t * H + h) * R;
+        for (int64_t i = 0; i < R; ++i) qa[i] = oracle_bf16_decode(src[i]);
+        oracle_rope_row(qa, qb, R, fr, 0);
+        for (int64_t i = 0; i < R; ++i) dst[i] = oracle_bf16_encode(qb[i]);
+      }
+
+      /* latent: RMSNorm on the first Dn values, RoPE on the R-value tail. */
+      for (int64_t k = 0; k < W; ++k) x[k] = oracle_bf16_decode(latent[t * W + k]);
+      oracle_rmsnorm_row(x, y, Dn, g, eps);
+      oracle_rope_row(x + Dn, y + Dn, R, fr, 0);
+
+      const int64_t row = ((layer_idx * num_pages + page) * page_size + off);
+      if (cache_type == ORACLE_CACHE_BF16) {
+        uint16_t* dst = (uint16_t*)cache + row * W;
+        for (int64_t k = 0; k < W; ++k) dst[k] = oracle_bf16_encode(y[k]);
+        continue;
+      }
+      uint8_t* dst = (uint8_t*)cache + row * W;
+      if (scale_mode == ORACLE_SCALE_PER_TENSOR) {
+        const double s = (double)tensor_scale;
+        for (int64_t k = 0; k < W; ++k) dst[k] = oracle_e4m3fn_encode_sat(y[k] / s);
+      } else if (scale_mode == ORACLE_SCALE_PER_TOKEN) {
+        double amax = 0.0;
+        for (int64_t k = 0; k < W; ++k)
+          if (fabs(y[k]) > amax) amax = fabs(y[k]);
+        const float st = (float)(amax / 448.0); /* stored fp32, one rounding */
+        for (int64_t k = 0; k < W; ++k)
+          dst[k] = oracle_e4m3fn_encode_sat(st == 0.0f ? y[k] : y[k] / (double)st);
+        token_scales[row] = st;
+      } else {
+        return ORACLE_BAD_ARG;
+      }
+    }
+  }
+  return status;
+}
+
+/*
+ * Paged-ragged Q/K RoPE ([QK] summary, Parameters, Args).  Q is rotated out
+ * of place into q_out; the K rows of the new tokens are rotated in place in
+ * the bf16 cache of layer `layer_idx`.  With k_gamma non-NULL the K row of
+ * every head is first RMS-normalised over its first k_norm_cols columns (the
+ * optional per-head K norm), still unrounded, then rotated, then rounded once.
+ *
+ *   q_out, q_in   bf16 bits [T][Hq][D]
+ *   k_cache       bf16 bits [L][P][S][Hkv][D]
+ *   freqs         f32 [max_seq_len][D]
+ *   position_ids  u32 [T] or NULL (then position = cache length + index)
+ *   k_gamma       bf16 bits [k_norm_cols] or NULL
+ */
+int oracle_qk_rope_paged_ragged(
+    uint16_t* q_out, const uint16_t* q_in, int64_t Hq, int64_t D,
+    const uint32_t* row_offsets, const uint32_t* cache_lengths, int64_t B,
+    const uint32_t* page_table, int64_t pt_stride, uint16_t* k_cache,
+    int64_t num_layers, int64_t num_pages, int64_t page_size, int64_t Hkv,
+    int64_t layer_idx, const float* freqs, int64_t max_seq_len,
+    const uint32_t* position_ids, int interleaved, const uint16_t* k_gamma,
+    int64_t k_norm_cols, float epsilon) {
+  if (D <= 0 || D % 2 || D > 1024 || layer_idx < 0 || layer_idx >= num_layers ||
+      page_size <= 0 || (k_gamma && (k_norm_cols <= 0 || k_norm_cols > D)))
+    return ORACLE_BAD_ARG;
+  double a[1024], r[1024], g[1024];
+  if (k_gamma)
+    for (int64_t k = 0; k < k_norm_cols; ++k) g[k] = oracle_bf16_decode(k_gamma[k]);
+  const double eps = (double)epsilon;
+  int status = ORACLE_OK;
+
+  for (int64_t b = 0; b < B; ++b) {
+    for (int64_t t = row_offsets[b]; t < (int64_t)row_offsets[b + 1]; ++t) {
+      const int64_t j = t - (int64_t)row_offsets[b];
+      const int64_t slot = (int64_t)cache_lengths[b] + j;
+      const int64_t pos = position_ids ? (int64_t)position_ids[t] : slot;
+      if (pos >= max_seq_len) { status = ORACLE_BAD_POSITION; continue; }
+      const int64_t page = page_of(page_table, pt_stride, num_pages,
+                                   page_size, b, slot);
+      if (page < 0) { status = ORACLE_BAD_PAGE; continue; }
+      const int64_t off = slot % page_size;
+      const float* fr = freqs + pos * D;
+
+      for (int64_t h = 0; h < Hq; ++h) {
+        const uint16_t* src = q_in + (t * Hq + h) * D;
+        uint16_t* dst = q_out + (t * Hq + h) * D;
+        for (int64_t i = 0; i < D; ++i) a[i] = oracle_bf16_decode(src[i]);
+        oracle_rope_row(a, r, D, fr, interleaved);
+        for (int64_t i = 0; i < D; ++i) dst[i] = oracle_bf16_encode(r[i]);
+      }
+      for (int64_t h = 0; h < Hkv; ++h) {
+        uint16_t* row = k_cache +
+            ((((layer_idx * num_pages + page) * page_size + off) * Hkv + h) * D);
+        for (int64_t i = 0; i < D; ++i) a[i] = oracle_bf16_decode(row[i]);
+        if (k_gamma) {
+          double inv = oracle_inv_rms(a, k_norm_cols, eps);
+          for (int64_t i = 0; i < k_norm_cols; ++i) a[i] = a[i] * inv * g[i];
+        }
+        oracle_rope_row(a, r, D, fr, interleaved);
+        for (int64_t i = 0; i < D; ++i) row[i] = oracle_bf16_encode(r[i]);
+      }
+    }
+  }
+  return status;
+}
+
+/*
+ * In-place RMSNorm of the new K-cache entries ([NORM] description): tokens
+ * t < total_seq_len are mapped to (request, index) through row_offsets; each
+ * head's first gamma_len columns are normalised with (gamma + weight_offset);
+ * the other columns are left alone.  multiply_before_cast = 1 rounds once,
+ * after the gamma product; = 0 rounds the normalised value to bf16 first,
+ * then multiplies by (gamma + weight_offset) and rounds again.  Only the
+ * per-head form is defined here.
+ *
+ *   k_cache   bf16 bits [L][P][S][Hkv][D]
+ *   gamma     bf16 bits [gamma_len]
+ */
+int oracle_rms_norm_kv_cache_paged(
+    uint16_t* k_cache, int64_t num_layers, int64_t num_pages, int64_t page_size,
+    int64_t Hkv, int64_t D, int64_t layer_idx, const uint32_t* row_offsets,
+    const uint32_t* cache_lengths, int64_t B, const uint32_t* page_table,
+    int64_t pt_stride, const uint16_t* gamma, int64_t gamma_len, float epsilon,
+    float weight_offset, int64_t total_seq_len, int multiply_before_cast) {
+  if (gamma_len <= 0 || gamma_len > D || D > 1024 || layer_idx < 0 ||
+      layer_idx >= num_layers || page_size <= 0)
+    return ORACLE_BAD_ARG;
+  double a[1024], g[1024];
+  for (int64_t k = 0; k < gamma_len; ++k)
+    g[k] = oracle_bf16_decode(gamma[k]) + (double)weight_offset;
+  const double eps = (double)epsilon;
+  int status = ORACLE_OK;
+
+  for (int64_t b = 0; b < B; ++b) {
+    for (int64_t t = row_offsets[b]; t < (int64_t)row_offsets[b + 1]; ++t) {
+      if (t >= total_seq_len) break;
+      const int64_t slot = (int64_t)cache_lengths[b] + (t - (int64_t)row_offsets[b]);
+      const int64_t page = page_of(page_table, pt_stride, num_pages,
+                                   page_size, b, slot);
+      if (page < 0) { status = ORACLE_BAD_PAGE; continue; }
+      const int64_t off = slot % page_size;
+      for (int64_t h = 0; h < Hkv; ++h) {
+        uint16_t* row = k_cache +
+            ((((layer_idx * num_pages + page) * page_size + off) * Hkv + h) * D);
+        for (int64_t i = 0; i < gamma_len; ++i) a[i] = oracle_bf16_decode(row[i]);
+        double inv = oracle_inv_rms(a, gamma_len, eps);
+        for (int64_t i = 0; i < gamma_len; ++i) {
+          if (multiply_before_cast) {
+            row[i] = oracle_bf16_encode(a[i] * inv * g[i]);
+          } else {
+            double n = oracle_bf16_decode(oracle_bf16_encode(a[i] * inv));
+            row[i] = oracle_bf16_encode(n * g[i]);
+          }
+        }
+      }
+    }
+  }
+  return status;
+}

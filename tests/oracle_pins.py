@@ -1,0 +1,647 @@
+"""Pins of the CPU oracle: each check compares the oracle with something other
+than itself -- landmark values of the number formats (``tests/golden/``),
+library routines (torch's fp8/bf16 casts and rms_norm, numpy's complex
+multiply), brute force over every representable value, closed forms and
+invariants of rotation and normalisation, and an inverse (physical slot ->
+token) scan of the page table.
+
+Every pin is a plain function taking an ``oracle.Oracle`` and raising
+AssertionError on failure, so the same pins run against the committed oracle
+(``test_oracle_*.py``) and against deliberately broken builds of it
+(``test_oracle_mutations.py``).
+"""
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+import torch
+
+import workloads
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+# -- independent number-format helpers (test side) ------------------------------
+
+
+def fp8_values_torch() -> np.ndarray:
+    """The 256 E4M3FN codes decoded by torch (a library routine)."""
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    return codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    b = np.asarray(bits, np.uint16).astype(np.uint32) << 16
+    with np.errstate(invalid="ignore"):
+        return b.view(np.float32).astype(np.float64)
+
+
+def fp8_to_f64(codes: np.ndarray) -> np.ndarray:
+    return fp8_values_torch()[np.asarray(codes, np.uint8)]
+
+
+def ulp_bf16(v: np.ndarray) -> np.ndarray:
+    """Spacing of bf16 values at |v| (8 significant bits, quantum >= 2^-133)."""
+    _, e = np.frexp(np.maximum(np.abs(v), 2.0 ** -126))
+    return np.ldexp(1.0, e - 1 - 7)
+
+
+def ulp_fp8(v: np.ndarray) -> np.ndarray:
+    """Spacing of E4M3FN values at |v| (4 significant bits, quantum >= 2^-9)."""
+    _, e = np.frexp(np.maximum(np.abs(v), 2.0 ** -6))
+    return np.ldexp(1.0, e - 1 - 3)
+
+
+def assert_correctly_rounded(got: np.ndarray, ref: np.ndarray, ulp_fn, what: str,
+                             sat: float | None = None) -> None:
+    """|got - ref| <= ulp(ref)/2: got is a nearest representable value of ref.
+    With ``sat``, references beyond +-sat must come back as +-sat."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    if sat is not None:
+        over = np.abs(ref) > sat
+        assert np.all(got[over] == np.sign(ref[over]) * sat), f"{what}: saturation"
+        got, ref = got[~over], ref[~over]
+    err = np.abs(got - ref)
+    bound = 0.5 * ulp_fn(ref) * (1.0 + 1e-12)
+    bad = err > bound
+    if bad.any():
+        i = int(np.flatnonzero(bad)[0])
+        raise AssertionError(
+            f"{what}: {int(bad.sum())} of {bad.size} values not correctly rounded; "
+            f"first ref={ref.ravel()[i]!r} got={got.ravel()[i]!r}")
+
+
+def fp8_encode_bruteforce(v: np.ndarray) -> np.ndarray:
+    """Nearest finite E4M3FN code by exhaustive search (ties -> even code),
+    magnitudes clamped to 448, sign taken from the sign bit."""
+    v = np.asarray(v, np.float64).ravel()
+    mags = fp8_values_torch()[:0x7F]          # codes 0x00..0x7E, increasing
+    codes = np.arange(0x7F)
+    out = np.empty(v.size, np.uint8)
+    for s in range(0, v.size, 4096):
+        a = np.minimum(np.abs(v[s:s + 4096]), 448.0)
+        d = np.abs(a[:, None] - mags[None, :])
+        cand = d == d.min(axis=1, keepdims=True)
+        even = cand & (codes[None, :] % 2 == 0)
+        pick = np.where(even.any(axis=1), even.argmax(axis=1), cand.argmax(axis=1))
+        out[s:s + 4096] = pick.astype(np.uint8) | (
+            np.signbit(v[s:s + 4096]).astype(np.uint8) << 7)
+    return out
+
+
+def bf16_encode_bruteforce(v: np.ndarray) -> np.ndarray:
+    """Nearest bf16 to each fp64 value (ties -> even pattern) among the
+    patterns around numpy's fp32 rounding of it, by direct comparison."""
+    v = np.asarray(v, np.float64).ravel()
+    t = (v.astype(np.float32).view(np.uint32) >> 16).astype(np.int64)
+    cands = np.stack([t - 1, t, t + 1, t + 2], axis=1)
+    sign = (t & 0x8000)
+    mag = cands & 0x7FFF
+    mag = np.clip(mag, 0, 0x7F80)
+    pats = (mag | sign[:, None]).astype(np.uint16)
+    vals = bf16_to_f64(pats)
+    d = np.abs(vals - v[:, None])
+    cand = d == d.min(axis=1, keepdims=True)
+    even = cand & (pats % 2 == 0)
+    pick = np.where(even.any(axis=1), even.argmax(axis=1), cand.argmax(axis=1))
+    return pats[np.arange(v.size), pick]
+
+
+def read_golden(name: str):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                rows.append(line.split())
+    return rows
+
+
+def all_finite_bf16() -> np.ndarray:
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    v = bf16_to_f64(bits)
+    return v[np.isfinite(v)]
+
+
+# -- codec pins -------------------------------------------------------------------
+
+
+def pin_fp8_decode(orc):
+    """Oracle decode == torch decode for all 256 codes, and == the OCP table."""
+    ref = fp8_values_torch()
+    got = np.array([orc.e4m3fn_decode(c) for c in range(256)])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan), "fp8 NaN codes"
+    assert np.array_equal(got[~nan], ref[~nan]), "fp8 decode vs torch"
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan])), "fp8 -0"
+    for row in read_golden("e4m3fn_landmarks.txt"):
+        if row[0] == "decode":
+            code, val = int(row[1], 16), float(row[2])
+            d = orc.e4m3fn_decode(code)
+            assert (math.isnan(val) and math.isnan(d)) or (
+                d == val and math.copysign(1, d) == math.copysign(1, val)), row
+
+
+def pin_fp8_encode_landmarks(orc):
+    for row in read_golden("e4m3fn_landmarks.txt"):
+        if row[0] == "encode":
+            val, code = float(row[1]), int(row[2], 16)
+            assert orc.e4m3fn_encode(val) == code, row
+
+
+def fp8_sweep_values(rng) -> np.ndarray:
+    """Every finite bf16 value at several scales, every midpoint between
+    neighbouring fp8 magnitudes and its fp64 neighbours, and the saturation
+    and subnormal edges."""
+    bf = all_finite_bf16()
+    bf = bf[np.abs(bf) < 1e6]
+    mags = fp8_values_torch()[:0x7F]
+    mids = (mags[1:] + mags[:-1]) / 2.0
+    pts = np.concatenate([mids, np.nextafter(mids, 0), np.nextafter(mids, 1e9)])
+    edges = np.array([447.0, 448.0, 449.0, 463.9, 464.0, 464.1, 479.9, 480.0,
+                      1e6, 1e30, 2.0 ** -10, 2.0 ** -11, 2.0 ** -9, 0.0])
+    scaled = [bf, bf / np.float64(np.float32(0.05)), bf * 2.0 ** -7]
+    sweep = np.concatenate(scaled + [pts, -pts, edges, -edges,
+                                     rng.standard_normal(20000) * 100])
+    return sweep
+
+
+def pin_fp8_encode_bruteforce(orc, n_limit: int | None = None):
+    rng = np.random.Generator(np.random.PCG64(7))
+    v = fp8_sweep_values(rng)
+    if n_limit is not None:
+        v = v[rng.permutation(v.size)[:n_limit]]
+    got = orc.e4m3fn_encode_array(v)
+    ref = fp8_encode_bruteforce(v)
+    bad = got != ref
+    if bad.any():
+        i = int(np.flatnonzero(bad)[0])
+        raise AssertionError(f"fp8 encode: {int(bad.sum())} mismatches; first "
+                             f"v={v[i]!r} got={got[i]:#04x} ref={ref[i]:#04x}")
+
+
+def pin_fp8_encode_torch(orc):
+    """In range (|v| <= 448) the oracle equals torch's fp32 -> e4m3fn cast."""
+    rng = np.random.Generator(np.random.PCG64(8))
+    mag = np.exp(rng.uniform(np.log(2.0 ** -12), np.log(448.0), 20000))
+    v = (mag * np.where(rng.random(mag.size) < 0.5, -1, 1)).astype(np.float32)
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = orc.e4m3fn_encode_array(v.astype(np.float64))
+    assert np.array_equal(got, ref), f"fp8 vs torch: {int((got != ref).sum())} differ"
+
+
+def pin_bf16_landmarks(orc):
+    for row in read_golden("bf16_landmarks.txt"):
+        if row[0] == "decode":
+            code, val = int(row[1], 16), float(row[2])
+            d = orc.bf16_decode(code)
+            assert d == val and math.copysign(1, d) == math.copysign(1, val), row
+        else:
+            val, code = float(row[1]), int(row[2], 16)
+            assert orc.bf16_encode(val) == code, row
+
+
+def pin_bf16_encode_torch(orc):
+    """For fp32 inputs the oracle equals torch's fp32 -> bf16 cast (RNE)."""
+    rng = np.random.Generator(np.random.PCG64(9))
+    bits = rng.integers(0, 2 ** 32, size=30000, dtype=np.uint64).astype(np.uint32)
+    f = bits.view(np.float32)
+    f = f[np.isfinite(f)]
+    ref = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = orc.bf16_encode_array(f.astype(np.float64))
+    assert np.array_equal(got, ref), f"bf16 vs torch: {int((got != ref).sum())} differ"
+
+
+def pin_bf16_encode_bruteforce(orc):
+    """For fp64 inputs between bf16 values (and at their midpoints) the oracle
+    returns the nearest pattern, ties to even, with no double rounding."""
+    rng = np.random.Generator(np.random.PCG64(10))
+    base = rng.standard_normal(20000) * np.exp(rng.uniform(-30, 30, 20000))
+    pats = (base.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    lo = bf16_to_f64(pats)
+    hi = bf16_to_f64(pats + np.uint16(1))    # next pattern: next larger magnitude
+    mid = (lo + hi) / 2.0
+    v = np.concatenate([base, mid, np.nextafter(mid, 0), np.nextafter(mid, np.inf),
+                        lo + (hi - lo) * (0.5 + 2.0 ** -30)])
+    v = v[np.isfinite(v) & (np.abs(v) < 1e38)]
+    got = orc.bf16_encode_array(v)
+    ref = bf16_encode_bruteforce(v)
+    bad = got != ref
+    if bad.any():
+        i = int(np.flatnonzero(bad)[0])
+        raise AssertionError(f"bf16 encode: {int(bad.sum())} mismatches; first "
+                             f"v={v[i]!r} got={got[i]:#06x} ref={ref[i]:#06x}")
+
+
+# -- RoPE row pins -------------------------------------------------------------------
+
+
+def _angle_row(dim, pos, theta, dtype=np.float32):
+    return workloads.freqs_table(pos + 1, dim, theta)[pos].astype(dtype)
+
+
+def pin_rope_pos0_identity(orc):
+    """Row 0 of the table is (1, 0, 1, 0, ...): rotation by 0 is the identity."""
+    rng = np.random.Generator(np.random.PCG64(11))
+    for dim in (2, 64, 128):
+        x = rng.standard_normal(dim)
+        row0 = workloads.freqs_table(4, dim, 10000.0)[0]
+        for inter in (0, 1):
+            assert np.array_equal(orc.rope_row(x, row0, inter), x), (dim, inter)
+
+
+def pin_rope_complex(orc):
+    """Rotate-half pairs (i, i+d/2) and interleaved pairs (2i, 2i+1), each
+    multiplied as complex numbers by cos + i sin (numpy complex128)."""
+    rng = np.random.Generator(np.random.PCG64(12))
+    for dim in (2, 8, 64, 128):
+        for pos in (1, 7, 1000):
+            x = rng.standard_normal(dim)
+            fr = _angle_row(dim, pos, 10000.0)
+            w = fr[0::2].astype(np.float64) + 1j * fr[1::2].astype(np.float64)
+            h = dim // 2
+            z = (x[:h] + 1j * x[h:]) * w
+            ref = np.concatenate([z.real, z.imag])
+            got = orc.rope_row(x, fr, 0)
+            assert np.allclose(got, ref, rtol=1e-15, atol=1e-15), ("half", dim, pos)
+            z = (x[0::2] + 1j * x[1::2]) * w
+            ref = np.empty(dim)
+            ref[0::2], ref[1::2] = z.real, z.imag
+            got = orc.rope_row(x, fr, 1)
+            assert np.allclose(got, ref, rtol=1e-15, atol=1e-15), ("inter", dim, pos)
+
+
+def pin_rope_pair_norm(orc):
+    """|rotated pair|^2 = |pair|^2 (cos^2 + sin^2) holds exactly in fp64 up to
+    rounding: a dropped term or a wrong sign breaks it."""
+    rng = np.random.Generator(np.random.PCG64(13))
+    dim = 64
+    for inter in (0, 1):
+        for pos in (3, 4095):
+            x = rng.standard_normal(dim)
+            fr = _angle_row(dim, pos, 10000.0).astype(np.float64)
+            y = orc.rope_row(x, fr.astype(np.float32), inter)
+            idx = (np.arange(0, dim, 2), np.arange(1, dim, 2)) if inter else (
+                np.arange(dim // 2), np.arange(dim // 2, dim))
+            n_in = (x[idx[0]] ** 2 + x[idx[1]] ** 2) * (fr[0::2] ** 2 + fr[1::2] ** 2)
+            n_out = y[idx[0]] ** 2 + y[idx[1]] ** 2
+            assert np.allclose(n_out, n_in, rtol=1e-13), (inter, pos)
+
+
+def pin_rope_textbook_2d(orc):
+    """dim = 2: (1, 0) rotated by theta lands on (cos, sin); (0, 1) on
+    (-sin, cos) -- the counter-clockwise rotation matrix."""
+    fr = np.array([0.6, 0.8], np.float32)
+    c, s = float(fr[0]), float(fr[1])
+    for inter in (0, 1):
+        assert np.array_equal(orc.rope_row(np.array([1.0, 0.0]), fr, inter), [c, s])
+        assert np.array_equal(orc.rope_row(np.array([0.0, 1.0]), fr, inter), [-s, c])
+
+
+def pin_rope_inverse(orc):
+    """Rotating by the table row with negated sines undoes the rotation up to
+    the fp32 rounding of cos/sin."""
+    rng = np.random.Generator(np.random.PCG64(14))
+    dim = 128
+    x = rng.standard_normal(dim)
+    for inter in (0, 1):
+        fr = _angle_row(dim, 777, 500000.0)
+        inv = fr.copy()
+        inv[1::2] = -inv[1::2]
+        back = orc.rope_row(orc.rope_row(x, fr, inter), inv, inter)
+        assert np.allclose(back, x, rtol=0, atol=1e-6), inter
+
+
+def pin_rope_relative_position(orc):
+    """<rope_m q, rope_n k> = <rope_(m-n) q, k> (fp32 table: to ~1e-6)."""
+    rng = np.random.Generator(np.random.PCG64(15))
+    dim = 64
+    tab = workloads.freqs_table(512, dim, 10000.0)
+    q, k = rng.standard_normal(dim), rng.standard_normal(dim)
+    for inter in (0, 1):
+        for m, n in ((10, 3), (300, 299), (511, 0)):
+            lhs = orc.rope_row(q, tab[m], inter) @ orc.rope_row(k, tab[n], inter)
+            rhs = orc.rope_row(q, tab[m - n], inter) @ k
+            assert abs(lhs - rhs) <= 1e-5 * np.linalg.norm(q) * np.linalg.norm(k), (
+                inter, m, n, lhs, rhs)
+
+
+def pin_rope_interleaved_permutation(orc):
+    """Interleaved rotation of P x equals P (rotate-half rotation of x), where
+    P sends element i to 2i and element i + d/2 to 2i + 1 (bit-exact)."""
+    rng = np.random.Generator(np.random.PCG64(16))
+    for dim in (64, 128):
+        x = rng.standard_normal(dim)
+        fr = _angle_row(dim, 123, 10000.0)
+        h = dim // 2
+        perm = np.empty(dim, np.int64)
+        perm[0::2] = np.arange(h)
+        perm[1::2] = np.arange(h, dim)
+        assert np.array_equal(orc.rope_row(x[perm], fr, 1), orc.rope_row(x, fr, 0)[perm])
+
+
+# -- RMSNorm row pins ----------------------------------------------------------------
+
+
+def pin_rmsnorm_closed_forms(orc):
+    rng = np.random.Generator(np.random.PCG64(17))
+    n = 512
+    x = rng.standard_normal(n) * 3.0
+    ms = float(np.mean(x * x))
+    ones = np.ones(n)
+    for eps in (0.0, 1e-6, 0.25, 10.0):
+        y = orc.rmsnorm_row(x, ones, eps)
+        rms = math.sqrt(float(np.mean(y * y)))
+        assert abs(rms - math.sqrt(ms / (ms + eps))) <= 1e-14, eps
+    # scale invariance (eps = 0)
+    y1 = orc.rmsnorm_row(x, ones, 0.0)
+    assert np.allclose(orc.rmsnorm_row(x * 37.5, ones, 0.0), y1, rtol=1e-14, atol=0)
+    assert np.array_equal(orc.rmsnorm_row(x * 4.0, ones, 0.0), y1)
+    # constant row c: y_k = c g_k / sqrt(c^2 + eps)
+    g = rng.uniform(0.5, 1.5, n)
+    for c in (-2.5, 0.125, 3.0):
+        y = orc.rmsnorm_row(np.full(n, c), g, 0.01)
+        assert np.allclose(y, c * g / math.sqrt(c * c + 0.01), rtol=1e-14), c
+    # inv_rms alone
+    assert abs(orc.inv_rms(x, 0.5) - 1 / math.sqrt(ms + 0.5)) <= 1e-15
+
+
+def pin_rmsnorm_torch(orc):
+    """Equal to torch.nn.functional.rms_norm in float64."""
+    rng = np.random.Generator(np.random.PCG64(18))
+    for n in (8, 128, 512):
+        x = rng.standard_normal(n)
+        g = rng.uniform(0.5, 1.5, n)
+        for eps in (1e-6, 0.3):
+            ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (n,),
+                                               weight=torch.from_numpy(g), eps=eps).numpy()
+            assert np.allclose(orc.rmsnorm_row(x, g, eps), ref, rtol=1e-14, atol=1e-15)
+
+
+# -- composite (entry point) pins -----------------------------------------------------
+
+
+def slot_owners(row_offsets, cache_lengths, page_table, page_size):
+    """Inverse scan of the page table: for every physical (page, offset) that
+    holds one of this step's tokens, that token and its cache slot."""
+    owners = {}
+    B = row_offsets.size - 1
+    for b in range(B):
+        c, n = int(cache_lengths[b]), int(row_offsets[b + 1] - row_offsets[b])
+        for col, page in enumerate(page_table[b]):
+            if page == workloads.UNUSED_PAGE:
+                continue
+            for off in range(page_size):
+                slot = col * page_size + off
+                if c <= slot < c + n:
+                    key = (int(page), off)
+                    assert key not in owners, f"page table maps {key} twice"
+                    owners[key] = (int(row_offsets[b]) + slot - c, slot)
+    return owners
+
+
+def _complex_rope(x, cs, sn, interleaved):
+    """x [..., d] fp64, cs/sn broadcastable to [..., d/2]."""
+    w = cs + 1j * sn
+    out = np.empty_like(x)
+    if interleaved:
+        z = (x[..., 0::2] + 1j * x[..., 1::2]) * w
+        out[..., 0::2], out[..., 1::2] = z.real, z.imag
+    else:
+        h = x.shape[-1] // 2
+        z = (x[..., :h] + 1j * x[..., h:]) * w
+        out[..., :h], out[..., h:] = z.real, z.imag
+    return out
+
+
+def mla_reference(case):
+    """Independent fp64 reference for a fused MLA case: numpy complex RoPE and
+    torch's float64 rms_norm, tokens located by the inverse page-table scan.
+    Returns (q_ref [T,H,R], y_ref [T,W], owners)."""
+    S = case.meta["page_size"]
+    owners = slot_owners(case.row_offsets, case.cache_lengths, case.page_table, S)
+    assert len(owners) == case.T, "some token has no slot"
+    pos = np.empty(case.T, np.int64)
+    for (page, off), (t, slot) in owners.items():
+        pos[t] = slot
+    fr = case.freqs[pos].astype(np.float64)
+    cs, sn = fr[:, 0::2], fr[:, 1::2]
+    q_ref = _complex_rope(bf16_to_f64(case.q), cs[:, None, :], sn[:, None, :], False)
+    x = bf16_to_f64(case.latent)
+    Dn = case.Dn
+    y_ref = np.empty_like(x)
+    y_ref[:, :Dn] = torch.nn.functional.rms_norm(
+        torch.from_numpy(x[:, :Dn].copy()), (Dn,),
+        weight=torch.from_numpy(bf16_to_f64(case.gamma)), eps=case.epsilon).numpy()
+    y_ref[:, Dn:] = _complex_rope(x[:, Dn:], cs, sn, False)
+    return q_ref, y_ref, owners
+
+
+def run_mla(orc, case):
+    q_out = np.zeros_like(case.q)
+    cache = case.cache.copy()
+    ts = None if case.token_scales is None else case.token_scales.copy()
+    orc.mla_rope_rmsnorm_quant(q_out, case.q, case.latent, case.row_offsets,
+                               case.cache_lengths, case.page_table, case.freqs,
+                               case.gamma, case.epsilon, cache, case.layer_idx,
+                               case.scale_mode, case.tensor_scale, ts)
+    return q_out, cache, ts
+
+
+def check_mla_against_reference(case, q_out, cache, ts):
+    q_ref, y_ref, owners = mla_reference(case)
+    assert_correctly_rounded(bf16_to_f64(q_out), q_ref, ulp_bf16, "q_rope_output")
+    L = case.layer_idx
+    expect = case.cache.copy()
+    written = np.zeros(case.cache.shape[:3], bool)
+    for (page, off), (t, slot) in owners.items():
+        written[L, page, off] = True
+        row = cache[L, page, off, 0]
+        if case.cache.dtype == np.uint16:
+            assert_correctly_rounded(bf16_to_f64(row), y_ref[t], ulp_bf16, f"row {t}")
+        else:
+            if case.scale_mode == "per_tensor":
+                s = float(case.tensor_scale)
+            else:
+                amax = float(np.max(np.abs(y_ref[t])))
+                s = float(np.float32(amax / 448.0))
+                got_s = float(ts[L, page, off, 0])
+                assert got_s == s or abs(got_s - s) <= 2.0 ** -23 * s, (t, got_s, s)
+                s = got_s
+                if amax > 0:
+                    assert np.any((row & 0x7F) == 0x7E), f"row {t}: no +-448 code"
+            if s == 0.0:
+                assert np.all((row & 0x7F) == 0), f"row {t}: zero scale"
+            else:
+                assert_correctly_rounded(fp8_to_f64(row), y_ref[t] / s, ulp_fp8,
+                                         f"fp8 row {t}", sat=448.0)
+        expect[L, page, off] = cache[L, page, off]
+    # every byte outside the new tokens' rows is unchanged
+    assert np.array_equal(cache, expect), "bytes outside the new rows changed"
+    if ts is not None:
+        keep = ~written
+        assert np.array_equal(ts[keep].view(np.uint32),
+                              case.token_scales[keep].view(np.uint32)), "scales outside"
+
+
+def small_mla_cases():
+    """Small cases covering ragged batches, prior lengths, page crossings,
+    zero-length requests, both scale modes and a bf16 cache."""
+    yield workloads.mla_tiny()
+    yield workloads.build_mla("mla_small_decode", 2001, [1] * 9, [0, 5, 15, 16, 17, 31, 32, 47, 63],
+                              H=8, page_size=16, max_seq_len=64, spare_pages=3,
+                              scale_mode="per_tensor", tensor_scale=0.05)
+    yield workloads.build_mla("mla_small_ragged", 2002, [7, 0, 13, 1, 0, 20], [3, 9, 0, 30, 0, 2],
+                              H=16, page_size=8, max_seq_len=64, spare_pages=5,
+                              latent_sigma=2.0, scale_mode="per_tensor", tensor_scale=0.05)
+    yield workloads.build_mla("mla_small_token", 2003, [1, 1, 1, 9, 12], [40, 0, 100, 0, 3],
+                              H=4, page_size=16, max_seq_len=128, spare_pages=2,
+                              outlier_p=0.01, scale_mode="per_token")
+    yield workloads.build_mla("mla_small_bf16", 2004, [4, 6], [2, 0], H=4,
+                              page_size=4, max_seq_len=16, spare_pages=2,
+                              scale_mode="none", cache_dtype="bf16")
+
+
+def pin_mla_composite(orc):
+    for case in small_mla_cases():
+        q_out, cache, ts = run_mla(orc, case)
+        check_mla_against_reference(case, q_out, cache, ts)
+
+
+def pin_mla_position0(orc):
+    """Tokens at position 0 come back unchanged in q (values; +-0 equal)."""
+    case = workloads.build_mla("mla_pos0", 2005, [1] * 6, [0] * 6, H=8,
+                               page_size=4, max_seq_len=8, spare_pages=1)
+    q_out, _, _ = run_mla(orc, case)
+    assert np.array_equal(bf16_to_f64(q_out), bf16_to_f64(case.q))
+
+
+def pin_mla_zero_row_per_token(orc):
+    """An all-zero latent row under per-token scaling stores scale 0 and zero
+    codes; the non-rope part keeps each input's sign (x r g with r, g > 0)."""
+    case = workloads.build_mla("mla_zero", 2006, [2], [0], H=4, page_size=4,
+                               max_seq_len=8, spare_pages=1, scale_mode="per_token")
+    case.latent[0, :] = 0x0000
+    case.latent[0, ::3] = 0x8000
+    q_out, cache, ts = run_mla(orc, case)
+    page = int(case.page_table[0, 0])
+    row = cache[case.layer_idx, page, 0, 0]
+    assert ts[case.layer_idx, page, 0, 0] == 0.0
+    assert np.all((row & 0x7F) == 0)
+    Dn = case.Dn
+    assert np.array_equal(row[:Dn] >> 7, (case.latent[0, :Dn] >> 15).astype(np.uint8))
+
+
+def qk_reference(case, k_norm: bool):
+    S = case.meta["page_size"]
+    owners = slot_owners(case.row_offsets, case.cache_lengths, case.page_table, S)
+    assert len(owners) == case.T
+    slot_of = np.empty(case.T, np.int64)
+    for (page, off), (t, slot) in owners.items():
+        slot_of[t] = slot
+    pos = case.position_ids.astype(np.int64) if case.position_ids is not None else slot_of
+    fr = case.freqs[pos].astype(np.float64)
+    cs, sn = fr[:, 0::2], fr[:, 1::2]
+    q_ref = _complex_rope(bf16_to_f64(case.q), cs[:, None, :], sn[:, None, :],
+                          case.interleaved)
+    L = case.layer_idx
+    k_ref = {}
+    for (page, off), (t, slot) in owners.items():
+        x = bf16_to_f64(case.k_cache[L, page, off])            # [Hkv, D]
+        if k_norm:
+            C = case.gamma.size
+            x[:, :C] = torch.nn.functional.rms_norm(
+                torch.from_numpy(x[:, :C].copy()), (C,),
+                weight=torch.from_numpy(bf16_to_f64(case.gamma)),
+                eps=case.epsilon).numpy()
+        k_ref[(page, off)] = _complex_rope(x, cs[t][None, :], sn[t][None, :],
+                                           case.interleaved)
+    return q_ref, k_ref
+
+
+def small_qk_cases():
+    yield workloads.build_qk("qk_small_inter", 3001, [5, 0, 17, 1], [0, 4, 11, 31],
+                             Hq=4, Hkv=2, D=128, page_size=16, max_seq_len=4096,
+                             theta=500000.0, interleaved=True, with_position_ids=True,
+                             norm_cols=128, spare_pages=3)
+    yield workloads.build_qk("qk_small_half", 3002, [3, 9], [14, 0], Hq=3, Hkv=1, D=64,
+                             page_size=4, max_seq_len=64, theta=10000.0,
+                             interleaved=False, with_position_ids=False,
+                             norm_cols=40, spare_pages=2)
+    yield workloads.build_qk("qk_small_nonorm", 3003, [6, 2], [1, 7], Hq=2, Hkv=2, D=128,
+                             page_size=8, max_seq_len=64, theta=10000.0,
+                             interleaved=True, with_position_ids=False,
+                             norm_cols=None, spare_pages=1)
+
+
+def pin_qk_composite(orc):
+    for case in small_qk_cases():
+        for use_norm in ((False, True) if case.gamma is not None else (False,)):
+            q_out = np.zeros_like(case.q)
+            k = case.k_cache.copy()
+            orc.qk_rope_paged_ragged(q_out, case.q, case.row_offsets, case.cache_lengths,
+                                     case.page_table, k, case.layer_idx, case.freqs,
+                                     case.position_ids, case.interleaved,
+                                     case.gamma if use_norm else None, case.epsilon)
+            q_ref, k_ref = qk_reference(case, use_norm)
+            assert_correctly_rounded(bf16_to_f64(q_out), q_ref, ulp_bf16, "qk q")
+            expect = case.k_cache.copy()
+            L = case.layer_idx
+            for (page, off), ref in k_ref.items():
+                assert_correctly_rounded(bf16_to_f64(k[L, page, off]), ref, ulp_bf16,
+                                         f"qk k {page},{off}")
+                expect[L, page, off] = k[L, page, off]
+            assert np.array_equal(k, expect), "K elements outside the new rows changed"
+
+
+def pin_rms_norm_kv(orc):
+    """In-place K RMSNorm against torch rms_norm (fp64) with gamma + offset:
+    multiply_before_cast rounds once; otherwise the normalised value is
+    rounded to bf16 (by the separately pinned codec) before the gamma product."""
+    for case in small_qk_cases():
+        C = case.gamma.size if case.gamma is not None else 48
+        rng = np.random.Generator(np.random.PCG64(case.seed))
+        gamma = workloads.bf16_bits(rng.uniform(0.5, 1.5, C).astype(np.float32))
+        for mbc in (True, False):
+            for w in (0.0, 0.25):
+                for total in (case.T, max(case.T - 3, 0)):
+                    k = case.k_cache.copy()
+                    orc.rms_norm_kv_cache_paged(k, case.layer_idx, case.row_offsets,
+                                                case.cache_lengths, case.page_table,
+                                                gamma, case.epsilon, w, total, mbc)
+                    S = case.meta["page_size"]
+                    owners = slot_owners(case.row_offsets, case.cache_lengths,
+                                         case.page_table, S)
+                    L = case.layer_idx
+                    expect = case.k_cache.copy()
+                    g = bf16_to_f64(gamma) + w
+                    for (page, off), (t, slot) in owners.items():
+                        if t >= total:
+                            continue
+                        x = bf16_to_f64(case.k_cache[L, page, off])[:, :C]
+                        if mbc:
+                            ref = torch.nn.functional.rms_norm(
+                                torch.from_numpy(x.copy()), (C,),
+                                weight=torch.from_numpy(g), eps=case.epsilon).numpy()
+                        else:
+                            nrm = torch.nn.functional.rms_norm(
+                                torch.from_numpy(x.copy()), (C,), eps=case.epsilon).numpy()
+                            ref = bf16_to_f64(orc.bf16_encode_array(nrm)) * g
+                        assert_correctly_rounded(bf16_to_f64(k[L, page, off][:, :C]), ref,
+                                                 ulp_bf16, f"kvnorm {t} mbc={mbc}")
+                        expect[L, page, off, :, :C] = k[L, page, off, :, :C]
+                    assert np.array_equal(k, expect), "kvnorm touched other elements"
+
+
+ALL_PINS = [
+    pin_fp8_decode, pin_fp8_encode_landmarks, pin_fp8_encode_bruteforce,
+    pin_fp8_encode_torch, pin_bf16_landmarks, pin_bf16_encode_torch,
+    pin_bf16_encode_bruteforce, pin_rope_pos0_identity, pin_rope_complex,
+    pin_rope_pair_norm, pin_rope_textbook_2d, pin_rope_inverse,
+    pin_rope_relative_position, pin_rope_interleaved_permutation,
+    pin_rmsnorm_closed_forms, pin_rmsnorm_torch, pin_mla_composite,
+    pin_mla_position0, pin_mla_zero_row_per_token, pin_qk_composite,
+    pin_rms_norm_kv,
+]

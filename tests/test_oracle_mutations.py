@@ -1,0 +1,128 @@
+"""The pins must catch plausible mistakes in the oracle.
+
+Each mutant is the committed oracle source with one small, plausible error
+planted in it (a flipped sign, a swapped operand or index, a dropped term, a
+wrong rounding rule, a wrong address).  The mutant is compiled with gcc into
+a temporary directory and every pin is run against it in a child process; the
+child must fail (an assertion, or a crash of the mutant).  Everything here
+runs on the CPU; the HIP library is not involved.
+"""
+import os
+import subprocess
+import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "pkv_oracle.c")
+
+# (name, text in the committed source, replacement)
+MUTANTS = [
+    ("rope_first_sign", "out[ia] = a * cs - b * sn;", "out[ia] = a * cs + b * sn;"),
+    ("rope_second_sign", "out[ib] = b * cs + a * sn;", "out[ib] = b * cs - a * sn;"),
+    ("rope_swapped_operand", "out[ib] = b * cs + a * sn;", "out[ib] = a * cs + b * sn;"),
+    ("rope_cos_sin_columns", "double cs = (double)freqs_row[2 * i];",
+     "double cs = (double)freqs_row[2 * i + 1];"),
+    ("rope_split_table", "double sn = (double)freqs_row[2 * i + 1];",
+     "double sn = (double)freqs_row[half + i];"),
+    ("rope_half_pairing", "int64_t ib = interleaved ? 2 * i + 1 : i + half;",
+     "int64_t ib = interleaved ? 2 * i + 1 : half - 1 - i;"),
+    ("rope_interleaved_pairing", "int64_t ia = interleaved ? 2 * i : i;",
+     "int64_t ia = interleaved ? i : i;"),
+    ("rms_dropped_eps", "return 1.0 / sqrt(ss / (double)n + eps);",
+     "return 1.0 / sqrt(ss / (double)n);"),
+    ("rms_eps_outside_root", "return 1.0 / sqrt(ss / (double)n + eps);",
+     "return 1.0 / (sqrt(ss / (double)n) + eps);"),
+    ("rms_sum_not_mean", "return 1.0 / sqrt(ss / (double)n + eps);",
+     "return 1.0 / sqrt(ss + eps);"),
+    ("rms_dropped_gamma", "for (int64_t k = 0; k < n; ++k) y[k] = x[k] * r * g[k];",
+     "for (int64_t k = 0; k < n; ++k) y[k] = x[k] * r;"),
+    ("mla_position_ignores_prior", "const int64_t pos = (int64_t)cache_lengths[b] + j;",
+     "const int64_t pos = j;"),
+    ("mla_rope_tail_normalised", "oracle_rope_row(x + Dn, y + Dn, R, fr, 0);",
+     "oracle_rope_row(y + Dn, x + Dn, R, fr, 0); memcpy(y + Dn, x + Dn, R * sizeof(double));"),
+    ("mla_scale_multiplied", "dst[k] = oracle_e4m3fn_encode_sat(y[k] / s);",
+     "dst[k] = oracle_e4m3fn_encode_sat(y[k] * s);"),
+    ("mla_amax_nope_only", "for (int64_t k = 0; k < W; ++k)\n          if (fabs(y[k]) > amax)",
+     "for (int64_t k = 0; k < Dn; ++k)\n          if (fabs(y[k]) > amax)"),
+    ("mla_token_scale_448", "const float st = (float)(amax / 448.0);",
+     "const float st = (float)(amax / 240.0);"),
+    ("page_offset", "const int64_t off = slot % page_size;\n      const float* fr = freqs + pos * R;",
+     "const int64_t off = (slot + 1) % page_size;\n      const float* fr = freqs + pos * R;"),
+    ("page_table_column", "int64_t col = slot / page_size;", "int64_t col = slot / page_size + 1;"),
+    ("wrong_layer", "const int64_t row = ((layer_idx * num_pages + page) * page_size + off);",
+     "const int64_t row = (((layer_idx - 1) * num_pages + page) * page_size + off);"),
+    ("fp8_ties_away", "double n = nearbyint(ldexp(a, -qexp));\n  double r = ldexp(n, qexp);    /* rounded magnitude",
+     "double n = round(ldexp(a, -qexp));\n  double r = ldexp(n, qexp);    /* rounded magnitude"),
+    ("fp8_no_saturation", "if (a > 448.0) a = 448.0;", "if (a > 480.0) a = 480.0;"),
+    ("fp8_flush_subnormals", "if (qexp < -9) qexp = -9;     /* subnormal quantum 2^-9 */",
+     "if (qexp < -6) qexp = -6;"),
+    ("fp8_bias", "return (uint8_t)(sign | ((E + 7) << 3) | m);",
+     "return (uint8_t)(sign | ((E + 8) << 3) | m);"),
+    ("fp8_decode_subnormal", "mag = ldexp((double)m, -9);", "mag = ldexp((double)m, -10);"),
+    ("bf16_truncate", "double n = nearbyint(ldexp(a, -qexp)); /* default mode: ties to even */",
+     "double n = trunc(ldexp(a, -qexp));"),
+    ("bf16_precision", "int qexp = e - 8;             /* keep 8 significant bits */",
+     "int qexp = e - 9;"),
+    ("qk_ignores_position_ids",
+     "const int64_t pos = position_ids ? (int64_t)position_ids[t] : slot;",
+     "const int64_t pos = slot;"),
+    ("qk_norm_skips_gamma", "for (int64_t i = 0; i < k_norm_cols; ++i) a[i] = a[i] * inv * g[i];",
+     "for (int64_t i = 0; i < k_norm_cols; ++i) a[i] = a[i] * inv;"),
+    ("qk_norm_all_columns", "double inv = oracle_inv_rms(a, k_norm_cols, eps);",
+     "double inv = oracle_inv_rms(a, D, eps);"),
+    ("kvnorm_no_offset", "g[k] = oracle_bf16_decode(gamma[k]) + (double)weight_offset;",
+     "g[k] = oracle_bf16_decode(gamma[k]);"),
+    ("kvnorm_cast_order", "if (multiply_before_cast) {", "if (!multiply_before_cast) {"),
+    ("kvnorm_ignores_total", "if (t >= total_seq_len) break;", "(void)total_seq_len;"),
+]
+
+RUNNER = r"""
+import sys
+sys.path[:0] = [{root!r}, {tests!r}]
+import oracle, oracle_pins
+orc = oracle.Oracle({lib!r})
+for pin in oracle_pins.ALL_PINS:
+    try:
+        pin(orc)
+    except Exception as e:
+        print("CAUGHT by", pin.__name__, ":", str(e)[:200])
+        sys.exit(1)
+print("SURVIVED")
+"""
+
+
+def _run_mutant(name, old, new, tmp):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"{name}: anchor text must occur once"
+    path = os.path.join(tmp, f"{name}.c")
+    with open(path, "w") as f:
+        f.write(src.replace(old, new))
+    lib = os.path.join(tmp, f"lib_{name}.so")
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-ffp-contract=off", "-shared",
+                    "-o", lib, path, "-lm"], check=True, capture_output=True)
+    code = RUNNER.format(root=ROOT, tests=os.path.dirname(os.path.abspath(__file__)), lib=lib)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                       timeout=600)
+    return name, r.returncode, (r.stdout + r.stderr)[-400:]
+
+
+@pytest.mark.slow
+def test_every_mutant_is_caught():
+    with tempfile.TemporaryDirectory() as tmp:
+        with ThreadPoolExecutor(max_workers=6) as ex:
+            results = list(ex.map(lambda m: _run_mutant(*m, tmp), MUTANTS))
+    survived = [(n, out) for n, rc, out in results if rc == 0]
+    assert not survived, f"mutants not caught by any pin: {survived}"
+
+
+def test_committed_oracle_passes_runner():
+    """The same runner reports no failure on the committed oracle."""
+    import oracle
+    code = RUNNER.format(root=ROOT, tests=os.path.dirname(os.path.abspath(__file__)),
+                         lib=oracle.LIB_PATH)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                       timeout=600)
+    assert r.returncode == 0 and "SURVIVED" in r.stdout, r.stdout + r.stderr
