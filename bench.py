@@ -1,0 +1,280 @@
+"""Benchmark of the fused MLA pre-attention step on one MI355X.
+
+Default workload: DeepSeek-V3-shaped prefill -- 8 requests with new lengths
+U{512..4096} (seeded; 17108 tokens), no prior cache, 128 query heads x rope
+64, latent 512 + 64, FP8 E4M3FN paged cache (page size 128) with per-tensor
+scale 0.05.  One step = one mla_rope_rmsnorm_quant launch over the whole
+batch (q RoPE, latent RMSNorm + RoPE, FP8 quantisation, paged store), inputs
+resident in HBM.  Prints one JSON line.
+
+Also reported (``siblings``): the other workloads and entry points, each timed
+the same way -- MLA decode (256 x 1 token, 128 heads), mixed prefill + decode
+with per-token scales (16 heads), the Llama-shaped paged-ragged Q/K RoPE with
+fused per-head K norm, and the in-place K-cache RMSNorm.
+
+``--calibrate-copy`` runs a plain elementwise copy of known size instead (the
+reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E peak, GB/s
+METRIC = "fused MLA RoPE+RMSNorm+FP8 cache-write: tokens/s and effective HBM GB/s (% of peak)"
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_wavefront_amd", "csrc",
+                          "mla_rope_rmsnorm_quant.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# -- algorithmic bytes (what the method must move, read + written) ---------------------
+
+def mla_bytes(case) -> int:
+    """q in + q out (2 x H x R x 2) + latent row in (W x 2) + cache row out
+    (W x 1, + 4 for a per-token scale) per token; once per launch: freqs rows
+    of the distinct positions (R x 4 each), gamma, offsets, prior lengths,
+    the page-table entries read, the per-tensor scale."""
+    T, H, R, W = case.T, case.H, case.R, case.latent.shape[1]
+    per_tok = 2 * H * R * 2 + W * 2 + W * 1 + (4 if case.scale_mode == "per_token" else 0)
+    pos = np.concatenate([np.arange(c, c + n) for c, n in
+                          zip(case.cache_lengths.astype(np.int64),
+                              np.diff(case.row_offsets.astype(np.int64)))]) if T else np.zeros(0)
+    S = case.meta["page_size"]
+    pages_read = len({(b, int(p) // S) for b, (c, n) in enumerate(
+        zip(case.cache_lengths, np.diff(case.row_offsets.astype(np.int64))))
+        for p in range(int(c), int(c) + int(n))})
+    shared = (len(np.unique(pos)) * R * 4 + case.Dn * 2 + (case.B + 1) * 4 + case.B * 4
+              + 4 * pages_read + (4 if case.scale_mode == "per_tensor" else 0))
+    return T * per_tok + shared
+
+
+def qk_bytes(case, with_norm: bool) -> int:
+    """Q in + out, K rows in + out (in place), one position id and one freqs
+    row per token; gamma, offsets, prior lengths and page-table entries once."""
+    T, Hq, D = case.q.shape
+    Hkv = case.k_cache.shape[3]
+    per_tok = 2 * Hq * D * 2 + 2 * Hkv * D * 2 + D * 4 + (4 if case.position_ids is not None else 0)
+    shared = (case.B + 1) * 4 + case.B * 4 + T * 4 // case.meta["page_size"] + \
+        (case.gamma.size * 2 if with_norm else 0)
+    return T * per_tok + shared
+
+
+def kv_norm_bytes(case, cols: int) -> int:
+    T = case.T
+    Hkv = case.k_cache.shape[3]
+    return T * 2 * Hkv * cols * 2 + (case.B + 1) * 4 + case.B * 4 + cols * 2
+
+
+# -- timing ------------------------------------------------------------------------------
+
+def time_launches(fn, steps: int, warmup: int):
+    """Warm up, then time exactly `steps` launches bracketed by device syncs.
+    Returns (wall seconds, per-launch durations in seconds from HIP events
+    recorded on the launch stream)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    t0 = time.perf_counter()
+    events[0].record()
+    for i in range(steps):
+        fn()
+        events[i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    durs = np.array([events[i].elapsed_time(events[i + 1]) for i in range(steps)]) * 1e-3
+    return wall, durs
+
+
+def profiled_traffic(name: str):
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it was
+    taken on the current kernel source; otherwise None."""
+    path = os.path.join(PROFILES, f"{name}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    m_h = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    if not (m_b and m_h):
+        return None
+    cur = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    return float(m_b.group(1)) if m_h.group(1) == cur else None
+
+
+# -- workloads -------------------------------------------------------------------------
+
+def mla_runner(case):
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import gpu_helpers as gh
+    dev = gh.MlaDevice(case)
+    return dev, dev.run
+
+
+def measure_mla(case, steps, warmup):
+    dev, fn = mla_runner(case)
+    wall, durs = time_launches(fn, steps, warmup)
+    nbytes = mla_bytes(case)
+    return dict(T=case.T, bytes=nbytes, wall=wall, durs=durs,
+                avg=float(durs.mean()), med=float(np.median(durs)))
+
+
+def summarize(name, r, steps):
+    gbps = r["bytes"] / r["avg"] / 1e9
+    return {"workload": name, "tokens": r["T"], "bytes_per_launch": r["bytes"],
+            "kernel_us_avg": round(r["avg"] * 1e6, 2), "kernel_us_p50": round(r["med"] * 1e6, 2),
+            "kernel_us_p10": round(float(np.percentile(r["durs"], 10)) * 1e6, 2),
+            "kernel_us_p90": round(float(np.percentile(r["durs"], 90)) * 1e6, 2),
+            "tokens_per_s": round(r["T"] * steps / r["wall"], 1),
+            "effective_GBps": round(gbps, 1), "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2)}
+
+
+def measure_siblings(steps, warmup):
+    import workloads
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import gpu_helpers as gh
+    out = {}
+    for name in ("mla_decode", "mla_mixed"):
+        log(f"[bench] sibling {name}")
+        case = workloads.NAMED[name]()
+        out[name] = summarize(name, measure_mla(case, steps, warmup), steps)
+        del case
+    case = workloads.qk_generic()
+    dev = gh.QkDevice(case)
+    log("[bench] sibling qk_rope_paged_ragged")
+    wall, durs = time_launches(lambda: dev.rope(True), steps, warmup)
+    out["qk_rope_paged_ragged"] = summarize(
+        "qk_generic (interleaved, position ids, fused per-head K norm)",
+        dict(T=case.T, bytes=qk_bytes(case, True), wall=wall, durs=durs,
+             avg=float(durs.mean()), med=float(np.median(durs))), steps)
+    log("[bench] sibling rms_norm_kv_cache_paged")
+    wall, durs = time_launches(lambda: dev.kv_norm(dev.gamma, 0.0, case.T, True), steps, warmup)
+    out["rms_norm_kv_cache_paged"] = summarize(
+        "qk_generic K cache (8 heads x 128, gamma 128)",
+        dict(T=case.T, bytes=kv_norm_bytes(case, 128), wall=wall, durs=durs,
+             avg=float(durs.mean()), med=float(np.median(durs))), steps)
+    return out
+
+
+def cpu_baseline(case, budget_s=10.0):
+    """The oracle (single-threaded C, binary64) on the same host arrays,
+    repeated over the whole workload until about budget_s has elapsed."""
+    import oracle
+    orc = oracle.default()
+    q_out = np.zeros_like(case.q)
+    tokens, t0 = 0, time.perf_counter()
+    runs = 0
+    while True:
+        cache = case.cache.copy()
+        t1 = time.perf_counter()
+        orc.mla_rope_rmsnorm_quant(q_out, case.q, case.latent, case.row_offsets,
+                                   case.cache_lengths, case.page_table, case.freqs, case.gamma,
+                                   case.epsilon, cache, case.layer_idx, case.scale_mode,
+                                   case.tensor_scale, None)
+        runs += 1
+        tokens += case.T
+        spent = time.perf_counter() - t0
+        if spent >= budget_s or (time.perf_counter() - t1) * (runs + 1) > 3 * budget_s:
+            break
+    oracle_s = time.perf_counter() - t0
+    return {"value": round(tokens / oracle_s, 1), "unit": "tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"whole workload ({case.T} tokens) x {runs} run(s), "
+                      f"{oracle_s:.1f} s, single thread"}
+
+
+def calibrate_copy(steps, warmup, mib=1024):
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    wall, durs = time_launches(lambda: torch.neg(src, out=dst), steps, warmup)
+    nbytes = 2 * n * 4
+    print(json.dumps({"calibrate_copy_bytes_read": n * 4, "bytes_written": n * 4,
+                      "kernel_us_avg": round(float(durs.mean()) * 1e6, 2),
+                      "GBps": round(nbytes / float(durs.mean()) / 1e9, 1)}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mla_prefill",
+                    choices=["mla_prefill", "mla_decode", "mla_mixed"])
+    ap.add_argument("--no-siblings", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the path needs no inter-GPU exchange and is measured on a single MI355X.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no ROCm GPU visible", file=sys.stderr)
+        sys.exit(1)
+    if args.calibrate_copy:
+        calibrate_copy(args.steps, args.warmup)
+        return
+    import workloads
+    log(f"[bench] generating {args.workload}")
+    case = workloads.NAMED[args.workload]()
+    log(f"[bench] T={case.T} B={case.B} H={case.H}; timing {args.steps} steps")
+    r = measure_mla(case, args.steps, args.warmup)
+    main_sum = summarize(args.workload, r, args.steps)
+    gbps = main_sum["effective_GBps"]
+    siblings = None if args.no_siblings else measure_siblings(max(10, args.steps // 2),
+                                                              args.warmup)
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        cpu = cpu_baseline(case)
+    traffic = profiled_traffic(args.workload)
+    line = {
+        "metric": METRIC,
+        "value": round(case.T * args.steps / r["wall"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["wall"] / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 in, fp32 math, fp8 e4m3fn cache",
+        "data": "synthetic (seeded; DeepSeek-V3-shaped random tensors, no weights)",
+        "config": {"workload": args.workload, "tokens": case.T, "requests": case.B,
+                   "q_heads": case.H, "rope_dim": case.R, "kv_norm_dim": case.Dn,
+                   "page_size": case.meta["page_size"], "scale_mode": case.scale_mode,
+                   "parallelism": "single GPU"},
+        "effective_GBps": gbps,
+        "pct_of_hbm_peak": main_sum["pct_of_hbm_peak"],
+        "kernel_us": {k: main_sum[k] for k in ("kernel_us_avg", "kernel_us_p10",
+                                               "kernel_us_p50", "kernel_us_p90")},
+        "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "algorithmic_bytes": r["bytes"]},
+        "cpu_baseline": cpu,
+        "siblings": siblings,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

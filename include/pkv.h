@@ -1,0 +1,205 @@
+/*
+ * pkv.h -- C ABI of the paged-KV pre-attention library (gfx950 / MI355X).
+ *
+ * Three entry points, each one stream-ordered kernel launch:
+ *
+ *   mla_rope_rmsnorm_quant   fused MLA step: RoPE on q_rope, RMSNorm on the
+ *                            latent row's non-rope part, RoPE on its rope tail,
+ *                            FP8 E4M3FN quantisation, paged cache write.
+ *                            Page "mla_fused_rope_rmsnorm_quantization"
+ *                            (summary, Args) and the
+ *                            fused_rope_rmsnorm_quantization_kernel entry of
+ *                            the "mla_graph" module page.
+ *   qk_rope_paged_ragged     RoPE on Q (out of place) and on the new K rows of a
+ *                            paged cache (in place), optional per-head K
+ *                            RMSNorm fused in front of the K rotation.
+ *                            Page "generic_fused_qk_rope_bshd_paged_ragged".
+ *   rms_norm_kv_cache_paged  in-place RMSNorm of the new K-cache rows.
+ *                            Page "rms_norm_kv_cache_ragged_paged".
+ *
+ * Conventions shared by all entry points
+ * --------------------------------------
+ * Pointers are DEVICE pointers unless marked (host).  Element types: bf16 is
+ * stored as its 16-bit pattern, fp8 as its byte; "stride" arguments count
+ * elements, not bytes, and the innermost dimension is always contiguous.
+ *
+ * Ragged batch: input_row_offsets[0..batch] (device, u32) is non-decreasing
+ * with input_row_offsets[0] = 0 and input_row_offsets[batch] = total tokens;
+ * request b owns tokens input_row_offsets[b] .. input_row_offsets[b+1]-1.
+ * Token j of request b (counted from 0) goes to cache slot
+ * cache_lengths[b] + j, where cache_lengths[b] is the request's length before
+ * this step; slot s lives in physical page page_table[b*stride + s/page_size]
+ * at offset s % page_size.  Without explicit position ids the token's RoPE
+ * position equals its slot.
+ *
+ * freqs_cis: [max_seq_len][dim] fp32, row p holds for pair i the cosine in
+ * column 2i and the sine in column 2i+1 of the angle p * theta_i.
+ *
+ * Ownership: the caller allocates and frees every buffer.  The library
+ * allocates nothing, keeps no state between calls, never synchronises and may
+ * be called from several host threads.  Outputs may alias their inputs only
+ * exactly (q_out == q_in); partial overlap is undefined.
+ *
+ * Errors: every entry point returns PKV_OK (0) or a pkv_status.  All argument
+ * checks run on the host before anything is enqueued; on error nothing is
+ * enqueued and no memory is touched.  PKV_ERR_LAUNCH reports a refused launch.
+ * Faults inside the kernel surface at the caller's next synchronisation.
+ *
+ * Device-data rules the host cannot check (offsets monotone, positions below
+ * max_seq_len, page-table entries below num_pages, table wide enough for every
+ * slot, no two tokens mapped to one slot): the kernels check the first four
+ * per token before dereferencing anything derived from them; a token that
+ * fails a check is skipped entirely (no output written for it) and, when the
+ * cache descriptor carries an error counter, the counter is incremented once
+ * per skipped token.  Tokens sharing a slot race (undefined result).
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pkv_status {
+  PKV_OK = 0,
+  PKV_ERR_NULL = 1,        /* a required pointer is NULL */
+  PKV_ERR_SHAPE = 2,       /* sizes inconsistent with each other */
+  PKV_ERR_DTYPE = 3,       /* element type not accepted by this entry point */
+  PKV_ERR_ALIGN = 4,       /* pointer or stride breaks the 16-byte rule */
+  PKV_ERR_UNSUPPORTED = 5, /* valid request that this build does not implement */
+  PKV_ERR_RANGE = 6,       /* index argument out of range (e.g. layer_idx) */
+  PKV_ERR_LAUNCH = 7       /* the HIP runtime refused the kernel launch */
+} pkv_status;
+
+typedef enum pkv_dtype {
+  PKV_DTYPE_BF16 = 0,
+  PKV_DTYPE_FP8_E4M3FN = 1 /* OCP FP8 E4M3FN: bias 7, max 448, no inf */
+} pkv_dtype;
+
+typedef enum pkv_scale_mode {
+  PKV_SCALE_NONE = 0,       /* bf16 cache, no quantisation */
+  PKV_SCALE_PER_TENSOR = 1, /* scales[0] (read only): one dequant multiplier */
+  PKV_SCALE_PER_TOKEN = 2   /* scales[layer][page][slot][head] written per row:
+                               max|row| / 448 rounded to fp32 */
+} pkv_scale_mode;
+
+/*
+ * A paged cache for all layers (the collection's role on the pages: one pool
+ * of pages per layer, retrieved by layer_idx).  Element (layer, page, slot,
+ * head, d) sits at data + layer*layer_stride + page*page_stride +
+ * slot*slot_stride + head*head_stride + d (element units, d contiguous).
+ * Host struct; the pointers inside it are device pointers.
+ */
+typedef struct pkv_paged_cache {
+  void* data;                     /* pool base, 16-byte aligned */
+  int32_t dtype;                  /* pkv_dtype */
+  uint32_t num_layers;
+  uint32_t num_pages;             /* pages per layer */
+  uint32_t page_size;             /* slots per page (> 0) */
+  uint32_t num_heads;             /* heads per slot */
+  uint32_t head_dim;              /* elements per head */
+  int64_t layer_stride, page_stride, slot_stride, head_stride; /* elements */
+  const uint32_t* cache_lengths;  /* [batch] prior length of each request */
+  const uint32_t* page_table;     /* [batch][page_table_stride] page ids */
+  uint32_t page_table_stride;     /* entries per request row (>= 1) */
+  int32_t scale_mode;             /* pkv_scale_mode */
+  float* scales;                  /* PER_TENSOR: [1]; PER_TOKEN: dense
+                                     [num_layers][num_pages][page_size][num_heads] */
+  uint32_t* error_count;          /* optional (may be NULL): skipped tokens */
+} pkv_paged_cache;
+
+/*
+ * Fused MLA pre-attention step.  For every token t (request b, index j,
+ * position p = cache_lengths[b] + j):
+ *   q_rope_out[t,h,:] = RoPE_p(q_rope[t,h,:]) for every head h, rotate-half
+ *                       pairs (i, i + rope_dim/2), fp32 math, one bf16 RNE;
+ *   y[0:kv_norm_dim]  = x * r * gamma,  r = 1/sqrt(mean(x^2) + epsilon),
+ *                       x = kv_latent[t, 0:kv_norm_dim];
+ *   y[kv_norm_dim: ]  = RoPE_p(kv_latent[t, kv_norm_dim:kv_norm_dim+rope_dim]);
+ *   cache[layer_idx][page][slot][0][:] = E4M3FN_sat_rne(y / scale)  (fp8) or
+ *                                        bf16_rne(y)                  (bf16).
+ * Per-token scale mode writes scale = fp32(max|y| / 448) beside the row.
+ *
+ *   q_rope_out      bf16 [total_tokens][num_heads][rope_dim], strides
+ *                   qo_tok_stride / qo_head_stride (elements, multiples of 8)
+ *   q_rope          bf16, same shape, strides qi_tok_stride / qi_head_stride
+ *   kv_latent       bf16 [total_tokens][kv_norm_dim + rope_dim], row stride
+ *                   kv_row_stride (multiple of 8)
+ *   input_row_offsets u32 [batch_size + 1]
+ *   total_tokens    (host) number of new tokens = input_row_offsets[batch_size]
+ *   freqs_cis       fp32 [max_seq_len][rope_dim]
+ *   gamma           bf16 [kv_norm_dim]
+ *   kv_cache        (host) descriptor: dtype FP8_E4M3FN with scale mode
+ *                   PER_TENSOR or PER_TOKEN, or BF16 with scale mode NONE;
+ *                   num_heads 1, head_dim kv_norm_dim + rope_dim
+ *   stream          hipStream_t to enqueue on (NULL = default stream)
+ * Supported here: rope_dim 64, kv_norm_dim 512, any num_heads >= 0.
+ */
+int mla_rope_rmsnorm_quant(void* q_rope_out, int64_t qo_tok_stride, int64_t qo_head_stride,
+                           const void* q_rope, int64_t qi_tok_stride, int64_t qi_head_stride,
+                           const void* kv_latent, int64_t kv_row_stride,
+                           const uint32_t* input_row_offsets, uint32_t batch_size,
+                           uint32_t total_tokens, uint32_t num_heads, uint32_t rope_dim,
+                           uint32_t kv_norm_dim, const float* freqs_cis, uint32_t max_seq_len,
+                           const void* gamma, float epsilon, const pkv_paged_cache* kv_cache,
+                           uint32_t layer_idx, void* stream);
+
+/*
+ * Paged-ragged fused Q/K RoPE.  Q is rotated into q_out; the K rows of the
+ * new tokens (slot cache_lengths[b] + j) are rotated in place for every KV
+ * head.  Position = position_ids[t] when position_ids != NULL, else the slot.
+ * interleaved != 0 rotates adjacent pairs (2i, 2i+1), otherwise pairs
+ * (i, i + head_dim/2); pair i always uses freqs_cis columns 2i, 2i+1.
+ * With k_norm_gamma != NULL, each K head's first k_norm_cols columns are
+ * first RMS-normalised with gamma (fp32, unrounded), then the row is
+ * rotated and rounded to bf16 once.
+ *
+ *   q_out, q_proj   bf16 [total_tokens][num_q_heads][head_dim] with strides
+ *   k_cache         (host) descriptor: dtype BF16, scale mode NONE,
+ *                   head_dim == the q head_dim
+ *   freqs_cis       fp32 [max_seq_len][head_dim]
+ *   position_ids    u32 [total_tokens] or NULL
+ *   k_norm_gamma    bf16 [k_norm_cols] or NULL; 0 < k_norm_cols <= head_dim
+ * Supported here: head_dim 64 or 128.
+ */
+int qk_rope_paged_ragged(void* q_out, int64_t qo_tok_stride, int64_t qo_head_stride,
+                         const void* q_proj, int64_t qi_tok_stride, int64_t qi_head_stride,
+                         uint32_t total_tokens, uint32_t num_q_heads, uint32_t head_dim,
+                         const uint32_t* input_row_offsets, uint32_t batch_size,
+                         const pkv_paged_cache* k_cache, uint32_t layer_idx,
+                         const float* freqs_cis, uint32_t max_seq_len,
+                         const uint32_t* position_ids, int interleaved,
+                         const void* k_norm_gamma, uint32_t k_norm_cols, float epsilon,
+                         void* stream);
+
+/*
+ * In-place RMSNorm of the new K-cache rows.  Tokens t < total_seq_len (host
+ * value) are mapped to (request, index) through input_row_offsets; for every
+ * head the first gamma_len columns become x * r * (gamma + weight_offset)
+ * with r = 1/sqrt(mean over those columns of x^2 + epsilon); the remaining
+ * columns are not written.  multiply_before_cast != 0 rounds to bf16 once,
+ * after the gamma product; 0 rounds x * r to bf16, then multiplies by
+ * (gamma + weight_offset) and rounds again.
+ *
+ *   k_cache        (host) descriptor: dtype BF16, scale mode NONE
+ *   gamma          bf16 [gamma_len], 0 < gamma_len <= head_dim
+ *   per_head_norm  must be non-zero (one norm per head); 0 returns
+ *                  PKV_ERR_UNSUPPORTED
+ * Supported here: head_dim 64 or 128.
+ */
+int rms_norm_kv_cache_paged(const pkv_paged_cache* k_cache, uint32_t layer_idx,
+                            const void* gamma, uint32_t gamma_len, float epsilon,
+                            float weight_offset, uint32_t total_seq_len,
+                            const uint32_t* input_row_offsets, uint32_t batch_size,
+                            int per_head_norm, int multiply_before_cast, void* stream);
+
+/* Static, NUL-terminated name of a status code. */
+const char* pkv_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -1,0 +1,191 @@
+"""Python binding of the paged-KV pre-attention library (``include/pkv.h``).
+
+Argument marshalling only: every function here checks nothing beyond what it
+needs to fill the C call, passes torch device tensors as raw pointers with
+element strides, and raises :class:`PkvError` when the library returns a
+non-zero status.  All computation happens in the HIP kernels of ``libpkv.so``
+(built for gfx950 by ``paged_kv_cache_wavefront_amd.build``); there is no
+fallback: importing the module without the built library raises.
+
+Tensor conventions: bf16 data is ``torch.bfloat16``; the FP8 cache is
+``torch.uint8`` (or ``torch.float8_e4m3fn``) holding E4M3FN codes; index
+arrays are ``torch.int32`` or ``torch.uint32`` holding unsigned values; all of
+them live on the same ROCm device.  Kernels are enqueued on ``stream`` (a
+``torch.cuda.Stream``) or on torch's current stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpkv.so")
+
+PKV_DTYPE_BF16 = 0
+PKV_DTYPE_FP8_E4M3FN = 1
+PKV_SCALE_NONE = 0
+PKV_SCALE_PER_TENSOR = 1
+PKV_SCALE_PER_TOKEN = 2
+
+EXPORTED = ("mla_rope_rmsnorm_quant", "qk_rope_paged_ragged", "rms_norm_kv_cache_paged",
+            "pkv_status_string")
+
+
+class PkvError(RuntimeError):
+    def __init__(self, func: str, status: int, text: str):
+        super().__init__(f"{func} failed: {text} (status {status})")
+        self.status = status
+
+
+class PagedCache(ctypes.Structure):
+    """Mirror of ``pkv_paged_cache``."""
+
+    _fields_ = [
+        ("data", ctypes.c_void_p),
+        ("dtype", ctypes.c_int32),
+        ("num_layers", ctypes.c_uint32),
+        ("num_pages", ctypes.c_uint32),
+        ("page_size", ctypes.c_uint32),
+        ("num_heads", ctypes.c_uint32),
+        ("head_dim", ctypes.c_uint32),
+        ("layer_stride", ctypes.c_int64),
+        ("page_stride", ctypes.c_int64),
+        ("slot_stride", ctypes.c_int64),
+        ("head_stride", ctypes.c_int64),
+        ("cache_lengths", ctypes.c_void_p),
+        ("page_table", ctypes.c_void_p),
+        ("page_table_stride", ctypes.c_uint32),
+        ("scale_mode", ctypes.c_int32),
+        ("scales", ctypes.c_void_p),
+        ("error_count", ctypes.c_void_p),
+    ]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m paged_kv_cache_wavefront_amd.build` "
+            "(hipcc, gfx950) first -- there is no CPU fallback")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, u32, vp, f32 = ctypes.c_int64, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_float
+    cache_p = ctypes.POINTER(PagedCache)
+    lib.mla_rope_rmsnorm_quant.restype = ctypes.c_int
+    lib.mla_rope_rmsnorm_quant.argtypes = [
+        vp, i64, i64, vp, i64, i64, vp, i64, vp, u32, u32, u32, u32, u32, vp, u32, vp, f32,
+        cache_p, u32, vp]
+    lib.qk_rope_paged_ragged.restype = ctypes.c_int
+    lib.qk_rope_paged_ragged.argtypes = [
+        vp, i64, i64, vp, i64, i64, u32, u32, u32, vp, u32, cache_p, u32, vp, u32, vp,
+        ctypes.c_int, vp, u32, f32, vp]
+    lib.rms_norm_kv_cache_paged.restype = ctypes.c_int
+    lib.rms_norm_kv_cache_paged.argtypes = [
+        cache_p, u32, vp, u32, f32, f32, u32, vp, u32, ctypes.c_int, ctypes.c_int, vp]
+    lib.pkv_status_string.restype = ctypes.c_char_p
+    lib.pkv_status_string.argtypes = [ctypes.c_int]
+    return lib
+
+
+_lib = _load()
+
+
+def library() -> ctypes.CDLL:
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return _lib.pkv_status_string(int(status)).decode()
+
+
+def _check(func: str, status: int) -> None:
+    if status != 0:
+        raise PkvError(func, status, status_string(status))
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def paged_cache(data: torch.Tensor, cache_lengths: torch.Tensor, page_table: torch.Tensor,
+                scale_mode: int = PKV_SCALE_NONE, scales: torch.Tensor | None = None,
+                error_count: torch.Tensor | None = None) -> PagedCache:
+    """Describe a 5-D cache pool ``data[layer, page, slot, head, dim]`` (bf16,
+    or uint8 / float8_e4m3fn for FP8), its per-request prior lengths and its
+    page table ``[batch, stride]``.  ``scales``: fp32 ``[1]`` (per-tensor) or
+    ``[layers, pages, page_size, heads]`` (per-token)."""
+    if data.dim() != 5:
+        raise ValueError("cache data must be [layers, pages, page_size, heads, head_dim]")
+    if data.dtype == torch.bfloat16:
+        dt = PKV_DTYPE_BF16
+    elif data.dtype in (torch.uint8, torch.float8_e4m3fn):
+        dt = PKV_DTYPE_FP8_E4M3FN
+    else:
+        raise TypeError(f"unsupported cache dtype {data.dtype}")
+    if data.stride(4) != 1:
+        raise ValueError("the head_dim axis of the cache must be contiguous")
+    if page_table.dim() != 2 or page_table.stride(1) != 1:
+        raise ValueError("page_table must be a row-major [batch, stride] tensor")
+    L, P, S, H, D = data.shape
+    return PagedCache(
+        data=data.data_ptr(), dtype=dt, num_layers=L, num_pages=P, page_size=S,
+        num_heads=H, head_dim=D, layer_stride=data.stride(0), page_stride=data.stride(1),
+        slot_stride=data.stride(2), head_stride=data.stride(3),
+        cache_lengths=cache_lengths.data_ptr(), page_table=page_table.data_ptr(),
+        page_table_stride=page_table.stride(0), scale_mode=scale_mode,
+        scales=_ptr(scales), error_count=_ptr(error_count))
+
+
+def mla_rope_rmsnorm_quant(q_rope_output: torch.Tensor, q_rope: torch.Tensor,
+                           kv_latent: torch.Tensor, input_row_offsets: torch.Tensor,
+                           freqs_cis: torch.Tensor, gamma: torch.Tensor, epsilon: float,
+                           kv_cache: PagedCache, layer_idx: int, stream=None) -> None:
+    """Fused MLA step (C: ``mla_rope_rmsnorm_quant``).  q tensors are
+    ``[tokens, heads, rope_dim]`` bf16 (rope_dim axis contiguous), kv_latent
+    ``[tokens, kv_norm_dim + rope_dim]`` bf16, freqs_cis ``[max_seq_len,
+    rope_dim]`` fp32, gamma ``[kv_norm_dim]`` bf16."""
+    T, H, R = q_rope.shape
+    st = _lib.mla_rope_rmsnorm_quant(
+        _ptr(q_rope_output), q_rope_output.stride(0), q_rope_output.stride(1),
+        _ptr(q_rope), q_rope.stride(0), q_rope.stride(1),
+        _ptr(kv_latent), kv_latent.stride(0),
+        _ptr(input_row_offsets), input_row_offsets.numel() - 1, T, H, R,
+        kv_latent.shape[1] - R, _ptr(freqs_cis), freqs_cis.shape[0], _ptr(gamma),
+        float(epsilon), ctypes.byref(kv_cache), int(layer_idx), _stream(stream))
+    _check("mla_rope_rmsnorm_quant", st)
+
+
+def qk_rope_paged_ragged(q_out: torch.Tensor, q_proj: torch.Tensor,
+                         input_row_offsets: torch.Tensor, k_cache: PagedCache,
+                         layer_idx: int, freqs_cis: torch.Tensor,
+                         position_ids: torch.Tensor | None, interleaved: bool,
+                         k_norm_gamma: torch.Tensor | None = None, epsilon: float = 1e-6,
+                         stream=None) -> None:
+    """Paged-ragged fused Q/K RoPE (C: ``qk_rope_paged_ragged``).  Q tensors
+    are ``[tokens, heads, head_dim]`` bf16; K is rotated in place."""
+    T, Hq, D = q_proj.shape
+    st = _lib.qk_rope_paged_ragged(
+        _ptr(q_out), q_out.stride(0), q_out.stride(1), _ptr(q_proj), q_proj.stride(0),
+        q_proj.stride(1), T, Hq, D, _ptr(input_row_offsets), input_row_offsets.numel() - 1,
+        ctypes.byref(k_cache), int(layer_idx), _ptr(freqs_cis), freqs_cis.shape[0],
+        _ptr(position_ids), int(bool(interleaved)), _ptr(k_norm_gamma),
+        0 if k_norm_gamma is None else k_norm_gamma.numel(), float(epsilon), _stream(stream))
+    _check("qk_rope_paged_ragged", st)
+
+
+def rms_norm_kv_cache_paged(k_cache: PagedCache, layer_idx: int, gamma: torch.Tensor,
+                            epsilon: float, weight_offset: float, total_seq_len: int,
+                            input_row_offsets: torch.Tensor, per_head_norm: bool = True,
+                            multiply_before_cast: bool = True, stream=None) -> None:
+    """In-place K-cache RMSNorm (C: ``rms_norm_kv_cache_paged``)."""
+    st = _lib.rms_norm_kv_cache_paged(
+        ctypes.byref(k_cache), int(layer_idx), _ptr(gamma), gamma.numel(), float(epsilon),
+        float(weight_offset), int(total_seq_len), _ptr(input_row_offsets),
+        input_row_offsets.numel() - 1, int(bool(per_head_norm)),
+        int(bool(multiply_before_cast)), _stream(stream))
+    _check("rms_norm_kv_cache_paged", st)

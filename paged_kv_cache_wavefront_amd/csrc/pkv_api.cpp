@@ -1,0 +1,239 @@
+// pkv_api.cpp -- the exported C ABI (include/pkv.h): host-side argument
+// validation, kernel selection and launch.  Every check runs before anything
+// is enqueued; no entry point allocates, synchronises or keeps state.
+#include "../../include/pkv.h"
+
+#include <hip/hip_runtime.h>
+
+#include "pkv_internal.h"
+
+namespace {
+
+using pkv::CacheView;
+
+constexpr uint32_t kMlaRope = 64;
+constexpr uint32_t kMlaNope = 512;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool mult(int64_t v, int64_t k) { return v >= 0 && v % k == 0; }
+
+size_t elem_bytes(int32_t dtype) { return dtype == PKV_DTYPE_BF16 ? 2 : 1; }
+
+// Checks common to every cache descriptor; fills the per-layer view.
+int check_cache(const pkv_paged_cache* c, uint32_t layer_idx, uint32_t batch_size,
+                CacheView* view) {
+  if (c == nullptr) return PKV_ERR_NULL;
+  if (c->dtype != PKV_DTYPE_BF16 && c->dtype != PKV_DTYPE_FP8_E4M3FN) return PKV_ERR_DTYPE;
+  if (c->num_layers == 0 || c->num_pages == 0 || c->page_size == 0 || c->num_heads == 0 ||
+      c->head_dim == 0 || c->page_table_stride == 0)
+    return PKV_ERR_SHAPE;
+  if (layer_idx >= c->num_layers) return PKV_ERR_RANGE;
+  if (batch_size > 0 && (c->cache_lengths == nullptr || c->page_table == nullptr))
+    return PKV_ERR_NULL;
+  if (c->data == nullptr) return PKV_ERR_NULL;
+  // Every 16-byte vector access stays aligned when the pool base and every
+  // stride are multiples of 16 bytes.
+  const int64_t per16 = 16 / (int64_t)elem_bytes(c->dtype);
+  if (!aligned16(c->data) || !mult(c->layer_stride, per16) || !mult(c->page_stride, per16) ||
+      !mult(c->slot_stride, per16) || !mult(c->head_stride, per16))
+    return PKV_ERR_ALIGN;
+  view->layer_base = static_cast<char*>(c->data) +
+                     (int64_t)layer_idx * c->layer_stride * (int64_t)elem_bytes(c->dtype);
+  view->page_stride = c->page_stride;
+  view->slot_stride = c->slot_stride;
+  view->head_stride = c->head_stride;
+  view->num_pages = c->num_pages;
+  view->page_size = c->page_size;
+  view->num_heads = c->num_heads;
+  view->cache_lengths = c->cache_lengths;
+  view->page_table = c->page_table;
+  view->pt_stride = c->page_table_stride;
+  view->error_count = c->error_count;
+  return PKV_OK;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH; }
+
+// Heads per wave for the MLA kernel: the widest chunk that still gives the
+// chip at least 16 waves per CU (256 CUs); decode-sized batches split the
+// heads of a token over several waves.
+int mla_heads_per_wave(uint32_t tokens, uint32_t heads) {
+  const uint64_t want = 4096;
+  for (int hpw : {128, 64, 32}) {
+    const uint64_t chunks = (heads + hpw - 1) / hpw;
+    if ((uint64_t)tokens * (chunks ? chunks : 1) >= want) return hpw;
+  }
+  return 16;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_status_string(int status) {
+  switch (status) {
+    case PKV_OK: return "PKV_OK";
+    case PKV_ERR_NULL: return "PKV_ERR_NULL: a required pointer is NULL";
+    case PKV_ERR_SHAPE: return "PKV_ERR_SHAPE: inconsistent sizes";
+    case PKV_ERR_DTYPE: return "PKV_ERR_DTYPE: element type not accepted";
+    case PKV_ERR_ALIGN: return "PKV_ERR_ALIGN: pointer or stride not 16-byte aligned";
+    case PKV_ERR_UNSUPPORTED: return "PKV_ERR_UNSUPPORTED: not implemented for these sizes";
+    case PKV_ERR_RANGE: return "PKV_ERR_RANGE: index argument out of range";
+    case PKV_ERR_LAUNCH: return "PKV_ERR_LAUNCH: kernel launch refused";
+    default: return "unknown pkv status";
+  }
+}
+
+int mla_rope_rmsnorm_quant(void* q_rope_out, int64_t qo_tok_stride, int64_t qo_head_stride,
+                           const void* q_rope, int64_t qi_tok_stride, int64_t qi_head_stride,
+                           const void* kv_latent, int64_t kv_row_stride,
+                           const uint32_t* input_row_offsets, uint32_t batch_size,
+                           uint32_t total_tokens, uint32_t num_heads, uint32_t rope_dim,
+                           uint32_t kv_norm_dim, const float* freqs_cis, uint32_t max_seq_len,
+                           const void* gamma, float epsilon, const pkv_paged_cache* kv_cache,
+                           uint32_t layer_idx, void* stream) {
+  if (kv_cache == nullptr) return PKV_ERR_NULL;
+  if (rope_dim == 0 || rope_dim % 2 != 0 || kv_norm_dim == 0) return PKV_ERR_SHAPE;
+  if (kv_cache->num_heads != 1 || kv_cache->head_dim != kv_norm_dim + rope_dim)
+    return PKV_ERR_SHAPE;
+  if (rope_dim != kMlaRope || kv_norm_dim != kMlaNope) return PKV_ERR_UNSUPPORTED;
+  pkv::MlaOut mode;
+  if (kv_cache->dtype == PKV_DTYPE_FP8_E4M3FN && kv_cache->scale_mode == PKV_SCALE_PER_TENSOR)
+    mode = pkv::MlaOut::Fp8PerTensor;
+  else if (kv_cache->dtype == PKV_DTYPE_FP8_E4M3FN && kv_cache->scale_mode == PKV_SCALE_PER_TOKEN)
+    mode = pkv::MlaOut::Fp8PerToken;
+  else if (kv_cache->dtype == PKV_DTYPE_BF16 && kv_cache->scale_mode == PKV_SCALE_NONE)
+    mode = pkv::MlaOut::Bf16;
+  else
+    return PKV_ERR_DTYPE;
+  if (total_tokens > 0 && batch_size == 0) return PKV_ERR_SHAPE;
+  if (max_seq_len == 0) return PKV_ERR_SHAPE;
+  CacheView view{};
+  int st = check_cache(kv_cache, layer_idx, batch_size, &view);
+  if (st != PKV_OK) return st;
+  if (total_tokens == 0) return PKV_OK;
+
+  if (input_row_offsets == nullptr || freqs_cis == nullptr || gamma == nullptr ||
+      kv_latent == nullptr)
+    return PKV_ERR_NULL;
+  if (num_heads > 0 && (q_rope == nullptr || q_rope_out == nullptr)) return PKV_ERR_NULL;
+  if (mode != pkv::MlaOut::Bf16 && kv_cache->scales == nullptr) return PKV_ERR_NULL;
+  if (!aligned16(q_rope) || !aligned16(q_rope_out) || !aligned16(kv_latent) ||
+      !aligned16(gamma) || !aligned16(freqs_cis) || !mult(qo_tok_stride, 8) ||
+      !mult(qo_head_stride, 8) || !mult(qi_tok_stride, 8) || !mult(qi_head_stride, 8) ||
+      !mult(kv_row_stride, 8))
+    return PKV_ERR_ALIGN;
+
+  pkv::MlaArgs a{};
+  a.q_out = static_cast<uint16_t*>(q_rope_out);
+  a.qo_tok = qo_tok_stride;
+  a.qo_head = qo_head_stride;
+  a.q_in = static_cast<const uint16_t*>(q_rope);
+  a.qi_tok = qi_tok_stride;
+  a.qi_head = qi_head_stride;
+  a.latent = static_cast<const uint16_t*>(kv_latent);
+  a.kv_row = kv_row_stride;
+  a.offsets = input_row_offsets;
+  a.batch = batch_size;
+  a.total_tokens = total_tokens;
+  a.num_heads = num_heads;
+  const int hpw = mla_heads_per_wave(total_tokens, num_heads);
+  a.chunks = num_heads == 0 ? 1u : (num_heads + (uint32_t)hpw - 1) / (uint32_t)hpw;
+  a.freqs = freqs_cis;
+  a.max_seq_len = max_seq_len;
+  a.gamma = static_cast<const uint16_t*>(gamma);
+  a.epsilon = epsilon;
+  a.tensor_scale = kv_cache->scales;
+  a.token_scales = nullptr;
+  if (mode == pkv::MlaOut::Fp8PerToken)
+    a.token_scales = kv_cache->scales + (int64_t)layer_idx * kv_cache->num_pages *
+                                            kv_cache->page_size * kv_cache->num_heads;
+  a.cache = view;
+  return launch_status(pkv::launch_mla(a, mode, hpw, static_cast<hipStream_t>(stream)));
+}
+
+int qk_rope_paged_ragged(void* q_out, int64_t qo_tok_stride, int64_t qo_head_stride,
+                         const void* q_proj, int64_t qi_tok_stride, int64_t qi_head_stride,
+                         uint32_t total_tokens, uint32_t num_q_heads, uint32_t head_dim,
+                         const uint32_t* input_row_offsets, uint32_t batch_size,
+                         const pkv_paged_cache* k_cache, uint32_t layer_idx,
+                         const float* freqs_cis, uint32_t max_seq_len,
+                         const uint32_t* position_ids, int interleaved,
+                         const void* k_norm_gamma, uint32_t k_norm_cols, float epsilon,
+                         void* stream) {
+  if (k_cache == nullptr) return PKV_ERR_NULL;
+  if (head_dim == 0 || head_dim % 2 != 0 || k_cache->head_dim != head_dim) return PKV_ERR_SHAPE;
+  if (k_cache->dtype != PKV_DTYPE_BF16 || k_cache->scale_mode != PKV_SCALE_NONE)
+    return PKV_ERR_DTYPE;
+  if (k_norm_gamma != nullptr && (k_norm_cols == 0 || k_norm_cols > head_dim))
+    return PKV_ERR_SHAPE;
+  if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
+  if (total_tokens > 0 && batch_size == 0) return PKV_ERR_SHAPE;
+  if (max_seq_len == 0) return PKV_ERR_SHAPE;
+  CacheView view{};
+  int st = check_cache(k_cache, layer_idx, batch_size, &view);
+  if (st != PKV_OK) return st;
+  if (total_tokens == 0) return PKV_OK;
+  if (input_row_offsets == nullptr || freqs_cis == nullptr) return PKV_ERR_NULL;
+  if (num_q_heads > 0 && (q_proj == nullptr || q_out == nullptr)) return PKV_ERR_NULL;
+  if (!aligned16(q_proj) || !aligned16(q_out) || !aligned16(freqs_cis) ||
+      !aligned16(k_norm_gamma) || !mult(qo_tok_stride, 8) || !mult(qo_head_stride, 8) ||
+      !mult(qi_tok_stride, 8) || !mult(qi_head_stride, 8))
+    return PKV_ERR_ALIGN;
+
+  pkv::QkArgs a{};
+  a.q_out = static_cast<uint16_t*>(q_out);
+  a.qo_tok = qo_tok_stride;
+  a.qo_head = qo_head_stride;
+  a.q_in = static_cast<const uint16_t*>(q_proj);
+  a.qi_tok = qi_tok_stride;
+  a.qi_head = qi_head_stride;
+  a.total_tokens = total_tokens;
+  a.num_q_heads = num_q_heads;
+  a.offsets = input_row_offsets;
+  a.batch = batch_size;
+  a.freqs = freqs_cis;
+  a.max_seq_len = max_seq_len;
+  a.position_ids = position_ids;
+  a.k_gamma = static_cast<const uint16_t*>(k_norm_gamma);
+  a.k_norm_cols = k_norm_gamma ? k_norm_cols : 0;
+  a.epsilon = epsilon;
+  a.cache = view;
+  return launch_status(
+      pkv::launch_qk_rope(a, (int)head_dim, interleaved != 0, static_cast<hipStream_t>(stream)));
+}
+
+int rms_norm_kv_cache_paged(const pkv_paged_cache* k_cache, uint32_t layer_idx,
+                            const void* gamma, uint32_t gamma_len, float epsilon,
+                            float weight_offset, uint32_t total_seq_len,
+                            const uint32_t* input_row_offsets, uint32_t batch_size,
+                            int per_head_norm, int multiply_before_cast, void* stream) {
+  if (k_cache == nullptr) return PKV_ERR_NULL;
+  if (k_cache->dtype != PKV_DTYPE_BF16 || k_cache->scale_mode != PKV_SCALE_NONE)
+    return PKV_ERR_DTYPE;
+  if (gamma_len == 0 || gamma_len > k_cache->head_dim) return PKV_ERR_SHAPE;
+  if (!per_head_norm) return PKV_ERR_UNSUPPORTED;
+  if (k_cache->head_dim != 64 && k_cache->head_dim != 128) return PKV_ERR_UNSUPPORTED;
+  if (total_seq_len > 0 && batch_size == 0) return PKV_ERR_SHAPE;
+  CacheView view{};
+  int st = check_cache(k_cache, layer_idx, batch_size, &view);
+  if (st != PKV_OK) return st;
+  if (total_seq_len == 0) return PKV_OK;
+  if (gamma == nullptr || input_row_offsets == nullptr) return PKV_ERR_NULL;
+  if (!aligned16(gamma)) return PKV_ERR_ALIGN;
+
+  pkv::KvNormArgs a{};
+  a.total_tokens = total_seq_len;
+  a.offsets = input_row_offsets;
+  a.batch = batch_size;
+  a.gamma = static_cast<const uint16_t*>(gamma);
+  a.gamma_len = gamma_len;
+  a.epsilon = epsilon;
+  a.weight_offset = weight_offset;
+  a.cache = view;
+  a.head_dim = k_cache->head_dim;
+  return launch_status(
+      pkv::launch_kv_norm(a, multiply_before_cast != 0, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,190 @@
+// pkv_device.h -- device-side building blocks shared by the gfx950 kernels:
+// bf16 / fp8 packing, wave64 cross-lane reductions, the XCD-aware block
+// order, and the ragged / paged address chain.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+constexpr int kWave = 64;
+constexpr uint32_t kNumXcd = 8;  // MI355X: 8 XCDs, workgroups dealt round-robin
+
+// ---- bf16 <-> fp32 ---------------------------------------------------------
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Unpack 8 bf16 (one 16-byte chunk) into fp32.
+__device__ __forceinline__ void unpack8(const uint4& v, float (&f)[8]) {
+  f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+  f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+  f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
+  f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+}
+
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> two bf16 in one dword, round-to-nearest-even
+// (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2_t f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+
+__device__ __forceinline__ uint4 pack8_bf16(const float (&f)[8]) {
+  return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                    pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
+}
+
+// ---- fp32 -> FP8 E4M3FN (OCP), saturating, round-to-nearest-even -----------
+// Values are clamped to +-448 (the largest finite E4M3FN value) and then
+// converted by v_cvt_pk_fp8_f32, which rounds to nearest even in the OCP
+// format on gfx950; -0 keeps its sign.
+
+__device__ __forceinline__ float sat448(float v) { return fminf(fmaxf(v, -448.0f), 448.0f); }
+
+__device__ __forceinline__ uint32_t pack4_fp8(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(a), sat448(b), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(c), sat448(d), w, true);
+  return (uint32_t)w;
+}
+
+__device__ __forceinline__ uint2 pack8_fp8(const float (&f)[8]) {
+  return make_uint2(pack4_fp8(f[0], f[1], f[2], f[3]), pack4_fp8(f[4], f[5], f[6], f[7]));
+}
+
+// ---- rotation of one pair -----------------------------------------------------
+// (x, y) -> (x c - y s, y c + x s).  Each output is a difference (or sum) of
+// two products evaluated with Kahan's FMA algorithm: the rounding error of
+// one product is recovered exactly and added back, so the fp32 result is
+// within 2 ulps of the exact value even when the two products nearly cancel
+// (a plain fma would lose all relative accuracy there).
+__device__ __forceinline__ void rotate_pair(float& x, float& y, float c, float s) {
+  const float ys = y * s;
+  const float ys_err = fmaf(-y, s, ys);     // ys - y*s, exact
+  const float xs = x * s;
+  const float xs_err = fmaf(x, s, -xs);     // x*s - xs, exact
+  const float nx = fmaf(x, c, -ys) + ys_err;
+  const float ny = fmaf(y, c, xs) + xs_err;
+  x = nx;
+  y = ny;
+}
+
+// ---- wave64 reductions (DPP inside 16-lane rows, readlane across rows) ------
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7-i inside each 8 lanes
+constexpr int kDppMirror = 0x140;      // lane i <-> 15-i inside each 16 lanes
+
+// Sum over aligned groups of N lanes (N in 1, 2, 4, 8, 16); every lane of a
+// group receives the group's sum.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (N >= 2) v += dpp<kDppXor1>(v);
+  if constexpr (N >= 4) v += dpp<kDppXor2>(v);
+  if constexpr (N >= 8) v += dpp<kDppHalfMirror>(v);
+  if constexpr (N >= 16) v += dpp<kDppMirror>(v);
+  return v;
+}
+
+template <int N>
+__device__ __forceinline__ float group_max(float v) {
+  if constexpr (N >= 2) v = fmaxf(v, dpp<kDppXor1>(v));
+  if constexpr (N >= 4) v = fmaxf(v, dpp<kDppXor2>(v));
+  if constexpr (N >= 8) v = fmaxf(v, dpp<kDppHalfMirror>(v));
+  if constexpr (N >= 16) v = fmaxf(v, dpp<kDppMirror>(v));
+  return v;
+}
+
+__device__ __forceinline__ float lane_value(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// Wave-uniform sum / max of one value per lane (all 64 lanes active).
+__device__ __forceinline__ float wave_sum(float v) {
+  v = group_sum<16>(v);
+  return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  v = group_max<16>(v);
+  return fmaxf(fmaxf(lane_value(v, 0), lane_value(v, 16)),
+               fmaxf(lane_value(v, 32), lane_value(v, 48)));
+}
+
+// ---- launch order ------------------------------------------------------------
+
+// Hardware block b runs on XCD b % 8.  Renumber blocks so that each XCD
+// receives one contiguous range of logical blocks: neighbouring tokens (whose
+// cache rows share 128-byte lines) then stay in one XCD's L2.
+__device__ __forceinline__ uint32_t xcd_block(uint32_t hw_block, uint32_t num_blocks) {
+  const uint32_t xcd = hw_block % kNumXcd, local = hw_block / kNumXcd;
+  const uint32_t per = num_blocks / kNumXcd, extra = num_blocks % kNumXcd;
+  return xcd * per + (xcd < extra ? xcd : extra) + local;
+}
+
+__device__ __forceinline__ uint32_t uniform(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
+}
+
+// ---- ragged batch and page table -------------------------------------------
+
+// Request owning token t: the number of offsets[1..B] that are <= t (offsets
+// non-decreasing).  All 64 lanes load in parallel; the result is wave-uniform.
+// Returns B when t lies past offsets[B].
+__device__ __forceinline__ uint32_t find_request(const uint32_t* __restrict__ offsets,
+                                                 uint32_t B, uint32_t t, int lane) {
+  uint32_t count = 0;
+  for (uint32_t base = 0; base < B; base += kWave) {
+    const uint32_t i = base + (uint32_t)lane + 1;
+    const uint32_t v = (i <= B) ? offsets[i] : 0xffffffffu;
+    count += (uint32_t)__popcll(__ballot(v <= t));
+  }
+  return uniform(count);
+}
+
+struct SlotAddr {
+  uint32_t request;  // b
+  uint32_t slot;     // cache slot (= position when no explicit ids)
+  uint32_t page;     // physical page
+  uint32_t offset;   // slot within the page
+  bool ok;
+};
+
+// Address chain of token t: request, slot, page, offset, with every
+// device-data bound checked before use.
+__device__ __forceinline__ SlotAddr locate(const uint32_t* __restrict__ offsets, uint32_t B,
+                                           const uint32_t* __restrict__ cache_lengths,
+                                           const uint32_t* __restrict__ page_table,
+                                           uint32_t pt_stride, uint32_t num_pages,
+                                           uint32_t page_size, uint32_t t, int lane) {
+  SlotAddr a{};
+  a.request = find_request(offsets, B, t, lane);
+  a.ok = a.request < B;
+  if (!a.ok) return a;
+  const uint32_t j = t - offsets[a.request];
+  a.slot = uniform(cache_lengths[a.request] + j);
+  const uint32_t col = a.slot / page_size;
+  a.ok = col < pt_stride;
+  if (!a.ok) return a;
+  a.page = uniform(page_table[(uint64_t)a.request * pt_stride + col]);
+  a.offset = a.slot - col * page_size;
+  a.ok = a.page < num_pages;
+  return a;
+}
+
+__device__ __forceinline__ void count_skip(uint32_t* error_count, int lane) {
+  if (error_count != nullptr && lane == 0) atomicAdd(error_count, 1u);
+}
+
+}  // namespace pkv

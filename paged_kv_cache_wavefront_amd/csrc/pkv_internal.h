@@ -1,0 +1,80 @@
+// pkv_internal.h -- kernel argument blocks and launchers (host side of the
+// kernels).  The C ABI in pkv_api.cpp validates arguments, fills these
+// blocks and calls the launchers; nothing here is exported.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+// Paged cache geometry of one layer, in elements of the cache type.
+struct CacheView {
+  void* layer_base;            // data + layer_idx * layer_stride (in bytes)
+  int64_t page_stride, slot_stride, head_stride;
+  uint32_t num_pages, page_size, num_heads;
+  const uint32_t* cache_lengths;
+  const uint32_t* page_table;
+  uint32_t pt_stride;
+  uint32_t* error_count;
+};
+
+enum class MlaOut : int { Fp8PerTensor = 0, Fp8PerToken = 1, Bf16 = 2 };
+
+struct MlaArgs {
+  uint16_t* q_out;
+  int64_t qo_tok, qo_head;
+  const uint16_t* q_in;
+  int64_t qi_tok, qi_head;
+  const uint16_t* latent;
+  int64_t kv_row;
+  const uint32_t* offsets;
+  uint32_t batch;
+  uint32_t total_tokens;
+  uint32_t num_heads;
+  uint32_t chunks;             // waves per token (head chunks)
+  const float* freqs;
+  uint32_t max_seq_len;
+  const uint16_t* gamma;
+  float epsilon;
+  const float* tensor_scale;   // per-tensor mode: device scalar
+  float* token_scales;         // per-token mode: this layer's [pages][page_size][heads]
+  CacheView cache;
+};
+
+// heads_per_wave is 16, 32, 64 or 128.
+hipError_t launch_mla(const MlaArgs& a, MlaOut mode, int heads_per_wave, hipStream_t stream);
+
+struct QkArgs {
+  uint16_t* q_out;
+  int64_t qo_tok, qo_head;
+  const uint16_t* q_in;
+  int64_t qi_tok, qi_head;
+  uint32_t total_tokens, num_q_heads;
+  const uint32_t* offsets;
+  uint32_t batch;
+  const float* freqs;
+  uint32_t max_seq_len;
+  const uint32_t* position_ids;  // may be null
+  const uint16_t* k_gamma;       // may be null
+  uint32_t k_norm_cols;
+  float epsilon;
+  CacheView cache;               // bf16 K cache
+};
+
+hipError_t launch_qk_rope(const QkArgs& a, int head_dim, bool interleaved, hipStream_t stream);
+
+struct KvNormArgs {
+  uint32_t total_tokens;
+  const uint32_t* offsets;
+  uint32_t batch;
+  const uint16_t* gamma;
+  uint32_t gamma_len;
+  float epsilon, weight_offset;
+  CacheView cache;               // bf16 K cache
+  uint32_t head_dim;
+};
+
+hipError_t launch_kv_norm(const KvNormArgs& a, bool multiply_before_cast, hipStream_t stream);
+
+}  // namespace pkv

@@ -1,0 +1,160 @@
+"""The C ABI on the CPU: the library loads, exports every function that
+include/pkv.h declares, and rejects bad arguments on the host with the
+documented status before touching the device (no kernel is launched here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+
+OK, NULL, SHAPE, DTYPE, ALIGN, UNSUP, RANGE, LAUNCH = range(8)
+FAKE = 0x10000          # 16-byte aligned stand-in for a device pointer (never dereferenced)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|const char\s*\*)\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def pkv():
+    import paged_kv_cache_wavefront_amd as pkv
+    return pkv
+
+
+def test_header_declares_entry_points():
+    assert declared_functions() == sorted(["mla_rope_rmsnorm_quant", "qk_rope_paged_ragged",
+                                           "rms_norm_kv_cache_paged", "pkv_status_string"])
+
+
+def test_library_exports_every_declared_function(pkv):
+    lib = pkv.library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", pkv.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert set(declared_functions()) <= exported
+
+
+def test_binding_names_match_header(pkv):
+    for name in declared_functions():
+        if name != "pkv_status_string":
+            assert callable(getattr(pkv, name)), name
+
+
+def test_status_strings(pkv):
+    assert pkv.status_string(OK) == "PKV_OK"
+    for code in range(1, 8):
+        assert pkv.status_string(code).startswith("PKV_ERR_")
+    assert "unknown" in pkv.status_string(99)
+
+
+def mla_cache(pkv, **kw):
+    base = dict(data=FAKE, dtype=pkv.PKV_DTYPE_FP8_E4M3FN, num_layers=2, num_pages=8,
+                page_size=16, num_heads=1, head_dim=576, layer_stride=8 * 16 * 576,
+                page_stride=16 * 576, slot_stride=576, head_stride=576, cache_lengths=FAKE,
+                page_table=FAKE, page_table_stride=4, scale_mode=pkv.PKV_SCALE_PER_TENSOR,
+                scales=FAKE, error_count=None)
+    base.update(kw)
+    return pkv.PagedCache(**base)
+
+
+def call_mla(pkv, cache, T=16, H=4, R=64, Dn=512, q=FAKE, qo=FAKE, lat=FAKE, qstride=4 * 64,
+             layer=1, batch=2, freqs=FAKE, gamma=FAKE, max_seq=64):
+    lib = pkv.library()
+    cp = None if cache is None else ctypes.byref(cache)
+    return lib.mla_rope_rmsnorm_quant(qo, qstride, R, q, qstride, R, lat, Dn + R, FAKE, batch,
+                                      T, H, R, Dn, freqs, max_seq, gamma, 1e-6, cp, layer, None)
+
+
+def test_mla_validation(pkv):
+    assert call_mla(pkv, None) == NULL
+    assert call_mla(pkv, mla_cache(pkv), R=63) == SHAPE
+    assert call_mla(pkv, mla_cache(pkv), R=32) == SHAPE                 # head_dim != Dn + R
+    assert call_mla(pkv, mla_cache(pkv, head_dim=544), R=32) == UNSUP
+    assert call_mla(pkv, mla_cache(pkv, num_heads=2)) == SHAPE
+    assert call_mla(pkv, mla_cache(pkv, scale_mode=pkv.PKV_SCALE_NONE)) == DTYPE
+    assert call_mla(pkv, mla_cache(pkv, dtype=pkv.PKV_DTYPE_BF16)) == DTYPE
+    assert call_mla(pkv, mla_cache(pkv, dtype=7)) == DTYPE
+    assert call_mla(pkv, mla_cache(pkv), layer=2) == RANGE
+    assert call_mla(pkv, mla_cache(pkv, page_size=0)) == SHAPE
+    assert call_mla(pkv, mla_cache(pkv), batch=0) == SHAPE
+    assert call_mla(pkv, mla_cache(pkv), max_seq=0) == SHAPE
+    assert call_mla(pkv, mla_cache(pkv, data=None)) == NULL
+    assert call_mla(pkv, mla_cache(pkv, page_table=None)) == NULL
+    assert call_mla(pkv, mla_cache(pkv, scales=None)) == NULL
+    assert call_mla(pkv, mla_cache(pkv), q=None) == NULL
+    assert call_mla(pkv, mla_cache(pkv), freqs=None) == NULL
+    assert call_mla(pkv, mla_cache(pkv), q=FAKE + 8) == ALIGN
+    assert call_mla(pkv, mla_cache(pkv), qstride=4 * 64 + 4) == ALIGN
+    assert call_mla(pkv, mla_cache(pkv), gamma=FAKE + 2) == ALIGN
+    assert call_mla(pkv, mla_cache(pkv, slot_stride=584)) == ALIGN
+    assert call_mla(pkv, mla_cache(pkv, data=FAKE + 8)) == ALIGN
+    # nothing to do: accepted without a launch
+    assert call_mla(pkv, mla_cache(pkv), T=0) == OK
+
+
+def kcache(pkv, **kw):
+    base = dict(data=FAKE, dtype=pkv.PKV_DTYPE_BF16, num_layers=2, num_pages=8, page_size=16,
+                num_heads=8, head_dim=128, layer_stride=8 * 16 * 8 * 128,
+                page_stride=16 * 8 * 128, slot_stride=8 * 128, head_stride=128,
+                cache_lengths=FAKE, page_table=FAKE, page_table_stride=4,
+                scale_mode=pkv.PKV_SCALE_NONE, scales=None, error_count=None)
+    base.update(kw)
+    return pkv.PagedCache(**base)
+
+
+def call_qk(pkv, cache, T=16, Hq=32, D=128, gamma=None, cols=0, layer=1, q=FAKE):
+    lib = pkv.library()
+    cp = None if cache is None else ctypes.byref(cache)
+    return lib.qk_rope_paged_ragged(FAKE, Hq * D, D, q, Hq * D, D, T, Hq, D, FAKE, 2, cp, layer,
+                                    FAKE, 4096, None, 1, gamma, cols, 1e-6, None)
+
+
+def test_qk_validation(pkv):
+    assert call_qk(pkv, None) == NULL
+    assert call_qk(pkv, kcache(pkv, dtype=pkv.PKV_DTYPE_FP8_E4M3FN)) == DTYPE
+    assert call_qk(pkv, kcache(pkv, scale_mode=pkv.PKV_SCALE_PER_TENSOR)) == DTYPE
+    assert call_qk(pkv, kcache(pkv, head_dim=96), D=96) == UNSUP
+    assert call_qk(pkv, kcache(pkv), D=64) == SHAPE                    # q vs cache head_dim
+    assert call_qk(pkv, kcache(pkv), gamma=FAKE, cols=129) == SHAPE
+    assert call_qk(pkv, kcache(pkv), gamma=FAKE, cols=0) == SHAPE
+    assert call_qk(pkv, kcache(pkv), layer=5) == RANGE
+    assert call_qk(pkv, kcache(pkv), q=FAKE + 4) == ALIGN
+    assert call_qk(pkv, kcache(pkv), gamma=FAKE + 2, cols=128) == ALIGN
+    assert call_qk(pkv, kcache(pkv), T=0) == OK
+
+
+def call_norm(pkv, cache, gamma_len=128, per_head=1, T=16, gamma=FAKE):
+    lib = pkv.library()
+    cp = None if cache is None else ctypes.byref(cache)
+    return lib.rms_norm_kv_cache_paged(cp, 1, gamma, gamma_len, 1e-6, 0.0, T, FAKE, 2,
+                                       per_head, 1, None)
+
+
+def test_kv_norm_validation(pkv):
+    assert call_norm(pkv, None) == NULL
+    assert call_norm(pkv, kcache(pkv, dtype=pkv.PKV_DTYPE_FP8_E4M3FN)) == DTYPE
+    assert call_norm(pkv, kcache(pkv), gamma_len=0) == SHAPE
+    assert call_norm(pkv, kcache(pkv), gamma_len=129) == SHAPE
+    assert call_norm(pkv, kcache(pkv), per_head=0) == UNSUP
+    assert call_norm(pkv, kcache(pkv, head_dim=256), gamma_len=128) == UNSUP
+    assert call_norm(pkv, kcache(pkv), gamma=None) == NULL
+    assert call_norm(pkv, kcache(pkv), gamma=FAKE + 2) == ALIGN
+    assert call_norm(pkv, kcache(pkv), T=0) == OK
+
+
+def test_product_path_does_not_reference_the_oracle():
+    """The HIP library and its binding never load or import the oracle."""
+    pkg = os.path.join(ROOT, "paged_kv_cache_wavefront_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text, os.path.join(dirpath, f)

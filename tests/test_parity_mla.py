@@ -1,0 +1,153 @@
+"""GPU parity of mla_rope_rmsnorm_quant against the CPU oracle, through the
+C ABI (binding -> libpkv.so), on the four MLA workloads at full size, small
+ragged cases, q layouts, degenerate inputs, the E4M3FN codec over every bf16
+value, and determinism."""
+import numpy as np
+import pytest
+import torch
+
+import gpu_helpers as gh
+import oracle_pins
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _run_and_compare(orc, case, q_layout="dense"):
+    _say(f"[mla] case={case.name} seed={case.seed} T={case.T} B={case.B} H={case.H} "
+         f"scale={case.scale_mode} layout={q_layout}")
+    dev = gh.MlaDevice(case, q_layout)
+    dev.run()
+    gpu = dev.results()
+    assert gpu[3] == 0, f"{gpu[3]} tokens skipped"
+    stats = gh.compare_mla(case, gpu, gh.oracle_mla(orc, case))
+    _say(f"[mla] {case.name}: {stats}")
+    return stats
+
+
+@pytest.mark.parametrize("name", ["mla_tiny", "mla_decode", "mla_prefill", "mla_mixed"])
+def test_named_workload(orc, name):
+    _run_and_compare(orc, workloads.NAMED[name]())
+
+
+@pytest.mark.parametrize("idx", range(5))
+def test_small_cases(orc, idx):
+    case = list(oracle_pins.small_mla_cases())[idx]
+    _run_and_compare(orc, case)
+
+
+@pytest.mark.parametrize("layout", ["strided", "inplace"])
+def test_q_layouts(orc, layout):
+    case = workloads.build_mla("mla_layout", 4001, [7, 0, 13, 1, 20], [3, 9, 0, 30, 2], H=24,
+                               page_size=8, max_seq_len=64, spare_pages=5,
+                               scale_mode="per_tensor", tensor_scale=0.05)
+    _run_and_compare(orc, case, layout)
+
+
+def test_heads_not_multiple_of_16(orc):
+    # 4100 tokens x 40 heads: wide-chunk kernel with masked head lanes
+    rng = workloads.make_rng(4002)
+    new = rng.integers(1, 300, size=30, endpoint=True)
+    new = np.append(new, 4100 - new.sum()) if new.sum() < 4100 else new
+    case = workloads.build_mla("mla_h40", 4002, new, rng.integers(0, 100, size=new.size), H=40,
+                               page_size=32, max_seq_len=8192, spare_pages=4,
+                               scale_mode="per_token", rng=rng)
+    _run_and_compare(orc, case)
+
+
+def test_empty_batch(orc):
+    import paged_kv_cache_wavefront_amd as pkv
+    case = workloads.build_mla("mla_empty", 4003, [0, 0], [5, 0], H=4, page_size=16,
+                               max_seq_len=64, spare_pages=2)
+    assert case.T == 0
+    dev = gh.MlaDevice(case)
+    dev.run()
+    q, cache, _, skipped = dev.results()
+    assert skipped == 0 and q.size == 0
+    assert np.array_equal(cache, case.cache)
+    _ = pkv
+
+
+def test_codec_every_bf16_value(orc):
+    """Every finite bf16 value goes through the rope tail at position 0
+    (cos 1, sin 0: the value is passed through exactly) and is quantised with
+    scale 1 and with scale 1/8: the fp8 codes must equal the oracle's (+-0
+    equal) -- this pins the hardware conversion (rounding, ties, subnormals,
+    saturation)."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    finite = bits[(bits & 0x7F80) != 0x7F80]
+    rows = -(-finite.size // 64)
+    tail = np.zeros(rows * 64, np.uint16)
+    tail[: finite.size] = finite
+    for scale in (1.0, 0.125):
+        case = workloads.build_mla("mla_codec", 4004, [1] * rows, [0] * rows, H=1,
+                                   page_size=4, max_seq_len=1, spare_pages=3,
+                                   scale_mode="per_tensor", tensor_scale=scale)
+        case.latent[:, case.Dn:] = tail.reshape(rows, 64)
+        dev = gh.MlaDevice(case)
+        dev.run()
+        q, cache, _, skipped = dev.results()
+        assert skipped == 0
+        _, cache_o, _ = gh.oracle_mla(orc, case)
+        rows_mask = gh.written_rows(case)
+        got = cache[rows_mask][:, 0, case.Dn:]
+        want = cache_o[rows_mask][:, 0, case.Dn:]
+        d = gh.fp8_ulp_diff(got, want)
+        _say(f"[codec] scale={scale}: {int((d != 0).sum())} of {d.size} tail codes differ")
+        assert int(d.max()) == 0
+        stats = gh.compare_mla(case, (q, cache, None, 0), gh.oracle_mla(orc, case))
+        _say(f"[codec] scale={scale}: {stats}")
+
+
+def test_skipped_tokens_are_counted(orc):
+    """Device data that breaks the rules (a page id beyond the pool, slots past
+    the page table / positions past the freqs table) makes the kernel skip those
+    tokens, leave their outputs alone and count them; the other tokens are
+    unaffected."""
+    def make():
+        return workloads.build_mla("mla_bad", 4005, [3, 4, 5], [0, 10, 2], H=8, page_size=8,
+                                   max_seq_len=16, spare_pages=2)
+    good, case = make(), make()
+    case.page_table[0, 0] = case.meta["num_pages"] + 3   # request 0: page beyond the pool
+    case.cache_lengths[1] = 14                            # request 1: slots 14..17; 16, 17 break
+    dev = gh.MlaDevice(case)
+    dev.q_out.zero_()
+    dev.run()
+    q, cache, _, skipped = dev.results()
+    assert skipped == 5, skipped
+    assert not q[[0, 1, 2, 5, 6]].any(), "skipped tokens wrote q"
+    q_o, cache_o, _ = gh.oracle_mla(orc, good)
+    assert gh.bf16_ulp_diff(q[7:], q_o[7:]).max() <= 1       # request 2 unaffected
+    owners = oracle_pins.slot_owners(good.row_offsets, good.cache_lengths, good.page_table, 8)
+    L = good.layer_idx
+    for (page, off), (t, slot) in owners.items():
+        if t >= 7:
+            assert gh.fp8_ulp_diff(cache[L, page, off], cache_o[L, page, off]).max() <= 1
+        elif t < 3:
+            assert np.array_equal(cache[L, page, off], good.cache[L, page, off])
+
+
+def test_deterministic(orc):
+    case = workloads.mla_prefill()
+    a = gh.MlaDevice(case)
+    a.run()
+    ra = a.results()
+    b = gh.MlaDevice(case)
+    b.run()
+    rb = b.results()
+    assert np.array_equal(ra[0], rb[0]) and np.array_equal(ra[1], rb[1])
+
+
+def test_stream_ordering(orc):
+    """A launch on a side stream is ordered on that stream only."""
+    case = workloads.mla_tiny()
+    dev = gh.MlaDevice(case)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        dev.run(stream=s)
+    s.synchronize()
+    gh.compare_mla(case, dev.results(), gh.oracle_mla(orc, case))

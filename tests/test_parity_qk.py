@@ -1,0 +1,182 @@
+"""GPU parity of qk_rope_paged_ragged and rms_norm_kv_cache_paged against the
+CPU oracle, through the C ABI: the Llama-shaped paged-ragged workload at full
+size (fused per-head K norm, and the two-call form), both rope styles, with
+and without position ids, head_dim 64 and 128, partial norm widths,
+weight_offset, both cast orders, and determinism."""
+import numpy as np
+import pytest
+
+import gpu_helpers as gh
+import oracle_pins
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def bf16_f64(u):
+    return oracle_pins.bf16_to_f64(u)
+
+
+def pair_magnitude(v: np.ndarray, interleaved: bool) -> np.ndarray:
+    """|(a, b)| of the rotation pair each element belongs to (last axis)."""
+    out = np.empty_like(v)
+    if interleaved:
+        m = np.hypot(v[..., 0::2], v[..., 1::2])
+        out[..., 0::2], out[..., 1::2] = m, m
+    else:
+        h = v.shape[-1] // 2
+        m = np.hypot(v[..., :h], v[..., h:])
+        out[..., :h], out[..., h:] = m, m
+    return out
+
+
+def check_k_rows(case, k_gpu, k_orc, what, slack_rel=0.0, max_ulp=1):
+    """Rows the new tokens own: within max_ulp (plus slack_rel x the pair
+    magnitude where the path carries an fp32 normalisation into the rotation);
+    every other element bit-exact against the starting pool."""
+    rows = gh.written_k_rows(case)
+    assert np.array_equal(k_gpu[~rows], case.k_cache[~rows]), f"{what}: untouched rows changed"
+    g, o = k_gpu[rows], k_orc[rows]
+    d = gh.bf16_ulp_diff(g, o)
+    frac = float((d != 0).sum() / max(d.size, 1))
+    if slack_rel > 0:
+        of = bf16_f64(o)
+        allowed = oracle_pins.ulp_bf16(of) * max_ulp + slack_rel * pair_magnitude(of, case.interleaved)
+        err = np.abs(bf16_f64(g) - of)
+        worst = float(np.max(err / allowed, initial=0))
+        assert worst <= 1.0, f"{what}: error {worst:.3f} x allowed"
+    else:
+        assert int(d.max(initial=0)) <= max_ulp, f"{what}: max ulp {int(d.max())}"
+    assert frac <= gh.BF16_MAX_DIFF_FRAC, f"{what}: diff frac {frac}"
+    return dict(max_ulp=int(d.max(initial=0)), diff_frac=frac, n=d.size)
+
+
+# fp32 normalisation in front of the rotation: relative error of the
+# normalised values <= ~1.1e-6 (8-term lane sums + 4-level DPP tree, sqrt,
+# divide, two products), amplified by cancellation in the rotation; 2^-18
+# (3.8e-6) of the pair magnitude covers it with margin.
+NORM_SLACK = 2.0 ** -18
+
+
+def oracle_qk(orc, case, with_norm):
+    q_out = np.zeros_like(case.q)
+    k = case.k_cache.copy()
+    orc.qk_rope_paged_ragged(q_out, case.q, case.row_offsets, case.cache_lengths,
+                             case.page_table, k, case.layer_idx, case.freqs, case.position_ids,
+                             case.interleaved, case.gamma if with_norm else None, case.epsilon)
+    return q_out, k
+
+
+def run_qk(orc, case, with_norm):
+    _say(f"[qk] case={case.name} T={case.T} interleaved={case.interleaved} "
+         f"pos_ids={case.position_ids is not None} norm={with_norm}")
+    dev = gh.QkDevice(case)
+    dev.rope(with_norm)
+    q = gh.host_bf16(dev.q_out)
+    k = gh.host_bf16(dev.k)
+    assert int(dev.error_count.item()) == 0
+    q_o, k_o = oracle_qk(orc, case, with_norm)
+    stats = {"q": gh.check_bf16(q, q_o, "q")}
+    stats["k"] = check_k_rows(case, k, k_o, "k", NORM_SLACK if with_norm else 0.0)
+    _say(f"[qk] {case.name}: {stats}")
+    return q, k
+
+
+@pytest.mark.parametrize("with_norm", [True, False])
+def test_llama_workload(orc, with_norm):
+    run_qk(orc, workloads.qk_generic(), with_norm)
+
+
+@pytest.mark.parametrize("idx", range(3))
+@pytest.mark.parametrize("with_norm", [True, False])
+def test_small_cases(orc, idx, with_norm):
+    case = list(oracle_pins.small_qk_cases())[idx]
+    if with_norm and case.gamma is None:
+        pytest.skip("case has no K norm")
+    run_qk(orc, case, with_norm)
+
+
+@pytest.mark.parametrize("D,interleaved,pos_ids",
+                         [(128, False, True), (128, False, False), (64, True, True),
+                          (64, False, False)])
+def test_styles_and_dims(orc, D, interleaved, pos_ids):
+    rng = workloads.make_rng(5000 + D)
+    new = rng.integers(1, 200, size=12, endpoint=True)
+    prior = rng.integers(0, 300, size=12, endpoint=True)
+    case = workloads.build_qk(f"qk_d{D}", 5000 + D, new, prior, Hq=12, Hkv=3, D=D,
+                              page_size=16, max_seq_len=2048, theta=10000.0,
+                              interleaved=interleaved, with_position_ids=pos_ids,
+                              norm_cols=D if D == 64 else 72, rng=rng)
+    run_qk(orc, case, True)
+    run_qk(orc, case, False)
+
+
+def oracle_kv_norm(orc, case, gamma, w, total, mbc):
+    k = case.k_cache.copy()
+    orc.rms_norm_kv_cache_paged(k, case.layer_idx, case.row_offsets, case.cache_lengths,
+                                case.page_table, gamma, case.epsilon, w, total, mbc)
+    return k
+
+
+@pytest.mark.parametrize("cols,w,mbc,short",
+                         [(128, 0.0, True, False), (128, 0.0, False, False),
+                          (40, 0.25, True, True), (100, 0.25, False, False)])
+def test_kv_norm(orc, cols, w, mbc, short):
+    case = workloads.qk_generic() if cols == 128 and not short else list(
+        oracle_pins.small_qk_cases())[0]
+    rng = workloads.make_rng(6000 + cols)
+    gamma = workloads.bf16_bits(rng.uniform(0.5, 1.5, cols).astype(np.float32))
+    total = case.T - 3 if short else case.T
+    _say(f"[kvnorm] case={case.name} cols={cols} w={w} mbc={mbc} total={total}/{case.T}")
+    dev = gh.QkDevice(case)
+    dev.kv_norm(gh.dev_bf16(gamma), w, total, mbc)
+    k = gh.host_bf16(dev.k)
+    assert int(dev.error_count.item()) == 0
+    k_o = oracle_kv_norm(orc, case, gamma, w, total, mbc)
+    # multiply_before_cast=False rounds twice; a 1-ulp difference in the inner
+    # rounding becomes < 2 ulps after the gamma product.
+    rows = gh.written_k_rows(case)
+    assert np.array_equal(k[~rows], case.k_cache[~rows])
+    d = gh.bf16_ulp_diff(k[rows], k_o[rows])
+    frac = float((d != 0).sum() / max(d.size, 1))
+    _say(f"[kvnorm] max_ulp={int(d.max())} diff_frac={frac}")
+    assert int(d.max()) <= (1 if mbc else 2)
+    assert frac <= gh.BF16_MAX_DIFF_FRAC
+    # columns past gamma_len and tokens past total_seq_len untouched
+    assert np.array_equal(k[rows][..., cols:], case.k_cache[rows][..., cols:])
+
+
+def test_two_call_form(orc):
+    """K norm by rms_norm_kv_cache_paged, then RoPE without the fused norm:
+    each call matches its oracle; the composition stays within one bf16 ulp
+    plus one intermediate-ulp of the pair magnitude."""
+    case = workloads.qk_generic()
+    dev = gh.QkDevice(case)
+    dev.kv_norm(dev.gamma, 0.0, case.T, True)
+    dev.rope(False)
+    k = gh.host_bf16(dev.k)
+    q = gh.host_bf16(dev.q_out)
+    k_mid = oracle_kv_norm(orc, case, case.gamma, 0.0, case.T, True)
+    mid_case = workloads.QkCase(**{**case.__dict__, "k_cache": k_mid})
+    q_o, k_o = oracle_qk(orc, mid_case, False)
+    gh.check_bf16(q, q_o, "q")
+    rows = gh.written_k_rows(case)
+    of = bf16_f64(k_o[rows])
+    err = np.abs(bf16_f64(k[rows]) - of)
+    allowed = oracle_pins.ulp_bf16(of) + 2.0 ** -7 * pair_magnitude(of, case.interleaved)
+    assert np.all(err <= allowed)
+    assert np.array_equal(k[~rows], case.k_cache[~rows])
+
+
+def test_deterministic(orc):
+    case = workloads.qk_generic()
+    outs = []
+    for _ in range(2):
+        dev = gh.QkDevice(case)
+        dev.rope(True)
+        outs.append((gh.host_bf16(dev.q_out), gh.host_bf16(dev.k)))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
