@@ -81,24 +81,34 @@ def kv_norm_bytes(case, cols: int) -> int:
 
 # -- timing ------------------------------------------------------------------------------
 
-def time_launches(fn, steps: int, warmup: int):
-    """Warm up, then time exactly `steps` launches bracketed by device syncs.
-    Returns (wall seconds, per-launch durations in seconds from HIP events
-    recorded on the launch stream)."""
+def time_launches(fn, steps: int, warmup: int, spread_samples: int = 20):
+    """Warm up, then time exactly `steps` back-to-back launches bracketed by
+    device syncs, with one pair of HIP events (on the launch stream: torch's
+    current stream) around the timed region.  Returns (wall seconds, average
+    seconds per launch from the events, per-launch durations from a separate,
+    untimed pass with an event pair around each launch)."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    events = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    events[0].record()
-    for i in range(steps):
+    e0.record()
+    for _ in range(steps):
         fn()
-        events[i + 1].record()
+    e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    durs = np.array([events[i].elapsed_time(events[i + 1]) for i in range(steps)]) * 1e-3
-    return wall, durs
+    avg = e0.elapsed_time(e1) * 1e-3 / steps
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(spread_samples)]
+    for a, b in pairs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    durs = np.array([a.elapsed_time(b) for a, b in pairs]) * 1e-3
+    return wall, avg, durs
 
 
 def profiled_traffic(name: str):
@@ -127,10 +137,9 @@ def mla_runner(case):
 
 def measure_mla(case, steps, warmup):
     dev, fn = mla_runner(case)
-    wall, durs = time_launches(fn, steps, warmup)
-    nbytes = mla_bytes(case)
-    return dict(T=case.T, bytes=nbytes, wall=wall, durs=durs,
-                avg=float(durs.mean()), med=float(np.median(durs)))
+    wall, avg, durs = time_launches(fn, steps, warmup)
+    return dict(T=case.T, bytes=mla_bytes(case), wall=wall, durs=durs, avg=avg,
+                med=float(np.median(durs)))
 
 
 def summarize(name, r, steps):
@@ -156,17 +165,18 @@ def measure_siblings(steps, warmup):
     case = workloads.qk_generic()
     dev = gh.QkDevice(case)
     log("[bench] sibling qk_rope_paged_ragged")
-    wall, durs = time_launches(lambda: dev.rope(True), steps, warmup)
+    wall, avg, durs = time_launches(lambda: dev.rope(True), steps, warmup)
     out["qk_rope_paged_ragged"] = summarize(
         "qk_generic (interleaved, position ids, fused per-head K norm)",
-        dict(T=case.T, bytes=qk_bytes(case, True), wall=wall, durs=durs,
-             avg=float(durs.mean()), med=float(np.median(durs))), steps)
+        dict(T=case.T, bytes=qk_bytes(case, True), wall=wall, durs=durs, avg=avg,
+             med=float(np.median(durs))), steps)
     log("[bench] sibling rms_norm_kv_cache_paged")
-    wall, durs = time_launches(lambda: dev.kv_norm(dev.gamma, 0.0, case.T, True), steps, warmup)
+    wall, avg, durs = time_launches(lambda: dev.kv_norm(dev.gamma, 0.0, case.T, True), steps,
+                                    warmup)
     out["rms_norm_kv_cache_paged"] = summarize(
         "qk_generic K cache (8 heads x 128, gamma 128)",
-        dict(T=case.T, bytes=kv_norm_bytes(case, 128), wall=wall, durs=durs,
-             avg=float(durs.mean()), med=float(np.median(durs))), steps)
+        dict(T=case.T, bytes=kv_norm_bytes(case, 128), wall=wall, durs=durs, avg=avg,
+             med=float(np.median(durs))), steps)
     return out
 
 
@@ -202,11 +212,11 @@ def calibrate_copy(steps, warmup, mib=1024):
     n = mib * (1 << 20) // 4
     src = torch.ones(n, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
-    wall, durs = time_launches(lambda: torch.neg(src, out=dst), steps, warmup)
+    wall, avg, durs = time_launches(lambda: torch.neg(src, out=dst), steps, warmup)
     nbytes = 2 * n * 4
     print(json.dumps({"calibrate_copy_bytes_read": n * 4, "bytes_written": n * 4,
-                      "kernel_us_avg": round(float(durs.mean()) * 1e6, 2),
-                      "GBps": round(nbytes / float(durs.mean()) / 1e9, 1)}))
+                      "kernel_us_avg": round(avg * 1e6, 2),
+                      "GBps": round(nbytes / avg / 1e9, 1)}))
 
 
 def main():

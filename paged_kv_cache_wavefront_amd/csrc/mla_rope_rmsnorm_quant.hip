@@ -8,23 +8,28 @@
 // cache of layer layer_idx at the token's slot.
 //
 // Design (bandwidth bound; no dense contraction, so no MFMA):
-// * One wave64 per (token, chunk of heads).  Lane l handles head
-//   16*g + l/4 of each 16-head group g, and within it the 8 rotate-half pairs
-//   (8m + k, 32 + 8m + k), m = l % 4: two 16-byte loads per head per lane,
-//   one per half, so no cross-lane exchange is needed for the pairing and each
-//   wave instruction reads 16 heads x 64 contiguous bytes.
-// * All q loads of the wave are issued before the address chain (offsets ->
-//   cache length -> page table -> freqs row), so the chain's latency hides
+// * One wave64 per (token, chunk of heads).  Each wave instruction moves 8
+//   whole heads = 1 KiB of contiguous q: lane l serves head l/8 of the
+//   instruction and one 16-byte chunk (8 values) of it.  Within a head's 8
+//   lanes, lane k < 4 holds values 8k..8k+7 (first half) and lane k >= 4 holds
+//   values 32 + 8(7-k) .. (second half, mirrored), so the rotate-half partner
+//   of lane k is lane 7-k and arrives with one DPP row_half_mirror per dword:
+//   no LDS round trip, and every load and store covers full 128-byte lines.
+// * q and latent are read with non-temporal loads (streamed once); all q
+//   loads of the wave are issued before the address chain
+//   ({offsets, cache lengths} -> page table -> freqs row), which then hides
 //   behind the bulk traffic.
 // * The 16 cos/sin floats a lane needs sit contiguously in the freqs row and
-//   are identical for the 16 heads the wave touches: one 64-byte vector load
-//   per lane per token, kept in registers (no LDS round trip).
+//   are the same for every head: one 64-byte load per lane per token, kept in
+//   registers.
 // * The head-chunk-0 wave also owns the latent row: lane l holds non-rope
-//   values 8l..8l+7 (one 16-byte load), lanes 0..3 hold the rope tail with
-//   the same pairing and cos/sin as q.  The sum of squares (and the per-token
-//   amax) reduce across the wave with DPP inside rows and readlane across
-//   rows.  The row is converted to fp8 in registers (clamp to +-448, then
-//   hardware round-to-nearest-even) and written with 8-byte stores.
+//   values 8l..8l+7; lanes 0..7 hold the 64-value rope tail with the q
+//   mapping.  The sum of squares (and the per-token amax) reduce across the
+//   wave with DPP inside rows and readlane across rows.  The non-rope value is
+//   formed as (x * gamma) * (r / scale): x * gamma is exact in fp32 (two 8-bit
+//   significands).  The row is converted to fp8 in registers (clamp to +-448,
+//   then hardware round-to-nearest-even) and written with 8-byte
+//   non-temporal stores.
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -33,18 +38,38 @@ namespace {
 
 constexpr int kRope = 64;               // rope_dim
 constexpr int kNope = 512;              // kv_norm_dim = 64 lanes x 8
-constexpr int kHalf = kRope / 2;
 constexpr int kWavesPerBlock = 4;
 
-// Rotate the 8 rotate-half pairs (lo[k], hi[k]) of one lane.  cs holds
-// cos, sin of pair k at 2k, 2k+1.
-__device__ __forceinline__ void rotate_pairs(float (&lo)[8], float (&hi)[8],
-                                             const float (&cs)[16]) {
-#pragma unroll
-  for (int k = 0; k < 8; ++k) rotate_pair(lo[k], hi[k], cs[2 * k], cs[2 * k + 1]);
+// Lane roles inside an 8-lane head group (rotate-half, rope_dim 64).
+struct HeadLane {
+  int k;          // lane within the group
+  bool first;     // holds first-half values
+  int pair_block; // holds pairs 8*pair_block .. 8*pair_block+7
+  int chunk;      // 16-byte chunk of the 128-byte head row it loads/stores
+};
+
+__device__ __forceinline__ HeadLane head_lane(int lane) {
+  HeadLane h;
+  h.k = lane & 7;
+  h.first = h.k < 4;
+  h.pair_block = h.first ? h.k : 7 - h.k;
+  h.chunk = h.first ? h.k : 11 - h.k;
+  return h;
 }
 
-template <int G, MlaOut MODE>
+// Rotate the 8 values this lane owns, given its partner's 8 values: first
+// half  out = own*cos - partner*sin;  second half  out = own*cos + partner*sin.
+__device__ __forceinline__ void rotate_own(float (&own)[8], const float (&par)[8],
+                                           const float (&cs)[16], uint32_t neg) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float p = __uint_as_float(__float_as_uint(par[j]) ^ neg);
+    own[j] = sum_of_products(own[j], cs[2 * j], p, cs[2 * j + 1]);
+  }
+}
+
+// NI = 8-head instructions per wave (heads per wave / 8).
+template <int NI, MlaOut MODE>
 __global__ __launch_bounds__(256) void mla_kernel(const MlaArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   const uint32_t wave =
@@ -52,31 +77,26 @@ __global__ __launch_bounds__(256) void mla_kernel(const MlaArgs a) {
   const uint32_t t = uniform(wave / a.chunks);
   const uint32_t chunk = uniform(wave - t * a.chunks);
   if (t >= a.total_tokens) return;
+  const HeadLane hl = head_lane(lane);
+  const uint32_t neg = hl.first ? 0x80000000u : 0u;
 
   // ---- issue the bulk loads (addresses depend on t only) --------------------
-  const int m = lane & 3;
-  const uint32_t h_lane = chunk * (16 * G) + (uint32_t)(lane >> 2);
-  const uint16_t* qsrc = a.q_in + (int64_t)t * a.qi_tok + 8 * m;
-  uint4 qlo[G], qhi[G];
+  const uint32_t h_lane = chunk * (8 * NI) + (uint32_t)(lane >> 3);
+  const uint16_t* qsrc = a.q_in + (int64_t)t * a.qi_tok + 8 * hl.chunk;
+  uint4 q[NI];
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const uint32_t h = h_lane + 16 * g;
-    if (h < a.num_heads) {
-      const uint16_t* p = qsrc + (int64_t)h * a.qi_head;
-      qlo[g] = *reinterpret_cast<const uint4*>(p);
-      qhi[g] = *reinterpret_cast<const uint4*>(p + kHalf);
-    }
+  for (int i = 0; i < NI; ++i) {
+    const uint32_t h = h_lane + 8 * i;
+    q[i] = make_uint4(0, 0, 0, 0);
+    if (h < a.num_heads) q[i] = load16_stream(qsrc + (int64_t)h * a.qi_head);
   }
   const bool latent_wave = chunk == 0;
-  uint4 xn = {}, gm = {}, tlo = {}, thi = {};
+  uint4 xn = {}, gm = {}, tail = {};
   if (latent_wave) {
     const uint16_t* row = a.latent + (int64_t)t * a.kv_row;
-    xn = *reinterpret_cast<const uint4*>(row + 8 * lane);
-    gm = *reinterpret_cast<const uint4*>(a.gamma + 8 * lane);
-    if (lane < 4) {
-      tlo = *reinterpret_cast<const uint4*>(row + kNope + 8 * lane);
-      thi = *reinterpret_cast<const uint4*>(row + kNope + kHalf + 8 * lane);
-    }
+    xn = load16_stream(row + 8 * lane);
+    gm = load16(a.gamma + 8 * lane);
+    if (lane < 8) tail = load16_stream(row + kNope + 8 * hl.chunk);
   }
 
   // ---- address chain: request, slot (= position), page, offset -------------
@@ -89,8 +109,8 @@ __global__ __launch_bounds__(256) void mla_kernel(const MlaArgs a) {
   }
   float cs[16];
   {
-    const float4* fr =
-        reinterpret_cast<const float4*>(a.freqs + (int64_t)s.slot * kRope + 16 * m);
+    const float4* fr = reinterpret_cast<const float4*>(a.freqs + (int64_t)s.slot * kRope +
+                                                       16 * hl.pair_block);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float4 v = fr[i];
@@ -98,94 +118,91 @@ __global__ __launch_bounds__(256) void mla_kernel(const MlaArgs a) {
     }
   }
 
-  // ---- q: rotate and store ---------------------------------------------------
-  uint16_t* qdst = a.q_out + (int64_t)t * a.qo_tok + 8 * m;
+  // ---- q: exchange with the mirrored lane, rotate, store --------------------
+  uint16_t* qdst = a.q_out + (int64_t)t * a.qo_tok + 8 * hl.chunk;
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const uint32_t h = h_lane + 16 * g;
-    if (h < a.num_heads) {
-      float lo[8], hi[8];
-      unpack8(qlo[g], lo);
-      unpack8(qhi[g], hi);
-      rotate_pairs(lo, hi, cs);
-      uint16_t* p = qdst + (int64_t)h * a.qo_head;
-      *reinterpret_cast<uint4*>(p) = pack8_bf16(lo);
-      *reinterpret_cast<uint4*>(p + kHalf) = pack8_bf16(hi);
-    }
+  for (int i = 0; i < NI; ++i) {
+    const uint4 partner = mirror16<8>(q[i]);
+    float own[8], par[8];
+    unpack8(q[i], own);
+    unpack8(partner, par);
+    rotate_own(own, par, cs, neg);
+    const uint32_t h = h_lane + 8 * i;
+    if (h < a.num_heads) store16(qdst + (int64_t)h * a.qo_head, pack8_bf16(own));
   }
   if (!latent_wave) return;
 
   // ---- latent row: RMSNorm (non-rope part), RoPE (tail) ---------------------
-  float y[8], g8[8];
-  unpack8(xn, y);
+  float xg[8], g8[8];
+  unpack8(xn, xg);
   unpack8(gm, g8);
   float ss = 0.0f;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) ss = fmaf(y[k], y[k], ss);
+  for (int k = 0; k < 8; ++k) {
+    ss = fmaf(xg[k], xg[k], ss);
+    xg[k] *= g8[k];  // exact: bf16 x bf16
+  }
   ss = wave_sum(ss);
   const float r = 1.0f / sqrtf(ss * (1.0f / kNope) + a.epsilon);
-#pragma unroll
-  for (int k = 0; k < 8; ++k) y[k] = y[k] * r * g8[k];
-  float tl[8], th[8];
-  unpack8(tlo, tl);
-  unpack8(thi, th);
-  rotate_pairs(tl, th, cs);  // meaningful on lanes 0..3 only
+  float tv[8], tp[8];
+  unpack8(tail, tv);
+  unpack8(mirror16<8>(tail), tp);
+  rotate_own(tv, tp, cs, neg);  // meaningful on lanes 0..7 only
 
   const int64_t row_elems = (int64_t)s.page * cv.page_stride + (int64_t)s.offset * cv.slot_stride;
   if constexpr (MODE == MlaOut::Bf16) {
     uint16_t* row = static_cast<uint16_t*>(cv.layer_base) + row_elems;
-    *reinterpret_cast<uint4*>(row + 8 * lane) = pack8_bf16(y);
-    if (lane < 4) {
-      *reinterpret_cast<uint4*>(row + kNope + 8 * lane) = pack8_bf16(tl);
-      *reinterpret_cast<uint4*>(row + kNope + kHalf + 8 * lane) = pack8_bf16(th);
-    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) xg[k] *= r;
+    store16(row + 8 * lane, pack8_bf16(xg));
+    if (lane < 8) store16(row + kNope + 8 * hl.chunk, pack8_bf16(tv));
     return;
   } else {
     float inv;
     if constexpr (MODE == MlaOut::Fp8PerTensor) {
       inv = 1.0f / *a.tensor_scale;
     } else {
+      // max |y| over the row: the non-rope part scales monotonically by r
       float am = 0.0f;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) am = fmaxf(am, fabsf(y[k]));
-      if (lane < 4) {
+      for (int k = 0; k < 8; ++k) am = fmaxf(am, fabsf(xg[k]));
+      am = wave_max(am) * r;
+      float at = 0.0f;
+      if (lane < 8) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) am = fmaxf(am, fmaxf(fabsf(tl[k]), fabsf(th[k])));
+        for (int k = 0; k < 8; ++k) at = fmaxf(at, fabsf(tv[k]));
       }
-      am = wave_max(am);
+      am = fmaxf(am, wave_max(at));
       const float st = am / 448.0f;
       inv = st > 0.0f ? 1.0f / st : 0.0f;
       if (lane == 0)
         a.token_scales[((int64_t)s.page * cv.page_size + s.offset) * cv.num_heads] = st;
     }
+    const float rs = r * inv;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      y[k] *= inv;
-      tl[k] *= inv;
-      th[k] *= inv;
+      xg[k] *= rs;
+      tv[k] *= inv;
     }
     uint8_t* row = static_cast<uint8_t*>(cv.layer_base) + row_elems;
-    *reinterpret_cast<uint2*>(row + 8 * lane) = pack8_fp8(y);
-    if (lane < 4) {
-      *reinterpret_cast<uint2*>(row + kNope + 8 * lane) = pack8_fp8(tl);
-      *reinterpret_cast<uint2*>(row + kNope + kHalf + 8 * lane) = pack8_fp8(th);
-    }
+    store8_stream(row + 8 * lane, pack8_fp8(xg));
+    if (lane < 8) store8_stream(row + kNope + 8 * hl.chunk, pack8_fp8(tv));
   }
 }
 
-template <int G>
+template <int NI>
 hipError_t launch_g(const MlaArgs& a, MlaOut mode, uint32_t blocks, hipStream_t stream) {
   switch (mode) {
     case MlaOut::Fp8PerTensor:
-      hipLaunchKernelGGL((mla_kernel<G, MlaOut::Fp8PerTensor>), dim3(blocks), dim3(256), 0,
+      hipLaunchKernelGGL((mla_kernel<NI, MlaOut::Fp8PerTensor>), dim3(blocks), dim3(256), 0,
                          stream, a);
       break;
     case MlaOut::Fp8PerToken:
-      hipLaunchKernelGGL((mla_kernel<G, MlaOut::Fp8PerToken>), dim3(blocks), dim3(256), 0,
+      hipLaunchKernelGGL((mla_kernel<NI, MlaOut::Fp8PerToken>), dim3(blocks), dim3(256), 0,
                          stream, a);
       break;
     case MlaOut::Bf16:
-      hipLaunchKernelGGL((mla_kernel<G, MlaOut::Bf16>), dim3(blocks), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((mla_kernel<NI, MlaOut::Bf16>), dim3(blocks), dim3(256), 0, stream, a);
       break;
   }
   return hipGetLastError();
@@ -199,10 +216,10 @@ hipError_t launch_mla(const MlaArgs& a, MlaOut mode, int heads_per_wave, hipStre
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffull) return hipErrorInvalidValue;
   switch (heads_per_wave) {
-    case 16: return launch_g<1>(a, mode, (uint32_t)blocks, stream);
-    case 32: return launch_g<2>(a, mode, (uint32_t)blocks, stream);
-    case 64: return launch_g<4>(a, mode, (uint32_t)blocks, stream);
-    case 128: return launch_g<8>(a, mode, (uint32_t)blocks, stream);
+    case 16: return launch_g<2>(a, mode, (uint32_t)blocks, stream);
+    case 32: return launch_g<4>(a, mode, (uint32_t)blocks, stream);
+    case 64: return launch_g<8>(a, mode, (uint32_t)blocks, stream);
+    case 128: return launch_g<16>(a, mode, (uint32_t)blocks, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -56,21 +56,38 @@ __device__ __forceinline__ uint2 pack8_fp8(const float (&f)[8]) {
   return make_uint2(pack4_fp8(f[0], f[1], f[2], f[3]), pack4_fp8(f[4], f[5], f[6], f[7]));
 }
 
-// ---- rotation of one pair -----------------------------------------------------
-// (x, y) -> (x c - y s, y c + x s).  Each output is a difference (or sum) of
-// two products evaluated with Kahan's FMA algorithm: the rounding error of
-// one product is recovered exactly and added back, so the fp32 result is
-// within 2 ulps of the exact value even when the two products nearly cancel
-// (a plain fma would lose all relative accuracy there).
-__device__ __forceinline__ void rotate_pair(float& x, float& y, float c, float s) {
-  const float ys = y * s;
-  const float ys_err = fmaf(-y, s, ys);     // ys - y*s, exact
-  const float xs = x * s;
-  const float xs_err = fmaf(x, s, -xs);     // x*s - xs, exact
-  const float nx = fmaf(x, c, -ys) + ys_err;
-  const float ny = fmaf(y, c, xs) + xs_err;
-  x = nx;
-  y = ny;
+// ---- rotation arithmetic --------------------------------------------------------
+// A rotated value is x c - y s or y c + x s: a sum of two products.  It is
+// evaluated with Kahan's FMA algorithm -- the rounding error of one product is
+// recovered exactly and added back -- so the fp32 result is within 2 ulps of
+// the exact value even when the two products nearly cancel (a plain fma would
+// lose all relative accuracy there).
+// a*b + c*d with the rounding error of c*d recovered exactly.
+__device__ __forceinline__ float sum_of_products(float a, float b, float c, float d) {
+  const float cd = c * d;
+  const float cd_err = fmaf(c, d, -cd);     // c*d - cd, exact
+  return fmaf(a, b, cd) + cd_err;
+}
+
+// ---- memory access helpers ---------------------------------------------------
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+// 16-byte load marked non-temporal (streamed once; keeps it from displacing
+// reusable lines in the caches).
+__device__ __forceinline__ uint4 load16_stream(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void store16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+
+// 8-byte non-temporal store (cache rows: written once, never re-read here).
+__device__ __forceinline__ void store8_stream(void* p, uint2 v) {
+  const u32x2_t w = {v.x, v.y};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x2_t*>(p));
 }
 
 // ---- wave64 reductions (DPP inside 16-lane rows, readlane across rows) ------
@@ -88,6 +105,20 @@ constexpr int kDppMirror = 0x140;      // lane i <-> 15-i inside each 16 lanes
 
 // Sum over aligned groups of N lanes (N in 1, 2, 4, 8, 16); every lane of a
 // group receives the group's sum.
+// Exchange a 16-byte chunk with the mirrored lane of its 8-lane (MIRROR=8) or
+// 16-lane (MIRROR=16) group: lane k receives lane (N-1-k)'s data.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+}
+
+template <int MIRROR>
+__device__ __forceinline__ uint4 mirror16(const uint4& v) {
+  constexpr int ctrl = MIRROR == 8 ? 0x141 : 0x140;  // row_half_mirror / row_mirror
+  return make_uint4(dpp_u32<ctrl>(v.x), dpp_u32<ctrl>(v.y), dpp_u32<ctrl>(v.z),
+                    dpp_u32<ctrl>(v.w));
+}
+
 template <int N>
 __device__ __forceinline__ float group_sum(float v) {
   if constexpr (N >= 2) v += dpp<kDppXor1>(v);
@@ -161,19 +192,54 @@ struct SlotAddr {
   bool ok;
 };
 
+__device__ __forceinline__ uint32_t lane_u32(uint32_t v, uint32_t lane) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, (int)lane);
+}
+
 // Address chain of token t: request, slot, page, offset, with every
-// device-data bound checked before use.
+// device-data bound checked before use.  For batches of up to 256 requests the
+// request's start offset and prior length are fetched in the same round of
+// loads as the search (lane i holds entries i, i+64, ...), so the chain is two
+// dependent rounds: {offsets, cache_lengths} -> {page table}.
 __device__ __forceinline__ SlotAddr locate(const uint32_t* __restrict__ offsets, uint32_t B,
                                            const uint32_t* __restrict__ cache_lengths,
                                            const uint32_t* __restrict__ page_table,
                                            uint32_t pt_stride, uint32_t num_pages,
                                            uint32_t page_size, uint32_t t, int lane) {
   SlotAddr a{};
-  a.request = find_request(offsets, B, t, lane);
-  a.ok = a.request < B;
-  if (!a.ok) return a;
-  const uint32_t j = t - offsets[a.request];
-  a.slot = uniform(cache_lengths[a.request] + j);
+  constexpr int kChunks = 4;
+  if (B <= kChunks * kWave) {
+    uint32_t nxt[kChunks], beg[kChunks], len[kChunks];
+#pragma unroll
+    for (int k = 0; k < kChunks; ++k) {
+      const uint32_t i = k * kWave + (uint32_t)lane;
+      const bool in = i < B;
+      nxt[k] = in ? offsets[i + 1] : 0xffffffffu;
+      beg[k] = in ? offsets[i] : 0u;
+      len[k] = in ? cache_lengths[i] : 0u;
+    }
+    uint32_t count = 0;
+#pragma unroll
+    for (int k = 0; k < kChunks; ++k) count += (uint32_t)__popcll(__ballot(nxt[k] <= t));
+    a.request = uniform(count);
+    a.ok = a.request < B;
+    if (!a.ok) return a;
+    const uint32_t kb = a.request / kWave, lb = a.request % kWave;
+    uint32_t start = 0, prior = 0;
+#pragma unroll
+    for (int k = 0; k < kChunks; ++k) {
+      if (kb == (uint32_t)k) {
+        start = lane_u32(beg[k], lb);
+        prior = lane_u32(len[k], lb);
+      }
+    }
+    a.slot = prior + (t - start);
+  } else {
+    a.request = find_request(offsets, B, t, lane);
+    a.ok = a.request < B;
+    if (!a.ok) return a;
+    a.slot = uniform(cache_lengths[a.request] + (t - offsets[a.request]));
+  }
   const uint32_t col = a.slot / page_size;
   a.ok = col < pt_stride;
   if (!a.ok) return a;
