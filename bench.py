@@ -33,8 +33,16 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E peak, GB/s
 METRIC = "fused MLA RoPE+RMSNorm+FP8 cache-write: tokens/s and effective HBM GB/s (% of peak)"
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_wavefront_amd", "csrc",
-                          "mla_rope_rmsnorm_quant.hip")
+CSRC = os.path.join(ROOT, "paged_kv_cache_wavefront_amd", "csrc")
+# sources that decide what the MLA launch does (kernel, helpers, launch policy)
+KERNEL_SOURCES = ("mla_rope_rmsnorm_quant.hip", "pkv_device.h", "pkv_internal.h", "pkv_api.cpp")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        h.update(open(os.path.join(CSRC, name), "rb").read())
+    return h.hexdigest()
 
 
 def log(*a):
@@ -111,6 +119,32 @@ def time_launches(fn, steps: int, warmup: int, spread_samples: int = 20):
     return wall, avg, durs
 
 
+def time_graph(fn, steps: int, warmup: int):
+    """Seconds per launch when `steps` launches are captured in one HIP graph
+    (torch.cuda.CUDAGraph) and replayed: the kernels back to back with no
+    host launch overhead between them."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(max(1, warmup)):
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(steps):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / steps
+
+
 def profiled_traffic(name: str):
     """HBM bytes per launch from the committed rocprofv3 PMC summary, if it was
     taken on the current kernel source; otherwise None."""
@@ -122,61 +156,72 @@ def profiled_traffic(name: str):
     m_h = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
     if not (m_b and m_h):
         return None
-    cur = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
-    return float(m_b.group(1)) if m_h.group(1) == cur else None
+    return float(m_b.group(1)) if m_h.group(1) == kernel_source_hash() else None
 
 
 # -- workloads -------------------------------------------------------------------------
 
-def mla_runner(case):
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    import gpu_helpers as gh
-    dev = gh.MlaDevice(case)
-    return dev, dev.run
-
-
-def measure_mla(case, steps, warmup):
-    dev, fn = mla_runner(case)
+def measure(fn, tokens, nbytes, steps, warmup, graph=True):
     wall, avg, durs = time_launches(fn, steps, warmup)
-    return dict(T=case.T, bytes=mla_bytes(case), wall=wall, durs=durs, avg=avg,
-                med=float(np.median(durs)))
+    r = dict(T=tokens, bytes=nbytes, wall=wall, durs=durs, avg=avg, med=float(np.median(durs)))
+    r["graph_avg"] = time_graph(fn, steps, warmup) if graph else None
+    return r
 
 
-def summarize(name, r, steps):
-    gbps = r["bytes"] / r["avg"] / 1e9
-    return {"workload": name, "tokens": r["T"], "bytes_per_launch": r["bytes"],
-            "kernel_us_avg": round(r["avg"] * 1e6, 2), "kernel_us_p50": round(r["med"] * 1e6, 2),
-            "kernel_us_p10": round(float(np.percentile(r["durs"], 10)) * 1e6, 2),
-            "kernel_us_p90": round(float(np.percentile(r["durs"], 90)) * 1e6, 2),
-            "tokens_per_s": round(r["T"] * steps / r["wall"], 1),
-            "effective_GBps": round(gbps, 1), "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2)}
+def summarize(name, r, steps, use_graph=False):
+    """use_graph: quote throughput from the graph-replay time (short kernels,
+    where eager timing would measure the host's launch overhead)."""
+    t = r["graph_avg"] if use_graph and r["graph_avg"] else r["avg"]
+    gbps = r["bytes"] / t / 1e9
+    out = {"workload": name, "tokens": r["T"], "bytes_per_launch": r["bytes"],
+           "timed_as": "hip graph replay" if use_graph else "eager launches",
+           "kernel_us_avg": round(t * 1e6, 2),
+           "eager_us_avg": round(r["avg"] * 1e6, 2),
+           "eager_us_p10_p50_p90": [round(float(np.percentile(r["durs"], q)) * 1e6, 2)
+                                    for q in (10, 50, 90)],
+           "graph_us_avg": round(r["graph_avg"] * 1e6, 2) if r["graph_avg"] else None,
+           "tokens_per_s": round(r["T"] / t, 1),
+           "effective_GBps": round(gbps, 1), "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2)}
+    return out
 
 
-def measure_siblings(steps, warmup):
+def run_workload(name, steps, warmup):
+    """(summary, case) for one named workload of any entry point."""
     import workloads
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     import gpu_helpers as gh
-    out = {}
-    for name in ("mla_decode", "mla_mixed"):
-        log(f"[bench] sibling {name}")
+    if name.startswith("mla_"):
         case = workloads.NAMED[name]()
-        out[name] = summarize(name, measure_mla(case, steps, warmup), steps)
-        del case
-    case = workloads.qk_generic()
-    dev = gh.QkDevice(case)
-    log("[bench] sibling qk_rope_paged_ragged")
-    wall, avg, durs = time_launches(lambda: dev.rope(True), steps, warmup)
-    out["qk_rope_paged_ragged"] = summarize(
-        "qk_generic (interleaved, position ids, fused per-head K norm)",
-        dict(T=case.T, bytes=qk_bytes(case, True), wall=wall, durs=durs, avg=avg,
-             med=float(np.median(durs))), steps)
-    log("[bench] sibling rms_norm_kv_cache_paged")
-    wall, avg, durs = time_launches(lambda: dev.kv_norm(dev.gamma, 0.0, case.T, True), steps,
-                                    warmup)
-    out["rms_norm_kv_cache_paged"] = summarize(
-        "qk_generic K cache (8 heads x 128, gamma 128)",
-        dict(T=case.T, bytes=kv_norm_bytes(case, 128), wall=wall, durs=durs, avg=avg,
-             med=float(np.median(durs))), steps)
+        dev = gh.MlaDevice(case)
+        r = measure(dev.run, case.T, mla_bytes(case), steps, warmup)
+        label = name
+    elif name == "qk_generic":
+        case = workloads.qk_generic()
+        dev = gh.QkDevice(case)
+        r = measure(lambda: dev.rope(True), case.T, qk_bytes(case, True), steps, warmup)
+        label = "qk_generic (interleaved, position ids, fused per-head K norm)"
+    elif name == "kv_norm":
+        case = workloads.qk_generic()
+        dev = gh.QkDevice(case)
+        r = measure(lambda: dev.kv_norm(dev.gamma, 0.0, case.T, True), case.T,
+                    kv_norm_bytes(case, 128), steps, warmup)
+        label = "qk_generic K cache (8 heads x 128, gamma 128)"
+    else:
+        raise ValueError(name)
+    return r, label, case
+
+
+def measure_siblings(main, steps, warmup):
+    out = {}
+    for name, entry in (("mla_decode", "mla_rope_rmsnorm_quant"),
+                        ("mla_mixed", "mla_rope_rmsnorm_quant"),
+                        ("qk_generic", "qk_rope_paged_ragged"),
+                        ("kv_norm", "rms_norm_kv_cache_paged")):
+        if name == main:
+            continue
+        log(f"[bench] sibling {name}")
+        r, label, _ = run_workload(name, steps, warmup)
+        out[name] = {"entry_point": entry, **summarize(label, r, steps, use_graph=True)}
     return out
 
 
@@ -225,11 +270,17 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mla_prefill",
-                    choices=["mla_prefill", "mla_decode", "mla_mixed"])
+                    choices=["mla_prefill", "mla_decode", "mla_mixed", "mla_tiny",
+                             "qk_generic", "kv_norm"])
     ap.add_argument("--no-siblings", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--source-hash", action="store_true",
+                    help="print the hash of the MLA kernel sources and exit")
     args = ap.parse_args()
+    if args.source_hash:
+        print(kernel_source_hash())
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "the path needs no inter-GPU exchange and is measured on a single MI355X.",
@@ -242,22 +293,28 @@ def main():
     if args.calibrate_copy:
         calibrate_copy(args.steps, args.warmup)
         return
-    import workloads
-    log(f"[bench] generating {args.workload}")
-    case = workloads.NAMED[args.workload]()
-    log(f"[bench] T={case.T} B={case.B} H={case.H}; timing {args.steps} steps")
-    r = measure_mla(case, args.steps, args.warmup)
-    main_sum = summarize(args.workload, r, args.steps)
+    log(f"[bench] workload {args.workload}; timing {args.steps} steps")
+    r, label, case = run_workload(args.workload, args.steps, args.warmup)
+    main_sum = summarize(label, r, args.steps)
     gbps = main_sum["effective_GBps"]
-    siblings = None if args.no_siblings else measure_siblings(max(10, args.steps // 2),
-                                                              args.warmup)
+    siblings = None if args.no_siblings else measure_siblings(
+        args.workload, max(20, args.steps // 2), args.warmup)
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.workload.startswith("mla_"):
         log("[bench] cpu baseline (oracle)")
         cpu = cpu_baseline(case)
     traffic = profiled_traffic(args.workload)
+    is_mla = args.workload.startswith("mla_")
+    config = ({"workload": args.workload, "tokens": case.T, "requests": case.B,
+               "q_heads": case.H, "rope_dim": case.R, "kv_norm_dim": case.Dn,
+               "page_size": case.meta["page_size"], "scale_mode": case.scale_mode,
+               "parallelism": "single GPU"} if is_mla else
+              {"workload": args.workload, "tokens": case.T, "requests": case.B,
+               "q_heads": int(case.q.shape[1]), "kv_heads": int(case.k_cache.shape[3]),
+               "head_dim": int(case.q.shape[2]), "page_size": case.meta["page_size"],
+               "parallelism": "single GPU"})
     line = {
-        "metric": METRIC,
+        "metric": METRIC if is_mla else f"{label}: tokens/s and effective HBM GB/s",
         "value": round(case.T * args.steps / r["wall"], 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -267,16 +324,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 in, fp32 math, fp8 e4m3fn cache",
+        "dtype": "bf16 in, fp32 math, fp8 e4m3fn cache" if is_mla else "bf16 in, fp32 math, bf16 out",
         "data": "synthetic (seeded; DeepSeek-V3-shaped random tensors, no weights)",
-        "config": {"workload": args.workload, "tokens": case.T, "requests": case.B,
-                   "q_heads": case.H, "rope_dim": case.R, "kv_norm_dim": case.Dn,
-                   "page_size": case.meta["page_size"], "scale_mode": case.scale_mode,
-                   "parallelism": "single GPU"},
+        "config": config,
         "effective_GBps": gbps,
         "pct_of_hbm_peak": main_sum["pct_of_hbm_peak"],
-        "kernel_us": {k: main_sum[k] for k in ("kernel_us_avg", "kernel_us_p10",
-                                               "kernel_us_p50", "kernel_us_p90")},
+        "kernel_us": {k: main_sum[k] for k in ("kernel_us_avg", "eager_us_p10_p50_p90",
+                                               "graph_us_avg")},
         "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbps / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "algorithmic_bytes": r["bytes"]},

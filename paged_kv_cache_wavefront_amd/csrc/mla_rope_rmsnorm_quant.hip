@@ -59,12 +59,44 @@ __device__ __forceinline__ HeadLane head_lane(int lane) {
 
 // Rotate the 8 values this lane owns, given its partner's 8 values: first
 // half  out = own*cos - partner*sin;  second half  out = own*cos + partner*sin.
+// cs holds (cos, sin) per pair with the sines already negated on first-half
+// lanes (negation is exact, so the products and roundings are unchanged).
 __device__ __forceinline__ void rotate_own(float (&own)[8], const float (&par)[8],
-                                           const float (&cs)[16], uint32_t neg) {
+                                           const float (&cs)[16]) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const float p = __uint_as_float(__float_as_uint(par[j]) ^ neg);
-    own[j] = sum_of_products(own[j], cs[2 * j], p, cs[2 * j + 1]);
+  for (int j = 0; j < 8; ++j) own[j] = sum_of_products(own[j], cs[2 * j], par[j], cs[2 * j + 1]);
+}
+
+// q loads / stores of one wave: NI instructions of 8 heads each.  The token
+// and chunk parts of the address are wave-uniform (scalar registers); each
+// lane adds a 32-bit offset.  GUARD masks heads past num_heads.
+// (base and step in bytes, wave-uniform; lane_off in bytes, per lane.)
+template <int NI, bool GUARD>
+__device__ __forceinline__ void load_q(uint4 (&q)[NI], const char* base, int64_t step,
+                                       uint32_t lane_off, uint32_t h_lane, uint32_t num_heads) {
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    if (GUARD) {
+      q[i] = make_uint4(0, 0, 0, 0);
+      if (h_lane + 8 * i >= num_heads) continue;
+    }
+    q[i] = load16_stream(base + i * step + lane_off);
+  }
+}
+
+template <int NI, bool GUARD>
+__device__ __forceinline__ void rotate_store_q(const uint4 (&q)[NI], const float (&cs)[16],
+                                               char* base, int64_t step, uint32_t lane_off,
+                                               uint32_t h_lane, uint32_t num_heads) {
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const uint4 partner = mirror16<8>(q[i]);
+    float own[8], par[8];
+    unpack8(q[i], own);
+    unpack8(partner, par);
+    rotate_own(own, par, cs);
+    if (GUARD && h_lane + 8 * i >= num_heads) continue;
+    store16(base + i * step + lane_off, pack8_bf16(own));
   }
 }
 
@@ -78,18 +110,19 @@ __global__ __launch_bounds__(256) void mla_kernel(const MlaArgs a) {
   const uint32_t chunk = uniform(wave - t * a.chunks);
   if (t >= a.total_tokens) return;
   const HeadLane hl = head_lane(lane);
-  const uint32_t neg = hl.first ? 0x80000000u : 0u;
 
   // ---- issue the bulk loads (addresses depend on t only) --------------------
-  const uint32_t h_lane = chunk * (8 * NI) + (uint32_t)(lane >> 3);
-  const uint16_t* qsrc = a.q_in + (int64_t)t * a.qi_tok + 8 * hl.chunk;
+  const uint32_t h0 = chunk * (8 * NI);  // first head of this wave
+  const uint32_t h_lane = h0 + (uint32_t)(lane >> 3);
+  const bool all_heads = h0 + 8 * NI <= a.num_heads;  // wave-uniform
+  const char* qsrc = reinterpret_cast<const char*>(a.q_in + (int64_t)t * a.qi_tok +
+                                                    (int64_t)h0 * a.qi_head);
+  const uint32_t qi_lane = 2 * ((uint32_t)(lane >> 3) * (uint32_t)a.qi_head + 8 * hl.chunk);
   uint4 q[NI];
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const uint32_t h = h_lane + 8 * i;
-    q[i] = make_uint4(0, 0, 0, 0);
-    if (h < a.num_heads) q[i] = load16_stream(qsrc + (int64_t)h * a.qi_head);
-  }
+  if (all_heads)
+    load_q<NI, false>(q, qsrc, 16 * a.qi_head, qi_lane, h_lane, a.num_heads);
+  else
+    load_q<NI, true>(q, qsrc, 16 * a.qi_head, qi_lane, h_lane, a.num_heads);
   const bool latent_wave = chunk == 0;
   uint4 xn = {}, gm = {}, tail = {};
   if (latent_wave) {
@@ -116,20 +149,19 @@ __global__ __launch_bounds__(256) void mla_kernel(const MlaArgs a) {
       const float4 v = fr[i];
       cs[4 * i] = v.x; cs[4 * i + 1] = v.y; cs[4 * i + 2] = v.z; cs[4 * i + 3] = v.w;
     }
+    if (hl.first) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) cs[2 * j + 1] = -cs[2 * j + 1];
+    }
   }
 
   // ---- q: exchange with the mirrored lane, rotate, store --------------------
-  uint16_t* qdst = a.q_out + (int64_t)t * a.qo_tok + 8 * hl.chunk;
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const uint4 partner = mirror16<8>(q[i]);
-    float own[8], par[8];
-    unpack8(q[i], own);
-    unpack8(partner, par);
-    rotate_own(own, par, cs, neg);
-    const uint32_t h = h_lane + 8 * i;
-    if (h < a.num_heads) store16(qdst + (int64_t)h * a.qo_head, pack8_bf16(own));
-  }
+  char* qdst = reinterpret_cast<char*>(a.q_out + (int64_t)t * a.qo_tok + (int64_t)h0 * a.qo_head);
+  const uint32_t qo_lane = 2 * ((uint32_t)(lane >> 3) * (uint32_t)a.qo_head + 8 * hl.chunk);
+  if (all_heads)
+    rotate_store_q<NI, false>(q, cs, qdst, 16 * a.qo_head, qo_lane, h_lane, a.num_heads);
+  else
+    rotate_store_q<NI, true>(q, cs, qdst, 16 * a.qo_head, qo_lane, h_lane, a.num_heads);
   if (!latent_wave) return;
 
   // ---- latent row: RMSNorm (non-rope part), RoPE (tail) ---------------------
@@ -147,7 +179,7 @@ __global__ __launch_bounds__(256) void mla_kernel(const MlaArgs a) {
   float tv[8], tp[8];
   unpack8(tail, tv);
   unpack8(mirror16<8>(tail), tp);
-  rotate_own(tv, tp, cs, neg);  // meaningful on lanes 0..7 only
+  rotate_own(tv, tp, cs);  // meaningful on lanes 0..7 only
 
   const int64_t row_elems = (int64_t)s.page * cv.page_stride + (int64_t)s.offset * cv.slot_stride;
   if constexpr (MODE == MlaOut::Bf16) {

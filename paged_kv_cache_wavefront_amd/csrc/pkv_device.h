@@ -92,10 +92,12 @@ __device__ __forceinline__ void store8_stream(void* p, uint2 v) {
 
 // ---- wave64 reductions (DPP inside 16-lane rows, readlane across rows) ------
 
+// Lane permutation within 16-lane rows (every lane reads a valid source for
+// the patterns used here, so no "old" value is needed).
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
 
 constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
@@ -109,7 +111,7 @@ constexpr int kDppMirror = 0x140;      // lane i <-> 15-i inside each 16 lanes
 // 16-lane (MIRROR=16) group: lane k receives lane (N-1-k)'s data.
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xF, 0xF, true);
 }
 
 template <int MIRROR>

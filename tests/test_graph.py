@@ -1,0 +1,68 @@
+"""The entry points inside a captured HIP graph (torch.cuda.CUDAGraph): every
+replay, with eager work and synchronisations between replays, must reproduce
+the eager result bit for bit.  The MLA call is out of place, so replays are
+idempotent; the in-place K paths are replayed on a fresh copy of K each time."""
+import numpy as np
+import pytest
+import torch
+
+import gpu_helpers as gh
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name", ["mla_tiny", "mla_prefill", "mla_mixed"])
+def test_mla_graph_replays(name):
+    case = workloads.NAMED[name]()
+    print(f"[graph] {name} T={case.T}", flush=True)
+    eager = gh.MlaDevice(case)
+    eager.run()
+    want = eager.results()
+    dev = gh.MlaDevice(case)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        dev.run()          # warm-up outside the graph
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dev.run()
+    for rep in range(3):
+        dev.q_out.zero_()                       # eager work between replays
+        junk = torch.ones(1 << 20, device="cuda") * rep
+        torch.cuda.synchronize()
+        g.replay()
+        got = dev.results()
+        assert np.array_equal(got[0], want[0]), f"replay {rep}: q differs"
+        assert np.array_equal(got[1], want[1]), f"replay {rep}: cache differs"
+        if got[2] is not None:
+            assert np.array_equal(got[2].view(np.uint32), want[2].view(np.uint32))
+        del junk
+
+
+def test_qk_graph_replays():
+    case = workloads.qk_generic()
+    eager = gh.QkDevice(case)
+    eager.rope(True)
+    want_q, want_k = gh.host_bf16(eager.q_out), gh.host_bf16(eager.k)
+    dev = gh.QkDevice(case)
+    k0 = dev.k.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        dev.rope(True)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dev.rope(True)
+    for rep in range(3):
+        dev.k.copy_(k0)                         # K is rotated in place: restore it
+        dev.q_out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(gh.host_bf16(dev.q_out), want_q), f"replay {rep}: q"
+        assert np.array_equal(gh.host_bf16(dev.k), want_k), f"replay {rep}: k"
