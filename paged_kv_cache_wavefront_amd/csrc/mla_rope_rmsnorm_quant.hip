@@ -16,9 +16,9 @@
 //   of lane k is lane 7-k and arrives with one DPP row_half_mirror per dword:
 //   no LDS round trip, and every load and store covers full 128-byte lines.
 // * q and latent are read with non-temporal loads (streamed once); all q
-//   loads of the wave are issued before the address chain
-//   ({offsets, cache lengths} -> page table -> freqs row), which then hides
-//   behind the bulk traffic.
+//   loads of the wave are issued before the address chain, which takes two
+//   dependent rounds ({offsets, cache lengths}, then {freqs row, page-table
+//   entry}) and hides behind the bulk traffic.
 // * The 16 cos/sin floats a lane needs sit contiguously in the freqs row and
 //   are the same for every head: one 64-byte load per lane per token, kept in
 //   registers.
@@ -132,27 +132,30 @@ __global__ __launch_bounds__(256) void mla_kernel(const MlaArgs a) {
     if (lane < 8) tail = load16_stream(row + kNope + 8 * hl.chunk);
   }
 
-  // ---- address chain: request, slot (= position), page, offset -------------
+  // ---- address chain -----------------------------------------------------------
+  // round 1: request and slot (= position); round 2: the freqs row and the
+  // page-table entry, both needing only the slot, issued together.
   const CacheView& cv = a.cache;
-  const SlotAddr s = locate(a.offsets, a.batch, cv.cache_lengths, cv.page_table, cv.pt_stride,
-                            cv.num_pages, cv.page_size, t, lane);
-  if (!s.ok || s.slot >= a.max_seq_len) {
-    if (latent_wave) count_skip(cv.error_count, lane);
-    return;
-  }
+  const TokenSlot ts = find_slot(a.offsets, a.batch, cv.cache_lengths, t, lane);
+  const bool pos_ok = ts.ok && ts.slot < a.max_seq_len;
   float cs[16];
-  {
-    const float4* fr = reinterpret_cast<const float4*>(a.freqs + (int64_t)s.slot * kRope +
+  if (pos_ok) {
+    const float4* fr = reinterpret_cast<const float4*>(a.freqs + (int64_t)ts.slot * kRope +
                                                        16 * hl.pair_block);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float4 v = fr[i];
       cs[4 * i] = v.x; cs[4 * i + 1] = v.y; cs[4 * i + 2] = v.z; cs[4 * i + 3] = v.w;
     }
-    if (hl.first) {
+  }
+  PageSlot ps{};
+  if (!(pos_ok && page_of(cv.page_table, cv.pt_stride, cv.num_pages, cv.page_size, ts, &ps))) {
+    if (latent_wave) count_skip(cv.error_count, lane);
+    return;
+  }
+  if (hl.first) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) cs[2 * j + 1] = -cs[2 * j + 1];
-    }
+    for (int j = 0; j < 8; ++j) cs[2 * j + 1] = -cs[2 * j + 1];
   }
 
   // ---- q: exchange with the mirrored lane, rotate, store --------------------
@@ -181,7 +184,7 @@ __global__ __launch_bounds__(256) void mla_kernel(const MlaArgs a) {
   unpack8(mirror16<8>(tail), tp);
   rotate_own(tv, tp, cs);  // meaningful on lanes 0..7 only
 
-  const int64_t row_elems = (int64_t)s.page * cv.page_stride + (int64_t)s.offset * cv.slot_stride;
+  const int64_t row_elems = (int64_t)ps.page * cv.page_stride + (int64_t)ps.offset * cv.slot_stride;
   if constexpr (MODE == MlaOut::Bf16) {
     uint16_t* row = static_cast<uint16_t*>(cv.layer_base) + row_elems;
 #pragma unroll
@@ -208,7 +211,7 @@ __global__ __launch_bounds__(256) void mla_kernel(const MlaArgs a) {
       const float st = am / 448.0f;
       inv = st > 0.0f ? 1.0f / st : 0.0f;
       if (lane == 0)
-        a.token_scales[((int64_t)s.page * cv.page_size + s.offset) * cv.num_heads] = st;
+        a.token_scales[((int64_t)ps.page * cv.page_size + ps.offset) * cv.num_heads] = st;
     }
     const float rs = r * inv;
 #pragma unroll

@@ -185,6 +185,8 @@ int qk_rope_paged_ragged(void* q_out, int64_t qo_tok_stride, int64_t qo_head_str
   a.qi_head = qi_head_stride;
   a.total_tokens = total_tokens;
   a.num_q_heads = num_q_heads;
+  const uint32_t qhpw = pkv::qk_heads_per_wave((int)head_dim);
+  a.chunks = num_q_heads == 0 ? 1u : (num_q_heads + qhpw - 1) / qhpw;
   a.offsets = input_row_offsets;
   a.batch = batch_size;
   a.freqs = freqs_cis;

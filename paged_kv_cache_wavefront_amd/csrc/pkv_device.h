@@ -186,29 +186,25 @@ __device__ __forceinline__ uint32_t find_request(const uint32_t* __restrict__ of
   return uniform(count);
 }
 
-struct SlotAddr {
-  uint32_t request;  // b
-  uint32_t slot;     // cache slot (= position when no explicit ids)
-  uint32_t page;     // physical page
-  uint32_t offset;   // slot within the page
-  bool ok;
-};
-
 __device__ __forceinline__ uint32_t lane_u32(uint32_t v, uint32_t lane) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, (int)lane);
 }
 
-// Address chain of token t: request, slot, page, offset, with every
-// device-data bound checked before use.  For batches of up to 256 requests the
-// request's start offset and prior length are fetched in the same round of
-// loads as the search (lane i holds entries i, i+64, ...), so the chain is two
-// dependent rounds: {offsets, cache_lengths} -> {page table}.
-__device__ __forceinline__ SlotAddr locate(const uint32_t* __restrict__ offsets, uint32_t B,
-                                           const uint32_t* __restrict__ cache_lengths,
-                                           const uint32_t* __restrict__ page_table,
-                                           uint32_t pt_stride, uint32_t num_pages,
-                                           uint32_t page_size, uint32_t t, int lane) {
-  SlotAddr a{};
+// First round of the address chain: the request owning token t and the
+// token's cache slot (prior length + index within the request).  For batches
+// of up to 256 requests every lane loads entries i, i+64, ... of the offsets
+// and the prior lengths in one round; the request is the number of offsets
+// <= t (ballot), and its start and prior length are read from the owning lane.
+struct TokenSlot {
+  uint32_t request;
+  uint32_t slot;
+  bool ok;           // request < B
+};
+
+__device__ __forceinline__ TokenSlot find_slot(const uint32_t* __restrict__ offsets, uint32_t B,
+                                               const uint32_t* __restrict__ cache_lengths,
+                                               uint32_t t, int lane) {
+  TokenSlot r{};
   constexpr int kChunks = 4;
   if (B <= kChunks * kWave) {
     uint32_t nxt[kChunks], beg[kChunks], len[kChunks];
@@ -223,10 +219,10 @@ __device__ __forceinline__ SlotAddr locate(const uint32_t* __restrict__ offsets,
     uint32_t count = 0;
 #pragma unroll
     for (int k = 0; k < kChunks; ++k) count += (uint32_t)__popcll(__ballot(nxt[k] <= t));
-    a.request = uniform(count);
-    a.ok = a.request < B;
-    if (!a.ok) return a;
-    const uint32_t kb = a.request / kWave, lb = a.request % kWave;
+    r.request = uniform(count);
+    r.ok = r.request < B;
+    if (!r.ok) return r;
+    const uint32_t kb = r.request / kWave, lb = r.request % kWave;
     uint32_t start = 0, prior = 0;
 #pragma unroll
     for (int k = 0; k < kChunks; ++k) {
@@ -235,20 +231,35 @@ __device__ __forceinline__ SlotAddr locate(const uint32_t* __restrict__ offsets,
         prior = lane_u32(len[k], lb);
       }
     }
-    a.slot = prior + (t - start);
+    r.slot = prior + (t - start);
   } else {
-    a.request = find_request(offsets, B, t, lane);
-    a.ok = a.request < B;
-    if (!a.ok) return a;
-    a.slot = uniform(cache_lengths[a.request] + (t - offsets[a.request]));
+    r.request = find_request(offsets, B, t, lane);
+    r.ok = r.request < B;
+    if (!r.ok) return r;
+    r.slot = uniform(cache_lengths[r.request] + (t - offsets[r.request]));
   }
-  const uint32_t col = a.slot / page_size;
-  a.ok = col < pt_stride;
-  if (!a.ok) return a;
-  a.page = uniform(page_table[(uint64_t)a.request * pt_stride + col]);
-  a.offset = a.slot - col * page_size;
-  a.ok = a.page < num_pages;
-  return a;
+  return r;
+}
+
+// Second round: physical page and offset of a slot.  Returns false when the
+// slot lies past the request's page-table row or the page id past the pool.
+struct PageSlot {
+  uint32_t page;
+  uint32_t offset;
+};
+
+__device__ __forceinline__ uint32_t page_column(uint32_t slot, uint32_t page_size) {
+  return slot / page_size;
+}
+
+__device__ __forceinline__ bool page_of(const uint32_t* __restrict__ page_table,
+                                        uint32_t pt_stride, uint32_t num_pages,
+                                        uint32_t page_size, const TokenSlot& ts, PageSlot* ps) {
+  const uint32_t col = page_column(ts.slot, page_size);
+  if (col >= pt_stride) return false;
+  ps->page = uniform(page_table[(uint64_t)ts.request * pt_stride + col]);
+  ps->offset = ts.slot - col * page_size;
+  return ps->page < num_pages;
 }
 
 __device__ __forceinline__ void count_skip(uint32_t* error_count, int lane) {

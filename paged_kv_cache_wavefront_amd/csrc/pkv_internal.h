@@ -51,6 +51,7 @@ struct QkArgs {
   const uint16_t* q_in;
   int64_t qi_tok, qi_head;
   uint32_t total_tokens, num_q_heads;
+  uint32_t chunks;               // waves per token (Q head chunks)
   const uint32_t* offsets;
   uint32_t batch;
   const float* freqs;
@@ -62,6 +63,8 @@ struct QkArgs {
   CacheView cache;               // bf16 K cache
 };
 
+// Q heads one wave of the Q/K kernel handles (head_dim 64 or 128).
+uint32_t qk_heads_per_wave(int head_dim);
 hipError_t launch_qk_rope(const QkArgs& a, int head_dim, bool interleaved, hipStream_t stream);
 
 struct KvNormArgs {

@@ -30,6 +30,7 @@ namespace pkv {
 namespace {
 
 constexpr int kWavesPerBlock = 4;
+constexpr int kQInstrPerWave = 4;  // 16-byte Q loads per lane per wave
 
 // gamma for the 8 columns base..base+7; 1 where the column lies past cols or
 // when there is no norm.
@@ -52,7 +53,6 @@ struct Geometry {
   static constexpr int kLanesPerHead = D / 8;
   static constexpr int kHeadsPerInstr = kWave / kLanesPerHead;
   static constexpr int kCs = INTER ? 8 : 16;  // cos/sin floats per lane
-  static constexpr int kQBatch = 8;            // head-instructions in flight
 };
 
 template <int D, bool INTER>
@@ -73,19 +73,37 @@ struct LaneRole {
       first = k < HALF;
       const int pb = first ? k : LP - 1 - k;  // pair block: pairs 8pb..8pb+7
       chunk = first ? k : LP + HALF - 1 - k;
-      partner_chunk = first ? LP + HALF - 1 - (LP - 1 - k) : LP - 1 - k;
+      partner_chunk = first ? HALF + k : LP - 1 - k;
       cs_base = 16 * pb;
     }
   }
 };
 
-// Rotate the lane's values.  own: this lane's 8 values; par: the partner's
-// (rotate-half only).  pre_own / pre_par scale inputs, post scales outputs.
+// Plain rotation of one lane's values (Q, and K without a norm).  cs holds
+// (cos, sin) per pair; for rotate-half the sines are pre-negated on
+// first-half lanes, so every output is own*cos + other*sin.
 template <bool INTER>
-__device__ __forceinline__ void rotate_lane(float (&own)[8], const float (&par)[8],
-                                            const float* cs, bool first,
-                                            const float (&pre_own)[8], const float (&pre_par)[8],
-                                            const float (&post)[8]) {
+__device__ __forceinline__ void rotate_plain(float (&own)[8], const float (&par)[8],
+                                             const float* cs) {
+  if constexpr (INTER) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float a = own[2 * q], b = own[2 * q + 1], c = cs[2 * q], s = cs[2 * q + 1];
+      own[2 * q] = sum_of_products(a, c, -b, s);
+      own[2 * q + 1] = sum_of_products(b, c, a, s);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) own[j] = sum_of_products(own[j], cs[2 * j], par[j], cs[2 * j + 1]);
+  }
+}
+
+// Rotation with per-value scalings (K with a norm): inputs scaled by pre_own /
+// pre_par before, outputs by post after.
+template <bool INTER>
+__device__ __forceinline__ void rotate_scaled(float (&own)[8], const float (&par)[8],
+                                              const float* cs, const float (&pre_own)[8],
+                                              const float (&pre_par)[8], const float (&post)[8]) {
   if constexpr (INTER) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -96,51 +114,79 @@ __device__ __forceinline__ void rotate_lane(float (&own)[8], const float (&par)[
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float p = par[j] * pre_par[j];
-      own[j] = sum_of_products(own[j] * pre_own[j], cs[2 * j], first ? -p : p, cs[2 * j + 1]) *
-               post[j];
-    }
+    for (int j = 0; j < 8; ++j)
+      own[j] = sum_of_products(own[j] * pre_own[j], cs[2 * j], par[j] * pre_par[j],
+                               cs[2 * j + 1]) * post[j];
   }
 }
 
-template <int D, bool INTER>
+// Q of one wave: NI instructions of HPI heads.  Base and step are wave-uniform
+// byte addresses; lane_off is the lane's byte offset.  GUARD masks heads past
+// num_heads.
+template <int D, bool INTER, int NI, bool GUARD>
+__device__ __forceinline__ void q_rope(const char* src, char* dst, int64_t in_step,
+                                       int64_t out_step, uint32_t in_off, uint32_t out_off,
+                                       uint32_t h_lane, uint32_t num_heads, const float* cs) {
+  constexpr int HPI = Geometry<D, INTER>::kHeadsPerInstr;
+  constexpr int LP = Geometry<D, INTER>::kLanesPerHead;
+  uint4 v[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    if (GUARD) {
+      v[i] = make_uint4(0, 0, 0, 0);
+      if (h_lane + HPI * i >= num_heads) continue;
+    }
+    v[i] = load16_stream(src + i * in_step + in_off);
+  }
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    float own[8], par[8] = {};
+    unpack8(v[i], own);
+    if constexpr (!INTER) unpack8(mirror16<LP>(v[i]), par);
+    rotate_plain<INTER>(own, par, cs);
+    if (GUARD && h_lane + HPI * i >= num_heads) continue;
+    store16(dst + i * out_step + out_off, pack8_bf16(own));
+  }
+}
+
+// One wave per (token, chunk of Q heads); chunk 0 also rotates (and
+// optionally normalises) the token's K heads.
+template <int D, bool INTER, int NI>
 __global__ __launch_bounds__(256) void qk_rope_kernel(const QkArgs a) {
   using Geo = Geometry<D, INTER>;
-  constexpr int LP = Geo::kLanesPerHead, HPI = Geo::kHeadsPerInstr, QB = Geo::kQBatch;
+  constexpr int LP = Geo::kLanesPerHead, HPI = Geo::kHeadsPerInstr;
   const int lane = threadIdx.x & (kWave - 1);
-  const uint32_t t =
-      uniform(xcd_block(blockIdx.x, gridDim.x) * kWavesPerBlock + (threadIdx.x / kWave));
+  const uint32_t wave =
+      xcd_block(blockIdx.x, gridDim.x) * kWavesPerBlock + (threadIdx.x / kWave);
+  const uint32_t t = uniform(wave / a.chunks);
+  const uint32_t chunk = uniform(wave - t * a.chunks);
   if (t >= a.total_tokens) return;
   const LaneRole<D, INTER> role(lane);
   const uint32_t hl = (uint32_t)(lane / LP);
   const int col = 8 * role.chunk;          // first column this lane owns
   const int pcol = 8 * role.partner_chunk;  // first column of the partner's values
 
-  const uint16_t* qsrc = a.q_in + (int64_t)t * a.qi_tok + col;
-  uint16_t* qdst = a.q_out + (int64_t)t * a.qo_tok + col;
-  uint4 qv[QB];
-  auto load_q = [&](uint32_t hbase) {
-#pragma unroll
-    for (int i = 0; i < QB; ++i) {
-      const uint32_t h = hbase + i * HPI + hl;
-      qv[i] = make_uint4(0, 0, 0, 0);
-      if (h < a.num_q_heads) qv[i] = load16_stream(qsrc + (int64_t)h * a.qi_head);
-    }
-  };
-  load_q(0);
+  // ---- Q loads first (addresses need only t) --------------------------------
+  const uint32_t h0 = chunk * (HPI * NI);
+  const uint32_t h_lane = h0 + hl;
+  const bool all_heads = h0 + HPI * NI <= a.num_q_heads;
+  const char* qsrc = reinterpret_cast<const char*>(a.q_in + (int64_t)t * a.qi_tok +
+                                                    (int64_t)h0 * a.qi_head);
+  char* qdst = reinterpret_cast<char*>(a.q_out + (int64_t)t * a.qo_tok + (int64_t)h0 * a.qo_head);
+  const uint32_t qi_off = 2 * (hl * (uint32_t)a.qi_head + (uint32_t)col);
+  const uint32_t qo_off = 2 * (hl * (uint32_t)a.qo_head + (uint32_t)col);
+  const int64_t qi_step = 2 * HPI * a.qi_head, qo_step = 2 * HPI * a.qo_head;
 
+  // ---- address chain: round 1 = {position id, offsets, prior lengths};
+  //      round 2 = {freqs row, page-table entry} ---------------------------------
   const CacheView& cv = a.cache;
-  const SlotAddr s = locate(a.offsets, a.batch, cv.cache_lengths, cv.page_table, cv.pt_stride,
-                            cv.num_pages, cv.page_size, t, lane);
-  uint32_t pos = s.slot;
-  if (s.ok && a.position_ids != nullptr) pos = uniform(a.position_ids[t]);
-  if (!s.ok || pos >= a.max_seq_len) {
-    count_skip(cv.error_count, lane);
-    return;
-  }
+  uint32_t pos_id = 0;
+  if (a.position_ids != nullptr) pos_id = uniform(a.position_ids[t]);
+  const TokenSlot ts = find_slot(a.offsets, a.batch, cv.cache_lengths, t, lane);
+  const uint32_t pos = a.position_ids != nullptr ? pos_id : ts.slot;
+  const bool pos_ok = ts.ok && pos < a.max_seq_len;
   float cs[Geo::kCs];
-  {
+  if (pos_ok) {
     const float4* fr = reinterpret_cast<const float4*>(a.freqs + (int64_t)pos * D + role.cs_base);
 #pragma unroll
     for (int i = 0; i < Geo::kCs / 4; ++i) {
@@ -148,27 +194,26 @@ __global__ __launch_bounds__(256) void qk_rope_kernel(const QkArgs a) {
       cs[4 * i] = v.x; cs[4 * i + 1] = v.y; cs[4 * i + 2] = v.z; cs[4 * i + 3] = v.w;
     }
   }
-  float ones[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) ones[j] = 1.0f;
-
-  // ---- Q ----------------------------------------------------------------------
-  auto rotate_store_q = [&](uint32_t hbase) {
-#pragma unroll
-    for (int i = 0; i < QB; ++i) {
-      float own[8], par[8] = {};
-      unpack8(qv[i], own);
-      if constexpr (!INTER) unpack8(mirror16<LP>(qv[i]), par);
-      rotate_lane<INTER>(own, par, cs, role.first, ones, ones, ones);
-      const uint32_t h = hbase + i * HPI + hl;
-      if (h < a.num_q_heads) store16(qdst + (int64_t)h * a.qo_head, pack8_bf16(own));
-    }
-  };
-  rotate_store_q(0);
-  for (uint32_t hbase = HPI * QB; hbase < a.num_q_heads; hbase += HPI * QB) {
-    load_q(hbase);
-    rotate_store_q(hbase);
+  PageSlot ps{};
+  if (!(pos_ok && page_of(cv.page_table, cv.pt_stride, cv.num_pages, cv.page_size, ts, &ps))) {
+    if (chunk == 0) count_skip(cv.error_count, lane);
+    return;
   }
+  if constexpr (!INTER) {
+    if (role.first) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) cs[2 * j + 1] = -cs[2 * j + 1];
+    }
+  }
+
+  // ---- Q ------------------------------------------------------------------------
+  if (all_heads)
+    q_rope<D, INTER, NI, false>(qsrc, qdst, qi_step, qo_step, qi_off, qo_off, h_lane,
+                                a.num_q_heads, cs);
+  else if (h0 < a.num_q_heads)
+    q_rope<D, INTER, NI, true>(qsrc, qdst, qi_step, qo_step, qi_off, qo_off, h_lane,
+                               a.num_q_heads, cs);
+  if (chunk != 0) return;
 
   // ---- K (in place), optional per-head RMSNorm first ------------------------
   const bool knorm = a.k_gamma != nullptr;
@@ -176,67 +221,70 @@ __global__ __launch_bounds__(256) void qk_rope_kernel(const QkArgs a) {
   float g[8], gp[8];  // gamma of this lane's columns and of the partner's
   load_gamma8(a.k_gamma, col, C, knorm, g);
   load_gamma8(a.k_gamma, pcol, C, knorm && !INTER, gp);
-  uint16_t* krow = static_cast<uint16_t*>(cv.layer_base) + (int64_t)s.page * cv.page_stride +
-                   (int64_t)s.offset * cv.slot_stride + col;
+  char* krow = static_cast<char*>(cv.layer_base) +
+               2 * ((int64_t)ps.page * cv.page_stride + (int64_t)ps.offset * cv.slot_stride);
+  const uint32_t k_off = 2 * (hl * (uint32_t)cv.head_stride + (uint32_t)col);
   for (uint32_t hbase = 0; hbase < cv.num_heads; hbase += HPI) {
-    const uint32_t h = hbase + hl;
-    const bool valid = h < cv.num_heads;
-    uint16_t* p = krow + (int64_t)h * cv.head_stride;
+    const bool valid = hbase + hl < cv.num_heads;
+    char* p = krow + 2 * (int64_t)hbase * cv.head_stride + k_off;
     uint4 kv = make_uint4(0, 0, 0, 0);
     if (valid) kv = load16(p);
     float own[8], par[8] = {};
     unpack8(kv, own);
     if constexpr (!INTER) unpack8(mirror16<LP>(kv), par);
-    float pre_own[8], pre_par[8], post[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) pre_own[j] = pre_par[j] = post[j] = 1.0f;
-    if (knorm) {
+    if (!knorm) {
+      rotate_plain<INTER>(own, par, cs);
+    } else {
       float ss = 0.0f;
 #pragma unroll
       for (int j = 0; j < 8; ++j)
         if (col + j < C) ss = fmaf(own[j], own[j], ss);
       ss = group_sum<LP>(ss);
       const float r = 1.0f / sqrtf(ss / (float)C + a.epsilon);
+      float pre_own[8], pre_par[8], post[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         own[j] *= g[j];  // exact (bf16 x bf16); g = 1 past C
         par[j] *= gp[j];
         // is this value / its pair partner inside the normalised span?
-        bool in_me, in_other;
-        if constexpr (INTER) {
-          in_me = col + j < C;
-          in_other = col + (j ^ 1) < C;
-        } else {
-          in_me = col + j < C;
-          in_other = pcol + j < C;
-        }
+        const bool in_me = col + j < C;
+        const bool in_other = INTER ? (col + (j ^ 1) < C) : (pcol + j < C);
         pre_own[j] = (in_me && !in_other) ? r : 1.0f;
         pre_par[j] = (in_other && !in_me) ? r : 1.0f;
         post[j] = (in_me && in_other) ? r : 1.0f;
       }
+      rotate_scaled<INTER>(own, par, cs, pre_own, pre_par, post);
     }
-    rotate_lane<INTER>(own, par, cs, role.first, pre_own, pre_par, post);
     if (valid) store16(p, pack8_bf16(own));
   }
 }
 
-template <int D, bool INTER>
+template <int D, bool INTER, int NI>
 hipError_t launch_one(const QkArgs& a, uint32_t blocks, hipStream_t stream) {
-  hipLaunchKernelGGL((qk_rope_kernel<D, INTER>), dim3(blocks), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((qk_rope_kernel<D, INTER, NI>), dim3(blocks), dim3(256), 0, stream, a);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const QkArgs& a, bool interleaved, uint32_t blocks, hipStream_t stream) {
+  return interleaved ? launch_one<D, true, kQInstrPerWave>(a, blocks, stream)
+                     : launch_one<D, false, kQInstrPerWave>(a, blocks, stream);
 }
 
 }  // namespace
 
+// Q heads per wave: kQInstrPerWave instructions of 64 / (head_dim / 8) heads,
+// i.e. 4 KiB of Q per wave (16 heads of 128 or 32 heads of 64).
+uint32_t qk_heads_per_wave(int head_dim) { return (uint32_t)kQInstrPerWave * (512u / (uint32_t)head_dim); }
+
 hipError_t launch_qk_rope(const QkArgs& a, int head_dim, bool interleaved, hipStream_t stream) {
-  const uint64_t blocks = ((uint64_t)a.total_tokens + kWavesPerBlock - 1) / kWavesPerBlock;
+  const uint64_t waves = (uint64_t)a.total_tokens * a.chunks;
+  const uint64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffull) return hipErrorInvalidValue;
   const uint32_t nb = (uint32_t)blocks;
-  if (head_dim == 128)
-    return interleaved ? launch_one<128, true>(a, nb, stream) : launch_one<128, false>(a, nb, stream);
-  if (head_dim == 64)
-    return interleaved ? launch_one<64, true>(a, nb, stream) : launch_one<64, false>(a, nb, stream);
+  if (head_dim == 128) return launch_d<128>(a, interleaved, nb, stream);
+  if (head_dim == 64) return launch_d<64>(a, interleaved, nb, stream);
   return hipErrorInvalidValue;
 }
 

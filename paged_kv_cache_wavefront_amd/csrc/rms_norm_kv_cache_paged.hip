@@ -34,9 +34,9 @@ __global__ __launch_bounds__(256) void kv_norm_kernel(const KvNormArgs a) {
   const uint32_t C = a.gamma_len;
 
   const CacheView& cv = a.cache;
-  const SlotAddr s = locate(a.offsets, a.batch, cv.cache_lengths, cv.page_table, cv.pt_stride,
-                            cv.num_pages, cv.page_size, t, lane);
-  if (!s.ok) {
+  const TokenSlot ts = find_slot(a.offsets, a.batch, cv.cache_lengths, t, lane);
+  PageSlot ps{};
+  if (!(ts.ok && page_of(cv.page_table, cv.pt_stride, cv.num_pages, cv.page_size, ts, &ps))) {
     count_skip(cv.error_count, lane);
     return;
   }
@@ -51,8 +51,8 @@ __global__ __launch_bounds__(256) void kv_norm_kernel(const KvNormArgs a) {
 #pragma unroll
   for (int k = 0; k < 8; ++k) g[k] += a.weight_offset;
 
-  uint16_t* krow = static_cast<uint16_t*>(cv.layer_base) + (int64_t)s.page * cv.page_stride +
-                   (int64_t)s.offset * cv.slot_stride + col0;
+  uint16_t* krow = static_cast<uint16_t*>(cv.layer_base) + (int64_t)ps.page * cv.page_stride +
+                   (int64_t)ps.offset * cv.slot_stride + col0;
   const bool touches = col0 < C;
   for (uint32_t hbase = 0; hbase < cv.num_heads; hbase += HPI) {
     const uint32_t h = hbase + hl;
