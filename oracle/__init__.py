@@ -14,6 +14,8 @@ point of the method:
   "mla_graph" module page;
 * :func:`qk_rope_paged_ragged` -- page "generic_fused_qk_rope_bshd_paged_ragged";
 * :func:`rms_norm_kv_cache_paged` -- page "rms_norm_kv_cache_ragged_paged";
+* :func:`mla_gather_latent_paged` -- the paged-to-contiguous latent copy and
+  fp8 (de)quantisation step of mla_prefill_branch_fp8 ("mla_graph" page);
 * the bf16 and FP8 E4M3FN codecs and the RoPE / RMSNorm row steps, exposed so
   that tests can pin each step on its own.
 
@@ -79,6 +81,10 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.oracle_qk_rope_paged_ragged.argtypes = [
         _vp, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64,
         _i64, _i64, _vp, _i64, _vp, ctypes.c_int, _vp, _i64, ctypes.c_float]
+    lib.oracle_mla_gather_latent_paged.restype = ctypes.c_int
+    lib.oracle_mla_gather_latent_paged.argtypes = [
+        _vp, ctypes.c_int, _vp, ctypes.c_float, _vp, _i64, _vp, _i64, _vp, ctypes.c_int,
+        ctypes.c_int, _vp, _i64, _i64, _i64, _i64, _i64]
     lib.oracle_rms_norm_kv_cache_paged.restype = ctypes.c_int
     lib.oracle_rms_norm_kv_cache_paged.argtypes = [
         _vp, _i64, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _i64,
@@ -214,6 +220,26 @@ class Oracle:
             int(bool(interleaved)), _ptr(k_gamma, np.uint16),
             0 if k_gamma is None else k_gamma.size, float(epsilon))
         _check(rc, "qk_rope_paged_ragged")
+
+    def mla_gather_latent_paged(self, out, kv_row_offsets, page_table, cache, layer_idx,
+                                scale_mode="none", cache_scales=None, out_scales=None,
+                                out_tensor_scale=1.0):
+        """Fill ``out`` [rows, W] (u8 = fp8 codes, u16 = bf16 bits) with the
+        cache rows of every request's context; cache [L,P,S,1,W] u8 or u16;
+        cache_scales f32 [1] (per-tensor) or [L,P,S,1] (per-token)."""
+        L, P, S, one, W = cache.shape
+        if one != 1 or out.shape[1] != W:
+            raise ValueError("inconsistent gather shapes")
+        B = kv_row_offsets.size - 1
+        mode = {"per_tensor": SCALE_PER_TENSOR, "per_token": SCALE_PER_TOKEN, "none": 0}[scale_mode]
+        rc = self.lib.oracle_mla_gather_latent_paged(
+            _ptr(out, out.dtype), CACHE_BF16 if out.dtype == np.uint16 else CACHE_FP8,
+            _ptr(out_scales, np.float32), float(out_tensor_scale),
+            _ptr(kv_row_offsets, np.uint32), B, _ptr(page_table, np.uint32),
+            page_table.shape[1], _ptr(cache, cache.dtype),
+            CACHE_BF16 if cache.dtype == np.uint16 else CACHE_FP8, mode,
+            _ptr(cache_scales, np.float32), W, L, P, S, int(layer_idx))
+        _check(rc, "mla_gather_latent_paged")
 
     def rms_norm_kv_cache_paged(self, k_cache, layer_idx, row_offsets,
                                 cache_lengths, page_table, gamma, epsilon,

@@ -349,6 +349,65 @@ int oracle_qk_rope_paged_ragged(
 }
 
 /*
+ * Gather of whole request contexts from the paged latent cache into a dense
+ * buffer ([GRAPH] mla_prefill_branch_fp8: the latent values are copied from
+ * the paged cache to a contiguous buffer and quantised to fp8 there).
+ * Row kv_row_offsets[b] + j of `out` receives cache slot j of request b, for
+ * j < kv_row_offsets[b+1] - kv_row_offsets[b].  Element conversions:
+ *   fp8  -> fp8 : the code itself; per-token scales copied to out_scales[row]
+ *   fp8  -> bf16: bf16_rne(decode(code) * scale), scale = the tensor scale or
+ *                 the row's per-token scale
+ *   bf16 -> bf16: the bits themselves
+ *   bf16 -> fp8 : e4m3fn_sat_rne(value / out_tensor_scale)
+ *
+ *   out     [total_rows][W] of u8 (fp8) or u16 (bf16), dense
+ *   cache   [L][P][S][W] of u8 (fp8) or u16 (bf16)
+ *   cache_scales  fp8 cache: [1] (per-tensor) or [L][P][S] (per-token)
+ */
+int oracle_mla_gather_latent_paged(
+    void* out, int out_type, float* out_scales, float out_tensor_scale,
+    const uint32_t* kv_row_offsets, int64_t B, const uint32_t* page_table,
+    int64_t pt_stride, const void* cache, int cache_type, int scale_mode,
+    const float* cache_scales, int64_t W, int64_t num_layers, int64_t num_pages,
+    int64_t page_size, int64_t layer_idx) {
+  if (W <= 0 || layer_idx < 0 || layer_idx >= num_layers || page_size <= 0)
+    return ORACLE_BAD_ARG;
+  int status = ORACLE_OK;
+  for (int64_t b = 0; b < B; ++b) {
+    for (int64_t row = kv_row_offsets[b]; row < (int64_t)kv_row_offsets[b + 1]; ++row) {
+      const int64_t slot = row - (int64_t)kv_row_offsets[b];
+      const int64_t page = page_of(page_table, pt_stride, num_pages, page_size, b, slot);
+      if (page < 0) { status = ORACLE_BAD_PAGE; continue; }
+      const int64_t src_row = (layer_idx * num_pages + page) * page_size + slot % page_size;
+      double scale = 1.0;
+      if (cache_type == ORACLE_CACHE_FP8)
+        scale = (double)(scale_mode == ORACLE_SCALE_PER_TOKEN ? cache_scales[src_row]
+                                                               : cache_scales[0]);
+      for (int64_t k = 0; k < W; ++k) {
+        if (cache_type == ORACLE_CACHE_FP8) {
+          const uint8_t code = ((const uint8_t*)cache)[src_row * W + k];
+          if (out_type == ORACLE_CACHE_FP8)
+            ((uint8_t*)out)[row * W + k] = code;
+          else
+            ((uint16_t*)out)[row * W + k] = oracle_bf16_encode(oracle_e4m3fn_decode(code) * scale);
+        } else {
+          const uint16_t bits = ((const uint16_t*)cache)[src_row * W + k];
+          if (out_type == ORACLE_CACHE_BF16)
+            ((uint16_t*)out)[row * W + k] = bits;
+          else
+            ((uint8_t*)out)[row * W + k] = oracle_e4m3fn_encode_sat(
+                oracle_bf16_decode(bits) / (double)out_tensor_scale);
+        }
+      }
+      if (cache_type == ORACLE_CACHE_FP8 && out_type == ORACLE_CACHE_FP8 &&
+          scale_mode == ORACLE_SCALE_PER_TOKEN && out_scales)
+        out_scales[row] = cache_scales[src_row];
+    }
+  }
+  return status;
+}
+
+/*
  * In-place RMSNorm of the new K-cache entries ([NORM] description): tokens
  * t < total_seq_len are mapped to (request, index) through row_offsets; each
  * head's first gamma_len columns are normalised with (gamma + weight_offset);

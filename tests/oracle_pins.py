@@ -635,6 +635,86 @@ def pin_rms_norm_kv(orc):
                     assert np.array_equal(k, expect), "kvnorm touched other elements"
 
 
+def gather_case(kind: str, seed: int = 3101):
+    """A paged latent cache holding whole request contexts: ``kind`` is
+    "fp8_tensor", "fp8_token" or "bf16".  Cache bytes are finite values (no
+    NaN codes); per-token scales are finite and positive.  Returns the case
+    and kv_row_offsets (prefix sums of prior + new lengths)."""
+    mode = {"fp8_tensor": "per_tensor", "fp8_token": "per_token", "bf16": "none"}[kind]
+    case = workloads.build_mla(f"gather_{kind}", seed, [3, 0, 9, 1, 20], [13, 5, 0, 30, 2],
+                               H=1, page_size=8, max_seq_len=64, spare_pages=3,
+                               scale_mode=mode, tensor_scale=0.05,
+                               cache_dtype="bf16" if kind == "bf16" else "fp8")
+    rng = np.random.Generator(np.random.PCG64(seed))
+    if kind == "bf16":
+        case.cache[...] = workloads.bf16_bits(
+            rng.standard_normal(case.cache.shape).astype(np.float32) * 3)
+    else:
+        nan = (case.cache & 0x7F) == 0x7F
+        case.cache[nan] ^= 0x01
+    if kind == "fp8_token":
+        case.token_scales[...] = rng.uniform(1e-3, 2.0, case.token_scales.shape).astype(np.float32)
+    ctx = case.cache_lengths.astype(np.int64) + np.diff(case.row_offsets.astype(np.int64))
+    kvo = np.zeros(ctx.size + 1, np.uint32)
+    kvo[1:] = np.cumsum(ctx)
+    return case, kvo
+
+
+def gather_owners(case, kvo):
+    """Inverse page-table scan: (page, offset) -> output row of the context."""
+    S = case.meta["page_size"]
+    owners = {}
+    for b in range(kvo.size - 1):
+        L = int(kvo[b + 1] - kvo[b])
+        for col, page in enumerate(case.page_table[b]):
+            if page == workloads.UNUSED_PAGE:
+                continue
+            for off in range(S):
+                slot = col * S + off
+                if slot < L:
+                    owners[(int(page), off)] = int(kvo[b]) + slot
+    return owners
+
+
+def pin_gather(orc):
+    """Each output row is the cache row its slot maps to: bit-exact copies,
+    correctly rounded dequantisation (code x scale -> bf16), brute-force
+    nearest fp8 codes for quantisation; per-token scales travel with rows."""
+    for kind in ("fp8_tensor", "fp8_token", "bf16"):
+        case, kvo = gather_case(kind)
+        rows = int(kvo[-1])
+        W = case.cache.shape[-1]
+        owners = gather_owners(case, kvo)
+        assert len(owners) == rows
+        L = case.layer_idx
+        src = np.empty((rows, W), case.cache.dtype)
+        row_scale = np.empty(rows)
+        for (page, off), r in owners.items():
+            src[r] = case.cache[L, page, off, 0]
+            row_scale[r] = (case.token_scales[L, page, off, 0] if kind == "fp8_token"
+                            else case.tensor_scale)
+        scales = (case.token_scales if kind == "fp8_token" else
+                  np.array([case.tensor_scale], np.float32))
+        for out_fp8 in (True, False):
+            out = np.zeros((rows, W), np.uint8 if out_fp8 else np.uint16)
+            osc = np.full(rows, -1.0, np.float32)
+            orc.mla_gather_latent_paged(out, kvo, case.page_table, case.cache, L,
+                                        case.scale_mode, scales if kind != "bf16" else None,
+                                        osc, out_tensor_scale=0.25)
+            if kind == "bf16" and not out_fp8:
+                assert np.array_equal(out, src), "bf16 copy"
+            elif kind == "bf16":
+                want = fp8_encode_bruteforce(bf16_to_f64(src).ravel() / 0.25).reshape(rows, W)
+                assert np.array_equal(out, want), "bf16 -> fp8"
+            elif out_fp8:
+                assert np.array_equal(out, src), "fp8 copy"
+                if kind == "fp8_token":
+                    assert np.array_equal(osc, row_scale.astype(np.float32)), "scales copy"
+            else:
+                ref = fp8_to_f64(src) * row_scale[:, None]
+                assert_correctly_rounded(bf16_to_f64(out), ref, ulp_bf16, f"dequant {kind}")
+
+
 ALL_PINS = [
     pin_fp8_decode, pin_fp8_encode_landmarks, pin_fp8_encode_bruteforce,
     pin_fp8_encode_torch, pin_bf16_landmarks, pin_bf16_encode_torch,
@@ -643,5 +723,5 @@ ALL_PINS = [
     pin_rope_relative_position, pin_rope_interleaved_permutation,
     pin_rmsnorm_closed_forms, pin_rmsnorm_torch, pin_mla_composite,
     pin_mla_position0, pin_mla_zero_row_per_token, pin_qk_composite,
-    pin_rms_norm_kv,
+    pin_rms_norm_kv, pin_gather,
 ]

@@ -77,6 +77,13 @@ MUTANTS = [
      "g[k] = oracle_bf16_decode(gamma[k]);"),
     ("kvnorm_cast_order", "if (multiply_before_cast) {", "if (!multiply_before_cast) {"),
     ("kvnorm_ignores_total", "if (t >= total_seq_len) break;", "(void)total_seq_len;"),
+    ("gather_slot_shift", "const int64_t slot = row - (int64_t)kv_row_offsets[b];",
+     "const int64_t slot = row - (int64_t)kv_row_offsets[b] + (b > 0);"),
+    ("gather_tensor_scale_only",
+     "scale = (double)(scale_mode == ORACLE_SCALE_PER_TOKEN ? cache_scales[src_row]",
+     "scale = (double)(scale_mode == ORACLE_SCALE_PER_TENSOR ? cache_scales[src_row]"),
+    ("gather_quant_multiplies", "oracle_bf16_decode(bits) / (double)out_tensor_scale);",
+     "oracle_bf16_decode(bits) * (double)out_tensor_scale);"),
 ]
 
 RUNNER = r"""
