@@ -81,6 +81,12 @@ def qk_bytes(case, with_norm: bool) -> int:
     return T * per_tok + shared
 
 
+def gather_bytes(rows: int, batch: int, page_size: int, in_bytes=576, out_bytes=1152) -> int:
+    """Each context row read from the cache and written to the dense buffer,
+    plus the offsets and one page-table entry per page of context."""
+    return rows * (in_bytes + out_bytes) + (batch + 1) * 4 + 4 * (-(-rows // page_size))
+
+
 def kv_norm_bytes(case, cols: int) -> int:
     T = case.T
     Hkv = case.k_cache.shape[3]
@@ -206,6 +212,24 @@ def run_workload(name, steps, warmup):
         r = measure(lambda: dev.kv_norm(dev.gamma, 0.0, case.T, True), case.T,
                     kv_norm_bytes(case, 128), steps, warmup)
         label = "qk_generic K cache (8 heads x 128, gamma 128)"
+    elif name == "gather":
+        import torch
+        import paged_kv_cache_wavefront_amd as pkv
+        case = workloads.mla_decode()
+        ctx = case.cache_lengths.astype(np.int64) + 1
+        kvo = np.zeros(ctx.size + 1, np.uint32)
+        kvo[1:] = np.cumsum(ctx)
+        rows = int(kvo[-1])
+        cache = gh.dev_u8(case.cache)
+        desc = pkv.paged_cache(cache, None, gh.dev_u32(case.page_table), pkv.PKV_SCALE_PER_TENSOR,
+                               gh.dev_f32(np.array([case.tensor_scale], np.float32)))
+        kv = gh.dev_u32(kvo)
+        out = torch.empty((rows, 576), dtype=torch.bfloat16, device="cuda")
+        keep = (cache, kv, out)
+        r = measure(lambda: pkv.mla_gather_latent_paged(out, kv, desc, case.layer_idx), rows,
+                    gather_bytes(rows, case.B, case.meta["page_size"]), steps, warmup)
+        r["keep"] = keep
+        label = f"gather of {case.B} request contexts ({rows} rows) fp8 -> bf16"
     else:
         raise ValueError(name)
     return r, label, case
@@ -216,7 +240,8 @@ def measure_siblings(main, steps, warmup):
     for name, entry in (("mla_decode", "mla_rope_rmsnorm_quant"),
                         ("mla_mixed", "mla_rope_rmsnorm_quant"),
                         ("qk_generic", "qk_rope_paged_ragged"),
-                        ("kv_norm", "rms_norm_kv_cache_paged")):
+                        ("kv_norm", "rms_norm_kv_cache_paged"),
+                        ("gather", "mla_gather_latent_paged")):
         if name == main:
             continue
         log(f"[bench] sibling {name}")
@@ -271,7 +296,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mla_prefill",
                     choices=["mla_prefill", "mla_decode", "mla_mixed", "mla_tiny",
-                             "qk_generic", "kv_norm"])
+                             "qk_generic", "kv_norm", "gather"])
     ap.add_argument("--no-siblings", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
@@ -305,17 +330,23 @@ def main():
         cpu = cpu_baseline(case)
     traffic = profiled_traffic(args.workload)
     is_mla = args.workload.startswith("mla_")
-    config = ({"workload": args.workload, "tokens": case.T, "requests": case.B,
-               "q_heads": case.H, "rope_dim": case.R, "kv_norm_dim": case.Dn,
-               "page_size": case.meta["page_size"], "scale_mode": case.scale_mode,
-               "parallelism": "single GPU"} if is_mla else
-              {"workload": args.workload, "tokens": case.T, "requests": case.B,
-               "q_heads": int(case.q.shape[1]), "kv_heads": int(case.k_cache.shape[3]),
-               "head_dim": int(case.q.shape[2]), "page_size": case.meta["page_size"],
-               "parallelism": "single GPU"})
+    if is_mla:
+        config = {"workload": args.workload, "tokens": case.T, "requests": case.B,
+                  "q_heads": case.H, "rope_dim": case.R, "kv_norm_dim": case.Dn,
+                  "page_size": case.meta["page_size"], "scale_mode": case.scale_mode,
+                  "parallelism": "single GPU"}
+    elif args.workload == "gather":
+        config = {"workload": args.workload, "rows": r["T"], "requests": case.B,
+                  "row": "576 fp8 -> 576 bf16", "page_size": case.meta["page_size"],
+                  "parallelism": "single GPU"}
+    else:
+        config = {"workload": args.workload, "tokens": case.T, "requests": case.B,
+                  "q_heads": int(case.q.shape[1]), "kv_heads": int(case.k_cache.shape[3]),
+                  "head_dim": int(case.q.shape[2]), "page_size": case.meta["page_size"],
+                  "parallelism": "single GPU"}
     line = {
         "metric": METRIC if is_mla else f"{label}: tokens/s and effective HBM GB/s",
-        "value": round(case.T * args.steps / r["wall"], 1),
+        "value": round(r["T"] * args.steps / r["wall"], 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,

@@ -16,6 +16,12 @@
  *                            Page "generic_fused_qk_rope_bshd_paged_ragged".
  *   rms_norm_kv_cache_paged  in-place RMSNorm of the new K-cache rows.
  *                            Page "rms_norm_kv_cache_ragged_paged".
+ *   mla_gather_latent_paged  copy of whole request contexts from the paged
+ *                            latent cache into a dense buffer, with fp8
+ *                            dequantisation / quantisation on the way (the
+ *                            paged-to-contiguous copy and fp8 quantisation
+ *                            steps of mla_prefill_branch_fp8, "mla_graph"
+ *                            module page).
  *
  * Conventions shared by all entry points
  * --------------------------------------
@@ -194,6 +200,37 @@ int rms_norm_kv_cache_paged(const pkv_paged_cache* k_cache, uint32_t layer_idx,
                             float weight_offset, uint32_t total_seq_len,
                             const uint32_t* input_row_offsets, uint32_t batch_size,
                             int per_head_norm, int multiply_before_cast, void* stream);
+
+/*
+ * Gather of request contexts from the paged latent cache.  For request b and
+ * j < kv_row_offsets[b+1] - kv_row_offsets[b], row kv_row_offsets[b] + j of
+ * out receives cache slot j of request b (layer layer_idx), converted:
+ *   fp8 cache  -> fp8 out : the codes; with per-token cache scales the row's
+ *                           scale is also written to out_scales[row]
+ *   fp8 cache  -> bf16 out: bf16_rne(decode(code) * scale), scale = the
+ *                           tensor scale or the row's per-token scale
+ *   bf16 cache -> bf16 out: the bits
+ *   bf16 cache -> fp8 out : E4M3FN_sat_rne(value / out_scale[0])
+ *
+ *   out             [total_rows][head_dim] of out_dtype, row stride
+ *                   out_row_stride (elements; 16-byte multiple)
+ *   out_dtype       PKV_DTYPE_FP8_E4M3FN or PKV_DTYPE_BF16
+ *   out_scales      fp32 [total_rows], written for fp8 -> fp8 with per-token
+ *                   scales; may be NULL otherwise
+ *   out_scale       fp32 [1], read for bf16 -> fp8; may be NULL otherwise
+ *   kv_row_offsets  u32 [batch_size + 1], prefix sums of context lengths
+ *   total_rows      (host) kv_row_offsets[batch_size]
+ *   cache           (host) latent cache descriptor, one head; its
+ *                   cache_lengths field is not used
+ * Rows whose slot has no valid page are skipped (not written) and counted.
+ * Supported here: head_dim * element size a multiple of 16 bytes, at most
+ * 1 KiB (fp8) / 2 KiB (bf16).
+ */
+int mla_gather_latent_paged(void* out, int32_t out_dtype, int64_t out_row_stride,
+                            float* out_scales, const float* out_scale,
+                            const uint32_t* kv_row_offsets, uint32_t batch_size,
+                            uint32_t total_rows, const pkv_paged_cache* cache,
+                            uint32_t layer_idx, void* stream);
 
 /* Static, NUL-terminated name of a status code. */
 const char* pkv_status_string(int status);

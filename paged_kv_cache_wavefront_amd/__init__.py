@@ -30,7 +30,7 @@ PKV_SCALE_PER_TENSOR = 1
 PKV_SCALE_PER_TOKEN = 2
 
 EXPORTED = ("mla_rope_rmsnorm_quant", "qk_rope_paged_ragged", "rms_norm_kv_cache_paged",
-            "pkv_status_string")
+            "mla_gather_latent_paged", "pkv_status_string")
 
 
 class PkvError(RuntimeError):
@@ -66,7 +66,7 @@ class PagedCache(ctypes.Structure):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is not built; run `python -m paged_kv_cache_wavefront_amd.build` "
+            f"{LIB_PATH} is not built; run `python paged_kv_cache_wavefront_amd/build.py` "
             "(hipcc, gfx950) first -- there is no CPU fallback")
     lib = ctypes.CDLL(LIB_PATH)
     i64, u32, vp, f32 = ctypes.c_int64, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_float
@@ -82,6 +82,9 @@ def _load() -> ctypes.CDLL:
     lib.rms_norm_kv_cache_paged.restype = ctypes.c_int
     lib.rms_norm_kv_cache_paged.argtypes = [
         cache_p, u32, vp, u32, f32, f32, u32, vp, u32, ctypes.c_int, ctypes.c_int, vp]
+    lib.mla_gather_latent_paged.restype = ctypes.c_int
+    lib.mla_gather_latent_paged.argtypes = [
+        vp, ctypes.c_int32, i64, vp, vp, vp, u32, u32, cache_p, u32, vp]
     lib.pkv_status_string.restype = ctypes.c_char_p
     lib.pkv_status_string.argtypes = [ctypes.c_int]
     return lib
@@ -112,13 +115,14 @@ def _stream(stream) -> int | None:
     return s.cuda_stream
 
 
-def paged_cache(data: torch.Tensor, cache_lengths: torch.Tensor, page_table: torch.Tensor,
+def paged_cache(data: torch.Tensor, cache_lengths: torch.Tensor | None, page_table: torch.Tensor,
                 scale_mode: int = PKV_SCALE_NONE, scales: torch.Tensor | None = None,
                 error_count: torch.Tensor | None = None) -> PagedCache:
     """Describe a 5-D cache pool ``data[layer, page, slot, head, dim]`` (bf16,
     or uint8 / float8_e4m3fn for FP8), its per-request prior lengths and its
     page table ``[batch, stride]``.  ``scales``: fp32 ``[1]`` (per-tensor) or
-    ``[layers, pages, page_size, heads]`` (per-token)."""
+    ``[layers, pages, page_size, heads]`` (per-token).  The returned descriptor
+    keeps references to the tensors it points to."""
     if data.dim() != 5:
         raise ValueError("cache data must be [layers, pages, page_size, heads, head_dim]")
     if data.dtype == torch.bfloat16:
@@ -132,13 +136,16 @@ def paged_cache(data: torch.Tensor, cache_lengths: torch.Tensor, page_table: tor
     if page_table.dim() != 2 or page_table.stride(1) != 1:
         raise ValueError("page_table must be a row-major [batch, stride] tensor")
     L, P, S, H, D = data.shape
-    return PagedCache(
+    desc = PagedCache(
         data=data.data_ptr(), dtype=dt, num_layers=L, num_pages=P, page_size=S,
         num_heads=H, head_dim=D, layer_stride=data.stride(0), page_stride=data.stride(1),
         slot_stride=data.stride(2), head_stride=data.stride(3),
-        cache_lengths=cache_lengths.data_ptr(), page_table=page_table.data_ptr(),
+        cache_lengths=_ptr(cache_lengths), page_table=page_table.data_ptr(),
         page_table_stride=page_table.stride(0), scale_mode=scale_mode,
         scales=_ptr(scales), error_count=_ptr(error_count))
+    # the struct holds raw device pointers: keep the tensors alive with it
+    desc._tensors = (data, cache_lengths, page_table, scales, error_count)
+    return desc
 
 
 def mla_rope_rmsnorm_quant(q_rope_output: torch.Tensor, q_rope: torch.Tensor,
@@ -189,3 +196,18 @@ def rms_norm_kv_cache_paged(k_cache: PagedCache, layer_idx: int, gamma: torch.Te
         input_row_offsets.numel() - 1, int(bool(per_head_norm)),
         int(bool(multiply_before_cast)), _stream(stream))
     _check("rms_norm_kv_cache_paged", st)
+
+
+def mla_gather_latent_paged(out: torch.Tensor, kv_row_offsets: torch.Tensor,
+                            cache: PagedCache, layer_idx: int,
+                            out_scales: torch.Tensor | None = None,
+                            out_scale: torch.Tensor | None = None, stream=None) -> None:
+    """Paged latent cache -> dense ``out`` [rows, head_dim] (C:
+    ``mla_gather_latent_paged``).  ``out`` is bf16 (dequantise / copy) or
+    uint8 / float8_e4m3fn (copy / quantise with ``out_scale``)."""
+    out_dt = PKV_DTYPE_BF16 if out.dtype == torch.bfloat16 else PKV_DTYPE_FP8_E4M3FN
+    st = _lib.mla_gather_latent_paged(
+        _ptr(out), out_dt, out.stride(0), _ptr(out_scales), _ptr(out_scale),
+        _ptr(kv_row_offsets), kv_row_offsets.numel() - 1, out.shape[0], ctypes.byref(cache),
+        int(layer_idx), _stream(stream))
+    _check("mla_gather_latent_paged", st)

@@ -2,8 +2,9 @@
 
 Compiles every ``csrc/*.hip`` and ``csrc/*.cpp`` with hipcc into
 ``paged_kv_cache_wavefront_amd/libpkv.so``, in-tree, so that the library
-travels with the source tree.  ``python -m paged_kv_cache_wavefront_amd.build``
-runs it from the command line.
+travels with the source tree.  Run it as a script,
+``python paged_kv_cache_wavefront_amd/build.py``, or load it by path: importing
+it through the package would load the (possibly stale) library first.
 """
 from __future__ import annotations
 

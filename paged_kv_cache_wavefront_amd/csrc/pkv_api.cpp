@@ -21,14 +21,14 @@ size_t elem_bytes(int32_t dtype) { return dtype == PKV_DTYPE_BF16 ? 2 : 1; }
 
 // Checks common to every cache descriptor; fills the per-layer view.
 int check_cache(const pkv_paged_cache* c, uint32_t layer_idx, uint32_t batch_size,
-                CacheView* view) {
+                CacheView* view, bool need_lengths = true) {
   if (c == nullptr) return PKV_ERR_NULL;
   if (c->dtype != PKV_DTYPE_BF16 && c->dtype != PKV_DTYPE_FP8_E4M3FN) return PKV_ERR_DTYPE;
   if (c->num_layers == 0 || c->num_pages == 0 || c->page_size == 0 || c->num_heads == 0 ||
       c->head_dim == 0 || c->page_table_stride == 0)
     return PKV_ERR_SHAPE;
   if (layer_idx >= c->num_layers) return PKV_ERR_RANGE;
-  if (batch_size > 0 && (c->cache_lengths == nullptr || c->page_table == nullptr))
+  if (batch_size > 0 && ((need_lengths && c->cache_lengths == nullptr) || c->page_table == nullptr))
     return PKV_ERR_NULL;
   if (c->data == nullptr) return PKV_ERR_NULL;
   // Every 16-byte vector access stays aligned when the pool base and every
@@ -231,6 +231,56 @@ int rms_norm_kv_cache_paged(const pkv_paged_cache* k_cache, uint32_t layer_idx,
   a.head_dim = k_cache->head_dim;
   return launch_status(
       pkv::launch_kv_norm(a, multiply_before_cast != 0, static_cast<hipStream_t>(stream)));
+}
+
+int mla_gather_latent_paged(void* out, int32_t out_dtype, int64_t out_row_stride,
+                            float* out_scales, const float* out_scale,
+                            const uint32_t* kv_row_offsets, uint32_t batch_size,
+                            uint32_t total_rows, const pkv_paged_cache* cache,
+                            uint32_t layer_idx, void* stream) {
+  if (cache == nullptr) return PKV_ERR_NULL;
+  if (out_dtype != PKV_DTYPE_BF16 && out_dtype != PKV_DTYPE_FP8_E4M3FN) return PKV_ERR_DTYPE;
+  const bool in_fp8 = cache->dtype == PKV_DTYPE_FP8_E4M3FN;
+  const bool out_fp8 = out_dtype == PKV_DTYPE_FP8_E4M3FN;
+  if (in_fp8 && cache->scale_mode != PKV_SCALE_PER_TENSOR && cache->scale_mode != PKV_SCALE_PER_TOKEN)
+    return PKV_ERR_DTYPE;
+  if (cache->dtype == PKV_DTYPE_BF16 && cache->scale_mode != PKV_SCALE_NONE) return PKV_ERR_DTYPE;
+  if (cache->num_heads != 1) return PKV_ERR_SHAPE;
+  const uint64_t in_eb = in_fp8 ? 1 : 2, out_eb = out_fp8 ? 1 : 2;
+  const uint64_t row_bytes = (uint64_t)cache->head_dim * in_eb;
+  if (row_bytes % 16 != 0 || ((uint64_t)cache->head_dim * out_eb) % 8 != 0) return PKV_ERR_ALIGN;
+  if ((in_fp8 ? 16 : 8) * (row_bytes / 16) > 1024) return PKV_ERR_UNSUPPORTED;
+  if (out_row_stride < (int64_t)cache->head_dim) return PKV_ERR_SHAPE;
+  if (total_rows > 0 && batch_size == 0) return PKV_ERR_SHAPE;
+  CacheView view{};
+  int st = check_cache(cache, layer_idx, batch_size, &view, /*need_lengths=*/false);
+  if (st != PKV_OK) return st;
+  if (total_rows == 0) return PKV_OK;
+  if (out == nullptr || kv_row_offsets == nullptr) return PKV_ERR_NULL;
+  if (in_fp8 && cache->scales == nullptr) return PKV_ERR_NULL;
+  if (in_fp8 && out_fp8 && cache->scale_mode == PKV_SCALE_PER_TOKEN && out_scales == nullptr)
+    return PKV_ERR_NULL;
+  if (!in_fp8 && out_fp8 && out_scale == nullptr) return PKV_ERR_NULL;
+  if (!aligned16(out) || ((uint64_t)out_row_stride * out_eb) % 16 != 0) return PKV_ERR_ALIGN;
+
+  pkv::GatherArgs a{};
+  a.out = out;
+  a.out_row_bytes = out_row_stride * (int64_t)out_eb;
+  a.out_scales = out_scales;
+  a.out_scale = out_scale;
+  a.kv_row_offsets = kv_row_offsets;
+  a.batch = batch_size;
+  a.total_rows = total_rows;
+  a.row_bytes = (uint32_t)row_bytes;
+  const bool per_token = in_fp8 && cache->scale_mode == PKV_SCALE_PER_TOKEN;
+  a.cache_scale = cache->scales;
+  if (per_token)
+    a.cache_scale = cache->scales + (int64_t)layer_idx * cache->num_pages * cache->page_size *
+                                        cache->num_heads;
+  a.cache = view;
+  const pkv::GatherKind kind = in_fp8 ? (out_fp8 ? pkv::GatherKind::Fp8ToFp8 : pkv::GatherKind::Fp8ToBf16)
+                                      : (out_fp8 ? pkv::GatherKind::Bf16ToFp8 : pkv::GatherKind::Bf16ToBf16);
+  return launch_status(pkv::launch_gather(a, kind, per_token, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -84,6 +84,12 @@ __device__ __forceinline__ uint4 load16_stream(const void* p) {
 __device__ __forceinline__ uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ void store16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
 
+// 16-byte non-temporal store (large outputs written once, never re-read here).
+__device__ __forceinline__ void store16_stream(void* p, uint4 v) {
+  const u32x4_t w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(p));
+}
+
 // 8-byte non-temporal store (cache rows: written once, never re-read here).
 __device__ __forceinline__ void store8_stream(void* p, uint2 v) {
   const u32x2_t w = {v.x, v.y};

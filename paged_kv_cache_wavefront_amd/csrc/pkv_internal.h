@@ -80,4 +80,21 @@ struct KvNormArgs {
 
 hipError_t launch_kv_norm(const KvNormArgs& a, bool multiply_before_cast, hipStream_t stream);
 
+struct GatherArgs {
+  void* out;
+  int64_t out_row_bytes;        // output row stride in bytes
+  float* out_scales;            // per-token scale copy target (may be null)
+  const float* out_scale;       // bf16 -> fp8 per-tensor scale (may be null)
+  const uint32_t* kv_row_offsets;
+  uint32_t batch;
+  uint32_t total_rows;
+  uint32_t row_bytes;           // cache row size in bytes (head_dim * element size)
+  const float* cache_scale;     // fp8 cache: per-tensor [1] or this layer's per-token scales
+  CacheView cache;
+};
+
+enum class GatherKind : int { Fp8ToFp8 = 0, Fp8ToBf16 = 1, Bf16ToBf16 = 2, Bf16ToFp8 = 3 };
+
+hipError_t launch_gather(const GatherArgs& a, GatherKind kind, bool per_token, hipStream_t stream);
+
 }  // namespace pkv

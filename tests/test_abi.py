@@ -29,7 +29,8 @@ def pkv():
 
 def test_header_declares_entry_points():
     assert declared_functions() == sorted(["mla_rope_rmsnorm_quant", "qk_rope_paged_ragged",
-                                           "rms_norm_kv_cache_paged", "pkv_status_string"])
+                                           "rms_norm_kv_cache_paged", "mla_gather_latent_paged",
+                                           "pkv_status_string"])
 
 
 def test_library_exports_every_declared_function(pkv):
@@ -150,6 +151,35 @@ def test_kv_norm_validation(pkv):
     assert call_norm(pkv, kcache(pkv), T=0) == OK
 
 
+def call_gather(pkv, cache, out_dtype=None, stride=576, rows=32, out=FAKE, oscales=FAKE,
+                oscale=FAKE, layer=1):
+    lib = pkv.library()
+    cp = None if cache is None else ctypes.byref(cache)
+    dt = pkv.PKV_DTYPE_BF16 if out_dtype is None else out_dtype
+    return lib.mla_gather_latent_paged(out, dt, stride, oscales, oscale, FAKE, 2, rows, cp,
+                                       layer, None)
+
+
+def test_gather_validation(pkv):
+    c = lambda **kw: mla_cache(pkv, cache_lengths=None, **kw)  # noqa: E731
+    assert call_gather(pkv, None) == NULL
+    assert call_gather(pkv, c(), out_dtype=9) == DTYPE
+    assert call_gather(pkv, c(scale_mode=pkv.PKV_SCALE_NONE)) == DTYPE
+    assert call_gather(pkv, c(dtype=pkv.PKV_DTYPE_BF16)) == DTYPE      # bf16 needs NONE
+    assert call_gather(pkv, c(num_heads=2)) == SHAPE
+    assert call_gather(pkv, c(head_dim=100)) == ALIGN
+    assert call_gather(pkv, c(head_dim=2048, slot_stride=2048)) == UNSUP
+    assert call_gather(pkv, c(), stride=500) == SHAPE
+    assert call_gather(pkv, c(), stride=580) == ALIGN
+    assert call_gather(pkv, c(), layer=2) == RANGE
+    assert call_gather(pkv, c(), out=None) == NULL
+    assert call_gather(pkv, c(scales=None)) == NULL
+    assert call_gather(pkv, c(scale_mode=pkv.PKV_SCALE_PER_TOKEN),
+                       out_dtype=pkv.PKV_DTYPE_FP8_E4M3FN, oscales=None) == NULL
+    assert call_gather(pkv, c(), out=FAKE + 8) == ALIGN
+    assert call_gather(pkv, c(), rows=0) == OK
+
+
 def test_product_path_does_not_reference_the_oracle():
     """The HIP library and its binding never load or import the oracle."""
     pkg = os.path.join(ROOT, "paged_kv_cache_wavefront_amd")
@@ -158,3 +188,19 @@ def test_product_path_does_not_reference_the_oracle():
             if f.endswith((".py", ".hip", ".cpp", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text, os.path.join(dirpath, f)
+
+
+def test_descriptor_keeps_its_tensors_alive(pkv):
+    """A descriptor stores raw pointers; it must hold references to the tensors
+    so that temporaries passed to paged_cache() are not freed and reused."""
+    import gc
+    import weakref
+
+    import torch
+    pt = torch.zeros((2, 4), dtype=torch.int32)
+    ref = weakref.ref(pt)
+    desc = pkv.paged_cache(torch.zeros((1, 2, 4, 1, 576), dtype=torch.uint8), None, pt,
+                           pkv.PKV_SCALE_PER_TENSOR, torch.ones(1))
+    del pt
+    gc.collect()
+    assert ref() is not None and desc.page_table == ref().data_ptr()

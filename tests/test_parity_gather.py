@@ -1,0 +1,137 @@
+"""GPU parity of mla_gather_latent_paged against the oracle, through the C ABI:
+fp8 -> fp8 (with per-token scales), fp8 -> bf16 (per-tensor and per-token),
+bf16 -> bf16 and bf16 -> fp8, on small ragged contexts and on long contexts
+taken from the decode workload's pool."""
+import numpy as np
+import pytest
+import torch
+
+import gpu_helpers as gh
+import oracle_pins
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def finite_pool(case, seed):
+    """Make the pool's values finite (fp8: no NaN codes; per-token scales
+    finite and positive) so that every output has a numeric value."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    if case.cache.dtype == np.uint8:
+        nan = (case.cache & 0x7F) == 0x7F
+        case.cache[nan] ^= 0x01
+    else:
+        case.cache[...] = workloads.bf16_bits(
+            rng.standard_normal(case.cache.shape).astype(np.float32) * 3)
+    if case.token_scales is not None:
+        case.token_scales[...] = rng.uniform(1e-3, 2.0, case.token_scales.shape).astype(np.float32)
+
+
+def run_gather(orc, case, kvo, out_fp8, out_scale=0.25, subset=None):
+    import paged_kv_cache_wavefront_amd as pkv
+    rows = int(kvo[-1])
+    W = case.cache.shape[-1]
+    _say(f"[gather] case={case.name} rows={rows} in={case.cache.dtype} out_fp8={out_fp8} "
+         f"scale={case.scale_mode}")
+    cache = gh.dev_bf16(case.cache) if case.cache.dtype == np.uint16 else gh.dev_u8(case.cache)
+    pt = gh.dev_u32(case.page_table)
+    kv = gh.dev_u32(kvo)
+    if case.cache.dtype == np.uint16:
+        mode, scales = pkv.PKV_SCALE_NONE, None
+    elif case.scale_mode == "per_token":
+        mode, scales = pkv.PKV_SCALE_PER_TOKEN, gh.dev_f32(case.token_scales)
+    else:
+        mode, scales = pkv.PKV_SCALE_PER_TENSOR, gh.dev_f32(np.array([case.tensor_scale], np.float32))
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    desc = pkv.paged_cache(cache, None, pt, mode, scales, err)
+    out = torch.full((rows, W), 0x55 if out_fp8 else 0x5555, device="cuda",
+                     dtype=torch.uint8 if out_fp8 else torch.int16)
+    if not out_fp8:
+        out = out.view(torch.bfloat16)
+    osc = torch.full((max(rows, 1),), -7.0, device="cuda")
+    oscale = gh.dev_f32(np.array([out_scale], np.float32))
+    pkv.mla_gather_latent_paged(out, kv, desc, case.layer_idx, osc, oscale)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    got = gh.host_u8(out) if out_fp8 else gh.host_bf16(out)
+    got_sc = gh.host_f32(osc)
+    want = np.zeros((rows, W), np.uint8 if out_fp8 else np.uint16)
+    want_sc = np.full(max(rows, 1), -7.0, np.float32)
+    sc_host = (case.token_scales if case.scale_mode == "per_token" else
+               np.array([case.tensor_scale], np.float32))
+    orc.mla_gather_latent_paged(want, kvo, case.page_table, case.cache, case.layer_idx,
+                                case.scale_mode if case.cache.dtype == np.uint8 else "none",
+                                sc_host if case.cache.dtype == np.uint8 else None,
+                                want_sc, out_tensor_scale=out_scale)
+    if out_fp8:
+        d = gh.fp8_ulp_diff(got, want)
+        if case.cache.dtype == np.uint8:
+            assert np.array_equal(got, want), "fp8 copy must be exact"
+        stats = dict(max_ulp=int(d.max(initial=0)), diff_frac=float((d != 0).mean()) if d.size else 0.0)
+        assert stats["max_ulp"] <= gh.FP8_MAX_ULP and stats["diff_frac"] <= gh.FP8_MAX_DIFF_FRAC
+        if case.scale_mode == "per_token" and case.cache.dtype == np.uint8:
+            assert np.array_equal(got_sc[:rows].view(np.uint32), want_sc[:rows].view(np.uint32))
+    else:
+        if case.cache.dtype == np.uint16:
+            assert np.array_equal(got, want), "bf16 copy must be exact"
+        stats = gh.check_bf16(got, want, "gather bf16")
+    _say(f"[gather] {case.name}: {stats}")
+
+
+@pytest.mark.parametrize("kind", ["fp8_tensor", "fp8_token", "bf16"])
+@pytest.mark.parametrize("out_fp8", [True, False])
+def test_small_contexts(orc, kind, out_fp8):
+    case, kvo = oracle_pins.gather_case(kind)
+    run_gather(orc, case, kvo, out_fp8)
+
+
+@pytest.mark.parametrize("out_fp8", [True, False])
+def test_long_contexts(orc, out_fp8):
+    """16 requests of the decode workload's pool, each gathered over its whole
+    prior context plus the new token (page size 128, per-tensor scale 0.05)."""
+    case = workloads.mla_decode()
+    finite_pool(case, 7001)
+    n = 16
+    ctx = case.cache_lengths[:n].astype(np.int64) + 1
+    kvo = np.zeros(n + 1, np.uint32)
+    kvo[1:] = np.cumsum(ctx)
+    case.page_table = np.ascontiguousarray(case.page_table[:n])
+    run_gather(orc, case, kvo, out_fp8)
+
+
+def test_mixed_per_token(orc):
+    case = workloads.mla_mixed()
+    finite_pool(case, 7002)
+    n = 6
+    sel = np.r_[0:2, 64:68]      # two decode rows (long contexts) + the 4 prefill requests
+    ctx = case.cache_lengths[sel].astype(np.int64) + np.diff(case.row_offsets.astype(np.int64))[sel]
+    kvo = np.zeros(n + 1, np.uint32)
+    kvo[1:] = np.cumsum(ctx)
+    case.page_table = np.ascontiguousarray(case.page_table[sel])
+    run_gather(orc, case, kvo, out_fp8=False)
+    run_gather(orc, case, kvo, out_fp8=True)
+
+
+def test_bad_page_rows_skipped(orc):
+    """A row whose page id lies past the pool is skipped (not written) and
+    counted; the other rows are exact."""
+    import paged_kv_cache_wavefront_amd as pkv
+    case, kvo = oracle_pins.gather_case("fp8_tensor")
+    case.page_table[2, 0] = case.meta["num_pages"] + 1     # request 2: its first page
+    cache = gh.dev_u8(case.cache)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    desc = pkv.paged_cache(cache, None, gh.dev_u32(case.page_table), pkv.PKV_SCALE_PER_TENSOR,
+                           gh.dev_f32(np.array([case.tensor_scale], np.float32)), err)
+    rows = int(kvo[-1])
+    out = torch.full((rows, 576), 0x55, dtype=torch.uint8, device="cuda")
+    pkv.mla_gather_latent_paged(out, gh.dev_u32(kvo), desc, case.layer_idx)
+    torch.cuda.synchronize()
+    got = gh.host_u8(out)
+    r2 = range(int(kvo[2]), int(kvo[3]))
+    bad = [r for r in r2 if (r - int(kvo[2])) < case.meta["page_size"]]
+    assert int(err.item()) == len(bad)
+    assert np.all(got[bad] == 0x55)
