@@ -79,16 +79,17 @@ def load(path: str | None = None) -> ctypes.CDLL:
         _i64, ctypes.c_int, ctypes.c_float, _vp]
     lib.oracle_qk_rope_paged_ragged.restype = ctypes.c_int
     lib.oracle_qk_rope_paged_ragged.argtypes = [
-        _vp, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64,
-        _i64, _i64, _vp, _i64, _vp, ctypes.c_int, _vp, _i64, ctypes.c_float]
+        _vp, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _i64, _vp, ctypes.c_int, ctypes.c_int,
+        _vp, _i64, _i64, _i64, _i64, _i64, _vp, _i64, _vp, ctypes.c_int, _vp, _i64,
+        ctypes.c_float]
     lib.oracle_mla_gather_latent_paged.restype = ctypes.c_int
     lib.oracle_mla_gather_latent_paged.argtypes = [
         _vp, ctypes.c_int, _vp, ctypes.c_float, _vp, _i64, _vp, _i64, _vp, ctypes.c_int,
         ctypes.c_int, _vp, _i64, _i64, _i64, _i64, _i64]
     lib.oracle_rms_norm_kv_cache_paged.restype = ctypes.c_int
     lib.oracle_rms_norm_kv_cache_paged.argtypes = [
-        _vp, _i64, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _i64,
-        _vp, _i64, ctypes.c_float, ctypes.c_float, _i64, ctypes.c_int]
+        _vp, ctypes.c_int, ctypes.c_int, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _vp, _vp,
+        _i64, _vp, _i64, _vp, _i64, ctypes.c_float, ctypes.c_float, _i64, ctypes.c_int]
     return lib
 
 
@@ -200,22 +201,27 @@ class Oracle:
 
     def qk_rope_paged_ragged(self, q_out, q_in, row_offsets, cache_lengths,
                              page_table, k_cache, layer_idx, freqs, position_ids,
-                             interleaved, k_gamma=None, epsilon=1e-6):
+                             interleaved, k_gamma=None, epsilon=1e-6, k_scale_mode="none",
+                             k_scales=None):
         """Fill ``q_out``; rotate (and optionally K-normalise) ``k_cache``.
 
-        Shapes: q [T,Hq,D] u16; k_cache [L,P,S,Hkv,D] u16; freqs [max_seq,D]
-        f32; position_ids [T] u32 or None; k_gamma [C] u16 or None.
+        Shapes: q [T,Hq,D] u16; k_cache [L,P,S,Hkv,D] u16 (bf16) or u8 (fp8,
+        with k_scale_mode "per_tensor" -> k_scales f32 [1], "per_token" ->
+        k_scales f32 [L,P,S,Hkv], rewritten); freqs [max_seq,D] f32;
+        position_ids [T] u32 or None; k_gamma [C] u16 or None.
         """
         T, Hq, D = q_in.shape
         L, P, S, Hkv, Dk = k_cache.shape
         if Dk != D or q_out.shape != q_in.shape:
             raise ValueError("inconsistent QK shapes")
         B = row_offsets.size - 1
+        k_type = CACHE_BF16 if k_cache.dtype == np.uint16 else CACHE_FP8
+        mode = {"per_tensor": SCALE_PER_TENSOR, "per_token": SCALE_PER_TOKEN, "none": 0}[k_scale_mode]
         rc = self.lib.oracle_qk_rope_paged_ragged(
             _ptr(q_out, np.uint16), _ptr(q_in, np.uint16), Hq, D,
             _ptr(row_offsets, np.uint32), _ptr(cache_lengths, np.uint32), B,
-            _ptr(page_table, np.uint32), page_table.shape[1],
-            _ptr(k_cache, np.uint16), L, P, S, Hkv, int(layer_idx),
+            _ptr(page_table, np.uint32), page_table.shape[1], _ptr(k_cache, k_cache.dtype),
+            k_type, mode, _ptr(k_scales, np.float32), L, P, S, Hkv, int(layer_idx),
             _ptr(freqs, np.float32), freqs.shape[0], _ptr(position_ids, np.uint32),
             int(bool(interleaved)), _ptr(k_gamma, np.uint16),
             0 if k_gamma is None else k_gamma.size, float(epsilon))
@@ -244,12 +250,17 @@ class Oracle:
     def rms_norm_kv_cache_paged(self, k_cache, layer_idx, row_offsets,
                                 cache_lengths, page_table, gamma, epsilon,
                                 weight_offset, total_seq_len,
-                                multiply_before_cast=True):
-        """Normalise the new K rows of ``k_cache`` in place (per-head form)."""
+                                multiply_before_cast=True, k_scale_mode="none",
+                                k_scales=None):
+        """Normalise the new K rows of ``k_cache`` in place (per-head form);
+        fp8 caches as in :meth:`qk_rope_paged_ragged`."""
         L, P, S, Hkv, D = k_cache.shape
         B = row_offsets.size - 1
+        k_type = CACHE_BF16 if k_cache.dtype == np.uint16 else CACHE_FP8
+        mode = {"per_tensor": SCALE_PER_TENSOR, "per_token": SCALE_PER_TOKEN, "none": 0}[k_scale_mode]
         rc = self.lib.oracle_rms_norm_kv_cache_paged(
-            _ptr(k_cache, np.uint16), L, P, S, Hkv, D, int(layer_idx),
+            _ptr(k_cache, k_cache.dtype), k_type, mode, _ptr(k_scales, np.float32),
+            L, P, S, Hkv, D, int(layer_idx),
             _ptr(row_offsets, np.uint32), _ptr(cache_lengths, np.uint32), B,
             _ptr(page_table, np.uint32), page_table.shape[1],
             _ptr(gamma, np.uint16), gamma.size, float(epsilon),

@@ -296,14 +296,48 @@ int oracle_mla_rope_rmsnorm_quant(
  *   position_ids  u32 [T] or NULL (then position = cache length + index)
  *   k_gamma       bf16 bits [k_norm_cols] or NULL
  */
+/* K row of one head, widened to binary64: bf16 bits, or fp8 code times the
+ * row's scale. */
+static void load_k_row(const void* k_cache, int k_type, int64_t elem, int64_t D,
+                       double scale, double* a) {
+  for (int64_t i = 0; i < D; ++i)
+    a[i] = k_type == ORACLE_CACHE_BF16
+               ? oracle_bf16_decode(((const uint16_t*)k_cache)[elem + i])
+               : oracle_e4m3fn_decode(((const uint8_t*)k_cache)[elem + i]) * scale;
+}
+
+/* Write a processed K row back: bf16 round, or fp8 with the tensor scale, or
+ * (per-token) with a fresh scale fp32(max|y| / 448) that is stored too.
+ * Only the columns lo..hi-1 are written; the per-token statistic covers the
+ * whole row (columns left as they were keep their own values, re-encoded). */
+static void store_k_row(void* k_cache, int k_type, int scale_mode, int64_t elem, int64_t D,
+                        const double* y, float tensor_scale, float* token_scale,
+                        int64_t lo, int64_t hi) {
+  if (k_type == ORACLE_CACHE_BF16) {
+    for (int64_t i = lo; i < hi; ++i) ((uint16_t*)k_cache)[elem + i] = oracle_bf16_encode(y[i]);
+    return;
+  }
+  double s = (double)tensor_scale;
+  if (scale_mode == ORACLE_SCALE_PER_TOKEN) {
+    double amax = 0.0;
+    for (int64_t i = 0; i < D; ++i)
+      if (fabs(y[i]) > amax) amax = fabs(y[i]);
+    const float st = (float)(amax / 448.0);
+    *token_scale = st;
+    s = (double)st;
+  }
+  for (int64_t i = lo; i < hi; ++i)
+    ((uint8_t*)k_cache)[elem + i] = oracle_e4m3fn_encode_sat(s == 0.0 ? y[i] : y[i] / s);
+}
+
 int oracle_qk_rope_paged_ragged(
     uint16_t* q_out, const uint16_t* q_in, int64_t Hq, int64_t D,
     const uint32_t* row_offsets, const uint32_t* cache_lengths, int64_t B,
-    const uint32_t* page_table, int64_t pt_stride, uint16_t* k_cache,
-    int64_t num_layers, int64_t num_pages, int64_t page_size, int64_t Hkv,
-    int64_t layer_idx, const float* freqs, int64_t max_seq_len,
-    const uint32_t* position_ids, int interleaved, const uint16_t* k_gamma,
-    int64_t k_norm_cols, float epsilon) {
+    const uint32_t* page_table, int64_t pt_stride, void* k_cache, int k_type,
+    int scale_mode, float* k_scales, int64_t num_layers, int64_t num_pages,
+    int64_t page_size, int64_t Hkv, int64_t layer_idx, const float* freqs,
+    int64_t max_seq_len, const uint32_t* position_ids, int interleaved,
+    const uint16_t* k_gamma, int64_t k_norm_cols, float epsilon) {
   if (D <= 0 || D % 2 || D > 1024 || layer_idx < 0 || layer_idx >= num_layers ||
       page_size <= 0 || (k_gamma && (k_norm_cols <= 0 || k_norm_cols > D)))
     return ORACLE_BAD_ARG;
@@ -333,15 +367,19 @@ int oracle_qk_rope_paged_ragged(
         for (int64_t i = 0; i < D; ++i) dst[i] = oracle_bf16_encode(r[i]);
       }
       for (int64_t h = 0; h < Hkv; ++h) {
-        uint16_t* row = k_cache +
-            ((((layer_idx * num_pages + page) * page_size + off) * Hkv + h) * D);
-        for (int64_t i = 0; i < D; ++i) a[i] = oracle_bf16_decode(row[i]);
+        const int64_t head = ((layer_idx * num_pages + page) * page_size + off) * Hkv + h;
+        const double ks = k_type == ORACLE_CACHE_FP8
+            ? (double)(scale_mode == ORACLE_SCALE_PER_TOKEN ? k_scales[head] : k_scales[0])
+            : 1.0;
+        load_k_row(k_cache, k_type, head * D, D, ks, a);
         if (k_gamma) {
           double inv = oracle_inv_rms(a, k_norm_cols, eps);
           for (int64_t i = 0; i < k_norm_cols; ++i) a[i] = a[i] * inv * g[i];
         }
         oracle_rope_row(a, r, D, fr, interleaved);
-        for (int64_t i = 0; i < D; ++i) row[i] = oracle_bf16_encode(r[i]);
+        store_k_row(k_cache, k_type, scale_mode, head * D, D, r,
+                    k_type == ORACLE_CACHE_FP8 ? k_scales[0] : 1.0f,
+                    scale_mode == ORACLE_SCALE_PER_TOKEN ? &k_scales[head] : NULL, 0, D);
       }
     }
   }
@@ -420,15 +458,17 @@ int oracle_mla_gather_latent_paged(
  *   gamma     bf16 bits [gamma_len]
  */
 int oracle_rms_norm_kv_cache_paged(
-    uint16_t* k_cache, int64_t num_layers, int64_t num_pages, int64_t page_size,
-    int64_t Hkv, int64_t D, int64_t layer_idx, const uint32_t* row_offsets,
-    const uint32_t* cache_lengths, int64_t B, const uint32_t* page_table,
-    int64_t pt_stride, const uint16_t* gamma, int64_t gamma_len, float epsilon,
-    float weight_offset, int64_t total_seq_len, int multiply_before_cast) {
+    void* k_cache, int k_type, int scale_mode, float* k_scales, int64_t num_layers,
+    int64_t num_pages, int64_t page_size, int64_t Hkv, int64_t D, int64_t layer_idx,
+    const uint32_t* row_offsets, const uint32_t* cache_lengths, int64_t B,
+    const uint32_t* page_table, int64_t pt_stride, const uint16_t* gamma,
+    int64_t gamma_len, float epsilon, float weight_offset, int64_t total_seq_len,
+    int multiply_before_cast) {
   if (gamma_len <= 0 || gamma_len > D || D > 1024 || layer_idx < 0 ||
       layer_idx >= num_layers || page_size <= 0)
     return ORACLE_BAD_ARG;
   double a[1024], g[1024];
+  if (k_type == ORACLE_CACHE_FP8 && !multiply_before_cast) return ORACLE_BAD_ARG;
   for (int64_t k = 0; k < gamma_len; ++k)
     g[k] = oracle_bf16_decode(gamma[k]) + (double)weight_offset;
   const double eps = (double)epsilon;
@@ -443,18 +483,25 @@ int oracle_rms_norm_kv_cache_paged(
       if (page < 0) { status = ORACLE_BAD_PAGE; continue; }
       const int64_t off = slot % page_size;
       for (int64_t h = 0; h < Hkv; ++h) {
-        uint16_t* row = k_cache +
-            ((((layer_idx * num_pages + page) * page_size + off) * Hkv + h) * D);
-        for (int64_t i = 0; i < gamma_len; ++i) a[i] = oracle_bf16_decode(row[i]);
+        const int64_t head = ((layer_idx * num_pages + page) * page_size + off) * Hkv + h;
+        const double ks = k_type == ORACLE_CACHE_FP8
+            ? (double)(scale_mode == ORACLE_SCALE_PER_TOKEN ? k_scales[head] : k_scales[0])
+            : 1.0;
+        load_k_row(k_cache, k_type, head * D, D, ks, a);
         double inv = oracle_inv_rms(a, gamma_len, eps);
         for (int64_t i = 0; i < gamma_len; ++i) {
           if (multiply_before_cast) {
-            row[i] = oracle_bf16_encode(a[i] * inv * g[i]);
-          } else {
-            double n = oracle_bf16_decode(oracle_bf16_encode(a[i] * inv));
-            row[i] = oracle_bf16_encode(n * g[i]);
+            a[i] = a[i] * inv * g[i];
+          } else {  /* bf16 only: round the normalised value, then apply gamma */
+            a[i] = oracle_bf16_decode(oracle_bf16_encode(a[i] * inv)) * g[i];
           }
         }
+        /* only the normalised columns are written (per-token: the fresh scale
+         * covers the whole head, the other columns are re-encoded with it) */
+        const int per_token = k_type == ORACLE_CACHE_FP8 && scale_mode == ORACLE_SCALE_PER_TOKEN;
+        store_k_row(k_cache, k_type, scale_mode, head * D, D, a,
+                    k_type == ORACLE_CACHE_FP8 ? k_scales[0] : 1.0f,
+                    per_token ? &k_scales[head] : NULL, 0, per_token ? D : gamma_len);
       }
     }
   }

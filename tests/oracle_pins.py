@@ -635,6 +635,117 @@ def pin_rms_norm_kv(orc):
                     assert np.array_equal(k, expect), "kvnorm touched other elements"
 
 
+def small_qk_fp8_cases():
+    """fp8 K caches: per-tensor scale (interleaved, position ids, full-width
+    norm) and per-token scales (rotate-half, partial norm width)."""
+    yield workloads.build_qk("qk_fp8_tensor", 3011, [5, 0, 17, 1], [0, 4, 11, 31],
+                             Hq=4, Hkv=2, D=128, page_size=16, max_seq_len=4096,
+                             theta=500000.0, interleaved=True, with_position_ids=True,
+                             norm_cols=128, spare_pages=3, k_dtype="fp8",
+                             k_scale_mode="per_tensor")
+    yield workloads.build_qk("qk_fp8_token", 3012, [3, 9], [14, 0], Hq=3, Hkv=2, D=64,
+                             page_size=4, max_seq_len=64, theta=10000.0, interleaved=False,
+                             with_position_ids=False, norm_cols=40, spare_pages=2,
+                             k_dtype="fp8", k_scale_mode="per_token")
+
+
+def k_scale_of(case, page, off):
+    """Per-head dequantisation scales [Hkv] of one slot."""
+    if case.k_scale_mode == "per_token":
+        return case.k_scales[case.layer_idx, page, off].astype(np.float64)
+    return np.full(case.k_cache.shape[3], float(case.k_scales[0]))
+
+
+def check_fp8_k_rows(case, k_new, s_new, refs, what, cols=None):
+    """refs: (page, off) -> fp64 [Hkv, D] expected values.  Per-tensor: codes
+    are the correctly rounded values / scale; per-token: the stored scale is
+    fp32(max|y| / 448) per head and codes are values / that scale.  Columns
+    outside ``cols`` (per-tensor only) and every other slot are unchanged."""
+    L = case.layer_idx
+    expect = case.k_cache.copy()
+    expect_s = None if case.k_scales is None else case.k_scales.copy()
+    for (page, off), ref in refs.items():
+        lo, hi = (0, ref.shape[1]) if cols is None else cols
+        if case.k_scale_mode == "per_token":
+            amax = np.max(np.abs(ref), axis=1)
+            want_s = (amax / 448.0).astype(np.float32)
+            got_s = s_new[L, page, off]
+            assert np.all(np.abs(got_s.astype(np.float64) - want_s) <= 2.0 ** -23 * want_s), what
+            for h in range(ref.shape[0]):
+                sc = float(got_s[h])
+                assert_correctly_rounded(fp8_to_f64(k_new[L, page, off, h]), ref[h] / sc,
+                                         ulp_fp8, f"{what} token head {h}", sat=448.0)
+            expect[L, page, off] = k_new[L, page, off]
+            expect_s[L, page, off] = got_s
+        else:
+            sc = float(case.k_scales[0])
+            assert_correctly_rounded(fp8_to_f64(k_new[L, page, off][:, lo:hi]), ref[:, lo:hi] / sc,
+                                     ulp_fp8, f"{what} tensor", sat=448.0)
+            expect[L, page, off, :, lo:hi] = k_new[L, page, off, :, lo:hi]
+    assert np.array_equal(k_new, expect), f"{what}: K codes outside the written span changed"
+    if expect_s is not None and case.k_scale_mode == "per_token":
+        assert np.array_equal(s_new.view(np.uint32), expect_s.view(np.uint32)), f"{what}: scales"
+
+
+def pin_qk_fp8(orc):
+    for case in small_qk_fp8_cases():
+        for use_norm in (False, True):
+            q_out = np.zeros_like(case.q)
+            k = case.k_cache.copy()
+            ks = case.k_scales.copy()
+            orc.qk_rope_paged_ragged(q_out, case.q, case.row_offsets, case.cache_lengths,
+                                     case.page_table, k, case.layer_idx, case.freqs,
+                                     case.position_ids, case.interleaved,
+                                     case.gamma if use_norm else None, case.epsilon,
+                                     case.k_scale_mode, ks)
+            S = case.meta["page_size"]
+            owners = slot_owners(case.row_offsets, case.cache_lengths, case.page_table, S)
+            slot_of = {t: slot for (page, off), (t, slot) in owners.items()}
+            refs = {}
+            for (page, off), (t, slot) in owners.items():
+                pos = int(case.position_ids[t]) if case.position_ids is not None else slot
+                fr = case.freqs[pos].astype(np.float64)
+                x = fp8_to_f64(case.k_cache[case.layer_idx, page, off]) * \
+                    k_scale_of(case, page, off)[:, None]
+                if use_norm:
+                    C = case.gamma.size
+                    x[:, :C] = torch.nn.functional.rms_norm(
+                        torch.from_numpy(x[:, :C].copy()), (C,),
+                        weight=torch.from_numpy(bf16_to_f64(case.gamma)),
+                        eps=case.epsilon).numpy()
+                refs[(page, off)] = _complex_rope(x, fr[0::2][None, :], fr[1::2][None, :],
+                                                  case.interleaved)
+            check_fp8_k_rows(case, k, ks if case.k_scale_mode == "per_token" else None, refs,
+                             f"qk fp8 {case.name} norm={use_norm}")
+            _ = slot_of
+
+
+def pin_rms_norm_kv_fp8(orc):
+    for case in small_qk_fp8_cases():
+        C = case.gamma.size
+        k = case.k_cache.copy()
+        ks = case.k_scales.copy()
+        total = case.T - 2
+        orc.rms_norm_kv_cache_paged(k, case.layer_idx, case.row_offsets, case.cache_lengths,
+                                    case.page_table, case.gamma, case.epsilon, 0.25, total,
+                                    True, case.k_scale_mode, ks)
+        S = case.meta["page_size"]
+        owners = slot_owners(case.row_offsets, case.cache_lengths, case.page_table, S)
+        refs = {}
+        g = bf16_to_f64(case.gamma) + 0.25
+        for (page, off), (t, slot) in owners.items():
+            if t >= total:
+                continue
+            x = fp8_to_f64(case.k_cache[case.layer_idx, page, off]) * \
+                k_scale_of(case, page, off)[:, None]
+            x[:, :C] = torch.nn.functional.rms_norm(torch.from_numpy(x[:, :C].copy()), (C,),
+                                                    weight=torch.from_numpy(g),
+                                                    eps=case.epsilon).numpy()
+            refs[(page, off)] = x
+        check_fp8_k_rows(case, k, ks if case.k_scale_mode == "per_token" else None, refs,
+                         f"kvnorm fp8 {case.name}", cols=(0, C))
+
+
 def gather_case(kind: str, seed: int = 3101):
     """A paged latent cache holding whole request contexts: ``kind`` is
     "fp8_tensor", "fp8_token" or "bf16".  Cache bytes are finite values (no
@@ -723,5 +834,5 @@ ALL_PINS = [
     pin_rope_relative_position, pin_rope_interleaved_permutation,
     pin_rmsnorm_closed_forms, pin_rmsnorm_torch, pin_mla_composite,
     pin_mla_position0, pin_mla_zero_row_per_token, pin_qk_composite,
-    pin_rms_norm_kv, pin_gather,
+    pin_rms_norm_kv, pin_gather, pin_qk_fp8, pin_rms_norm_kv_fp8,
 ]

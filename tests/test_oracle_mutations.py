@@ -47,8 +47,8 @@ MUTANTS = [
      "dst[k] = oracle_e4m3fn_encode_sat(y[k] * s);"),
     ("mla_amax_nope_only", "for (int64_t k = 0; k < W; ++k)\n          if (fabs(y[k]) > amax)",
      "for (int64_t k = 0; k < Dn; ++k)\n          if (fabs(y[k]) > amax)"),
-    ("mla_token_scale_448", "const float st = (float)(amax / 448.0);",
-     "const float st = (float)(amax / 240.0);"),
+    ("mla_token_scale_448", "const float st = (float)(amax / 448.0); /* stored fp32",
+     "const float st = (float)(amax / 240.0); /* stored fp32"),
     ("page_offset", "const int64_t off = slot % page_size;\n      const float* fr = freqs + pos * R;",
      "const int64_t off = (slot + 1) % page_size;\n      const float* fr = freqs + pos * R;"),
     ("page_table_column", "int64_t col = slot / page_size;", "int64_t col = slot / page_size + 1;"),
@@ -82,6 +82,11 @@ MUTANTS = [
     ("gather_tensor_scale_only",
      "scale = (double)(scale_mode == ORACLE_SCALE_PER_TOKEN ? cache_scales[src_row]",
      "scale = (double)(scale_mode == ORACLE_SCALE_PER_TENSOR ? cache_scales[src_row]"),
+    ("k_fp8_ignores_scale",
+     ": oracle_e4m3fn_decode(((const uint8_t*)k_cache)[elem + i]) * scale;",
+     ": oracle_e4m3fn_decode(((const uint8_t*)k_cache)[elem + i]);"),
+    ("k_fp8_token_scale_stale", "    *token_scale = st;\n    s = (double)st;",
+     "    *token_scale = st;"),
     ("gather_quant_multiplies", "oracle_bf16_decode(bits) / (double)out_tensor_scale);",
      "oracle_bf16_decode(bits) * (double)out_tensor_scale);"),
 ]

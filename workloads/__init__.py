@@ -243,6 +243,8 @@ class QkCase:
     epsilon: float
     layer_idx: int
     meta: dict = field(default_factory=dict)
+    k_scale_mode: str = "none"   # fp8 K cache: "per_tensor" | "per_token"
+    k_scales: np.ndarray | None = None  # f32 [1] or [L, P, S, Hkv]
 
     @property
     def T(self) -> int:
@@ -253,11 +255,20 @@ class QkCase:
         return int(self.row_offsets.size - 1)
 
 
+def fp8_codes(x: np.ndarray) -> np.ndarray:
+    """E4M3FN codes of float32 values by torch's cast (inputs within +-448)."""
+    t = torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.float8_e4m3fn)
+    return t.view(torch.uint8).numpy().copy()
+
+
 def build_qk(name, seed, new_lens, prior_lens, Hq, Hkv, D, *, page_size,
              max_seq_len, theta, interleaved, with_position_ids,
              norm_cols=None, eps=1e-6, spare_pages=64, num_layers=2, layer_idx=1,
-             rng=None):
-    """Generic Q/K RoPE case; ``rng`` continues a preset's stream if given."""
+             rng=None, k_dtype="bf16", k_scale_mode="per_tensor", k_scale=0.05):
+    """Generic Q/K RoPE case; ``rng`` continues a preset's stream if given.
+    k_dtype "fp8": the K pool holds E4M3FN codes of N(0,1) values divided by
+    the scale -- one tensor scale, or per (slot, head) scales ~U(0.5, 1.5) x
+    k_scale (k_scale_mode "per_token")."""
     rng = make_rng(seed) if rng is None else rng
     offsets, clens, pt, P = ragged_batch(new_lens, prior_lens, page_size,
                                          spare_pages, rng)
@@ -266,7 +277,19 @@ def build_qk(name, seed, new_lens, prior_lens, Hq, Hkv, D, *, page_size,
     # The whole pool holds N(0,1) bf16 values, so the new K rows (written by a
     # preceding projection) are normal draws wherever they sit, and every other
     # slot is a finite value whose bits must survive the call unchanged.
-    k_cache = _normal_bf16(rng, (num_layers, P, page_size, Hkv, D))
+    k_shape = (num_layers, P, page_size, Hkv, D)
+    k_scales = None
+    if k_dtype == "bf16":
+        k_cache = _normal_bf16(rng, k_shape)
+        k_scale_mode = "none"
+    else:
+        x = rng.standard_normal(size=k_shape, dtype=np.float32)
+        if k_scale_mode == "per_token":
+            k_scales = (rng.uniform(0.5, 1.5, size=k_shape[:4]) * k_scale).astype(np.float32)
+            k_cache = fp8_codes(x / k_scales[..., None])
+        else:
+            k_scales = np.array([k_scale], np.float32)
+            k_cache = fp8_codes(x / k_scales[0])
     freqs = freqs_table(max_seq_len, D, theta)
     pos = None
     if with_position_ids:
@@ -279,7 +302,8 @@ def build_qk(name, seed, new_lens, prior_lens, Hq, Hkv, D, *, page_size,
                   position_ids=pos, interleaved=interleaved, gamma=gamma,
                   epsilon=float(np.float32(eps)), layer_idx=layer_idx,
                   meta=dict(page_size=page_size, num_pages=P, theta=theta,
-                            max_seq_len=max_seq_len))
+                            max_seq_len=max_seq_len),
+                  k_scale_mode=k_scale_mode, k_scales=k_scales)
 
 
 def qk_generic(seed: int = 1005) -> QkCase:
