@@ -163,8 +163,12 @@ int mla_rope_rmsnorm_quant(void* q_rope_out, int64_t qo_tok_stride, int64_t qo_h
  * rotated and rounded to bf16 once.
  *
  *   q_out, q_proj   bf16 [total_tokens][num_q_heads][head_dim] with strides
- *   k_cache         (host) descriptor: dtype BF16, scale mode NONE,
- *                   head_dim == the q head_dim
+ *   k_cache         (host) descriptor, head_dim == the q head_dim: dtype
+ *                   BF16 with scale mode NONE, or FP8_E4M3FN with
+ *                   PER_TENSOR (K = code * scales[0], re-encoded with the
+ *                   same scale) or PER_TOKEN (K = code * the slot/head
+ *                   scale; after the rotation the head's scale is replaced
+ *                   by max|y| / 448 and the head re-encoded with it)
  *   freqs_cis       fp32 [max_seq_len][head_dim]
  *   position_ids    u32 [total_tokens] or NULL
  *   k_norm_gamma    bf16 [k_norm_cols] or NULL; 0 < k_norm_cols <= head_dim
@@ -189,7 +193,11 @@ int qk_rope_paged_ragged(void* q_out, int64_t qo_tok_stride, int64_t qo_head_str
  * after the gamma product; 0 rounds x * r to bf16, then multiplies by
  * (gamma + weight_offset) and rounds again.
  *
- *   k_cache        (host) descriptor: dtype BF16, scale mode NONE
+ *   k_cache        (host) descriptor: BF16 + NONE, or FP8_E4M3FN with
+ *                  PER_TENSOR (normalised columns re-encoded with the tensor
+ *                  scale) or PER_TOKEN (the head's scale becomes max|y| / 448
+ *                  and the whole head is re-encoded with it); fp8 caches
+ *                  need multiply_before_cast != 0
  *   gamma          bf16 [gamma_len], 0 < gamma_len <= head_dim
  *   per_head_norm  must be non-zero (one norm per head); 0 returns
  *                  PKV_ERR_UNSUPPORTED

@@ -54,6 +54,28 @@ int check_cache(const pkv_paged_cache* c, uint32_t layer_idx, uint32_t batch_siz
 
 int launch_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH; }
 
+// Element encoding of a K cache for the sibling entry points; false if the
+// dtype / scale-mode pair is not one of bf16 + none, fp8 + tensor / token.
+bool k_mode_of(const pkv_paged_cache* c, pkv::KMode* km) {
+  if (c->dtype == PKV_DTYPE_BF16 && c->scale_mode == PKV_SCALE_NONE) {
+    *km = pkv::KMode::Bf16;
+  } else if (c->dtype == PKV_DTYPE_FP8_E4M3FN && c->scale_mode == PKV_SCALE_PER_TENSOR) {
+    *km = pkv::KMode::Fp8PerTensor;
+  } else if (c->dtype == PKV_DTYPE_FP8_E4M3FN && c->scale_mode == PKV_SCALE_PER_TOKEN) {
+    *km = pkv::KMode::Fp8PerToken;
+  } else {
+    return false;
+  }
+  return true;
+}
+
+// fp8 K scales: the tensor scale, or this layer's per-token (slot, head) block.
+float* k_scales_of(const pkv_paged_cache* c, uint32_t layer_idx, pkv::KMode km) {
+  if (km == pkv::KMode::Fp8PerToken)
+    return c->scales + (int64_t)layer_idx * c->num_pages * c->page_size * c->num_heads;
+  return c->scales;
+}
+
 // Heads per wave for the MLA kernel.  32 heads (4 instructions of 8 heads)
 // per wave measured best on 128-head prefill and decode batches: small
 // enough to keep 7 waves per SIMD resident and to spread a token over 4
@@ -158,8 +180,8 @@ int qk_rope_paged_ragged(void* q_out, int64_t qo_tok_stride, int64_t qo_head_str
                          void* stream) {
   if (k_cache == nullptr) return PKV_ERR_NULL;
   if (head_dim == 0 || head_dim % 2 != 0 || k_cache->head_dim != head_dim) return PKV_ERR_SHAPE;
-  if (k_cache->dtype != PKV_DTYPE_BF16 || k_cache->scale_mode != PKV_SCALE_NONE)
-    return PKV_ERR_DTYPE;
+  pkv::KMode km;
+  if (!k_mode_of(k_cache, &km)) return PKV_ERR_DTYPE;
   if (k_norm_gamma != nullptr && (k_norm_cols == 0 || k_norm_cols > head_dim))
     return PKV_ERR_SHAPE;
   if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
@@ -171,6 +193,7 @@ int qk_rope_paged_ragged(void* q_out, int64_t qo_tok_stride, int64_t qo_head_str
   if (total_tokens == 0) return PKV_OK;
   if (input_row_offsets == nullptr || freqs_cis == nullptr) return PKV_ERR_NULL;
   if (num_q_heads > 0 && (q_proj == nullptr || q_out == nullptr)) return PKV_ERR_NULL;
+  if (km != pkv::KMode::Bf16 && k_cache->scales == nullptr) return PKV_ERR_NULL;
   if (!aligned16(q_proj) || !aligned16(q_out) || !aligned16(freqs_cis) ||
       !aligned16(k_norm_gamma) || !mult(qo_tok_stride, 8) || !mult(qo_head_stride, 8) ||
       !mult(qi_tok_stride, 8) || !mult(qi_head_stride, 8))
@@ -195,9 +218,10 @@ int qk_rope_paged_ragged(void* q_out, int64_t qo_tok_stride, int64_t qo_head_str
   a.k_gamma = static_cast<const uint16_t*>(k_norm_gamma);
   a.k_norm_cols = k_norm_gamma ? k_norm_cols : 0;
   a.epsilon = epsilon;
+  a.k_scales = k_scales_of(k_cache, layer_idx, km);
   a.cache = view;
-  return launch_status(
-      pkv::launch_qk_rope(a, (int)head_dim, interleaved != 0, static_cast<hipStream_t>(stream)));
+  return launch_status(pkv::launch_qk_rope(a, (int)head_dim, interleaved != 0, km,
+                                           static_cast<hipStream_t>(stream)));
 }
 
 int rms_norm_kv_cache_paged(const pkv_paged_cache* k_cache, uint32_t layer_idx,
@@ -206,10 +230,11 @@ int rms_norm_kv_cache_paged(const pkv_paged_cache* k_cache, uint32_t layer_idx,
                             const uint32_t* input_row_offsets, uint32_t batch_size,
                             int per_head_norm, int multiply_before_cast, void* stream) {
   if (k_cache == nullptr) return PKV_ERR_NULL;
-  if (k_cache->dtype != PKV_DTYPE_BF16 || k_cache->scale_mode != PKV_SCALE_NONE)
-    return PKV_ERR_DTYPE;
+  pkv::KMode km;
+  if (!k_mode_of(k_cache, &km)) return PKV_ERR_DTYPE;
   if (gamma_len == 0 || gamma_len > k_cache->head_dim) return PKV_ERR_SHAPE;
   if (!per_head_norm) return PKV_ERR_UNSUPPORTED;
+  if (km != pkv::KMode::Bf16 && !multiply_before_cast) return PKV_ERR_UNSUPPORTED;
   if (k_cache->head_dim != 64 && k_cache->head_dim != 128) return PKV_ERR_UNSUPPORTED;
   if (total_seq_len > 0 && batch_size == 0) return PKV_ERR_SHAPE;
   CacheView view{};
@@ -217,6 +242,7 @@ int rms_norm_kv_cache_paged(const pkv_paged_cache* k_cache, uint32_t layer_idx,
   if (st != PKV_OK) return st;
   if (total_seq_len == 0) return PKV_OK;
   if (gamma == nullptr || input_row_offsets == nullptr) return PKV_ERR_NULL;
+  if (km != pkv::KMode::Bf16 && k_cache->scales == nullptr) return PKV_ERR_NULL;
   if (!aligned16(gamma)) return PKV_ERR_ALIGN;
 
   pkv::KvNormArgs a{};
@@ -227,10 +253,11 @@ int rms_norm_kv_cache_paged(const pkv_paged_cache* k_cache, uint32_t layer_idx,
   a.gamma_len = gamma_len;
   a.epsilon = epsilon;
   a.weight_offset = weight_offset;
+  a.k_scales = k_scales_of(k_cache, layer_idx, km);
   a.cache = view;
   a.head_dim = k_cache->head_dim;
-  return launch_status(
-      pkv::launch_kv_norm(a, multiply_before_cast != 0, static_cast<hipStream_t>(stream)));
+  return launch_status(pkv::launch_kv_norm(a, multiply_before_cast != 0, km,
+                                           static_cast<hipStream_t>(stream)));
 }
 
 int mla_gather_latent_paged(void* out, int32_t out_dtype, int64_t out_row_stride,

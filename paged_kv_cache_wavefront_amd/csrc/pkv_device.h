@@ -52,6 +52,20 @@ __device__ __forceinline__ uint32_t pack4_fp8(float a, float b, float c, float d
   return (uint32_t)w;
 }
 
+// 8 fp8 codes (two dwords) -> 8 fp32 values (exact; v_cvt_pk_f32_fp8).
+__device__ __forceinline__ void unpack8_fp8(uint32_t w0, uint32_t w1, float (&f)[8]) {
+  const uint32_t w[2] = {w0, w1};
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[q], false);
+    const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[q], true);
+    f[4 * q] = lo[0];
+    f[4 * q + 1] = lo[1];
+    f[4 * q + 2] = hi[0];
+    f[4 * q + 3] = hi[1];
+  }
+}
+
 __device__ __forceinline__ uint2 pack8_fp8(const float (&f)[8]) {
   return make_uint2(pack4_fp8(f[0], f[1], f[2], f[3]), pack4_fp8(f[4], f[5], f[6], f[7]));
 }

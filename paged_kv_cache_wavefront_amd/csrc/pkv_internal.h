@@ -8,6 +8,9 @@
 
 namespace pkv {
 
+// K cache element encoding of the sibling entry points.
+enum class KMode : int { Bf16 = 0, Fp8PerTensor = 1, Fp8PerToken = 2 };
+
 // Paged cache geometry of one layer, in elements of the cache type.
 struct CacheView {
   void* layer_base;            // data + layer_idx * layer_stride (in bytes)
@@ -60,12 +63,14 @@ struct QkArgs {
   const uint16_t* k_gamma;       // may be null
   uint32_t k_norm_cols;
   float epsilon;
-  CacheView cache;               // bf16 K cache
+  float* k_scales;               // fp8 K: tensor scale [1] or this layer's per-token scales
+  CacheView cache;               // K cache
 };
 
 // Q heads one wave of the Q/K kernel handles (head_dim 64 or 128).
 uint32_t qk_heads_per_wave(int head_dim);
-hipError_t launch_qk_rope(const QkArgs& a, int head_dim, bool interleaved, hipStream_t stream);
+hipError_t launch_qk_rope(const QkArgs& a, int head_dim, bool interleaved, KMode kmode,
+                          hipStream_t stream);
 
 struct KvNormArgs {
   uint32_t total_tokens;
@@ -74,11 +79,13 @@ struct KvNormArgs {
   const uint16_t* gamma;
   uint32_t gamma_len;
   float epsilon, weight_offset;
-  CacheView cache;               // bf16 K cache
+  float* k_scales;               // fp8 K: tensor scale [1] or this layer's per-token scales
+  CacheView cache;               // K cache
   uint32_t head_dim;
 };
 
-hipError_t launch_kv_norm(const KvNormArgs& a, bool multiply_before_cast, hipStream_t stream);
+hipError_t launch_kv_norm(const KvNormArgs& a, bool multiply_before_cast, KMode kmode,
+                          hipStream_t stream);
 
 struct GatherArgs {
   void* out;

@@ -151,7 +151,7 @@ __device__ __forceinline__ void q_rope(const char* src, char* dst, int64_t in_st
 
 // One wave per (token, chunk of Q heads); chunk 0 also rotates (and
 // optionally normalises) the token's K heads.
-template <int D, bool INTER, int NI>
+template <int D, bool INTER, int NI, KMode KM>
 __global__ __launch_bounds__(256) void qk_rope_kernel(const QkArgs a) {
   using Geo = Geometry<D, INTER>;
   constexpr int LP = Geo::kLanesPerHead, HPI = Geo::kHeadsPerInstr;
@@ -216,22 +216,48 @@ __global__ __launch_bounds__(256) void qk_rope_kernel(const QkArgs a) {
   if (chunk != 0) return;
 
   // ---- K (in place), optional per-head RMSNorm first ------------------------
+  // bf16: 16 bytes per lane; fp8: 8 bytes per lane (code * scale on load, a
+  // per-tensor cache re-encodes with its scale, a per-token cache stores a
+  // fresh max|y| / 448 per head).
+  constexpr int64_t EB = KM == KMode::Bf16 ? 2 : 1;
   const bool knorm = a.k_gamma != nullptr;
   const int C = (int)a.k_norm_cols;
   float g[8], gp[8];  // gamma of this lane's columns and of the partner's
   load_gamma8(a.k_gamma, col, C, knorm, g);
   load_gamma8(a.k_gamma, pcol, C, knorm && !INTER, gp);
   char* krow = static_cast<char*>(cv.layer_base) +
-               2 * ((int64_t)ps.page * cv.page_stride + (int64_t)ps.offset * cv.slot_stride);
-  const uint32_t k_off = 2 * (hl * (uint32_t)cv.head_stride + (uint32_t)col);
+               EB * ((int64_t)ps.page * cv.page_stride + (int64_t)ps.offset * cv.slot_stride);
+  const uint32_t k_off = (uint32_t)EB * (hl * (uint32_t)cv.head_stride + (uint32_t)col);
+  const int64_t slot_head0 = ((int64_t)ps.page * cv.page_size + ps.offset) * cv.num_heads;
+  float tensor_inv = 1.0f;
+  if constexpr (KM == KMode::Fp8PerTensor) tensor_inv = 1.0f / a.k_scales[0];
   for (uint32_t hbase = 0; hbase < cv.num_heads; hbase += HPI) {
-    const bool valid = hbase + hl < cv.num_heads;
-    char* p = krow + 2 * (int64_t)hbase * cv.head_stride + k_off;
-    uint4 kv = make_uint4(0, 0, 0, 0);
-    if (valid) kv = load16(p);
+    const uint32_t h = hbase + hl;
+    const bool valid = h < cv.num_heads;
+    char* p = krow + EB * (int64_t)hbase * cv.head_stride + k_off;
     float own[8], par[8] = {};
-    unpack8(kv, own);
-    if constexpr (!INTER) unpack8(mirror16<LP>(kv), par);
+    if constexpr (KM == KMode::Bf16) {
+      uint4 kv = make_uint4(0, 0, 0, 0);
+      if (valid) kv = load16(p);
+      unpack8(kv, own);
+      if constexpr (!INTER) unpack8(mirror16<LP>(kv), par);
+    } else {
+      uint2 kv = make_uint2(0, 0);
+      float ks = 0.0f;
+      if (valid) {
+        kv = *reinterpret_cast<const uint2*>(p);
+        ks = KM == KMode::Fp8PerTensor ? a.k_scales[0] : a.k_scales[slot_head0 + h];
+      }
+      unpack8_fp8(kv.x, kv.y, own);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) own[j] *= ks;
+      if constexpr (!INTER) {  // the partner lane belongs to the same head: same scale
+        constexpr int ctrl = LP == 8 ? 0x141 : 0x140;  // row_half_mirror / row_mirror
+        unpack8_fp8(dpp_u32<ctrl>(kv.x), dpp_u32<ctrl>(kv.y), par);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) par[j] *= ks;
+      }
+    }
     if (!knorm) {
       rotate_plain<INTER>(own, par, cs);
     } else {
@@ -244,7 +270,7 @@ __global__ __launch_bounds__(256) void qk_rope_kernel(const QkArgs a) {
       float pre_own[8], pre_par[8], post[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        own[j] *= g[j];  // exact (bf16 x bf16); g = 1 past C
+        own[j] *= g[j];  // exact for bf16 K (bf16 x bf16); g = 1 past C
         par[j] *= gp[j];
         // is this value / its pair partner inside the normalised span?
         const bool in_me = col + j < C;
@@ -255,20 +281,48 @@ __global__ __launch_bounds__(256) void qk_rope_kernel(const QkArgs a) {
       }
       rotate_scaled<INTER>(own, par, cs, pre_own, pre_par, post);
     }
-    if (valid) store16(p, pack8_bf16(own));
+    if constexpr (KM == KMode::Bf16) {
+      if (valid) store16(p, pack8_bf16(own));
+    } else {
+      float inv = tensor_inv;
+      if constexpr (KM == KMode::Fp8PerToken) {
+        float am = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(own[j]));
+        am = group_max<LP>(am);
+        const float st = am / 448.0f;
+        inv = st > 0.0f ? 1.0f / st : 0.0f;
+        if (valid && role.k == 0) a.k_scales[slot_head0 + h] = st;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) own[j] *= inv;
+      if (valid) *reinterpret_cast<uint2*>(p) = pack8_fp8(own);
+    }
   }
 }
 
-template <int D, bool INTER, int NI>
+template <int D, bool INTER, KMode KM>
 hipError_t launch_one(const QkArgs& a, uint32_t blocks, hipStream_t stream) {
-  hipLaunchKernelGGL((qk_rope_kernel<D, INTER, NI>), dim3(blocks), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((qk_rope_kernel<D, INTER, kQInstrPerWave, KM>), dim3(blocks), dim3(256), 0,
+                     stream, a);
   return hipGetLastError();
 }
 
+template <int D, bool INTER>
+hipError_t launch_k(const QkArgs& a, KMode km, uint32_t blocks, hipStream_t stream) {
+  switch (km) {
+    case KMode::Bf16: return launch_one<D, INTER, KMode::Bf16>(a, blocks, stream);
+    case KMode::Fp8PerTensor: return launch_one<D, INTER, KMode::Fp8PerTensor>(a, blocks, stream);
+    case KMode::Fp8PerToken: return launch_one<D, INTER, KMode::Fp8PerToken>(a, blocks, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
 template <int D>
-hipError_t launch_d(const QkArgs& a, bool interleaved, uint32_t blocks, hipStream_t stream) {
-  return interleaved ? launch_one<D, true, kQInstrPerWave>(a, blocks, stream)
-                     : launch_one<D, false, kQInstrPerWave>(a, blocks, stream);
+hipError_t launch_d(const QkArgs& a, bool interleaved, KMode km, uint32_t blocks,
+                    hipStream_t stream) {
+  return interleaved ? launch_k<D, true>(a, km, blocks, stream)
+                     : launch_k<D, false>(a, km, blocks, stream);
 }
 
 }  // namespace
@@ -277,14 +331,15 @@ hipError_t launch_d(const QkArgs& a, bool interleaved, uint32_t blocks, hipStrea
 // i.e. 4 KiB of Q per wave (16 heads of 128 or 32 heads of 64).
 uint32_t qk_heads_per_wave(int head_dim) { return (uint32_t)kQInstrPerWave * (512u / (uint32_t)head_dim); }
 
-hipError_t launch_qk_rope(const QkArgs& a, int head_dim, bool interleaved, hipStream_t stream) {
+hipError_t launch_qk_rope(const QkArgs& a, int head_dim, bool interleaved, KMode kmode,
+                          hipStream_t stream) {
   const uint64_t waves = (uint64_t)a.total_tokens * a.chunks;
   const uint64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffull) return hipErrorInvalidValue;
   const uint32_t nb = (uint32_t)blocks;
-  if (head_dim == 128) return launch_d<128>(a, interleaved, nb, stream);
-  if (head_dim == 64) return launch_d<64>(a, interleaved, nb, stream);
+  if (head_dim == 128) return launch_d<128>(a, interleaved, kmode, nb, stream);
+  if (head_dim == 64) return launch_d<64>(a, interleaved, kmode, nb, stream);
   return hipErrorInvalidValue;
 }
 

@@ -212,10 +212,23 @@ class QkDevice:
         self.freqs = dev_f32(case.freqs)
         self.pos = None if case.position_ids is None else dev_u32(case.position_ids)
         self.gamma = None if case.gamma is None else dev_bf16(case.gamma)
-        self.k = dev_bf16(case.k_cache)
         self.error_count = torch.zeros(1, dtype=torch.int32, device=DEV)
+        if case.k_cache.dtype == np.uint16:
+            self.k = dev_bf16(case.k_cache)
+            mode, self.k_scales = pkv.PKV_SCALE_NONE, None
+        else:
+            self.k = dev_u8(case.k_cache)
+            self.k_scales = dev_f32(case.k_scales)
+            mode = (pkv.PKV_SCALE_PER_TOKEN if case.k_scale_mode == "per_token"
+                    else pkv.PKV_SCALE_PER_TENSOR)
         self.desc = pkv.paged_cache(self.k, self.cache_lengths, self.page_table,
-                                    pkv.PKV_SCALE_NONE, None, self.error_count)
+                                    mode, self.k_scales, self.error_count)
+
+    def k_host(self):
+        torch.cuda.synchronize()
+        k = host_bf16(self.k) if self.case.k_cache.dtype == np.uint16 else host_u8(self.k)
+        ks = None if self.k_scales is None else host_f32(self.k_scales)
+        return k, ks
 
     def rope(self, with_norm: bool):
         import paged_kv_cache_wavefront_amd as pkv

@@ -62,13 +62,84 @@ def check_k_rows(case, k_gpu, k_orc, what, slack_rel=0.0, max_ulp=1):
 NORM_SLACK = 2.0 ** -18
 
 
-def oracle_qk(orc, case, with_norm):
+def oracle_qk(orc, case, with_norm, with_scales=False):
     q_out = np.zeros_like(case.q)
     k = case.k_cache.copy()
+    ks = None if case.k_scales is None else case.k_scales.copy()
     orc.qk_rope_paged_ragged(q_out, case.q, case.row_offsets, case.cache_lengths,
                              case.page_table, k, case.layer_idx, case.freqs, case.position_ids,
-                             case.interleaved, case.gamma if with_norm else None, case.epsilon)
-    return q_out, k
+                             case.interleaved, case.gamma if with_norm else None, case.epsilon,
+                             case.k_scale_mode, ks)
+    return (q_out, k, ks) if with_scales else (q_out, k)
+
+
+def check_fp8_k(case, k_gpu, ks_gpu, k_orc, ks_orc, what):
+    """fp8 K rows: codes within 1 step on at most 0.1 % of written bytes;
+    per-token scales within 1e-5 relative; everything else bit-exact."""
+    rows = gh.written_k_rows(case)
+    assert np.array_equal(k_gpu[~rows], case.k_cache[~rows]), f"{what}: untouched rows changed"
+    d = gh.fp8_ulp_diff(k_gpu[rows], k_orc[rows])
+    frac = float((d != 0).sum() / max(d.size, 1))
+    stats = dict(max_ulp=int(d.max(initial=0)), diff_frac=frac, n=d.size)
+    assert stats["max_ulp"] <= gh.FP8_MAX_ULP and frac <= gh.FP8_MAX_DIFF_FRAC, f"{what}: {stats}"
+    if case.k_scale_mode == "per_token":
+        assert np.array_equal(ks_gpu[~rows].view(np.uint32), case.k_scales[~rows].view(np.uint32))
+        sg, so = ks_gpu[rows].astype(np.float64), ks_orc[rows].astype(np.float64)
+        rel = np.abs(sg - so) / np.maximum(np.abs(so), 1e-30)
+        stats["scale_max_rel"] = float(rel.max(initial=0))
+        assert stats["scale_max_rel"] <= gh.SCALE_MAX_REL, f"{what}: {stats}"
+    else:
+        assert np.array_equal(ks_gpu, case.k_scales)
+    return stats
+
+
+def run_qk_fp8(orc, case, with_norm):
+    _say(f"[qk8] case={case.name} T={case.T} mode={case.k_scale_mode} norm={with_norm}")
+    dev = gh.QkDevice(case)
+    dev.rope(with_norm)
+    q = gh.host_bf16(dev.q_out)
+    k, ks = dev.k_host()
+    assert int(dev.error_count.item()) == 0
+    q_o, k_o, ks_o = oracle_qk(orc, case, with_norm, with_scales=True)
+    stats = {"q": gh.check_bf16(q, q_o, "q"), "k": check_fp8_k(case, k, ks, k_o, ks_o, "k")}
+    _say(f"[qk8] {case.name}: {stats}")
+
+
+@pytest.mark.parametrize("idx", range(2))
+@pytest.mark.parametrize("with_norm", [True, False])
+def test_fp8_k_small(orc, idx, with_norm):
+    run_qk_fp8(orc, list(oracle_pins.small_qk_fp8_cases())[idx], with_norm)
+
+
+@pytest.mark.parametrize("mode", ["per_tensor", "per_token"])
+def test_fp8_k_llama_shape(orc, mode):
+    """The Llama-shaped batch (19k tokens, Q 32 x 128, K 8 x 128, interleaved,
+    position ids, fused K norm) with an fp8 K cache."""
+    rng = workloads.make_rng(1005)
+    new = rng.integers(1, 1024, size=32, endpoint=True)
+    prior = rng.integers(0, 1023, size=32, endpoint=True)
+    case = workloads.build_qk(f"qk_generic_fp8_{mode}", 1005, new, prior, Hq=32, Hkv=8, D=128,
+                              page_size=16, max_seq_len=131072, theta=500000.0,
+                              interleaved=True, with_position_ids=True, norm_cols=128, rng=rng,
+                              k_dtype="fp8", k_scale_mode=mode)
+    run_qk_fp8(orc, case, True)
+
+
+@pytest.mark.parametrize("idx", range(2))
+def test_fp8_kv_norm(orc, idx):
+    case = list(oracle_pins.small_qk_fp8_cases())[idx]
+    total = case.T - 2
+    _say(f"[kvnorm8] case={case.name} mode={case.k_scale_mode} total={total}")
+    dev = gh.QkDevice(case)
+    dev.kv_norm(dev.gamma, 0.25, total, True)
+    k, ks = dev.k_host()
+    assert int(dev.error_count.item()) == 0
+    k_o = case.k_cache.copy()
+    ks_o = case.k_scales.copy()
+    orc.rms_norm_kv_cache_paged(k_o, case.layer_idx, case.row_offsets, case.cache_lengths,
+                                case.page_table, case.gamma, case.epsilon, 0.25, total, True,
+                                case.k_scale_mode, ks_o)
+    _say(f"[kvnorm8] {case.name}: {check_fp8_k(case, k, ks, k_o, ks_o, 'kvnorm fp8')}")
 
 
 def run_qk(orc, case, with_norm):
@@ -77,7 +148,7 @@ def run_qk(orc, case, with_norm):
     dev = gh.QkDevice(case)
     dev.rope(with_norm)
     q = gh.host_bf16(dev.q_out)
-    k = gh.host_bf16(dev.k)
+    k, _ = dev.k_host()
     assert int(dev.error_count.item()) == 0
     q_o, k_o = oracle_qk(orc, case, with_norm)
     stats = {"q": gh.check_bf16(q, q_o, "q")}
