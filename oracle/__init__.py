@@ -80,7 +80,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.oracle_qk_rope_paged_ragged.restype = ctypes.c_int
     lib.oracle_qk_rope_paged_ragged.argtypes = [
         _vp, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _i64, _vp, ctypes.c_int, ctypes.c_int,
-        _vp, _i64, _i64, _i64, _i64, _i64, _vp, _i64, _vp, ctypes.c_int, _vp, _i64,
+        _vp, _i64, _i64, _i64, _i64, _i64, _vp, _i64, _vp, _vp, ctypes.c_int, _vp, _i64,
         ctypes.c_float]
     lib.oracle_mla_gather_latent_paged.restype = ctypes.c_int
     lib.oracle_mla_gather_latent_paged.argtypes = [
@@ -202,13 +202,15 @@ class Oracle:
     def qk_rope_paged_ragged(self, q_out, q_in, row_offsets, cache_lengths,
                              page_table, k_cache, layer_idx, freqs, position_ids,
                              interleaved, k_gamma=None, epsilon=1e-6, k_scale_mode="none",
-                             k_scales=None):
+                             k_scales=None, mrope_section=None):
         """Fill ``q_out``; rotate (and optionally K-normalise) ``k_cache``.
 
         Shapes: q [T,Hq,D] u16; k_cache [L,P,S,Hkv,D] u16 (bf16) or u8 (fp8,
         with k_scale_mode "per_tensor" -> k_scales f32 [1], "per_token" ->
         k_scales f32 [L,P,S,Hkv], rewritten); freqs [max_seq,D] f32;
-        position_ids [T] u32 or None; k_gamma [C] u16 or None.
+        position_ids [T] u32 or None, or [3, T] u32 with mrope_section =
+        (temporal, height, width) pair counts summing to D/2; k_gamma [C]
+        u16 or None.
         """
         T, Hq, D = q_in.shape
         L, P, S, Hkv, Dk = k_cache.shape
@@ -217,12 +219,16 @@ class Oracle:
         B = row_offsets.size - 1
         k_type = CACHE_BF16 if k_cache.dtype == np.uint16 else CACHE_FP8
         mode = {"per_tensor": SCALE_PER_TENSOR, "per_token": SCALE_PER_TOKEN, "none": 0}[k_scale_mode]
+        sec = None if mrope_section is None else np.asarray(mrope_section, np.int64)
+        if sec is not None and (position_ids is None or position_ids.shape != (3, T)):
+            raise ValueError("multimodal RoPE needs position ids of shape [3, T]")
         rc = self.lib.oracle_qk_rope_paged_ragged(
             _ptr(q_out, np.uint16), _ptr(q_in, np.uint16), Hq, D,
             _ptr(row_offsets, np.uint32), _ptr(cache_lengths, np.uint32), B,
             _ptr(page_table, np.uint32), page_table.shape[1], _ptr(k_cache, k_cache.dtype),
             k_type, mode, _ptr(k_scales, np.float32), L, P, S, Hkv, int(layer_idx),
             _ptr(freqs, np.float32), freqs.shape[0], _ptr(position_ids, np.uint32),
+            None if sec is None else sec.ctypes.data,
             int(bool(interleaved)), _ptr(k_gamma, np.uint16),
             0 if k_gamma is None else k_gamma.size, float(epsilon))
         _check(rc, "qk_rope_paged_ragged")

@@ -336,12 +336,18 @@ int oracle_qk_rope_paged_ragged(
     const uint32_t* page_table, int64_t pt_stride, void* k_cache, int k_type,
     int scale_mode, float* k_scales, int64_t num_layers, int64_t num_pages,
     int64_t page_size, int64_t Hkv, int64_t layer_idx, const float* freqs,
-    int64_t max_seq_len, const uint32_t* position_ids, int interleaved,
-    const uint16_t* k_gamma, int64_t k_norm_cols, float epsilon) {
+    int64_t max_seq_len, const uint32_t* position_ids, const int64_t* mrope_section,
+    int interleaved, const uint16_t* k_gamma, int64_t k_norm_cols, float epsilon) {
   if (D <= 0 || D % 2 || D > 1024 || layer_idx < 0 || layer_idx >= num_layers ||
       page_size <= 0 || (k_gamma && (k_norm_cols <= 0 || k_norm_cols > D)))
     return ORACLE_BAD_ARG;
+  if (mrope_section && (!position_ids || mrope_section[0] < 0 || mrope_section[1] < 0 ||
+                        mrope_section[2] < 0 ||
+                        mrope_section[0] + mrope_section[1] + mrope_section[2] != D / 2))
+    return ORACLE_BAD_ARG;
   double a[1024], r[1024], g[1024];
+  float mixed[1024];  /* multimodal: per-pair cos/sin gathered from three rows */
+  int64_t T = row_offsets[B];
   if (k_gamma)
     for (int64_t k = 0; k < k_norm_cols; ++k) g[k] = oracle_bf16_decode(k_gamma[k]);
   const double eps = (double)epsilon;
@@ -358,6 +364,21 @@ int oracle_qk_rope_paged_ragged(
       if (page < 0) { status = ORACLE_BAD_PAGE; continue; }
       const int64_t off = slot % page_size;
       const float* fr = freqs + pos * D;
+      if (mrope_section) {
+        /* [QK] Parameters, mrope_section: pair i of section k (temporal,
+         * height, width) is rotated by the angle of position row k. */
+        int bad = 0;
+        for (int64_t i = 0; i < D / 2; ++i) {
+          const int64_t k = i < mrope_section[0] ? 0
+                            : i < mrope_section[0] + mrope_section[1] ? 1 : 2;
+          const int64_t pk = (int64_t)position_ids[k * T + t];
+          if (pk >= max_seq_len) { bad = 1; break; }
+          mixed[2 * i] = freqs[pk * D + 2 * i];
+          mixed[2 * i + 1] = freqs[pk * D + 2 * i + 1];
+        }
+        if (bad) { status = ORACLE_BAD_POSITION; continue; }
+        fr = mixed;
+      }
 
       for (int64_t h = 0; h < Hq; ++h) {
         const uint16_t* src = q_in + (t * Hq + h) * D;

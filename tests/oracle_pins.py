@@ -746,6 +746,65 @@ def pin_rms_norm_kv_fp8(orc):
                          f"kvnorm fp8 {case.name}", cols=(0, C))
 
 
+def small_mrope_cases():
+    """Multimodal RoPE: sections over 64 pairs (D = 128), both rope styles."""
+    yield workloads.build_qk("mrope_inter", 3201, [4, 0, 11, 2], [0, 3, 7, 20], Hq=3, Hkv=2,
+                             D=128, page_size=8, max_seq_len=512, theta=10000.0,
+                             interleaved=True, with_position_ids=True, norm_cols=None,
+                             spare_pages=2, mrope_section=(16, 24, 24))
+    yield workloads.build_qk("mrope_half", 3202, [6, 5], [1, 12], Hq=2, Hkv=1, D=128,
+                             page_size=16, max_seq_len=512, theta=10000.0, interleaved=False,
+                             with_position_ids=True, norm_cols=128, spare_pages=1,
+                             mrope_section=(8, 40, 16))
+
+
+def run_qk_oracle(orc, case, with_norm, position_ids=None, mrope_section="case"):
+    q_out = np.zeros_like(case.q)
+    k = case.k_cache.copy()
+    orc.qk_rope_paged_ragged(
+        q_out, case.q, case.row_offsets, case.cache_lengths, case.page_table, k,
+        case.layer_idx, case.freqs,
+        case.position_ids if position_ids is None else position_ids, case.interleaved,
+        case.gamma if with_norm else None, case.epsilon,
+        mrope_section=case.mrope_section if mrope_section == "case" else mrope_section)
+    return q_out, k
+
+
+def pin_mrope(orc):
+    """Multimodal RoPE: with three equal position rows it is plain RoPE at that
+    position (bit-exact); in general every pair is rotated by the angle of its
+    section's row (numpy complex reference, correct rounding)."""
+    for case in small_mrope_cases():
+        with_norm = case.gamma is not None
+        same = np.repeat(case.position_ids[:1], 3, axis=0)
+        q1, k1 = run_qk_oracle(orc, case, with_norm, position_ids=same)
+        q2, k2 = run_qk_oracle(orc, case, with_norm, position_ids=same[0].copy(),
+                               mrope_section=None)
+        assert np.array_equal(q1, q2) and np.array_equal(k1, k2), "equal rows != plain"
+        q, k = run_qk_oracle(orc, case, with_norm)
+        D = case.q.shape[2]
+        s0, s1, _ = case.mrope_section
+        sec = np.where(np.arange(D // 2) < s0, 0, np.where(np.arange(D // 2) < s0 + s1, 1, 2))
+        pos = case.position_ids[sec, :].T.astype(np.int64)          # [T, D/2]
+        fr = case.freqs.astype(np.float64)
+        cs = fr[pos, 2 * np.arange(D // 2)[None, :]]
+        sn = fr[pos, 2 * np.arange(D // 2)[None, :] + 1]
+        q_ref = _complex_rope(bf16_to_f64(case.q), cs[:, None, :], sn[:, None, :], case.interleaved)
+        assert_correctly_rounded(bf16_to_f64(q), q_ref, ulp_bf16, "mrope q")
+        owners = slot_owners(case.row_offsets, case.cache_lengths, case.page_table,
+                             case.meta["page_size"])
+        for (page, off), (t, slot) in owners.items():
+            x = bf16_to_f64(case.k_cache[case.layer_idx, page, off])
+            if with_norm:
+                C = case.gamma.size
+                x[:, :C] = torch.nn.functional.rms_norm(
+                    torch.from_numpy(x[:, :C].copy()), (C,),
+                    weight=torch.from_numpy(bf16_to_f64(case.gamma)), eps=case.epsilon).numpy()
+            ref = _complex_rope(x, cs[t][None, :], sn[t][None, :], case.interleaved)
+            assert_correctly_rounded(bf16_to_f64(k[case.layer_idx, page, off]), ref, ulp_bf16,
+                                     "mrope k")
+
+
 def gather_case(kind: str, seed: int = 3101):
     """A paged latent cache holding whole request contexts: ``kind`` is
     "fp8_tensor", "fp8_token" or "bf16".  Cache bytes are finite values (no
@@ -834,5 +893,5 @@ ALL_PINS = [
     pin_rope_relative_position, pin_rope_interleaved_permutation,
     pin_rmsnorm_closed_forms, pin_rmsnorm_torch, pin_mla_composite,
     pin_mla_position0, pin_mla_zero_row_per_token, pin_qk_composite,
-    pin_rms_norm_kv, pin_gather, pin_qk_fp8, pin_rms_norm_kv_fp8,
+    pin_rms_norm_kv, pin_gather, pin_qk_fp8, pin_rms_norm_kv_fp8, pin_mrope,
 ]

@@ -87,6 +87,10 @@ MUTANTS = [
      ": oracle_e4m3fn_decode(((const uint8_t*)k_cache)[elem + i]);"),
     ("k_fp8_token_scale_stale", "    *token_scale = st;\n    s = (double)st;",
      "    *token_scale = st;"),
+    ("mrope_section_boundary", "const int64_t k = i < mrope_section[0] ? 0",
+     "const int64_t k = i <= mrope_section[0] ? 0"),
+    ("mrope_row_layout", "const int64_t pk = (int64_t)position_ids[k * T + t];",
+     "const int64_t pk = (int64_t)position_ids[t * 3 + k];"),
     ("gather_quant_multiplies", "oracle_bf16_decode(bits) / (double)out_tensor_scale);",
      "oracle_bf16_decode(bits) * (double)out_tensor_scale);"),
 ]

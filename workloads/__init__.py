@@ -245,6 +245,7 @@ class QkCase:
     meta: dict = field(default_factory=dict)
     k_scale_mode: str = "none"   # fp8 K cache: "per_tensor" | "per_token"
     k_scales: np.ndarray | None = None  # f32 [1] or [L, P, S, Hkv]
+    mrope_section: tuple | None = None  # (temporal, height, width) pair counts
 
     @property
     def T(self) -> int:
@@ -264,7 +265,8 @@ def fp8_codes(x: np.ndarray) -> np.ndarray:
 def build_qk(name, seed, new_lens, prior_lens, Hq, Hkv, D, *, page_size,
              max_seq_len, theta, interleaved, with_position_ids,
              norm_cols=None, eps=1e-6, spare_pages=64, num_layers=2, layer_idx=1,
-             rng=None, k_dtype="bf16", k_scale_mode="per_tensor", k_scale=0.05):
+             rng=None, k_dtype="bf16", k_scale_mode="per_tensor", k_scale=0.05,
+             mrope_section=None):
     """Generic Q/K RoPE case; ``rng`` continues a preset's stream if given.
     k_dtype "fp8": the K pool holds E4M3FN codes of N(0,1) values divided by
     the scale -- one tensor scale, or per (slot, head) scales ~U(0.5, 1.5) x
@@ -292,7 +294,9 @@ def build_qk(name, seed, new_lens, prior_lens, Hq, Hkv, D, *, page_size,
             k_cache = fp8_codes(x / k_scales[0])
     freqs = freqs_table(max_seq_len, D, theta)
     pos = None
-    if with_position_ids:
+    if mrope_section is not None:
+        pos = rng.integers(0, max_seq_len - 1, size=(3, T), endpoint=True).astype(np.uint32)
+    elif with_position_ids:
         pos = rng.integers(0, max_seq_len - 1, size=T, endpoint=True).astype(np.uint32)
     gamma = None
     if norm_cols is not None:
@@ -303,7 +307,8 @@ def build_qk(name, seed, new_lens, prior_lens, Hq, Hkv, D, *, page_size,
                   epsilon=float(np.float32(eps)), layer_idx=layer_idx,
                   meta=dict(page_size=page_size, num_pages=P, theta=theta,
                             max_seq_len=max_seq_len),
-                  k_scale_mode=k_scale_mode, k_scales=k_scales)
+                  k_scale_mode=k_scale_mode, k_scales=k_scales,
+                  mrope_section=None if mrope_section is None else tuple(mrope_section))
 
 
 def qk_generic(seed: int = 1005) -> QkCase:
