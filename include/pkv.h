@@ -156,6 +156,10 @@ int mla_rope_rmsnorm_quant(void* q_rope_out, int64_t qo_tok_stride, int64_t qo_h
  * Paged-ragged fused Q/K RoPE.  Q is rotated into q_out; the K rows of the
  * new tokens (slot cache_lengths[b] + j) are rotated in place for every KV
  * head.  Position = position_ids[t] when position_ids != NULL, else the slot.
+ * Multimodal RoPE (mrope_section != NULL, three host values summing to
+ * head_dim/2: temporal, height, width pair counts): position_ids is
+ * [3][total_tokens] and pair i is rotated by the angle of the row of its
+ * section (page "generic_fused_qk_rope_bshd_paged_ragged", Parameters).
  * interleaved != 0 rotates adjacent pairs (2i, 2i+1), otherwise pairs
  * (i, i + head_dim/2); pair i always uses freqs_cis columns 2i, 2i+1.
  * With k_norm_gamma != NULL, each K head's first k_norm_cols columns are
@@ -170,7 +174,9 @@ int mla_rope_rmsnorm_quant(void* q_rope_out, int64_t qo_tok_stride, int64_t qo_h
  *                   scale; after the rotation the head's scale is replaced
  *                   by max|y| / 448 and the head re-encoded with it)
  *   freqs_cis       fp32 [max_seq_len][head_dim]
- *   position_ids    u32 [total_tokens] or NULL
+ *   position_ids    u32 [total_tokens] or NULL ([3][total_tokens] with
+ *                   mrope_section)
+ *   mrope_section   (host) u32 [3] or NULL
  *   k_norm_gamma    bf16 [k_norm_cols] or NULL; 0 < k_norm_cols <= head_dim
  * Supported here: head_dim 64 or 128.
  */
@@ -180,9 +186,9 @@ int qk_rope_paged_ragged(void* q_out, int64_t qo_tok_stride, int64_t qo_head_str
                          const uint32_t* input_row_offsets, uint32_t batch_size,
                          const pkv_paged_cache* k_cache, uint32_t layer_idx,
                          const float* freqs_cis, uint32_t max_seq_len,
-                         const uint32_t* position_ids, int interleaved,
-                         const void* k_norm_gamma, uint32_t k_norm_cols, float epsilon,
-                         void* stream);
+                         const uint32_t* position_ids, const uint32_t* mrope_section,
+                         int interleaved, const void* k_norm_gamma, uint32_t k_norm_cols,
+                         float epsilon, void* stream);
 
 /*
  * In-place RMSNorm of the new K-cache rows.  Tokens t < total_seq_len (host

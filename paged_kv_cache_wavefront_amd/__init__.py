@@ -77,7 +77,7 @@ def _load() -> ctypes.CDLL:
         cache_p, u32, vp]
     lib.qk_rope_paged_ragged.restype = ctypes.c_int
     lib.qk_rope_paged_ragged.argtypes = [
-        vp, i64, i64, vp, i64, i64, u32, u32, u32, vp, u32, cache_p, u32, vp, u32, vp,
+        vp, i64, i64, vp, i64, i64, u32, u32, u32, vp, u32, cache_p, u32, vp, u32, vp, vp,
         ctypes.c_int, vp, u32, f32, vp]
     lib.rms_norm_kv_cache_paged.restype = ctypes.c_int
     lib.rms_norm_kv_cache_paged.argtypes = [
@@ -172,15 +172,20 @@ def qk_rope_paged_ragged(q_out: torch.Tensor, q_proj: torch.Tensor,
                          layer_idx: int, freqs_cis: torch.Tensor,
                          position_ids: torch.Tensor | None, interleaved: bool,
                          k_norm_gamma: torch.Tensor | None = None, epsilon: float = 1e-6,
-                         stream=None) -> None:
+                         stream=None, mrope_section=None) -> None:
     """Paged-ragged fused Q/K RoPE (C: ``qk_rope_paged_ragged``).  Q tensors
-    are ``[tokens, heads, head_dim]`` bf16; K is rotated in place."""
+    are ``[tokens, heads, head_dim]`` bf16; K is rotated in place.
+    ``mrope_section``: three ints (temporal, height, width pair counts) with
+    ``position_ids`` of shape [3, tokens]."""
     T, Hq, D = q_proj.shape
+    sec = None
+    if mrope_section is not None:
+        sec = (ctypes.c_uint32 * 3)(*[int(v) for v in mrope_section])
     st = _lib.qk_rope_paged_ragged(
         _ptr(q_out), q_out.stride(0), q_out.stride(1), _ptr(q_proj), q_proj.stride(0),
         q_proj.stride(1), T, Hq, D, _ptr(input_row_offsets), input_row_offsets.numel() - 1,
         ctypes.byref(k_cache), int(layer_idx), _ptr(freqs_cis), freqs_cis.shape[0],
-        _ptr(position_ids), int(bool(interleaved)), _ptr(k_norm_gamma),
+        _ptr(position_ids), sec, int(bool(interleaved)), _ptr(k_norm_gamma),
         0 if k_norm_gamma is None else k_norm_gamma.numel(), float(epsilon), _stream(stream))
     _check("qk_rope_paged_ragged", st)
 

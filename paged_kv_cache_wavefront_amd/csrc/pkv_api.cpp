@@ -175,10 +175,13 @@ int qk_rope_paged_ragged(void* q_out, int64_t qo_tok_stride, int64_t qo_head_str
                          const uint32_t* input_row_offsets, uint32_t batch_size,
                          const pkv_paged_cache* k_cache, uint32_t layer_idx,
                          const float* freqs_cis, uint32_t max_seq_len,
-                         const uint32_t* position_ids, int interleaved,
-                         const void* k_norm_gamma, uint32_t k_norm_cols, float epsilon,
-                         void* stream) {
+                         const uint32_t* position_ids, const uint32_t* mrope_section,
+                         int interleaved, const void* k_norm_gamma, uint32_t k_norm_cols,
+                         float epsilon, void* stream) {
   if (k_cache == nullptr) return PKV_ERR_NULL;
+  if (mrope_section != nullptr &&
+      (uint64_t)mrope_section[0] + mrope_section[1] + mrope_section[2] != head_dim / 2)
+    return PKV_ERR_SHAPE;
   if (head_dim == 0 || head_dim % 2 != 0 || k_cache->head_dim != head_dim) return PKV_ERR_SHAPE;
   pkv::KMode km;
   if (!k_mode_of(k_cache, &km)) return PKV_ERR_DTYPE;
@@ -194,6 +197,7 @@ int qk_rope_paged_ragged(void* q_out, int64_t qo_tok_stride, int64_t qo_head_str
   if (input_row_offsets == nullptr || freqs_cis == nullptr) return PKV_ERR_NULL;
   if (num_q_heads > 0 && (q_proj == nullptr || q_out == nullptr)) return PKV_ERR_NULL;
   if (km != pkv::KMode::Bf16 && k_cache->scales == nullptr) return PKV_ERR_NULL;
+  if (mrope_section != nullptr && position_ids == nullptr) return PKV_ERR_NULL;
   if (!aligned16(q_proj) || !aligned16(q_out) || !aligned16(freqs_cis) ||
       !aligned16(k_norm_gamma) || !mult(qo_tok_stride, 8) || !mult(qo_head_stride, 8) ||
       !mult(qi_tok_stride, 8) || !mult(qi_head_stride, 8))
@@ -215,6 +219,11 @@ int qk_rope_paged_ragged(void* q_out, int64_t qo_tok_stride, int64_t qo_head_str
   a.freqs = freqs_cis;
   a.max_seq_len = max_seq_len;
   a.position_ids = position_ids;
+  a.mrope = mrope_section != nullptr;
+  if (a.mrope) {
+    a.mrope_end0 = mrope_section[0];
+    a.mrope_end1 = mrope_section[0] + mrope_section[1];
+  }
   a.k_gamma = static_cast<const uint16_t*>(k_norm_gamma);
   a.k_norm_cols = k_norm_gamma ? k_norm_cols : 0;
   a.epsilon = epsilon;

@@ -59,7 +59,9 @@ struct QkArgs {
   uint32_t batch;
   const float* freqs;
   uint32_t max_seq_len;
-  const uint32_t* position_ids;  // may be null
+  const uint32_t* position_ids;  // may be null; [3][total_tokens] with mrope
+  uint32_t mrope;                // 1: multimodal RoPE with the two section ends below
+  uint32_t mrope_end0, mrope_end1;  // pairs [0,end0) temporal, [end0,end1) height, rest width
   const uint16_t* k_gamma;       // may be null
   uint32_t k_norm_cols;
   float epsilon;

@@ -18,6 +18,9 @@
 // Pair i needs freqs columns 2i, 2i+1: 8 or 16 consecutive floats per lane,
 // loaded once per token.  Q is read with non-temporal loads.
 //
+// Multimodal RoPE: three position rows; pair i uses the row of its section
+// (temporal / height / width pair ranges), cos/sin fetched per pair.
+//
 // Optional K norm: r = 1/sqrt(mean(x^2) + eps) over the first C columns of a
 // head (DPP sum over the head's lanes).  Normalised values enter the rotation
 // as x * gamma (exact in fp32) and r is applied after it, so an fp32 rounding
@@ -177,21 +180,38 @@ __global__ __launch_bounds__(256) void qk_rope_kernel(const QkArgs a) {
   const uint32_t qo_off = 2 * (hl * (uint32_t)a.qo_head + (uint32_t)col);
   const int64_t qi_step = 2 * HPI * a.qi_head, qo_step = 2 * HPI * a.qo_head;
 
-  // ---- address chain: round 1 = {position id, offsets, prior lengths};
-  //      round 2 = {freqs row, page-table entry} ---------------------------------
+  // ---- address chain: round 1 = {position id(s), offsets, prior lengths};
+  //      round 2 = {freqs row(s), page-table entry} ---------------------------------
   const CacheView& cv = a.cache;
-  uint32_t pos_id = 0;
-  if (a.position_ids != nullptr) pos_id = uniform(a.position_ids[t]);
+  uint32_t pid[3] = {0, 0, 0};
+  if (a.position_ids != nullptr) {
+    pid[0] = uniform(a.position_ids[t]);
+    if (a.mrope) {
+      pid[1] = uniform(a.position_ids[(uint64_t)a.total_tokens + t]);
+      pid[2] = uniform(a.position_ids[2 * (uint64_t)a.total_tokens + t]);
+    }
+  }
   const TokenSlot ts = find_slot(a.offsets, a.batch, cv.cache_lengths, t, lane);
-  const uint32_t pos = a.position_ids != nullptr ? pos_id : ts.slot;
-  const bool pos_ok = ts.ok && pos < a.max_seq_len;
+  const uint32_t pos = a.position_ids != nullptr ? pid[0] : ts.slot;
+  bool pos_ok = ts.ok && pos < a.max_seq_len;
+  if (a.mrope) pos_ok = pos_ok && pid[1] < a.max_seq_len && pid[2] < a.max_seq_len;
   float cs[Geo::kCs];
-  if (pos_ok) {
+  if (pos_ok && !a.mrope) {
     const float4* fr = reinterpret_cast<const float4*>(a.freqs + (int64_t)pos * D + role.cs_base);
 #pragma unroll
     for (int i = 0; i < Geo::kCs / 4; ++i) {
       const float4 v = fr[i];
       cs[4 * i] = v.x; cs[4 * i + 1] = v.y; cs[4 * i + 2] = v.z; cs[4 * i + 3] = v.w;
+    }
+  } else if (pos_ok) {
+    // multimodal RoPE: pair i takes cos/sin from the row of its section
+#pragma unroll
+    for (int j = 0; j < Geo::kCs / 2; ++j) {
+      const uint32_t i = (uint32_t)role.cs_base / 2 + j;
+      const uint32_t p = i < a.mrope_end0 ? pid[0] : (i < a.mrope_end1 ? pid[1] : pid[2]);
+      const float2 v = *reinterpret_cast<const float2*>(a.freqs + (int64_t)p * D + 2 * i);
+      cs[2 * j] = v.x;
+      cs[2 * j + 1] = v.y;
     }
   }
   PageSlot ps{};

@@ -235,7 +235,8 @@ class QkDevice:
         pkv.qk_rope_paged_ragged(self.q_out, self.q_in, self.offsets, self.desc,
                                  self.case.layer_idx, self.freqs, self.pos,
                                  self.case.interleaved,
-                                 self.gamma if with_norm else None, self.case.epsilon)
+                                 self.gamma if with_norm else None, self.case.epsilon,
+                                 mrope_section=self.case.mrope_section)
 
     def kv_norm(self, gamma: torch.Tensor, weight_offset=0.0, total=None, mbc=True):
         import paged_kv_cache_wavefront_amd as pkv

@@ -111,11 +111,13 @@ def kcache(pkv, **kw):
     return pkv.PagedCache(**base)
 
 
-def call_qk(pkv, cache, T=16, Hq=32, D=128, gamma=None, cols=0, layer=1, q=FAKE):
+def call_qk(pkv, cache, T=16, Hq=32, D=128, gamma=None, cols=0, layer=1, q=FAKE, pos=None,
+            mrope=None):
     lib = pkv.library()
     cp = None if cache is None else ctypes.byref(cache)
+    sec = None if mrope is None else (ctypes.c_uint32 * 3)(*mrope)
     return lib.qk_rope_paged_ragged(FAKE, Hq * D, D, q, Hq * D, D, T, Hq, D, FAKE, 2, cp, layer,
-                                    FAKE, 4096, None, 1, gamma, cols, 1e-6, None)
+                                    FAKE, 4096, pos, sec, 1, gamma, cols, 1e-6, None)
 
 
 def test_qk_validation(pkv):
@@ -130,6 +132,12 @@ def test_qk_validation(pkv):
     assert call_qk(pkv, kcache(pkv), q=FAKE + 4) == ALIGN
     assert call_qk(pkv, kcache(pkv), gamma=FAKE + 2, cols=128) == ALIGN
     assert call_qk(pkv, kcache(pkv), T=0) == OK
+    # fp8 K caches need their scales; multimodal sections must cover D/2 pairs
+    assert call_qk(pkv, kcache(pkv, dtype=pkv.PKV_DTYPE_FP8_E4M3FN,
+                               scale_mode=pkv.PKV_SCALE_PER_TOKEN, head_stride=128)) == NULL
+    assert call_qk(pkv, kcache(pkv), mrope=(16, 24, 23), pos=FAKE) == SHAPE
+    assert call_qk(pkv, kcache(pkv), mrope=(16, 24, 24), pos=None) == NULL
+    assert call_qk(pkv, kcache(pkv), mrope=(16, 24, 24), pos=FAKE, T=0) == OK
 
 
 def call_norm(pkv, cache, gamma_len=128, per_head=1, T=16, gamma=FAKE):
@@ -149,6 +157,12 @@ def test_kv_norm_validation(pkv):
     assert call_norm(pkv, kcache(pkv), gamma=None) == NULL
     assert call_norm(pkv, kcache(pkv), gamma=FAKE + 2) == ALIGN
     assert call_norm(pkv, kcache(pkv), T=0) == OK
+    fp8 = dict(dtype=pkv.PKV_DTYPE_FP8_E4M3FN, scale_mode=pkv.PKV_SCALE_PER_TENSOR)
+    assert call_norm(pkv, kcache(pkv, **fp8)) == NULL                      # no scales
+    lib = pkv.library()
+    c8 = kcache(pkv, scales=FAKE, **fp8)
+    assert lib.rms_norm_kv_cache_paged(ctypes.byref(c8), 1, FAKE, 128, 1e-6, 0.0, 16, FAKE, 2,
+                                       1, 0, None) == UNSUP                # fp8 needs mbc
 
 
 def call_gather(pkv, cache, out_dtype=None, stride=576, rows=32, out=FAKE, oscales=FAKE,

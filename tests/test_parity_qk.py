@@ -69,7 +69,7 @@ def oracle_qk(orc, case, with_norm, with_scales=False):
     orc.qk_rope_paged_ragged(q_out, case.q, case.row_offsets, case.cache_lengths,
                              case.page_table, k, case.layer_idx, case.freqs, case.position_ids,
                              case.interleaved, case.gamma if with_norm else None, case.epsilon,
-                             case.k_scale_mode, ks)
+                             case.k_scale_mode, ks, mrope_section=case.mrope_section)
     return (q_out, k, ks) if with_scales else (q_out, k)
 
 
@@ -123,6 +123,25 @@ def test_fp8_k_llama_shape(orc, mode):
                               interleaved=True, with_position_ids=True, norm_cols=128, rng=rng,
                               k_dtype="fp8", k_scale_mode=mode)
     run_qk_fp8(orc, case, True)
+
+
+@pytest.mark.parametrize("idx", range(2))
+def test_mrope_small(orc, idx):
+    case = list(oracle_pins.small_mrope_cases())[idx]
+    run_qk(orc, case, case.gamma is not None)
+
+
+def test_mrope_vision_batch(orc):
+    """A Qwen2-VL-like batch: 8 requests of up to 900 tokens, Q 16 x 128, K 2 x
+    128, sections (16, 24, 24), three random position rows below 4096."""
+    rng = workloads.make_rng(5301)
+    new = rng.integers(100, 900, size=8, endpoint=True)
+    prior = rng.integers(0, 200, size=8, endpoint=True)
+    case = workloads.build_qk("mrope_vision", 5301, new, prior, Hq=16, Hkv=2, D=128,
+                              page_size=16, max_seq_len=4096, theta=1000000.0,
+                              interleaved=False, with_position_ids=True, norm_cols=None,
+                              rng=rng, mrope_section=(16, 24, 24))
+    run_qk(orc, case, False)
 
 
 @pytest.mark.parametrize("idx", range(2))
