@@ -74,7 +74,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.oracle_rmsnorm_row.argtypes = [_vp, _vp, _i64, _vp, ctypes.c_double]
     lib.oracle_mla_rope_rmsnorm_quant.restype = ctypes.c_int
     lib.oracle_mla_rope_rmsnorm_quant.argtypes = [
-        _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
+        _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
         ctypes.c_float, _i64, _i64, _i64, _vp, ctypes.c_int, _i64, _i64, _i64,
         _i64, ctypes.c_int, ctypes.c_float, _vp]
     lib.oracle_qk_rope_paged_ragged.restype = ctypes.c_int
@@ -172,7 +172,8 @@ class Oracle:
                                token_scales=None):
         """Fill ``q_out`` and the new rows of ``cache`` (and ``token_scales``).
 
-        Shapes: q [T,H,R] u16; latent [T,Dn+R] u16; row_offsets [B+1] u32;
+        Shapes: q_in [T,H,R] u16; q_out the same shape, u16 (bf16) or f32;
+        latent [T,Dn+R] u16; row_offsets [B+1] u32;
         cache_lengths [B] u32; page_table [B,stride] u32; freqs [max_seq,R]
         f32; gamma [Dn] u16; cache [L,P,S,1,Dn+R] u8 (fp8) or u16 (bf16);
         token_scales [L,P,S,1] f32.  ``scale_mode``: "per_tensor" |
@@ -189,8 +190,10 @@ class Oracle:
         cache_type = CACHE_BF16 if cache.dtype == np.uint16 else CACHE_FP8
         mode = {"per_tensor": SCALE_PER_TENSOR, "per_token": SCALE_PER_TOKEN,
                 "none": 0}[scale_mode]
+        q_f32 = q_out.dtype == np.float32
         rc = self.lib.oracle_mla_rope_rmsnorm_quant(
-            _ptr(q_out, np.uint16), _ptr(q_in, np.uint16), _ptr(latent, np.uint16),
+            _ptr(q_out, np.float32 if q_f32 else np.uint16), int(q_f32),
+            _ptr(q_in, np.uint16), _ptr(latent, np.uint16),
             _ptr(row_offsets, np.uint32), _ptr(cache_lengths, np.uint32), B,
             _ptr(page_table, np.uint32), page_table.shape[1],
             _ptr(freqs, np.float32), freqs.shape[0], _ptr(gamma, np.uint16),
@@ -257,9 +260,10 @@ class Oracle:
                                 cache_lengths, page_table, gamma, epsilon,
                                 weight_offset, total_seq_len,
                                 multiply_before_cast=True, k_scale_mode="none",
-                                k_scales=None):
-        """Normalise the new K rows of ``k_cache`` in place (per-head form);
-        fp8 caches as in :meth:`qk_rope_paged_ragged`."""
+                                k_scales=None, per_head_norm=True):
+        """Normalise the new K rows of ``k_cache`` in place (one statistic per
+        head, or per token over all heads with per_head_norm=False); fp8
+        caches as in :meth:`qk_rope_paged_ragged`."""
         L, P, S, Hkv, D = k_cache.shape
         B = row_offsets.size - 1
         k_type = CACHE_BF16 if k_cache.dtype == np.uint16 else CACHE_FP8
@@ -271,7 +275,7 @@ class Oracle:
             _ptr(page_table, np.uint32), page_table.shape[1],
             _ptr(gamma, np.uint16), gamma.size, float(epsilon),
             float(weight_offset), int(total_seq_len),
-            int(bool(multiply_before_cast)))
+            int(bool(multiply_before_cast)), int(bool(per_head_norm)))
         _check(rc, "rms_norm_kv_cache_paged")
 
 

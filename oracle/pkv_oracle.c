@@ -202,7 +202,8 @@ static int64_t page_of(const uint32_t* page_table, int64_t pt_stride,
  * quantise at the end, write into the cache).
  *
  * Host arrays, all dense and row-major:
- *   q_out, q_in   bf16 bits [T][H][R]            (q_rope_output, q_rope)
+ *   q_out         [T][H][R] bf16 bits, or fp32 when q_out_f32 (q_rope_output)
+ *   q_in          bf16 bits [T][H][R]            (q_rope)
  *   latent        bf16 bits [T][Dn + R]          (the KV latent input)
  *   row_offsets   u32 [B + 1]                    (input_row_offsets)
  *   cache_lengths u32 [B]  length of each request's cache before this step
@@ -214,7 +215,7 @@ static int64_t page_of(const uint32_t* page_table, int64_t pt_stride,
  * Only layer `layer_idx` and only the new tokens' slots are written.
  */
 int oracle_mla_rope_rmsnorm_quant(
-    uint16_t* q_out, const uint16_t* q_in, const uint16_t* latent,
+    void* q_out, int q_out_f32, const uint16_t* q_in, const uint16_t* latent,
     const uint32_t* row_offsets, const uint32_t* cache_lengths, int64_t B,
     const uint32_t* page_table, int64_t pt_stride, const float* freqs,
     int64_t max_seq_len, const uint16_t* gamma, float epsilon, int64_t H,
@@ -243,13 +244,19 @@ int oracle_mla_rope_rmsnorm_quant(
       const int64_t off = slot % page_size;
       const float* fr = freqs + pos * R;
 
-      /* q: RoPE on every head, one bf16 rounding per value. */
+      /* q: RoPE on every head, one rounding per value into the output type
+       * ([MLA] Parameters: out_rope_dtype; bf16 or fp32 here). */
       for (int64_t h = 0; h < H; ++h) {
         const uint16_t* src = q_in + (t * H + h) * R;
-        uint16_t* dst = q_out + (t * H + h) * R;
         for (int64_t i = 0; i < R; ++i) qa[i] = oracle_bf16_decode(src[i]);
         oracle_rope_row(qa, qb, R, fr, 0);
-        for (int64_t i = 0; i < R; ++i) dst[i] = oracle_bf16_encode(qb[i]);
+        if (q_out_f32) {
+          float* dst = (float*)q_out + (t * H + h) * R;
+          for (int64_t i = 0; i < R; ++i) dst[i] = (float)qb[i];  /* RNE */
+        } else {
+          uint16_t* dst = (uint16_t*)q_out + (t * H + h) * R;
+          for (int64_t i = 0; i < R; ++i) dst[i] = oracle_bf16_encode(qb[i]);
+        }
       }
 
       /* latent: RMSNorm on the first Dn values, RoPE on the R-value tail. */
@@ -472,8 +479,8 @@ int oracle_mla_gather_latent_paged(
  * head's first gamma_len columns are normalised with (gamma + weight_offset);
  * the other columns are left alone.  multiply_before_cast = 1 rounds once,
  * after the gamma product; = 0 rounds the normalised value to bf16 first,
- * then multiplies by (gamma + weight_offset) and rounds again.  Only the
- * per-head form is defined here.
+ * then multiplies by (gamma + weight_offset) and rounds again.
+ * per_head_norm = 1: one statistic per head; 0: one per token over all heads.
  *
  *   k_cache   bf16 bits [L][P][S][Hkv][D]
  *   gamma     bf16 bits [gamma_len]
@@ -484,7 +491,7 @@ int oracle_rms_norm_kv_cache_paged(
     const uint32_t* row_offsets, const uint32_t* cache_lengths, int64_t B,
     const uint32_t* page_table, int64_t pt_stride, const uint16_t* gamma,
     int64_t gamma_len, float epsilon, float weight_offset, int64_t total_seq_len,
-    int multiply_before_cast) {
+    int multiply_before_cast, int per_head_norm) {
   if (gamma_len <= 0 || gamma_len > D || D > 1024 || layer_idx < 0 ||
       layer_idx >= num_layers || page_size <= 0)
     return ORACLE_BAD_ARG;
@@ -503,13 +510,29 @@ int oracle_rms_norm_kv_cache_paged(
                                    page_size, b, slot);
       if (page < 0) { status = ORACLE_BAD_PAGE; continue; }
       const int64_t off = slot % page_size;
+      double token_inv = 0.0;
+      if (!per_head_norm) {
+        /* Reading of per_head_norm = False (listed on the page, not
+         * described): one statistic over the first gamma_len columns of all
+         * heads of the token. */
+        double ss = 0.0;
+        for (int64_t h = 0; h < Hkv; ++h) {
+          const int64_t head = ((layer_idx * num_pages + page) * page_size + off) * Hkv + h;
+          const double ks = k_type == ORACLE_CACHE_FP8
+              ? (double)(scale_mode == ORACLE_SCALE_PER_TOKEN ? k_scales[head] : k_scales[0])
+              : 1.0;
+          load_k_row(k_cache, k_type, head * D, D, ks, a);
+          for (int64_t i = 0; i < gamma_len; ++i) ss += a[i] * a[i];
+        }
+        token_inv = 1.0 / sqrt(ss / (double)(Hkv * gamma_len) + eps);
+      }
       for (int64_t h = 0; h < Hkv; ++h) {
         const int64_t head = ((layer_idx * num_pages + page) * page_size + off) * Hkv + h;
         const double ks = k_type == ORACLE_CACHE_FP8
             ? (double)(scale_mode == ORACLE_SCALE_PER_TOKEN ? k_scales[head] : k_scales[0])
             : 1.0;
         load_k_row(k_cache, k_type, head * D, D, ks, a);
-        double inv = oracle_inv_rms(a, gamma_len, eps);
+        double inv = per_head_norm ? oracle_inv_rms(a, gamma_len, eps) : token_inv;
         for (int64_t i = 0; i < gamma_len; ++i) {
           if (multiply_before_cast) {
             a[i] = a[i] * inv * g[i];

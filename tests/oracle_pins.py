@@ -510,6 +510,23 @@ def pin_mla_composite(orc):
         check_mla_against_reference(case, q_out, cache, ts)
 
 
+def pin_mla_f32_q(orc):
+    """fp32 q output: the correctly rounded fp32 of the exact rotation, and the
+    bf16 output is that value's bf16 rounding up to the double-rounding case."""
+    case = list(small_mla_cases())[2]
+    q32 = np.zeros(case.q.shape, np.float32)
+    cache = case.cache.copy()
+    orc.mla_rope_rmsnorm_quant(q32, case.q, case.latent, case.row_offsets, case.cache_lengths,
+                               case.page_table, case.freqs, case.gamma, case.epsilon, cache,
+                               case.layer_idx, case.scale_mode, case.tensor_scale, None)
+    q_ref, _, _ = mla_reference(case)
+    ulp32 = np.ldexp(1.0, np.frexp(np.maximum(np.abs(q_ref), 2.0 ** -126))[1] - 1 - 23)
+    assert np.all(np.abs(q32.astype(np.float64) - q_ref) <= 0.5 * ulp32 * (1 + 1e-12)), "fp32 q"
+    # the fp32 run writes the same cache rows as the bf16 run
+    _, cache_b, _ = run_mla(orc, case)
+    assert np.array_equal(cache, cache_b)
+
+
 def pin_mla_position0(orc):
     """Tokens at position 0 come back unchanged in q (values; +-0 equal)."""
     case = workloads.build_mla("mla_pos0", 2005, [1] * 6, [0] * 6, H=8,
@@ -805,6 +822,43 @@ def pin_mrope(orc):
                                      "mrope k")
 
 
+def pin_rms_norm_kv_token(orc):
+    """per_head_norm = False (reading: one statistic over all heads' first C
+    columns): equals the per-head form for a single head, and matches torch
+    rms_norm over the flattened heads with gamma repeated per head."""
+    one = list(small_qk_cases())[1]                       # Hkv = 1
+    g1 = workloads.bf16_bits(np.linspace(0.6, 1.4, 40).astype(np.float32))
+    outs = []
+    for per_head in (True, False):
+        k = one.k_cache.copy()
+        orc.rms_norm_kv_cache_paged(k, one.layer_idx, one.row_offsets, one.cache_lengths,
+                                    one.page_table, g1, one.epsilon, 0.0, one.T, True,
+                                    per_head_norm=per_head)
+        outs.append(k)
+    assert np.array_equal(outs[0], outs[1]), "single head: token norm != head norm"
+    case = list(small_qk_cases())[0]                      # Hkv = 2, D = 128
+    C = 100
+    gamma = workloads.bf16_bits(np.linspace(0.5, 1.5, C).astype(np.float32))
+    k = case.k_cache.copy()
+    orc.rms_norm_kv_cache_paged(k, case.layer_idx, case.row_offsets, case.cache_lengths,
+                                case.page_table, gamma, case.epsilon, 0.25, case.T, True,
+                                per_head_norm=False)
+    owners = slot_owners(case.row_offsets, case.cache_lengths, case.page_table,
+                         case.meta["page_size"])
+    H = case.k_cache.shape[3]
+    g = np.tile(bf16_to_f64(gamma) + 0.25, H)
+    L = case.layer_idx
+    expect = case.k_cache.copy()
+    for (page, off), (t, slot) in owners.items():
+        x = bf16_to_f64(case.k_cache[L, page, off])[:, :C].reshape(-1)
+        ref = torch.nn.functional.rms_norm(torch.from_numpy(x.copy()), (H * C,),
+                                           weight=torch.from_numpy(g),
+                                           eps=case.epsilon).numpy().reshape(H, C)
+        assert_correctly_rounded(bf16_to_f64(k[L, page, off][:, :C]), ref, ulp_bf16, "token norm")
+        expect[L, page, off, :, :C] = k[L, page, off, :, :C]
+    assert np.array_equal(k, expect)
+
+
 def gather_case(kind: str, seed: int = 3101):
     """A paged latent cache holding whole request contexts: ``kind`` is
     "fp8_tensor", "fp8_token" or "bf16".  Cache bytes are finite values (no
@@ -894,4 +948,5 @@ ALL_PINS = [
     pin_rmsnorm_closed_forms, pin_rmsnorm_torch, pin_mla_composite,
     pin_mla_position0, pin_mla_zero_row_per_token, pin_qk_composite,
     pin_rms_norm_kv, pin_gather, pin_qk_fp8, pin_rms_norm_kv_fp8, pin_mrope,
+    pin_mla_f32_q, pin_rms_norm_kv_token,
 ]

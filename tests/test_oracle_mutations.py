@@ -87,6 +87,10 @@ MUTANTS = [
      ": oracle_e4m3fn_decode(((const uint8_t*)k_cache)[elem + i]);"),
     ("k_fp8_token_scale_stale", "    *token_scale = st;\n    s = (double)st;",
      "    *token_scale = st;"),
+    ("mla_f32_q_truncated", "for (int64_t i = 0; i < R; ++i) dst[i] = (float)qb[i];  /* RNE */",
+     "for (int64_t i = 0; i < R; ++i) dst[i] = (float)(qb[i] * (1 - 1e-7));"),
+    ("token_norm_per_head_count", "token_inv = 1.0 / sqrt(ss / (double)(Hkv * gamma_len) + eps);",
+     "token_inv = 1.0 / sqrt(ss / (double)(gamma_len) + eps);"),
     ("mrope_section_boundary", "const int64_t k = i < mrope_section[0] ? 0",
      "const int64_t k = i <= mrope_section[0] ? 0"),
     ("mrope_row_layout", "const int64_t pk = (int64_t)position_ids[k * T + t];",
