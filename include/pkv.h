@@ -81,7 +81,8 @@ typedef enum pkv_status {
 
 typedef enum pkv_dtype {
   PKV_DTYPE_BF16 = 0,
-  PKV_DTYPE_FP8_E4M3FN = 1 /* OCP FP8 E4M3FN: bias 7, max 448, no inf */
+  PKV_DTYPE_FP8_E4M3FN = 1, /* OCP FP8 E4M3FN: bias 7, max 448, no inf */
+  PKV_DTYPE_F32 = 2         /* IEEE binary32 (MLA q output only) */
 } pkv_dtype;
 
 typedef enum pkv_scale_mode {
@@ -128,8 +129,11 @@ typedef struct pkv_paged_cache {
  *                                        bf16_rne(y)                  (bf16).
  * Per-token scale mode writes scale = fp32(max|y| / 448) beside the row.
  *
- *   q_rope_out      bf16 [total_tokens][num_heads][rope_dim], strides
- *                   qo_tok_stride / qo_head_stride (elements, multiples of 8)
+ *   q_rope_out      [total_tokens][num_heads][rope_dim] of q_out_dtype
+ *                   (PKV_DTYPE_BF16, or PKV_DTYPE_F32: the rotation rounded
+ *                   to fp32 instead of bf16 -- the pages' out_rope_dtype),
+ *                   strides qo_tok_stride / qo_head_stride (elements,
+ *                   16-byte multiples)
  *   q_rope          bf16, same shape, strides qi_tok_stride / qi_head_stride
  *   kv_latent       bf16 [total_tokens][kv_norm_dim + rope_dim], row stride
  *                   kv_row_stride (multiple of 8)
@@ -150,7 +154,7 @@ int mla_rope_rmsnorm_quant(void* q_rope_out, int64_t qo_tok_stride, int64_t qo_h
                            uint32_t total_tokens, uint32_t num_heads, uint32_t rope_dim,
                            uint32_t kv_norm_dim, const float* freqs_cis, uint32_t max_seq_len,
                            const void* gamma, float epsilon, const pkv_paged_cache* kv_cache,
-                           uint32_t layer_idx, void* stream);
+                           uint32_t layer_idx, int32_t q_out_dtype, void* stream);
 
 /*
  * Paged-ragged fused Q/K RoPE.  Q is rotated into q_out; the K rows of the
@@ -205,9 +209,12 @@ int qk_rope_paged_ragged(void* q_out, int64_t qo_tok_stride, int64_t qo_head_str
  *                  and the whole head is re-encoded with it); fp8 caches
  *                  need multiply_before_cast != 0
  *   gamma          bf16 [gamma_len], 0 < gamma_len <= head_dim
- *   per_head_norm  must be non-zero (one norm per head); 0 returns
- *                  PKV_ERR_UNSUPPORTED
- * Supported here: head_dim 64 or 128.
+ *   per_head_norm  non-zero: one statistic per head; 0: one statistic per
+ *                  token over the first gamma_len columns of all its heads
+ *                  (the page lists the flag without describing it; this is
+ *                  the reading taken)
+ * Supported here: head_dim 64 or 128; per_head_norm 0 with at most
+ * 2048 / head_dim heads.
  */
 int rms_norm_kv_cache_paged(const pkv_paged_cache* k_cache, uint32_t layer_idx,
                             const void* gamma, uint32_t gamma_len, float epsilon,

@@ -27,6 +27,7 @@ RMSNorm row step it is built from.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import subprocess
@@ -90,7 +91,13 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.oracle_rms_norm_kv_cache_paged.argtypes = [
         _vp, ctypes.c_int, ctypes.c_int, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _vp, _vp,
         _i64, _vp, _i64, _vp, _i64, ctypes.c_float, ctypes.c_float, _i64, ctypes.c_int]
+    _declare_probe(lib)
     return lib
+
+
+def _declare_probe(lib):
+    lib.oracle_set_fp8_probe.argtypes = [_vp, _i64, _vp]
+    lib.oracle_set_fp8_probe.restype = None
 
 
 def _ptr(a: np.ndarray | None, dtype) -> int | None:
@@ -117,6 +124,22 @@ class Oracle:
     def __init__(self, path: str | None = None):
         self.path = path or LIB_PATH
         self.lib = load(self.path)
+
+    # -- observation ----------------------------------------------------------
+    @contextlib.contextmanager
+    def fp8_probe(self, codes: np.ndarray):
+        """While active, every fp8 code an entry point writes into ``codes``
+        (a uint8 array passed to that call) records the binary64 value it was
+        rounded from; yields that float64 array (same shape, NaN where no code
+        was encoded: bytes left alone or copied as they were)."""
+        if codes.dtype != np.uint8 or not codes.flags.c_contiguous:
+            raise ValueError("probe needs a contiguous uint8 array")
+        pre = np.full(codes.shape, np.nan)
+        self.lib.oracle_set_fp8_probe(codes.ctypes.data, codes.size, pre.ctypes.data)
+        try:
+            yield pre
+        finally:
+            self.lib.oracle_set_fp8_probe(None, 0, None)
 
     # -- codecs and row steps --------------------------------------------------
     def bf16_decode(self, bits: int) -> float:

@@ -130,6 +130,28 @@ uint8_t oracle_e4m3fn_encode_sat(double v) {
   return (uint8_t)(sign | ((E + 7) << 3) | m);
 }
 
+/* Observation of fp8 decisions, for tests.  While a probe is set, every fp8
+ * code that an entry point below writes into [probe_base, probe_base + n)
+ * also leaves the binary64 value it was rounded from at the same index of
+ * probe_pre.  A test then knows how close each code was to a rounding
+ * midpoint; nothing else changes. */
+static uintptr_t probe_base;
+static int64_t probe_n;
+static double* probe_pre;
+
+void oracle_set_fp8_probe(const void* base, int64_t n, double* pre) {
+  probe_base = (uintptr_t)base;
+  probe_n = pre ? n : 0;
+  probe_pre = pre;
+}
+
+static void put_fp8(uint8_t* dst, double v) {
+  *dst = oracle_e4m3fn_encode_sat(v);
+  const uintptr_t a = (uintptr_t)dst;
+  if (probe_pre && a >= probe_base && a - probe_base < (uintptr_t)probe_n)
+    probe_pre[a - probe_base] = v;
+}
+
 /* ------------------------------------------------------------------------- */
 /* Steps of the method, in binary64                                           */
 /* ------------------------------------------------------------------------- */
@@ -273,14 +295,14 @@ int oracle_mla_rope_rmsnorm_quant(
       uint8_t* dst = (uint8_t*)cache + row * W;
       if (scale_mode == ORACLE_SCALE_PER_TENSOR) {
         const double s = (double)tensor_scale;
-        for (int64_t k = 0; k < W; ++k) dst[k] = oracle_e4m3fn_encode_sat(y[k] / s);
+        for (int64_t k = 0; k < W; ++k) put_fp8(&dst[k], y[k] / s);
       } else if (scale_mode == ORACLE_SCALE_PER_TOKEN) {
         double amax = 0.0;
         for (int64_t k = 0; k < W; ++k)
           if (fabs(y[k]) > amax) amax = fabs(y[k]);
         const float st = (float)(amax / 448.0); /* stored fp32, one rounding */
         for (int64_t k = 0; k < W; ++k)
-          dst[k] = oracle_e4m3fn_encode_sat(st == 0.0f ? y[k] : y[k] / (double)st);
+          put_fp8(&dst[k], st == 0.0f ? y[k] : y[k] / (double)st);
         token_scales[row] = st;
       } else {
         return ORACLE_BAD_ARG;
@@ -334,7 +356,7 @@ static void store_k_row(void* k_cache, int k_type, int scale_mode, int64_t elem,
     s = (double)st;
   }
   for (int64_t i = lo; i < hi; ++i)
-    ((uint8_t*)k_cache)[elem + i] = oracle_e4m3fn_encode_sat(s == 0.0 ? y[i] : y[i] / s);
+    put_fp8(&((uint8_t*)k_cache)[elem + i], s == 0.0 ? y[i] : y[i] / s);
 }
 
 int oracle_qk_rope_paged_ragged(
@@ -461,8 +483,8 @@ int oracle_mla_gather_latent_paged(
           if (out_type == ORACLE_CACHE_BF16)
             ((uint16_t*)out)[row * W + k] = bits;
           else
-            ((uint8_t*)out)[row * W + k] = oracle_e4m3fn_encode_sat(
-                oracle_bf16_decode(bits) / (double)out_tensor_scale);
+            put_fp8(&((uint8_t*)out)[row * W + k],
+                    oracle_bf16_decode(bits) / (double)out_tensor_scale);
         }
       }
       if (cache_type == ORACLE_CACHE_FP8 && out_type == ORACLE_CACHE_FP8 &&

@@ -25,6 +25,7 @@ LIB_PATH = os.path.join(_PKG, "libpkv.so")
 
 PKV_DTYPE_BF16 = 0
 PKV_DTYPE_FP8_E4M3FN = 1
+PKV_DTYPE_F32 = 2
 PKV_SCALE_NONE = 0
 PKV_SCALE_PER_TENSOR = 1
 PKV_SCALE_PER_TOKEN = 2
@@ -74,7 +75,7 @@ def _load() -> ctypes.CDLL:
     lib.mla_rope_rmsnorm_quant.restype = ctypes.c_int
     lib.mla_rope_rmsnorm_quant.argtypes = [
         vp, i64, i64, vp, i64, i64, vp, i64, vp, u32, u32, u32, u32, u32, vp, u32, vp, f32,
-        cache_p, u32, vp]
+        cache_p, u32, ctypes.c_int32, vp]
     lib.qk_rope_paged_ragged.restype = ctypes.c_int
     lib.qk_rope_paged_ragged.argtypes = [
         vp, i64, i64, vp, i64, i64, u32, u32, u32, vp, u32, cache_p, u32, vp, u32, vp, vp,
@@ -153,7 +154,8 @@ def mla_rope_rmsnorm_quant(q_rope_output: torch.Tensor, q_rope: torch.Tensor,
                            freqs_cis: torch.Tensor, gamma: torch.Tensor, epsilon: float,
                            kv_cache: PagedCache, layer_idx: int, stream=None) -> None:
     """Fused MLA step (C: ``mla_rope_rmsnorm_quant``).  q tensors are
-    ``[tokens, heads, rope_dim]`` bf16 (rope_dim axis contiguous), kv_latent
+    ``[tokens, heads, rope_dim]`` (rope_dim axis contiguous; q_rope bf16,
+    q_rope_output bf16 or float32), kv_latent
     ``[tokens, kv_norm_dim + rope_dim]`` bf16, freqs_cis ``[max_seq_len,
     rope_dim]`` fp32, gamma ``[kv_norm_dim]`` bf16."""
     T, H, R = q_rope.shape
@@ -163,7 +165,9 @@ def mla_rope_rmsnorm_quant(q_rope_output: torch.Tensor, q_rope: torch.Tensor,
         _ptr(kv_latent), kv_latent.stride(0),
         _ptr(input_row_offsets), input_row_offsets.numel() - 1, T, H, R,
         kv_latent.shape[1] - R, _ptr(freqs_cis), freqs_cis.shape[0], _ptr(gamma),
-        float(epsilon), ctypes.byref(kv_cache), int(layer_idx), _stream(stream))
+        float(epsilon), ctypes.byref(kv_cache), int(layer_idx),
+        PKV_DTYPE_F32 if q_rope_output.dtype == torch.float32 else PKV_DTYPE_BF16,
+        _stream(stream))
     _check("mla_rope_rmsnorm_quant", st)
 
 

@@ -84,7 +84,9 @@ __device__ __forceinline__ void load_q(uint4 (&q)[NI], const char* base, int64_t
   }
 }
 
-template <int NI, bool GUARD>
+// Rotate and store: bf16 output (16 bytes per lane) or fp32 output (32
+// bytes per lane: two 16-byte stores).
+template <int NI, bool GUARD, bool QF32>
 __device__ __forceinline__ void rotate_store_q(const uint4 (&q)[NI], const float (&cs)[16],
                                                char* base, int64_t step, uint32_t lane_off,
                                                uint32_t h_lane, uint32_t num_heads) {
@@ -96,12 +98,20 @@ __device__ __forceinline__ void rotate_store_q(const uint4 (&q)[NI], const float
     unpack8(partner, par);
     rotate_own(own, par, cs);
     if (GUARD && h_lane + 8 * i >= num_heads) continue;
-    store16(base + i * step + lane_off, pack8_bf16(own));
+    char* p = base + i * step + lane_off;
+    if constexpr (QF32) {
+      store16(p, make_uint4(__float_as_uint(own[0]), __float_as_uint(own[1]),
+                            __float_as_uint(own[2]), __float_as_uint(own[3])));
+      store16(p + 16, make_uint4(__float_as_uint(own[4]), __float_as_uint(own[5]),
+                                 __float_as_uint(own[6]), __float_as_uint(own[7])));
+    } else {
+      store16(p, pack8_bf16(own));
+    }
   }
 }
 
 // NI = 8-head instructions per wave (heads per wave / 8).
-template <int NI, MlaOut MODE>
+template <int NI, MlaOut MODE, bool QF32>
 __global__ __launch_bounds__(256) void mla_kernel(const MlaArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   const uint32_t wave =
@@ -159,12 +169,16 @@ __global__ __launch_bounds__(256) void mla_kernel(const MlaArgs a) {
   }
 
   // ---- q: exchange with the mirrored lane, rotate, store --------------------
-  char* qdst = reinterpret_cast<char*>(a.q_out + (int64_t)t * a.qo_tok + (int64_t)h0 * a.qo_head);
-  const uint32_t qo_lane = 2 * ((uint32_t)(lane >> 3) * (uint32_t)a.qo_head + 8 * hl.chunk);
+  constexpr int64_t QB = QF32 ? 4 : 2;  // bytes per q output element
+  char* qdst = static_cast<char*>(a.q_out) + QB * ((int64_t)t * a.qo_tok + (int64_t)h0 * a.qo_head);
+  const uint32_t qo_lane =
+      (uint32_t)QB * ((uint32_t)(lane >> 3) * (uint32_t)a.qo_head + 8 * hl.chunk);
   if (all_heads)
-    rotate_store_q<NI, false>(q, cs, qdst, 16 * a.qo_head, qo_lane, h_lane, a.num_heads);
+    rotate_store_q<NI, false, QF32>(q, cs, qdst, 8 * QB * a.qo_head, qo_lane, h_lane,
+                                    a.num_heads);
   else
-    rotate_store_q<NI, true>(q, cs, qdst, 16 * a.qo_head, qo_lane, h_lane, a.num_heads);
+    rotate_store_q<NI, true, QF32>(q, cs, qdst, 8 * QB * a.qo_head, qo_lane, h_lane,
+                                   a.num_heads);
   if (!latent_wave) return;
 
   // ---- latent row: RMSNorm (non-rope part), RoPE (tail) ---------------------
@@ -225,22 +239,35 @@ __global__ __launch_bounds__(256) void mla_kernel(const MlaArgs a) {
   }
 }
 
-template <int NI>
+template <int NI, bool QF32>
 hipError_t launch_g(const MlaArgs& a, MlaOut mode, uint32_t blocks, hipStream_t stream) {
   switch (mode) {
     case MlaOut::Fp8PerTensor:
-      hipLaunchKernelGGL((mla_kernel<NI, MlaOut::Fp8PerTensor>), dim3(blocks), dim3(256), 0,
-                         stream, a);
+      hipLaunchKernelGGL((mla_kernel<NI, MlaOut::Fp8PerTensor, QF32>), dim3(blocks), dim3(256),
+                         0, stream, a);
       break;
     case MlaOut::Fp8PerToken:
-      hipLaunchKernelGGL((mla_kernel<NI, MlaOut::Fp8PerToken>), dim3(blocks), dim3(256), 0,
-                         stream, a);
+      hipLaunchKernelGGL((mla_kernel<NI, MlaOut::Fp8PerToken, QF32>), dim3(blocks), dim3(256),
+                         0, stream, a);
       break;
     case MlaOut::Bf16:
-      hipLaunchKernelGGL((mla_kernel<NI, MlaOut::Bf16>), dim3(blocks), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((mla_kernel<NI, MlaOut::Bf16, QF32>), dim3(blocks), dim3(256), 0,
+                         stream, a);
       break;
   }
   return hipGetLastError();
+}
+
+template <bool QF32>
+hipError_t launch_q(const MlaArgs& a, MlaOut mode, int heads_per_wave, uint32_t blocks,
+                    hipStream_t stream) {
+  switch (heads_per_wave) {
+    case 16: return launch_g<2, QF32>(a, mode, blocks, stream);
+    case 32: return launch_g<4, QF32>(a, mode, blocks, stream);
+    case 64: return launch_g<8, QF32>(a, mode, blocks, stream);
+    case 128: return launch_g<16, QF32>(a, mode, blocks, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
@@ -250,13 +277,8 @@ hipError_t launch_mla(const MlaArgs& a, MlaOut mode, int heads_per_wave, hipStre
   const uint64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffull) return hipErrorInvalidValue;
-  switch (heads_per_wave) {
-    case 16: return launch_g<2>(a, mode, (uint32_t)blocks, stream);
-    case 32: return launch_g<4>(a, mode, (uint32_t)blocks, stream);
-    case 64: return launch_g<8>(a, mode, (uint32_t)blocks, stream);
-    case 128: return launch_g<16>(a, mode, (uint32_t)blocks, stream);
-    default: return hipErrorInvalidValue;
-  }
+  return a.q_out_f32 ? launch_q<true>(a, mode, heads_per_wave, (uint32_t)blocks, stream)
+                     : launch_q<false>(a, mode, heads_per_wave, (uint32_t)blocks, stream);
 }
 
 }  // namespace pkv

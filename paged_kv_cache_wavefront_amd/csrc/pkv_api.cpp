@@ -108,8 +108,10 @@ int mla_rope_rmsnorm_quant(void* q_rope_out, int64_t qo_tok_stride, int64_t qo_h
                            uint32_t total_tokens, uint32_t num_heads, uint32_t rope_dim,
                            uint32_t kv_norm_dim, const float* freqs_cis, uint32_t max_seq_len,
                            const void* gamma, float epsilon, const pkv_paged_cache* kv_cache,
-                           uint32_t layer_idx, void* stream) {
+                           uint32_t layer_idx, int32_t q_out_dtype, void* stream) {
   if (kv_cache == nullptr) return PKV_ERR_NULL;
+  if (q_out_dtype != PKV_DTYPE_BF16 && q_out_dtype != PKV_DTYPE_F32) return PKV_ERR_DTYPE;
+  const int64_t qo_align = q_out_dtype == PKV_DTYPE_F32 ? 4 : 8;  // 16 bytes in elements
   if (rope_dim == 0 || rope_dim % 2 != 0 || kv_norm_dim == 0) return PKV_ERR_SHAPE;
   if (kv_cache->num_heads != 1 || kv_cache->head_dim != kv_norm_dim + rope_dim)
     return PKV_ERR_SHAPE;
@@ -136,13 +138,14 @@ int mla_rope_rmsnorm_quant(void* q_rope_out, int64_t qo_tok_stride, int64_t qo_h
   if (num_heads > 0 && (q_rope == nullptr || q_rope_out == nullptr)) return PKV_ERR_NULL;
   if (mode != pkv::MlaOut::Bf16 && kv_cache->scales == nullptr) return PKV_ERR_NULL;
   if (!aligned16(q_rope) || !aligned16(q_rope_out) || !aligned16(kv_latent) ||
-      !aligned16(gamma) || !aligned16(freqs_cis) || !mult(qo_tok_stride, 8) ||
-      !mult(qo_head_stride, 8) || !mult(qi_tok_stride, 8) || !mult(qi_head_stride, 8) ||
+      !aligned16(gamma) || !aligned16(freqs_cis) || !mult(qo_tok_stride, qo_align) ||
+      !mult(qo_head_stride, qo_align) || !mult(qi_tok_stride, 8) || !mult(qi_head_stride, 8) ||
       !mult(kv_row_stride, 8))
     return PKV_ERR_ALIGN;
 
   pkv::MlaArgs a{};
-  a.q_out = static_cast<uint16_t*>(q_rope_out);
+  a.q_out = q_rope_out;
+  a.q_out_f32 = q_out_dtype == PKV_DTYPE_F32;
   a.qo_tok = qo_tok_stride;
   a.qo_head = qo_head_stride;
   a.q_in = static_cast<const uint16_t*>(q_rope);
@@ -242,9 +245,10 @@ int rms_norm_kv_cache_paged(const pkv_paged_cache* k_cache, uint32_t layer_idx,
   pkv::KMode km;
   if (!k_mode_of(k_cache, &km)) return PKV_ERR_DTYPE;
   if (gamma_len == 0 || gamma_len > k_cache->head_dim) return PKV_ERR_SHAPE;
-  if (!per_head_norm) return PKV_ERR_UNSUPPORTED;
   if (km != pkv::KMode::Bf16 && !multiply_before_cast) return PKV_ERR_UNSUPPORTED;
   if (k_cache->head_dim != 64 && k_cache->head_dim != 128) return PKV_ERR_UNSUPPORTED;
+  if (!per_head_norm && k_cache->num_heads > pkv::kv_norm_max_heads(k_cache->head_dim))
+    return PKV_ERR_UNSUPPORTED;
   if (total_seq_len > 0 && batch_size == 0) return PKV_ERR_SHAPE;
   CacheView view{};
   int st = check_cache(k_cache, layer_idx, batch_size, &view);
@@ -260,6 +264,7 @@ int rms_norm_kv_cache_paged(const pkv_paged_cache* k_cache, uint32_t layer_idx,
   a.batch = batch_size;
   a.gamma = static_cast<const uint16_t*>(gamma);
   a.gamma_len = gamma_len;
+  a.per_head = per_head_norm != 0;
   a.epsilon = epsilon;
   a.weight_offset = weight_offset;
   a.k_scales = k_scales_of(k_cache, layer_idx, km);

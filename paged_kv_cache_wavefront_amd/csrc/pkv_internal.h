@@ -25,7 +25,8 @@ struct CacheView {
 enum class MlaOut : int { Fp8PerTensor = 0, Fp8PerToken = 1, Bf16 = 2 };
 
 struct MlaArgs {
-  uint16_t* q_out;
+  void* q_out;                 // bf16, or fp32 when q_out_f32
+  bool q_out_f32;
   int64_t qo_tok, qo_head;
   const uint16_t* q_in;
   int64_t qi_tok, qi_head;
@@ -45,7 +46,7 @@ struct MlaArgs {
   CacheView cache;
 };
 
-// heads_per_wave is 16, 32, 64 or 128.
+// heads_per_wave is 16, 32, 64 or 128 (the two widest are kept for tuning).
 hipError_t launch_mla(const MlaArgs& a, MlaOut mode, int heads_per_wave, hipStream_t stream);
 
 struct QkArgs {
@@ -80,12 +81,15 @@ struct KvNormArgs {
   uint32_t batch;
   const uint16_t* gamma;
   uint32_t gamma_len;
+  bool per_head;                 // false: one statistic per token over all heads
   float epsilon, weight_offset;
   float* k_scales;               // fp8 K: tensor scale [1] or this layer's per-token scales
   CacheView cache;               // K cache
   uint32_t head_dim;
 };
 
+// Most KV heads per token the per-token K-norm statistic handles.
+uint32_t kv_norm_max_heads(uint32_t head_dim);
 hipError_t launch_kv_norm(const KvNormArgs& a, bool multiply_before_cast, KMode kmode,
                           hipStream_t stream);
 

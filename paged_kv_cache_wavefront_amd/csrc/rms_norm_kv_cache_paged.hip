@@ -8,6 +8,12 @@
 // selects one bf16 rounding after the gamma product, or a rounding of x * r
 // before it and another after it.
 //
+// Per-token statistic (per_head_norm = 0, a reading: the page lists the flag
+// without describing it): one r over the first len(gamma) columns of every
+// head of the token, from a wave-wide sum.  Both forms load a chunk of up to
+// 4 head groups first (phase 1, sums), then normalise and store it (phase 2);
+// the per-token form needs all heads in one chunk.
+//
 // One wave64 per token; lane holds 8 consecutive columns (16 bytes of bf16,
 // 8 bytes of fp8) of one head, D/8 lanes per head, and the per-head sum of
 // squares (and, for a per-token fp8 cache, the max for the fresh scale)
@@ -22,10 +28,11 @@ namespace pkv {
 namespace {
 
 constexpr int kWavesPerBlock = 4;
+constexpr int kMaxIter = 4;  // head groups held in registers at once
 
 __device__ __forceinline__ float round_bf16(float v) { return __uint_as_float(pack_bf16x2(v, 0.0f) << 16); }
 
-template <int D, bool MBC, KMode KM>
+template <int D, bool MBC, KMode KM, bool PER_HEAD>
 __global__ __launch_bounds__(256) void kv_norm_kernel(const KvNormArgs a) {
   constexpr int LP = D / 8, HPI = kWave / LP;
   constexpr int64_t EB = KM == KMode::Bf16 ? 2 : 1;
@@ -70,88 +77,123 @@ __global__ __launch_bounds__(256) void kv_norm_kernel(const KvNormArgs a) {
     tensor_scale = a.k_scales[0];
     tensor_inv = 1.0f / tensor_scale;
   }
-  for (uint32_t hbase = 0; hbase < cv.num_heads; hbase += HPI) {
-    const uint32_t h = hbase + hl;
-    const bool valid = h < cv.num_heads && touches;
-    char* p = krow + EB * (int64_t)h * cv.head_stride;
-    float x[8];
-    if constexpr (KM == KMode::Bf16) {
-      uint4 raw = make_uint4(0, 0, 0, 0);
-      if (valid) raw = *reinterpret_cast<const uint4*>(p);
-      unpack8(raw, x);
-    } else {
-      uint2 raw = make_uint2(0, 0);
-      float ks = 0.0f;
-      if (valid) {
-        raw = *reinterpret_cast<const uint2*>(p);
-        ks = KM == KMode::Fp8PerTensor ? tensor_scale : a.k_scales[slot_head0 + h];
-      }
-      unpack8_fp8(raw.x, raw.y, x);
+  // head groups of HPI heads; the per-token statistic needs them all in one
+  // chunk (host-checked), per-head statistics go kMaxIter groups at a time
+  const uint32_t nit = (cv.num_heads + HPI - 1) / HPI;
+  for (uint32_t base = 0; base < nit; base += kMaxIter) {
+    // phase 1: load the chunk's heads this lane serves, sums of squares
+    float x[kMaxIter][8], rh[kMaxIter];
+    float ss_token = 0.0f;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) x[k] *= ks;
-    }
-    float ss = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-      if (col0 + k < C) ss = fmaf(x[k], x[k], ss);
-    ss = group_sum<LP>(ss);
-    const float r = 1.0f / sqrtf(ss / (float)C + a.epsilon);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      if (col0 + k >= C) continue;
-      if constexpr (MBC) {
-        x[k] = x[k] * g[k] * r;
+    for (int it = 0; it < kMaxIter; ++it) {
+      if (base + it >= nit) break;
+      const uint32_t h = (base + it) * HPI + hl;
+      const bool valid = h < cv.num_heads && touches;
+      const char* p = krow + EB * (int64_t)h * cv.head_stride;
+      if constexpr (KM == KMode::Bf16) {
+        uint4 raw = make_uint4(0, 0, 0, 0);
+        if (valid) raw = *reinterpret_cast<const uint4*>(p);
+        unpack8(raw, x[it]);
       } else {
-        x[k] = round_bf16(x[k] * r) * g[k];
+        uint2 raw = make_uint2(0, 0);
+        float ks = 0.0f;
+        if (valid) {
+          raw = *reinterpret_cast<const uint2*>(p);
+          ks = KM == KMode::Fp8PerTensor ? tensor_scale : a.k_scales[slot_head0 + h];
+        }
+        unpack8_fp8(raw.x, raw.y, x[it]);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) x[it][k] *= ks;
+      }
+      float ss = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (col0 + k < C) ss = fmaf(x[it][k], x[it][k], ss);
+      if constexpr (PER_HEAD) {
+        ss = group_sum<LP>(ss);
+        rh[it] = 1.0f / sqrtf(ss / (float)C + a.epsilon);
+      } else {
+        ss_token += ss;
       }
     }
-    if constexpr (KM == KMode::Bf16) {
-      if (valid) {
-        if (col0 + 8 <= C) {
-          *reinterpret_cast<uint4*>(p) = pack8_bf16(x);
-        } else {
-          uint16_t* e = reinterpret_cast<uint16_t*>(p);
+    float r_token = 0.0f;
+    if constexpr (!PER_HEAD)
+      r_token = 1.0f / sqrtf(wave_sum(ss_token) / (float)(C * cv.num_heads) + a.epsilon);
+
+    // phase 2: normalise, re-encode, store
 #pragma unroll
-          for (int k = 0; k < 8; ++k)
-            if (col0 + k < C) e[k] = (uint16_t)(pack_bf16x2(x[k], 0.0f) & 0xffffu);
+    for (int it = 0; it < kMaxIter; ++it) {
+      if (base + it >= nit) break;
+      const uint32_t h = (base + it) * HPI + hl;
+      const bool valid = h < cv.num_heads && touches;
+      char* p = krow + EB * (int64_t)h * cv.head_stride;
+      const float r = PER_HEAD ? rh[it] : r_token;
+      float* v = x[it];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        if (col0 + k >= C) continue;
+        if constexpr (MBC) {
+          v[k] = v[k] * g[k] * r;
+        } else {
+          v[k] = round_bf16(v[k] * r) * g[k];
         }
       }
-    } else {
-      float inv = tensor_inv;
-      if constexpr (KM == KMode::Fp8PerToken) {
-        float am = 0.0f;
+      if constexpr (KM == KMode::Bf16) {
+        if (valid) {
+          if (col0 + 8 <= C) {
+            *reinterpret_cast<uint4*>(p) = pack8_bf16(x[it]);
+          } else {
+            uint16_t* e = reinterpret_cast<uint16_t*>(p);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) am = fmaxf(am, fabsf(x[k]));
-        am = group_max<LP>(am);
-        const float st = am / 448.0f;
-        inv = st > 0.0f ? 1.0f / st : 0.0f;
-        if (valid && m == 0) a.k_scales[slot_head0 + h] = st;
-      }
+            for (int k = 0; k < 8; ++k)
+              if (col0 + k < C) e[k] = (uint16_t)(pack_bf16x2(v[k], 0.0f) & 0xffffu);
+          }
+        }
+      } else {
+        float inv = tensor_inv;
+        if constexpr (KM == KMode::Fp8PerToken) {
+          float am = 0.0f;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) x[k] *= inv;
-      const uint2 codes = pack8_fp8(x);
-      if (valid) {
-        if (kWholeHead || col0 + 8 <= C) {
-          *reinterpret_cast<uint2*>(p) = codes;
-        } else {
-          uint8_t* e = reinterpret_cast<uint8_t*>(p);
-          const uint32_t w[2] = {codes.x, codes.y};
+          for (int k = 0; k < 8; ++k) am = fmaxf(am, fabsf(v[k]));
+          am = group_max<LP>(am);
+          const float st = am / 448.0f;
+          inv = st > 0.0f ? 1.0f / st : 0.0f;
+          if (valid && m == 0) a.k_scales[slot_head0 + h] = st;
+        }
 #pragma unroll
-          for (int k = 0; k < 8; ++k)
-            if (col0 + k < C) e[k] = (uint8_t)(w[k / 4] >> (8 * (k % 4)));
+        for (int k = 0; k < 8; ++k) v[k] *= inv;
+        const uint2 codes = pack8_fp8(x[it]);
+        if (valid) {
+          if (kWholeHead || col0 + 8 <= C) {
+            *reinterpret_cast<uint2*>(p) = codes;
+          } else {
+            uint8_t* e = reinterpret_cast<uint8_t*>(p);
+            const uint32_t w[2] = {codes.x, codes.y};
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+              if (col0 + k < C) e[k] = (uint8_t)(w[k / 4] >> (8 * (k % 4)));
+          }
         }
       }
     }
-  }
+  }  // chunk
+}
+
+template <int D, KMode KM, bool PER_HEAD>
+hipError_t launch_dkh(const KvNormArgs& a, bool mbc, uint32_t blocks, hipStream_t stream) {
+  if (mbc)
+    hipLaunchKernelGGL((kv_norm_kernel<D, true, KM, PER_HEAD>), dim3(blocks), dim3(256), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL((kv_norm_kernel<D, false, KM, PER_HEAD>), dim3(blocks), dim3(256), 0,
+                       stream, a);
+  return hipGetLastError();
 }
 
 template <int D, KMode KM>
 hipError_t launch_dk(const KvNormArgs& a, bool mbc, uint32_t blocks, hipStream_t stream) {
-  if (mbc)
-    hipLaunchKernelGGL((kv_norm_kernel<D, true, KM>), dim3(blocks), dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL((kv_norm_kernel<D, false, KM>), dim3(blocks), dim3(256), 0, stream, a);
-  return hipGetLastError();
+  return a.per_head ? launch_dkh<D, KM, true>(a, mbc, blocks, stream)
+                    : launch_dkh<D, KM, false>(a, mbc, blocks, stream);
 }
 
 template <int D>
@@ -166,8 +208,12 @@ hipError_t launch_d(const KvNormArgs& a, bool mbc, KMode km, uint32_t blocks, hi
 
 }  // namespace
 
+uint32_t kv_norm_max_heads(uint32_t head_dim) { return kMaxIter * (kWave / (head_dim / 8)); }
+
 hipError_t launch_kv_norm(const KvNormArgs& a, bool multiply_before_cast, KMode kmode,
                           hipStream_t stream) {
+  if (!a.per_head && a.cache.num_heads > kv_norm_max_heads(a.head_dim))
+    return hipErrorInvalidValue;
   const uint64_t blocks = ((uint64_t)a.total_tokens + kWavesPerBlock - 1) / kWavesPerBlock;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffull) return hipErrorInvalidValue;

@@ -31,6 +31,29 @@ def fp8_values_torch() -> np.ndarray:
     return codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
 
 
+def fp8_midpoint_dist(v: np.ndarray):
+    """(distance, midpoint): |v|'s distance from the nearest rounding midpoint
+    between two adjacent finite E4M3FN magnitudes (the values torch decodes
+    for codes 0x00..0x7E), and that midpoint.  Above 448 saturation decides,
+    so there is no midpoint: distance +inf.  NaN stays NaN."""
+    mags = np.unique(fp8_values_torch()[:0x7F])
+    mids = (mags[1:] + mags[:-1]) / 2
+    a = np.abs(np.asarray(v, np.float64))
+    i = np.clip(np.searchsorted(mids, a), 1, mids.size - 1)
+    with np.errstate(invalid="ignore"):
+        lo, hi = np.abs(a - mids[i - 1]), np.abs(a - mids[i])
+        mid = np.where(lo <= hi, mids[i - 1], mids[i])
+        d = np.minimum(lo, hi)
+    d = np.where(a > 448.0, np.inf, d)
+    return np.where(np.isnan(a), np.nan, d), mid
+
+
+def fp8_midpoint_rel(v: np.ndarray) -> np.ndarray:
+    """fp8_midpoint_dist's distance relative to the midpoint."""
+    d, mid = fp8_midpoint_dist(v)
+    return d / mid
+
+
 def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
     b = np.asarray(bits, np.uint16).astype(np.uint32) << 16
     with np.errstate(invalid="ignore"):

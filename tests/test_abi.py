@@ -67,11 +67,13 @@ def mla_cache(pkv, **kw):
 
 
 def call_mla(pkv, cache, T=16, H=4, R=64, Dn=512, q=FAKE, qo=FAKE, lat=FAKE, qstride=4 * 64,
-             layer=1, batch=2, freqs=FAKE, gamma=FAKE, max_seq=64):
+             layer=1, batch=2, freqs=FAKE, gamma=FAKE, max_seq=64, qo_dtype=0, qostride=None):
     lib = pkv.library()
     cp = None if cache is None else ctypes.byref(cache)
-    return lib.mla_rope_rmsnorm_quant(qo, qstride, R, q, qstride, R, lat, Dn + R, FAKE, batch,
-                                      T, H, R, Dn, freqs, max_seq, gamma, 1e-6, cp, layer, None)
+    qos = qstride if qostride is None else qostride
+    return lib.mla_rope_rmsnorm_quant(qo, qos, R, q, qstride, R, lat, Dn + R, FAKE, batch,
+                                      T, H, R, Dn, freqs, max_seq, gamma, 1e-6, cp, layer,
+                                      qo_dtype, None)
 
 
 def test_mla_validation(pkv):
@@ -95,6 +97,12 @@ def test_mla_validation(pkv):
     assert call_mla(pkv, mla_cache(pkv), q=FAKE + 8) == ALIGN
     assert call_mla(pkv, mla_cache(pkv), qstride=4 * 64 + 4) == ALIGN
     assert call_mla(pkv, mla_cache(pkv), gamma=FAKE + 2) == ALIGN
+    # q output dtype: bf16 or fp32 (16-byte strides: multiples of 4 fp32)
+    assert call_mla(pkv, mla_cache(pkv), qo_dtype=pkv.PKV_DTYPE_FP8_E4M3FN) == DTYPE
+    assert call_mla(pkv, mla_cache(pkv), qo_dtype=9) == DTYPE
+    assert call_mla(pkv, mla_cache(pkv), T=0, qo_dtype=pkv.PKV_DTYPE_F32,
+                    qostride=4 * 64 + 4) == OK
+    assert call_mla(pkv, mla_cache(pkv), qo_dtype=pkv.PKV_DTYPE_F32, qostride=4 * 64 + 2) == ALIGN
     assert call_mla(pkv, mla_cache(pkv, slot_stride=584)) == ALIGN
     assert call_mla(pkv, mla_cache(pkv, data=FAKE + 8)) == ALIGN
     # nothing to do: accepted without a launch
@@ -152,7 +160,12 @@ def test_kv_norm_validation(pkv):
     assert call_norm(pkv, kcache(pkv, dtype=pkv.PKV_DTYPE_FP8_E4M3FN)) == DTYPE
     assert call_norm(pkv, kcache(pkv), gamma_len=0) == SHAPE
     assert call_norm(pkv, kcache(pkv), gamma_len=129) == SHAPE
-    assert call_norm(pkv, kcache(pkv), per_head=0) == UNSUP
+    # one statistic per token: every head of the token in one wave's registers
+    assert call_norm(pkv, kcache(pkv), per_head=0, T=0) == OK
+    assert call_norm(pkv, kcache(pkv, num_heads=17, slot_stride=17 * 128, page_stride=16 * 17 * 128,
+                                  layer_stride=8 * 16 * 17 * 128), per_head=0) == UNSUP
+    assert call_norm(pkv, kcache(pkv, num_heads=17, slot_stride=17 * 128, page_stride=16 * 17 * 128,
+                                  layer_stride=8 * 16 * 17 * 128), per_head=1, T=0) == OK
     assert call_norm(pkv, kcache(pkv, head_dim=256), gamma_len=128) == UNSUP
     assert call_norm(pkv, kcache(pkv), gamma=None) == NULL
     assert call_norm(pkv, kcache(pkv), gamma=FAKE + 2) == ALIGN

@@ -43,8 +43,8 @@ MUTANTS = [
      "const int64_t pos = j;"),
     ("mla_rope_tail_normalised", "oracle_rope_row(x + Dn, y + Dn, R, fr, 0);",
      "oracle_rope_row(y + Dn, x + Dn, R, fr, 0); memcpy(y + Dn, x + Dn, R * sizeof(double));"),
-    ("mla_scale_multiplied", "dst[k] = oracle_e4m3fn_encode_sat(y[k] / s);",
-     "dst[k] = oracle_e4m3fn_encode_sat(y[k] * s);"),
+    ("mla_scale_multiplied", "put_fp8(&dst[k], y[k] / s);",
+     "put_fp8(&dst[k], y[k] * s);"),
     ("mla_amax_nope_only", "for (int64_t k = 0; k < W; ++k)\n          if (fabs(y[k]) > amax)",
      "for (int64_t k = 0; k < Dn; ++k)\n          if (fabs(y[k]) > amax)"),
     ("mla_token_scale_448", "const float st = (float)(amax / 448.0); /* stored fp32",

@@ -63,16 +63,16 @@ def run_gather(orc, case, kvo, out_fp8, out_scale=0.25, subset=None):
     want_sc = np.full(max(rows, 1), -7.0, np.float32)
     sc_host = (case.token_scales if case.scale_mode == "per_token" else
                np.array([case.tensor_scale], np.float32))
-    orc.mla_gather_latent_paged(want, kvo, case.page_table, case.cache, case.layer_idx,
-                                case.scale_mode if case.cache.dtype == np.uint8 else "none",
-                                sc_host if case.cache.dtype == np.uint8 else None,
-                                want_sc, out_tensor_scale=out_scale)
+    import contextlib
+    with (orc.fp8_probe(want) if out_fp8 else contextlib.nullcontext()) as pre:
+        orc.mla_gather_latent_paged(want, kvo, case.page_table, case.cache, case.layer_idx,
+                                    case.scale_mode if case.cache.dtype == np.uint8 else "none",
+                                    sc_host if case.cache.dtype == np.uint8 else None,
+                                    want_sc, out_tensor_scale=out_scale)
     if out_fp8:
-        d = gh.fp8_ulp_diff(got, want)
         if case.cache.dtype == np.uint8:
             assert np.array_equal(got, want), "fp8 copy must be exact"
-        stats = dict(max_ulp=int(d.max(initial=0)), diff_frac=float((d != 0).mean()) if d.size else 0.0)
-        assert stats["max_ulp"] <= gh.FP8_MAX_ULP and stats["diff_frac"] <= gh.FP8_MAX_DIFF_FRAC
+        stats = gh.check_fp8(got, want, pre, "gather fp8")
         if case.scale_mode == "per_token" and case.cache.dtype == np.uint8:
             assert np.array_equal(got_sc[:rows].view(np.uint32), want_sc[:rows].view(np.uint32))
     else:

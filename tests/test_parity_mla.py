@@ -17,14 +17,14 @@ def _say(*a):
     print(*a, flush=True)
 
 
-def _run_and_compare(orc, case, q_layout="dense"):
+def _run_and_compare(orc, case, q_layout="dense", q_f32=False):
     _say(f"[mla] case={case.name} seed={case.seed} T={case.T} B={case.B} H={case.H} "
-         f"scale={case.scale_mode} layout={q_layout}")
-    dev = gh.MlaDevice(case, q_layout)
+         f"scale={case.scale_mode} layout={q_layout} q_f32={q_f32}")
+    dev = gh.MlaDevice(case, q_layout, q_f32)
     dev.run()
     gpu = dev.results()
     assert gpu[3] == 0, f"{gpu[3]} tokens skipped"
-    stats = gh.compare_mla(case, gpu, gh.oracle_mla(orc, case))
+    stats = gh.compare_mla(case, gpu, gh.oracle_mla(orc, case, q_f32))
     _say(f"[mla] {case.name}: {stats}")
     return stats
 
@@ -32,6 +32,20 @@ def _run_and_compare(orc, case, q_layout="dense"):
 @pytest.mark.parametrize("name", ["mla_tiny", "mla_decode", "mla_prefill", "mla_mixed"])
 def test_named_workload(orc, name):
     _run_and_compare(orc, workloads.NAMED[name]())
+
+
+@pytest.mark.parametrize("name", ["mla_tiny", "mla_decode", "mla_mixed"])
+def test_fp32_q_output(orc, name):
+    """q_rope_output in float32 (the pages' out_rope_dtype): every value within
+    2 fp32 ulps of the oracle's once-rounded result; cache rows as for bf16."""
+    _run_and_compare(orc, workloads.NAMED[name](), q_f32=True)
+
+
+def test_fp32_q_output_h40(orc):
+    case = workloads.build_mla("mla_h40_f32", 4005, [5, 0, 77, 1, 300], [0, 3, 9, 200, 1],
+                               H=40, page_size=16, max_seq_len=1024, spare_pages=3,
+                               scale_mode="per_token")
+    _run_and_compare(orc, case, q_f32=True)
 
 
 @pytest.mark.parametrize("idx", range(5))
@@ -92,7 +106,7 @@ def test_codec_every_bf16_value(orc):
         dev.run()
         q, cache, _, skipped = dev.results()
         assert skipped == 0
-        _, cache_o, _ = gh.oracle_mla(orc, case)
+        _, cache_o, _, _ = gh.oracle_mla(orc, case)
         rows_mask = gh.written_rows(case)
         got = cache[rows_mask][:, 0, case.Dn:]
         want = cache_o[rows_mask][:, 0, case.Dn:]
@@ -120,13 +134,13 @@ def test_skipped_tokens_are_counted(orc):
     q, cache, _, skipped = dev.results()
     assert skipped == 5, skipped
     assert not q[[0, 1, 2, 5, 6]].any(), "skipped tokens wrote q"
-    q_o, cache_o, _ = gh.oracle_mla(orc, good)
+    q_o, cache_o, _, pre = gh.oracle_mla(orc, good)
     assert gh.bf16_ulp_diff(q[7:], q_o[7:]).max() <= 1       # request 2 unaffected
     owners = oracle_pins.slot_owners(good.row_offsets, good.cache_lengths, good.page_table, 8)
     L = good.layer_idx
     for (page, off), (t, slot) in owners.items():
         if t >= 7:
-            assert gh.fp8_ulp_diff(cache[L, page, off], cache_o[L, page, off]).max() <= 1
+            gh.check_fp8(cache[L, page, off], cache_o[L, page, off], pre[L, page, off], "row")
         elif t < 3:
             assert np.array_equal(cache[L, page, off], good.cache[L, page, off])
 

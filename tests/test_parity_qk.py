@@ -63,25 +63,41 @@ NORM_SLACK = 2.0 ** -18
 
 
 def oracle_qk(orc, case, with_norm, with_scales=False):
+    """(q_out, k) or, with_scales, (q_out, k, k_scales, pre): ``pre`` holds the
+    binary64 value each fp8 K code was rounded from (None: bf16 K)."""
+    import contextlib
     q_out = np.zeros_like(case.q)
     k = case.k_cache.copy()
     ks = None if case.k_scales is None else case.k_scales.copy()
-    orc.qk_rope_paged_ragged(q_out, case.q, case.row_offsets, case.cache_lengths,
-                             case.page_table, k, case.layer_idx, case.freqs, case.position_ids,
-                             case.interleaved, case.gamma if with_norm else None, case.epsilon,
-                             case.k_scale_mode, ks, mrope_section=case.mrope_section)
-    return (q_out, k, ks) if with_scales else (q_out, k)
+    probe = orc.fp8_probe(k) if k.dtype == np.uint8 else contextlib.nullcontext()
+    with probe as pre:
+        orc.qk_rope_paged_ragged(q_out, case.q, case.row_offsets, case.cache_lengths,
+                                 case.page_table, k, case.layer_idx, case.freqs,
+                                 case.position_ids, case.interleaved,
+                                 case.gamma if with_norm else None, case.epsilon,
+                                 case.k_scale_mode, ks, mrope_section=case.mrope_section)
+    return (q_out, k, ks, pre) if with_scales else (q_out, k)
 
 
-def check_fp8_k(case, k_gpu, ks_gpu, k_orc, ks_orc, what):
-    """fp8 K rows: codes within 1 step on at most 0.1 % of written bytes;
+# fp8 K through the rotation: the kernel decodes code x scale into fp32 (one
+# rounding) and multiplies by gamma (another) before rotating, so each input
+# of a pair carries up to 2^-23 relative error; cancellation in the rotation
+# turns that into up to 2^-23 * sqrt(2) of the pair magnitude, absolute.
+# 2^-20 of the pair magnitude (in scaled units) bounds it with margin.
+FP8_ROT_SLACK = 2.0 ** -20
+
+
+def check_fp8_k(case, k_gpu, ks_gpu, k_orc, ks_orc, pre, what, rotated=True):
+    """fp8 K rows: codes as the oracle's but for near-ties (gh.check_fp8,
+    widened by FP8_ROT_SLACK x pair magnitude where the rows were rotated);
     per-token scales within 1e-5 relative; everything else bit-exact."""
     rows = gh.written_k_rows(case)
     assert np.array_equal(k_gpu[~rows], case.k_cache[~rows]), f"{what}: untouched rows changed"
-    d = gh.fp8_ulp_diff(k_gpu[rows], k_orc[rows])
-    frac = float((d != 0).sum() / max(d.size, 1))
-    stats = dict(max_ulp=int(d.max(initial=0)), diff_frac=frac, n=d.size)
-    assert stats["max_ulp"] <= gh.FP8_MAX_ULP and frac <= gh.FP8_MAX_DIFF_FRAC, f"{what}: {stats}"
+    slack = None
+    if rotated:
+        p = np.where(np.isnan(pre[rows]), 0.0, pre[rows])
+        slack = FP8_ROT_SLACK * pair_magnitude(p, case.interleaved)
+    stats = gh.check_fp8(k_gpu[rows], k_orc[rows], pre[rows], what, slack)
     if case.k_scale_mode == "per_token":
         assert np.array_equal(ks_gpu[~rows].view(np.uint32), case.k_scales[~rows].view(np.uint32))
         sg, so = ks_gpu[rows].astype(np.float64), ks_orc[rows].astype(np.float64)
@@ -100,8 +116,9 @@ def run_qk_fp8(orc, case, with_norm):
     q = gh.host_bf16(dev.q_out)
     k, ks = dev.k_host()
     assert int(dev.error_count.item()) == 0
-    q_o, k_o, ks_o = oracle_qk(orc, case, with_norm, with_scales=True)
-    stats = {"q": gh.check_bf16(q, q_o, "q"), "k": check_fp8_k(case, k, ks, k_o, ks_o, "k")}
+    q_o, k_o, ks_o, pre = oracle_qk(orc, case, with_norm, with_scales=True)
+    stats = {"q": gh.check_bf16(q, q_o, "q"),
+             "k": check_fp8_k(case, k, ks, k_o, ks_o, pre, "k")}
     _say(f"[qk8] {case.name}: {stats}")
 
 
@@ -155,10 +172,84 @@ def test_fp8_kv_norm(orc, idx):
     assert int(dev.error_count.item()) == 0
     k_o = case.k_cache.copy()
     ks_o = case.k_scales.copy()
+    with orc.fp8_probe(k_o) as pre:
+        orc.rms_norm_kv_cache_paged(k_o, case.layer_idx, case.row_offsets, case.cache_lengths,
+                                    case.page_table, case.gamma, case.epsilon, 0.25, total, True,
+                                    case.k_scale_mode, ks_o)
+    stats = check_fp8_k(case, k, ks, k_o, ks_o, pre, "kvnorm fp8", False)
+    _say(f"[kvnorm8] {case.name}: {stats}")
+
+
+@pytest.mark.parametrize("kind", ["bf16_mbc", "bf16_two_roundings", "bf16_32_heads",
+                                  "fp8_per_tensor", "fp8_per_token"])
+def test_kv_norm_per_token_statistic(orc, kind):
+    """per_head_norm=False: one statistic over the first len(gamma) columns of
+    all of a token's heads."""
+    if kind == "bf16_32_heads":
+        # the most heads one wave holds at head_dim 64: 4 groups of 8
+        rng = workloads.make_rng(6150)
+        case = workloads.build_qk("qk_h32", 6150, rng.integers(1, 40, size=5, endpoint=True),
+                                  rng.integers(0, 90, size=5, endpoint=True), Hq=32, Hkv=32,
+                                  D=64, page_size=16, max_seq_len=256, theta=10000.0,
+                                  interleaved=False, with_position_ids=False, norm_cols=64,
+                                  rng=rng)
+        mbc = True
+    elif kind.startswith("bf16"):
+        case = list(oracle_pins.small_qk_cases())[0]
+        mbc = kind == "bf16_mbc"
+    else:
+        case = list(oracle_pins.small_qk_fp8_cases())[0 if kind == "fp8_per_tensor" else 1]
+        mbc = True
+    Hkv, D = case.k_cache.shape[3:]
+    rng = workloads.make_rng(6100 + D)
+    cols = D - 24
+    gamma = workloads.bf16_bits(rng.uniform(0.5, 1.5, cols).astype(np.float32))
+    total = case.T - 1
+    _say(f"[kvnorm-tok] case={case.name} kind={kind} Hkv={Hkv} D={D} cols={cols} total={total}")
+    dev = gh.QkDevice(case)
+    dev.kv_norm(gh.dev_bf16(gamma), 0.125, total, mbc, per_head=False)
+    k, ks = dev.k_host()
+    assert int(dev.error_count.item()) == 0
+    k_o = case.k_cache.copy()
+    ks_o = None if case.k_scales is None else case.k_scales.copy()
+    if ks_o is not None:
+        with orc.fp8_probe(k_o) as pre:
+            orc.rms_norm_kv_cache_paged(k_o, case.layer_idx, case.row_offsets,
+                                        case.cache_lengths, case.page_table, gamma, case.epsilon,
+                                        0.125, total, mbc, case.k_scale_mode, ks_o,
+                                        per_head_norm=False)
+        stats = check_fp8_k(case, k, ks, k_o, ks_o, pre, "kvnorm per-token fp8", False)
+        _say(f"[kvnorm-tok] {stats}")
+        return
     orc.rms_norm_kv_cache_paged(k_o, case.layer_idx, case.row_offsets, case.cache_lengths,
-                                case.page_table, case.gamma, case.epsilon, 0.25, total, True,
-                                case.k_scale_mode, ks_o)
-    _say(f"[kvnorm8] {case.name}: {check_fp8_k(case, k, ks, k_o, ks_o, 'kvnorm fp8')}")
+                                case.page_table, gamma, case.epsilon, 0.125, total, mbc,
+                                per_head_norm=False)
+    rows = gh.written_k_rows(case)
+    assert np.array_equal(k[~rows], case.k_cache[~rows])
+    d = gh.bf16_ulp_diff(k[rows], k_o[rows])
+    frac = float((d != 0).sum() / max(d.size, 1))
+    _say(f"[kvnorm-tok] max_ulp={int(d.max())} diff_frac={frac}")
+    assert int(d.max()) <= (1 if mbc else 2)
+    assert frac <= gh.BF16_MAX_DIFF_FRAC
+    assert np.array_equal(k[rows][..., cols:], case.k_cache[rows][..., cols:])
+
+
+def test_kv_norm_per_token_statistic_llama(orc):
+    case = workloads.qk_generic()
+    rng = workloads.make_rng(6200)
+    gamma = workloads.bf16_bits(rng.uniform(0.5, 1.5, 128).astype(np.float32))
+    _say(f"[kvnorm-tok] case={case.name} T={case.T}")
+    dev = gh.QkDevice(case)
+    dev.kv_norm(gh.dev_bf16(gamma), 0.0, case.T, True, per_head=False)
+    k = gh.host_bf16(dev.k)
+    assert int(dev.error_count.item()) == 0
+    k_o = case.k_cache.copy()
+    orc.rms_norm_kv_cache_paged(k_o, case.layer_idx, case.row_offsets, case.cache_lengths,
+                                case.page_table, gamma, case.epsilon, 0.0, case.T, True,
+                                per_head_norm=False)
+    rows = gh.written_k_rows(case)
+    assert np.array_equal(k[~rows], case.k_cache[~rows])
+    gh.check_bf16(k[rows], k_o[rows], "kvnorm per-token llama")
 
 
 def run_qk(orc, case, with_norm):
