@@ -34,13 +34,18 @@ HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E peak, GB/s
 METRIC = "fused MLA RoPE+RMSNorm+FP8 cache-write: tokens/s and effective HBM GB/s (% of peak)"
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "paged_kv_cache_wavefront_amd", "csrc")
-# sources that decide what the MLA launch does (kernel, helpers, launch policy)
-KERNEL_SOURCES = ("mla_rope_rmsnorm_quant.hip", "pkv_device.h", "pkv_internal.h", "pkv_api.cpp")
+# sources that decide what a workload's launch does: its kernel, plus the
+# shared device helpers and launch policy
+COMMON_SOURCES = ("pkv_device.h", "pkv_internal.h", "pkv_api.cpp")
+KERNEL_OF = {"mla_prefill": "mla_rope_rmsnorm_quant.hip", "mla_decode": "mla_rope_rmsnorm_quant.hip",
+             "mla_mixed": "mla_rope_rmsnorm_quant.hip", "mla_tiny": "mla_rope_rmsnorm_quant.hip",
+             "qk_generic": "qk_rope_paged_ragged.hip", "kv_norm": "rms_norm_kv_cache_paged.hip",
+             "gather": "mla_gather_latent_paged.hip"}
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(workload: str = "mla_prefill") -> str:
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in (KERNEL_OF[workload],) + COMMON_SOURCES:
         h.update(open(os.path.join(CSRC, name), "rb").read())
     return h.hexdigest()
 
@@ -162,7 +167,7 @@ def profiled_traffic(name: str):
     m_h = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
     if not (m_b and m_h):
         return None
-    return float(m_b.group(1)) if m_h.group(1) == kernel_source_hash() else None
+    return float(m_b.group(1)) if m_h.group(1) == kernel_source_hash(name) else None
 
 
 # -- workloads -------------------------------------------------------------------------
@@ -246,7 +251,8 @@ def measure_siblings(main, steps, warmup):
             continue
         log(f"[bench] sibling {name}")
         r, label, _ = run_workload(name, steps, warmup)
-        out[name] = {"entry_point": entry, **summarize(label, r, steps, use_graph=True)}
+        out[name] = {"entry_point": entry, **summarize(label, r, steps, use_graph=True),
+                     "traffic": profiled_traffic(name)}
     return out
 
 
@@ -289,6 +295,19 @@ def calibrate_copy(steps, warmup, mib=1024):
                       "GBps": round(nbytes / avg / 1e9, 1)}))
 
 
+def measured_copy(steps, warmup, mib=300):
+    """Device-to-device copy on the same GPU (torch copy_, mib MiB each way):
+    the bandwidth a plain read-and-write stream reaches here, for context."""
+    import torch
+    n = mib * (1 << 20) // 2
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    _, avg, _ = time_launches(lambda: dst.copy_(src), steps, warmup)
+    moved = 2 * n * 2
+    return {"GBps": round(moved / avg / 1e9, 1), "bytes_per_copy": moved,
+            "how": f"torch copy_ of {mib} MiB bf16, device to device, average of {steps}"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -301,10 +320,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--source-hash", action="store_true",
-                    help="print the hash of the MLA kernel sources and exit")
+                    help="print the hash of the workload's kernel sources and exit")
     args = ap.parse_args()
     if args.source_hash:
-        print(kernel_source_hash())
+        print(kernel_source_hash(args.workload))
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -328,6 +347,7 @@ def main():
     if not args.no_cpu_baseline and args.workload.startswith("mla_"):
         log("[bench] cpu baseline (oracle)")
         cpu = cpu_baseline(case)
+    copy_ref = measured_copy(args.steps, args.warmup)
     traffic = profiled_traffic(args.workload)
     is_mla = args.workload.startswith("mla_")
     if is_mla:
@@ -360,6 +380,8 @@ def main():
         "config": config,
         "effective_GBps": gbps,
         "pct_of_hbm_peak": main_sum["pct_of_hbm_peak"],
+        "measured_copy": copy_ref,
+        "pct_of_measured_copy": round(100.0 * gbps / copy_ref["GBps"], 1),
         "kernel_us": {k: main_sum[k] for k in ("kernel_us_avg", "eager_us_p10_p50_p90",
                                                "graph_us_avg")},
         "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
