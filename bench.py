@@ -172,9 +172,32 @@ def profiled_traffic(name: str):
 
 # -- workloads -------------------------------------------------------------------------
 
+def time_cold(fn, samples: int = 20, flush_mib: int = 512):
+    """Per-launch durations with cold caches: before each sampled launch, a
+    reduction reads flush_mib MiB of other data (more than the 256 MiB
+    Infinity Cache and the L2s together), outside the event pair around the
+    launch.  Reading rather than writing leaves no dirty lines behind, so the
+    timed launch pays no write-back of the flush."""
+    import torch
+    junk = torch.ones((flush_mib << 20) // 4, dtype=torch.int32, device="cuda")
+    acc = torch.zeros((), dtype=torch.int64, device="cuda")
+    torch.cuda.synchronize()
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(samples)]
+    for a, b in pairs:
+        acc += junk.sum()
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    del junk
+    return np.array([a.elapsed_time(b) for a, b in pairs]) * 1e-3
+
+
 def measure(fn, tokens, nbytes, steps, warmup, graph=True):
     wall, avg, durs = time_launches(fn, steps, warmup)
     r = dict(T=tokens, bytes=nbytes, wall=wall, durs=durs, avg=avg, med=float(np.median(durs)))
+    r["cold_durs"] = time_cold(fn)
     r["graph_avg"] = time_graph(fn, steps, warmup) if graph else None
     return r
 
@@ -190,6 +213,8 @@ def summarize(name, r, steps, use_graph=False):
            "eager_us_avg": round(r["avg"] * 1e6, 2),
            "eager_us_p10_p50_p90": [round(float(np.percentile(r["durs"], q)) * 1e6, 2)
                                     for q in (10, 50, 90)],
+           "cold_us_p10_p50_p90": [round(float(np.percentile(r["cold_durs"], q)) * 1e6, 2)
+                                   for q in (10, 50, 90)],
            "graph_us_avg": round(r["graph_avg"] * 1e6, 2) if r["graph_avg"] else None,
            "tokens_per_s": round(r["T"] / t, 1),
            "effective_GBps": round(gbps, 1), "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2)}
@@ -383,7 +408,7 @@ def main():
         "measured_copy": copy_ref,
         "pct_of_measured_copy": round(100.0 * gbps / copy_ref["GBps"], 1),
         "kernel_us": {k: main_sum[k] for k in ("kernel_us_avg", "eager_us_p10_p50_p90",
-                                               "graph_us_avg")},
+                                               "cold_us_p10_p50_p90", "graph_us_avg")},
         "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbps / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "algorithmic_bytes": r["bytes"]},

@@ -276,7 +276,8 @@ hipError_t launch_mla(const MlaArgs& a, MlaOut mode, int heads_per_wave, hipStre
   const uint64_t waves = (uint64_t)a.total_tokens * a.chunks;
   const uint64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
   if (blocks == 0) return hipSuccess;
-  if (blocks > 0x7fffffffull) return hipErrorInvalidValue;
+  // the kernel numbers waves (block * waves per block + wave) in 32 bits
+  if (blocks * kWavesPerBlock > 0xffffffffull) return hipErrorInvalidValue;
   return a.q_out_f32 ? launch_q<true>(a, mode, heads_per_wave, (uint32_t)blocks, stream)
                      : launch_q<false>(a, mode, heads_per_wave, (uint32_t)blocks, stream);
 }

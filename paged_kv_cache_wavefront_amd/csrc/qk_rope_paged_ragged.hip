@@ -356,7 +356,8 @@ hipError_t launch_qk_rope(const QkArgs& a, int head_dim, bool interleaved, KMode
   const uint64_t waves = (uint64_t)a.total_tokens * a.chunks;
   const uint64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
   if (blocks == 0) return hipSuccess;
-  if (blocks > 0x7fffffffull) return hipErrorInvalidValue;
+  // the kernel numbers waves (block * waves per block + wave) in 32 bits
+  if (blocks * kWavesPerBlock > 0xffffffffull) return hipErrorInvalidValue;
   const uint32_t nb = (uint32_t)blocks;
   if (head_dim == 128) return launch_d<128>(a, interleaved, kmode, nb, stream);
   if (head_dim == 64) return launch_d<64>(a, interleaved, kmode, nb, stream);
