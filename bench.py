@@ -351,7 +351,7 @@ def main():
         print(kernel_source_hash(args.workload))
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: this benchmark runs on one GPU only (asked for --gpus {args.gpus}); "
               "the path needs no inter-GPU exchange and is measured on a single MI355X.",
               file=sys.stderr)
         sys.exit(2)

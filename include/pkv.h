@@ -74,7 +74,7 @@ typedef enum pkv_status {
   PKV_ERR_SHAPE = 2,       /* sizes inconsistent with each other */
   PKV_ERR_DTYPE = 3,       /* element type not accepted by this entry point */
   PKV_ERR_ALIGN = 4,       /* pointer or stride breaks the 16-byte rule */
-  PKV_ERR_UNSUPPORTED = 5, /* valid request that this build does not implement */
+  PKV_ERR_UNSUPPORTED = 5, /* valid request that this library does not implement */
   PKV_ERR_RANGE = 6,       /* index argument out of range (e.g. layer_idx) */
   PKV_ERR_LAUNCH = 7       /* the HIP runtime refused the kernel launch */
 } pkv_status;

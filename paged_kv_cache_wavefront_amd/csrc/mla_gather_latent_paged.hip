@@ -41,7 +41,7 @@ __global__ __launch_bounds__(256) void gather_kernel(const GatherArgs a) {
   const CacheView& cv = a.cache;
   const uint32_t B = a.batch;
 
-  // ---- round 1: request and slot of each row (lane j <- row r0 + j) ----------
+  // ---- stage 1: request and slot of each row (lane j <- row r0 + j) ----------
   uint32_t my_req = 0xffffffffu, my_slot = 0;
   if (B <= 4 * kWave) {
     uint32_t nxt[4], beg[4];
@@ -94,7 +94,7 @@ __global__ __launch_bounds__(256) void gather_kernel(const GatherArgs a) {
     }
   }
 
-  // ---- round 2: page of each row, its source offset and scale ----------------
+  // ---- stage 2: page of each row, its source offset and scale ----------------
   bool row_ok = false;
   uint64_t row_src = 0;  // byte offset of the row inside this layer's pool
   float row_scale = 1.0f;
@@ -124,7 +124,7 @@ __global__ __launch_bounds__(256) void gather_kernel(const GatherArgs a) {
     if (row_ok && a.out_scales != nullptr) a.out_scales[r0 + lane] = row_scale;
   }
 
-  // ---- round 3: copies -------------------------------------------------------------
+  // ---- stage 3: copies -------------------------------------------------------------
   // piece g = i * 64 + lane of the wave's rows: row g / ppr, piece g % ppr.  A
   // piece is 16 input bytes, except for fp8 -> bf16 where it is 8 input bytes
   // so that every lane stores 16 contiguous output bytes.

@@ -17,7 +17,7 @@
 //   no LDS round trip, and every load and store covers full 128-byte lines.
 // * q and latent are read with non-temporal loads (streamed once); all q
 //   loads of the wave are issued before the address chain, which takes two
-//   dependent rounds ({offsets, cache lengths}, then {freqs row, page-table
+//   dependent steps ({offsets, cache lengths}, then {freqs row, page-table
 //   entry}) and hides behind the bulk traffic.
 // * The 16 cos/sin floats a lane needs sit contiguously in the freqs row and
 //   are the same for every head: one 64-byte load per lane per token, kept in
@@ -143,7 +143,7 @@ __global__ __launch_bounds__(256) void mla_kernel(const MlaArgs a) {
   }
 
   // ---- address chain -----------------------------------------------------------
-  // round 1: request and slot (= position); round 2: the freqs row and the
+  // step 1: request and slot (= position); step 2: the freqs row and the
   // page-table entry, both needing only the slot, issued together.
   const CacheView& cv = a.cache;
   const TokenSlot ts = find_slot(a.offsets, a.batch, cv.cache_lengths, t, lane);

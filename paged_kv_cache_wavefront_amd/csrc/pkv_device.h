@@ -210,10 +210,10 @@ __device__ __forceinline__ uint32_t lane_u32(uint32_t v, uint32_t lane) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, (int)lane);
 }
 
-// First round of the address chain: the request owning token t and the
+// First step of the address chain: the request owning token t and the
 // token's cache slot (prior length + index within the request).  For batches
 // of up to 256 requests every lane loads entries i, i+64, ... of the offsets
-// and the prior lengths in one round; the request is the number of offsets
+// and the prior lengths in one step; the request is the number of offsets
 // <= t (ballot), and its start and prior length are read from the owning lane.
 struct TokenSlot {
   uint32_t request;
@@ -261,7 +261,7 @@ __device__ __forceinline__ TokenSlot find_slot(const uint32_t* __restrict__ offs
   return r;
 }
 
-// Second round: physical page and offset of a slot.  Returns false when the
+// Second step: physical page and offset of a slot.  Returns false when the
 // slot lies past the request's page-table row or the page id past the pool.
 struct PageSlot {
   uint32_t page;

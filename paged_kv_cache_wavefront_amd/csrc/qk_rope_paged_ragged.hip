@@ -180,8 +180,8 @@ __global__ __launch_bounds__(256) void qk_rope_kernel(const QkArgs a) {
   const uint32_t qo_off = 2 * (hl * (uint32_t)a.qo_head + (uint32_t)col);
   const int64_t qi_step = 2 * HPI * a.qi_head, qo_step = 2 * HPI * a.qo_head;
 
-  // ---- address chain: round 1 = {position id(s), offsets, prior lengths};
-  //      round 2 = {freqs row(s), page-table entry} ---------------------------------
+  // ---- address chain: step 1 = {position id(s), offsets, prior lengths};
+  //      step 2 = {freqs row(s), page-table entry} ----------------------------------
   const CacheView& cv = a.cache;
   uint32_t pid[3] = {0, 0, 0};
   if (a.position_ids != nullptr) {
