@@ -34,9 +34,9 @@ HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E peak, GB/s
 METRIC = "fused MLA RoPE+RMSNorm+FP8 cache-write: tokens/s and effective HBM GB/s (% of peak)"
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "paged_kv_cache_wavefront_amd", "csrc")
-# sources that decide what a workload's launch does: its kernel, plus the
-# shared device helpers and launch policy
-COMMON_SOURCES = ("pkv_device.h", "pkv_internal.h", "pkv_api.cpp")
+# sources that decide what a workload's launch does: its kernel file (kernel
+# and launch policy) plus the shared device helpers and argument structs
+COMMON_SOURCES = ("pkv_device.h", "pkv_internal.h")
 KERNEL_OF = {"mla_prefill": "mla_rope_rmsnorm_quant.hip", "mla_decode": "mla_rope_rmsnorm_quant.hip",
              "mla_mixed": "mla_rope_rmsnorm_quant.hip", "mla_tiny": "mla_rope_rmsnorm_quant.hip",
              "qk_generic": "qk_rope_paged_ragged.hip", "kv_norm": "rms_norm_kv_cache_paged.hip",

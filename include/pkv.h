@@ -145,7 +145,8 @@ typedef struct pkv_paged_cache {
  *                   PER_TENSOR or PER_TOKEN, or BF16 with scale mode NONE;
  *                   num_heads 1, head_dim kv_norm_dim + rope_dim
  *   stream          hipStream_t to enqueue on (NULL = default stream)
- * Supported here: rope_dim 64, kv_norm_dim 512, any num_heads >= 0.
+ * Supported here: rope_dim 64, kv_norm_dim 512, any num_heads >= 0, q head
+ * strides up to 2^27 elements (else PKV_ERR_UNSUPPORTED).
  */
 int mla_rope_rmsnorm_quant(void* q_rope_out, int64_t qo_tok_stride, int64_t qo_head_stride,
                            const void* q_rope, int64_t qi_tok_stride, int64_t qi_head_stride,
@@ -182,7 +183,8 @@ int mla_rope_rmsnorm_quant(void* q_rope_out, int64_t qo_tok_stride, int64_t qo_h
  *                   mrope_section)
  *   mrope_section   (host) u32 [3] or NULL
  *   k_norm_gamma    bf16 [k_norm_cols] or NULL; 0 < k_norm_cols <= head_dim
- * Supported here: head_dim 64 or 128.
+ * Supported here: head_dim 64 or 128; q and K head strides up to 2^27
+ * elements (else PKV_ERR_UNSUPPORTED).
  */
 int qk_rope_paged_ragged(void* q_out, int64_t qo_tok_stride, int64_t qo_head_stride,
                          const void* q_proj, int64_t qi_tok_stride, int64_t qi_head_stride,

@@ -272,6 +272,13 @@ hipError_t launch_q(const MlaArgs& a, MlaOut mode, int heads_per_wave, uint32_t 
 
 }  // namespace
 
+// 32 heads (4 instructions of 8 heads) per wave measured best on 128-head
+// prefill and decode batches: small enough to keep 8 waves per SIMD resident
+// and to spread a token over 4 waves, large enough to amortise each wave's
+// address chain.  Heads beyond a multiple of 16 are never padded past the
+// next multiple of 16.
+uint32_t mla_heads_per_wave(uint32_t heads) { return heads > 16 ? 32 : 16; }
+
 hipError_t launch_mla(const MlaArgs& a, MlaOut mode, int heads_per_wave, hipStream_t stream) {
   const uint64_t waves = (uint64_t)a.total_tokens * a.chunks;
   const uint64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;

@@ -15,6 +15,10 @@ constexpr uint32_t kMlaRope = 64;
 constexpr uint32_t kMlaNope = 512;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Head strides the kernels add to per-lane 32-bit byte offsets (up to 7
+// heads away, 4-byte elements): at most 2^27 elements.
+constexpr int64_t kMaxHeadStride = int64_t(1) << 27;
 bool mult(int64_t v, int64_t k) { return v >= 0 && v % k == 0; }
 
 size_t elem_bytes(int32_t dtype) { return dtype == PKV_DTYPE_BF16 ? 2 : 1; }
@@ -76,13 +80,6 @@ float* k_scales_of(const pkv_paged_cache* c, uint32_t layer_idx, pkv::KMode km) 
   return c->scales;
 }
 
-// Heads per wave for the MLA kernel.  32 heads (4 instructions of 8 heads)
-// per wave measured best on 128-head prefill and decode batches: small
-// enough to keep 7 waves per SIMD resident and to spread a token over 4
-// waves, large enough to amortise each wave's address chain.  Heads beyond
-// a multiple of 16 are never padded past the next multiple of 16.
-int mla_heads_per_wave(uint32_t /*tokens*/, uint32_t heads) { return heads > 16 ? 32 : 16; }
-
 }  // namespace
 
 extern "C" {
@@ -142,6 +139,8 @@ int mla_rope_rmsnorm_quant(void* q_rope_out, int64_t qo_tok_stride, int64_t qo_h
       !mult(qo_head_stride, qo_align) || !mult(qi_tok_stride, 8) || !mult(qi_head_stride, 8) ||
       !mult(kv_row_stride, 8))
     return PKV_ERR_ALIGN;
+  if (qi_head_stride > kMaxHeadStride || qo_head_stride > kMaxHeadStride)
+    return PKV_ERR_UNSUPPORTED;
 
   pkv::MlaArgs a{};
   a.q_out = q_rope_out;
@@ -157,7 +156,7 @@ int mla_rope_rmsnorm_quant(void* q_rope_out, int64_t qo_tok_stride, int64_t qo_h
   a.batch = batch_size;
   a.total_tokens = total_tokens;
   a.num_heads = num_heads;
-  const int hpw = mla_heads_per_wave(total_tokens, num_heads);
+  const int hpw = (int)pkv::mla_heads_per_wave(num_heads);
   a.chunks = num_heads == 0 ? 1u : (num_heads + (uint32_t)hpw - 1) / (uint32_t)hpw;
   a.freqs = freqs_cis;
   a.max_seq_len = max_seq_len;
@@ -205,6 +204,9 @@ int qk_rope_paged_ragged(void* q_out, int64_t qo_tok_stride, int64_t qo_head_str
       !aligned16(k_norm_gamma) || !mult(qo_tok_stride, 8) || !mult(qo_head_stride, 8) ||
       !mult(qi_tok_stride, 8) || !mult(qi_head_stride, 8))
     return PKV_ERR_ALIGN;
+  if (qi_head_stride > kMaxHeadStride || qo_head_stride > kMaxHeadStride ||
+      k_cache->head_stride > kMaxHeadStride)
+    return PKV_ERR_UNSUPPORTED;
 
   pkv::QkArgs a{};
   a.q_out = static_cast<uint16_t*>(q_out);

@@ -103,6 +103,12 @@ def test_mla_validation(pkv):
     assert call_mla(pkv, mla_cache(pkv), T=0, qo_dtype=pkv.PKV_DTYPE_F32,
                     qostride=4 * 64 + 4) == OK
     assert call_mla(pkv, mla_cache(pkv), qo_dtype=pkv.PKV_DTYPE_F32, qostride=4 * 64 + 2) == ALIGN
+    # per-lane byte offsets are 32-bit: head strides above 2^27 elements refused
+    lib = pkv.library()
+    big = (1 << 27) + 8
+    assert lib.mla_rope_rmsnorm_quant(FAKE, 4 * big, big, FAKE, 4 * big, big, FAKE, 576, FAKE, 2,
+                                      16, 4, 64, 512, FAKE, 64, FAKE, 1e-6,
+                                      ctypes.byref(mla_cache(pkv)), 1, 0, None) == UNSUP
     assert call_mla(pkv, mla_cache(pkv, slot_stride=584)) == ALIGN
     assert call_mla(pkv, mla_cache(pkv, data=FAKE + 8)) == ALIGN
     # nothing to do: accepted without a launch
@@ -134,6 +140,9 @@ def test_qk_validation(pkv):
     assert call_qk(pkv, kcache(pkv, scale_mode=pkv.PKV_SCALE_PER_TENSOR)) == DTYPE
     assert call_qk(pkv, kcache(pkv, head_dim=96), D=96) == UNSUP
     assert call_qk(pkv, kcache(pkv), D=64) == SHAPE                    # q vs cache head_dim
+    big = (1 << 27) + 8
+    assert call_qk(pkv, kcache(pkv, head_stride=big, slot_stride=8 * big,
+                              page_stride=16 * 8 * big, layer_stride=8 * 16 * 8 * big)) == UNSUP
     assert call_qk(pkv, kcache(pkv), gamma=FAKE, cols=129) == SHAPE
     assert call_qk(pkv, kcache(pkv), gamma=FAKE, cols=0) == SHAPE
     assert call_qk(pkv, kcache(pkv), layer=5) == RANGE
