@@ -88,6 +88,8 @@ def _load() -> ctypes.CDLL:
         vp, ctypes.c_int32, i64, vp, vp, vp, u32, u32, cache_p, u32, vp]
     lib.pkv_status_string.restype = ctypes.c_char_p
     lib.pkv_status_string.argtypes = [ctypes.c_int]
+    lib.pkv_stream_copy.restype = ctypes.c_int
+    lib.pkv_stream_copy.argtypes = [vp, vp, ctypes.c_uint64, u32, vp]
     return lib
 
 
@@ -220,3 +222,13 @@ def mla_gather_latent_paged(out: torch.Tensor, kv_row_offsets: torch.Tensor,
         _ptr(kv_row_offsets), kv_row_offsets.numel() - 1, out.shape[0], ctypes.byref(cache),
         int(layer_idx), _stream(stream))
     _check("mla_gather_latent_paged", st)
+
+
+def pkv_stream_copy(dst: torch.Tensor, src: torch.Tensor, blocks: int, stream=None) -> None:
+    """Measurement helper (C: ``pkv_stream_copy``, include/pkv_bench.h): copy
+    src's bytes into dst with a plain streaming kernel of ``blocks`` blocks."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("dst smaller than src")
+    st = _lib.pkv_stream_copy(_ptr(src), _ptr(dst), nbytes, int(blocks), _stream(stream))
+    _check("pkv_stream_copy", st)

@@ -1,5 +1,5 @@
 """The C ABI on the CPU: the library loads, exports every function that
-include/pkv.h declares, and rejects bad arguments on the host with the
+include/*.h declares, and rejects bad arguments on the host with the
 documented status before touching the device (no kernel is launched here)."""
 import ctypes
 import os
@@ -9,16 +9,19 @@ import subprocess
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "pkv.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 OK, NULL, SHAPE, DTYPE, ALIGN, UNSUP, RANGE, LAUNCH = range(8)
 FAKE = 0x10000          # 16-byte aligned stand-in for a device pointer (never dereferenced)
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:int|const char\s*\*)\s*(\w+)\s*\(", text, flags=re.M)))
+    names = set()
+    for header in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(header).read(), flags=re.S)
+        names |= set(re.findall(r"^\s*(?:int|const char\s*\*)\s*(\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -30,7 +33,7 @@ def pkv():
 def test_header_declares_entry_points():
     assert declared_functions() == sorted(["mla_rope_rmsnorm_quant", "qk_rope_paged_ragged",
                                            "rms_norm_kv_cache_paged", "mla_gather_latent_paged",
-                                           "pkv_status_string"])
+                                           "pkv_status_string", "pkv_stream_copy"])
 
 
 def test_library_exports_every_declared_function(pkv):
@@ -47,6 +50,15 @@ def test_binding_names_match_header(pkv):
     for name in declared_functions():
         if name != "pkv_status_string":
             assert callable(getattr(pkv, name)), name
+
+
+def test_stream_copy_validation(pkv):
+    lib = pkv.library()
+    assert lib.pkv_stream_copy(None, FAKE, 16, 1, None) == NULL
+    assert lib.pkv_stream_copy(FAKE, FAKE + 4096, 16, 0, None) == SHAPE
+    assert lib.pkv_stream_copy(FAKE + 8, FAKE + 4096, 16, 1, None) == ALIGN
+    assert lib.pkv_stream_copy(FAKE, FAKE + 4096, 24, 1, None) == ALIGN
+    assert lib.pkv_stream_copy(FAKE, FAKE + 4096, 0, 1, None) == OK
 
 
 def test_status_strings(pkv):
