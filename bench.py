@@ -217,34 +217,102 @@ def summarize(name, r, steps, use_graph=False):
                                    for q in (10, 50, 90)],
            "graph_us_avg": round(r["graph_avg"] * 1e6, 2) if r["graph_avg"] else None,
            "tokens_per_s": round(r["T"] / t, 1),
+           "buffer_rotation": r.get("sets"),
            "effective_GBps": round(gbps, 1), "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2)}
     return out
 
 
+# Buffer rotation.  Consecutive steps write different memory: a step that
+# rewrote the previous step's output buffer would find part of it still in
+# the 256 MiB Infinity Cache as dirty lines and overwrite them there, so
+# some of its writes would never reach HBM.  Each workload cycles over
+# enough output sets that the distinct bytes written per cycle reach
+# ROTATE_BYTES, within a device-memory budget for the copies.
+ROTATE_BYTES = 1 << 30
+ROTATE_BUDGET = 8 << 30
+
+
+def rotation_count(written_bytes: int, set_bytes: int, cap: int = 64) -> int:
+    want = -(-ROTATE_BYTES // max(written_bytes, 1))
+    fit = max(2, ROTATE_BUDGET // max(set_bytes, 1))
+    return int(max(2, min(want, fit, cap)))
+
+
+def cycle(fns):
+    """One callable that runs fns[0], fns[1], ... in turn."""
+    state = {"i": 0}
+
+    def step():
+        fns[state["i"] % len(fns)]()
+        state["i"] += 1
+    return step
+
+
 def run_workload(name, steps, warmup):
-    """(summary, case) for one named workload of any entry point."""
+    """(summary, label, case) for one named workload of any entry point; the
+    summary's "sets" is the number of buffer sets the steps rotate over."""
+    import torch
     import workloads
+    import paged_kv_cache_wavefront_amd as pkv
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     import gpu_helpers as gh
     if name.startswith("mla_"):
         case = workloads.NAMED[name]()
-        dev = gh.MlaDevice(case)
-        r = measure(dev.run, case.T, mla_bytes(case), steps, warmup)
+        q_out_bytes = case.q.size * 2
+        written = q_out_bytes + case.T * case.latent.shape[1]
+        set_bytes = 2 * q_out_bytes + case.latent.nbytes + case.cache.nbytes
+        n = rotation_count(written, set_bytes)
+        if n * written >= ROTATE_BYTES:
+            # whole device sets: inputs, outputs and cache pool
+            devs = [gh.MlaDevice(case) for _ in range(n)]
+            fns = [d.run for d in devs]
+            how = f"{n} sets of q, q_out, latent and cache pool"
+        else:
+            # the pool is large and the new rows few: rotate q_out only
+            n = rotation_count(q_out_bytes, q_out_bytes, cap=256)
+            dev = gh.MlaDevice(case)
+            outs = [dev.q_out] + [torch.empty_like(dev.q_out) for _ in range(n - 1)]
+
+            def make(o):
+                return lambda: pkv.mla_rope_rmsnorm_quant(o, dev.q_in, dev.latent, dev.offsets,
+                                                          dev.freqs, dev.gamma, case.epsilon,
+                                                          dev.desc, case.layer_idx)
+            fns = [make(o) for o in outs]
+            devs = (dev, outs)
+            how = f"{n} q_out buffers (one cache pool; its new rows are {case.T * 576} bytes)"
+        r = measure(cycle(fns), case.T, mla_bytes(case), steps, warmup)
         label = name
     elif name == "qk_generic":
         case = workloads.qk_generic()
-        dev = gh.QkDevice(case)
-        r = measure(lambda: dev.rope(True), case.T, qk_bytes(case, True), steps, warmup)
+        written = case.q.size * 2 + int(gh.written_k_rows(case).sum()) * case.k_cache[0, 0, 0].nbytes
+        set_bytes = 2 * case.q.nbytes + case.k_cache.nbytes
+        n = rotation_count(written, set_bytes)
+        devs = [gh.QkDevice(case) for _ in range(n)]
+        fns = [(lambda d: (lambda: d.rope(True)))(d) for d in devs]
+        how = f"{n} sets of q, q_out and K pool"
+        r = measure(cycle(fns), case.T, qk_bytes(case, True), steps, warmup)
         label = "qk_generic (interleaved, position ids, fused per-head K norm)"
     elif name == "kv_norm":
         case = workloads.qk_generic()
-        dev = gh.QkDevice(case)
-        r = measure(lambda: dev.kv_norm(dev.gamma, 0.0, case.T, True), case.T,
-                    kv_norm_bytes(case, 128), steps, warmup)
+        written = int(gh.written_k_rows(case).sum()) * case.k_cache[0, 0, 0].nbytes
+        n = rotation_count(written, case.k_cache.nbytes)
+        base = gh.QkDevice(case)
+        descs = []
+        pools = [base.k] + [base.k.clone() for _ in range(n - 1)]
+        for pool in pools:
+            descs.append(pkv.paged_cache(pool, base.cache_lengths, base.page_table,
+                                         pkv.PKV_SCALE_NONE, None, base.error_count))
+
+        def make(dsc):
+            return lambda: pkv.rms_norm_kv_cache_paged(dsc, case.layer_idx, base.gamma,
+                                                       case.epsilon, 0.0, case.T, base.offsets,
+                                                       True, True)
+        fns = [make(d) for d in descs]
+        devs = (base, pools, descs)
+        how = f"{n} K pools"
+        r = measure(cycle(fns), case.T, kv_norm_bytes(case, 128), steps, warmup)
         label = "qk_generic K cache (8 heads x 128, gamma 128)"
     elif name == "gather":
-        import torch
-        import paged_kv_cache_wavefront_amd as pkv
         case = workloads.mla_decode()
         ctx = case.cache_lengths.astype(np.int64) + 1
         kvo = np.zeros(ctx.size + 1, np.uint32)
@@ -254,14 +322,21 @@ def run_workload(name, steps, warmup):
         desc = pkv.paged_cache(cache, None, gh.dev_u32(case.page_table), pkv.PKV_SCALE_PER_TENSOR,
                                gh.dev_f32(np.array([case.tensor_scale], np.float32)))
         kv = gh.dev_u32(kvo)
-        out = torch.empty((rows, 576), dtype=torch.bfloat16, device="cuda")
-        keep = (cache, kv, out)
-        r = measure(lambda: pkv.mla_gather_latent_paged(out, kv, desc, case.layer_idx), rows,
-                    gather_bytes(rows, case.B, case.meta["page_size"]), steps, warmup)
-        r["keep"] = keep
+        n = rotation_count(rows * 1152, rows * 1152)
+        outs = [torch.empty((rows, 576), dtype=torch.bfloat16, device="cuda") for _ in range(n)]
+
+        def make(o):
+            return lambda: pkv.mla_gather_latent_paged(o, kv, desc, case.layer_idx)
+        fns = [make(o) for o in outs]
+        devs = (cache, kv, outs, desc)
+        how = f"{n} output buffers"
+        r = measure(cycle(fns), rows, gather_bytes(rows, case.B, case.meta["page_size"]), steps,
+                    warmup)
         label = f"gather of {case.B} request contexts ({rows} rows) fp8 -> bf16"
     else:
         raise ValueError(name)
+    r["keep"] = devs
+    r["sets"] = how
     return r, label, case
 
 

@@ -34,7 +34,7 @@ __global__ __launch_bounds__(256) void gather_kernel(const GatherArgs a) {
   constexpr uint32_t RPW = IN_FP8 ? 16 : 8;  // rows per wave
   const int lane = threadIdx.x & (kWave - 1);
   const uint32_t wave =
-      xcd_block(blockIdx.x, gridDim.x) * kWavesPerBlock + (threadIdx.x / kWave);
+      blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
   const uint32_t r0 = uniform(wave * RPW);
   if (r0 >= a.total_rows) return;
   const uint32_t nrows = min(RPW, a.total_rows - r0);

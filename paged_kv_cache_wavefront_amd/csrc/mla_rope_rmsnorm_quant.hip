@@ -15,8 +15,9 @@
 //   values 32 + 8(7-k) .. (second half, mirrored), so the rotate-half partner
 //   of lane k is lane 7-k and arrives with one DPP row_half_mirror per dword:
 //   no LDS round trip, and every load and store covers full 128-byte lines.
-// * q and latent are read with non-temporal loads (streamed once); all q
-//   loads of the wave are issued before the address chain, which takes two
+// * q and latent are read and q_rope_output written with non-temporal
+//   accesses (streamed once); all q loads of the wave are issued before the
+//   address chain, which takes two
 //   dependent steps ({offsets, cache lengths}, then {freqs row, page-table
 //   entry}) and hides behind the bulk traffic.
 // * The 16 cos/sin floats a lane needs sit contiguously in the freqs row and
@@ -100,12 +101,12 @@ __device__ __forceinline__ void rotate_store_q(const uint4 (&q)[NI], const float
     if (GUARD && h_lane + 8 * i >= num_heads) continue;
     char* p = base + i * step + lane_off;
     if constexpr (QF32) {
-      store16(p, make_uint4(__float_as_uint(own[0]), __float_as_uint(own[1]),
+      store16_stream(p, make_uint4(__float_as_uint(own[0]), __float_as_uint(own[1]),
                             __float_as_uint(own[2]), __float_as_uint(own[3])));
-      store16(p + 16, make_uint4(__float_as_uint(own[4]), __float_as_uint(own[5]),
+      store16_stream(p + 16, make_uint4(__float_as_uint(own[4]), __float_as_uint(own[5]),
                                  __float_as_uint(own[6]), __float_as_uint(own[7])));
     } else {
-      store16(p, pack8_bf16(own));
+      store16_stream(p, pack8_bf16(own));
     }
   }
 }
@@ -115,7 +116,7 @@ template <int NI, MlaOut MODE, bool QF32>
 __global__ __launch_bounds__(256) void mla_kernel(const MlaArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   const uint32_t wave =
-      xcd_block(blockIdx.x, gridDim.x) * kWavesPerBlock + (threadIdx.x / kWave);
+      blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
   const uint32_t t = uniform(wave / a.chunks);
   const uint32_t chunk = uniform(wave - t * a.chunks);
   if (t >= a.total_tokens) return;
@@ -203,8 +204,8 @@ __global__ __launch_bounds__(256) void mla_kernel(const MlaArgs a) {
     uint16_t* row = static_cast<uint16_t*>(cv.layer_base) + row_elems;
 #pragma unroll
     for (int k = 0; k < 8; ++k) xg[k] *= r;
-    store16(row + 8 * lane, pack8_bf16(xg));
-    if (lane < 8) store16(row + kNope + 8 * hl.chunk, pack8_bf16(tv));
+    store16_stream(row + 8 * lane, pack8_bf16(xg));
+    if (lane < 8) store16_stream(row + kNope + 8 * hl.chunk, pack8_bf16(tv));
     return;
   } else {
     float inv;

@@ -1,6 +1,11 @@
 // pkv_device.h -- device-side building blocks shared by the gfx950 kernels:
-// bf16 / fp8 packing, wave64 cross-lane reductions, the XCD-aware block
-// order, and the ragged / paged address chain.
+// bf16 / fp8 packing, wave64 cross-lane reductions, streaming loads and
+// stores, and the ragged / paged address chain.
+//
+// Launch order: every kernel numbers its waves in hardware block order, so
+// consecutive tokens are spread over the 8 XCDs and the whole chip streams
+// through one window of addresses at a time; giving each XCD its own
+// contiguous token range measured slower (more DRAM streams open at once).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -9,7 +14,6 @@
 namespace pkv {
 
 constexpr int kWave = 64;
-constexpr uint32_t kNumXcd = 8;  // MI355X: 8 XCDs, workgroups dealt round-robin
 
 // ---- bf16 <-> fp32 ---------------------------------------------------------
 
@@ -96,9 +100,16 @@ __device__ __forceinline__ uint4 load16_stream(const void* p) {
 }
 
 __device__ __forceinline__ uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
-__device__ __forceinline__ void store16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
 
-// 16-byte non-temporal store (large outputs written once, never re-read here).
+// 8-byte non-temporal load.
+__device__ __forceinline__ uint2 load8_stream(const void* p) {
+  const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+  return make_uint2(v.x, v.y);
+}
+
+// 16-byte non-temporal store.  Every output of the path is written with these:
+// a store that allocates in the Infinity Cache leaves dirty lines there whose
+// write-back the next kernel pays for.
 __device__ __forceinline__ void store16_stream(void* p, uint4 v) {
   const u32x4_t w = {v.x, v.y, v.z, v.w};
   __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(p));
@@ -173,17 +184,6 @@ __device__ __forceinline__ float wave_max(float v) {
   v = group_max<16>(v);
   return fmaxf(fmaxf(lane_value(v, 0), lane_value(v, 16)),
                fmaxf(lane_value(v, 32), lane_value(v, 48)));
-}
-
-// ---- launch order ------------------------------------------------------------
-
-// Hardware block b runs on XCD b % 8.  Renumber blocks so that each XCD
-// receives one contiguous range of logical blocks: neighbouring tokens (whose
-// cache rows share 128-byte lines) then stay in one XCD's L2.
-__device__ __forceinline__ uint32_t xcd_block(uint32_t hw_block, uint32_t num_blocks) {
-  const uint32_t xcd = hw_block % kNumXcd, local = hw_block / kNumXcd;
-  const uint32_t per = num_blocks / kNumXcd, extra = num_blocks % kNumXcd;
-  return xcd * per + (xcd < extra ? xcd : extra) + local;
 }
 
 __device__ __forceinline__ uint32_t uniform(uint32_t v) {

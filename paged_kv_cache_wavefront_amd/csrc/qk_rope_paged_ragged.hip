@@ -16,7 +16,8 @@
 //   k >= D/16 holds the second-half values of pairs 8(D/8-1-k)..; the partner
 //   of lane k is lane D/8-1-k, reached by one DPP mirror per dword.
 // Pair i needs freqs columns 2i, 2i+1: 8 or 16 consecutive floats per lane,
-// loaded once per token.  Q is read with non-temporal loads.
+// loaded once per token.  Q is read, and Q and K are written, with
+// non-temporal accesses.
 //
 // Multimodal RoPE: three position rows; pair i uses the row of its section
 // (temporal / height / width pair ranges), cos/sin fetched per pair.
@@ -148,7 +149,7 @@ __device__ __forceinline__ void q_rope(const char* src, char* dst, int64_t in_st
     if constexpr (!INTER) unpack8(mirror16<LP>(v[i]), par);
     rotate_plain<INTER>(own, par, cs);
     if (GUARD && h_lane + HPI * i >= num_heads) continue;
-    store16(dst + i * out_step + out_off, pack8_bf16(own));
+    store16_stream(dst + i * out_step + out_off, pack8_bf16(own));
   }
 }
 
@@ -160,7 +161,7 @@ __global__ __launch_bounds__(256) void qk_rope_kernel(const QkArgs a) {
   constexpr int LP = Geo::kLanesPerHead, HPI = Geo::kHeadsPerInstr;
   const int lane = threadIdx.x & (kWave - 1);
   const uint32_t wave =
-      xcd_block(blockIdx.x, gridDim.x) * kWavesPerBlock + (threadIdx.x / kWave);
+      blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
   const uint32_t t = uniform(wave / a.chunks);
   const uint32_t chunk = uniform(wave - t * a.chunks);
   if (t >= a.total_tokens) return;
@@ -302,7 +303,7 @@ __global__ __launch_bounds__(256) void qk_rope_kernel(const QkArgs a) {
       rotate_scaled<INTER>(own, par, cs, pre_own, pre_par, post);
     }
     if constexpr (KM == KMode::Bf16) {
-      if (valid) store16(p, pack8_bf16(own));
+      if (valid) store16_stream(p, pack8_bf16(own));
     } else {
       float inv = tensor_inv;
       if constexpr (KM == KMode::Fp8PerToken) {
@@ -316,7 +317,7 @@ __global__ __launch_bounds__(256) void qk_rope_kernel(const QkArgs a) {
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) own[j] *= inv;
-      if (valid) *reinterpret_cast<uint2*>(p) = pack8_fp8(own);
+      if (valid) store8_stream(p, pack8_fp8(own));
     }
   }
 }

@@ -20,7 +20,9 @@
 // reduces with DPP inside the head's lanes.  An fp8 cache is read as
 // code * scale; a per-tensor cache re-encodes the normalised columns with its
 // scale, a per-token cache stores max|y| / 448 per head and re-encodes the
-// whole head.
+// whole head.  K rows are read and written with non-temporal accesses (they
+// are touched once; plain loads measured slower here, before the
+// non-temporal stores of the same lines).
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -40,7 +42,7 @@ __global__ __launch_bounds__(256) void kv_norm_kernel(const KvNormArgs a) {
   constexpr bool kWholeHead = KM == KMode::Fp8PerToken;
   const int lane = threadIdx.x & (kWave - 1);
   const uint32_t t =
-      uniform(xcd_block(blockIdx.x, gridDim.x) * kWavesPerBlock + (threadIdx.x / kWave));
+      uniform(blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave));
   if (t >= a.total_tokens) return;
   const int m = lane % LP;
   const uint32_t hl = (uint32_t)(lane / LP);
@@ -92,13 +94,13 @@ __global__ __launch_bounds__(256) void kv_norm_kernel(const KvNormArgs a) {
       const char* p = krow + EB * (int64_t)h * cv.head_stride;
       if constexpr (KM == KMode::Bf16) {
         uint4 raw = make_uint4(0, 0, 0, 0);
-        if (valid) raw = *reinterpret_cast<const uint4*>(p);
+        if (valid) raw = load16_stream(p);
         unpack8(raw, x[it]);
       } else {
         uint2 raw = make_uint2(0, 0);
         float ks = 0.0f;
         if (valid) {
-          raw = *reinterpret_cast<const uint2*>(p);
+          raw = load8_stream(p);
           ks = KM == KMode::Fp8PerTensor ? tensor_scale : a.k_scales[slot_head0 + h];
         }
         unpack8_fp8(raw.x, raw.y, x[it]);
@@ -141,7 +143,7 @@ __global__ __launch_bounds__(256) void kv_norm_kernel(const KvNormArgs a) {
       if constexpr (KM == KMode::Bf16) {
         if (valid) {
           if (col0 + 8 <= C) {
-            *reinterpret_cast<uint4*>(p) = pack8_bf16(x[it]);
+            store16_stream(p, pack8_bf16(x[it]));
           } else {
             uint16_t* e = reinterpret_cast<uint16_t*>(p);
 #pragma unroll
@@ -165,7 +167,7 @@ __global__ __launch_bounds__(256) void kv_norm_kernel(const KvNormArgs a) {
         const uint2 codes = pack8_fp8(x[it]);
         if (valid) {
           if (kWholeHead || col0 + 8 <= C) {
-            *reinterpret_cast<uint2*>(p) = codes;
+            store8_stream(p, codes);
           } else {
             uint8_t* e = reinterpret_cast<uint8_t*>(p);
             const uint32_t w[2] = {codes.x, codes.y};
