@@ -488,6 +488,7 @@ def main():
         "config": config,
         "effective_GBps": gbps,
         "pct_of_hbm_peak": main_sum["pct_of_hbm_peak"],
+        "buffer_rotation": main_sum["buffer_rotation"],
         "measured_copy": copy_ref,
         "pct_of_measured_copy": round(100.0 * gbps / copy_ref["GBps"], 1),
         "kernel_us": {k: main_sum[k] for k in ("kernel_us_avg", "eager_us_p10_p50_p90",
