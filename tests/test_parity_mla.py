@@ -48,6 +48,36 @@ def test_fp32_q_output_h40(orc):
     _run_and_compare(orc, case, q_f32=True)
 
 
+def test_fp32_q_output_strided(orc):
+    """fp32 q_rope_output written into a view of a wider buffer (token stride
+    H*R + 4 floats, head stride 2*R: the rope slice of a [T, H, 2R] tensor)
+    from a strided bf16 q; every float outside the view keeps its sentinel."""
+    import paged_kv_cache_wavefront_amd as pkv
+    case = workloads.build_mla("mla_f32_strided", 4006, [3, 9, 0, 14], [5, 0, 2, 30], H=20,
+                               page_size=8, max_seq_len=64, spare_pages=3,
+                               scale_mode="per_tensor", tensor_scale=0.05)
+    T, H, R = case.q.shape
+    dev = gh.MlaDevice(case, "strided")
+    big = torch.full((T, 2 * H * R + 4), -3.0, dtype=torch.float32, device="cuda")
+    view = big[:, : 2 * H * R].view(T, H, 2 * R)[:, :, R:]
+    pkv.mla_rope_rmsnorm_quant(view, dev.q_in, dev.latent, dev.offsets, dev.freqs, dev.gamma,
+                               case.epsilon, dev.desc, case.layer_idx)
+    torch.cuda.synchronize()
+    host = big.cpu().numpy()
+    got = host[:, : 2 * H * R].reshape(T, H, 2 * R)[:, :, R:]
+    rest = np.concatenate([host[:, : 2 * H * R].reshape(T, H, 2 * R)[:, :, :R].ravel(),
+                           host[:, 2 * H * R:].ravel()])
+    assert np.all(rest == -3.0), "floats outside the output view changed"
+    q_o, cache_o, _, pre = gh.oracle_mla(orc, case, q_f32=True)
+    d = gh.f32_ulp_diff(np.ascontiguousarray(got), q_o)
+    assert int(d.max(initial=0)) <= gh.F32_MAX_ULP
+    _, cache_g, _, skipped = dev.results()
+    assert skipped == 0
+    rows = gh.written_rows(case)
+    assert np.array_equal(cache_g[~rows], case.cache[~rows])
+    gh.check_fp8(cache_g[rows], cache_o[rows], pre[rows], "cache rows", max_frac=1e-3)
+
+
 @pytest.mark.parametrize("idx", range(5))
 def test_small_cases(orc, idx):
     case = list(oracle_pins.small_mla_cases())[idx]

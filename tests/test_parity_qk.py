@@ -161,6 +161,21 @@ def test_mrope_vision_batch(orc):
     run_qk(orc, case, False)
 
 
+@pytest.mark.parametrize("mode,with_norm", [("per_tensor", False), ("per_token", True)])
+def test_mrope_fp8_k(orc, mode, with_norm):
+    """Multimodal RoPE with an fp8 K cache (both scale modes; the per-token
+    case with the fused K norm): the features combine as their oracles do."""
+    rng = workloads.make_rng(5302)
+    new = rng.integers(20, 200, size=6, endpoint=True)
+    prior = rng.integers(0, 100, size=6, endpoint=True)
+    case = workloads.build_qk(f"mrope_fp8_{mode}", 5302, new, prior, Hq=8, Hkv=2, D=128,
+                              page_size=16, max_seq_len=2048, theta=1000000.0,
+                              interleaved=False, with_position_ids=True,
+                              norm_cols=96 if with_norm else None, rng=rng,
+                              mrope_section=(16, 24, 24), k_dtype="fp8", k_scale_mode=mode)
+    run_qk_fp8(orc, case, with_norm)
+
+
 @pytest.mark.parametrize("idx", range(2))
 def test_fp8_kv_norm(orc, idx):
     case = list(oracle_pins.small_qk_fp8_cases())[idx]
