@@ -252,3 +252,29 @@ def test_descriptor_keeps_its_tensors_alive(pkv):
     del pt
     gc.collect()
     assert ref() is not None and desc.page_table == ref().data_ptr()
+
+
+def test_headers_compile_as_c_and_cxx(tmp_path):
+    """The public headers are plain C (C99) and C++ (17), warning-free, and
+    declare the entry points with the argument lists the binding uses."""
+    src = tmp_path / "use.c"
+    src.write_text('#include <string.h>\n#include "pkv.h"\n#include "pkv_bench.h"\n'
+                   "int main(void) {\n"
+                   "  pkv_paged_cache c;\n"
+                   "  memset(&c, 0, sizeof c);\n"
+                   "  (void)c;\n"
+                   "  int (*f1)(void*, int64_t, int64_t, const void*, int64_t, int64_t, const void*,"
+                   " int64_t, const uint32_t*, uint32_t, uint32_t, uint32_t, uint32_t, uint32_t,"
+                   " const float*, uint32_t, const void*, float, const pkv_paged_cache*, uint32_t,"
+                   " int32_t, void*) = mla_rope_rmsnorm_quant;\n"
+                   "  const char* (*f2)(int) = pkv_status_string;\n"
+                   "  int (*f3)(const void*, void*, uint64_t, uint32_t, void*) = pkv_stream_copy;\n"
+                   "  (void)f1; (void)f2; (void)f3;\n"
+                   "  return 0;\n}\n")
+    inc = os.path.join(ROOT, "include")
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic",
+                    "-fsyntax-only", "-I", inc, str(src)], check=True)
+    cxx = tmp_path / "use.cpp"
+    cxx.write_text(src.read_text())
+    subprocess.run(["g++", "-std=c++17", "-Wall", "-Wextra", "-Werror", "-fsyntax-only",
+                    "-I", inc, str(cxx)], check=True)
