@@ -43,8 +43,10 @@ def test_mla_random(orc, seed):
     layout = str(rng.choice(["dense", "strided", "inplace"]))
     q_f32 = layout == "dense" and bool(rng.random() < 0.3)
     max_seq = int((prior + new).max()) + int(rng.integers(1, 50))
+    layers = int(rng.integers(1, 3, endpoint=True))
+    layer = int(rng.integers(0, layers))
     cfg = dict(B=B, T=int(new.sum()), H=H, page=page, kind=kind, layout=layout, q_f32=q_f32,
-               max_seq=max_seq)
+               max_seq=max_seq, layers=layers, layer=layer)
     _say(f"[rand-mla] seed={seed} {cfg}")
     case = workloads.build_mla(
         f"rand_mla_{seed}", 9000 + seed, new, prior, H=H, page_size=page, max_seq_len=max_seq,
@@ -52,7 +54,8 @@ def test_mla_random(orc, seed):
         outlier_p=float(rng.choice([0.0, 0.01])),
         scale_mode="per_token" if kind == "fp8_token" else "per_tensor",
         tensor_scale=float(rng.choice([0.02, 0.05, 0.2, 1.0])),
-        cache_dtype="bf16" if kind == "bf16" else "fp8", rng=rng)
+        cache_dtype="bf16" if kind == "bf16" else "fp8", num_layers=layers, layer_idx=layer,
+        rng=rng)
     dev = gh.MlaDevice(case, layout, q_f32)
     dev.run()
     gpu = dev.results()
@@ -78,16 +81,18 @@ def _random_qk(rng, seed):
     k_dtype = str(rng.choice(["bf16", "fp8"]))
     k_mode = str(rng.choice(["per_tensor", "per_token"]))
     max_seq = int((prior + new).max()) + int(rng.integers(1, 300))
+    layers = int(rng.integers(1, 3, endpoint=True))
+    layer = int(rng.integers(0, layers))
     cfg = dict(B=B, T=int(new.sum()), D=D, Hq=Hq, Hkv=Hkv, page=page, interleaved=interleaved,
                mrope=mrope, pos_ids=pos_ids, norm_cols=norm_cols, k=k_dtype,
-               k_mode=k_mode if k_dtype == "fp8" else None)
+               k_mode=k_mode if k_dtype == "fp8" else None, layers=layers, layer=layer)
     case = workloads.build_qk(f"rand_qk_{seed}", 9100 + seed, new, prior, Hq=Hq, Hkv=Hkv, D=D,
                               page_size=page, max_seq_len=max_seq,
                               theta=float(rng.choice([1e4, 5e5, 1e6])), interleaved=interleaved,
                               with_position_ids=pos_ids, norm_cols=norm_cols, rng=rng,
                               spare_pages=int(rng.integers(1, 6)), k_dtype=k_dtype,
                               k_scale_mode=k_mode, k_scale=float(rng.choice([0.02, 0.05, 0.2])),
-                              mrope_section=mrope)
+                              mrope_section=mrope, num_layers=layers, layer_idx=layer)
     return case, cfg
 
 
