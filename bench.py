@@ -483,7 +483,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 in, fp32 math, fp8 e4m3fn cache" if is_mla else "bf16 in, fp32 math, bf16 out",
+        "dtype": "f32",
+        "io_dtypes": ("bf16 q and latent in; bf16 q out; fp8 e4m3fn cache rows out" if is_mla
+                      else "bf16 in, bf16 out" if args.workload != "gather"
+                      else "fp8 e4m3fn cache rows in, bf16 rows out"),
         "data": "synthetic (seeded; DeepSeek-V3-shaped random tensors, no weights)",
         "config": config,
         "effective_GBps": gbps,
