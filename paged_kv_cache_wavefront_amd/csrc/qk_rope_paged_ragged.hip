@@ -6,11 +6,17 @@
 // layer layer_idx (one launch, so the K rotation is ordered after whatever
 // wrote K).  Position = position_ids[t] when given, else the token's slot.
 // Optional per-head RMSNorm of K (first k_norm_cols columns, gamma) runs
-// before the rotation, with a single bf16 rounding at the end.
+// before the rotation, with a single rounding at the end (bf16, or fp8 for
+// an fp8 K cache).
 //
-// Lane geometry (one wave64 per token, D = head_dim): each lane owns one
-// 16-byte chunk (8 values) of a head, D/8 lanes per head, so every wave
-// instruction moves 64 x 16 contiguous bytes.
+// Waves: one wave64 per (token, chunk of kQInstrPerWave x 64/(D/8) Q heads);
+// the chunk-0 wave of a token also rotates the token's K heads.  Lane
+// geometry (D = head_dim): each lane owns one 16-byte chunk (8 values) of a
+// head, D/8 lanes per head, so every Q instruction moves 64 x 16 contiguous
+// bytes.  An fp8 K head is read as 8 codes per lane (8 bytes), decoded and
+// scaled in registers (code x scale), and re-encoded with the tensor scale or
+// with a fresh per-(slot, head) scale max|y| / 448 from a DPP max over the
+// head's lanes.
 // * interleaved: lane k holds values 8k..8k+7 = adjacent pairs 4k..4k+3.
 // * rotate-half: lane k < D/16 holds values 8k.. of the first half; lane
 //   k >= D/16 holds the second-half values of pairs 8(D/8-1-k)..; the partner
