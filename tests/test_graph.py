@@ -66,3 +66,54 @@ def test_qk_graph_replays():
         torch.cuda.synchronize()
         assert np.array_equal(gh.host_bf16(dev.q_out), want_q), f"replay {rep}: q"
         assert np.array_equal(gh.host_bf16(dev.k), want_k), f"replay {rep}: k"
+
+
+def test_kv_norm_graph_replays():
+    case = workloads.qk_generic()
+    eager = gh.QkDevice(case)
+    eager.kv_norm(eager.gamma, 0.25, case.T, True, per_head=False)
+    want = gh.host_bf16(eager.k)
+    dev = gh.QkDevice(case)
+    k0 = dev.k.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        dev.kv_norm(dev.gamma, 0.25, case.T, True, per_head=False)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dev.kv_norm(dev.gamma, 0.25, case.T, True, per_head=False)
+    for rep in range(3):
+        dev.k.copy_(k0)                         # normalised in place: restore it
+        junk = torch.ones(1 << 20, device="cuda") * rep
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(gh.host_bf16(dev.k), want), f"replay {rep}: k"
+        del junk
+
+
+def test_gather_graph_replays():
+    import oracle_pins
+    import paged_kv_cache_wavefront_amd as pkv
+    case, kvo = oracle_pins.gather_case("fp8_token")
+    cache = gh.dev_u8(case.cache)
+    scales = gh.dev_f32(case.token_scales)
+    desc = pkv.paged_cache(cache, None, gh.dev_u32(case.page_table), pkv.PKV_SCALE_PER_TOKEN,
+                           scales)
+    kv = gh.dev_u32(kvo)
+    rows = int(kvo[-1])
+    out = torch.zeros((rows, 576), dtype=torch.bfloat16, device="cuda")
+    pkv.mla_gather_latent_paged(out, kv, desc, case.layer_idx)
+    torch.cuda.synchronize()
+    want = gh.host_bf16(out)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pkv.mla_gather_latent_paged(out, kv, desc, case.layer_idx)
+    for rep in range(3):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(gh.host_bf16(out), want), f"replay {rep}: gather"
