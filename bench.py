@@ -7,10 +7,16 @@ scale 0.05.  One step = one mla_rope_rmsnorm_quant launch over the whole
 batch (q RoPE, latent RMSNorm + RoPE, FP8 quantisation, paged store), inputs
 resident in HBM.  Prints one JSON line.
 
-Also reported (``siblings``): the other workloads and entry points, each timed
-the same way -- MLA decode (256 x 1 token, 128 heads), mixed prefill + decode
-with per-token scales (16 heads), the Llama-shaped paged-ragged Q/K RoPE with
-fused per-head K norm, and the in-place K-cache RMSNorm.
+Consecutive steps rotate over enough output-buffer sets that each cycle
+writes at least 1 GiB of distinct memory, so no step rewrites lines the
+previous one left dirty in the Infinity Cache (``buffer_rotation`` names the
+sets).  Also reported: 20 isolated launches after a 512 MiB read that
+flushes the caches (``cold_us_p10_p50_p90``); a plain streaming copy timed in
+the same run (``measured_copy``); and (``siblings``) the other workloads and
+entry points, each timed the same way -- MLA decode (256 x 1 token, 128
+heads), mixed prefill + decode with per-token scales (16 heads), the
+Llama-shaped paged-ragged Q/K RoPE with fused per-head K norm, the in-place
+K-cache RMSNorm and the paged latent gather.
 
 ``--calibrate-copy`` runs a plain elementwise copy of known size instead (the
 reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings).
