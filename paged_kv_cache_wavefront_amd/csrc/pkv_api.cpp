@@ -189,7 +189,7 @@ int qk_rope_paged_ragged(void* q_out, int64_t qo_tok_stride, int64_t qo_head_str
   if (!k_mode_of(k_cache, &km)) return PKV_ERR_DTYPE;
   if (k_norm_gamma != nullptr && (k_norm_cols == 0 || k_norm_cols > head_dim))
     return PKV_ERR_SHAPE;
-  if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return PKV_ERR_UNSUPPORTED;
   if (total_tokens > 0 && batch_size == 0) return PKV_ERR_SHAPE;
   if (max_seq_len == 0) return PKV_ERR_SHAPE;
   CacheView view{};
@@ -248,7 +248,8 @@ int rms_norm_kv_cache_paged(const pkv_paged_cache* k_cache, uint32_t layer_idx,
   if (!k_mode_of(k_cache, &km)) return PKV_ERR_DTYPE;
   if (gamma_len == 0 || gamma_len > k_cache->head_dim) return PKV_ERR_SHAPE;
   if (km != pkv::KMode::Bf16 && !multiply_before_cast) return PKV_ERR_UNSUPPORTED;
-  if (k_cache->head_dim != 64 && k_cache->head_dim != 128) return PKV_ERR_UNSUPPORTED;
+  if (k_cache->head_dim != 64 && k_cache->head_dim != 128 && k_cache->head_dim != 256)
+    return PKV_ERR_UNSUPPORTED;
   if (!per_head_norm && k_cache->num_heads > pkv::kv_norm_max_heads(k_cache->head_dim))
     return PKV_ERR_UNSUPPORTED;
   if (total_seq_len > 0 && batch_size == 0) return PKV_ERR_SHAPE;

@@ -136,28 +136,52 @@ constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7-i inside each 8 lanes
 constexpr int kDppMirror = 0x140;      // lane i <-> 15-i inside each 16 lanes
 
-// Sum over aligned groups of N lanes (N in 1, 2, 4, 8, 16); every lane of a
-// group receives the group's sum.
-// Exchange a 16-byte chunk with the mirrored lane of its 8-lane (MIRROR=8) or
-// 16-lane (MIRROR=16) group: lane k receives lane (N-1-k)'s data.
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xF, 0xF, true);
 }
 
-template <int MIRROR>
-__device__ __forceinline__ uint4 mirror16(const uint4& v) {
-  constexpr int ctrl = MIRROR == 8 ? 0x141 : 0x140;  // row_half_mirror / row_mirror
-  return make_uint4(dpp_u32<ctrl>(v.x), dpp_u32<ctrl>(v.y), dpp_u32<ctrl>(v.z),
-                    dpp_u32<ctrl>(v.w));
+// Lane exchanges across 16-lane rows, inside 32-lane halves: ds_swizzle in
+// bitmask mode (source lane = (lane & 0x1F) ^ xor_mask within each half).
+constexpr int kSwizzleXor16 = 0x1F | (0x10 << 10);  // lane i <-> i ^ 16
+constexpr int kSwizzleMirror32 = 0x1F | (0x1F << 10);  // lane i <-> 31 - i
+
+template <int PATTERN>
+__device__ __forceinline__ uint32_t swizzle_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, PATTERN);
 }
 
+template <int PATTERN>
+__device__ __forceinline__ float swizzle(float v) {
+  return __uint_as_float(swizzle_u32<PATTERN>(__float_as_uint(v)));
+}
+
+// Lane k of an aligned group of N lanes (N = 8, 16 or 32) receives lane
+// (N-1-k)'s 32-bit value.
+template <int N>
+__device__ __forceinline__ uint32_t mirror_u32(uint32_t x) {
+  static_assert(N == 8 || N == 16 || N == 32, "mirror over 8, 16 or 32 lanes");
+  if constexpr (N == 8) return dpp_u32<kDppHalfMirror>(x);
+  else if constexpr (N == 16) return dpp_u32<kDppMirror>(x);
+  else return swizzle_u32<kSwizzleMirror32>(x);
+}
+
+// Exchange a 16-byte chunk with the mirrored lane of its group of N lanes.
+template <int N>
+__device__ __forceinline__ uint4 mirror16(const uint4& v) {
+  return make_uint4(mirror_u32<N>(v.x), mirror_u32<N>(v.y), mirror_u32<N>(v.z),
+                    mirror_u32<N>(v.w));
+}
+
+// Sum over aligned groups of N lanes (N in 1, 2, 4, 8, 16, 32); every lane of
+// a group receives the group's sum.
 template <int N>
 __device__ __forceinline__ float group_sum(float v) {
   if constexpr (N >= 2) v += dpp<kDppXor1>(v);
   if constexpr (N >= 4) v += dpp<kDppXor2>(v);
   if constexpr (N >= 8) v += dpp<kDppHalfMirror>(v);
   if constexpr (N >= 16) v += dpp<kDppMirror>(v);
+  if constexpr (N >= 32) v += swizzle<kSwizzleXor16>(v);
   return v;
 }
 
@@ -167,6 +191,7 @@ __device__ __forceinline__ float group_max(float v) {
   if constexpr (N >= 4) v = fmaxf(v, dpp<kDppXor2>(v));
   if constexpr (N >= 8) v = fmaxf(v, dpp<kDppHalfMirror>(v));
   if constexpr (N >= 16) v = fmaxf(v, dpp<kDppMirror>(v));
+  if constexpr (N >= 32) v = fmaxf(v, swizzle<kSwizzleXor16>(v));
   return v;
 }
 

@@ -20,7 +20,8 @@
 // * interleaved: lane k holds values 8k..8k+7 = adjacent pairs 4k..4k+3.
 // * rotate-half: lane k < D/16 holds values 8k.. of the first half; lane
 //   k >= D/16 holds the second-half values of pairs 8(D/8-1-k)..; the partner
-//   of lane k is lane D/8-1-k, reached by one DPP mirror per dword.
+//   of lane k is lane D/8-1-k, reached by one DPP mirror per dword (a
+//   ds_swizzle for D = 256, whose heads span 32 lanes).
 // Pair i needs freqs columns 2i, 2i+1: 8 or 16 consecutive floats per lane,
 // loaded once per token.  Q is read, and Q and K are written, with
 // non-temporal accesses.
@@ -279,8 +280,7 @@ __global__ __launch_bounds__(256) void qk_rope_kernel(const QkArgs a) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) own[j] *= ks;
       if constexpr (!INTER) {  // the partner lane belongs to the same head: same scale
-        constexpr int ctrl = LP == 8 ? 0x141 : 0x140;  // row_half_mirror / row_mirror
-        unpack8_fp8(dpp_u32<ctrl>(kv.x), dpp_u32<ctrl>(kv.y), par);
+        unpack8_fp8(mirror_u32<LP>(kv.x), mirror_u32<LP>(kv.y), par);
 #pragma unroll
         for (int j = 0; j < 8; ++j) par[j] *= ks;
       }
@@ -355,7 +355,7 @@ hipError_t launch_d(const QkArgs& a, bool interleaved, KMode km, uint32_t blocks
 }  // namespace
 
 // Q heads per wave: kQInstrPerWave instructions of 64 / (head_dim / 8) heads,
-// i.e. 4 KiB of Q per wave (16 heads of 128 or 32 heads of 64).
+// i.e. 4 KiB of Q per wave (8 heads of 256, 16 of 128 or 32 of 64).
 uint32_t qk_heads_per_wave(int head_dim) { return (uint32_t)kQInstrPerWave * (512u / (uint32_t)head_dim); }
 
 hipError_t launch_qk_rope(const QkArgs& a, int head_dim, bool interleaved, KMode kmode,
@@ -366,6 +366,7 @@ hipError_t launch_qk_rope(const QkArgs& a, int head_dim, bool interleaved, KMode
   // the kernel numbers waves (block * waves per block + wave) in 32 bits
   if (blocks * kWavesPerBlock > 0xffffffffull) return hipErrorInvalidValue;
   const uint32_t nb = (uint32_t)blocks;
+  if (head_dim == 256) return launch_d<256>(a, interleaved, kmode, nb, stream);
   if (head_dim == 128) return launch_d<128>(a, interleaved, kmode, nb, stream);
   if (head_dim == 64) return launch_d<64>(a, interleaved, kmode, nb, stream);
   return hipErrorInvalidValue;

@@ -223,6 +223,7 @@ hipError_t launch_kv_norm(const KvNormArgs& a, bool multiply_before_cast, KMode 
   switch (a.head_dim) {
     case 64: return launch_d<64>(a, multiply_before_cast, kmode, nb, stream);
     case 128: return launch_d<128>(a, multiply_before_cast, kmode, nb, stream);
+    case 256: return launch_d<256>(a, multiply_before_cast, kmode, nb, stream);
     default: return hipErrorInvalidValue;
   }
 }

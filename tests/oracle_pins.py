@@ -614,6 +614,10 @@ def small_qk_cases():
                              page_size=8, max_seq_len=64, theta=10000.0,
                              interleaved=True, with_position_ids=False,
                              norm_cols=None, spare_pages=1)
+    yield workloads.build_qk("qk_small_d256", 3004, [4, 7, 0], [3, 0, 9], Hq=3, Hkv=2, D=256,
+                             page_size=8, max_seq_len=128, theta=10000.0,
+                             interleaved=False, with_position_ids=True,
+                             norm_cols=200, spare_pages=2)
 
 
 def pin_qk_composite(orc):

@@ -151,6 +151,10 @@ def test_qk_validation(pkv):
     assert call_qk(pkv, kcache(pkv, dtype=pkv.PKV_DTYPE_FP8_E4M3FN)) == DTYPE
     assert call_qk(pkv, kcache(pkv, scale_mode=pkv.PKV_SCALE_PER_TENSOR)) == DTYPE
     assert call_qk(pkv, kcache(pkv, head_dim=96), D=96) == UNSUP
+    assert call_qk(pkv, kcache(pkv, head_dim=512), D=512) == UNSUP
+    assert call_qk(pkv, kcache(pkv, head_dim=256, head_stride=256, slot_stride=8 * 256,
+                              page_stride=16 * 8 * 256, layer_stride=8 * 16 * 8 * 256),
+                   D=256, T=0) == OK
     assert call_qk(pkv, kcache(pkv), D=64) == SHAPE                    # q vs cache head_dim
     big = (1 << 27) + 8
     assert call_qk(pkv, kcache(pkv, head_stride=big, slot_stride=8 * big,
@@ -187,7 +191,7 @@ def test_kv_norm_validation(pkv):
                                   layer_stride=8 * 16 * 17 * 128), per_head=0) == UNSUP
     assert call_norm(pkv, kcache(pkv, num_heads=17, slot_stride=17 * 128, page_stride=16 * 17 * 128,
                                   layer_stride=8 * 16 * 17 * 128), per_head=1, T=0) == OK
-    assert call_norm(pkv, kcache(pkv, head_dim=256), gamma_len=128) == UNSUP
+    assert call_norm(pkv, kcache(pkv, head_dim=512), gamma_len=128) == UNSUP
     assert call_norm(pkv, kcache(pkv), gamma=None) == NULL
     assert call_norm(pkv, kcache(pkv), gamma=FAKE + 2) == ALIGN
     assert call_norm(pkv, kcache(pkv), T=0) == OK

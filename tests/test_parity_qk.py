@@ -162,6 +162,43 @@ def test_mrope_vision_batch(orc):
     run_qk(orc, case, False)
 
 
+@pytest.mark.parametrize("mode", ["per_tensor", "per_token"])
+def test_fp8_k_head_dim_256(orc, mode):
+    """fp8 K cache with 256-wide heads (32 lanes per head: the rotate-half
+    partner and the per-token max cross 16-lane rows), fused K norm."""
+    rng = workloads.make_rng(5400)
+    new = rng.integers(1, 60, size=7, endpoint=True)
+    prior = rng.integers(0, 80, size=7, endpoint=True)
+    case = workloads.build_qk(f"qk_fp8_d256_{mode}", 5400, new, prior, Hq=6, Hkv=3, D=256,
+                              page_size=16, max_seq_len=1024, theta=10000.0,
+                              interleaved=False, with_position_ids=True, norm_cols=256, rng=rng,
+                              k_dtype="fp8", k_scale_mode=mode)
+    run_qk_fp8(orc, case, True)
+
+
+@pytest.mark.parametrize("per_head", [True, False])
+def test_kv_norm_head_dim_256(orc, per_head):
+    rng = workloads.make_rng(5401)
+    new = rng.integers(1, 40, size=6, endpoint=True)
+    prior = rng.integers(0, 60, size=6, endpoint=True)
+    case = workloads.build_qk("kvnorm_d256", 5401, new, prior, Hq=2, Hkv=8, D=256, page_size=8,
+                              max_seq_len=256, theta=10000.0, interleaved=False,
+                              with_position_ids=False, norm_cols=None, rng=rng)
+    gamma = workloads.bf16_bits(rng.uniform(0.5, 1.5, 256).astype(np.float32))
+    _say(f"[kvnorm256] T={case.T} per_head={per_head}")
+    dev = gh.QkDevice(case)
+    dev.kv_norm(gh.dev_bf16(gamma), 0.0, case.T, True, per_head)
+    k = gh.host_bf16(dev.k)
+    assert int(dev.error_count.item()) == 0
+    k_o = case.k_cache.copy()
+    orc.rms_norm_kv_cache_paged(k_o, case.layer_idx, case.row_offsets, case.cache_lengths,
+                                case.page_table, gamma, case.epsilon, 0.0, case.T, True,
+                                per_head_norm=per_head)
+    rows = gh.written_k_rows(case)
+    assert np.array_equal(k[~rows], case.k_cache[~rows])
+    _say(f"[kvnorm256] {gh.check_bf16(k[rows], k_o[rows], 'k')}")
+
+
 @pytest.mark.parametrize("mode,with_norm", [("per_tensor", False), ("per_token", True)])
 def test_mrope_fp8_k(orc, mode, with_norm):
     """Multimodal RoPE with an fp8 K cache (both scale modes; the per-token
@@ -288,9 +325,10 @@ def test_llama_workload(orc, with_norm):
     run_qk(orc, workloads.qk_generic(), with_norm)
 
 
-# (case index, with K norm): the third small case has no K norm gamma
+# (case index, with K norm): the third small case has no K norm gamma; the
+# fourth has head_dim 256 (heads spanning 32 lanes)
 @pytest.mark.parametrize("idx,with_norm", [(0, True), (0, False), (1, True), (1, False),
-                                           (2, False)])
+                                           (2, False), (3, True), (3, False)])
 def test_small_cases(orc, idx, with_norm):
     case = list(oracle_pins.small_qk_cases())[idx]
     assert with_norm is False or case.gamma is not None
@@ -299,7 +337,7 @@ def test_small_cases(orc, idx, with_norm):
 
 @pytest.mark.parametrize("D,interleaved,pos_ids",
                          [(128, False, True), (128, False, False), (64, True, True),
-                          (64, False, False)])
+                          (64, False, False), (256, False, True), (256, True, False)])
 def test_styles_and_dims(orc, D, interleaved, pos_ids):
     rng = workloads.make_rng(5000 + D)
     new = rng.integers(1, 200, size=12, endpoint=True)

@@ -66,15 +66,15 @@ def test_mla_random(orc, seed):
 def _random_qk(rng, seed):
     B = int(rng.integers(1, 30))
     new, prior = _lengths(rng, B, 20, 200)
-    D = int(rng.choice([64, 128]))
+    D = int(rng.choice([64, 128, 256]))
     Hq = int(rng.choice([1, 2, 5, 8, 16, 31, 32, 40]))
     Hkv = int(rng.choice([1, 2, 4, 8]))
     page = int(rng.choice([8, 16, 32]))
     interleaved = bool(rng.random() < 0.5)
     mrope = None
-    if D == 128 and rng.random() < 0.3:
-        cut = np.sort(rng.integers(0, 64, size=2, endpoint=True))
-        mrope = (int(cut[0]), int(cut[1] - cut[0]), int(64 - cut[1]))
+    if D >= 128 and rng.random() < 0.3:
+        cut = np.sort(rng.integers(0, D // 2, size=2, endpoint=True))
+        mrope = (int(cut[0]), int(cut[1] - cut[0]), int(D // 2 - cut[1]))
     pos_ids = mrope is not None or bool(rng.random() < 0.5)
     norm = rng.choice([0, 1, 2])
     norm_cols = None if norm == 0 else (D if norm == 1 else int(rng.integers(1, D)))
