@@ -97,14 +97,25 @@ MUTANTS = [
      "const int64_t pk = (int64_t)position_ids[t * 3 + k];"),
     ("gather_quant_multiplies", "oracle_bf16_decode(bits) / (double)out_tensor_scale);",
      "oracle_bf16_decode(bits) * (double)out_tensor_scale);"),
+    # rounding-rule slips only the exact-arithmetic pins see: a per-token
+    # scale rounded twice, and exact ties broken upwards
+    ("mla_token_scale_two_roundings", "const float st = (float)(amax / 448.0); /* stored fp32",
+     "const float st = (float)amax / 448.0f; /* stored fp32"),
+    ("k_token_scale_two_roundings", "const float st = (float)(amax / 448.0);\n    *token_scale = st;",
+     "const float st = (float)amax / 448.0f;\n    *token_scale = st;"),
+    ("mla_f32_q_ties_up", "dst[i] = (float)qb[i];  /* RNE */",
+     "dst[i] = (float)(qb[i] * (1 + 0x1p-40));  /* RNE */"),
+    ("kvnorm_unrounded_ties_up",
+     "a[i] = oracle_bf16_decode(oracle_bf16_encode(a[i] * inv)) * g[i];",
+     "a[i] = oracle_bf16_decode(oracle_bf16_encode(a[i] * inv)) * g[i] * (1 + 0x1p-40);"),
 ]
 
 RUNNER = r"""
 import sys
 sys.path[:0] = [{root!r}, {tests!r}]
-import oracle, oracle_pins
+import oracle, oracle_pins, exact_pins
 orc = oracle.Oracle({lib!r})
-for pin in oracle_pins.ALL_PINS:
+for pin in oracle_pins.ALL_PINS + exact_pins.ALL_EXACT_PINS:
     try:
         pin(orc)
     except Exception as e:

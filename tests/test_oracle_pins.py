@@ -2,12 +2,46 @@
 force, library special cases, format landmarks)."""
 import pytest
 
+import exact_pins
 import oracle_pins
 
 
 @pytest.mark.parametrize("pin", oracle_pins.ALL_PINS, ids=lambda f: f.__name__)
 def test_pin(orc, pin):
     pin(orc)
+
+
+@pytest.mark.parametrize("pin", exact_pins.ALL_EXACT_PINS, ids=lambda f: f.__name__)
+def test_exact_pin(orc, pin):
+    """Every output of the entry points on tiny cases equals the exact value
+    (120-digit decimal arithmetic) rounded once, exact ties to even."""
+    pin(orc)
+
+
+def test_exact_rounding_helpers(orc):
+    """The decimal rounding helpers themselves: format landmarks, exact ties
+    to even, saturation, signed zero, and agreement with the oracle's own
+    (separately pinned) encoders away from ties."""
+    from decimal import Decimal
+    import numpy as np
+    E = exact_pins
+    assert E.round_fp8(Decimal(448))[0] == 0x7E and E.round_fp8(Decimal(10 ** 6))[0] == 0x7E
+    assert E.round_fp8(Decimal(-464))[0] == 0xFE
+    assert E.round_fp8(Decimal(2) ** -10) == (0x00, E.TIE)      # halfway to the first subnormal
+    assert E.round_fp8(Decimal(3) * Decimal(2) ** -10) == (0x02, E.TIE)
+    assert E.round_fp8(Decimal("-0"))[0] == 0x80
+    assert E.round_fp8(Decimal(17))[0] == 0x58                    # 17 between 16 and 18: even 16
+    assert E.round_bf16(Decimal(1) + Decimal(2) ** -8) == (0x3F80, E.TIE)
+    assert E.round_bf16(Decimal(1) + Decimal(3) * Decimal(2) ** -8) == (0x3F82, E.TIE)
+    assert E.round_bf16(Decimal(1) + Decimal(2) ** -8 + Decimal(2) ** -60) == (0x3F81, E.NEAR_TIE)
+    assert E.round_f32(Decimal(1) + Decimal(2) ** -24) == (0x3F800000, E.TIE)
+    assert E.round_f32(Decimal(-1) - Decimal(2) ** -23) == (0xBF800001, E.OK)
+    assert E.fp8_value(0x80).is_signed() and E.fp8_value(0x7E) == 448
+    rng = np.random.default_rng(5)
+    for v in rng.standard_normal(300) * 50:
+        d = Decimal(float(v))
+        assert E.round_bf16(d)[0] == orc.bf16_encode(float(v))
+        assert E.round_fp8(d)[0] == orc.e4m3fn_encode(float(v))
 
 
 def test_fp8_midpoint_distance():
