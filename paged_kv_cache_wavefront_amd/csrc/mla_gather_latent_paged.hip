@@ -6,16 +6,22 @@
 // of request b, copied, dequantised (fp8 code x scale -> bf16) or quantised
 // (bf16 / scale -> fp8, saturating round-to-nearest-even).
 //
-// One wave per group of rows: 16 rows of an fp8 cache (36 sixteen-byte
-// pieces per 576-byte row: 16 rows = 9 full wave instructions) or 8 rows of
-// a bf16 cache.  Lanes 0..rows-1 each resolve one row (request by ballot over
-// the offsets -- once for the whole group when it lies in one request --,
-// slot, page-table entry, per-token scale); a piece lane fetches its row's
-// source address from the row lane with ds_bpermute.  Loads are non-temporal
-// (each cache byte is read once) and so are the stores (the dense output is
-// written once); every wave instruction reads and writes contiguous runs
-// (fp8 -> bf16 reads 8-byte pieces so that each lane writes 16 contiguous
-// bytes).
+// One wave per group of rows: 6 rows (3 for bf16 -> bf16).  Lanes
+// 0..rows-1 each resolve one row (request by ballot over the offsets -- once
+// for the whole group when it lies in one request --, slot, page-table entry,
+// per-token scale); a piece lane fetches its row's source address from the
+// row lane with ds_bpermute.  Loads are non-temporal (each cache byte is read
+// once) and so are the stores (the dense output is written once); every wave
+// instruction reads and writes contiguous runs (fp8 -> bf16 reads 8-byte
+// pieces so that each lane writes 16 contiguous bytes; writing 32 bytes per
+// lane as two 16-byte stores at a 32-byte lane stride measured 1.8x slower).
+//
+// Rows per wave, measured on MI355X with rotating outputs over 1 022 807
+// rows of 576 elements (microseconds, 16 / 8 / 6 / 4 / 3 rows per wave):
+// fp8 -> bf16 326 / 320 / 316 / 317 / 327, fp8 -> fp8 217 / - / 202 / 206 /
+// 217; bf16 -> bf16 (8 / 6 / 4 / 3 / 2 rows) 435 / 430 / 414 / 400 / 411,
+// bf16 -> fp8 292 / 288 / 291 / 311 / 352.  Two rows or one per wave leave
+// lanes idle and cost far more (fp8 -> bf16 383 and 548).
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -23,7 +29,21 @@ namespace pkv {
 namespace {
 
 constexpr int kWavesPerBlock = 4;
-constexpr int kMaxInstr = 16;  // most 16-byte chunks one lane moves per wave
+constexpr uint32_t kMaxElems = 1024;  // widest row supported
+constexpr uint32_t kMlaElems = 576;   // the MLA latent row
+
+// Launch geometry of one conversion: rows per wave, input bytes per piece
+// (one lane's share of one wave instruction) and the wave instructions that
+// cover the rows of a given width.
+template <bool IN_FP8, bool OUT_FP8>
+struct Shape {
+  static constexpr uint32_t kRows = (!IN_FP8 && !OUT_FP8) ? 3 : 6;
+  static constexpr uint32_t kPiece = (IN_FP8 && !OUT_FP8) ? 8 : 16;
+  static constexpr uint32_t kInBytes = IN_FP8 ? 1 : 2;
+  static constexpr int instr(uint32_t elems) {
+    return (int)((kRows * (elems * kInBytes / kPiece) + kWave - 1) / kWave);
+  }
+};
 
 __device__ __forceinline__ uint32_t shfl_u32(uint32_t v, int src_lane) {
   return (uint32_t)__builtin_amdgcn_ds_bpermute(src_lane << 2, (int)v);
@@ -31,7 +51,8 @@ __device__ __forceinline__ uint32_t shfl_u32(uint32_t v, int src_lane) {
 
 template <bool IN_FP8, bool OUT_FP8, bool PER_TOKEN, int NI>
 __global__ __launch_bounds__(256) void gather_kernel(const GatherArgs a) {
-  constexpr uint32_t RPW = IN_FP8 ? 16 : 8;  // rows per wave
+  using G = Shape<IN_FP8, OUT_FP8>;
+  constexpr uint32_t RPW = G::kRows;
   const int lane = threadIdx.x & (kWave - 1);
   const uint32_t wave =
       blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
@@ -128,13 +149,13 @@ __global__ __launch_bounds__(256) void gather_kernel(const GatherArgs a) {
   // piece g = i * 64 + lane of the wave's rows: row g / ppr, piece g % ppr.  A
   // piece is 16 input bytes, except for fp8 -> bf16 where it is 8 input bytes
   // so that every lane stores 16 contiguous output bytes.
-  constexpr uint32_t PIECE = (IN_FP8 && !OUT_FP8) ? 8 : 16;
+  constexpr uint32_t PIECE = G::kPiece;
   constexpr uint32_t OUT_PIECE = IN_FP8 == OUT_FP8 ? PIECE : (IN_FP8 ? 2 * PIECE : PIECE / 2);
   const uint32_t ppr = a.row_bytes / PIECE;  // pieces per row
   const uint32_t pieces = nrows * ppr;
   const char* src_base = static_cast<const char*>(cv.layer_base);
   char* out_base = static_cast<char*>(a.out) + (int64_t)r0 * a.out_row_bytes;
-  const uint32_t ok_rows = (uint32_t)__ballot(row_ok);  // bit j: row j has a page
+  const uint64_t ok_rows = __ballot(row_ok);  // bit j: row j has a page
   uint4 v[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
@@ -201,32 +222,37 @@ hipError_t launch_ni(const GatherArgs& a, bool per_token, uint32_t blocks, hipSt
   return hipGetLastError();
 }
 
-// Wave instructions per row group: rows x pieces per row / 64, i.e. 9 (18
-// for fp8 -> bf16, whose pieces are 8 bytes) for rows of up to 576 bytes
-// (fp8) / 1152 bytes (bf16), otherwise 16 (32).
+// Wave instructions per row group: enough for rows of the MLA latent width,
+// or for the widest rows supported.
 template <bool IN_FP8, bool OUT_FP8>
 hipError_t launch_kind(const GatherArgs& a, bool per_token, uint32_t blocks, hipStream_t stream) {
-  constexpr int SCALE = (IN_FP8 && !OUT_FP8) ? 2 : 1;
-  const uint32_t rpw = IN_FP8 ? 16 : 8;
-  if (rpw * (a.row_bytes / 16) <= 9 * kWave)
-    return launch_ni<IN_FP8, OUT_FP8, 9 * SCALE>(a, per_token, blocks, stream);
-  return launch_ni<IN_FP8, OUT_FP8, 16 * SCALE>(a, per_token, blocks, stream);
+  using G = Shape<IN_FP8, OUT_FP8>;
+  const uint32_t elems = a.row_bytes / G::kInBytes;
+  if (elems <= kMlaElems)
+    return launch_ni<IN_FP8, OUT_FP8, G::instr(kMlaElems)>(a, per_token, blocks, stream);
+  return launch_ni<IN_FP8, OUT_FP8, G::instr(kMaxElems)>(a, per_token, blocks, stream);
+}
+
+template <bool IN_FP8, bool OUT_FP8>
+hipError_t launch_checked(const GatherArgs& a, bool per_token, hipStream_t stream) {
+  using G = Shape<IN_FP8, OUT_FP8>;
+  if (a.row_bytes % G::kPiece != 0 || a.row_bytes / G::kInBytes > kMaxElems)
+    return hipErrorInvalidValue;
+  const uint64_t waves = ((uint64_t)a.total_rows + G::kRows - 1) / G::kRows;
+  const uint64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7fffffffull) return hipErrorInvalidValue;
+  return launch_kind<IN_FP8, OUT_FP8>(a, per_token, (uint32_t)blocks, stream);
 }
 
 }  // namespace
 
 hipError_t launch_gather(const GatherArgs& a, GatherKind kind, bool per_token, hipStream_t stream) {
-  const uint32_t rpw = (kind == GatherKind::Fp8ToFp8 || kind == GatherKind::Fp8ToBf16) ? 16 : 8;
-  const uint64_t waves = ((uint64_t)a.total_rows + rpw - 1) / rpw;
-  const uint64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
-  if (blocks == 0) return hipSuccess;
-  if (blocks > 0x7fffffffull || (uint64_t)rpw * (a.row_bytes / 16) > (uint64_t)kMaxInstr * kWave)
-    return hipErrorInvalidValue;
   switch (kind) {
-    case GatherKind::Fp8ToFp8: return launch_kind<true, true>(a, per_token, (uint32_t)blocks, stream);
-    case GatherKind::Fp8ToBf16: return launch_kind<true, false>(a, per_token, (uint32_t)blocks, stream);
-    case GatherKind::Bf16ToBf16: return launch_kind<false, false>(a, false, (uint32_t)blocks, stream);
-    case GatherKind::Bf16ToFp8: return launch_kind<false, true>(a, false, (uint32_t)blocks, stream);
+    case GatherKind::Fp8ToFp8: return launch_checked<true, true>(a, per_token, stream);
+    case GatherKind::Fp8ToBf16: return launch_checked<true, false>(a, per_token, stream);
+    case GatherKind::Bf16ToBf16: return launch_checked<false, false>(a, false, stream);
+    case GatherKind::Bf16ToFp8: return launch_checked<false, true>(a, false, stream);
   }
   return hipErrorInvalidValue;
 }

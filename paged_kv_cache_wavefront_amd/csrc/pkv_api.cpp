@@ -293,7 +293,7 @@ int mla_gather_latent_paged(void* out, int32_t out_dtype, int64_t out_row_stride
   const uint64_t in_eb = in_fp8 ? 1 : 2, out_eb = out_fp8 ? 1 : 2;
   const uint64_t row_bytes = (uint64_t)cache->head_dim * in_eb;
   if (row_bytes % 16 != 0 || ((uint64_t)cache->head_dim * out_eb) % 8 != 0) return PKV_ERR_ALIGN;
-  if ((in_fp8 ? 16 : 8) * (row_bytes / 16) > 1024) return PKV_ERR_UNSUPPORTED;
+  if (cache->head_dim > 1024) return PKV_ERR_UNSUPPORTED;
   if (out_row_stride < (int64_t)cache->head_dim) return PKV_ERR_SHAPE;
   if (total_rows > 0 && batch_size == 0) return PKV_ERR_SHAPE;
   CacheView view{};
