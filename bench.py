@@ -14,7 +14,8 @@ sets).  Also reported: 20 isolated launches after a 512 MiB read that
 flushes the caches (``cold_us_p10_p50_p90``); a plain streaming copy timed in
 the same run (``measured_copy``); and (``siblings``) the other workloads and
 entry points, each timed the same way -- MLA decode (256 x 1 token, 128
-heads), mixed prefill + decode with per-token scales (16 heads), the
+heads), mixed prefill + decode with per-token scales (16 heads), the same
+prefill batch in place on a bf16 latent cache (mla_rope_rmsnorm_inplace), the
 Llama-shaped paged-ragged Q/K RoPE with fused per-head K norm, the in-place
 K-cache RMSNorm and the paged latent gather.
 
@@ -45,6 +46,7 @@ CSRC = os.path.join(ROOT, "paged_kv_cache_wavefront_amd", "csrc")
 COMMON_SOURCES = ("pkv_device.h", "pkv_internal.h")
 KERNEL_OF = {"mla_prefill": "mla_rope_rmsnorm_quant.hip", "mla_decode": "mla_rope_rmsnorm_quant.hip",
              "mla_mixed": "mla_rope_rmsnorm_quant.hip", "mla_tiny": "mla_rope_rmsnorm_quant.hip",
+             "mla_prefill_inplace": "mla_rope_rmsnorm_quant.hip",
              "qk_generic": "qk_rope_paged_ragged.hip", "kv_norm": "rms_norm_kv_cache_paged.hip",
              "gather": "mla_gather_latent_paged.hip"}
 
@@ -63,12 +65,14 @@ def log(*a):
 # -- algorithmic bytes (what the method must move, read + written) ---------------------
 
 def mla_bytes(case) -> int:
-    """q in + q out (2 x H x R x 2) + latent row in (W x 2) + cache row out
-    (W x 1, + 4 for a per-token scale) per token; once per launch: freqs rows
-    of the distinct positions (R x 4 each), gamma, offsets, prior lengths,
-    the page-table entries read, the per-tensor scale."""
+    """q in + q out (2 x H x R x 2) + latent row in (W x 2, from its buffer or,
+    in place, from the cache) + cache row out (W x 1 fp8 / W x 2 bf16, + 4 for
+    a per-token scale) per token; once per launch: freqs rows of the distinct
+    positions (R x 4 each), gamma, offsets, prior lengths, the page-table
+    entries read, the per-tensor scale."""
     T, H, R, W = case.T, case.H, case.R, case.latent.shape[1]
-    per_tok = 2 * H * R * 2 + W * 2 + W * 1 + (4 if case.scale_mode == "per_token" else 0)
+    out_b = 2 if case.cache.dtype == np.uint16 else 1
+    per_tok = 2 * H * R * 2 + W * 2 + W * out_b + (4 if case.scale_mode == "per_token" else 0)
     pos = np.concatenate([np.arange(c, c + n) for c, n in
                           zip(case.cache_lengths.astype(np.int64),
                               np.diff(case.row_offsets.astype(np.int64)))]) if T else np.zeros(0)
@@ -262,7 +266,19 @@ def run_workload(name, steps, warmup):
     import paged_kv_cache_wavefront_amd as pkv
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     import gpu_helpers as gh
-    if name.startswith("mla_"):
+    if name == "mla_prefill_inplace":
+        case = workloads.NAMED[name]()
+        written = case.q.size * 2 + case.T * case.latent.shape[1] * 2
+        set_bytes = 2 * case.q.nbytes + case.cache.nbytes
+        n = rotation_count(written, set_bytes)
+        devs = [gh.MlaDevice(case) for _ in range(n)]
+        for d in devs:
+            d.place_rows()
+        fns = [d.run_inplace for d in devs]
+        how = f"{n} sets of q, q_out and bf16 cache pool"
+        r = measure(cycle(fns), case.T, mla_bytes(case), steps, warmup)
+        label = name
+    elif name.startswith("mla_"):
         case = workloads.NAMED[name]()
         q_out_bytes = case.q.size * 2
         written = q_out_bytes + case.T * case.latent.shape[1]
@@ -350,6 +366,7 @@ def measure_siblings(main, steps, warmup):
     out = {}
     for name, entry in (("mla_decode", "mla_rope_rmsnorm_quant"),
                         ("mla_mixed", "mla_rope_rmsnorm_quant"),
+                        ("mla_prefill_inplace", "mla_rope_rmsnorm_inplace"),
                         ("qk_generic", "qk_rope_paged_ragged"),
                         ("kv_norm", "rms_norm_kv_cache_paged"),
                         ("gather", "mla_gather_latent_paged")):
@@ -429,7 +446,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mla_prefill",
                     choices=["mla_prefill", "mla_decode", "mla_mixed", "mla_tiny",
-                             "qk_generic", "kv_norm", "gather"])
+                             "mla_prefill_inplace", "qk_generic", "kv_norm", "gather"])
     ap.add_argument("--no-siblings", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
@@ -490,7 +507,9 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
-        "io_dtypes": ("bf16 q and latent in; bf16 q out; fp8 e4m3fn cache rows out" if is_mla
+        "io_dtypes": ("bf16 q in and out; bf16 latent rows read and rewritten in the cache"
+                      if args.workload == "mla_prefill_inplace"
+                      else "bf16 q and latent in; bf16 q out; fp8 e4m3fn cache rows out" if is_mla
                       else "bf16 in, bf16 out" if args.workload != "gather"
                       else "fp8 e4m3fn cache rows in, bf16 rows out"),
         "data": "synthetic (seeded; DeepSeek-V3-shaped random tensors, no weights)",

@@ -1,7 +1,7 @@
 /*
  * pkv.h -- C ABI of the paged-KV pre-attention library (gfx950 / MI355X).
  *
- * Three entry points, each one stream-ordered kernel launch:
+ * Five entry points, each one stream-ordered kernel launch:
  *
  *   mla_rope_rmsnorm_quant   fused MLA step: RoPE on q_rope, RMSNorm on the
  *                            latent row's non-rope part, RoPE on its rope tail,
@@ -10,6 +10,11 @@
  *                            (summary, Args) and the
  *                            fused_rope_rmsnorm_quantization_kernel entry of
  *                            the "mla_graph" module page.
+ *   mla_rope_rmsnorm_inplace the same step on a bf16 cache that already
+ *                            holds the latent rows, in place
+ *                            (fused_rope_rmsnorm_kernel and the first two
+ *                            steps of mla_prefill_branch_fp8 /
+ *                            mla_decode_branch_fp8, "mla_graph" module page).
  *   qk_rope_paged_ragged     RoPE on Q (out of place) and on the new K rows of a
  *                            paged cache (in place), optional per-head K
  *                            RMSNorm fused in front of the K rotation.
@@ -156,6 +161,28 @@ int mla_rope_rmsnorm_quant(void* q_rope_out, int64_t qo_tok_stride, int64_t qo_h
                            uint32_t kv_norm_dim, const float* freqs_cis, uint32_t max_seq_len,
                            const void* gamma, float epsilon, const pkv_paged_cache* kv_cache,
                            uint32_t layer_idx, int32_t q_out_dtype, void* stream);
+
+/*
+ * Fused MLA pre-attention step in place on a bf16 latent cache ("mla_graph"
+ * module page: fused_rope_rmsnorm_kernel applies RoPE to q and RMSNorm to the
+ * cache; the fp8 prefill and decode branches apply RoPE and RMSNorm to the
+ * key cache in place).  Identical to mla_rope_rmsnorm_quant with a BF16 cache,
+ * except that x is read from the cache row the result replaces:
+ *   x = cache[layer_idx][page][slot][0][:]   (bf16, written earlier by the
+ *                                             caller at the token's slot)
+ *   cache[layer_idx][page][slot][0][:] = bf16_rne(y)
+ * Arguments as for mla_rope_rmsnorm_quant, without kv_latent / kv_row_stride;
+ * kv_cache must be dtype BF16 with scale mode NONE (else PKV_ERR_DTYPE).
+ * Rows of tokens that fail a device-data check are neither read nor written.
+ * Same supported sizes.
+ */
+int mla_rope_rmsnorm_inplace(void* q_rope_out, int64_t qo_tok_stride, int64_t qo_head_stride,
+                             const void* q_rope, int64_t qi_tok_stride, int64_t qi_head_stride,
+                             const uint32_t* input_row_offsets, uint32_t batch_size,
+                             uint32_t total_tokens, uint32_t num_heads, uint32_t rope_dim,
+                             uint32_t kv_norm_dim, const float* freqs_cis, uint32_t max_seq_len,
+                             const void* gamma, float epsilon, const pkv_paged_cache* kv_cache,
+                             uint32_t layer_idx, int32_t q_out_dtype, void* stream);
 
 /*
  * Paged-ragged fused Q/K RoPE.  Q is rotated into q_out; the K rows of the

@@ -78,6 +78,10 @@ def load(path: str | None = None) -> ctypes.CDLL:
         _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
         ctypes.c_float, _i64, _i64, _i64, _vp, ctypes.c_int, _i64, _i64, _i64,
         _i64, ctypes.c_int, ctypes.c_float, _vp]
+    lib.oracle_mla_rope_rmsnorm_inplace.restype = ctypes.c_int
+    lib.oracle_mla_rope_rmsnorm_inplace.argtypes = [
+        _vp, ctypes.c_int, _vp, _vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp, ctypes.c_float,
+        _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i64]
     lib.oracle_qk_rope_paged_ragged.restype = ctypes.c_int
     lib.oracle_qk_rope_paged_ragged.argtypes = [
         _vp, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _i64, _vp, ctypes.c_int, ctypes.c_int,
@@ -224,6 +228,26 @@ class Oracle:
             int(layer_idx), mode, float(tensor_scale),
             _ptr(token_scales, np.float32))
         _check(rc, "mla_rope_rmsnorm_quant")
+
+    def mla_rope_rmsnorm_inplace(self, q_out, q_in, row_offsets, cache_lengths, page_table,
+                                 freqs, gamma, epsilon, cache, layer_idx):
+        """In-place form on a bf16 cache [L,P,S,1,Dn+R] u16 that holds the new
+        tokens' latent rows at their slots; q as in
+        :meth:`mla_rope_rmsnorm_quant`."""
+        T, H, R = q_in.shape
+        L, P, S, one, W = cache.shape
+        if cache.dtype != np.uint16 or one != 1 or q_out.shape != q_in.shape:
+            raise ValueError("inconsistent in-place MLA arguments")
+        B = row_offsets.size - 1
+        q_f32 = q_out.dtype == np.float32
+        rc = self.lib.oracle_mla_rope_rmsnorm_inplace(
+            _ptr(q_out, np.float32 if q_f32 else np.uint16), int(q_f32),
+            _ptr(q_in, np.uint16), _ptr(row_offsets, np.uint32),
+            _ptr(cache_lengths, np.uint32), B, _ptr(page_table, np.uint32),
+            page_table.shape[1], _ptr(freqs, np.float32), freqs.shape[0],
+            _ptr(gamma, np.uint16), float(epsilon), H, R, W - R, _ptr(cache, np.uint16),
+            L, P, S, int(layer_idx))
+        _check(rc, "mla_rope_rmsnorm_inplace")
 
     def qk_rope_paged_ragged(self, q_out, q_in, row_offsets, cache_lengths,
                              page_table, k_cache, layer_idx, freqs, position_ids,

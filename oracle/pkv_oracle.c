@@ -235,6 +235,8 @@ static int64_t page_of(const uint32_t* page_table, int64_t pt_stride,
  *   cache         [L][P][S][Dn + R] of u8 (fp8 codes) or u16 (bf16 bits)
  *   token_scales  f32 [L][P][S]  (written in per-token mode only)
  * Only layer `layer_idx` and only the new tokens' slots are written.
+ * latent = NULL is the in-place form (see oracle_mla_rope_rmsnorm_inplace):
+ * each token's row x is read from its own slot of the bf16 cache.
  */
 int oracle_mla_rope_rmsnorm_quant(
     void* q_out, int q_out_f32, const uint16_t* q_in, const uint16_t* latent,
@@ -248,6 +250,7 @@ int oracle_mla_rope_rmsnorm_quant(
       layer_idx >= num_layers || page_size <= 0)
     return ORACLE_BAD_ARG;
   const int64_t W = Dn + R; /* latent row width */
+  if (!latent && cache_type != ORACLE_CACHE_BF16) return ORACLE_BAD_ARG;
   double x[4096], y[4096], g[4096], qa[1024], qb[1024];
   if (W > 4096 || R > 1024) return ORACLE_BAD_ARG;
   for (int64_t k = 0; k < Dn; ++k) g[k] = oracle_bf16_decode(gamma[k]);
@@ -281,12 +284,14 @@ int oracle_mla_rope_rmsnorm_quant(
         }
       }
 
-      /* latent: RMSNorm on the first Dn values, RoPE on the R-value tail. */
-      for (int64_t k = 0; k < W; ++k) x[k] = oracle_bf16_decode(latent[t * W + k]);
+      /* latent: RMSNorm on the first Dn values, RoPE on the R-value tail;
+       * the row comes from its buffer, or in place from the cache slot. */
+      const int64_t row = ((layer_idx * num_pages + page) * page_size + off);
+      const uint16_t* src = latent ? latent + t * W : (const uint16_t*)cache + row * W;
+      for (int64_t k = 0; k < W; ++k) x[k] = oracle_bf16_decode(src[k]);
       oracle_rmsnorm_row(x, y, Dn, g, eps);
       oracle_rope_row(x + Dn, y + Dn, R, fr, 0);
 
-      const int64_t row = ((layer_idx * num_pages + page) * page_size + off);
       if (cache_type == ORACLE_CACHE_BF16) {
         uint16_t* dst = (uint16_t*)cache + row * W;
         for (int64_t k = 0; k < W; ++k) dst[k] = oracle_bf16_encode(y[k]);
@@ -310,6 +315,25 @@ int oracle_mla_rope_rmsnorm_quant(
     }
   }
   return status;
+}
+
+/*
+ * In-place form ([GRAPH] fused_rope_rmsnorm_kernel; the fp8 prefill and
+ * decode branches apply RoPE and RMSNorm to the key cache in place): the
+ * latent row of every new token already sits in the bf16 cache at its slot
+ * and is replaced by its normalised, rotated value; q as above.
+ */
+int oracle_mla_rope_rmsnorm_inplace(
+    void* q_out, int q_out_f32, const uint16_t* q_in, const uint32_t* row_offsets,
+    const uint32_t* cache_lengths, int64_t B, const uint32_t* page_table, int64_t pt_stride,
+    const float* freqs, int64_t max_seq_len, const uint16_t* gamma, float epsilon, int64_t H,
+    int64_t R, int64_t Dn, uint16_t* cache, int64_t num_layers, int64_t num_pages,
+    int64_t page_size, int64_t layer_idx) {
+  return oracle_mla_rope_rmsnorm_quant(q_out, q_out_f32, q_in, NULL, row_offsets,
+                                       cache_lengths, B, page_table, pt_stride, freqs,
+                                       max_seq_len, gamma, epsilon, H, R, Dn, cache,
+                                       ORACLE_CACHE_BF16, num_layers, num_pages, page_size,
+                                       layer_idx, 0, 1.0f, NULL);
 }
 
 /*

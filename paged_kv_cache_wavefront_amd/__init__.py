@@ -30,8 +30,8 @@ PKV_SCALE_NONE = 0
 PKV_SCALE_PER_TENSOR = 1
 PKV_SCALE_PER_TOKEN = 2
 
-EXPORTED = ("mla_rope_rmsnorm_quant", "qk_rope_paged_ragged", "rms_norm_kv_cache_paged",
-            "mla_gather_latent_paged", "pkv_status_string")
+EXPORTED = ("mla_rope_rmsnorm_quant", "mla_rope_rmsnorm_inplace", "qk_rope_paged_ragged",
+            "rms_norm_kv_cache_paged", "mla_gather_latent_paged", "pkv_status_string")
 
 
 class PkvError(RuntimeError):
@@ -75,6 +75,10 @@ def _load() -> ctypes.CDLL:
     lib.mla_rope_rmsnorm_quant.restype = ctypes.c_int
     lib.mla_rope_rmsnorm_quant.argtypes = [
         vp, i64, i64, vp, i64, i64, vp, i64, vp, u32, u32, u32, u32, u32, vp, u32, vp, f32,
+        cache_p, u32, ctypes.c_int32, vp]
+    lib.mla_rope_rmsnorm_inplace.restype = ctypes.c_int
+    lib.mla_rope_rmsnorm_inplace.argtypes = [
+        vp, i64, i64, vp, i64, i64, vp, u32, u32, u32, u32, u32, vp, u32, vp, f32,
         cache_p, u32, ctypes.c_int32, vp]
     lib.qk_rope_paged_ragged.restype = ctypes.c_int
     lib.qk_rope_paged_ragged.argtypes = [
@@ -171,6 +175,26 @@ def mla_rope_rmsnorm_quant(q_rope_output: torch.Tensor, q_rope: torch.Tensor,
         PKV_DTYPE_F32 if q_rope_output.dtype == torch.float32 else PKV_DTYPE_BF16,
         _stream(stream))
     _check("mla_rope_rmsnorm_quant", st)
+
+
+def mla_rope_rmsnorm_inplace(q_rope_output: torch.Tensor, q_rope: torch.Tensor,
+                             input_row_offsets: torch.Tensor, freqs_cis: torch.Tensor,
+                             gamma: torch.Tensor, epsilon: float, kv_cache: PagedCache,
+                             layer_idx: int, stream=None) -> None:
+    """Fused MLA step in place on a bf16 latent cache that already holds the
+    new tokens' rows (C: ``mla_rope_rmsnorm_inplace``).  Shapes as for
+    :func:`mla_rope_rmsnorm_quant`; the latent row width is the cache's
+    head_dim."""
+    T, H, R = q_rope.shape
+    st = _lib.mla_rope_rmsnorm_inplace(
+        _ptr(q_rope_output), q_rope_output.stride(0), q_rope_output.stride(1),
+        _ptr(q_rope), q_rope.stride(0), q_rope.stride(1),
+        _ptr(input_row_offsets), input_row_offsets.numel() - 1, T, H, R,
+        kv_cache.head_dim - R, _ptr(freqs_cis), freqs_cis.shape[0], _ptr(gamma),
+        float(epsilon), ctypes.byref(kv_cache), int(layer_idx),
+        PKV_DTYPE_F32 if q_rope_output.dtype == torch.float32 else PKV_DTYPE_BF16,
+        _stream(stream))
+    _check("mla_rope_rmsnorm_inplace", st)
 
 
 def qk_rope_paged_ragged(q_out: torch.Tensor, q_proj: torch.Tensor,

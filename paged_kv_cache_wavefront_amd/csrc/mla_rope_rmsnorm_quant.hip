@@ -31,6 +31,13 @@
 //   significands).  The row is converted to fp8 in registers (clamp to +-448,
 //   then hardware round-to-nearest-even) and written with 8-byte
 //   non-temporal stores.
+// * In-place form ("mla_graph" module page: fused_rope_rmsnorm_kernel, and the
+//   first two steps of the fp8 prefill and decode branches, which apply RoPE
+//   and RMSNorm to the key cache in place): the latent row is not in a buffer
+//   but already sits in a bf16 cache at the token's slot; the chunk-0 wave
+//   reads it from there once the page lookup has resolved, issued before the
+//   q rotation so that its latency overlaps the q stores, and writes the
+//   normalised, rotated row back over it.
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -134,13 +141,16 @@ __global__ __launch_bounds__(256) void mla_kernel(const MlaArgs a) {
     load_q<NI, false>(q, qsrc, 16 * a.qi_head, qi_lane, h_lane, a.num_heads);
   else
     load_q<NI, true>(q, qsrc, 16 * a.qi_head, qi_lane, h_lane, a.num_heads);
+  constexpr bool INPLACE = MODE == MlaOut::Bf16InPlace;
   const bool latent_wave = chunk == 0;
   uint4 xn = {}, gm = {}, tail = {};
   if (latent_wave) {
-    const uint16_t* row = a.latent + (int64_t)t * a.kv_row;
-    xn = load16_stream(row + 8 * lane);
     gm = load16(a.gamma + 8 * lane);
-    if (lane < 8) tail = load16_stream(row + kNope + 8 * hl.chunk);
+    if constexpr (!INPLACE) {
+      const uint16_t* row = a.latent + (int64_t)t * a.kv_row;
+      xn = load16_stream(row + 8 * lane);
+      if (lane < 8) tail = load16_stream(row + kNope + 8 * hl.chunk);
+    }
   }
 
   // ---- address chain -----------------------------------------------------------
@@ -163,6 +173,14 @@ __global__ __launch_bounds__(256) void mla_kernel(const MlaArgs a) {
   if (!(pos_ok && page_of(cv.page_table, cv.pt_stride, cv.num_pages, cv.page_size, ts, &ps))) {
     if (latent_wave) count_skip(cv.error_count, lane);
     return;
+  }
+  const int64_t row_elems = (int64_t)ps.page * cv.page_stride + (int64_t)ps.offset * cv.slot_stride;
+  if constexpr (INPLACE) {
+    if (latent_wave) {
+      const uint16_t* row = static_cast<const uint16_t*>(cv.layer_base) + row_elems;
+      xn = load16_stream(row + 8 * lane);
+      if (lane < 8) tail = load16_stream(row + kNope + 8 * hl.chunk);
+    }
   }
   if (hl.first) {
 #pragma unroll
@@ -199,8 +217,7 @@ __global__ __launch_bounds__(256) void mla_kernel(const MlaArgs a) {
   unpack8(mirror16<8>(tail), tp);
   rotate_own(tv, tp, cs);  // meaningful on lanes 0..7 only
 
-  const int64_t row_elems = (int64_t)ps.page * cv.page_stride + (int64_t)ps.offset * cv.slot_stride;
-  if constexpr (MODE == MlaOut::Bf16) {
+  if constexpr (MODE == MlaOut::Bf16 || INPLACE) {
     uint16_t* row = static_cast<uint16_t*>(cv.layer_base) + row_elems;
 #pragma unroll
     for (int k = 0; k < 8; ++k) xg[k] *= r;
@@ -254,6 +271,10 @@ hipError_t launch_g(const MlaArgs& a, MlaOut mode, uint32_t blocks, hipStream_t 
     case MlaOut::Bf16:
       hipLaunchKernelGGL((mla_kernel<NI, MlaOut::Bf16, QF32>), dim3(blocks), dim3(256), 0,
                          stream, a);
+      break;
+    case MlaOut::Bf16InPlace:
+      hipLaunchKernelGGL((mla_kernel<NI, MlaOut::Bf16InPlace, QF32>), dim3(blocks), dim3(256),
+                         0, stream, a);
       break;
   }
   return hipGetLastError();

@@ -80,6 +80,83 @@ float* k_scales_of(const pkv_paged_cache* c, uint32_t layer_idx, pkv::KMode km) 
   return c->scales;
 }
 
+// Both MLA entry points: the latent row from kv_latent, or (in_place) from
+// the bf16 cache row it is written back to.
+int mla_entry(void* q_rope_out, int64_t qo_tok_stride, int64_t qo_head_stride,
+              const void* q_rope, int64_t qi_tok_stride, int64_t qi_head_stride,
+              const void* kv_latent, int64_t kv_row_stride, bool in_place,
+              const uint32_t* input_row_offsets, uint32_t batch_size, uint32_t total_tokens,
+              uint32_t num_heads, uint32_t rope_dim, uint32_t kv_norm_dim,
+              const float* freqs_cis, uint32_t max_seq_len, const void* gamma, float epsilon,
+              const pkv_paged_cache* kv_cache, uint32_t layer_idx, int32_t q_out_dtype,
+              void* stream) {
+  if (kv_cache == nullptr) return PKV_ERR_NULL;
+  if (q_out_dtype != PKV_DTYPE_BF16 && q_out_dtype != PKV_DTYPE_F32) return PKV_ERR_DTYPE;
+  const int64_t qo_align = q_out_dtype == PKV_DTYPE_F32 ? 4 : 8;  // 16 bytes in elements
+  if (rope_dim == 0 || rope_dim % 2 != 0 || kv_norm_dim == 0) return PKV_ERR_SHAPE;
+  if (kv_cache->num_heads != 1 || kv_cache->head_dim != kv_norm_dim + rope_dim)
+    return PKV_ERR_SHAPE;
+  if (rope_dim != kMlaRope || kv_norm_dim != kMlaNope) return PKV_ERR_UNSUPPORTED;
+  pkv::MlaOut mode;
+  if (kv_cache->dtype == PKV_DTYPE_FP8_E4M3FN && kv_cache->scale_mode == PKV_SCALE_PER_TENSOR)
+    mode = pkv::MlaOut::Fp8PerTensor;
+  else if (kv_cache->dtype == PKV_DTYPE_FP8_E4M3FN && kv_cache->scale_mode == PKV_SCALE_PER_TOKEN)
+    mode = pkv::MlaOut::Fp8PerToken;
+  else if (kv_cache->dtype == PKV_DTYPE_BF16 && kv_cache->scale_mode == PKV_SCALE_NONE)
+    mode = in_place ? pkv::MlaOut::Bf16InPlace : pkv::MlaOut::Bf16;
+  else
+    return PKV_ERR_DTYPE;
+  if (in_place && mode != pkv::MlaOut::Bf16InPlace) return PKV_ERR_DTYPE;
+  if (total_tokens > 0 && batch_size == 0) return PKV_ERR_SHAPE;
+  if (max_seq_len == 0) return PKV_ERR_SHAPE;
+  CacheView view{};
+  int st = check_cache(kv_cache, layer_idx, batch_size, &view);
+  if (st != PKV_OK) return st;
+  if (total_tokens == 0) return PKV_OK;
+
+  if (input_row_offsets == nullptr || freqs_cis == nullptr || gamma == nullptr ||
+      (!in_place && kv_latent == nullptr))
+    return PKV_ERR_NULL;
+  if (num_heads > 0 && (q_rope == nullptr || q_rope_out == nullptr)) return PKV_ERR_NULL;
+  const bool fp8 = mode == pkv::MlaOut::Fp8PerTensor || mode == pkv::MlaOut::Fp8PerToken;
+  if (fp8 && kv_cache->scales == nullptr) return PKV_ERR_NULL;
+  if (!aligned16(q_rope) || !aligned16(q_rope_out) || !aligned16(gamma) ||
+      !aligned16(freqs_cis) || !mult(qo_tok_stride, qo_align) ||
+      !mult(qo_head_stride, qo_align) || !mult(qi_tok_stride, 8) || !mult(qi_head_stride, 8))
+    return PKV_ERR_ALIGN;
+  if (!in_place && (!aligned16(kv_latent) || !mult(kv_row_stride, 8))) return PKV_ERR_ALIGN;
+  if (qi_head_stride > kMaxHeadStride || qo_head_stride > kMaxHeadStride)
+    return PKV_ERR_UNSUPPORTED;
+
+  pkv::MlaArgs a{};
+  a.q_out = q_rope_out;
+  a.q_out_f32 = q_out_dtype == PKV_DTYPE_F32;
+  a.qo_tok = qo_tok_stride;
+  a.qo_head = qo_head_stride;
+  a.q_in = static_cast<const uint16_t*>(q_rope);
+  a.qi_tok = qi_tok_stride;
+  a.qi_head = qi_head_stride;
+  a.latent = in_place ? nullptr : static_cast<const uint16_t*>(kv_latent);
+  a.kv_row = in_place ? 0 : kv_row_stride;
+  a.offsets = input_row_offsets;
+  a.batch = batch_size;
+  a.total_tokens = total_tokens;
+  a.num_heads = num_heads;
+  const int hpw = (int)pkv::mla_heads_per_wave(num_heads);
+  a.chunks = num_heads == 0 ? 1u : (num_heads + (uint32_t)hpw - 1) / (uint32_t)hpw;
+  a.freqs = freqs_cis;
+  a.max_seq_len = max_seq_len;
+  a.gamma = static_cast<const uint16_t*>(gamma);
+  a.epsilon = epsilon;
+  a.tensor_scale = kv_cache->scales;
+  a.token_scales = nullptr;
+  if (mode == pkv::MlaOut::Fp8PerToken)
+    a.token_scales = kv_cache->scales + (int64_t)layer_idx * kv_cache->num_pages *
+                                            kv_cache->page_size * kv_cache->num_heads;
+  a.cache = view;
+  return launch_status(pkv::launch_mla(a, mode, hpw, static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -106,69 +183,23 @@ int mla_rope_rmsnorm_quant(void* q_rope_out, int64_t qo_tok_stride, int64_t qo_h
                            uint32_t kv_norm_dim, const float* freqs_cis, uint32_t max_seq_len,
                            const void* gamma, float epsilon, const pkv_paged_cache* kv_cache,
                            uint32_t layer_idx, int32_t q_out_dtype, void* stream) {
-  if (kv_cache == nullptr) return PKV_ERR_NULL;
-  if (q_out_dtype != PKV_DTYPE_BF16 && q_out_dtype != PKV_DTYPE_F32) return PKV_ERR_DTYPE;
-  const int64_t qo_align = q_out_dtype == PKV_DTYPE_F32 ? 4 : 8;  // 16 bytes in elements
-  if (rope_dim == 0 || rope_dim % 2 != 0 || kv_norm_dim == 0) return PKV_ERR_SHAPE;
-  if (kv_cache->num_heads != 1 || kv_cache->head_dim != kv_norm_dim + rope_dim)
-    return PKV_ERR_SHAPE;
-  if (rope_dim != kMlaRope || kv_norm_dim != kMlaNope) return PKV_ERR_UNSUPPORTED;
-  pkv::MlaOut mode;
-  if (kv_cache->dtype == PKV_DTYPE_FP8_E4M3FN && kv_cache->scale_mode == PKV_SCALE_PER_TENSOR)
-    mode = pkv::MlaOut::Fp8PerTensor;
-  else if (kv_cache->dtype == PKV_DTYPE_FP8_E4M3FN && kv_cache->scale_mode == PKV_SCALE_PER_TOKEN)
-    mode = pkv::MlaOut::Fp8PerToken;
-  else if (kv_cache->dtype == PKV_DTYPE_BF16 && kv_cache->scale_mode == PKV_SCALE_NONE)
-    mode = pkv::MlaOut::Bf16;
-  else
-    return PKV_ERR_DTYPE;
-  if (total_tokens > 0 && batch_size == 0) return PKV_ERR_SHAPE;
-  if (max_seq_len == 0) return PKV_ERR_SHAPE;
-  CacheView view{};
-  int st = check_cache(kv_cache, layer_idx, batch_size, &view);
-  if (st != PKV_OK) return st;
-  if (total_tokens == 0) return PKV_OK;
+  return mla_entry(q_rope_out, qo_tok_stride, qo_head_stride, q_rope, qi_tok_stride,
+                   qi_head_stride, kv_latent, kv_row_stride, false, input_row_offsets,
+                   batch_size, total_tokens, num_heads, rope_dim, kv_norm_dim, freqs_cis,
+                   max_seq_len, gamma, epsilon, kv_cache, layer_idx, q_out_dtype, stream);
+}
 
-  if (input_row_offsets == nullptr || freqs_cis == nullptr || gamma == nullptr ||
-      kv_latent == nullptr)
-    return PKV_ERR_NULL;
-  if (num_heads > 0 && (q_rope == nullptr || q_rope_out == nullptr)) return PKV_ERR_NULL;
-  if (mode != pkv::MlaOut::Bf16 && kv_cache->scales == nullptr) return PKV_ERR_NULL;
-  if (!aligned16(q_rope) || !aligned16(q_rope_out) || !aligned16(kv_latent) ||
-      !aligned16(gamma) || !aligned16(freqs_cis) || !mult(qo_tok_stride, qo_align) ||
-      !mult(qo_head_stride, qo_align) || !mult(qi_tok_stride, 8) || !mult(qi_head_stride, 8) ||
-      !mult(kv_row_stride, 8))
-    return PKV_ERR_ALIGN;
-  if (qi_head_stride > kMaxHeadStride || qo_head_stride > kMaxHeadStride)
-    return PKV_ERR_UNSUPPORTED;
-
-  pkv::MlaArgs a{};
-  a.q_out = q_rope_out;
-  a.q_out_f32 = q_out_dtype == PKV_DTYPE_F32;
-  a.qo_tok = qo_tok_stride;
-  a.qo_head = qo_head_stride;
-  a.q_in = static_cast<const uint16_t*>(q_rope);
-  a.qi_tok = qi_tok_stride;
-  a.qi_head = qi_head_stride;
-  a.latent = static_cast<const uint16_t*>(kv_latent);
-  a.kv_row = kv_row_stride;
-  a.offsets = input_row_offsets;
-  a.batch = batch_size;
-  a.total_tokens = total_tokens;
-  a.num_heads = num_heads;
-  const int hpw = (int)pkv::mla_heads_per_wave(num_heads);
-  a.chunks = num_heads == 0 ? 1u : (num_heads + (uint32_t)hpw - 1) / (uint32_t)hpw;
-  a.freqs = freqs_cis;
-  a.max_seq_len = max_seq_len;
-  a.gamma = static_cast<const uint16_t*>(gamma);
-  a.epsilon = epsilon;
-  a.tensor_scale = kv_cache->scales;
-  a.token_scales = nullptr;
-  if (mode == pkv::MlaOut::Fp8PerToken)
-    a.token_scales = kv_cache->scales + (int64_t)layer_idx * kv_cache->num_pages *
-                                            kv_cache->page_size * kv_cache->num_heads;
-  a.cache = view;
-  return launch_status(pkv::launch_mla(a, mode, hpw, static_cast<hipStream_t>(stream)));
+int mla_rope_rmsnorm_inplace(void* q_rope_out, int64_t qo_tok_stride, int64_t qo_head_stride,
+                             const void* q_rope, int64_t qi_tok_stride, int64_t qi_head_stride,
+                             const uint32_t* input_row_offsets, uint32_t batch_size,
+                             uint32_t total_tokens, uint32_t num_heads, uint32_t rope_dim,
+                             uint32_t kv_norm_dim, const float* freqs_cis, uint32_t max_seq_len,
+                             const void* gamma, float epsilon, const pkv_paged_cache* kv_cache,
+                             uint32_t layer_idx, int32_t q_out_dtype, void* stream) {
+  return mla_entry(q_rope_out, qo_tok_stride, qo_head_stride, q_rope, qi_tok_stride,
+                   qi_head_stride, nullptr, 0, true, input_row_offsets, batch_size,
+                   total_tokens, num_heads, rope_dim, kv_norm_dim, freqs_cis, max_seq_len,
+                   gamma, epsilon, kv_cache, layer_idx, q_out_dtype, stream);
 }
 
 int qk_rope_paged_ragged(void* q_out, int64_t qo_tok_stride, int64_t qo_head_stride,

@@ -22,7 +22,10 @@ struct CacheView {
   uint32_t* error_count;
 };
 
-enum class MlaOut : int { Fp8PerTensor = 0, Fp8PerToken = 1, Bf16 = 2 };
+// Latent row source and cache encoding of the MLA kernel: from the latent
+// buffer into an fp8 (tensor / token scale) or bf16 cache, or in place on a
+// bf16 cache that already holds the row.
+enum class MlaOut : int { Fp8PerTensor = 0, Fp8PerToken = 1, Bf16 = 2, Bf16InPlace = 3 };
 
 struct MlaArgs {
   void* q_out;                 // bf16, or fp32 when q_out_f32
@@ -30,7 +33,7 @@ struct MlaArgs {
   int64_t qo_tok, qo_head;
   const uint16_t* q_in;
   int64_t qi_tok, qi_head;
-  const uint16_t* latent;
+  const uint16_t* latent;      // unused in place
   int64_t kv_row;
   const uint32_t* offsets;
   uint32_t batch;

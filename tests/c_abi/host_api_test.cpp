@@ -115,6 +115,14 @@ static int mla(const pkv_paged_cache* c, uint32_t T, uint32_t H, int32_t qdt, ui
                                 layer, qdt, nullptr);
 }
 
+static int mla_inplace(const pkv_paged_cache* c, uint32_t T, uint32_t H, uint32_t layer = 1) {
+  const int64_t qs = (int64_t)H * 64;
+  return mla_rope_rmsnorm_inplace(P(16384), qs, 64, P(20480), qs, 64,
+                                  static_cast<const uint32_t*>(P(28672)), 2, T, H, 64, 512,
+                                  static_cast<const float*>(P(32768)), 64, P(36864), 1e-6f, c,
+                                  layer, PKV_DTYPE_BF16, nullptr);
+}
+
 int main() {
   using namespace pkv;
   // --- MLA: per-token fp8, 40 heads, layer 1 of 2
@@ -151,6 +159,19 @@ int main() {
     t = latent_cache(PKV_DTYPE_FP8_E4M3FN, PKV_SCALE_PER_TENSOR, 7);
     t.slot_stride = 580;
     EXPECT(mla(&t, 3, 8, PKV_DTYPE_BF16) == PKV_ERR_ALIGN);
+    EXPECT(g_calls == before);
+  }
+  // --- MLA in place: bf16 cache only, no latent buffer
+  {
+    pkv_paged_cache c = latent_cache(PKV_DTYPE_BF16, PKV_SCALE_NONE, 7);
+    EXPECT(mla_inplace(&c, 3, 40) == PKV_OK && g_mla_mode == MlaOut::Bf16InPlace);
+    EXPECT(g_mla.latent == nullptr && g_mla.kv_row == 0 && g_mla.chunks == 2);
+    EXPECT(g_mla.cache.layer_base == static_cast<char*>(c.data) + 2 * c.layer_stride);
+    const int before = g_calls;
+    pkv_paged_cache t = latent_cache(PKV_DTYPE_FP8_E4M3FN, PKV_SCALE_PER_TENSOR, 7);
+    EXPECT(mla_inplace(&t, 3, 40) == PKV_ERR_DTYPE);
+    EXPECT(mla_inplace(&c, 0, 40) == PKV_OK);
+    EXPECT(mla_inplace(&c, 3, 40, 2) == PKV_ERR_RANGE);
     EXPECT(g_calls == before);
   }
   // --- Q/K RoPE: fp8 per-token K, mRoPE, K norm

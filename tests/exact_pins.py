@@ -214,17 +214,23 @@ def quantise_row(y, scale_mode, tensor_scale, tally_codes, tally_scale, got_code
 
 def pin_mla_exact(orc):
     """Fused MLA step: q rotation (bf16 and fp32 outputs), latent RMSNorm and
-    tail rotation, bf16 cache rows, fp8 codes with the tensor scale or a fresh
-    per-token scale, all equal to the exact value rounded once."""
+    tail rotation, bf16 cache rows (from the latent buffer, or in place from
+    the rows placed at their slots), fp8 codes with the tensor scale or a
+    fresh per-token scale, all equal to the exact value rounded once."""
     tq = Tally("mla q")
     tq32 = Tally("mla q fp32")
     tc = Tally("mla cache")
     ts_t = Tally("mla token scale")
-    cases = list(op.small_mla_cases())
+    runs = [(case, False) for case in op.small_mla_cases()]
+    runs += [(case, True) for case in list(op.small_mla_inplace_cases())[1:]]
     with localcontext() as ctx:
         ctx.prec = PREC
-        for ci, case in enumerate(cases):
-            q_out, cache, ts = op.run_mla(orc, case)
+        for ci, (case, in_place) in enumerate(runs):
+            if in_place:
+                q_out, cache = op.run_mla_inplace(orc, case)
+                ts = None
+            else:
+                q_out, cache, ts = op.run_mla(orc, case)
             q32 = None
             if ci == 2:
                 q32 = np.zeros(case.q.shape, np.float32)

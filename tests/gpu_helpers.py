@@ -198,6 +198,18 @@ class MlaDevice:
                                    self.freqs, self.gamma, self.case.epsilon, self.desc,
                                    self.case.layer_idx, stream=stream)
 
+    def place_rows(self):
+        """Write each new token's latent row into its slot of the (bf16)
+        device cache, as the in-place form expects."""
+        import oracle_pins
+        self.cache.copy_(dev_bf16(oracle_pins.place_latent_rows(self.case)))
+
+    def run_inplace(self, stream=None):
+        import paged_kv_cache_wavefront_amd as pkv
+        pkv.mla_rope_rmsnorm_inplace(self.q_out, self.q_in, self.offsets, self.freqs,
+                                     self.gamma, self.case.epsilon, self.desc,
+                                     self.case.layer_idx, stream=stream)
+
     def results(self):
         torch.cuda.synchronize()
         q = host_f32(self.q_out) if self.q_f32 else host_bf16(self.q_out)
@@ -220,6 +232,13 @@ def oracle_mla(orc, case, q_f32=False):
                                    case.epsilon, cache, case.layer_idx, case.scale_mode,
                                    case.tensor_scale, ts)
     return q_out, cache, ts, pre
+
+
+def oracle_mla_inplace(orc, case, q_f32=False):
+    """Oracle results of the in-place form, shaped like :func:`oracle_mla`."""
+    import oracle_pins
+    q_out, cache = oracle_pins.run_mla_inplace(orc, case, q_f32)
+    return q_out, cache, None, None
 
 
 def written_rows(case) -> np.ndarray:

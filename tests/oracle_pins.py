@@ -550,6 +550,70 @@ def pin_mla_f32_q(orc):
     assert np.array_equal(cache, cache_b)
 
 
+def small_mla_inplace_cases():
+    """bf16 latent caches for the in-place form: ragged prefill with page
+    crossings and zero-length requests, decode rows, fp32 q in one case."""
+    yield list(small_mla_cases())[4]
+    yield workloads.build_mla("mla_inplace_ragged", 2011, [7, 0, 13, 1, 0, 20], [3, 9, 0, 30, 0, 2],
+                              H=16, page_size=8, max_seq_len=64, spare_pages=5, latent_sigma=2.0,
+                              scale_mode="none", cache_dtype="bf16")
+    yield workloads.build_mla("mla_inplace_decode", 2012, [1] * 9, [0, 5, 15, 16, 17, 31, 32, 47, 63],
+                              H=8, page_size=16, max_seq_len=64, spare_pages=3,
+                              scale_mode="none", cache_dtype="bf16")
+
+
+def place_latent_rows(case):
+    """The case's bf16 cache with each new token's latent row written at its
+    slot (what the in-place form expects to find there)."""
+    cache = case.cache.copy()
+    owners = slot_owners(case.row_offsets, case.cache_lengths, case.page_table,
+                         case.meta["page_size"])
+    for (page, off), (t, slot) in owners.items():
+        cache[case.layer_idx, page, off, 0] = case.latent[t]
+    return cache
+
+
+def run_mla_inplace(orc, case, q_f32=False):
+    q_out = np.zeros(case.q.shape, np.float32 if q_f32 else np.uint16)
+    cache = place_latent_rows(case)
+    orc.mla_rope_rmsnorm_inplace(q_out, case.q, case.row_offsets, case.cache_lengths,
+                                 case.page_table, case.freqs, case.gamma, case.epsilon, cache,
+                                 case.layer_idx)
+    return q_out, cache
+
+
+def pin_mla_inplace(orc):
+    """In-place form: with the latent rows placed at their slots it gives
+    exactly what the (separately pinned) buffer form gives with a bf16 cache,
+    q included, and nothing else in the pool changes; rows placed elsewhere
+    are not read."""
+    for case in small_mla_inplace_cases():
+        for q_f32 in (False, True):
+            q_a, cache_a = run_mla_inplace(orc, case, q_f32)
+            q_b = np.zeros(case.q.shape, np.float32 if q_f32 else np.uint16)
+            cache_b = case.cache.copy()
+            orc.mla_rope_rmsnorm_quant(q_b, case.q, case.latent, case.row_offsets,
+                                       case.cache_lengths, case.page_table, case.freqs,
+                                       case.gamma, case.epsilon, cache_b, case.layer_idx, "none")
+            assert np.array_equal(q_a.view(np.uint8), q_b.view(np.uint8)), case.name
+            assert np.array_equal(cache_a, cache_b), case.name
+    # the rows are read from the token's own slot: garbage at the slots gives
+    # a different result, garbage elsewhere does not
+    case = list(small_mla_inplace_cases())[1]
+    _, ref = run_mla_inplace(orc, case)
+    cache = place_latent_rows(case)
+    owners = slot_owners(case.row_offsets, case.cache_lengths, case.page_table,
+                         case.meta["page_size"])
+    used = np.zeros(cache.shape[:3], bool)
+    for (page, off) in owners:
+        used[case.layer_idx, page, off] = True
+    cache[~used] ^= 0x5555
+    orc.mla_rope_rmsnorm_inplace(np.zeros_like(case.q), case.q, case.row_offsets,
+                                 case.cache_lengths, case.page_table, case.freqs, case.gamma,
+                                 case.epsilon, cache, case.layer_idx)
+    assert np.array_equal(cache[used], ref[used]), "rows outside the slots were read"
+
+
 def pin_mla_position0(orc):
     """Tokens at position 0 come back unchanged in q (values; +-0 equal)."""
     case = workloads.build_mla("mla_pos0", 2005, [1] * 6, [0] * 6, H=8,
@@ -975,5 +1039,5 @@ ALL_PINS = [
     pin_rmsnorm_closed_forms, pin_rmsnorm_torch, pin_mla_composite,
     pin_mla_position0, pin_mla_zero_row_per_token, pin_qk_composite,
     pin_rms_norm_kv, pin_gather, pin_qk_fp8, pin_rms_norm_kv_fp8, pin_mrope,
-    pin_mla_f32_q, pin_rms_norm_kv_token,
+    pin_mla_f32_q, pin_rms_norm_kv_token, pin_mla_inplace,
 ]

@@ -31,9 +31,10 @@ def pkv():
 
 
 def test_header_declares_entry_points():
-    assert declared_functions() == sorted(["mla_rope_rmsnorm_quant", "qk_rope_paged_ragged",
-                                           "rms_norm_kv_cache_paged", "mla_gather_latent_paged",
-                                           "pkv_status_string", "pkv_stream_copy"])
+    assert declared_functions() == sorted(["mla_rope_rmsnorm_quant", "mla_rope_rmsnorm_inplace",
+                                           "qk_rope_paged_ragged", "rms_norm_kv_cache_paged",
+                                           "mla_gather_latent_paged", "pkv_status_string",
+                                           "pkv_stream_copy"])
 
 
 def test_library_exports_every_declared_function(pkv):
@@ -125,6 +126,31 @@ def test_mla_validation(pkv):
     assert call_mla(pkv, mla_cache(pkv, data=FAKE + 8)) == ALIGN
     # nothing to do: accepted without a launch
     assert call_mla(pkv, mla_cache(pkv), T=0) == OK
+
+
+def call_mla_inplace(pkv, cache, T=16, H=4, R=64, Dn=512, q=FAKE, qo=FAKE, layer=1, batch=2,
+                     gamma=FAKE, qo_dtype=0):
+    lib = pkv.library()
+    cp = None if cache is None else ctypes.byref(cache)
+    return lib.mla_rope_rmsnorm_inplace(qo, 4 * 64, R, q, 4 * 64, R, FAKE, batch, T, H, R, Dn,
+                                        FAKE, 64, gamma, 1e-6, cp, layer, qo_dtype, None)
+
+
+def test_mla_inplace_validation(pkv):
+    bf16 = dict(dtype=pkv.PKV_DTYPE_BF16, scale_mode=pkv.PKV_SCALE_NONE, scales=None,
+                layer_stride=8 * 16 * 576)
+    assert call_mla_inplace(pkv, None) == NULL
+    # the rows are read from and written to a bf16 cache only
+    assert call_mla_inplace(pkv, mla_cache(pkv)) == DTYPE
+    assert call_mla_inplace(pkv, mla_cache(pkv, scale_mode=pkv.PKV_SCALE_PER_TOKEN)) == DTYPE
+    assert call_mla_inplace(pkv, mla_cache(pkv, dtype=pkv.PKV_DTYPE_BF16)) == DTYPE
+    assert call_mla_inplace(pkv, mla_cache(pkv, **bf16), T=0) == OK
+    assert call_mla_inplace(pkv, mla_cache(pkv, **bf16), layer=2) == RANGE
+    assert call_mla_inplace(pkv, mla_cache(pkv, **bf16), R=32) == SHAPE
+    assert call_mla_inplace(pkv, mla_cache(pkv, **bf16), gamma=None) == NULL
+    assert call_mla_inplace(pkv, mla_cache(pkv, **bf16), q=FAKE + 8) == ALIGN
+    assert call_mla_inplace(pkv, mla_cache(pkv, **bf16, slot_stride=580)) == ALIGN
+    assert call_mla_inplace(pkv, mla_cache(pkv, **bf16), qo_dtype=pkv.PKV_DTYPE_FP8_E4M3FN) == DTYPE
 
 
 def kcache(pkv, **kw):

@@ -97,6 +97,9 @@ MUTANTS = [
      "const int64_t pk = (int64_t)position_ids[t * 3 + k];"),
     ("gather_quant_multiplies", "oracle_bf16_decode(bits) / (double)out_tensor_scale);",
      "oracle_bf16_decode(bits) * (double)out_tensor_scale);"),
+    ("inplace_reads_next_slot",
+     "const uint16_t* src = latent ? latent + t * W : (const uint16_t*)cache + row * W;",
+     "const uint16_t* src = latent ? latent + t * W : (const uint16_t*)cache + (row + 1) * W;"),
     # rounding-rule slips only the exact-arithmetic pins see: a per-token
     # scale rounded twice, and exact ties broken upwards
     ("mla_token_scale_two_roundings", "const float st = (float)(amax / 448.0); /* stored fp32",

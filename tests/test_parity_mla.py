@@ -1,7 +1,8 @@
-"""GPU parity of mla_rope_rmsnorm_quant against the CPU oracle, through the
-C ABI (binding -> libpkv.so), on the four MLA workloads at full size, small
-ragged cases, q layouts, degenerate inputs, the E4M3FN codec over every bf16
-value, and determinism."""
+"""GPU parity of mla_rope_rmsnorm_quant (and of its in-place form,
+mla_rope_rmsnorm_inplace) against the CPU oracle, through the C ABI (binding
+-> libpkv.so), on the four MLA workloads at full size, small ragged cases, q
+layouts, degenerate inputs, the E4M3FN codec over every bf16 value, and
+determinism."""
 import numpy as np
 import pytest
 import torch
@@ -195,3 +196,83 @@ def test_stream_ordering(orc):
         dev.run(stream=s)
     s.synchronize()
     gh.compare_mla(case, dev.results(), gh.oracle_mla(orc, case))
+
+
+# -- in-place form on a bf16 cache that already holds the rows --------------------------
+
+
+def _run_inplace(orc, case, q_f32=False):
+    _say(f"[mla-inplace] case={case.name} seed={case.seed} T={case.T} B={case.B} H={case.H} "
+         f"q_f32={q_f32}")
+    dev = gh.MlaDevice(case, "dense", q_f32)
+    dev.place_rows()
+    dev.run_inplace()
+    gpu = dev.results()
+    assert gpu[3] == 0, f"{gpu[3]} tokens skipped"
+    stats = gh.compare_mla(case, gpu, gh.oracle_mla_inplace(orc, case, q_f32))
+    _say(f"[mla-inplace] {case.name}: {stats}")
+    return gpu
+
+
+@pytest.mark.parametrize("idx", range(3))
+@pytest.mark.parametrize("q_f32", [False, True])
+def test_inplace_small_cases(orc, idx, q_f32):
+    _run_inplace(orc, list(oracle_pins.small_mla_inplace_cases())[idx], q_f32)
+
+
+def _inplace_big():
+    rng = workloads.make_rng(4101)
+    new = rng.integers(1, 600, size=12, endpoint=True)
+    return workloads.build_mla("mla_inplace_big", 4101, new, rng.integers(0, 3000, size=12),
+                               H=128, page_size=128, max_seq_len=4096, spare_pages=4,
+                               latent_sigma=2.0, scale_mode="none", cache_dtype="bf16", rng=rng)
+
+
+def test_inplace_prefill_shaped(orc):
+    """128 heads, 12 ragged requests, page size 128, bf16 cache."""
+    _run_inplace(orc, _inplace_big())
+
+
+def test_inplace_equals_buffer_form(orc):
+    """The in-place form is the buffer form with the row read from the cache:
+    bit-identical q and cache to a buffer-form launch into a bf16 cache."""
+    case = _inplace_big()
+    a = gh.MlaDevice(case)
+    a.place_rows()
+    a.run_inplace()
+    ra = a.results()
+    b = gh.MlaDevice(case)
+    b.run()
+    rb = b.results()
+    rows = gh.written_rows(case)
+    assert np.array_equal(ra[0], rb[0]), "q differs"
+    assert np.array_equal(ra[1][rows], rb[1][rows]), "cache rows differ"
+    assert np.array_equal(ra[1][~rows], case.cache[~rows])
+
+
+def test_inplace_skipped_tokens(orc):
+    """A token whose page id lies beyond the pool is skipped and counted; its
+    row (wherever the table points) is neither read nor written."""
+    good = workloads.build_mla("mla_inplace_bad", 4102, [3, 4], [0, 10], H=8, page_size=8,
+                               max_seq_len=32, spare_pages=2, scale_mode="none",
+                               cache_dtype="bf16")
+    dev = gh.MlaDevice(good)
+    dev.place_rows()
+    placed = gh.host_bf16(dev.cache).copy()
+    bad_table = good.page_table.copy()
+    bad_table[0, 0] = good.meta["num_pages"] + 1
+    dev.page_table.copy_(gh.dev_u32(bad_table))
+    dev.q_out.zero_()
+    dev.run_inplace()
+    q, cache, _, skipped = dev.results()
+    assert skipped == 3, skipped
+    assert not q[:3].any(), "skipped tokens wrote q"
+    q_o, cache_o, _, _ = gh.oracle_mla_inplace(orc, good)
+    assert gh.bf16_ulp_diff(q[3:], q_o[3:]).max() <= 1
+    owners = oracle_pins.slot_owners(good.row_offsets, good.cache_lengths, good.page_table, 8)
+    L = good.layer_idx
+    for (page, off), (t, slot) in owners.items():
+        if t < 3:
+            assert np.array_equal(cache[L, page, off], placed[L, page, off]), "skipped row changed"
+        else:
+            gh.check_bf16(cache[L, page, off], cache_o[L, page, off], "row")

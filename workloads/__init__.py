@@ -211,6 +211,17 @@ def mla_prefill(seed: int = 1003) -> MlaCase:
                      rng=rng)
 
 
+def mla_prefill_inplace(seed: int = 1003) -> MlaCase:
+    """The DeepSeek-V3-shaped prefill batch of :func:`mla_prefill` over a bf16
+    latent cache, for the in-place form (the rows are placed at their slots
+    before the step)."""
+    rng = make_rng(seed)
+    new = rng.integers(512, 4096, size=8, endpoint=True)
+    return build_mla("mla_prefill_inplace", seed, new, np.zeros(8, np.int64), H=128,
+                     page_size=128, max_seq_len=16384, spare_pages=16,
+                     latent_sigma=2.0, scale_mode="none", cache_dtype="bf16", rng=rng)
+
+
 def mla_mixed(seed: int = 1004) -> MlaCase:
     """Mixed ragged batch: 64 decode rows (prior U{0..32767}) then 4 prefill
     requests of 2048 tokens; 16 heads (128 heads split 8 ways); inputs ~N(0,1)
@@ -331,5 +342,6 @@ NAMED = {
     "mla_decode": mla_decode,
     "mla_prefill": mla_prefill,
     "mla_mixed": mla_mixed,
+    "mla_prefill_inplace": mla_prefill_inplace,
     "qk_generic": qk_generic,
 }
