@@ -286,8 +286,6 @@ hipError_t launch_q(const MlaArgs& a, MlaOut mode, int heads_per_wave, uint32_t 
   switch (heads_per_wave) {
     case 16: return launch_g<2, QF32>(a, mode, blocks, stream);
     case 32: return launch_g<4, QF32>(a, mode, blocks, stream);
-    case 64: return launch_g<8, QF32>(a, mode, blocks, stream);
-    case 128: return launch_g<16, QF32>(a, mode, blocks, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -297,8 +295,9 @@ hipError_t launch_q(const MlaArgs& a, MlaOut mode, int heads_per_wave, uint32_t 
 // 32 heads (4 instructions of 8 heads) per wave measured best on 128-head
 // prefill and decode batches: small enough to keep 8 waves per SIMD resident
 // and to spread a token over 4 waves, large enough to amortise each wave's
-// address chain.  Heads beyond a multiple of 16 are never padded past the
-// next multiple of 16.
+// address chain (rotating outputs, 17108-token prefill: 16 heads per wave
+// 104 us, 32 heads 97 us, 64 heads 98 us).  Heads beyond a multiple of 16 are
+// never padded past the next multiple of 16.
 uint32_t mla_heads_per_wave(uint32_t heads) { return heads > 16 ? 32 : 16; }
 
 hipError_t launch_mla(const MlaArgs& a, MlaOut mode, int heads_per_wave, hipStream_t stream) {

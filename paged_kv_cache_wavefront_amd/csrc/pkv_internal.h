@@ -49,8 +49,8 @@ struct MlaArgs {
   CacheView cache;
 };
 
-// heads_per_wave is 16, 32, 64 or 128 (the two widest are kept for tuning).
-// Heads per MLA wave for a q with `heads` heads (16 or 32).
+// Heads per MLA wave for a q with `heads` heads (16 or 32); launch_mla takes
+// that value.
 uint32_t mla_heads_per_wave(uint32_t heads);
 hipError_t launch_mla(const MlaArgs& a, MlaOut mode, int heads_per_wave, hipStream_t stream);
 

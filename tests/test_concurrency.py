@@ -1,6 +1,7 @@
-"""Two entry points on two streams at once: the library keeps no state
-between calls, so concurrent launches on different streams (on disjoint
-outputs) give the same results as one after the other."""
+"""Two entry points on two streams at once, and several host threads calling
+at once: the library keeps no state between calls, so concurrent launches on
+different streams (on disjoint outputs) give the same results as one after
+the other."""
 import numpy as np
 import pytest
 import torch
@@ -53,3 +54,64 @@ def test_same_entry_point_two_streams(orc):
         s.synchronize()
     for c, d in zip(cases, devs):
         gh.compare_mla(c, d.results(), gh.oracle_mla(orc, c))
+
+
+def test_host_threads():
+    """Several host threads calling entry points at once, each on its own
+    stream (ctypes releases the GIL during the call, so the host-side
+    validation and launch code runs concurrently): every output is
+    bit-identical to a single-threaded launch of the same call."""
+    import threading
+    import paged_kv_cache_wavefront_amd as pkv
+    mcases = [list(oracle_pins.small_mla_cases())[i] for i in (1, 2, 3)]
+    mdevs = [gh.MlaDevice(c) for c in mcases]
+    gcase, kvo = oracle_pins.gather_case("fp8_token")
+    gdesc = pkv.paged_cache(gh.dev_u8(gcase.cache), None, gh.dev_u32(gcase.page_table),
+                            pkv.PKV_SCALE_PER_TOKEN, gh.dev_f32(gcase.token_scales))
+    gkv = gh.dev_u32(kvo)
+    gout = torch.zeros((int(kvo[-1]), gcase.cache.shape[-1]), dtype=torch.bfloat16,
+                       device="cuda")
+
+    def gather(stream=None):
+        pkv.mla_gather_latent_paged(gout, gkv, gdesc, gcase.layer_idx, stream=stream)
+
+    # single-threaded references
+    ref = []
+    for d in mdevs:
+        d.run()
+        ref.append(d.results())
+    gather()
+    torch.cuda.synchronize()
+    gref = gout.clone()
+    for d in mdevs:
+        d.q_out.zero_()
+    gout.zero_()
+    torch.cuda.synchronize()
+
+    jobs = [(lambda s, d=d: d.run(stream=s)) for d in mdevs] + [gather]
+    errors = []
+
+    def worker(job):
+        try:
+            s = torch.cuda.Stream()
+            for _ in range(10):
+                job(s)
+            s.synchronize()
+        except Exception as e:  # noqa: BLE001 -- reported below
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(j,)) for j in jobs]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=60)
+    assert not any(t.is_alive() for t in threads), "a host thread did not finish"
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for d, r in zip(mdevs, ref):
+        got = d.results()
+        assert np.array_equal(got[0], r[0]) and np.array_equal(got[1], r[1])
+        # scales compared as bits: untouched slots hold random bytes, NaNs among them
+        assert (got[2] is None and r[2] is None) or np.array_equal(got[2].view(np.uint32),
+                                                                   r[2].view(np.uint32))
+    assert torch.equal(gout.view(torch.int16), gref.view(torch.int16))
