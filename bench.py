@@ -379,31 +379,103 @@ def measure_siblings(main, steps, warmup):
     return out
 
 
+def token_chunks(case, n: int):
+    """Split the batch into n sub-batches of (nearly) equal token counts for
+    the multi-threaded oracle leg.  A request cut in two keeps its slots: the
+    later part's prior length is where the earlier part ends.  Returns
+    (row_offsets, cache_lengths, page_table) per chunk; token indices stay
+    absolute, so every chunk writes its own rows of the shared outputs."""
+    offs = case.row_offsets.astype(np.int64)
+    clens = case.cache_lengths.astype(np.int64)
+    bounds = np.linspace(0, int(offs[-1]), n + 1).astype(np.int64)
+    chunks = []
+    for lo, hi in zip(bounds[:-1], bounds[1:]):
+        ro, cl, rows = [int(lo)], [], []
+        for b in range(offs.size - 1):
+            s, e = max(int(offs[b]), int(lo)), min(int(offs[b + 1]), int(hi))
+            if s >= e:
+                continue
+            ro.append(e)
+            cl.append(int(clens[b]) + s - int(offs[b]))
+            rows.append(b)
+        if rows:
+            chunks.append((np.array(ro, np.uint32), np.array(cl, np.uint32),
+                           np.ascontiguousarray(case.page_table[rows])))
+    return chunks
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(case, budget_s=10.0):
-    """The oracle (single-threaded C, binary64) on the same host arrays,
-    repeated over the whole workload until about budget_s has elapsed."""
+    """The oracle (C, binary64) on the same host arrays: single-threaded over
+    the whole workload until about budget_s has elapsed; then the same oracle
+    function called from N host threads at once on N token-balanced slices of
+    the batch (ctypes releases the GIL, so the calls run in parallel), for
+    about budget_s / 2, with its outputs checked bit for bit against the
+    single-threaded run."""
     import oracle
+    from concurrent.futures import ThreadPoolExecutor
     orc = oracle.default()
     q_out = np.zeros_like(case.q)
+
+    def whole(cache):
+        orc.mla_rope_rmsnorm_quant(q_out, case.q, case.latent, case.row_offsets,
+                                   case.cache_lengths, case.page_table, case.freqs, case.gamma,
+                                   case.epsilon, cache, case.layer_idx, case.scale_mode,
+                                   case.tensor_scale, None)
+
     tokens, t0 = 0, time.perf_counter()
     runs = 0
     while True:
         cache = case.cache.copy()
         t1 = time.perf_counter()
-        orc.mla_rope_rmsnorm_quant(q_out, case.q, case.latent, case.row_offsets,
-                                   case.cache_lengths, case.page_table, case.freqs, case.gamma,
-                                   case.epsilon, cache, case.layer_idx, case.scale_mode,
-                                   case.tensor_scale, None)
+        whole(cache)
         runs += 1
         tokens += case.T
         spent = time.perf_counter() - t0
         if spent >= budget_s or (time.perf_counter() - t1) * (runs + 1) > 3 * budget_s:
             break
     oracle_s = time.perf_counter() - t0
-    return {"value": round(tokens / oracle_s, 1), "unit": "tokens/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"whole workload ({case.T} tokens) x {runs} run(s), "
-                      f"{oracle_s:.1f} s, single thread"}
+    out = {"value": round(tokens / oracle_s, 1), "unit": "tokens/s", "cores": 1,
+           "kind": "oracle", "cpu_model": cpu_model(),
+           "sample": f"whole workload ({case.T} tokens) x {runs} run(s), "
+                     f"{oracle_s:.1f} s, single thread"}
+
+    n = max(1, min(len(os.sched_getaffinity(0)), 16))
+    chunks = token_chunks(case, n)
+    q_par = np.zeros_like(case.q)
+
+    def part(args, cache):
+        ro, cl, pt = args
+        orc.mla_rope_rmsnorm_quant(q_par, case.q, case.latent, ro, cl, pt, case.freqs,
+                                   case.gamma, case.epsilon, cache, case.layer_idx,
+                                   case.scale_mode, case.tensor_scale, None)
+
+    tokens, runs = 0, 0
+    with ThreadPoolExecutor(len(chunks)) as ex:
+        t0 = time.perf_counter()
+        while True:
+            cache_par = case.cache.copy()
+            list(ex.map(lambda c: part(c, cache_par), chunks))
+            runs += 1
+            tokens += case.T
+            if time.perf_counter() - t0 >= budget_s / 2:
+                break
+        par_s = time.perf_counter() - t0
+    same = bool(np.array_equal(q_par, q_out) and np.array_equal(cache_par, cache))
+    out["threads"] = {"value": round(tokens / par_s, 1), "cores": len(chunks),
+                      "sample": f"whole workload x {runs} run(s), {par_s:.1f} s, "
+                                f"{len(chunks)} threads on token-balanced slices",
+                      "same_bits_as_single_thread": same}
+    return out
 
 
 def calibrate_copy(steps, warmup, mib=1024):
