@@ -210,8 +210,8 @@ int mla_rope_rmsnorm_inplace(void* q_rope_out, int64_t qo_tok_stride, int64_t qo
  *                   mrope_section)
  *   mrope_section   (host) u32 [3] or NULL
  *   k_norm_gamma    bf16 [k_norm_cols] or NULL; 0 < k_norm_cols <= head_dim
- * Supported here: head_dim 64, 128 or 256; q and K head strides up to 2^27
- * elements (else PKV_ERR_UNSUPPORTED).
+ * Supported here: head_dim 64, 80, 96, 128 or 256; q and K head strides up
+ * to 2^27 elements (else PKV_ERR_UNSUPPORTED).
  */
 int qk_rope_paged_ragged(void* q_out, int64_t qo_tok_stride, int64_t qo_head_stride,
                          const void* q_proj, int64_t qi_tok_stride, int64_t qi_head_stride,
@@ -242,8 +242,8 @@ int qk_rope_paged_ragged(void* q_out, int64_t qo_tok_stride, int64_t qo_head_str
  *                  token over the first gamma_len columns of all its heads
  *                  (the page lists the flag without describing it; this is
  *                  the reading taken)
- * Supported here: head_dim 64, 128 or 256; per_head_norm 0 with at most
- * 2048 / head_dim heads.
+ * Supported here: head_dim 64, 80, 96, 128 or 256; per_head_norm 0 with at
+ * most 32 heads of 64, 16 heads of 80, 96 or 128, 8 heads of 256.
  */
 int rms_norm_kv_cache_paged(const pkv_paged_cache* k_cache, uint32_t layer_idx,
                             const void* gamma, uint32_t gamma_len, float epsilon,

@@ -58,6 +58,9 @@ int check_cache(const pkv_paged_cache* c, uint32_t layer_idx, uint32_t batch_siz
 
 int launch_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH; }
 
+// Head dims the Q/K RoPE and K-norm kernels are built for.
+bool sibling_head_dim(uint32_t d) { return d == 64 || d == 80 || d == 96 || d == 128 || d == 256; }
+
 // Element encoding of a K cache for the sibling entry points; false if the
 // dtype / scale-mode pair is not one of bf16 + none, fp8 + tensor / token.
 bool k_mode_of(const pkv_paged_cache* c, pkv::KMode* km) {
@@ -220,7 +223,7 @@ int qk_rope_paged_ragged(void* q_out, int64_t qo_tok_stride, int64_t qo_head_str
   if (!k_mode_of(k_cache, &km)) return PKV_ERR_DTYPE;
   if (k_norm_gamma != nullptr && (k_norm_cols == 0 || k_norm_cols > head_dim))
     return PKV_ERR_SHAPE;
-  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return PKV_ERR_UNSUPPORTED;
+  if (!sibling_head_dim(head_dim)) return PKV_ERR_UNSUPPORTED;
   if (total_tokens > 0 && batch_size == 0) return PKV_ERR_SHAPE;
   if (max_seq_len == 0) return PKV_ERR_SHAPE;
   CacheView view{};
@@ -279,7 +282,7 @@ int rms_norm_kv_cache_paged(const pkv_paged_cache* k_cache, uint32_t layer_idx,
   if (!k_mode_of(k_cache, &km)) return PKV_ERR_DTYPE;
   if (gamma_len == 0 || gamma_len > k_cache->head_dim) return PKV_ERR_SHAPE;
   if (km != pkv::KMode::Bf16 && !multiply_before_cast) return PKV_ERR_UNSUPPORTED;
-  if (k_cache->head_dim != 64 && k_cache->head_dim != 128 && k_cache->head_dim != 256)
+  if (!sibling_head_dim(k_cache->head_dim))
     return PKV_ERR_UNSUPPORTED;
   if (!per_head_norm && k_cache->num_heads > pkv::kv_norm_max_heads(k_cache->head_dim))
     return PKV_ERR_UNSUPPORTED;

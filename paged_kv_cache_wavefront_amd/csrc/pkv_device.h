@@ -15,6 +15,14 @@ namespace pkv {
 
 constexpr int kWave = 64;
 
+// Smallest power of two >= n (n >= 1): lanes per head group for a head of n
+// 16-byte chunks.
+__host__ __device__ constexpr int pow2_at_least(int n) {
+  int p = 1;
+  while (p < n) p *= 2;
+  return p;
+}
+
 // ---- bf16 <-> fp32 ---------------------------------------------------------
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

@@ -75,7 +75,7 @@ struct QkArgs {
   CacheView cache;               // K cache
 };
 
-// Q heads one wave of the Q/K kernel handles (head_dim 64 or 128).
+// Q heads one wave of the Q/K kernel handles (head_dim 64, 80, 96, 128, 256).
 uint32_t qk_heads_per_wave(int head_dim);
 hipError_t launch_qk_rope(const QkArgs& a, int head_dim, bool interleaved, KMode kmode,
                           hipStream_t stream);

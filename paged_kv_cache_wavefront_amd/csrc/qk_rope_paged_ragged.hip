@@ -9,19 +9,22 @@
 // before the rotation, with a single rounding at the end (bf16, or fp8 for
 // an fp8 K cache).
 //
-// Waves: one wave64 per (token, chunk of kQInstrPerWave x 64/(D/8) Q heads);
+// Waves: one wave64 per (token, chunk of kQInstrPerWave x 64/LP Q heads);
 // the chunk-0 wave of a token also rotates the token's K heads.  Lane
 // geometry (D = head_dim): each lane owns one 16-byte chunk (8 values) of a
-// head, D/8 lanes per head, so every Q instruction moves 64 x 16 contiguous
-// bytes.  An fp8 K head is read as 8 codes per lane (8 bytes), decoded and
-// scaled in registers (code x scale), and re-encoded with the tensor scale or
-// with a fresh per-(slot, head) scale max|y| / 448 from a DPP max over the
-// head's lanes.
+// head; a head occupies a group of LP lanes, LP = D/8 rounded up to a power
+// of two, so for D = 64, 128, 256 every Q instruction moves 64 x 16
+// contiguous bytes, and for D = 80, 96 (10 or 12 chunks in a 16-lane group)
+// the idle lanes of each group neither load nor store.  An fp8 K head is read
+// as 8 codes per lane (8 bytes), decoded and scaled in registers (code x
+// scale), and re-encoded with the tensor scale or with a fresh per-(slot,
+// head) scale max|y| / 448 from a DPP max over the head's lanes.
 // * interleaved: lane k holds values 8k..8k+7 = adjacent pairs 4k..4k+3.
-// * rotate-half: lane k < D/16 holds values 8k.. of the first half; lane
-//   k >= D/16 holds the second-half values of pairs 8(D/8-1-k)..; the partner
-//   of lane k is lane D/8-1-k, reached by one DPP mirror per dword (a
-//   ds_swizzle for D = 256, whose heads span 32 lanes).
+// * rotate-half (H = D/16 chunks per half): lane k < H holds values 8k.. of
+//   the first half; lane LP-1-k holds the second-half values of the same
+//   pairs 8k..8k+7, so the partner of lane k is lane LP-1-k, reached by one
+//   DPP mirror per dword (a ds_swizzle for D = 256, whose heads span 32
+//   lanes).
 // Pair i needs freqs columns 2i, 2i+1: 8 or 16 consecutive floats per lane,
 // loaded once per token.  Q is read, and Q and K are written, with
 // non-temporal accesses.
@@ -63,32 +66,46 @@ __device__ __forceinline__ void load_gamma8(const uint16_t* __restrict__ g, int 
   }
 }
 
+// A head of D values is D/8 chunks of 8; it occupies a group of LP lanes,
+// LP = D/8 rounded up to a power of two so that the DPP / swizzle mirror and
+// the group reductions work inside the group (D = 80 and 96 leave 6 and 4
+// lanes of each 16-lane group idle).
 template <int D, bool INTER>
 struct Geometry {
-  static constexpr int kLanesPerHead = D / 8;
+  static constexpr int kChunks = D / 8;
+  static constexpr int kLanesPerHead = pow2_at_least(kChunks);
+  static constexpr bool kPadded = kLanesPerHead != kChunks;
   static constexpr int kHeadsPerInstr = kWave / kLanesPerHead;
   static constexpr int kCs = INTER ? 8 : 16;  // cos/sin floats per lane
 };
 
+// Rotate-half: the first HALF lanes of a group hold the first-half chunks in
+// order, the last HALF lanes hold the second-half chunks mirrored, so the
+// partner of lane k is lane LP-1-k; lanes in between (padded groups) idle.
+// Interleaved: lane k holds chunk k; lanes past the last chunk idle.
 template <int D, bool INTER>
 struct LaneRole {
-  int k;            // lane within the head
+  int k;            // lane within the head group
+  bool active;      // holds a chunk of the head
   bool first;       // rotate-half: holds first-half values
   int chunk;        // 16-byte chunk of the head row it loads / stores
   int partner_chunk;
   int cs_base;      // first freqs column it needs
   __device__ __forceinline__ explicit LaneRole(int lane) {
-    constexpr int LP = D / 8, HALF = LP / 2;
+    constexpr int LP = Geometry<D, INTER>::kLanesPerHead;
+    constexpr int NC = Geometry<D, INTER>::kChunks, HALF = NC / 2;
     k = lane % LP;
     if constexpr (INTER) {
+      active = k < NC;
       first = true;
-      chunk = partner_chunk = k;
-      cs_base = 8 * k;
+      chunk = partner_chunk = active ? k : 0;
+      cs_base = 8 * chunk;
     } else {
       first = k < HALF;
-      const int pb = first ? k : LP - 1 - k;  // pair block: pairs 8pb..8pb+7
-      chunk = first ? k : LP + HALF - 1 - k;
-      partner_chunk = first ? HALF + k : LP - 1 - k;
+      active = first || k >= LP - HALF;
+      const int pb = first ? k : (active ? LP - 1 - k : 0);  // pairs 8pb..8pb+7
+      chunk = first ? k : HALF + pb;
+      partner_chunk = first ? HALF + k : pb;
       cs_base = 16 * pb;
     }
   }
@@ -141,15 +158,16 @@ __device__ __forceinline__ void rotate_scaled(float (&own)[8], const float (&par
 template <int D, bool INTER, int NI, bool GUARD>
 __device__ __forceinline__ void q_rope(const char* src, char* dst, int64_t in_step,
                                        int64_t out_step, uint32_t in_off, uint32_t out_off,
-                                       uint32_t h_lane, uint32_t num_heads, const float* cs) {
-  constexpr int HPI = Geometry<D, INTER>::kHeadsPerInstr;
-  constexpr int LP = Geometry<D, INTER>::kLanesPerHead;
+                                       uint32_t h_lane, uint32_t num_heads, bool active,
+                                       const float* cs) {
+  using Geo = Geometry<D, INTER>;
+  constexpr int HPI = Geo::kHeadsPerInstr, LP = Geo::kLanesPerHead;
   uint4 v[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    if (GUARD) {
+    if (GUARD || Geo::kPadded) {
       v[i] = make_uint4(0, 0, 0, 0);
-      if (h_lane + HPI * i >= num_heads) continue;
+      if ((GUARD && h_lane + HPI * i >= num_heads) || (Geo::kPadded && !active)) continue;
     }
     v[i] = load16_stream(src + i * in_step + in_off);
   }
@@ -160,6 +178,7 @@ __device__ __forceinline__ void q_rope(const char* src, char* dst, int64_t in_st
     if constexpr (!INTER) unpack8(mirror16<LP>(v[i]), par);
     rotate_plain<INTER>(own, par, cs);
     if (GUARD && h_lane + HPI * i >= num_heads) continue;
+    if (Geo::kPadded && !active) continue;
     store16_stream(dst + i * out_step + out_off, pack8_bf16(own));
   }
 }
@@ -241,10 +260,10 @@ __global__ __launch_bounds__(256) void qk_rope_kernel(const QkArgs a) {
   // ---- Q ------------------------------------------------------------------------
   if (all_heads)
     q_rope<D, INTER, NI, false>(qsrc, qdst, qi_step, qo_step, qi_off, qo_off, h_lane,
-                                a.num_q_heads, cs);
+                                a.num_q_heads, role.active, cs);
   else if (h0 < a.num_q_heads)
     q_rope<D, INTER, NI, true>(qsrc, qdst, qi_step, qo_step, qi_off, qo_off, h_lane,
-                               a.num_q_heads, cs);
+                               a.num_q_heads, role.active, cs);
   if (chunk != 0) return;
 
   // ---- K (in place), optional per-head RMSNorm first ------------------------
@@ -265,7 +284,7 @@ __global__ __launch_bounds__(256) void qk_rope_kernel(const QkArgs a) {
   if constexpr (KM == KMode::Fp8PerTensor) tensor_inv = 1.0f / a.k_scales[0];
   for (uint32_t hbase = 0; hbase < cv.num_heads; hbase += HPI) {
     const uint32_t h = hbase + hl;
-    const bool valid = h < cv.num_heads;
+    const bool valid = h < cv.num_heads && (!Geo::kPadded || role.active);
     char* p = krow + EB * (int64_t)hbase * cv.head_stride + k_off;
     float own[8], par[8] = {};
     if constexpr (KM == KMode::Bf16) {
@@ -358,9 +377,12 @@ hipError_t launch_d(const QkArgs& a, bool interleaved, KMode km, uint32_t blocks
 
 }  // namespace
 
-// Q heads per wave: kQInstrPerWave instructions of 64 / (head_dim / 8) heads,
-// i.e. 4 KiB of Q per wave (8 heads of 256, 16 of 128 or 32 of 64).
-uint32_t qk_heads_per_wave(int head_dim) { return (uint32_t)kQInstrPerWave * (512u / (uint32_t)head_dim); }
+// Q heads per wave: kQInstrPerWave instructions of 64 / LP heads (LP = lanes
+// per head group), i.e. 4 KiB of Q per wave for head_dim 64, 128 and 256 (32,
+// 16 and 8 heads), 16 heads of 80 or 96.
+uint32_t qk_heads_per_wave(int head_dim) {
+  return (uint32_t)kQInstrPerWave * (uint32_t)(kWave / pow2_at_least(head_dim / 8));
+}
 
 hipError_t launch_qk_rope(const QkArgs& a, int head_dim, bool interleaved, KMode kmode,
                           hipStream_t stream) {
@@ -370,10 +392,14 @@ hipError_t launch_qk_rope(const QkArgs& a, int head_dim, bool interleaved, KMode
   // the kernel numbers waves (block * waves per block + wave) in 32 bits
   if (blocks * kWavesPerBlock > 0xffffffffull) return hipErrorInvalidValue;
   const uint32_t nb = (uint32_t)blocks;
-  if (head_dim == 256) return launch_d<256>(a, interleaved, kmode, nb, stream);
-  if (head_dim == 128) return launch_d<128>(a, interleaved, kmode, nb, stream);
-  if (head_dim == 64) return launch_d<64>(a, interleaved, kmode, nb, stream);
-  return hipErrorInvalidValue;
+  switch (head_dim) {
+    case 64: return launch_d<64>(a, interleaved, kmode, nb, stream);
+    case 80: return launch_d<80>(a, interleaved, kmode, nb, stream);
+    case 96: return launch_d<96>(a, interleaved, kmode, nb, stream);
+    case 128: return launch_d<128>(a, interleaved, kmode, nb, stream);
+    case 256: return launch_d<256>(a, interleaved, kmode, nb, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace pkv

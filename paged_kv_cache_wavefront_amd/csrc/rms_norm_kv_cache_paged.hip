@@ -15,9 +15,10 @@
 // the per-token form needs all heads in one chunk.
 //
 // One wave64 per token; lane holds 8 consecutive columns (16 bytes of bf16,
-// 8 bytes of fp8) of one head, D/8 lanes per head, and the per-head sum of
-// squares (and, for a per-token fp8 cache, the max for the fresh scale)
-// reduces with DPP inside the head's lanes.  An fp8 cache is read as
+// 8 bytes of fp8) of one head, a head occupies LP lanes (D/8 rounded up to a
+// power of two: the lanes past the head's D/8 chunks idle for D = 80, 96),
+// and the per-head sum of squares (and, for a per-token fp8 cache, the max
+// for the fresh scale) reduces with DPP inside the head's lanes.  An fp8 cache is read as
 // code * scale; a per-tensor cache re-encodes the normalised columns with its
 // scale, a per-token cache stores max|y| / 448 per head and re-encodes the
 // whole head.  K rows are read and written with non-temporal accesses (they
@@ -36,7 +37,7 @@ __device__ __forceinline__ float round_bf16(float v) { return __uint_as_float(pa
 
 template <int D, bool MBC, KMode KM, bool PER_HEAD>
 __global__ __launch_bounds__(256) void kv_norm_kernel(const KvNormArgs a) {
-  constexpr int LP = D / 8, HPI = kWave / LP;
+  constexpr int NC = D / 8, LP = pow2_at_least(NC), HPI = kWave / LP;
   constexpr int64_t EB = KM == KMode::Bf16 ? 2 : 1;
   // a per-token fp8 head shares one scale: the whole head is re-encoded
   constexpr bool kWholeHead = KM == KMode::Fp8PerToken;
@@ -45,8 +46,9 @@ __global__ __launch_bounds__(256) void kv_norm_kernel(const KvNormArgs a) {
       uniform(blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave));
   if (t >= a.total_tokens) return;
   const int m = lane % LP;
+  const bool active = m < NC;  // always true unless D/8 is not a power of two
   const uint32_t hl = (uint32_t)(lane / LP);
-  const uint32_t col0 = 8 * m;
+  const uint32_t col0 = active ? 8 * m : 0;
   const uint32_t C = a.gamma_len;
 
   // gamma (+ weight_offset) of this lane's columns, loaded before the chain
@@ -73,7 +75,7 @@ __global__ __launch_bounds__(256) void kv_norm_kernel(const KvNormArgs a) {
                EB * ((int64_t)ps.page * cv.page_stride + (int64_t)ps.offset * cv.slot_stride +
                      col0);
   const int64_t slot_head0 = ((int64_t)ps.page * cv.page_size + ps.offset) * cv.num_heads;
-  const bool touches = kWholeHead || col0 < C;
+  const bool touches = active && (kWholeHead || col0 < C);
   float tensor_scale = 1.0f, tensor_inv = 1.0f;
   if constexpr (KM == KMode::Fp8PerTensor) {
     tensor_scale = a.k_scales[0];
@@ -210,7 +212,9 @@ hipError_t launch_d(const KvNormArgs& a, bool mbc, KMode km, uint32_t blocks, hi
 
 }  // namespace
 
-uint32_t kv_norm_max_heads(uint32_t head_dim) { return kMaxIter * (kWave / (head_dim / 8)); }
+uint32_t kv_norm_max_heads(uint32_t head_dim) {
+  return kMaxIter * (uint32_t)(kWave / pow2_at_least((int)head_dim / 8));
+}
 
 hipError_t launch_kv_norm(const KvNormArgs& a, bool multiply_before_cast, KMode kmode,
                           hipStream_t stream) {
@@ -222,6 +226,8 @@ hipError_t launch_kv_norm(const KvNormArgs& a, bool multiply_before_cast, KMode 
   const uint32_t nb = (uint32_t)blocks;
   switch (a.head_dim) {
     case 64: return launch_d<64>(a, multiply_before_cast, kmode, nb, stream);
+    case 80: return launch_d<80>(a, multiply_before_cast, kmode, nb, stream);
+    case 96: return launch_d<96>(a, multiply_before_cast, kmode, nb, stream);
     case 128: return launch_d<128>(a, multiply_before_cast, kmode, nb, stream);
     case 256: return launch_d<256>(a, multiply_before_cast, kmode, nb, stream);
     default: return hipErrorInvalidValue;

@@ -33,12 +33,17 @@ hipError_t launch_mla(const MlaArgs& a, MlaOut mode, int hpw, hipStream_t) {
   ++g_calls; g_mla = a; g_mla_mode = mode; g_mla_hpw = hpw;
   return hipSuccess;
 }
-uint32_t qk_heads_per_wave(int head_dim) { return 4u * (512u / (uint32_t)head_dim); }
+static uint32_t lanes_per_head(uint32_t head_dim) {
+  uint32_t p = 1;
+  while (p < head_dim / 8) p *= 2;
+  return p;
+}
+uint32_t qk_heads_per_wave(int head_dim) { return 4u * (64u / lanes_per_head((uint32_t)head_dim)); }
 hipError_t launch_qk_rope(const QkArgs& a, int head_dim, bool inter, KMode km, hipStream_t) {
   ++g_calls; g_qk = a; g_qk_dim = head_dim; g_qk_inter = inter; g_qk_mode = km;
   return hipSuccess;
 }
-uint32_t kv_norm_max_heads(uint32_t head_dim) { return 4u * (64u / (head_dim / 8u)); }
+uint32_t kv_norm_max_heads(uint32_t head_dim) { return 4u * (64u / lanes_per_head(head_dim)); }
 hipError_t launch_kv_norm(const KvNormArgs& a, bool mbc, KMode km, hipStream_t) {
   ++g_calls; g_norm = a; g_norm_mbc = mbc; g_norm_mode = km;
   return hipSuccess;
@@ -198,6 +203,15 @@ int main() {
                                 static_cast<const uint32_t*>(P(36864)), bad, 0, nullptr, 0, 1e-6f,
                                 nullptr) == PKV_ERR_SHAPE);
     EXPECT(g_calls == before);
+  }
+  // --- Q/K RoPE with 96-wide heads: 16-lane groups, 16 heads per wave
+  {
+    pkv_paged_cache c = k_cache(PKV_DTYPE_BF16, PKV_SCALE_NONE, 2, 96);
+    EXPECT(qk_rope_paged_ragged(P(16384), 40 * 96, 96, P(20480), 40 * 96, 96, 9, 40, 96,
+                                static_cast<const uint32_t*>(P(28672)), 2, &c, 1,
+                                static_cast<const float*>(P(32768)), 512, nullptr, nullptr, 1,
+                                nullptr, 0, 1e-6f, nullptr) == PKV_OK);
+    EXPECT(g_qk_dim == 96 && g_qk_inter && g_qk.chunks == 3);
   }
   // --- K-cache norm: per-token statistic, bf16 two roundings
   {

@@ -682,6 +682,14 @@ def small_qk_cases():
                              page_size=8, max_seq_len=128, theta=10000.0,
                              interleaved=False, with_position_ids=True,
                              norm_cols=200, spare_pages=2)
+    yield workloads.build_qk("qk_small_d96", 3005, [6, 0, 9], [2, 5, 0], Hq=5, Hkv=3, D=96,
+                             page_size=8, max_seq_len=128, theta=10000.0,
+                             interleaved=False, with_position_ids=False,
+                             norm_cols=72, spare_pages=2)
+    yield workloads.build_qk("qk_small_d80", 3006, [3, 11], [7, 1], Hq=4, Hkv=1, D=80,
+                             page_size=4, max_seq_len=64, theta=10000.0,
+                             interleaved=True, with_position_ids=True,
+                             norm_cols=80, spare_pages=2)
 
 
 def pin_qk_composite(orc):

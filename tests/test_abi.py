@@ -176,8 +176,12 @@ def test_qk_validation(pkv):
     assert call_qk(pkv, None) == NULL
     assert call_qk(pkv, kcache(pkv, dtype=pkv.PKV_DTYPE_FP8_E4M3FN)) == DTYPE
     assert call_qk(pkv, kcache(pkv, scale_mode=pkv.PKV_SCALE_PER_TENSOR)) == DTYPE
-    assert call_qk(pkv, kcache(pkv, head_dim=96), D=96) == UNSUP
+    assert call_qk(pkv, kcache(pkv, head_dim=72), D=72) == UNSUP
     assert call_qk(pkv, kcache(pkv, head_dim=512), D=512) == UNSUP
+    for d in (80, 96):  # heads padded to 16-lane groups
+        assert call_qk(pkv, kcache(pkv, head_dim=d, head_stride=d, slot_stride=8 * d,
+                                  page_stride=16 * 8 * d, layer_stride=8 * 16 * 8 * d),
+                       D=d, T=0) == OK
     assert call_qk(pkv, kcache(pkv, head_dim=256, head_stride=256, slot_stride=8 * 256,
                               page_stride=16 * 8 * 256, layer_stride=8 * 16 * 8 * 256),
                    D=256, T=0) == OK
@@ -218,6 +222,11 @@ def test_kv_norm_validation(pkv):
     assert call_norm(pkv, kcache(pkv, num_heads=17, slot_stride=17 * 128, page_stride=16 * 17 * 128,
                                   layer_stride=8 * 16 * 17 * 128), per_head=1, T=0) == OK
     assert call_norm(pkv, kcache(pkv, head_dim=512), gamma_len=128) == UNSUP
+    assert call_norm(pkv, kcache(pkv, head_dim=112), gamma_len=64) == UNSUP
+    d96 = dict(head_dim=96, head_stride=96, slot_stride=17 * 96, page_stride=16 * 17 * 96,
+               layer_stride=8 * 16 * 17 * 96, num_heads=17)
+    assert call_norm(pkv, kcache(pkv, **d96), gamma_len=96, per_head=0) == UNSUP  # > 16 heads
+    assert call_norm(pkv, kcache(pkv, **d96), gamma_len=96, per_head=1, T=0) == OK
     assert call_norm(pkv, kcache(pkv), gamma=None) == NULL
     assert call_norm(pkv, kcache(pkv), gamma=FAKE + 2) == ALIGN
     assert call_norm(pkv, kcache(pkv), T=0) == OK

@@ -162,30 +162,35 @@ def test_mrope_vision_batch(orc):
     run_qk(orc, case, False)
 
 
+@pytest.mark.parametrize("D", [256, 96, 80])
 @pytest.mark.parametrize("mode", ["per_tensor", "per_token"])
-def test_fp8_k_head_dim_256(orc, mode):
+def test_fp8_k_head_dim_256(orc, mode, D):
     """fp8 K cache with 256-wide heads (32 lanes per head: the rotate-half
-    partner and the per-token max cross 16-lane rows), fused K norm."""
+    partner and the per-token max cross 16-lane rows), and with 96- and
+    80-wide heads (padded 16-lane groups), fused K norm."""
     rng = workloads.make_rng(5400)
     new = rng.integers(1, 60, size=7, endpoint=True)
     prior = rng.integers(0, 80, size=7, endpoint=True)
-    case = workloads.build_qk(f"qk_fp8_d256_{mode}", 5400, new, prior, Hq=6, Hkv=3, D=256,
+    case = workloads.build_qk(f"qk_fp8_d{D}_{mode}", 5400, new, prior, Hq=6, Hkv=3, D=D,
                               page_size=16, max_seq_len=1024, theta=10000.0,
-                              interleaved=False, with_position_ids=True, norm_cols=256, rng=rng,
+                              interleaved=False, with_position_ids=True, norm_cols=D, rng=rng,
                               k_dtype="fp8", k_scale_mode=mode)
     run_qk_fp8(orc, case, True)
 
 
+@pytest.mark.parametrize("D", [256, 96, 80])
 @pytest.mark.parametrize("per_head", [True, False])
-def test_kv_norm_head_dim_256(orc, per_head):
+def test_kv_norm_head_dim_256(orc, per_head, D):
+    """In-place K norm with 256-wide heads, and with 96- and 80-wide heads
+    (padded lane groups; 8 heads fit one wave's statistic either way)."""
     rng = workloads.make_rng(5401)
     new = rng.integers(1, 40, size=6, endpoint=True)
     prior = rng.integers(0, 60, size=6, endpoint=True)
-    case = workloads.build_qk("kvnorm_d256", 5401, new, prior, Hq=2, Hkv=8, D=256, page_size=8,
+    case = workloads.build_qk(f"kvnorm_d{D}", 5401, new, prior, Hq=2, Hkv=8, D=D, page_size=8,
                               max_seq_len=256, theta=10000.0, interleaved=False,
                               with_position_ids=False, norm_cols=None, rng=rng)
-    gamma = workloads.bf16_bits(rng.uniform(0.5, 1.5, 256).astype(np.float32))
-    _say(f"[kvnorm256] T={case.T} per_head={per_head}")
+    gamma = workloads.bf16_bits(rng.uniform(0.5, 1.5, D).astype(np.float32))
+    _say(f"[kvnorm{D}] T={case.T} per_head={per_head}")
     dev = gh.QkDevice(case)
     dev.kv_norm(gh.dev_bf16(gamma), 0.0, case.T, True, per_head)
     k = gh.host_bf16(dev.k)
@@ -196,7 +201,7 @@ def test_kv_norm_head_dim_256(orc, per_head):
                                 per_head_norm=per_head)
     rows = gh.written_k_rows(case)
     assert np.array_equal(k[~rows], case.k_cache[~rows])
-    _say(f"[kvnorm256] {gh.check_bf16(k[rows], k_o[rows], 'k')}")
+    _say(f"[kvnorm{D}] {gh.check_bf16(k[rows], k_o[rows], 'k')}")
 
 
 @pytest.mark.parametrize("mode,with_norm", [("per_tensor", False), ("per_token", True)])
@@ -326,9 +331,11 @@ def test_llama_workload(orc, with_norm):
 
 
 # (case index, with K norm): the third small case has no K norm gamma; the
-# fourth has head_dim 256 (heads spanning 32 lanes)
+# fourth has head_dim 256 (heads spanning 32 lanes); the fifth and sixth have
+# head_dim 96 and 80 (padded 16-lane head groups, rotate-half and interleaved)
 @pytest.mark.parametrize("idx,with_norm", [(0, True), (0, False), (1, True), (1, False),
-                                           (2, False), (3, True), (3, False)])
+                                           (2, False), (3, True), (3, False), (4, True),
+                                           (4, False), (5, True), (5, False)])
 def test_small_cases(orc, idx, with_norm):
     case = list(oracle_pins.small_qk_cases())[idx]
     assert with_norm is False or case.gamma is not None
@@ -337,7 +344,9 @@ def test_small_cases(orc, idx, with_norm):
 
 @pytest.mark.parametrize("D,interleaved,pos_ids",
                          [(128, False, True), (128, False, False), (64, True, True),
-                          (64, False, False), (256, False, True), (256, True, False)])
+                          (64, False, False), (256, False, True), (256, True, False),
+                          (96, False, True), (96, True, False), (80, False, False),
+                          (80, True, True)])
 def test_styles_and_dims(orc, D, interleaved, pos_ids):
     rng = workloads.make_rng(5000 + D)
     new = rng.integers(1, 200, size=12, endpoint=True)

@@ -66,7 +66,7 @@ def test_mla_random(orc, seed):
 def _random_qk(rng, seed):
     B = int(rng.integers(1, 30))
     new, prior = _lengths(rng, B, 20, 200)
-    D = int(rng.choice([64, 128, 256]))
+    D = int(rng.choice([64, 80, 96, 128, 256]))
     Hq = int(rng.choice([1, 2, 5, 8, 16, 31, 32, 40]))
     Hkv = int(rng.choice([1, 2, 4, 8]))
     page = int(rng.choice([8, 16, 32]))
