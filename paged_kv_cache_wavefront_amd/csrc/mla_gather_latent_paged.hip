@@ -10,18 +10,23 @@
 // 0..rows-1 each resolve one row (request by ballot over the offsets -- once
 // for the whole group when it lies in one request --, slot, page-table entry,
 // per-token scale); a piece lane fetches its row's source address from the
-// row lane with ds_bpermute.  Loads are non-temporal (each cache byte is read
-// once) and so are the stores (the dense output is written once); every wave
-// instruction reads and writes contiguous runs (fp8 -> bf16 reads 8-byte
-// pieces so that each lane writes 16 contiguous bytes; writing 32 bytes per
-// lane as two 16-byte stores at a 32-byte lane stride measured 1.8x slower).
+// row lane with ds_bpermute.  Every lane loads 16-byte pieces; loads are
+// non-temporal (each cache byte is read once) and so are the stores (the
+// dense output is written once).  Each wave store instruction must cover a
+// contiguous run: fp8 -> bf16 turns a lane's 16 codes into 32 output bytes,
+// so the converted rows are staged in LDS (a wave-private region, no block
+// barrier) and read back as 16-byte chunks in output order.  (Writing the 32
+// bytes as two 16-byte stores at a 32-byte lane stride measured 1.8x slower;
+// 8-byte loads so that each lane stores 16 contiguous bytes, 3.5 % slower
+// than the LDS staging.)
 //
 // Rows per wave, measured on MI355X with rotating outputs over 1 022 807
 // rows of 576 elements (microseconds, 16 / 8 / 6 / 4 / 3 rows per wave):
-// fp8 -> bf16 326 / 320 / 316 / 317 / 327, fp8 -> fp8 217 / - / 202 / 206 /
-// 217; bf16 -> bf16 (8 / 6 / 4 / 3 / 2 rows) 435 / 430 / 414 / 400 / 411,
-// bf16 -> fp8 292 / 288 / 291 / 311 / 352.  Two rows or one per wave leave
-// lanes idle and cost far more (fp8 -> bf16 383 and 548).
+// fp8 -> fp8 217 / - / 202 / 206 / 217; bf16 -> bf16 (8 / 6 / 4 / 3 / 2
+// rows) 435 / 430 / 414 / 400 / 411, bf16 -> fp8 292 / 288 / 291 / 311 / 352;
+// fp8 -> bf16 staged through LDS 310 (4 rows), 305 (6), 307 (8), 313 (10),
+// against 316 for 6 rows with 8-byte loads.  Two rows or one per wave leave
+// lanes idle and cost far more.
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -33,15 +38,19 @@ constexpr uint32_t kMaxElems = 1024;  // widest row supported
 constexpr uint32_t kMlaElems = 576;   // the MLA latent row
 
 // Launch geometry of one conversion: rows per wave, input bytes per piece
-// (one lane's share of one wave instruction) and the wave instructions that
-// cover the rows of a given width.
+// (one lane's share of one load instruction), the load instructions that
+// cover the rows of a given width, and the LDS staging area of a block.
 template <bool IN_FP8, bool OUT_FP8>
 struct Shape {
   static constexpr uint32_t kRows = (!IN_FP8 && !OUT_FP8) ? 3 : 6;
-  static constexpr uint32_t kPiece = (IN_FP8 && !OUT_FP8) ? 8 : 16;
+  static constexpr uint32_t kPiece = 16;
   static constexpr uint32_t kInBytes = IN_FP8 ? 1 : 2;
+  static constexpr bool kStaged = IN_FP8 && !OUT_FP8;  // output twice the input
   static constexpr int instr(uint32_t elems) {
     return (int)((kRows * (elems * kInBytes / kPiece) + kWave - 1) / kWave);
+  }
+  static uint32_t stage_bytes(uint32_t row_bytes) {
+    return kStaged ? (uint32_t)kWavesPerBlock * kRows * 2 * row_bytes : 0u;
   }
 };
 
@@ -146,11 +155,9 @@ __global__ __launch_bounds__(256) void gather_kernel(const GatherArgs a) {
   }
 
   // ---- stage 3: copies -------------------------------------------------------------
-  // piece g = i * 64 + lane of the wave's rows: row g / ppr, piece g % ppr.  A
-  // piece is 16 input bytes, except for fp8 -> bf16 where it is 8 input bytes
-  // so that every lane stores 16 contiguous output bytes.
+  // piece g = i * 64 + lane of the wave's rows: row g / ppr, piece g % ppr
+  // (16 input bytes).
   constexpr uint32_t PIECE = G::kPiece;
-  constexpr uint32_t OUT_PIECE = IN_FP8 == OUT_FP8 ? PIECE : (IN_FP8 ? 2 * PIECE : PIECE / 2);
   const uint32_t ppr = a.row_bytes / PIECE;  // pieces per row
   const uint32_t pieces = nrows * ppr;
   const char* src_base = static_cast<const char*>(cv.layer_base);
@@ -164,42 +171,63 @@ __global__ __launch_bounds__(256) void gather_kernel(const GatherArgs a) {
     const uint32_t lo = shfl_u32((uint32_t)row_src, (int)j);
     const uint32_t hi = shfl_u32((uint32_t)(row_src >> 32), (int)j);
     v[i] = make_uint4(0, 0, 0, 0);
-    if (g < pieces && ((ok_rows >> j) & 1u)) {
-      const char* p = src_base + ((uint64_t)hi << 32 | lo) + PIECE * (g - j * ppr);
-      if constexpr (PIECE == 16) {
-        v[i] = load16_stream(p);
-      } else {
-        const u32x2_t w = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
-        v[i].x = w.x;
-        v[i].y = w.y;
-      }
-    }
+    if (g < pieces && ((ok_rows >> j) & 1u))
+      v[i] = load16_stream(src_base + ((uint64_t)hi << 32 | lo) + PIECE * (g - j * ppr));
   }
+  if constexpr (G::kStaged) {
+    // 16 codes -> 32 bytes of bf16 per piece, staged densely (row j at
+    // j * 2 * row_bytes) in this wave's LDS region, then read back and
+    // stored as 16-byte chunks in output order.
+    extern __shared__ uint4 stage[];
+    const uint32_t opr = 2 * ppr;  // 16-byte output chunks per row
+    uint4* st = stage + (threadIdx.x / kWave) * (RPW * opr);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const uint32_t g = (uint32_t)i * kWave + (uint32_t)lane;
+      const uint32_t j = g < pieces ? g / ppr : 0;
+      const uint32_t c = g - j * ppr;
+      const float scl = __uint_as_float(shfl_u32(__float_as_uint(row_scale), (int)j));
+      if (!(g < pieces && ((ok_rows >> j) & 1u))) continue;
+      float f[2][8];
+      const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x2_t lo2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[q], false);
+        const f32x2_t hi2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[q], true);
+        f[q / 2][4 * (q & 1)] = lo2[0] * scl;
+        f[q / 2][4 * (q & 1) + 1] = lo2[1] * scl;
+        f[q / 2][4 * (q & 1) + 2] = hi2[0] * scl;
+        f[q / 2][4 * (q & 1) + 3] = hi2[1] * scl;
+      }
+      st[j * opr + 2 * c] = pack8_bf16(f[0]);
+      st[j * opr + 2 * c + 1] = pack8_bf16(f[1]);
+    }
+    // a wave's LDS accesses complete in issue order: only the compiler must
+    // not move the reads above the writes
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const uint32_t chunks = nrows * opr;
+#pragma unroll
+    for (int i = 0; i < 2 * NI; ++i) {
+      const uint32_t q = (uint32_t)i * kWave + (uint32_t)lane;
+      if (q >= chunks) continue;
+      const uint32_t j = q / opr;
+      if (!((ok_rows >> j) & 1u)) continue;
+      store16_stream(out_base + (int64_t)j * a.out_row_bytes + 16 * (q - j * opr), st[q]);
+    }
+    return;
+  }
+  constexpr uint32_t OUT_PIECE = IN_FP8 == OUT_FP8 ? PIECE : PIECE / 2;
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const uint32_t g = (uint32_t)i * kWave + (uint32_t)lane;
     const uint32_t j = g < pieces ? g / ppr : 0;
     const uint32_t c = g - j * ppr;
-    float scl = 1.0f;
-    if constexpr (IN_FP8 && !OUT_FP8) scl = __uint_as_float(shfl_u32(__float_as_uint(row_scale), (int)j));
     if (!(g < pieces && ((ok_rows >> j) & 1u))) continue;
     char* dst = out_base + (int64_t)j * a.out_row_bytes + OUT_PIECE * c;
     if constexpr (IN_FP8 == OUT_FP8) {
       store16_stream(dst, v[i]);
-    } else if constexpr (IN_FP8) {
-      // 8 fp8 codes -> 8 bf16 (one 16-byte store)
-      float f[8];
-      const uint32_t w[2] = {v[i].x, v[i].y};
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const f32x2_t lo2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[q], false);
-        const f32x2_t hi2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[q], true);
-        f[4 * q] = lo2[0] * scl;
-        f[4 * q + 1] = lo2[1] * scl;
-        f[4 * q + 2] = hi2[0] * scl;
-        f[4 * q + 3] = hi2[1] * scl;
-      }
-      store16_stream(dst, pack8_bf16(f));
     } else {
       // 8 bf16 -> 8 fp8 codes (one 8-byte store)
       float f[8];
@@ -213,11 +241,12 @@ __global__ __launch_bounds__(256) void gather_kernel(const GatherArgs a) {
 
 template <bool IN_FP8, bool OUT_FP8, int NI>
 hipError_t launch_ni(const GatherArgs& a, bool per_token, uint32_t blocks, hipStream_t stream) {
+  const uint32_t lds = Shape<IN_FP8, OUT_FP8>::stage_bytes(a.row_bytes);
   if (per_token)
-    hipLaunchKernelGGL((gather_kernel<IN_FP8, OUT_FP8, true, NI>), dim3(blocks), dim3(256), 0,
+    hipLaunchKernelGGL((gather_kernel<IN_FP8, OUT_FP8, true, NI>), dim3(blocks), dim3(256), lds,
                        stream, a);
   else
-    hipLaunchKernelGGL((gather_kernel<IN_FP8, OUT_FP8, false, NI>), dim3(blocks), dim3(256), 0,
+    hipLaunchKernelGGL((gather_kernel<IN_FP8, OUT_FP8, false, NI>), dim3(blocks), dim3(256), lds,
                        stream, a);
   return hipGetLastError();
 }
