@@ -1,7 +1,8 @@
 """The entry points inside a captured HIP graph (torch.cuda.CUDAGraph): every
 replay, with eager work and synchronisations between replays, must reproduce
 the eager result bit for bit.  The MLA call is out of place, so replays are
-idempotent; the in-place K paths are replayed on a fresh copy of K each time."""
+idempotent; the in-place K paths and the in-place MLA form are replayed on a
+fresh copy of their cache each time."""
 import numpy as np
 import pytest
 import torch
@@ -91,6 +92,39 @@ def test_kv_norm_graph_replays():
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(gh.host_bf16(dev.k), want), f"replay {rep}: k"
+        del junk
+
+
+def test_mla_inplace_graph_replays():
+    """The in-place MLA form inside a graph: the latent rows are placed again
+    before every replay (the step overwrites them)."""
+    import oracle_pins
+    case = list(oracle_pins.small_mla_inplace_cases())[1]
+    eager = gh.MlaDevice(case)
+    eager.place_rows()
+    eager.run_inplace()
+    want = eager.results()
+    dev = gh.MlaDevice(case)
+    placed = gh.dev_bf16(oracle_pins.place_latent_rows(case))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        dev.cache.copy_(placed)
+        dev.run_inplace()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dev.run_inplace()
+    for rep in range(3):
+        dev.cache.copy_(placed)                 # rewritten in place: put the rows back
+        dev.q_out.zero_()
+        junk = torch.ones(1 << 20, device="cuda") * rep
+        torch.cuda.synchronize()
+        g.replay()
+        got = dev.results()
+        assert np.array_equal(got[0], want[0]), f"replay {rep}: q differs"
+        assert np.array_equal(got[1], want[1]), f"replay {rep}: cache differs"
         del junk
 
 
