@@ -19,6 +19,10 @@ prefill batch in place on a bf16 latent cache (mla_rope_rmsnorm_inplace), the
 Llama-shaped paged-ragged Q/K RoPE with fused per-head K norm, the in-place
 K-cache RMSNorm and the paged latent gather.
 
+With the CPU baseline (the oracle on the same inputs, single-threaded and on
+N host threads) the line also carries ``parity``: one launch of the timed
+entry point compared with the oracle's outputs of that run.
+
 ``--calibrate-copy`` runs a plain elementwise copy of known size instead (the
 reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings).
 """
@@ -475,7 +479,32 @@ def cpu_baseline(case, budget_s=10.0):
                       "sample": f"whole workload x {runs} run(s), {par_s:.1f} s, "
                                 f"{len(chunks)} threads on token-balanced slices",
                       "same_bits_as_single_thread": same}
-    return out
+    return out, (q_out, cache)
+
+
+def parity_stats(case, oracle_out):
+    """One launch of the timed entry point on fresh device copies of the
+    workload, compared with the oracle's outputs from the CPU baseline (same
+    inputs): q within bf16 steps, cache codes within fp8 steps on the new
+    rows, every other cache byte unchanged.  Reported, not asserted (the
+    tests hold the bars)."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import gpu_helpers as gh
+    dev = gh.MlaDevice(case)
+    dev.run()
+    q, cache, _, skipped = dev.results()
+    q_o, cache_o = oracle_out
+    rows = gh.written_rows(case)
+    dq = gh.bf16_ulp_diff(q, q_o)
+    dc = gh.fp8_ulp_diff(cache[rows], cache_o[rows]) if cache.dtype == np.uint8 else \
+        gh.bf16_ulp_diff(cache[rows], cache_o[rows])
+    return {"q_max_ulp": int(dq.max(initial=0)),
+            "q_diff_frac": float((dq != 0).sum() / max(dq.size, 1)),
+            "cache_max_step": int(dc.max(initial=0)),
+            "cache_diff_frac": float((dc != 0).sum() / max(dc.size, 1)),
+            "untouched_ok": bool(np.array_equal(cache[~rows], case.cache[~rows])),
+            "skipped_tokens": int(skipped),
+            "against": "the oracle's outputs of the cpu_baseline run"}
 
 
 def calibrate_copy(steps, warmup, mib=1024):
@@ -546,10 +575,12 @@ def main():
     gbps = main_sum["effective_GBps"]
     siblings = None if args.no_siblings else measure_siblings(
         args.workload, max(20, args.steps // 2), args.warmup)
-    cpu = None
+    cpu = parity = None
     if not args.no_cpu_baseline and args.workload.startswith("mla_"):
         log("[bench] cpu baseline (oracle)")
-        cpu = cpu_baseline(case)
+        cpu, oracle_out = cpu_baseline(case)
+        if args.workload != "mla_prefill_inplace":
+            parity = parity_stats(case, oracle_out)
     copy_ref = measured_copy(args.steps, args.warmup)
     traffic = profiled_traffic(args.workload)
     is_mla = args.workload.startswith("mla_")
@@ -597,6 +628,7 @@ def main():
                      "frac": round(gbps / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "algorithmic_bytes": r["bytes"]},
         "cpu_baseline": cpu,
+        "parity": parity,
         "siblings": siblings,
     }
     print(json.dumps(line), flush=True)
