@@ -4,7 +4,10 @@
  * through include/pkv.h on a small ragged batch (fp8 cache, per-tensor scale),
  * runs the CPU oracle on the same host arrays and compares: q within 1 bf16
  * ulp, cache codes within 1 step, at most 3 values of each differing, every
- * byte outside the new rows unchanged.  Exit status 0 = pass.
+ * byte outside the new rows unchanged.  Then the same batch through
+ * mla_rope_rmsnorm_inplace on a bf16 cache that holds the latent rows at the
+ * new tokens' slots, against the oracle's in-place form.  Exit status 0 =
+ * pass.
  */
 #include <hip/hip_runtime_api.h>
 #include <math.h>
@@ -25,6 +28,13 @@ int oracle_mla_rope_rmsnorm_quant(void* q_out, int q_out_f32, const uint16_t* q_
                                   int64_t Dn, void* cache, int cache_type, int64_t num_layers,
                                   int64_t num_pages, int64_t page_size, int64_t layer_idx,
                                   int scale_mode, float tensor_scale, float* token_scales);
+int oracle_mla_rope_rmsnorm_inplace(void* q_out, int q_out_f32, const uint16_t* q_in,
+                                    const uint32_t* row_offsets, const uint32_t* cache_lengths,
+                                    int64_t B, const uint32_t* page_table, int64_t pt_stride,
+                                    const float* freqs, int64_t max_seq_len,
+                                    const uint16_t* gamma, float epsilon, int64_t H, int64_t R,
+                                    int64_t Dn, uint16_t* cache, int64_t num_layers,
+                                    int64_t num_pages, int64_t page_size, int64_t layer_idx);
 
 enum { B = 3, H = 5, R = 64, DN = 512, W = DN + R, S = 8, L = 2, LAYER = 1, MAXSEQ = 32 };
 
@@ -165,7 +175,60 @@ int main(void) {
   }
   printf("c-abi mla: T=%d q: %ld differ (max %ld ulp); cache: %ld differ (max %ld); "
          "oracle changed %ld bytes\n", T, q_diff, q_max, c_diff, c_max, rows_changed);
-  const int ok = q_max <= 1 && q_diff <= 3 && c_max <= 1 && c_diff <= 3 && rows_changed > 0;
+  int ok = q_max <= 1 && q_diff <= 3 && c_max <= 1 && c_diff <= 3 && rows_changed > 0;
+
+  /* in place: a bf16 cache holding each new token's latent row at its slot */
+  const size_t n16 = (size_t)L * P * S * W;
+  uint16_t* cache16 = malloc(sizeof(uint16_t) * n16);
+  for (size_t i = 0; i < n16; ++i) cache16[i] = rand_bf16();
+  for (int b = 0; b < B; ++b)
+    for (uint32_t j = 0; j < new_len[b]; ++j) {
+      const uint32_t slot = prior[b] + j;
+      const uint32_t page = page_table[b * PT_STRIDE + slot / S];
+      memcpy(cache16 + (((size_t)LAYER * P + page) * S + slot % S) * W,
+             latent + (size_t)(offsets[b] + j) * W, sizeof(uint16_t) * W);
+    }
+  void* d_cache16;
+  CHECK(hipMalloc(&d_cache16, sizeof(uint16_t) * n16));
+  CHECK(hipMemcpy(d_cache16, cache16, sizeof(uint16_t) * n16, hipMemcpyHostToDevice));
+  c.data = d_cache16;
+  c.dtype = PKV_DTYPE_BF16;
+  c.scale_mode = PKV_SCALE_NONE;
+  c.scales = NULL;
+  const int st2 = mla_rope_rmsnorm_inplace(d_qo, (int64_t)H * R, R, d_q, (int64_t)H * R, R, d_off,
+                                           B, (uint32_t)T, H, R, DN, d_freqs, MAXSEQ, d_gamma, eps,
+                                           &c, LAYER, PKV_DTYPE_BF16, NULL);
+  if (st2 != PKV_OK) {
+    fprintf(stderr, "mla_rope_rmsnorm_inplace: %s\n", pkv_status_string(st2));
+    return 1;
+  }
+  CHECK(hipDeviceSynchronize());
+  uint16_t* cache16_gpu = malloc(sizeof(uint16_t) * n16);
+  CHECK(hipMemcpy(q_gpu, d_qo, sizeof(uint16_t) * T * H * R, hipMemcpyDeviceToHost));
+  CHECK(hipMemcpy(cache16_gpu, d_cache16, sizeof(uint16_t) * n16, hipMemcpyDeviceToHost));
+  uint16_t* cache16_ref = malloc(sizeof(uint16_t) * n16);
+  memcpy(cache16_ref, cache16, sizeof(uint16_t) * n16);
+  if (oracle_mla_rope_rmsnorm_inplace(q_ref, 0, q, offsets, prior, B, page_table, PT_STRIDE, freqs,
+                                      MAXSEQ, gamma, eps, H, R, DN, cache16_ref, L, P, S,
+                                      LAYER) != 0) {
+    fprintf(stderr, "oracle (in place): precondition failed\n");
+    return 1;
+  }
+  long q2_diff = 0, q2_max = 0, r_diff = 0, r_max = 0, changed = 0;
+  for (int i = 0; i < T * H * R; ++i) {
+    const long d = labs(ord16(q_gpu[i]) - ord16(q_ref[i]));
+    q2_diff += d != 0;
+    if (d > q2_max) q2_max = d;
+  }
+  for (size_t i = 0; i < n16; ++i) {
+    const long d = labs(ord16(cache16_gpu[i]) - ord16(cache16_ref[i]));
+    r_diff += d != 0;
+    if (d > r_max) r_max = d;
+    changed += cache16_ref[i] != cache16[i];
+  }
+  printf("c-abi mla in place: q: %ld differ (max %ld ulp); cache: %ld differ (max %ld ulp); "
+         "oracle changed %ld values\n", q2_diff, q2_max, r_diff, r_max, changed);
+  ok = ok && q2_max <= 1 && q2_diff <= 3 && r_max <= 1 && r_diff <= 3 && changed > 0;
   puts(ok ? "PASS" : "FAIL");
   return ok ? 0 : 1;
 }
