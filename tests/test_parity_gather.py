@@ -146,25 +146,40 @@ def test_mixed_per_token(orc):
     run_gather(orc, case, kvo, out_fp8=True)
 
 
-def test_bad_page_rows_skipped(orc):
+@pytest.mark.parametrize("out_bf16", [False, True])
+def test_bad_page_rows_skipped(orc, out_bf16):
     """A row whose page id lies past the pool is skipped (not written) and
-    counted; the other rows are exact."""
+    counted; the other rows are exact (fp8 copy) or the oracle's (fp8 -> bf16,
+    the LDS-staged path, where a skipped row is neither staged nor stored)."""
     import paged_kv_cache_wavefront_amd as pkv
     case, kvo = oracle_pins.gather_case("fp8_tensor")
+    good_table = case.page_table.copy()
     case.page_table[2, 0] = case.meta["num_pages"] + 1     # request 2: its first page
     cache = gh.dev_u8(case.cache)
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     desc = pkv.paged_cache(cache, None, gh.dev_u32(case.page_table), pkv.PKV_SCALE_PER_TENSOR,
                            gh.dev_f32(np.array([case.tensor_scale], np.float32)), err)
     rows = int(kvo[-1])
-    out = torch.full((rows, 576), 0x55, dtype=torch.uint8, device="cuda")
+    if out_bf16:
+        out = torch.full((rows, 576), 0x5555, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    else:
+        out = torch.full((rows, 576), 0x55, dtype=torch.uint8, device="cuda")
     pkv.mla_gather_latent_paged(out, gh.dev_u32(kvo), desc, case.layer_idx)
     torch.cuda.synchronize()
-    got = gh.host_u8(out)
+    got = gh.host_bf16(out) if out_bf16 else gh.host_u8(out)
     r2 = range(int(kvo[2]), int(kvo[3]))
     bad = [r for r in r2 if (r - int(kvo[2])) < case.meta["page_size"]]
     assert int(err.item()) == len(bad)
-    assert np.all(got[bad] == 0x55)
+    assert np.all(got[bad] == (0x5555 if out_bf16 else 0x55))
+    want = np.zeros_like(got)
+    orc.mla_gather_latent_paged(want, kvo, good_table, case.cache, case.layer_idx, "per_tensor",
+                                np.array([case.tensor_scale], np.float32))
+    keep = np.ones(rows, bool)
+    keep[bad] = False
+    if out_bf16:
+        assert int(gh.bf16_ulp_diff(got[keep], want[keep]).max()) <= 1
+    else:
+        assert np.array_equal(got[keep], want[keep])
 
 
 @pytest.mark.parametrize("W", [80, 208, 1024])
