@@ -23,9 +23,9 @@ the Q/K RoPE page, Parameters; the K-cache RMSNorm page, Parameters):
 Exact ties are real and frequent here: a rotation of bf16 inputs by fp32
 angles has at most about 33 significant bits, so about one value in 2^8
 sits exactly on an fp32 midpoint; at 120 digits those rotations, products
-and their sums are computed without error, and such a tie is judged by the
+and their sums are computed without error, and such a tie is checked by the
 ties-to-even rule.  A value that lies within 2^-40 (relative) of a rounding
-boundary without being on it is not judged: the oracle computes in
+boundary without being on it is not checked: the oracle computes in
 binary64, and its own error (well under 2^-43 relative for these chains of
 at most a few hundred operations) may decide such a case.  The skipped count
 is bounded, so the pins cannot pass by skipping.
@@ -122,18 +122,18 @@ def round_fp8(v: Decimal):
 
 
 class Tally:
-    """Counts judged values (and among them exact ties) and skipped ones;
+    """Counts checked values (and among them exact ties) and skipped ones;
     collects the mismatches."""
 
     def __init__(self, what: str):
-        self.what, self.judged, self.ties, self.skipped, self.bad = what, 0, 0, 0, []
+        self.what, self.checked, self.ties, self.skipped, self.bad = what, 0, 0, 0, []
 
     def check(self, got: int, want_kind, where):
         want, kind = want_kind
         if kind == NEAR_TIE:
             self.skipped += 1
             return
-        self.judged += 1
+        self.checked += 1
         self.ties += kind == TIE
         if int(got) != want and len(self.bad) < 8:
             self.bad.append((where, hex(int(got)), hex(want)))
@@ -143,12 +143,12 @@ class Tally:
     def done(self, min_ties: int = 0):
         assert not self.bad, f"{self.what}: {len(self.bad)} values differ from the exact " \
                              f"rounding; first {[b for b in self.bad if b][:4]}"
-        total = self.judged + self.skipped
-        assert self.judged > 0, f"{self.what}: nothing judged"
+        total = self.checked + self.skipped
+        assert self.checked > 0, f"{self.what}: nothing checked"
         assert self.skipped <= max(2, MAX_SKIP_FRAC * total), \
             f"{self.what}: {self.skipped} of {total} values skipped as near ties"
         assert self.ties >= min_ties, f"{self.what}: {self.ties} exact ties, want {min_ties}"
-        print(f"[exact] {self.what}: {self.judged} judged ({self.ties} exact ties), "
+        print(f"[exact] {self.what}: {self.checked} checked ({self.ties} exact ties), "
               f"{self.skipped} skipped", flush=True)
 
 
