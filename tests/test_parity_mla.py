@@ -276,3 +276,36 @@ def test_inplace_skipped_tokens(orc):
             assert np.array_equal(cache[L, page, off], placed[L, page, off]), "skipped row changed"
         else:
             gh.check_bf16(cache[L, page, off], cache_o[L, page, off], "row")
+
+
+def test_zero_rows_per_token(orc):
+    """Per-token scale on degenerate latent rows: all +0, all -0, a mix of
+    signed zeros, only the rope tail non-zero, only the non-rope part
+    non-zero.  A zero row stores scale 0 and zero codes (its normalised part
+    keeps each value's sign); every row as the oracle."""
+    case = workloads.build_mla("mla_zero_rows", 4201, [6, 5], [0, 9], H=4, page_size=8,
+                               max_seq_len=32, spare_pages=2, scale_mode="per_token")
+    lat = case.latent
+    lat[0] = 0x0000
+    lat[1] = 0x8000
+    lat[2, ::2], lat[2, 1::2] = 0x0000, 0x8000
+    lat[3, : case.Dn] = 0x0000                 # rope tail only
+    lat[4, case.Dn:] = 0x8000                  # non-rope part only
+    dev = gh.MlaDevice(case)
+    dev.run()
+    gpu = dev.results()
+    assert gpu[3] == 0
+    stats = gh.compare_mla(case, gpu, gh.oracle_mla(orc, case))
+    _say(f"[mla-zero] {stats}")
+    owners = oracle_pins.slot_owners(case.row_offsets, case.cache_lengths, case.page_table,
+                                     case.meta["page_size"])
+    L = case.layer_idx
+    for (page, off), (t, slot) in owners.items():
+        if t < 3:
+            assert gpu[2][L, page, off, 0] == 0.0, f"token {t}: scale of a zero row"
+            codes = gpu[1][L, page, off, 0]
+            assert np.all((codes & 0x7F) == 0), f"token {t}: non-zero code"
+            # the normalised part keeps each zero's sign (x * r * gamma); the
+            # rotated tail's zero signs follow IEEE sums of signed zeros
+            assert np.array_equal(codes[: case.Dn] >> 7, (lat[t, : case.Dn] >> 15).astype(np.uint8)), \
+                f"token {t}: zero signs"
