@@ -309,3 +309,27 @@ def test_zero_rows_per_token(orc):
             # rotated tail's zero signs follow IEEE sums of signed zeros
             assert np.array_equal(codes[: case.Dn] >> 7, (lat[t, : case.Dn] >> 15).astype(np.uint8)), \
                 f"token {t}: zero signs"
+
+
+def test_launch_shape_invariance():
+    """The same tokens under different wave mappings give identical bits: a
+    32-head launch (32 heads per wave) against two 16-head launches over its
+    head halves (16 heads per wave, one wave per token), and a 40-head launch
+    (masked lanes) against the same 32 + 8 heads launched apart."""
+    import paged_kv_cache_wavefront_amd as pkv
+    base = workloads.build_mla("mla_shape", 4301, [37, 0, 120, 5], [3, 9, 0, 200], H=40,
+                               page_size=16, max_seq_len=512, spare_pages=3,
+                               scale_mode="per_token")
+    full = gh.MlaDevice(base)
+    full.run()
+    q_full, cache_full, ts_full, _ = full.results()
+    for lo, hi in ((0, 16), (16, 32), (32, 40), (0, 32)):
+        dev = gh.MlaDevice(base)
+        q_in = dev.q_in[:, lo:hi]
+        q_out = dev.q_out[:, lo:hi]
+        pkv.mla_rope_rmsnorm_quant(q_out, q_in, dev.latent, dev.offsets, dev.freqs, dev.gamma,
+                                   base.epsilon, dev.desc, base.layer_idx)
+        q, cache, ts, _ = dev.results()
+        assert np.array_equal(q[:, lo:hi], q_full[:, lo:hi]), f"heads {lo}:{hi}"
+        assert np.array_equal(cache, cache_full), f"cache with heads {lo}:{hi}"
+        assert np.array_equal(ts.view(np.uint32), ts_full.view(np.uint32))
