@@ -184,8 +184,6 @@ def profiled_traffic(name: str):
     return float(m_b.group(1)) if m_h.group(1) == kernel_source_hash(name) else None
 
 
-# -- workloads -------------------------------------------------------------------------
-
 def time_cold(fn, samples: int = 20, flush_mib: int = 512):
     """Per-launch durations with cold caches: before each sampled launch, a
     reduction reads flush_mib MiB of other data (more than the 256 MiB
@@ -207,6 +205,8 @@ def time_cold(fn, samples: int = 20, flush_mib: int = 512):
     del junk
     return np.array([a.elapsed_time(b) for a, b in pairs]) * 1e-3
 
+
+# -- workloads -------------------------------------------------------------------------
 
 def measure(fn, tokens, nbytes, steps, warmup, graph=True):
     wall, avg, durs = time_launches(fn, steps, warmup)
