@@ -3,7 +3,8 @@
 // block instead of launching, and the whole binary is built with AddressSanitizer
 // and UndefinedBehaviorSanitizer.  It checks that valid calls reach a launcher
 // with the right derived fields (layer base, scale blocks, chunk counts, flags),
-// that refused calls reach none, and that zero-token calls launch nothing.
+// that refused calls reach none, and that zero-token calls launch nothing; then
+// a seeded randomised sweep of 20 000 calls over all entry points.
 #include <cstdio>
 #include <cstring>
 
@@ -128,6 +129,143 @@ static int mla_inplace(const pkv_paged_cache* c, uint32_t T, uint32_t H, uint32_
                                   layer, PKV_DTYPE_BF16, nullptr);
 }
 
+// Randomised sweep of the validation: descriptors and arguments drawn from
+// mostly-valid values with one or more fields perturbed (zero, odd, huge,
+// misaligned, NULL, out of range).  Every call must return a status code of
+// the enum; a stand-in launcher may be reached only with PKV_OK and tokens
+// (or rows) to process, and every reached launch must see a layer base inside
+// the pool it was given.  AddressSanitizer / UBSan watch the whole sweep.
+static uint64_t fz = 0x2545F4914F6CDD1Dull;
+static uint32_t frand() {
+  fz ^= fz << 13; fz ^= fz >> 7; fz ^= fz << 17;
+  return (uint32_t)(fz >> 16);
+}
+static bool coin(uint32_t one_in) { return frand() % one_in == 0; }
+static uint32_t pick_u32(const uint32_t* v, int n) { return v[frand() % (uint32_t)n]; }
+
+static void perturb(pkv_paged_cache* c) {
+  switch (frand() % 12) {
+    case 0: c->data = coin(2) ? nullptr : static_cast<char*>(c->data) + 8; break;
+    case 1: c->dtype = (int32_t)(frand() % 4); break;
+    case 2: c->num_layers = frand() % 3; break;
+    case 3: c->num_pages = coin(2) ? 0u : frand(); break;
+    case 4: c->page_size = frand() % 3; break;
+    case 5: c->num_heads = frand() % 40; break;
+    case 6: c->head_dim = frand() % 1200; break;
+    case 7: c->slot_stride += (int64_t)(frand() % 16) - 8; break;
+    case 8: c->head_stride = coin(2) ? -16 : (int64_t)frand(); break;
+    case 9: c->page_table = nullptr; break;
+    case 10: c->scale_mode = (int32_t)(frand() % 4); break;
+    case 11: c->scales = nullptr; break;
+  }
+}
+
+static void fuzz(int iters) {
+  using namespace pkv;
+  const uint32_t dims[] = {64, 80, 96, 128, 256, 72, 512};
+  int launched = 0, refused = 0;
+  for (int it = 0; it < iters; ++it) {
+    const int entry = (int)(frand() % 5);
+    pkv_paged_cache c;
+    if (entry <= 1 || entry == 4) {
+      c = latent_cache(coin(2) ? PKV_DTYPE_BF16 : PKV_DTYPE_FP8_E4M3FN,
+                       (int32_t)(frand() % 3), 1 + frand() % 16);
+      if (entry == 1 || c.dtype == PKV_DTYPE_BF16) c.scale_mode = PKV_SCALE_NONE;
+    } else {
+      const uint32_t d = pick_u32(dims, 7);
+      c = k_cache(coin(3) ? PKV_DTYPE_FP8_E4M3FN : PKV_DTYPE_BF16, PKV_SCALE_NONE,
+                  1 + frand() % 20, d);
+      if (c.dtype == PKV_DTYPE_FP8_E4M3FN) c.scale_mode = coin(2) ? PKV_SCALE_PER_TENSOR
+                                                                  : PKV_SCALE_PER_TOKEN;
+      c.scales = static_cast<float*>(P(12288));
+    }
+    const int nbad = coin(3) ? 0 : 1 + (int)(frand() % 3);
+    for (int k = 0; k < nbad; ++k) perturb(&c);
+    const pkv_paged_cache* cp = coin(50) ? nullptr : &c;
+    const uint32_t T = coin(4) ? 0u : 1 + frand() % 5000;
+    const uint32_t B = coin(20) ? 0u : 1 + frand() % 600;
+    const uint32_t layer = frand() % 4;
+    void* q = coin(30) ? nullptr : (coin(20) ? P(16384 + 4) : P(16384));
+    const uint32_t H = frand() % 200;
+    const int before = g_calls;
+    int st = -1;
+    switch (entry) {
+      case 0:
+      case 1: {
+        const int64_t ts = (int64_t)H * 64 + (coin(10) ? 4 : 0);
+        const int32_t qdt = coin(10) ? (int32_t)(frand() % 4) : PKV_DTYPE_BF16;
+        if (entry == 0)
+          st = mla_rope_rmsnorm_quant(P(20480), ts, 64, q, ts, 64, coin(20) ? nullptr : P(24576),
+                                      coin(10) ? 580 : 576, static_cast<const uint32_t*>(P(28672)),
+                                      B, T, H, coin(10) ? 32 : 64, coin(10) ? 256 : 512,
+                                      static_cast<const float*>(P(32768)), 1 + frand() % 9000,
+                                      coin(30) ? nullptr : P(36864), 1e-6f, cp, layer, qdt,
+                                      nullptr);
+        else
+          st = mla_rope_rmsnorm_inplace(P(20480), ts, 64, q, ts, 64,
+                                        static_cast<const uint32_t*>(P(28672)), B, T, H,
+                                        coin(10) ? 32 : 64, 512,
+                                        static_cast<const float*>(P(32768)), 1 + frand() % 9000,
+                                        coin(30) ? nullptr : P(36864), 1e-6f, cp, layer, qdt,
+                                        nullptr);
+        break;
+      }
+      case 2: {
+        const uint32_t D = cp ? cp->head_dim : 128;
+        const uint32_t sec_ok[3] = {D / 4, D / 8, D / 2 - D / 4 - D / 8};
+        const uint32_t sec_bad[3] = {1, 2, 3};
+        const uint32_t* sec = coin(4) ? (coin(2) ? sec_ok : sec_bad) : nullptr;
+        const uint32_t cols = coin(3) ? 0u : frand() % (D + 2);
+        st = qk_rope_paged_ragged(P(20480), (int64_t)H * D, D, q, (int64_t)H * D, D, T, H, D,
+                                  static_cast<const uint32_t*>(P(28672)), B, cp, layer,
+                                  static_cast<const float*>(P(32768)), 4096,
+                                  coin(2) ? static_cast<const uint32_t*>(P(40960)) : nullptr, sec,
+                                  (int)(frand() % 2), cols ? P(45056) : nullptr, cols, 1e-6f,
+                                  nullptr);
+        break;
+      }
+      case 3: {
+        const uint32_t D = cp ? cp->head_dim : 128;
+        st = rms_norm_kv_cache_paged(cp, layer, coin(20) ? nullptr : P(45056),
+                                     coin(10) ? 0u : 1 + frand() % (D + 1), 1e-6f, 0.25f, T,
+                                     static_cast<const uint32_t*>(P(28672)), B,
+                                     (int)(frand() % 2), (int)(frand() % 2), nullptr);
+        break;
+      }
+      case 4: {
+        const int32_t odt = coin(2) ? PKV_DTYPE_BF16 : PKV_DTYPE_FP8_E4M3FN;
+        const uint32_t W = cp ? cp->head_dim : 576;
+        st = mla_gather_latent_paged(P(49152), odt, (int64_t)W + (coin(10) ? 8 : 0),
+                                     coin(5) ? nullptr : static_cast<float*>(P(53248)),
+                                     coin(5) ? nullptr : static_cast<const float*>(P(57344)),
+                                     static_cast<const uint32_t*>(P(28672)), B, T, cp, layer,
+                                     nullptr);
+        break;
+      }
+    }
+    EXPECT(st >= PKV_OK && st <= PKV_ERR_LAUNCH);
+    const bool reached = g_calls != before;
+    if (reached) {
+      ++launched;
+      EXPECT(st == PKV_OK && T > 0 && cp != nullptr);
+      const char* base = nullptr;
+      switch (entry) {
+        case 0: case 1: base = static_cast<const char*>(g_mla.cache.layer_base); break;
+        case 2: base = static_cast<const char*>(g_qk.cache.layer_base); break;
+        case 3: base = static_cast<const char*>(g_norm.cache.layer_base); break;
+        case 4: base = static_cast<const char*>(g_gather.cache.layer_base); break;
+      }
+      const int64_t eb = cp->dtype == PKV_DTYPE_BF16 ? 2 : 1;
+      EXPECT(base == static_cast<const char*>(cp->data) + (int64_t)layer * cp->layer_stride * eb);
+      EXPECT(layer < cp->num_layers);
+    } else {
+      refused += st != PKV_OK;
+    }
+  }
+  std::printf("host api sweep: %d calls, %d reached a launcher, %d refused\n", iters, launched,
+              refused);
+}
+
 int main() {
   using namespace pkv;
   // --- MLA: per-token fp8, 40 heads, layer 1 of 2
@@ -241,6 +379,7 @@ int main() {
     EXPECT(g_gather.cache_scale == c.scales + 7 * 16);
     EXPECT(g_gather.total_rows == 33 && g_gather.batch == 2);
   }
+  fuzz(20000);
   std::printf("host api: %d of %d checks passed\n", checks - failures, checks);
   return failures == 0 ? 0 : 1;
 }
