@@ -251,26 +251,35 @@ def written_rows(case) -> np.ndarray:
     return mask
 
 
-def compare_mla(case, gpu, orc_res) -> dict:
+def compare_mla(case, gpu, orc_res, small_case_floor: int = 0) -> dict:
+    """GPU results against the oracle's under the parity bars.  With
+    small_case_floor = k, the fraction bars allow at least k differing values
+    (for cases of a few hundred values, where one near-tie is already more
+    than 0.1 %); the per-value bars (1 step, fp8 near-ties only) still hold."""
     q_g, cache_g, ts_g, _ = gpu
     q_o, cache_o, ts_o, pre = orc_res
+
+    def cap(frac, n):
+        return max(frac, small_case_floor / max(n, 1))
     if q_o.dtype == np.float32:
         d = f32_ulp_diff(q_g, q_o)
         stats = {"q": dict(max_ulp=int(d.max(initial=0)),
                            diff_frac=float((d != 0).sum() / max(d.size, 1)), n=d.size)}
         assert stats["q"]["max_ulp"] <= F32_MAX_ULP, f"fp32 q_rope_output: {stats}"
     else:
-        stats = {"q": check_bf16(q_g, q_o, "q_rope_output")}
+        stats = {"q": check_bf16(q_g, q_o, "q_rope_output",
+                                 max_frac=cap(BF16_MAX_DIFF_FRAC, q_g.size))}
     rows = written_rows(case)
     # untouched rows: bit-exact against the starting pool (and the oracle's)
     assert np.array_equal(cache_g[~rows], case.cache[~rows]), "cache bytes outside new rows changed"
     assert np.array_equal(cache_o[~rows], case.cache[~rows]), "oracle changed bytes outside new rows"
     wg, wo = cache_g[rows], cache_o[rows]
     if case.cache.dtype == np.uint16:
-        stats["cache"] = check_bf16(wg, wo, "bf16 cache rows")
+        stats["cache"] = check_bf16(wg, wo, "bf16 cache rows",
+                                    max_frac=cap(BF16_MAX_DIFF_FRAC, wg.size))
     else:
         stats["cache"] = check_fp8(wg, wo, pre[rows], "fp8 cache rows",
-                                   max_frac=FP8_MAX_DIFF_FRAC)
+                                   max_frac=cap(FP8_MAX_DIFF_FRAC, wg.size))
     if ts_o is not None:
         keep = ~rows
         assert np.array_equal(ts_g[keep].view(np.uint32), case.token_scales[keep].view(np.uint32)), \
