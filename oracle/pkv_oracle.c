@@ -9,8 +9,13 @@
  * Style: plain scalar loops, every intermediate in IEEE binary64 (built with
  * -ffp-contract=off, no fast-math), and exactly one rounding into each output
  * type.  A bf16 value times an fp32 value is exact in binary64 (8 + 24
- * significant bits), so every output below is the correctly rounded value of
- * the plain definition, apart from measure-zero ties.
+ * significant bits), and so is the sum of two such products unless their
+ * magnitudes lie more than 2^21 apart: a rotated value is then the correctly
+ * rounded value of the plain definition, exact ties included.  Values that
+ * pass through the square root and divisions of the norm carry a binary64
+ * error well under 2^-43 relative, so they are correctly rounded except within
+ * that distance of a rounding boundary.  (tests/exact_pins.py checks both
+ * statements against 120-digit decimal arithmetic.)
  *
  * Sources (Modular MAX / Mojo API reference pages):
  *   [MLA]   "mla_fused_rope_rmsnorm_quantization" -- summary, Parameters, Args
