@@ -448,7 +448,9 @@ def cpu_baseline(case, budget_s=10.0):
         if spent >= budget_s or (time.perf_counter() - t1) * (runs + 1) > 3 * budget_s:
             break
     oracle_s = time.perf_counter() - t0
+    bytes_per_token = mla_bytes(case) / max(case.T, 1)  # the same byte model as the GPU line
     out = {"value": round(tokens / oracle_s, 1), "unit": "tokens/s", "cores": 1,
+           "GBps": round(tokens / oracle_s * bytes_per_token / 1e9, 3),
            "kind": "oracle", "cpu_model": cpu_model(),
            "sample": f"whole workload ({case.T} tokens) x {runs} run(s), "
                      f"{oracle_s:.1f} s, single thread"}
@@ -476,6 +478,7 @@ def cpu_baseline(case, budget_s=10.0):
         par_s = time.perf_counter() - t0
     same = bool(np.array_equal(q_par, q_out) and np.array_equal(cache_par, cache))
     out["threads"] = {"value": round(tokens / par_s, 1), "cores": len(chunks),
+                      "GBps": round(tokens / par_s * bytes_per_token / 1e9, 3),
                       "sample": f"whole workload x {runs} run(s), {par_s:.1f} s, "
                                 f"{len(chunks)} threads on token-balanced slices",
                       "same_bits_as_single_thread": same}
