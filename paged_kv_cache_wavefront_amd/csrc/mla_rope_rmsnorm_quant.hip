@@ -26,7 +26,9 @@
 // * The head-chunk-0 wave also owns the latent row: lane l holds non-rope
 //   values 8l..8l+7; lanes 0..7 hold the 64-value rope tail with the q
 //   mapping.  The sum of squares (and the per-token amax) reduce across the
-//   wave with DPP inside rows and readlane across rows.  The non-rope value is
+//   wave with DPP inside rows and readlane across rows; the sum of squares
+//   is reduced while the second step of the address chain is in flight.
+//   The non-rope value is
 //   formed as (x * gamma) * (r / scale): x * gamma is exact in fp32 (two 8-bit
 //   significands).  The row is converted to fp8 in registers (clamp to +-448,
 //   then hardware round-to-nearest-even) and written with 8-byte
@@ -118,6 +120,24 @@ __device__ __forceinline__ void rotate_store_q(const uint4 (&q)[NI], const float
   }
 }
 
+// RMSNorm statistic of the latent row's non-rope part (lane l holds values
+// 8l..8l+7): returns r = 1/sqrt(mean(x^2) + eps), wave-uniform, and leaves
+// x * gamma in xg (exact in fp32: two 8-bit significands).
+__device__ __forceinline__ float latent_rms(const uint4& xn, const uint4& gm, float (&xg)[8],
+                                            float epsilon) {
+  float g8[8];
+  unpack8(xn, xg);
+  unpack8(gm, g8);
+  float ss = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    ss = fmaf(xg[k], xg[k], ss);
+    xg[k] *= g8[k];
+  }
+  ss = wave_sum(ss);
+  return 1.0f / sqrtf(ss * (1.0f / kNope) + epsilon);
+}
+
 // NI = 8-head instructions per wave (heads per wave / 8).
 template <int NI, MlaOut MODE, bool QF32>
 __global__ __launch_bounds__(256) void mla_kernel(const MlaArgs a) {
@@ -159,18 +179,35 @@ __global__ __launch_bounds__(256) void mla_kernel(const MlaArgs a) {
   const CacheView& cv = a.cache;
   const TokenSlot ts = find_slot(a.offsets, a.batch, cv.cache_lengths, t, lane);
   const bool pos_ok = ts.ok && ts.slot < a.max_seq_len;
+  // The freqs row is loaded without a branch (a skipped token reads row 0,
+  // which always exists, and returns before using it), so that nothing
+  // issued after the latent row has to complete before the statistic below.
   float cs[16];
-  if (pos_ok) {
-    const float4* fr = reinterpret_cast<const float4*>(a.freqs + (int64_t)ts.slot * kRope +
-                                                       16 * hl.pair_block);
+  {
+    const float4* fr = reinterpret_cast<const float4*>(
+        a.freqs + (int64_t)(pos_ok ? ts.slot : 0u) * kRope + 16 * hl.pair_block);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float4 v = fr[i];
       cs[4 * i] = v.x; cs[4 * i + 1] = v.y; cs[4 * i + 2] = v.z; cs[4 * i + 3] = v.w;
     }
   }
+  const uint32_t col = pos_ok ? page_column(ts.slot, cv.page_size) : 0u;
+  const bool col_ok = pos_ok && col < cv.pt_stride;
+  uint32_t page = 0;
+  if (col_ok) page = cv.page_table[(uint64_t)ts.request * cv.pt_stride + col];
+  // Buffer form: the latent row arrived with the first step, so its
+  // statistic is reduced while the freqs row and the page-table entry are
+  // still in flight.
+  float xg[8];
+  float r = 0.0f;
+  if constexpr (!INPLACE) {
+    if (latent_wave) r = latent_rms(xn, gm, xg, a.epsilon);
+  }
   PageSlot ps{};
-  if (!(pos_ok && page_of(cv.page_table, cv.pt_stride, cv.num_pages, cv.page_size, ts, &ps))) {
+  ps.page = uniform(page);
+  ps.offset = ts.slot - col * cv.page_size;
+  if (!(col_ok && ps.page < cv.num_pages)) {
     if (latent_wave) count_skip(cv.error_count, lane);
     return;
   }
@@ -201,17 +238,7 @@ __global__ __launch_bounds__(256) void mla_kernel(const MlaArgs a) {
   if (!latent_wave) return;
 
   // ---- latent row: RMSNorm (non-rope part), RoPE (tail) ---------------------
-  float xg[8], g8[8];
-  unpack8(xn, xg);
-  unpack8(gm, g8);
-  float ss = 0.0f;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    ss = fmaf(xg[k], xg[k], ss);
-    xg[k] *= g8[k];  // exact: bf16 x bf16
-  }
-  ss = wave_sum(ss);
-  const float r = 1.0f / sqrtf(ss * (1.0f / kNope) + a.epsilon);
+  if constexpr (INPLACE) r = latent_rms(xn, gm, xg, a.epsilon);
   float tv[8], tp[8];
   unpack8(tail, tv);
   unpack8(mirror16<8>(tail), tp);
