@@ -14,6 +14,9 @@ point of the method:
   "mla_graph" module page;
 * :func:`qk_rope_paged_ragged` -- page "generic_fused_qk_rope_bshd_paged_ragged";
 * :func:`rms_norm_kv_cache_paged` -- page "rms_norm_kv_cache_ragged_paged";
+* :func:`token_plan` and :func:`mla_rope_rmsnorm_quant_planned` -- the same
+  step's ragged / paged addressing written out once per batch layout, and the
+  step placed by it;
 * :func:`mla_gather_latent_paged` -- the paged-to-contiguous latent copy and
   fp8 (de)quantisation step of mla_prefill_branch_fp8 ("mla_graph" page);
 * the bf16 and FP8 E4M3FN codecs and the RoPE / RMSNorm row steps, exposed so
@@ -78,6 +81,12 @@ def load(path: str | None = None) -> ctypes.CDLL:
         _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
         ctypes.c_float, _i64, _i64, _i64, _vp, ctypes.c_int, _i64, _i64, _i64,
         _i64, ctypes.c_int, ctypes.c_float, _vp]
+    lib.oracle_token_plan.restype = ctypes.c_int
+    lib.oracle_token_plan.argtypes = [_vp, _i64, _vp, _vp, _i64, _vp, _i64, _i64, _i64]
+    lib.oracle_mla_rope_rmsnorm_quant_planned.restype = ctypes.c_int
+    lib.oracle_mla_rope_rmsnorm_quant_planned.argtypes = [
+        _vp, ctypes.c_int, _vp, _vp, _vp, _i64, _vp, _i64, _vp, ctypes.c_float, _i64, _i64,
+        _i64, _vp, ctypes.c_int, _i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_float, _vp]
     lib.oracle_mla_rope_rmsnorm_inplace.restype = ctypes.c_int
     lib.oracle_mla_rope_rmsnorm_inplace.argtypes = [
         _vp, ctypes.c_int, _vp, _vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp, ctypes.c_float,
@@ -228,6 +237,42 @@ class Oracle:
             int(layer_idx), mode, float(tensor_scale),
             _ptr(token_scales, np.float32))
         _check(rc, "mla_rope_rmsnorm_quant")
+
+    def token_plan(self, T, row_offsets, cache_lengths, page_table, num_pages, page_size):
+        """Placement of each of the T new tokens: u32 [T, 4] rows (page,
+        offset, position, 1), or zeros for a token without a request or a
+        valid page."""
+        plan = np.zeros((T, 4), np.uint32)
+        rc = self.lib.oracle_token_plan(
+            _ptr(plan, np.uint32), int(T), _ptr(row_offsets, np.uint32),
+            _ptr(cache_lengths, np.uint32), row_offsets.size - 1, _ptr(page_table, np.uint32),
+            page_table.shape[1], int(num_pages), int(page_size))
+        _check(rc, "token_plan")
+        return plan
+
+    def mla_rope_rmsnorm_quant_planned(self, q_out, q_in, latent, plan, freqs, gamma,
+                                       epsilon, cache, layer_idx, scale_mode,
+                                       tensor_scale=1.0, token_scales=None):
+        """:meth:`mla_rope_rmsnorm_quant` with each token placed by ``plan``
+        (u32 [T, 4]: page, offset, position, placed flag) instead of the
+        ragged batch and the page table."""
+        T, H, R = q_in.shape
+        W = latent.shape[1]
+        L, P, S = cache.shape[:3]
+        if (cache.shape[3:] != (1, W) or q_out.shape != q_in.shape or latent.shape[0] != T
+                or plan.shape != (T, 4)):
+            raise ValueError("inconsistent MLA shapes")
+        cache_type = CACHE_BF16 if cache.dtype == np.uint16 else CACHE_FP8
+        mode = {"per_tensor": SCALE_PER_TENSOR, "per_token": SCALE_PER_TOKEN,
+                "none": 0}[scale_mode]
+        q_f32 = q_out.dtype == np.float32
+        rc = self.lib.oracle_mla_rope_rmsnorm_quant_planned(
+            _ptr(q_out, np.float32 if q_f32 else np.uint16), int(q_f32),
+            _ptr(q_in, np.uint16), _ptr(latent, np.uint16), _ptr(plan, np.uint32), T,
+            _ptr(freqs, np.float32), freqs.shape[0], _ptr(gamma, np.uint16), float(epsilon),
+            H, R, W - R, _ptr(cache, cache.dtype), cache_type, L, P, S, int(layer_idx), mode,
+            float(tensor_scale), _ptr(token_scales, np.float32))
+        _check(rc, "mla_rope_rmsnorm_quant_planned")
 
     def mla_rope_rmsnorm_inplace(self, q_out, q_in, row_offsets, cache_lengths, page_table,
                                  freqs, gamma, epsilon, cache, layer_idx):

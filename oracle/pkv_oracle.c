@@ -243,6 +243,65 @@ static int64_t page_of(const uint32_t* page_table, int64_t pt_stride,
  * latent = NULL is the in-place form (see oracle_mla_rope_rmsnorm_inplace):
  * each token's row x is read from its own slot of the bf16 cache.
  */
+/* One token of the fused MLA step: q of token t rotated at position pos into
+ * q_out, and the token's latent row (from the buffer, or in place from cache
+ * row `row`) normalised, rotated and written to cache row `row` (row counts
+ * latent rows of W = Dn + R elements from the start of the cache, layer
+ * included). */
+static int mla_token(void* q_out, int q_out_f32, const uint16_t* q_in, const uint16_t* latent,
+                     int64_t t, int64_t pos, int64_t row, const float* freqs, const double* g,
+                     double eps, int64_t H, int64_t R, int64_t Dn, void* cache,
+                     int cache_type, int scale_mode, float tensor_scale,
+                     float* token_scales) {
+  const int64_t W = Dn + R;
+  double x[4096], y[4096], qa[1024], qb[1024];
+  const float* fr = freqs + pos * R;
+
+  /* q: RoPE on every head, one rounding per value into the output type
+   * ([MLA] Parameters: out_rope_dtype; bf16 or fp32 here). */
+  for (int64_t h = 0; h < H; ++h) {
+    const uint16_t* src = q_in + (t * H + h) * R;
+    for (int64_t i = 0; i < R; ++i) qa[i] = oracle_bf16_decode(src[i]);
+    oracle_rope_row(qa, qb, R, fr, 0);
+    if (q_out_f32) {
+      float* dst = (float*)q_out + (t * H + h) * R;
+      for (int64_t i = 0; i < R; ++i) dst[i] = (float)qb[i];  /* RNE */
+    } else {
+      uint16_t* dst = (uint16_t*)q_out + (t * H + h) * R;
+      for (int64_t i = 0; i < R; ++i) dst[i] = oracle_bf16_encode(qb[i]);
+    }
+  }
+
+  /* latent: RMSNorm on the first Dn values, RoPE on the R-value tail;
+   * the row comes from its buffer, or in place from the cache slot. */
+  const uint16_t* src = latent ? latent + t * W : (const uint16_t*)cache + row * W;
+  for (int64_t k = 0; k < W; ++k) x[k] = oracle_bf16_decode(src[k]);
+  oracle_rmsnorm_row(x, y, Dn, g, eps);
+  oracle_rope_row(x + Dn, y + Dn, R, fr, 0);
+
+  if (cache_type == ORACLE_CACHE_BF16) {
+    uint16_t* dst = (uint16_t*)cache + row * W;
+    for (int64_t k = 0; k < W; ++k) dst[k] = oracle_bf16_encode(y[k]);
+    return ORACLE_OK;
+  }
+  uint8_t* dst = (uint8_t*)cache + row * W;
+  if (scale_mode == ORACLE_SCALE_PER_TENSOR) {
+    const double s = (double)tensor_scale;
+    for (int64_t k = 0; k < W; ++k) put_fp8(&dst[k], y[k] / s);
+  } else if (scale_mode == ORACLE_SCALE_PER_TOKEN) {
+    double amax = 0.0;
+    for (int64_t k = 0; k < W; ++k)
+      if (fabs(y[k]) > amax) amax = fabs(y[k]);
+    const float st = (float)(amax / 448.0); /* stored fp32, one rounding */
+    for (int64_t k = 0; k < W; ++k)
+      put_fp8(&dst[k], st == 0.0f ? y[k] : y[k] / (double)st);
+    token_scales[row] = st;
+  } else {
+    return ORACLE_BAD_ARG;
+  }
+  return ORACLE_OK;
+}
+
 int oracle_mla_rope_rmsnorm_quant(
     void* q_out, int q_out_f32, const uint16_t* q_in, const uint16_t* latent,
     const uint32_t* row_offsets, const uint32_t* cache_lengths, int64_t B,
@@ -254,10 +313,9 @@ int oracle_mla_rope_rmsnorm_quant(
   if (R <= 0 || R % 2 || Dn <= 0 || H < 0 || B < 0 || layer_idx < 0 ||
       layer_idx >= num_layers || page_size <= 0)
     return ORACLE_BAD_ARG;
-  const int64_t W = Dn + R; /* latent row width */
   if (!latent && cache_type != ORACLE_CACHE_BF16) return ORACLE_BAD_ARG;
-  double x[4096], y[4096], g[4096], qa[1024], qb[1024];
-  if (W > 4096 || R > 1024) return ORACLE_BAD_ARG;
+  double g[4096];
+  if (Dn + R > 4096 || R > 1024) return ORACLE_BAD_ARG;
   for (int64_t k = 0; k < Dn; ++k) g[k] = oracle_bf16_decode(gamma[k]);
   const double eps = (double)epsilon; /* the fp32 value, widened exactly */
   int status = ORACLE_OK;
@@ -272,52 +330,79 @@ int oracle_mla_rope_rmsnorm_quant(
                                    page_size, b, slot);
       if (page < 0) { status = ORACLE_BAD_PAGE; continue; }
       const int64_t off = slot % page_size;
-      const float* fr = freqs + pos * R;
-
-      /* q: RoPE on every head, one rounding per value into the output type
-       * ([MLA] Parameters: out_rope_dtype; bf16 or fp32 here). */
-      for (int64_t h = 0; h < H; ++h) {
-        const uint16_t* src = q_in + (t * H + h) * R;
-        for (int64_t i = 0; i < R; ++i) qa[i] = oracle_bf16_decode(src[i]);
-        oracle_rope_row(qa, qb, R, fr, 0);
-        if (q_out_f32) {
-          float* dst = (float*)q_out + (t * H + h) * R;
-          for (int64_t i = 0; i < R; ++i) dst[i] = (float)qb[i];  /* RNE */
-        } else {
-          uint16_t* dst = (uint16_t*)q_out + (t * H + h) * R;
-          for (int64_t i = 0; i < R; ++i) dst[i] = oracle_bf16_encode(qb[i]);
-        }
-      }
-
-      /* latent: RMSNorm on the first Dn values, RoPE on the R-value tail;
-       * the row comes from its buffer, or in place from the cache slot. */
       const int64_t row = ((layer_idx * num_pages + page) * page_size + off);
-      const uint16_t* src = latent ? latent + t * W : (const uint16_t*)cache + row * W;
-      for (int64_t k = 0; k < W; ++k) x[k] = oracle_bf16_decode(src[k]);
-      oracle_rmsnorm_row(x, y, Dn, g, eps);
-      oracle_rope_row(x + Dn, y + Dn, R, fr, 0);
-
-      if (cache_type == ORACLE_CACHE_BF16) {
-        uint16_t* dst = (uint16_t*)cache + row * W;
-        for (int64_t k = 0; k < W; ++k) dst[k] = oracle_bf16_encode(y[k]);
-        continue;
-      }
-      uint8_t* dst = (uint8_t*)cache + row * W;
-      if (scale_mode == ORACLE_SCALE_PER_TENSOR) {
-        const double s = (double)tensor_scale;
-        for (int64_t k = 0; k < W; ++k) put_fp8(&dst[k], y[k] / s);
-      } else if (scale_mode == ORACLE_SCALE_PER_TOKEN) {
-        double amax = 0.0;
-        for (int64_t k = 0; k < W; ++k)
-          if (fabs(y[k]) > amax) amax = fabs(y[k]);
-        const float st = (float)(amax / 448.0); /* stored fp32, one rounding */
-        for (int64_t k = 0; k < W; ++k)
-          put_fp8(&dst[k], st == 0.0f ? y[k] : y[k] / (double)st);
-        token_scales[row] = st;
-      } else {
-        return ORACLE_BAD_ARG;
-      }
+      const int rc = mla_token(q_out, q_out_f32, q_in, latent, t, pos, row, freqs, g, eps,
+                               H, R, Dn, cache, cache_type, scale_mode, tensor_scale,
+                               token_scales);
+      if (rc != ORACLE_OK) return rc;
     }
+  }
+  return status;
+}
+
+/*
+ * Placement of every new token of a ragged batch, written out once: the
+ * request of token t (t = o[b] + j), its cache slot and RoPE position
+ * c[b] + j, and the slot's physical page and offset (the addressing of [MLA]
+ * Args: input_row_offsets, the cache's lengths and page table).
+ *   plan  u32 [T][4]: (page, offset, position, 1) for a placed token;
+ *         (0, 0, 0, 0) for a token no request owns (t >= o[B]) or whose
+ *         slot has no page-table entry or a page id past the pool.
+ * Positions are not compared with a freqs table here.
+ */
+int oracle_token_plan(uint32_t* plan, int64_t T, const uint32_t* row_offsets,
+                      const uint32_t* cache_lengths, int64_t B, const uint32_t* page_table,
+                      int64_t pt_stride, int64_t num_pages, int64_t page_size) {
+  if (T < 0 || B < 0 || page_size <= 0) return ORACLE_BAD_ARG;
+  for (int64_t i = 0; i < 4 * T; ++i) plan[i] = 0;
+  for (int64_t b = 0; b < B; ++b) {
+    for (int64_t t = row_offsets[b]; t < (int64_t)row_offsets[b + 1] && t < T; ++t) {
+      const int64_t slot = (int64_t)cache_lengths[b] + (t - (int64_t)row_offsets[b]);
+      const int64_t page = page_of(page_table, pt_stride, num_pages, page_size, b, slot);
+      if (page < 0) continue;
+      plan[4 * t] = (uint32_t)page;
+      plan[4 * t + 1] = (uint32_t)(slot % page_size);
+      plan[4 * t + 2] = (uint32_t)slot;
+      plan[4 * t + 3] = 1;
+    }
+  }
+  return ORACLE_OK;
+}
+
+/*
+ * Fused MLA step placed by a token plan: token t is rotated at position
+ * plan[t][2] and its row stored at (page plan[t][0], offset plan[t][1]) of
+ * layer layer_idx.  A token whose entry is not marked placed, whose position
+ * is not below max_seq_len, or whose page or offset lies outside the pool is
+ * skipped (nothing written; the return value reports it).  Other arguments
+ * as for oracle_mla_rope_rmsnorm_quant with its latent buffer.
+ */
+int oracle_mla_rope_rmsnorm_quant_planned(
+    void* q_out, int q_out_f32, const uint16_t* q_in, const uint16_t* latent,
+    const uint32_t* plan, int64_t T, const float* freqs, int64_t max_seq_len,
+    const uint16_t* gamma, float epsilon, int64_t H, int64_t R, int64_t Dn, void* cache,
+    int cache_type, int64_t num_layers, int64_t num_pages, int64_t page_size,
+    int64_t layer_idx, int scale_mode, float tensor_scale, float* token_scales) {
+  if (R <= 0 || R % 2 || Dn <= 0 || H < 0 || T < 0 || layer_idx < 0 ||
+      layer_idx >= num_layers || page_size <= 0 || !latent)
+    return ORACLE_BAD_ARG;
+  double g[4096];
+  if (Dn + R > 4096 || R > 1024) return ORACLE_BAD_ARG;
+  for (int64_t k = 0; k < Dn; ++k) g[k] = oracle_bf16_decode(gamma[k]);
+  const double eps = (double)epsilon;
+  int status = ORACLE_OK;
+  for (int64_t t = 0; t < T; ++t) {
+    const uint32_t* e = plan + 4 * t;
+    if (e[3] == 0 || (int64_t)e[0] >= num_pages || (int64_t)e[1] >= page_size) {
+      status = ORACLE_BAD_PAGE;
+      continue;
+    }
+    if ((int64_t)e[2] >= max_seq_len) { status = ORACLE_BAD_POSITION; continue; }
+    const int64_t row = ((layer_idx * num_pages + e[0]) * page_size + e[1]);
+    const int rc = mla_token(q_out, q_out_f32, q_in, latent, t, (int64_t)e[2], row, freqs, g,
+                             eps, H, R, Dn, cache, cache_type, scale_mode, tensor_scale,
+                             token_scales);
+    if (rc != ORACLE_OK) return rc;
   }
   return status;
 }

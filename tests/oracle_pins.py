@@ -18,6 +18,7 @@ import os
 import numpy as np
 import torch
 
+import oracle
 import workloads
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
@@ -550,6 +551,139 @@ def pin_mla_f32_q(orc):
     assert np.array_equal(cache, cache_b)
 
 
+def expected_token_plan(case, T=None):
+    """The plan a batch implies, from the inverse page-table scan: row t is
+    (page, offset, slot, 1) for the physical (page, offset) that holds token
+    t's slot, zeros for a token no valid page-table entry places."""
+    T = case.T if T is None else T
+    P = case.cache.shape[1]
+    pt = case.page_table.copy()
+    pt[pt >= P] = workloads.UNUSED_PAGE      # ids past the pool place nothing
+    plan = np.zeros((T, 4), np.uint32)
+    for (page, off), (t, slot) in slot_owners(case.row_offsets, case.cache_lengths, pt,
+                                              case.meta["page_size"]).items():
+        if t < T:
+            plan[t] = (page, off, slot, 1)
+    return plan
+
+
+def run_token_plan(orc, case, T=None):
+    return orc.token_plan(case.T if T is None else T, case.row_offsets, case.cache_lengths,
+                          case.page_table, case.cache.shape[1], case.meta["page_size"])
+
+
+def token_plan_cases():
+    """The small MLA cases, plus one whose page table holds ids past the pool
+    and one more row than its offsets cover."""
+    yield from small_mla_cases()
+    bad = workloads.build_mla("mla_small_badpages", 2011, [5, 9, 3], [14, 0, 40], H=4,
+                              page_size=8, max_seq_len=64, spare_pages=2,
+                              scale_mode="per_tensor", tensor_scale=0.05)
+    P = bad.cache.shape[1]
+    bad.page_table[0, 2] = P                 # request 0: slots 16..23 lose their page
+    bad.page_table[2, 5] = P + 7             # request 2: slots 40..47
+    yield bad
+
+
+def pin_token_plan(orc):
+    for case in token_plan_cases():
+        got = run_token_plan(orc, case)
+        assert np.array_equal(got, expected_token_plan(case)), case.name
+    # rows past the last offset: nothing owns them
+    case = workloads.mla_tiny()
+    got = run_token_plan(orc, case, case.T + 3)
+    assert np.array_equal(got, expected_token_plan(case, case.T + 3))
+    assert not got[case.T:].any()
+
+
+def run_mla_planned(orc, case, plan, q_f32=False):
+    q_out = np.zeros(case.q.shape, np.float32) if q_f32 else np.zeros_like(case.q)
+    cache = case.cache.copy()
+    ts = None if case.token_scales is None else case.token_scales.copy()
+    skipped = False
+    try:
+        orc.mla_rope_rmsnorm_quant_planned(q_out, case.q, case.latent, plan, case.freqs,
+                                           case.gamma, case.epsilon, cache, case.layer_idx,
+                                           case.scale_mode, case.tensor_scale, ts)
+    except oracle.OracleError:
+        skipped = True                       # some token was skipped; the rest is written
+    return q_out, cache, ts, skipped
+
+
+def free_plan(case, rng, skip_every=0):
+    """A plan that places each token at a random distinct (page, offset) of
+    the pool with a random position, unrelated to the batch's page table;
+    every skip_every-th token (when > 0) is marked not placed."""
+    L, P, S = case.cache.shape[:3]
+    cells = rng.choice(P * S, size=case.T, replace=False)
+    plan = np.zeros((case.T, 4), np.uint32)
+    plan[:, 0], plan[:, 1] = cells // S, cells % S
+    plan[:, 2] = rng.integers(0, case.freqs.shape[0], size=case.T)
+    plan[:, 3] = 1
+    if skip_every:
+        plan[::skip_every, 3] = 0
+    return plan
+
+
+def check_mla_planned_free(case, plan, q_out, cache, ts):
+    """Outputs of a planned step against the float64 reference at each
+    token's planned position; rows land at the planned cells, nothing else
+    changes (q of a skipped token stays zero)."""
+    placed = plan[:, 3] != 0
+    pos = plan[:, 2].astype(np.int64)
+    fr = case.freqs[pos].astype(np.float64)
+    cs, sn = fr[:, 0::2], fr[:, 1::2]
+    q_ref = _complex_rope(bf16_to_f64(case.q), cs[:, None, :], sn[:, None, :], False)
+    assert_correctly_rounded(bf16_to_f64(q_out[placed]), q_ref[placed], ulp_bf16, "planned q")
+    assert not q_out[~placed].any(), "q written for a skipped token"
+    x = bf16_to_f64(case.latent)
+    Dn = case.Dn
+    y_ref = np.empty_like(x)
+    y_ref[:, :Dn] = torch.nn.functional.rms_norm(
+        torch.from_numpy(x[:, :Dn].copy()), (Dn,),
+        weight=torch.from_numpy(bf16_to_f64(case.gamma)), eps=case.epsilon).numpy()
+    y_ref[:, Dn:] = _complex_rope(x[:, Dn:], cs, sn, False)
+    L = case.layer_idx
+    expect = case.cache.copy()
+    for t in np.nonzero(placed)[0]:
+        page, off = int(plan[t, 0]), int(plan[t, 1])
+        row = cache[L, page, off, 0]
+        if case.cache.dtype == np.uint16:
+            assert_correctly_rounded(bf16_to_f64(row), y_ref[t], ulp_bf16, f"row {t}")
+        else:
+            if case.scale_mode == "per_tensor":
+                s = float(case.tensor_scale)
+            else:
+                s = float(ts[L, page, off, 0])
+                assert s == float(np.float32(np.max(np.abs(y_ref[t])) / 448.0)), t
+            assert_correctly_rounded(fp8_to_f64(row), y_ref[t] / s, ulp_fp8, f"fp8 row {t}",
+                                     sat=448.0)
+        expect[L, page, off] = row
+    assert np.array_equal(cache, expect), "bytes outside the planned rows changed"
+
+
+def pin_mla_planned(orc):
+    """The planned step: with the plan of its own batch it meets the same
+    independent reference as the batch form (and equals it bit for bit);
+    with a free placement, rows land at the planned cells with the planned
+    positions' rotation; tokens marked not placed are skipped."""
+    for case in small_mla_cases():
+        plan = run_token_plan(orc, case)
+        q_out, cache, ts, skipped = run_mla_planned(orc, case, plan)
+        assert not skipped
+        check_mla_against_reference(case, q_out, cache, ts)
+        q_b, cache_b, ts_b = run_mla(orc, case)
+        assert np.array_equal(q_out, q_b) and np.array_equal(cache, cache_b)
+        if ts is not None:
+            assert np.array_equal(ts.view(np.uint32), ts_b.view(np.uint32))
+    rng = np.random.default_rng(2020)
+    for k, case in enumerate(small_mla_cases()):
+        plan = free_plan(case, rng, skip_every=3 if k % 2 else 0)
+        q_out, cache, ts, skipped = run_mla_planned(orc, case, plan)
+        assert skipped == bool(k % 2 and case.T)
+        check_mla_planned_free(case, plan, q_out, cache, ts)
+
+
 def small_mla_inplace_cases():
     """bf16 latent caches for the in-place form: ragged prefill with page
     crossings and zero-length requests, decode rows, fp32 q in one case."""
@@ -1047,5 +1181,5 @@ ALL_PINS = [
     pin_rmsnorm_closed_forms, pin_rmsnorm_torch, pin_mla_composite,
     pin_mla_position0, pin_mla_zero_row_per_token, pin_qk_composite,
     pin_rms_norm_kv, pin_gather, pin_qk_fp8, pin_rms_norm_kv_fp8, pin_mrope,
-    pin_mla_f32_q, pin_rms_norm_kv_token, pin_mla_inplace,
+    pin_mla_f32_q, pin_rms_norm_kv_token, pin_mla_inplace, pin_token_plan, pin_mla_planned,
 ]

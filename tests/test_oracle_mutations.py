@@ -45,12 +45,12 @@ MUTANTS = [
      "oracle_rope_row(y + Dn, x + Dn, R, fr, 0); memcpy(y + Dn, x + Dn, R * sizeof(double));"),
     ("mla_scale_multiplied", "put_fp8(&dst[k], y[k] / s);",
      "put_fp8(&dst[k], y[k] * s);"),
-    ("mla_amax_nope_only", "for (int64_t k = 0; k < W; ++k)\n          if (fabs(y[k]) > amax)",
-     "for (int64_t k = 0; k < Dn; ++k)\n          if (fabs(y[k]) > amax)"),
+    ("mla_amax_nope_only", "for (int64_t k = 0; k < W; ++k)\n      if (fabs(y[k]) > amax)",
+     "for (int64_t k = 0; k < Dn; ++k)\n      if (fabs(y[k]) > amax)"),
     ("mla_token_scale_448", "const float st = (float)(amax / 448.0); /* stored fp32",
      "const float st = (float)(amax / 240.0); /* stored fp32"),
-    ("page_offset", "const int64_t off = slot % page_size;\n      const float* fr = freqs + pos * R;",
-     "const int64_t off = (slot + 1) % page_size;\n      const float* fr = freqs + pos * R;"),
+    ("page_offset", "const int64_t off = slot % page_size;\n      const int64_t row = ((layer_idx",
+     "const int64_t off = (slot + 1) % page_size;\n      const int64_t row = ((layer_idx"),
     ("page_table_column", "int64_t col = slot / page_size;", "int64_t col = slot / page_size + 1;"),
     ("wrong_layer", "const int64_t row = ((layer_idx * num_pages + page) * page_size + off);",
      "const int64_t row = (((layer_idx - 1) * num_pages + page) * page_size + off);"),
@@ -111,6 +111,15 @@ MUTANTS = [
     ("kvnorm_unrounded_ties_up",
      "a[i] = oracle_bf16_decode(oracle_bf16_encode(a[i] * inv)) * g[i];",
      "a[i] = oracle_bf16_decode(oracle_bf16_encode(a[i] * inv)) * g[i] * (1 + 0x1p-40);"),
+    # the token plan and the step placed by it
+    ("plan_offset", "plan[4 * t + 1] = (uint32_t)(slot % page_size);",
+     "plan[4 * t + 1] = (uint32_t)((slot + 1) % page_size);"),
+    ("plan_position", "plan[4 * t + 2] = (uint32_t)slot;", "plan[4 * t + 2] = (uint32_t)slot + 1;"),
+    ("planned_ignores_flag", "if (e[3] == 0 || (int64_t)e[0] >= num_pages",
+     "if ((int64_t)e[0] >= num_pages"),
+    ("planned_offset_as_position",
+     "mla_token(q_out, q_out_f32, q_in, latent, t, (int64_t)e[2], row,",
+     "mla_token(q_out, q_out_f32, q_in, latent, t, (int64_t)e[1], row,"),
 ]
 
 RUNNER = r"""
