@@ -1,7 +1,7 @@
 /*
  * pkv.h -- C ABI of the paged-KV pre-attention library (gfx950 / MI355X).
  *
- * Five entry points, each one stream-ordered kernel launch:
+ * Seven entry points, each one stream-ordered kernel launch:
  *
  *   mla_rope_rmsnorm_quant   fused MLA step: RoPE on q_rope, RMSNorm on the
  *                            latent row's non-rope part, RoPE on its rope tail,
@@ -15,6 +15,12 @@
  *                            (fused_rope_rmsnorm_kernel and the first two
  *                            steps of mla_prefill_branch_fp8 /
  *                            mla_decode_branch_fp8, "mla_graph" module page).
+ *   pkv_token_plan           each new token's cache placement (page, offset,
+ *                            position), written once per batch layout, and
+ *   mla_rope_rmsnorm_quant_planned
+ *                            the fused MLA step placed by such a plan (the
+ *                            same page's addressing, split so that every layer
+ *                            of a model step reuses it).
  *   qk_rope_paged_ragged     RoPE on Q (out of place) and on the new K rows of a
  *                            paged cache (in place), optional per-head K
  *                            RMSNorm fused in front of the K rotation.
@@ -183,6 +189,59 @@ int mla_rope_rmsnorm_inplace(void* q_rope_out, int64_t qo_tok_stride, int64_t qo
                              uint32_t kv_norm_dim, const float* freqs_cis, uint32_t max_seq_len,
                              const void* gamma, float epsilon, const pkv_paged_cache* kv_cache,
                              uint32_t layer_idx, int32_t q_out_dtype, void* stream);
+
+/*
+ * Token plan: the placement of every new token of a ragged batch, written
+ * once so that the fused MLA step of every layer can read it instead of
+ * resolving it again (page "mla_fused_rope_rmsnorm_quantization", Args:
+ * input_row_offsets and the KV collection's cache lengths and page table;
+ * every layer of a model step shares them).
+ *
+ *   token_plan      u32 [total_tokens][4], written, 16-byte aligned: for token
+ *                   t of request b (index j) the entry (page, offset,
+ *                   position, 1) with position = slot = cache_lengths[b] + j,
+ *                   page = page_table[b][slot / page_size], offset =
+ *                   slot % page_size.  A token that no request owns, or
+ *                   whose slot has no page-table column or a page id not
+ *                   below num_pages, gets (0, 0, 0, 0).
+ *   input_row_offsets u32 [batch_size + 1], total_tokens (host) as for
+ *                   mla_rope_rmsnorm_quant
+ *   cache           (host) descriptor: cache_lengths, page_table,
+ *                   page_table_stride, page_size and num_pages are read; the
+ *                   pool itself and the error counter are not touched
+ * Positions are not compared with a freqs table here (the planned step does
+ * that).  The plan stays valid while the batch layout, the cache lengths and
+ * the page table are unchanged.
+ */
+int pkv_token_plan(uint32_t* token_plan, const uint32_t* input_row_offsets,
+                   uint32_t batch_size, uint32_t total_tokens, const pkv_paged_cache* cache,
+                   void* stream);
+
+/*
+ * The fused MLA step of mla_rope_rmsnorm_quant with each token placed by a
+ * token plan: token t is rotated at position token_plan[t][2] and its row
+ * written at page token_plan[t][0], offset token_plan[t][1] of layer
+ * layer_idx.  With the plan pkv_token_plan wrote for the same batch the
+ * results equal mla_rope_rmsnorm_quant's bit for bit.  A token whose entry
+ * is not marked placed (fourth word 0), whose position is not below
+ * max_seq_len, or whose page or offset lies outside the pool is skipped and
+ * counted like a device-data failure.
+ *
+ *   token_plan      u32 [total_tokens][4], 16-byte aligned
+ * Other arguments as for mla_rope_rmsnorm_quant (same shapes, dtypes and
+ * supported sizes); the cache descriptor's cache_lengths and page_table are
+ * not read and may be NULL.
+ */
+int mla_rope_rmsnorm_quant_planned(void* q_rope_out, int64_t qo_tok_stride,
+                                   int64_t qo_head_stride, const void* q_rope,
+                                   int64_t qi_tok_stride, int64_t qi_head_stride,
+                                   const void* kv_latent, int64_t kv_row_stride,
+                                   const uint32_t* token_plan, uint32_t total_tokens,
+                                   uint32_t num_heads, uint32_t rope_dim, uint32_t kv_norm_dim,
+                                   const float* freqs_cis, uint32_t max_seq_len,
+                                   const void* gamma, float epsilon,
+                                   const pkv_paged_cache* kv_cache, uint32_t layer_idx,
+                                   int32_t q_out_dtype, void* stream);
 
 /*
  * Paged-ragged fused Q/K RoPE.  Q is rotated into q_out; the K rows of the

@@ -30,7 +30,8 @@ PKV_SCALE_NONE = 0
 PKV_SCALE_PER_TENSOR = 1
 PKV_SCALE_PER_TOKEN = 2
 
-EXPORTED = ("mla_rope_rmsnorm_quant", "mla_rope_rmsnorm_inplace", "qk_rope_paged_ragged",
+EXPORTED = ("mla_rope_rmsnorm_quant", "mla_rope_rmsnorm_inplace", "pkv_token_plan",
+            "mla_rope_rmsnorm_quant_planned", "qk_rope_paged_ragged",
             "rms_norm_kv_cache_paged", "mla_gather_latent_paged", "pkv_status_string")
 
 
@@ -79,6 +80,12 @@ def _load() -> ctypes.CDLL:
     lib.mla_rope_rmsnorm_inplace.restype = ctypes.c_int
     lib.mla_rope_rmsnorm_inplace.argtypes = [
         vp, i64, i64, vp, i64, i64, vp, u32, u32, u32, u32, u32, vp, u32, vp, f32,
+        cache_p, u32, ctypes.c_int32, vp]
+    lib.pkv_token_plan.restype = ctypes.c_int
+    lib.pkv_token_plan.argtypes = [vp, vp, u32, u32, cache_p, vp]
+    lib.mla_rope_rmsnorm_quant_planned.restype = ctypes.c_int
+    lib.mla_rope_rmsnorm_quant_planned.argtypes = [
+        vp, i64, i64, vp, i64, i64, vp, i64, vp, u32, u32, u32, u32, vp, u32, vp, f32,
         cache_p, u32, ctypes.c_int32, vp]
     lib.qk_rope_paged_ragged.restype = ctypes.c_int
     lib.qk_rope_paged_ragged.argtypes = [
@@ -195,6 +202,43 @@ def mla_rope_rmsnorm_inplace(q_rope_output: torch.Tensor, q_rope: torch.Tensor,
         PKV_DTYPE_F32 if q_rope_output.dtype == torch.float32 else PKV_DTYPE_BF16,
         _stream(stream))
     _check("mla_rope_rmsnorm_inplace", st)
+
+
+def pkv_token_plan(plan: torch.Tensor, input_row_offsets: torch.Tensor, kv_cache: PagedCache,
+                   stream=None) -> None:
+    """Write each new token's placement (C: ``pkv_token_plan``) into ``plan``,
+    a contiguous ``[tokens, 4]`` int32 / uint32 tensor: (page, offset,
+    position, 1), or zeros for a token without a valid placement.  The
+    token count is ``plan.shape[0]``."""
+    if plan.dim() != 2 or plan.shape[1] != 4 or not plan.is_contiguous():
+        raise ValueError("plan must be a contiguous [tokens, 4] tensor")
+    st = _lib.pkv_token_plan(_ptr(plan), _ptr(input_row_offsets),
+                             input_row_offsets.numel() - 1, plan.shape[0],
+                             ctypes.byref(kv_cache), _stream(stream))
+    _check("pkv_token_plan", st)
+
+
+def mla_rope_rmsnorm_quant_planned(q_rope_output: torch.Tensor, q_rope: torch.Tensor,
+                                   kv_latent: torch.Tensor, plan: torch.Tensor,
+                                   freqs_cis: torch.Tensor, gamma: torch.Tensor,
+                                   epsilon: float, kv_cache: PagedCache, layer_idx: int,
+                                   stream=None) -> None:
+    """Fused MLA step placed by a token plan (C:
+    ``mla_rope_rmsnorm_quant_planned``); arguments as for
+    :func:`mla_rope_rmsnorm_quant` with ``plan`` (``[tokens, 4]``, from
+    :func:`pkv_token_plan`) in place of the row offsets."""
+    T, H, R = q_rope.shape
+    if plan.dim() != 2 or plan.shape[1] != 4 or not plan.is_contiguous():
+        raise ValueError("plan must be a contiguous [tokens, 4] tensor")
+    st = _lib.mla_rope_rmsnorm_quant_planned(
+        _ptr(q_rope_output), q_rope_output.stride(0), q_rope_output.stride(1),
+        _ptr(q_rope), q_rope.stride(0), q_rope.stride(1),
+        _ptr(kv_latent), kv_latent.stride(0), _ptr(plan), T, H, R,
+        kv_latent.shape[1] - R, _ptr(freqs_cis), freqs_cis.shape[0], _ptr(gamma),
+        float(epsilon), ctypes.byref(kv_cache), int(layer_idx),
+        PKV_DTYPE_F32 if q_rope_output.dtype == torch.float32 else PKV_DTYPE_BF16,
+        _stream(stream))
+    _check("mla_rope_rmsnorm_quant_planned", st)
 
 
 def qk_rope_paged_ragged(q_out: torch.Tensor, q_proj: torch.Tensor,

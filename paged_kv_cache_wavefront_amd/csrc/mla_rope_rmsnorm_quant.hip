@@ -33,6 +33,10 @@
 //   significands).  The row is converted to fp8 in registers (clamp to +-448,
 //   then hardware round-to-nearest-even) and written with 8-byte
 //   non-temporal stores.
+// * Planned form: with a token plan (token_plan.hip) each wave reads its
+//   token's (page, offset, position, placed) entry with one scalar 16-byte
+//   load instead of the two-step chain; the entry is checked against the
+//   pool and the freqs table like the chain's results.
 // * In-place form ("mla_graph" module page: fused_rope_rmsnorm_kernel, and the
 //   first two steps of the fp8 prefill and decode branches, which apply RoPE
 //   and RMSNorm to the key cache in place): the latent row is not in a buffer
@@ -138,8 +142,9 @@ __device__ __forceinline__ float latent_rms(const uint4& xn, const uint4& gm, fl
   return 1.0f / sqrtf(ss * (1.0f / kNope) + epsilon);
 }
 
-// NI = 8-head instructions per wave (heads per wave / 8).
-template <int NI, MlaOut MODE, bool QF32>
+// NI = 8-head instructions per wave (heads per wave / 8).  PLANNED: each
+// token's placement comes from a token plan instead of the address chain.
+template <int NI, MlaOut MODE, bool QF32, bool PLANNED>
 __global__ __launch_bounds__(256) void mla_kernel(const MlaArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   const uint32_t wave =
@@ -176,8 +181,19 @@ __global__ __launch_bounds__(256) void mla_kernel(const MlaArgs a) {
   // ---- address chain -----------------------------------------------------------
   // step 1: request and slot (= position); step 2: the freqs row and the
   // page-table entry, both needing only the slot, issued together.
+  // Planned: one 16-byte plan entry (page, offset, position, placed) replaces
+  // both steps; the entry is checked against the pool and the freqs table
+  // before anything derived from it is dereferenced.
   const CacheView& cv = a.cache;
-  const TokenSlot ts = find_slot(a.offsets, a.batch, cv.cache_lengths, t, lane);
+  TokenSlot ts{};
+  uint4 pe{};
+  if constexpr (PLANNED) {
+    pe = *reinterpret_cast<const uint4*>(a.plan + 4 * (uint64_t)t);
+    ts.slot = uniform(pe.z);
+    ts.ok = pe.w != 0;
+  } else {
+    ts = find_slot(a.offsets, a.batch, cv.cache_lengths, t, lane);
+  }
   const bool pos_ok = ts.ok && ts.slot < a.max_seq_len;
   // The freqs row is loaded without a branch (a skipped token reads row 0,
   // which always exists, and returns before using it), so that nothing
@@ -192,10 +208,13 @@ __global__ __launch_bounds__(256) void mla_kernel(const MlaArgs a) {
       cs[4 * i] = v.x; cs[4 * i + 1] = v.y; cs[4 * i + 2] = v.z; cs[4 * i + 3] = v.w;
     }
   }
-  const uint32_t col = pos_ok ? page_column(ts.slot, cv.page_size) : 0u;
-  const bool col_ok = pos_ok && col < cv.pt_stride;
-  uint32_t page = 0;
-  if (col_ok) page = cv.page_table[(uint64_t)ts.request * cv.pt_stride + col];
+  uint32_t col = 0, page = 0;
+  bool col_ok = pos_ok;
+  if constexpr (!PLANNED) {
+    col = pos_ok ? page_column(ts.slot, cv.page_size) : 0u;
+    col_ok = pos_ok && col < cv.pt_stride;
+    if (col_ok) page = cv.page_table[(uint64_t)ts.request * cv.pt_stride + col];
+  }
   // Buffer form: the latent row arrived with the first step, so its
   // statistic is reduced while the freqs row and the page-table entry are
   // still in flight.
@@ -205,9 +224,17 @@ __global__ __launch_bounds__(256) void mla_kernel(const MlaArgs a) {
     if (latent_wave) r = latent_rms(xn, gm, xg, a.epsilon);
   }
   PageSlot ps{};
-  ps.page = uniform(page);
-  ps.offset = ts.slot - col * cv.page_size;
-  if (!(col_ok && ps.page < cv.num_pages)) {
+  bool placed;
+  if constexpr (PLANNED) {
+    ps.page = uniform(pe.x);
+    ps.offset = uniform(pe.y);
+    placed = pos_ok && ps.page < cv.num_pages && ps.offset < cv.page_size;
+  } else {
+    ps.page = uniform(page);
+    ps.offset = ts.slot - col * cv.page_size;
+    placed = col_ok && ps.page < cv.num_pages;
+  }
+  if (!placed) {
     if (latent_wave) count_skip(cv.error_count, lane);
     return;
   }
@@ -284,35 +311,39 @@ __global__ __launch_bounds__(256) void mla_kernel(const MlaArgs a) {
   }
 }
 
-template <int NI, bool QF32>
+// The planned form exists for the three buffer modes (the in-place form
+// keeps the address chain).
+template <int NI, bool QF32, bool PLANNED>
 hipError_t launch_g(const MlaArgs& a, MlaOut mode, uint32_t blocks, hipStream_t stream) {
   switch (mode) {
     case MlaOut::Fp8PerTensor:
-      hipLaunchKernelGGL((mla_kernel<NI, MlaOut::Fp8PerTensor, QF32>), dim3(blocks), dim3(256),
-                         0, stream, a);
+      hipLaunchKernelGGL((mla_kernel<NI, MlaOut::Fp8PerTensor, QF32, PLANNED>), dim3(blocks),
+                         dim3(256), 0, stream, a);
       break;
     case MlaOut::Fp8PerToken:
-      hipLaunchKernelGGL((mla_kernel<NI, MlaOut::Fp8PerToken, QF32>), dim3(blocks), dim3(256),
-                         0, stream, a);
+      hipLaunchKernelGGL((mla_kernel<NI, MlaOut::Fp8PerToken, QF32, PLANNED>), dim3(blocks),
+                         dim3(256), 0, stream, a);
       break;
     case MlaOut::Bf16:
-      hipLaunchKernelGGL((mla_kernel<NI, MlaOut::Bf16, QF32>), dim3(blocks), dim3(256), 0,
-                         stream, a);
+      hipLaunchKernelGGL((mla_kernel<NI, MlaOut::Bf16, QF32, PLANNED>), dim3(blocks),
+                         dim3(256), 0, stream, a);
       break;
     case MlaOut::Bf16InPlace:
-      hipLaunchKernelGGL((mla_kernel<NI, MlaOut::Bf16InPlace, QF32>), dim3(blocks), dim3(256),
-                         0, stream, a);
+      if constexpr (PLANNED) return hipErrorInvalidValue;
+      else
+        hipLaunchKernelGGL((mla_kernel<NI, MlaOut::Bf16InPlace, QF32, false>), dim3(blocks),
+                           dim3(256), 0, stream, a);
       break;
   }
   return hipGetLastError();
 }
 
-template <bool QF32>
+template <bool QF32, bool PLANNED>
 hipError_t launch_q(const MlaArgs& a, MlaOut mode, int heads_per_wave, uint32_t blocks,
                     hipStream_t stream) {
   switch (heads_per_wave) {
-    case 16: return launch_g<2, QF32>(a, mode, blocks, stream);
-    case 32: return launch_g<4, QF32>(a, mode, blocks, stream);
+    case 16: return launch_g<2, QF32, PLANNED>(a, mode, blocks, stream);
+    case 32: return launch_g<4, QF32, PLANNED>(a, mode, blocks, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -333,8 +364,11 @@ hipError_t launch_mla(const MlaArgs& a, MlaOut mode, int heads_per_wave, hipStre
   if (blocks == 0) return hipSuccess;
   // the kernel numbers waves (block * waves per block + wave) in 32 bits
   if (blocks * kWavesPerBlock > 0xffffffffull) return hipErrorInvalidValue;
-  return a.q_out_f32 ? launch_q<true>(a, mode, heads_per_wave, (uint32_t)blocks, stream)
-                     : launch_q<false>(a, mode, heads_per_wave, (uint32_t)blocks, stream);
+  if (a.plan != nullptr)
+    return a.q_out_f32 ? launch_q<true, true>(a, mode, heads_per_wave, (uint32_t)blocks, stream)
+                       : launch_q<false, true>(a, mode, heads_per_wave, (uint32_t)blocks, stream);
+  return a.q_out_f32 ? launch_q<true, false>(a, mode, heads_per_wave, (uint32_t)blocks, stream)
+                     : launch_q<false, false>(a, mode, heads_per_wave, (uint32_t)blocks, stream);
 }
 
 }  // namespace pkv

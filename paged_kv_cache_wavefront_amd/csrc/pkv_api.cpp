@@ -83,11 +83,15 @@ float* k_scales_of(const pkv_paged_cache* c, uint32_t layer_idx, pkv::KMode km) 
   return c->scales;
 }
 
-// Both MLA entry points: the latent row from kv_latent, or (in_place) from
-// the bf16 cache row it is written back to.
+// The latent row comes from kv_latent, or (in_place) from the bf16 cache row
+// it is written back to.
+// Both MLA entry points and the planned form: placement from the ragged
+// batch (input_row_offsets, the cache's lengths and page table) or, when
+// `planned`, from token_plan alone.
 int mla_entry(void* q_rope_out, int64_t qo_tok_stride, int64_t qo_head_stride,
               const void* q_rope, int64_t qi_tok_stride, int64_t qi_head_stride,
-              const void* kv_latent, int64_t kv_row_stride, bool in_place,
+              const void* kv_latent, int64_t kv_row_stride, bool in_place, bool planned,
+              const uint32_t* token_plan,
               const uint32_t* input_row_offsets, uint32_t batch_size, uint32_t total_tokens,
               uint32_t num_heads, uint32_t rope_dim, uint32_t kv_norm_dim,
               const float* freqs_cis, uint32_t max_seq_len, const void* gamma, float epsilon,
@@ -110,16 +114,18 @@ int mla_entry(void* q_rope_out, int64_t qo_tok_stride, int64_t qo_head_stride,
   else
     return PKV_ERR_DTYPE;
   if (in_place && mode != pkv::MlaOut::Bf16InPlace) return PKV_ERR_DTYPE;
-  if (total_tokens > 0 && batch_size == 0) return PKV_ERR_SHAPE;
+  if (!planned && total_tokens > 0 && batch_size == 0) return PKV_ERR_SHAPE;
   if (max_seq_len == 0) return PKV_ERR_SHAPE;
   CacheView view{};
-  int st = check_cache(kv_cache, layer_idx, batch_size, &view);
+  // the planned form reads neither the cache lengths nor the page table
+  int st = check_cache(kv_cache, layer_idx, planned ? 0u : batch_size, &view);
   if (st != PKV_OK) return st;
   if (total_tokens == 0) return PKV_OK;
 
-  if (input_row_offsets == nullptr || freqs_cis == nullptr || gamma == nullptr ||
-      (!in_place && kv_latent == nullptr))
+  if ((planned ? token_plan == nullptr : input_row_offsets == nullptr) ||
+      freqs_cis == nullptr || gamma == nullptr || (!in_place && kv_latent == nullptr))
     return PKV_ERR_NULL;
+  if (planned && !aligned16(token_plan)) return PKV_ERR_ALIGN;
   if (num_heads > 0 && (q_rope == nullptr || q_rope_out == nullptr)) return PKV_ERR_NULL;
   const bool fp8 = mode == pkv::MlaOut::Fp8PerTensor || mode == pkv::MlaOut::Fp8PerToken;
   if (fp8 && kv_cache->scales == nullptr) return PKV_ERR_NULL;
@@ -141,8 +147,9 @@ int mla_entry(void* q_rope_out, int64_t qo_tok_stride, int64_t qo_head_stride,
   a.qi_head = qi_head_stride;
   a.latent = in_place ? nullptr : static_cast<const uint16_t*>(kv_latent);
   a.kv_row = in_place ? 0 : kv_row_stride;
-  a.offsets = input_row_offsets;
-  a.batch = batch_size;
+  a.offsets = planned ? nullptr : input_row_offsets;
+  a.batch = planned ? 0u : batch_size;
+  a.plan = planned ? token_plan : nullptr;
   a.total_tokens = total_tokens;
   a.num_heads = num_heads;
   const int hpw = (int)pkv::mla_heads_per_wave(num_heads);
@@ -187,9 +194,51 @@ int mla_rope_rmsnorm_quant(void* q_rope_out, int64_t qo_tok_stride, int64_t qo_h
                            const void* gamma, float epsilon, const pkv_paged_cache* kv_cache,
                            uint32_t layer_idx, int32_t q_out_dtype, void* stream) {
   return mla_entry(q_rope_out, qo_tok_stride, qo_head_stride, q_rope, qi_tok_stride,
-                   qi_head_stride, kv_latent, kv_row_stride, false, input_row_offsets,
-                   batch_size, total_tokens, num_heads, rope_dim, kv_norm_dim, freqs_cis,
-                   max_seq_len, gamma, epsilon, kv_cache, layer_idx, q_out_dtype, stream);
+                   qi_head_stride, kv_latent, kv_row_stride, false, false, nullptr,
+                   input_row_offsets, batch_size, total_tokens, num_heads, rope_dim,
+                   kv_norm_dim, freqs_cis, max_seq_len, gamma, epsilon, kv_cache, layer_idx,
+                   q_out_dtype, stream);
+}
+
+int pkv_token_plan(uint32_t* token_plan, const uint32_t* input_row_offsets,
+                   uint32_t batch_size, uint32_t total_tokens, const pkv_paged_cache* cache,
+                   void* stream) {
+  if (cache == nullptr) return PKV_ERR_NULL;
+  if (cache->num_pages == 0 || cache->page_size == 0 || cache->page_table_stride == 0)
+    return PKV_ERR_SHAPE;
+  if (total_tokens > 0 && batch_size == 0) return PKV_ERR_SHAPE;
+  if (total_tokens == 0) return PKV_OK;
+  if (token_plan == nullptr || input_row_offsets == nullptr || cache->cache_lengths == nullptr ||
+      cache->page_table == nullptr)
+    return PKV_ERR_NULL;
+  if (!aligned16(token_plan)) return PKV_ERR_ALIGN;
+  pkv::PlanArgs a{};
+  a.plan = token_plan;
+  a.offsets = input_row_offsets;
+  a.batch = batch_size;
+  a.total_tokens = total_tokens;
+  a.cache_lengths = cache->cache_lengths;
+  a.page_table = cache->page_table;
+  a.pt_stride = cache->page_table_stride;
+  a.num_pages = cache->num_pages;
+  a.page_size = cache->page_size;
+  return launch_status(pkv::launch_plan(a, static_cast<hipStream_t>(stream)));
+}
+
+int mla_rope_rmsnorm_quant_planned(void* q_rope_out, int64_t qo_tok_stride,
+                                   int64_t qo_head_stride, const void* q_rope,
+                                   int64_t qi_tok_stride, int64_t qi_head_stride,
+                                   const void* kv_latent, int64_t kv_row_stride,
+                                   const uint32_t* token_plan, uint32_t total_tokens,
+                                   uint32_t num_heads, uint32_t rope_dim, uint32_t kv_norm_dim,
+                                   const float* freqs_cis, uint32_t max_seq_len,
+                                   const void* gamma, float epsilon,
+                                   const pkv_paged_cache* kv_cache, uint32_t layer_idx,
+                                   int32_t q_out_dtype, void* stream) {
+  return mla_entry(q_rope_out, qo_tok_stride, qo_head_stride, q_rope, qi_tok_stride,
+                   qi_head_stride, kv_latent, kv_row_stride, false, true, token_plan, nullptr,
+                   0, total_tokens, num_heads, rope_dim, kv_norm_dim, freqs_cis, max_seq_len,
+                   gamma, epsilon, kv_cache, layer_idx, q_out_dtype, stream);
 }
 
 int mla_rope_rmsnorm_inplace(void* q_rope_out, int64_t qo_tok_stride, int64_t qo_head_stride,
@@ -200,9 +249,9 @@ int mla_rope_rmsnorm_inplace(void* q_rope_out, int64_t qo_tok_stride, int64_t qo
                              const void* gamma, float epsilon, const pkv_paged_cache* kv_cache,
                              uint32_t layer_idx, int32_t q_out_dtype, void* stream) {
   return mla_entry(q_rope_out, qo_tok_stride, qo_head_stride, q_rope, qi_tok_stride,
-                   qi_head_stride, nullptr, 0, true, input_row_offsets, batch_size,
-                   total_tokens, num_heads, rope_dim, kv_norm_dim, freqs_cis, max_seq_len,
-                   gamma, epsilon, kv_cache, layer_idx, q_out_dtype, stream);
+                   qi_head_stride, nullptr, 0, true, false, nullptr, input_row_offsets,
+                   batch_size, total_tokens, num_heads, rope_dim, kv_norm_dim, freqs_cis,
+                   max_seq_len, gamma, epsilon, kv_cache, layer_idx, q_out_dtype, stream);
 }
 
 int qk_rope_paged_ragged(void* q_out, int64_t qo_tok_stride, int64_t qo_head_stride,

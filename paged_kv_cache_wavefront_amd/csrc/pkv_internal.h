@@ -47,12 +47,27 @@ struct MlaArgs {
   const float* tensor_scale;   // per-tensor mode: device scalar
   float* token_scales;         // per-token mode: this layer's [pages][page_size][heads]
   CacheView cache;
+  const uint32_t* plan;        // [total_tokens][4] (page, offset, position, placed), or
+                               // null: placement from offsets, lengths and page table
 };
 
 // Heads per MLA wave for a q with `heads` heads (16 or 32); launch_mla takes
 // that value.
 uint32_t mla_heads_per_wave(uint32_t heads);
 hipError_t launch_mla(const MlaArgs& a, MlaOut mode, int heads_per_wave, hipStream_t stream);
+
+// Per-token placement of a ragged batch (token_plan.hip).
+struct PlanArgs {
+  uint32_t* plan;                // [total_tokens][4] written
+  const uint32_t* offsets;
+  uint32_t batch;
+  uint32_t total_tokens;
+  const uint32_t* cache_lengths;
+  const uint32_t* page_table;
+  uint32_t pt_stride, num_pages, page_size;
+};
+
+hipError_t launch_plan(const PlanArgs& a, hipStream_t stream);
 
 struct QkArgs {
   uint16_t* q_out;

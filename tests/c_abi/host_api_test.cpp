@@ -27,6 +27,7 @@ KMode g_norm_mode;
 GatherArgs g_gather;
 GatherKind g_gather_kind;
 bool g_gather_per_token;
+PlanArgs g_plan;
 }  // namespace
 
 uint32_t mla_heads_per_wave(uint32_t heads) { return heads > 16 ? 32 : 16; }
@@ -51,6 +52,10 @@ hipError_t launch_kv_norm(const KvNormArgs& a, bool mbc, KMode km, hipStream_t) 
 }
 hipError_t launch_gather(const GatherArgs& a, GatherKind kind, bool per_token, hipStream_t) {
   ++g_calls; g_gather = a; g_gather_kind = kind; g_gather_per_token = per_token;
+  return hipSuccess;
+}
+hipError_t launch_plan(const PlanArgs& a, hipStream_t) {
+  ++g_calls; g_plan = a;
   return hipSuccess;
 }
 }  // namespace pkv
@@ -268,6 +273,42 @@ static void fuzz(int iters) {
 
 int main() {
   using namespace pkv;
+  // --- token plan and the planned MLA step
+  {
+    pkv_paged_cache c = latent_cache(PKV_DTYPE_FP8_E4M3FN, PKV_SCALE_PER_TENSOR, 7);
+    uint32_t* plan = static_cast<uint32_t*>(P(40960));
+    const uint32_t* offs = static_cast<const uint32_t*>(P(28672));
+    int before = g_calls;
+    EXPECT(pkv_token_plan(plan, offs, 2, 9, &c, nullptr) == PKV_OK && g_calls == before + 1);
+    EXPECT(g_plan.plan == plan && g_plan.offsets == offs && g_plan.batch == 2);
+    EXPECT(g_plan.total_tokens == 9 && g_plan.cache_lengths == c.cache_lengths);
+    EXPECT(g_plan.page_table == c.page_table && g_plan.pt_stride == 4);
+    EXPECT(g_plan.num_pages == 7 && g_plan.page_size == 16);
+    before = g_calls;
+    EXPECT(pkv_token_plan(plan, offs, 2, 0, &c, nullptr) == PKV_OK);
+    EXPECT(pkv_token_plan(plan + 1, offs, 2, 9, &c, nullptr) == PKV_ERR_ALIGN);
+    EXPECT(pkv_token_plan(plan, offs, 0, 9, &c, nullptr) == PKV_ERR_SHAPE);
+    EXPECT(g_calls == before);
+    // the planned step: no lengths or page table needed, plan passed through
+    c.cache_lengths = nullptr;
+    c.page_table = nullptr;
+    EXPECT(mla_rope_rmsnorm_quant_planned(P(16384), 40 * 64, 64, P(20480), 40 * 64, 64,
+                                          P(24576), 576, plan, 5, 40, 64, 512,
+                                          static_cast<const float*>(P(32768)), 64, P(36864),
+                                          1e-6f, &c, 1, PKV_DTYPE_BF16, nullptr) == PKV_OK);
+    EXPECT(g_calls == before + 1 && g_mla.plan == plan && g_mla.offsets == nullptr);
+    EXPECT(g_mla.batch == 0 && g_mla.total_tokens == 5 && g_mla.chunks == 2);
+    EXPECT(g_mla_mode == MlaOut::Fp8PerTensor);
+    EXPECT(g_mla.cache.layer_base == static_cast<char*>(c.data) + c.layer_stride);
+    EXPECT(mla_rope_rmsnorm_quant_planned(P(16384), 40 * 64, 64, P(20480), 40 * 64, 64,
+                                          P(24576), 576, plan + 2, 5, 40, 64, 512,
+                                          static_cast<const float*>(P(32768)), 64, P(36864),
+                                          1e-6f, &c, 1, PKV_DTYPE_BF16, nullptr) ==
+           PKV_ERR_ALIGN);
+    // the batch form never carries a plan
+    pkv_paged_cache b = latent_cache(PKV_DTYPE_FP8_E4M3FN, PKV_SCALE_PER_TENSOR, 7);
+    EXPECT(mla(&b, 5, 40, PKV_DTYPE_BF16) == PKV_OK && g_mla.plan == nullptr);
+  }
   // --- MLA: per-token fp8, 40 heads, layer 1 of 2
   {
     pkv_paged_cache c = latent_cache(PKV_DTYPE_FP8_E4M3FN, PKV_SCALE_PER_TOKEN, 7);

@@ -251,11 +251,13 @@ def written_rows(case) -> np.ndarray:
     return mask
 
 
-def compare_mla(case, gpu, orc_res, small_case_floor: int = 0) -> dict:
+def compare_mla(case, gpu, orc_res, small_case_floor: int = 0, rows=None) -> dict:
     """GPU results against the oracle's under the parity bars.  With
     small_case_floor = k, the fraction bars allow at least k differing values
     (for cases of a few hundred values, where one near-tie is already more
-    than 0.1 %); the per-value bars (1 step, fp8 near-ties only) still hold."""
+    than 0.1 %); the per-value bars (1 step, fp8 near-ties only) still hold.
+    rows: mask [L, P, S] of the cache rows the step writes (default: the new
+    tokens' slots under the case's page table)."""
     q_g, cache_g, ts_g, _ = gpu
     q_o, cache_o, ts_o, pre = orc_res
 
@@ -269,7 +271,7 @@ def compare_mla(case, gpu, orc_res, small_case_floor: int = 0) -> dict:
     else:
         stats = {"q": check_bf16(q_g, q_o, "q_rope_output",
                                  max_frac=cap(BF16_MAX_DIFF_FRAC, q_g.size))}
-    rows = written_rows(case)
+    rows = written_rows(case) if rows is None else rows
     # untouched rows: bit-exact against the starting pool (and the oracle's)
     assert np.array_equal(cache_g[~rows], case.cache[~rows]), "cache bytes outside new rows changed"
     assert np.array_equal(cache_o[~rows], case.cache[~rows]), "oracle changed bytes outside new rows"

@@ -32,6 +32,7 @@ def pkv():
 
 def test_header_declares_entry_points():
     assert declared_functions() == sorted(["mla_rope_rmsnorm_quant", "mla_rope_rmsnorm_inplace",
+                                           "pkv_token_plan", "mla_rope_rmsnorm_quant_planned",
                                            "qk_rope_paged_ragged", "rms_norm_kv_cache_paged",
                                            "mla_gather_latent_paged", "pkv_status_string",
                                            "pkv_stream_copy"])
@@ -151,6 +152,54 @@ def test_mla_inplace_validation(pkv):
     assert call_mla_inplace(pkv, mla_cache(pkv, **bf16), q=FAKE + 8) == ALIGN
     assert call_mla_inplace(pkv, mla_cache(pkv, **bf16, slot_stride=580)) == ALIGN
     assert call_mla_inplace(pkv, mla_cache(pkv, **bf16), qo_dtype=pkv.PKV_DTYPE_FP8_E4M3FN) == DTYPE
+
+
+def call_plan(pkv, cache, plan=FAKE, T=16, batch=2, offsets=FAKE):
+    lib = pkv.library()
+    cp = None if cache is None else ctypes.byref(cache)
+    return lib.pkv_token_plan(plan, offsets, batch, T, cp, None)
+
+
+def test_token_plan_validation(pkv):
+    assert call_plan(pkv, None) == NULL
+    assert call_plan(pkv, mla_cache(pkv), plan=None) == NULL
+    assert call_plan(pkv, mla_cache(pkv), offsets=None) == NULL
+    assert call_plan(pkv, mla_cache(pkv, cache_lengths=None)) == NULL
+    assert call_plan(pkv, mla_cache(pkv, page_table=None)) == NULL
+    assert call_plan(pkv, mla_cache(pkv), plan=FAKE + 4) == ALIGN
+    assert call_plan(pkv, mla_cache(pkv), batch=0) == SHAPE
+    assert call_plan(pkv, mla_cache(pkv, page_size=0)) == SHAPE
+    assert call_plan(pkv, mla_cache(pkv, num_pages=0)) == SHAPE
+    assert call_plan(pkv, mla_cache(pkv, page_table_stride=0)) == SHAPE
+    # the pool is not read: no data pointer needed; nothing to do for no tokens
+    assert call_plan(pkv, mla_cache(pkv), T=0, batch=0) == OK
+    assert call_plan(pkv, mla_cache(pkv, data=None), T=0) == OK
+
+
+def call_mla_planned(pkv, cache, T=16, H=4, R=64, Dn=512, plan=FAKE, q=FAKE, lat=FAKE,
+                     layer=1, max_seq=64, qo_dtype=0):
+    lib = pkv.library()
+    cp = None if cache is None else ctypes.byref(cache)
+    return lib.mla_rope_rmsnorm_quant_planned(FAKE, 4 * 64, R, q, 4 * 64, R, lat, Dn + R, plan,
+                                              T, H, R, Dn, FAKE, max_seq, FAKE, 1e-6, cp, layer,
+                                              qo_dtype, None)
+
+
+def test_mla_planned_validation(pkv):
+    assert call_mla_planned(pkv, None) == NULL
+    assert call_mla_planned(pkv, mla_cache(pkv), plan=None) == NULL
+    assert call_mla_planned(pkv, mla_cache(pkv), plan=FAKE + 8) == ALIGN
+    assert call_mla_planned(pkv, mla_cache(pkv), lat=None) == NULL
+    assert call_mla_planned(pkv, mla_cache(pkv), R=32) == SHAPE
+    assert call_mla_planned(pkv, mla_cache(pkv), layer=2) == RANGE
+    assert call_mla_planned(pkv, mla_cache(pkv), max_seq=0) == SHAPE
+    assert call_mla_planned(pkv, mla_cache(pkv, scales=None)) == NULL
+    assert call_mla_planned(pkv, mla_cache(pkv, dtype=pkv.PKV_DTYPE_BF16)) == DTYPE
+    assert call_mla_planned(pkv, mla_cache(pkv), qo_dtype=9) == DTYPE
+    # placement comes from the plan: lengths and page table may be absent
+    assert call_mla_planned(pkv, mla_cache(pkv, cache_lengths=None, page_table=None),
+                            T=0) == OK
+    assert call_mla_planned(pkv, mla_cache(pkv), T=0) == OK
 
 
 def kcache(pkv, **kw):
@@ -307,6 +356,14 @@ def test_headers_compile_as_c_and_cxx(tmp_path):
                    " const float*, uint32_t, const void*, float, const pkv_paged_cache*, uint32_t,"
                    " int32_t, void*) = mla_rope_rmsnorm_quant;\n"
                    "  const char* (*f2)(int) = pkv_status_string;\n"
+                   "  int (*f4)(uint32_t*, const uint32_t*, uint32_t, uint32_t,"
+                   " const pkv_paged_cache*, void*) = pkv_token_plan;\n"
+                   "  int (*f5)(void*, int64_t, int64_t, const void*, int64_t, int64_t,"
+                   " const void*, int64_t, const uint32_t*, uint32_t, uint32_t, uint32_t,"
+                   " uint32_t, const float*, uint32_t, const void*, float,"
+                   " const pkv_paged_cache*, uint32_t, int32_t, void*) ="
+                   " mla_rope_rmsnorm_quant_planned;\n"
+                   "  (void)f4; (void)f5;\n"
                    "  int (*f3)(const void*, void*, uint64_t, uint32_t, void*) = pkv_stream_copy;\n"
                    "  (void)f1; (void)f2; (void)f3;\n"
                    "  return 0;\n}\n")
