@@ -14,7 +14,9 @@ sets).  Also reported: 20 isolated launches after a 512 MiB read that
 flushes the caches (``cold_us_p10_p50_p90``); a plain streaming copy timed in
 the same run (``measured_copy``); and (``siblings``) the other workloads and
 entry points, each timed the same way -- MLA decode (256 x 1 token, 128
-heads), mixed prefill + decode with per-token scales (16 heads), the same
+heads), mixed prefill + decode with per-token scales (16 heads), both of them
+again placed by a token plan built once before the timed launches
+(mla_rope_rmsnorm_quant_planned; the plan build's own time beside them), the same
 prefill batch in place on a bf16 latent cache (mla_rope_rmsnorm_inplace), the
 Llama-shaped paged-ragged Q/K RoPE with fused per-head K norm, the in-place
 K-cache RMSNorm and the paged latent gather.
@@ -51,6 +53,8 @@ COMMON_SOURCES = ("pkv_device.h", "pkv_internal.h")
 KERNEL_OF = {"mla_prefill": "mla_rope_rmsnorm_quant.hip", "mla_decode": "mla_rope_rmsnorm_quant.hip",
              "mla_mixed": "mla_rope_rmsnorm_quant.hip", "mla_tiny": "mla_rope_rmsnorm_quant.hip",
              "mla_prefill_inplace": "mla_rope_rmsnorm_quant.hip",
+             "mla_decode_planned": "mla_rope_rmsnorm_quant.hip",
+             "mla_mixed_planned": "mla_rope_rmsnorm_quant.hip",
              "qk_generic": "qk_rope_paged_ragged.hip", "kv_norm": "rms_norm_kv_cache_paged.hip",
              "gather": "mla_gather_latent_paged.hip"}
 
@@ -68,12 +72,13 @@ def log(*a):
 
 # -- algorithmic bytes (what the method must move, read + written) ---------------------
 
-def mla_bytes(case) -> int:
+def mla_bytes(case, planned: bool = False) -> int:
     """q in + q out (2 x H x R x 2) + latent row in (W x 2, from its buffer or,
     in place, from the cache) + cache row out (W x 1 fp8 / W x 2 bf16, + 4 for
     a per-token scale) per token; once per launch: freqs rows of the distinct
     positions (R x 4 each), gamma, offsets, prior lengths, the page-table
-    entries read, the per-tensor scale."""
+    entries read, the per-tensor scale.  Planned: a 16-byte plan entry per
+    token replaces the offsets, prior lengths and page-table entries."""
     T, H, R, W = case.T, case.H, case.R, case.latent.shape[1]
     out_b = 2 if case.cache.dtype == np.uint16 else 1
     per_tok = 2 * H * R * 2 + W * 2 + W * out_b + (4 if case.scale_mode == "per_token" else 0)
@@ -84,9 +89,20 @@ def mla_bytes(case) -> int:
     pages_read = len({(b, int(p) // S) for b, (c, n) in enumerate(
         zip(case.cache_lengths, np.diff(case.row_offsets.astype(np.int64))))
         for p in range(int(c), int(c) + int(n))})
-    shared = (len(np.unique(pos)) * R * 4 + case.Dn * 2 + (case.B + 1) * 4 + case.B * 4
-              + 4 * pages_read + (4 if case.scale_mode == "per_tensor" else 0))
+    chain = 16 * T if planned else (case.B + 1) * 4 + case.B * 4 + 4 * pages_read
+    shared = (len(np.unique(pos)) * R * 4 + case.Dn * 2 + chain
+              + (4 if case.scale_mode == "per_tensor" else 0))
     return T * per_tok + shared
+
+
+def plan_bytes(case) -> int:
+    """pkv_token_plan: offsets, prior lengths and the page-table entries read,
+    16 bytes written per token."""
+    S = case.meta["page_size"]
+    pages_read = len({(b, int(p) // S) for b, (c, n) in enumerate(
+        zip(case.cache_lengths, np.diff(case.row_offsets.astype(np.int64))))
+        for p in range(int(c), int(c) + int(n))})
+    return (case.B + 1) * 4 + case.B * 4 + 4 * pages_read + 16 * case.T
 
 
 def qk_bytes(case, with_norm: bool) -> int:
@@ -282,6 +298,36 @@ def run_workload(name, steps, warmup):
         how = f"{n} sets of q, q_out and bf16 cache pool"
         r = measure(cycle(fns), case.T, mla_bytes(case), steps, warmup)
         label = name
+    elif name.endswith("_planned"):
+        # one plan per batch layout, built before the timed region (every
+        # layer of a model step reuses it); the plan build is timed on its own
+        case = workloads.NAMED[name[: -len("_planned")]]()
+        dev = gh.MlaDevice(case)
+        plan = torch.empty((case.T, 4), dtype=torch.int32, device="cuda")
+        pkv.pkv_token_plan(plan, dev.offsets, dev.desc)
+        n = rotation_count(case.q.size * 2, case.q.size * 2, cap=256)
+        outs = [dev.q_out] + [torch.empty_like(dev.q_out) for _ in range(n - 1)]
+
+        def make(o):
+            return lambda: pkv.mla_rope_rmsnorm_quant_planned(o, dev.q_in, dev.latent, plan,
+                                                              dev.freqs, dev.gamma,
+                                                              case.epsilon, dev.desc,
+                                                              case.layer_idx)
+        fns = [make(o) for o in outs]
+        plans = [torch.empty_like(plan) for _ in range(4)]
+
+        def make_plan(p):
+            return lambda: pkv.pkv_token_plan(p, dev.offsets, dev.desc)
+        build = measure(cycle([make_plan(p) for p in plans]), case.T, plan_bytes(case), steps,
+                        warmup)
+        devs = (dev, outs, plan, plans)
+        how = (f"{n} q_out buffers (one cache pool and one plan; the new rows are "
+               f"{case.T * 576} bytes)")
+        r = measure(cycle(fns), case.T, mla_bytes(case, planned=True), steps, warmup)
+        r["plan_build"] = {"entry_point": "pkv_token_plan", "timed_as": "hip graph replay",
+                           "us": round(build["graph_avg"] * 1e6, 2),
+                           "bytes": plan_bytes(case)}
+        label = f"{name} (plan built once, outside the timed launches)"
     elif name.startswith("mla_"):
         case = workloads.NAMED[name]()
         q_out_bytes = case.q.size * 2
@@ -370,6 +416,8 @@ def measure_siblings(main, steps, warmup):
     out = {}
     for name, entry in (("mla_decode", "mla_rope_rmsnorm_quant"),
                         ("mla_mixed", "mla_rope_rmsnorm_quant"),
+                        ("mla_decode_planned", "mla_rope_rmsnorm_quant_planned"),
+                        ("mla_mixed_planned", "mla_rope_rmsnorm_quant_planned"),
                         ("mla_prefill_inplace", "mla_rope_rmsnorm_inplace"),
                         ("qk_generic", "qk_rope_paged_ragged"),
                         ("kv_norm", "rms_norm_kv_cache_paged"),
@@ -380,6 +428,8 @@ def measure_siblings(main, steps, warmup):
         r, label, _ = run_workload(name, steps, warmup)
         out[name] = {"entry_point": entry, **summarize(label, r, steps, use_graph=True),
                      "traffic": profiled_traffic(name)}
+        if "plan_build" in r:
+            out[name]["plan_build"] = r["plan_build"]
     return out
 
 
@@ -550,7 +600,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mla_prefill",
                     choices=["mla_prefill", "mla_decode", "mla_mixed", "mla_tiny",
-                             "mla_prefill_inplace", "qk_generic", "kv_norm", "gather"])
+                             "mla_prefill_inplace", "mla_decode_planned", "mla_mixed_planned",
+                             "qk_generic", "kv_norm", "gather"])
     ap.add_argument("--no-siblings", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
@@ -579,7 +630,8 @@ def main():
     siblings = None if args.no_siblings else measure_siblings(
         args.workload, max(20, args.steps // 2), args.warmup)
     cpu = parity = None
-    if not args.no_cpu_baseline and args.workload.startswith("mla_"):
+    if (not args.no_cpu_baseline and args.workload.startswith("mla_")
+            and not args.workload.endswith("_planned")):
         log("[bench] cpu baseline (oracle)")
         cpu, oracle_out = cpu_baseline(case)
         if args.workload != "mla_prefill_inplace":
