@@ -170,9 +170,9 @@ static void fuzz(int iters) {
   const uint32_t dims[] = {64, 80, 96, 128, 256, 72, 512};
   int launched = 0, refused = 0;
   for (int it = 0; it < iters; ++it) {
-    const int entry = (int)(frand() % 5);
+    const int entry = (int)(frand() % 7);
     pkv_paged_cache c;
-    if (entry <= 1 || entry == 4) {
+    if (entry <= 1 || entry >= 4) {
       c = latent_cache(coin(2) ? PKV_DTYPE_BF16 : PKV_DTYPE_FP8_E4M3FN,
                        (int32_t)(frand() % 3), 1 + frand() % 16);
       if (entry == 1 || c.dtype == PKV_DTYPE_BF16) c.scale_mode = PKV_SCALE_NONE;
@@ -237,6 +237,25 @@ static void fuzz(int iters) {
                                      (int)(frand() % 2), (int)(frand() % 2), nullptr);
         break;
       }
+      case 5: {
+        const int64_t ts = (int64_t)H * 64 + (coin(10) ? 4 : 0);
+        const int32_t qdt = coin(10) ? (int32_t)(frand() % 4) : PKV_DTYPE_BF16;
+        const uint32_t* plan = coin(20) ? nullptr
+                                        : static_cast<const uint32_t*>(P(coin(20) ? 40964 : 40960));
+        st = mla_rope_rmsnorm_quant_planned(P(20480), ts, 64, q, ts, 64,
+                                            coin(20) ? nullptr : P(24576), coin(10) ? 580 : 576,
+                                            plan, T, H, coin(10) ? 32 : 64, coin(10) ? 256 : 512,
+                                            static_cast<const float*>(P(32768)),
+                                            1 + frand() % 9000, coin(30) ? nullptr : P(36864),
+                                            1e-6f, cp, layer, qdt, nullptr);
+        break;
+      }
+      case 6: {
+        uint32_t* plan = coin(20) ? nullptr : static_cast<uint32_t*>(P(coin(20) ? 40964 : 40960));
+        st = pkv_token_plan(plan, coin(20) ? nullptr : static_cast<const uint32_t*>(P(28672)), B,
+                            T, cp, nullptr);
+        break;
+      }
       case 4: {
         const int32_t odt = coin(2) ? PKV_DTYPE_BF16 : PKV_DTYPE_FP8_E4M3FN;
         const uint32_t W = cp ? cp->head_dim : 576;
@@ -255,14 +274,22 @@ static void fuzz(int iters) {
       EXPECT(st == PKV_OK && T > 0 && cp != nullptr);
       const char* base = nullptr;
       switch (entry) {
-        case 0: case 1: base = static_cast<const char*>(g_mla.cache.layer_base); break;
+        case 0: case 1: case 5: base = static_cast<const char*>(g_mla.cache.layer_base); break;
         case 2: base = static_cast<const char*>(g_qk.cache.layer_base); break;
         case 3: base = static_cast<const char*>(g_norm.cache.layer_base); break;
         case 4: base = static_cast<const char*>(g_gather.cache.layer_base); break;
       }
+      if (entry == 6) {
+        // the plan builder reads the lengths and page table, never the pool
+        EXPECT(g_plan.total_tokens == T && g_plan.batch == B && B > 0);
+        EXPECT(g_plan.page_table == cp->page_table && g_plan.page_size > 0);
+        EXPECT(((uintptr_t)g_plan.plan & 15u) == 0);
+        continue;
+      }
       const int64_t eb = cp->dtype == PKV_DTYPE_BF16 ? 2 : 1;
       EXPECT(base == static_cast<const char*>(cp->data) + (int64_t)layer * cp->layer_stride * eb);
       EXPECT(layer < cp->num_layers);
+      if (entry == 5) EXPECT(g_mla.plan != nullptr && g_mla.offsets == nullptr);
     } else {
       refused += st != PKV_OK;
     }

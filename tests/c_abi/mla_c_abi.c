@@ -6,8 +6,10 @@
  * ulp, cache codes within 1 step, at most 3 values of each differing, every
  * byte outside the new rows unchanged.  Then the same batch through
  * mla_rope_rmsnorm_inplace on a bf16 cache that holds the latent rows at the
- * new tokens' slots, against the oracle's in-place form.  Exit status 0 =
- * pass.
+ * new tokens' slots, against the oracle's in-place form.  Between the two,
+ * the batch through pkv_token_plan + mla_rope_rmsnorm_quant_planned on a fresh
+ * copy of the fp8 pool, which must write the batch form's bytes exactly.
+ * Exit status 0 = pass.
  */
 #include <hip/hip_runtime_api.h>
 #include <math.h>
@@ -176,6 +178,33 @@ int main(void) {
   printf("c-abi mla: T=%d q: %ld differ (max %ld ulp); cache: %ld differ (max %ld); "
          "oracle changed %ld bytes\n", T, q_diff, q_max, c_diff, c_max, rows_changed);
   int ok = q_max <= 1 && q_diff <= 3 && c_max <= 1 && c_diff <= 3 && rows_changed > 0;
+
+  /* planned: this batch's token plan, then the step placed by it */
+  void *d_plan, *d_cache_p, *d_qo_p;
+  CHECK(hipMalloc(&d_plan, sizeof(uint32_t) * 4 * T));
+  CHECK(hipMalloc(&d_cache_p, cache_bytes));
+  CHECK(hipMalloc(&d_qo_p, sizeof(uint16_t) * T * H * R));
+  CHECK(hipMemcpy(d_cache_p, cache0, cache_bytes, hipMemcpyHostToDevice));
+  c.data = d_cache_p;
+  int st3 = pkv_token_plan((uint32_t*)d_plan, d_off, B, (uint32_t)T, &c, NULL);
+  if (st3 == PKV_OK)
+    st3 = mla_rope_rmsnorm_quant_planned(d_qo_p, (int64_t)H * R, R, d_q, (int64_t)H * R, R,
+                                         d_lat, W, (const uint32_t*)d_plan, (uint32_t)T, H, R,
+                                         DN, d_freqs, MAXSEQ, d_gamma, eps, &c, LAYER,
+                                         PKV_DTYPE_BF16, NULL);
+  if (st3 != PKV_OK) {
+    fprintf(stderr, "planned: %s\n", pkv_status_string(st3));
+    return 1;
+  }
+  CHECK(hipDeviceSynchronize());
+  uint16_t* q_p = malloc(sizeof(uint16_t) * T * H * R);
+  uint8_t* cache_p = malloc(cache_bytes);
+  CHECK(hipMemcpy(q_p, d_qo_p, sizeof(uint16_t) * T * H * R, hipMemcpyDeviceToHost));
+  CHECK(hipMemcpy(cache_p, d_cache_p, cache_bytes, hipMemcpyDeviceToHost));
+  const int same = memcmp(q_p, q_gpu, sizeof(uint16_t) * T * H * R) == 0 &&
+                   memcmp(cache_p, cache_gpu, cache_bytes) == 0;
+  printf("c-abi mla planned: %s\n", same ? "bit-identical to the batch form" : "DIFFERS");
+  ok = ok && same;
 
   /* in place: a bf16 cache holding each new token's latent row at its slot */
   const size_t n16 = (size_t)L * P * S * W;

@@ -43,6 +43,50 @@ def test_mla_graph_replays(name):
         del junk
 
 
+@pytest.mark.parametrize("name", ["mla_decode", "mla_mixed"])
+def test_planned_graph_replays(name):
+    """A model step as a caller would capture it: the plan build, then the
+    planned MLA step on two layers, all inside one graph; every replay (the
+    plan cleared between replays) equals the batch form run eagerly."""
+    import paged_kv_cache_wavefront_amd as pkv
+    case = workloads.NAMED[name]()
+    print(f"[graph] planned {name} T={case.T}", flush=True)
+    eager = gh.MlaDevice(case)
+    layers = range(case.cache.shape[0])
+    for layer in layers:
+        pkv.mla_rope_rmsnorm_quant(eager.q_out, eager.q_in, eager.latent, eager.offsets,
+                                   eager.freqs, eager.gamma, case.epsilon, eager.desc, layer)
+    want = eager.results()
+    dev = gh.MlaDevice(case)
+    plan = torch.zeros((case.T, 4), dtype=torch.int32, device="cuda")
+
+    def step():
+        pkv.pkv_token_plan(plan, dev.offsets, dev.desc)
+        for layer in layers:
+            pkv.mla_rope_rmsnorm_quant_planned(dev.q_out, dev.q_in, dev.latent, plan, dev.freqs,
+                                               dev.gamma, case.epsilon, dev.desc, layer)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()             # warm-up outside the graph
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        dev.q_out.zero_()                       # eager work between replays
+        plan.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        got = dev.results()
+        assert np.array_equal(got[0], want[0]), f"replay {rep}: q differs"
+        assert np.array_equal(got[1], want[1]), f"replay {rep}: cache differs"
+        if got[2] is not None:
+            assert np.array_equal(got[2].view(np.uint32), want[2].view(np.uint32))
+        assert got[3] == 0
+
+
 def test_qk_graph_replays():
     case = workloads.qk_generic()
     eager = gh.QkDevice(case)

@@ -61,6 +61,20 @@ def test_mla_random(orc, seed):
     gpu = dev.results()
     assert gpu[3] == 0
     _say(f"[rand-mla] {gh.compare_mla(case, gpu, gh.oracle_mla(orc, case, q_f32), 3)}")
+    # the planned form, with the plan of this batch, writes the same bits
+    import torch
+    import paged_kv_cache_wavefront_amd as pkv
+    pdev = gh.MlaDevice(case, layout, q_f32)
+    plan = torch.empty((case.T, 4), dtype=torch.int32, device=gh.DEV)
+    pkv.pkv_token_plan(plan, pdev.offsets, pdev.desc)
+    pkv.mla_rope_rmsnorm_quant_planned(pdev.q_out, pdev.q_in, pdev.latent, plan, pdev.freqs,
+                                       pdev.gamma, case.epsilon, pdev.desc, case.layer_idx)
+    planned = pdev.results()
+    for got, want in zip(planned[:3], gpu[:3]):
+        assert (got is None) == (want is None)
+        if got is not None:
+            assert np.array_equal(got.view(np.uint8), want.view(np.uint8)), "planned differs"
+    assert planned[3] == 0
 
 
 def _random_qk(rng, seed):
