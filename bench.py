@@ -160,10 +160,12 @@ def time_launches(fn, steps: int, warmup: int, spread_samples: int = 20):
     return wall, avg, durs
 
 
-def time_graph(fn, steps: int, warmup: int):
-    """Seconds per launch when `steps` launches are captured in one HIP graph
-    (torch.cuda.CUDAGraph) and replayed: the kernels back to back with no
-    host launch overhead between them."""
+def time_graph(fn, steps: int, warmup: int, replays: int = 5, min_launches: int = 100):
+    """Seconds per launch when max(steps, min_launches) launches are captured
+    in one HIP graph (torch.cuda.CUDAGraph) and replayed: the kernels back to
+    back with no host launch overhead between them.  The median over
+    `replays` replays, each bracketed by its own event pair (a few-microsecond
+    kernel needs the longer graph and the median to settle)."""
     import torch
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -172,18 +174,22 @@ def time_graph(fn, steps: int, warmup: int):
             fn()
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
+    n = max(steps, min_launches)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        for _ in range(steps):
+        for _ in range(n):
             fn()
     g.replay()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1e-3 / steps
+    times = []
+    for _ in range(replays):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e-3 / n)
+    return float(np.median(times))
 
 
 def profiled_traffic(name: str):
