@@ -333,6 +333,19 @@ def run_workload(name, steps, warmup):
         r["plan_build"] = {"entry_point": "pkv_token_plan", "timed_as": "hip graph replay",
                            "us": round(build["graph_avg"] * 1e6, 2),
                            "bytes": plan_bytes(case)}
+        # the batch form on the same buffers, the two graph-replay timings
+        # alternating (figures of separate runs drift by a few tenths of a us)
+        batch = cycle([(lambda o: lambda: pkv.mla_rope_rmsnorm_quant(
+            o, dev.q_in, dev.latent, dev.offsets, dev.freqs, dev.gamma, case.epsilon, dev.desc,
+            case.layer_idx))(o) for o in outs])
+        planned_fn = cycle(fns)
+        ab = {"batch": [], "planned": []}
+        for _ in range(3):
+            ab["batch"].append(time_graph(batch, steps, warmup))
+            ab["planned"].append(time_graph(planned_fn, steps, warmup))
+        r["vs_batch_form"] = {k: round(float(np.median(v)) * 1e6, 2) for k, v in ab.items()}
+        r["vs_batch_form"]["how"] = ("graph replay, batch and planned forms alternating, "
+                                     "median of 3 x 5 replays")
         label = f"{name} (plan built once, outside the timed launches)"
     elif name.startswith("mla_"):
         case = workloads.NAMED[name]()
@@ -436,6 +449,7 @@ def measure_siblings(main, steps, warmup):
                      "traffic": profiled_traffic(name)}
         if "plan_build" in r:
             out[name]["plan_build"] = r["plan_build"]
+            out[name]["vs_batch_form_us"] = r["vs_batch_form"]
     return out
 
 
