@@ -14,9 +14,10 @@ point of the method:
   "mla_graph" module page;
 * :func:`qk_rope_paged_ragged` -- page "generic_fused_qk_rope_bshd_paged_ragged";
 * :func:`rms_norm_kv_cache_paged` -- page "rms_norm_kv_cache_ragged_paged";
-* :func:`token_plan` and :func:`mla_rope_rmsnorm_quant_planned` -- the same
-  step's ragged / paged addressing written out once per batch layout, and the
-  step placed by it;
+* :func:`token_plan`, :func:`mla_rope_rmsnorm_quant_planned` and
+  :func:`rms_norm_kv_cache_planned` -- the ragged / paged addressing written
+  out once per batch layout, and the MLA step and the K-cache norm placed by
+  it;
 * :func:`mla_gather_latent_paged` -- the paged-to-contiguous latent copy and
   fp8 (de)quantisation step of mla_prefill_branch_fp8 ("mla_graph" page);
 * the bf16 and FP8 E4M3FN codecs and the RoPE / RMSNorm row steps, exposed so
@@ -87,6 +88,10 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.oracle_mla_rope_rmsnorm_quant_planned.argtypes = [
         _vp, ctypes.c_int, _vp, _vp, _vp, _i64, _vp, _i64, _vp, ctypes.c_float, _i64, _i64,
         _i64, _vp, ctypes.c_int, _i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_float, _vp]
+    lib.oracle_rms_norm_kv_cache_planned.restype = ctypes.c_int
+    lib.oracle_rms_norm_kv_cache_planned.argtypes = [
+        _vp, ctypes.c_int, ctypes.c_int, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _vp, _vp,
+        _i64, ctypes.c_float, ctypes.c_float, _i64, ctypes.c_int, ctypes.c_int]
     lib.oracle_mla_rope_rmsnorm_inplace.restype = ctypes.c_int
     lib.oracle_mla_rope_rmsnorm_inplace.argtypes = [
         _vp, ctypes.c_int, _vp, _vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp, ctypes.c_float,
@@ -369,6 +374,23 @@ class Oracle:
             float(weight_offset), int(total_seq_len),
             int(bool(multiply_before_cast)), int(bool(per_head_norm)))
         _check(rc, "rms_norm_kv_cache_paged")
+
+    def rms_norm_kv_cache_planned(self, k_cache, layer_idx, plan, gamma, epsilon,
+                                  weight_offset, total_seq_len, multiply_before_cast=True,
+                                  k_scale_mode="none", k_scales=None, per_head_norm=True):
+        """:meth:`rms_norm_kv_cache_paged` with each token t < total_seq_len
+        placed by ``plan`` (u32 [T, 4]: page, offset, position, placed flag)."""
+        L, P, S, Hkv, D = k_cache.shape
+        k_type = CACHE_BF16 if k_cache.dtype == np.uint16 else CACHE_FP8
+        mode = {"per_tensor": SCALE_PER_TENSOR, "per_token": SCALE_PER_TOKEN, "none": 0}[k_scale_mode]
+        if plan.ndim != 2 or plan.shape[1] != 4 or plan.shape[0] < total_seq_len:
+            raise ValueError("plan must be [>= total_seq_len, 4]")
+        rc = self.lib.oracle_rms_norm_kv_cache_planned(
+            _ptr(k_cache, k_cache.dtype), k_type, mode, _ptr(k_scales, np.float32),
+            L, P, S, Hkv, D, int(layer_idx), _ptr(plan, np.uint32),
+            _ptr(gamma, np.uint16), gamma.size, float(epsilon), float(weight_offset),
+            int(total_seq_len), int(bool(multiply_before_cast)), int(bool(per_head_norm)))
+        _check(rc, "rms_norm_kv_cache_planned")
 
 
 _DEFAULT: Oracle | None = None

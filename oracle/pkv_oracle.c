@@ -243,6 +243,19 @@ static int64_t page_of(const uint32_t* page_table, int64_t pt_stride,
  * latent = NULL is the in-place form (see oracle_mla_rope_rmsnorm_inplace):
  * each token's row x is read from its own slot of the bf16 cache.
  */
+/* True when a token plan entry (page, offset, position, placed) is marked
+ * placed and names a slot inside the pool. */
+static int plan_entry_placed(const uint32_t* e, int64_t num_pages, int64_t page_size) {
+  return !(e[3] == 0 || (int64_t)e[0] >= num_pages || (int64_t)e[1] >= page_size);
+}
+
+/* gamma + weight_offset of the K-cache norm, widened ([NORM]: weight_offset
+ * is added to gamma). */
+static void kv_norm_gamma(const uint16_t* gamma, int64_t n, float weight_offset, double* g) {
+  for (int64_t k = 0; k < n; ++k)
+    g[k] = oracle_bf16_decode(gamma[k]) + (double)weight_offset;
+}
+
 /* One token of the fused MLA step: q of token t rotated at position pos into
  * q_out, and the token's latent row (from the buffer, or in place from cache
  * row `row`) normalised, rotated and written to cache row `row` (row counts
@@ -393,10 +406,7 @@ int oracle_mla_rope_rmsnorm_quant_planned(
   int status = ORACLE_OK;
   for (int64_t t = 0; t < T; ++t) {
     const uint32_t* e = plan + 4 * t;
-    if (e[3] == 0 || (int64_t)e[0] >= num_pages || (int64_t)e[1] >= page_size) {
-      status = ORACLE_BAD_PAGE;
-      continue;
-    }
+    if (!plan_entry_placed(e, num_pages, page_size)) { status = ORACLE_BAD_PAGE; continue; }
     if ((int64_t)e[2] >= max_seq_len) { status = ORACLE_BAD_POSITION; continue; }
     const int64_t row = ((layer_idx * num_pages + e[0]) * page_size + e[1]);
     const int rc = mla_token(q_out, q_out_f32, q_in, latent, t, (int64_t)e[2], row, freqs, g,
@@ -621,6 +631,54 @@ int oracle_mla_gather_latent_paged(
  *   k_cache   bf16 bits [L][P][S][Hkv][D]
  *   gamma     bf16 bits [gamma_len]
  */
+/* The K-cache RMSNorm of one token whose rows sit at (page, off) of layer
+ * layer_idx: every head's first gamma_len columns normalised with g (gamma
+ * plus weight_offset, widened), in place. */
+static void kv_norm_token(void* k_cache, int k_type, int scale_mode, float* k_scales,
+                          int64_t num_pages, int64_t page_size, int64_t Hkv, int64_t D,
+                          int64_t layer_idx, int64_t page, int64_t off, const double* g,
+                          int64_t gamma_len, double eps, int multiply_before_cast,
+                          int per_head_norm) {
+  double a[1024];
+  double token_inv = 0.0;
+  if (!per_head_norm) {
+    /* Reading of per_head_norm = False (listed on the page, not
+     * described): one statistic over the first gamma_len columns of all
+     * heads of the token. */
+    double ss = 0.0;
+    for (int64_t h = 0; h < Hkv; ++h) {
+      const int64_t head = ((layer_idx * num_pages + page) * page_size + off) * Hkv + h;
+      const double ks = k_type == ORACLE_CACHE_FP8
+          ? (double)(scale_mode == ORACLE_SCALE_PER_TOKEN ? k_scales[head] : k_scales[0])
+          : 1.0;
+      load_k_row(k_cache, k_type, head * D, D, ks, a);
+      for (int64_t i = 0; i < gamma_len; ++i) ss += a[i] * a[i];
+    }
+    token_inv = 1.0 / sqrt(ss / (double)(Hkv * gamma_len) + eps);
+  }
+  for (int64_t h = 0; h < Hkv; ++h) {
+    const int64_t head = ((layer_idx * num_pages + page) * page_size + off) * Hkv + h;
+    const double ks = k_type == ORACLE_CACHE_FP8
+        ? (double)(scale_mode == ORACLE_SCALE_PER_TOKEN ? k_scales[head] : k_scales[0])
+        : 1.0;
+    load_k_row(k_cache, k_type, head * D, D, ks, a);
+    double inv = per_head_norm ? oracle_inv_rms(a, gamma_len, eps) : token_inv;
+    for (int64_t i = 0; i < gamma_len; ++i) {
+      if (multiply_before_cast) {
+        a[i] = a[i] * inv * g[i];
+      } else {  /* bf16 only: round the normalised value, then apply gamma */
+        a[i] = oracle_bf16_decode(oracle_bf16_encode(a[i] * inv)) * g[i];
+      }
+    }
+    /* only the normalised columns are written (per-token: the fresh scale
+     * covers the whole head, the other columns are re-encoded with it) */
+    const int per_token = k_type == ORACLE_CACHE_FP8 && scale_mode == ORACLE_SCALE_PER_TOKEN;
+    store_k_row(k_cache, k_type, scale_mode, head * D, D, a,
+                k_type == ORACLE_CACHE_FP8 ? k_scales[0] : 1.0f,
+                per_token ? &k_scales[head] : NULL, 0, per_token ? D : gamma_len);
+  }
+}
+
 int oracle_rms_norm_kv_cache_paged(
     void* k_cache, int k_type, int scale_mode, float* k_scales, int64_t num_layers,
     int64_t num_pages, int64_t page_size, int64_t Hkv, int64_t D, int64_t layer_idx,
@@ -631,10 +689,9 @@ int oracle_rms_norm_kv_cache_paged(
   if (gamma_len <= 0 || gamma_len > D || D > 1024 || layer_idx < 0 ||
       layer_idx >= num_layers || page_size <= 0)
     return ORACLE_BAD_ARG;
-  double a[1024], g[1024];
+  double g[1024];
   if (k_type == ORACLE_CACHE_FP8 && !multiply_before_cast) return ORACLE_BAD_ARG;
-  for (int64_t k = 0; k < gamma_len; ++k)
-    g[k] = oracle_bf16_decode(gamma[k]) + (double)weight_offset;
+  kv_norm_gamma(gamma, gamma_len, weight_offset, g);
   const double eps = (double)epsilon;
   int status = ORACLE_OK;
 
@@ -646,44 +703,40 @@ int oracle_rms_norm_kv_cache_paged(
                                    page_size, b, slot);
       if (page < 0) { status = ORACLE_BAD_PAGE; continue; }
       const int64_t off = slot % page_size;
-      double token_inv = 0.0;
-      if (!per_head_norm) {
-        /* Reading of per_head_norm = False (listed on the page, not
-         * described): one statistic over the first gamma_len columns of all
-         * heads of the token. */
-        double ss = 0.0;
-        for (int64_t h = 0; h < Hkv; ++h) {
-          const int64_t head = ((layer_idx * num_pages + page) * page_size + off) * Hkv + h;
-          const double ks = k_type == ORACLE_CACHE_FP8
-              ? (double)(scale_mode == ORACLE_SCALE_PER_TOKEN ? k_scales[head] : k_scales[0])
-              : 1.0;
-          load_k_row(k_cache, k_type, head * D, D, ks, a);
-          for (int64_t i = 0; i < gamma_len; ++i) ss += a[i] * a[i];
-        }
-        token_inv = 1.0 / sqrt(ss / (double)(Hkv * gamma_len) + eps);
-      }
-      for (int64_t h = 0; h < Hkv; ++h) {
-        const int64_t head = ((layer_idx * num_pages + page) * page_size + off) * Hkv + h;
-        const double ks = k_type == ORACLE_CACHE_FP8
-            ? (double)(scale_mode == ORACLE_SCALE_PER_TOKEN ? k_scales[head] : k_scales[0])
-            : 1.0;
-        load_k_row(k_cache, k_type, head * D, D, ks, a);
-        double inv = per_head_norm ? oracle_inv_rms(a, gamma_len, eps) : token_inv;
-        for (int64_t i = 0; i < gamma_len; ++i) {
-          if (multiply_before_cast) {
-            a[i] = a[i] * inv * g[i];
-          } else {  /* bf16 only: round the normalised value, then apply gamma */
-            a[i] = oracle_bf16_decode(oracle_bf16_encode(a[i] * inv)) * g[i];
-          }
-        }
-        /* only the normalised columns are written (per-token: the fresh scale
-         * covers the whole head, the other columns are re-encoded with it) */
-        const int per_token = k_type == ORACLE_CACHE_FP8 && scale_mode == ORACLE_SCALE_PER_TOKEN;
-        store_k_row(k_cache, k_type, scale_mode, head * D, D, a,
-                    k_type == ORACLE_CACHE_FP8 ? k_scales[0] : 1.0f,
-                    per_token ? &k_scales[head] : NULL, 0, per_token ? D : gamma_len);
-      }
+      kv_norm_token(k_cache, k_type, scale_mode, k_scales, num_pages, page_size, Hkv, D,
+                    layer_idx, page, off, g, gamma_len, eps, multiply_before_cast,
+                    per_head_norm);
     }
+  }
+  return status;
+}
+
+/*
+ * The K-cache RMSNorm with each token placed by a token plan
+ * (oracle_token_plan): token t < total_seq_len is normalised at page
+ * plan[t][0], offset plan[t][1]; an entry not marked placed, or with a page
+ * or offset outside the pool, is skipped (reported by the return value).
+ * Other arguments as for oracle_rms_norm_kv_cache_paged.
+ */
+int oracle_rms_norm_kv_cache_planned(
+    void* k_cache, int k_type, int scale_mode, float* k_scales, int64_t num_layers,
+    int64_t num_pages, int64_t page_size, int64_t Hkv, int64_t D, int64_t layer_idx,
+    const uint32_t* plan, const uint16_t* gamma, int64_t gamma_len, float epsilon,
+    float weight_offset, int64_t total_seq_len, int multiply_before_cast, int per_head_norm) {
+  if (gamma_len <= 0 || gamma_len > D || D > 1024 || layer_idx < 0 ||
+      layer_idx >= num_layers || page_size <= 0 || total_seq_len < 0)
+    return ORACLE_BAD_ARG;
+  double g[1024];
+  if (k_type == ORACLE_CACHE_FP8 && !multiply_before_cast) return ORACLE_BAD_ARG;
+  kv_norm_gamma(gamma, gamma_len, weight_offset, g);
+  const double eps = (double)epsilon;
+  int status = ORACLE_OK;
+  for (int64_t t = 0; t < total_seq_len; ++t) {
+    const uint32_t* e = plan + 4 * t;
+    if (!plan_entry_placed(e, num_pages, page_size)) { status = ORACLE_BAD_PAGE; continue; }
+    kv_norm_token(k_cache, k_type, scale_mode, k_scales, num_pages, page_size, Hkv, D,
+                  layer_idx, (int64_t)e[0], (int64_t)e[1], g, gamma_len, eps,
+                  multiply_before_cast, per_head_norm);
   }
   return status;
 }

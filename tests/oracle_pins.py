@@ -885,6 +885,69 @@ def pin_rms_norm_kv(orc):
                     assert np.array_equal(k, expect), "kvnorm touched other elements"
 
 
+def qk_token_plan(orc, case):
+    L, P, S = case.k_cache.shape[:3]
+    return orc.token_plan(case.T, case.row_offsets, case.cache_lengths, case.page_table, P, S)
+
+
+def pin_rms_norm_kv_planned(orc):
+    """The planned K-cache norm: with the plan of its own batch it writes the
+    batch form's bits (bf16 both cast orders and weight offsets, fp8 tensor and
+    token scales, per-head and per-token statistic, total_seq_len short of
+    the batch); with a free placement every placed cell is normalised against
+    torch rms_norm in fp64 and nothing else changes."""
+    def run_both(case, gamma, w, total, mbc, mode, scales, per_head):
+        plan = qk_token_plan(orc, case)
+        k_b, k_p = case.k_cache.copy(), case.k_cache.copy()
+        s_b = None if scales is None else scales.copy()
+        s_p = None if scales is None else scales.copy()
+        orc.rms_norm_kv_cache_paged(k_b, case.layer_idx, case.row_offsets, case.cache_lengths,
+                                    case.page_table, gamma, case.epsilon, w, total, mbc, mode,
+                                    s_b, per_head)
+        orc.rms_norm_kv_cache_planned(k_p, case.layer_idx, plan, gamma, case.epsilon, w, total,
+                                      mbc, mode, s_p, per_head)
+        assert np.array_equal(k_b, k_p), (case.name, mbc, w, total, mode, per_head)
+        if s_b is not None:
+            assert np.array_equal(s_b.view(np.uint32), s_p.view(np.uint32))
+    for case in small_qk_cases():
+        C = case.gamma.size if case.gamma is not None else 48
+        rng = np.random.Generator(np.random.PCG64(case.seed))
+        gamma = workloads.bf16_bits(rng.uniform(0.5, 1.5, C).astype(np.float32))
+        for mbc, w, total, per_head in ((True, 0.0, case.T, True), (False, 0.25, case.T, True),
+                                        (True, 0.25, max(case.T - 3, 0), False)):
+            run_both(case, gamma, w, total, mbc, "none", None, per_head)
+    for case in small_qk_fp8_cases():
+        gamma = case.gamma if case.gamma is not None else workloads.bf16_bits(
+            np.linspace(0.5, 1.5, case.k_cache.shape[-1]).astype(np.float32))
+        run_both(case, gamma, 0.0, case.T, True, case.k_scale_mode, case.k_scales, True)
+    # free placement on a bf16 case
+    case = next(iter(small_qk_cases()))
+    L, P, S, Hkv, D = case.k_cache.shape
+    C = D // 2
+    rng = np.random.default_rng(4040)
+    gamma = workloads.bf16_bits(rng.uniform(0.5, 1.5, C).astype(np.float32))
+    cells = rng.choice(P * S, size=case.T, replace=False)
+    plan = np.zeros((case.T, 4), np.uint32)
+    plan[:, 0], plan[:, 1], plan[:, 3] = cells // S, cells % S, 1
+    plan[::4, 3] = 0
+    k = case.k_cache.copy()
+    try:
+        orc.rms_norm_kv_cache_planned(k, case.layer_idx, plan, gamma, case.epsilon, 0.0, case.T)
+    except oracle.OracleError:
+        pass                                  # entries marked not placed were skipped
+    expect = case.k_cache.copy()
+    g = bf16_to_f64(gamma)
+    for t in np.nonzero(plan[:, 3])[0]:
+        page, off = int(plan[t, 0]), int(plan[t, 1])
+        x = bf16_to_f64(case.k_cache[case.layer_idx, page, off])[:, :C]
+        ref = torch.nn.functional.rms_norm(torch.from_numpy(x.copy()), (C,),
+                                           weight=torch.from_numpy(g), eps=case.epsilon).numpy()
+        assert_correctly_rounded(bf16_to_f64(k[case.layer_idx, page, off][:, :C]), ref,
+                                 ulp_bf16, f"planned kvnorm {t}")
+        expect[case.layer_idx, page, off, :, :C] = k[case.layer_idx, page, off, :, :C]
+    assert np.array_equal(k, expect), "planned kvnorm touched other elements"
+
+
 def small_qk_fp8_cases():
     """fp8 K caches: per-tensor scale (interleaved, position ids, full-width
     norm) and per-token scales (rotate-half, partial norm width)."""
@@ -1182,4 +1245,5 @@ ALL_PINS = [
     pin_mla_position0, pin_mla_zero_row_per_token, pin_qk_composite,
     pin_rms_norm_kv, pin_gather, pin_qk_fp8, pin_rms_norm_kv_fp8, pin_mrope,
     pin_mla_f32_q, pin_rms_norm_kv_token, pin_mla_inplace, pin_token_plan, pin_mla_planned,
+    pin_rms_norm_kv_planned,
 ]

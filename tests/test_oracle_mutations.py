@@ -115,8 +115,12 @@ MUTANTS = [
     ("plan_offset", "plan[4 * t + 1] = (uint32_t)(slot % page_size);",
      "plan[4 * t + 1] = (uint32_t)((slot + 1) % page_size);"),
     ("plan_position", "plan[4 * t + 2] = (uint32_t)slot;", "plan[4 * t + 2] = (uint32_t)slot + 1;"),
-    ("planned_ignores_flag", "if (e[3] == 0 || (int64_t)e[0] >= num_pages",
-     "if ((int64_t)e[0] >= num_pages"),
+    ("planned_ignores_flag", "return !(e[3] == 0 || (int64_t)e[0] >= num_pages",
+     "return !((int64_t)e[0] >= num_pages"),
+    ("planned_kvnorm_drops_last", "for (int64_t t = 0; t < total_seq_len; ++t) {",
+     "for (int64_t t = 0; t + 1 < total_seq_len; ++t) {"),
+    ("planned_kvnorm_next_slot", "layer_idx, (int64_t)e[0], (int64_t)e[1], g, gamma_len, eps,",
+     "layer_idx, (int64_t)e[0], (int64_t)(e[1] ^ 1u), g, gamma_len, eps,"),
     ("planned_offset_as_position",
      "mla_token(q_out, q_out_f32, q_in, latent, t, (int64_t)e[2], row,",
      "mla_token(q_out, q_out_f32, q_in, latent, t, (int64_t)e[1], row,"),
