@@ -1,7 +1,7 @@
 /*
  * pkv.h -- C ABI of the paged-KV pre-attention library (gfx950 / MI355X).
  *
- * Seven entry points, each one stream-ordered kernel launch:
+ * Eight entry points, each one stream-ordered kernel launch:
  *
  *   mla_rope_rmsnorm_quant   fused MLA step: RoPE on q_rope, RMSNorm on the
  *                            latent row's non-rope part, RoPE on its rope tail,
@@ -25,7 +25,9 @@
  *                            paged cache (in place), optional per-head K
  *                            RMSNorm fused in front of the K rotation.
  *                            Page "generic_fused_qk_rope_bshd_paged_ragged".
- *   rms_norm_kv_cache_paged  in-place RMSNorm of the new K-cache rows.
+ *   rms_norm_kv_cache_paged  in-place RMSNorm of the new K-cache rows, and
+ *   rms_norm_kv_cache_paged_planned
+ *                            the same placed by a token plan.
  *                            Page "rms_norm_kv_cache_ragged_paged".
  *   mla_gather_latent_paged  copy of whole request contexts from the paged
  *                            latent cache into a dense buffer, with fp8
@@ -309,6 +311,25 @@ int rms_norm_kv_cache_paged(const pkv_paged_cache* k_cache, uint32_t layer_idx,
                             float weight_offset, uint32_t total_seq_len,
                             const uint32_t* input_row_offsets, uint32_t batch_size,
                             int per_head_norm, int multiply_before_cast, void* stream);
+
+/*
+ * rms_norm_kv_cache_paged with each token placed by a token plan (see
+ * pkv_token_plan): token t < total_seq_len is normalised in the rows at page
+ * token_plan[t][0], offset token_plan[t][1] of layer layer_idx.  With the plan
+ * pkv_token_plan wrote for the same batch the result equals
+ * rms_norm_kv_cache_paged's bit for bit.  An entry not marked placed, or whose
+ * page or offset lies outside the pool, is skipped and counted.
+ *
+ *   token_plan      u32 [>= total_seq_len][4], 16-byte aligned
+ * Other arguments as for rms_norm_kv_cache_paged; the descriptor's
+ * cache_lengths and page_table are not read and may be NULL.  Same supported
+ * sizes.
+ */
+int rms_norm_kv_cache_paged_planned(const pkv_paged_cache* k_cache, uint32_t layer_idx,
+                                    const void* gamma, uint32_t gamma_len, float epsilon,
+                                    float weight_offset, uint32_t total_seq_len,
+                                    const uint32_t* token_plan, int per_head_norm,
+                                    int multiply_before_cast, void* stream);
 
 /*
  * Gather of request contexts from the paged latent cache.  For request b and

@@ -32,7 +32,8 @@ PKV_SCALE_PER_TOKEN = 2
 
 EXPORTED = ("mla_rope_rmsnorm_quant", "mla_rope_rmsnorm_inplace", "pkv_token_plan",
             "mla_rope_rmsnorm_quant_planned", "qk_rope_paged_ragged",
-            "rms_norm_kv_cache_paged", "mla_gather_latent_paged", "pkv_status_string")
+            "rms_norm_kv_cache_paged", "rms_norm_kv_cache_paged_planned",
+            "mla_gather_latent_paged", "pkv_status_string")
 
 
 class PkvError(RuntimeError):
@@ -94,6 +95,9 @@ def _load() -> ctypes.CDLL:
     lib.rms_norm_kv_cache_paged.restype = ctypes.c_int
     lib.rms_norm_kv_cache_paged.argtypes = [
         cache_p, u32, vp, u32, f32, f32, u32, vp, u32, ctypes.c_int, ctypes.c_int, vp]
+    lib.rms_norm_kv_cache_paged_planned.restype = ctypes.c_int
+    lib.rms_norm_kv_cache_paged_planned.argtypes = [
+        cache_p, u32, vp, u32, f32, f32, u32, vp, ctypes.c_int, ctypes.c_int, vp]
     lib.mla_gather_latent_paged.restype = ctypes.c_int
     lib.mla_gather_latent_paged.argtypes = [
         vp, ctypes.c_int32, i64, vp, vp, vp, u32, u32, cache_p, u32, vp]
@@ -275,6 +279,24 @@ def rms_norm_kv_cache_paged(k_cache: PagedCache, layer_idx: int, gamma: torch.Te
         input_row_offsets.numel() - 1, int(bool(per_head_norm)),
         int(bool(multiply_before_cast)), _stream(stream))
     _check("rms_norm_kv_cache_paged", st)
+
+
+def rms_norm_kv_cache_paged_planned(k_cache: PagedCache, layer_idx: int, gamma: torch.Tensor,
+                                    epsilon: float, weight_offset: float, total_seq_len: int,
+                                    plan: torch.Tensor, per_head_norm: bool = True,
+                                    multiply_before_cast: bool = True, stream=None) -> None:
+    """In-place K-cache RMSNorm placed by a token plan (C:
+    ``rms_norm_kv_cache_paged_planned``); ``plan`` is the ``[tokens, 4]``
+    tensor :func:`pkv_token_plan` wrote."""
+    if plan.dim() != 2 or plan.shape[1] != 4 or not plan.is_contiguous():
+        raise ValueError("plan must be a contiguous [tokens, 4] tensor")
+    if plan.shape[0] < total_seq_len:
+        raise ValueError("plan has fewer rows than total_seq_len")
+    st = _lib.rms_norm_kv_cache_paged_planned(
+        ctypes.byref(k_cache), int(layer_idx), _ptr(gamma), gamma.numel(), float(epsilon),
+        float(weight_offset), int(total_seq_len), _ptr(plan), int(bool(per_head_norm)),
+        int(bool(multiply_before_cast)), _stream(stream))
+    _check("rms_norm_kv_cache_paged_planned", st)
 
 
 def mla_gather_latent_paged(out: torch.Tensor, kv_row_offsets: torch.Tensor,

@@ -321,11 +321,17 @@ int qk_rope_paged_ragged(void* q_out, int64_t qo_tok_stride, int64_t qo_head_str
                                            static_cast<hipStream_t>(stream)));
 }
 
-int rms_norm_kv_cache_paged(const pkv_paged_cache* k_cache, uint32_t layer_idx,
-                            const void* gamma, uint32_t gamma_len, float epsilon,
-                            float weight_offset, uint32_t total_seq_len,
-                            const uint32_t* input_row_offsets, uint32_t batch_size,
-                            int per_head_norm, int multiply_before_cast, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Both K-norm entry points: placement from the ragged batch or, when
+// `planned`, from token_plan alone.
+int kv_norm_entry(const pkv_paged_cache* k_cache, uint32_t layer_idx, const void* gamma,
+                  uint32_t gamma_len, float epsilon, float weight_offset,
+                  uint32_t total_seq_len, bool planned, const uint32_t* token_plan,
+                  const uint32_t* input_row_offsets, uint32_t batch_size, int per_head_norm,
+                  int multiply_before_cast, void* stream) {
   if (k_cache == nullptr) return PKV_ERR_NULL;
   pkv::KMode km;
   if (!k_mode_of(k_cache, &km)) return PKV_ERR_DTYPE;
@@ -335,19 +341,21 @@ int rms_norm_kv_cache_paged(const pkv_paged_cache* k_cache, uint32_t layer_idx,
     return PKV_ERR_UNSUPPORTED;
   if (!per_head_norm && k_cache->num_heads > pkv::kv_norm_max_heads(k_cache->head_dim))
     return PKV_ERR_UNSUPPORTED;
-  if (total_seq_len > 0 && batch_size == 0) return PKV_ERR_SHAPE;
+  if (!planned && total_seq_len > 0 && batch_size == 0) return PKV_ERR_SHAPE;
   CacheView view{};
-  int st = check_cache(k_cache, layer_idx, batch_size, &view);
+  int st = check_cache(k_cache, layer_idx, planned ? 0u : batch_size, &view);
   if (st != PKV_OK) return st;
   if (total_seq_len == 0) return PKV_OK;
-  if (gamma == nullptr || input_row_offsets == nullptr) return PKV_ERR_NULL;
+  if (gamma == nullptr || (planned ? token_plan == nullptr : input_row_offsets == nullptr))
+    return PKV_ERR_NULL;
   if (km != pkv::KMode::Bf16 && k_cache->scales == nullptr) return PKV_ERR_NULL;
-  if (!aligned16(gamma)) return PKV_ERR_ALIGN;
+  if (!aligned16(gamma) || (planned && !aligned16(token_plan))) return PKV_ERR_ALIGN;
 
   pkv::KvNormArgs a{};
   a.total_tokens = total_seq_len;
-  a.offsets = input_row_offsets;
-  a.batch = batch_size;
+  a.offsets = planned ? nullptr : input_row_offsets;
+  a.batch = planned ? 0u : batch_size;
+  a.plan = planned ? token_plan : nullptr;
   a.gamma = static_cast<const uint16_t*>(gamma);
   a.gamma_len = gamma_len;
   a.per_head = per_head_norm != 0;
@@ -358,6 +366,30 @@ int rms_norm_kv_cache_paged(const pkv_paged_cache* k_cache, uint32_t layer_idx,
   a.head_dim = k_cache->head_dim;
   return launch_status(pkv::launch_kv_norm(a, multiply_before_cast != 0, km,
                                            static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int rms_norm_kv_cache_paged(const pkv_paged_cache* k_cache, uint32_t layer_idx,
+                            const void* gamma, uint32_t gamma_len, float epsilon,
+                            float weight_offset, uint32_t total_seq_len,
+                            const uint32_t* input_row_offsets, uint32_t batch_size,
+                            int per_head_norm, int multiply_before_cast, void* stream) {
+  return kv_norm_entry(k_cache, layer_idx, gamma, gamma_len, epsilon, weight_offset,
+                       total_seq_len, false, nullptr, input_row_offsets, batch_size,
+                       per_head_norm, multiply_before_cast, stream);
+}
+
+int rms_norm_kv_cache_paged_planned(const pkv_paged_cache* k_cache, uint32_t layer_idx,
+                                    const void* gamma, uint32_t gamma_len, float epsilon,
+                                    float weight_offset, uint32_t total_seq_len,
+                                    const uint32_t* token_plan, int per_head_norm,
+                                    int multiply_before_cast, void* stream) {
+  return kv_norm_entry(k_cache, layer_idx, gamma, gamma_len, epsilon, weight_offset,
+                       total_seq_len, true, token_plan, nullptr, 0, per_head_norm,
+                       multiply_before_cast, stream);
 }
 
 int mla_gather_latent_paged(void* out, int32_t out_dtype, int64_t out_row_stride,

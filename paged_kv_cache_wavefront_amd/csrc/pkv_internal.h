@@ -106,6 +106,8 @@ struct KvNormArgs {
   float* k_scales;               // fp8 K: tensor scale [1] or this layer's per-token scales
   CacheView cache;               // K cache
   uint32_t head_dim;
+  const uint32_t* plan;          // [total_tokens][4] token plan, or null: placement
+                                 // from offsets, lengths and page table
 };
 
 // Most KV heads per token the per-token K-norm statistic handles.

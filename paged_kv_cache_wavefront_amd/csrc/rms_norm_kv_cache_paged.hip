@@ -14,6 +14,10 @@
 // 4 head groups first (phase 1, sums), then normalise and store it (phase 2);
 // the per-token form needs all heads in one chunk.
 //
+// Planned form: with a token plan (token_plan.hip) the token's (page,
+// offset) is one checked plan entry instead of the address chain, which in
+// this in-place kernel lies wholly in front of the row loads.
+//
 // One wave64 per token; lane holds 8 consecutive columns (16 bytes of bf16,
 // 8 bytes of fp8) of one head, a head occupies LP lanes (D/8 rounded up to a
 // power of two: the lanes past the head's D/8 chunks idle for D = 80, 96),
@@ -35,7 +39,9 @@ constexpr int kMaxIter = 4;  // head groups held in registers at once
 
 __device__ __forceinline__ float round_bf16(float v) { return __uint_as_float(pack_bf16x2(v, 0.0f) << 16); }
 
-template <int D, bool MBC, KMode KM, bool PER_HEAD>
+// PLANNED: each token's (page, offset) comes from a token plan entry, one
+// scalar 16-byte load, instead of the two-step address chain.
+template <int D, bool MBC, KMode KM, bool PER_HEAD, bool PLANNED>
 __global__ __launch_bounds__(256) void kv_norm_kernel(const KvNormArgs a) {
   constexpr int NC = D / 8, LP = pow2_at_least(NC), HPI = kWave / LP;
   constexpr int64_t EB = KM == KMode::Bf16 ? 2 : 1;
@@ -64,9 +70,18 @@ __global__ __launch_bounds__(256) void kv_norm_kernel(const KvNormArgs a) {
   for (int k = 0; k < 8; ++k) g[k] += a.weight_offset;
 
   const CacheView& cv = a.cache;
-  const TokenSlot ts = find_slot(a.offsets, a.batch, cv.cache_lengths, t, lane);
   PageSlot ps{};
-  if (!(ts.ok && page_of(cv.page_table, cv.pt_stride, cv.num_pages, cv.page_size, ts, &ps))) {
+  bool placed;
+  if constexpr (PLANNED) {
+    const uint4 e = *reinterpret_cast<const uint4*>(a.plan + 4 * (uint64_t)t);
+    ps.page = uniform(e.x);
+    ps.offset = uniform(e.y);
+    placed = e.w != 0 && ps.page < cv.num_pages && ps.offset < cv.page_size;
+  } else {
+    const TokenSlot ts = find_slot(a.offsets, a.batch, cv.cache_lengths, t, lane);
+    placed = ts.ok && page_of(cv.page_table, cv.pt_stride, cv.num_pages, cv.page_size, ts, &ps);
+  }
+  if (!placed) {
     count_skip(cv.error_count, lane);
     return;
   }
@@ -183,15 +198,21 @@ __global__ __launch_bounds__(256) void kv_norm_kernel(const KvNormArgs a) {
   }  // chunk
 }
 
+template <int D, KMode KM, bool PER_HEAD, bool PLANNED>
+hipError_t launch_dkhp(const KvNormArgs& a, bool mbc, uint32_t blocks, hipStream_t stream) {
+  if (mbc)
+    hipLaunchKernelGGL((kv_norm_kernel<D, true, KM, PER_HEAD, PLANNED>), dim3(blocks),
+                       dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((kv_norm_kernel<D, false, KM, PER_HEAD, PLANNED>), dim3(blocks),
+                       dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
 template <int D, KMode KM, bool PER_HEAD>
 hipError_t launch_dkh(const KvNormArgs& a, bool mbc, uint32_t blocks, hipStream_t stream) {
-  if (mbc)
-    hipLaunchKernelGGL((kv_norm_kernel<D, true, KM, PER_HEAD>), dim3(blocks), dim3(256), 0,
-                       stream, a);
-  else
-    hipLaunchKernelGGL((kv_norm_kernel<D, false, KM, PER_HEAD>), dim3(blocks), dim3(256), 0,
-                       stream, a);
-  return hipGetLastError();
+  return a.plan != nullptr ? launch_dkhp<D, KM, PER_HEAD, true>(a, mbc, blocks, stream)
+                           : launch_dkhp<D, KM, PER_HEAD, false>(a, mbc, blocks, stream);
 }
 
 template <int D, KMode KM>

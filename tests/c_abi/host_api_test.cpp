@@ -335,6 +335,18 @@ int main() {
     // the batch form never carries a plan
     pkv_paged_cache b = latent_cache(PKV_DTYPE_FP8_E4M3FN, PKV_SCALE_PER_TENSOR, 7);
     EXPECT(mla(&b, 5, 40, PKV_DTYPE_BF16) == PKV_OK && g_mla.plan == nullptr);
+    // the planned K norm
+    pkv_paged_cache k = k_cache(PKV_DTYPE_BF16, PKV_SCALE_NONE, 8, 128);
+    k.cache_lengths = nullptr;
+    k.page_table = nullptr;
+    before = g_calls;
+    EXPECT(rms_norm_kv_cache_paged_planned(&k, 2, P(45056), 128, 1e-6f, 0.0f, 7, plan, 1, 1,
+                                           nullptr) == PKV_OK);
+    EXPECT(g_calls == before + 1 && g_norm.plan == plan && g_norm.offsets == nullptr);
+    EXPECT(g_norm.total_tokens == 7 && g_norm.batch == 0);
+    EXPECT(g_norm.cache.layer_base == static_cast<char*>(k.data) + 2 * 2 * k.layer_stride);
+    EXPECT(rms_norm_kv_cache_paged_planned(&k, 2, P(45056), 128, 1e-6f, 0.0f, 7, plan + 1, 1, 1,
+                                           nullptr) == PKV_ERR_ALIGN);
   }
   // --- MLA: per-token fp8, 40 heads, layer 1 of 2
   {

@@ -34,6 +34,7 @@ def test_header_declares_entry_points():
     assert declared_functions() == sorted(["mla_rope_rmsnorm_quant", "mla_rope_rmsnorm_inplace",
                                            "pkv_token_plan", "mla_rope_rmsnorm_quant_planned",
                                            "qk_rope_paged_ragged", "rms_norm_kv_cache_paged",
+                                           "rms_norm_kv_cache_paged_planned",
                                            "mla_gather_latent_paged", "pkv_status_string",
                                            "pkv_stream_copy"])
 
@@ -174,6 +175,25 @@ def test_token_plan_validation(pkv):
     # the pool is not read: no data pointer needed; nothing to do for no tokens
     assert call_plan(pkv, mla_cache(pkv), T=0, batch=0) == OK
     assert call_plan(pkv, mla_cache(pkv, data=None), T=0) == OK
+
+
+def call_kv_planned(pkv, cache, plan=FAKE, T=16, gamma=FAKE, glen=128, layer=1):
+    lib = pkv.library()
+    cp = None if cache is None else ctypes.byref(cache)
+    return lib.rms_norm_kv_cache_paged_planned(cp, layer, gamma, glen, 1e-6, 0.0, T, plan, 1, 1,
+                                               None)
+
+
+def test_kv_norm_planned_validation(pkv):
+    assert call_kv_planned(pkv, None) == NULL
+    assert call_kv_planned(pkv, kcache(pkv), plan=None) == NULL
+    assert call_kv_planned(pkv, kcache(pkv), plan=FAKE + 4) == ALIGN
+    assert call_kv_planned(pkv, kcache(pkv), gamma=None) == NULL
+    assert call_kv_planned(pkv, kcache(pkv), glen=0) == SHAPE
+    assert call_kv_planned(pkv, kcache(pkv), glen=129) == SHAPE
+    assert call_kv_planned(pkv, kcache(pkv), layer=2) == RANGE
+    # placement comes from the plan: lengths and page table may be absent
+    assert call_kv_planned(pkv, kcache(pkv, cache_lengths=None, page_table=None), T=0) == OK
 
 
 def call_mla_planned(pkv, cache, T=16, H=4, R=64, Dn=512, plan=FAKE, q=FAKE, lat=FAKE,
@@ -363,7 +383,10 @@ def test_headers_compile_as_c_and_cxx(tmp_path):
                    " uint32_t, const float*, uint32_t, const void*, float,"
                    " const pkv_paged_cache*, uint32_t, int32_t, void*) ="
                    " mla_rope_rmsnorm_quant_planned;\n"
-                   "  (void)f4; (void)f5;\n"
+                   "  int (*f6)(const pkv_paged_cache*, uint32_t, const void*, uint32_t, float,"
+                   " float, uint32_t, const uint32_t*, int, int, void*) ="
+                   " rms_norm_kv_cache_paged_planned;\n"
+                   "  (void)f4; (void)f5; (void)f6;\n"
                    "  int (*f3)(const void*, void*, uint64_t, uint32_t, void*) = pkv_stream_copy;\n"
                    "  (void)f1; (void)f2; (void)f3;\n"
                    "  return 0;\n}\n")

@@ -1,9 +1,10 @@
-"""GPU parity of pkv_token_plan and mla_rope_rmsnorm_quant_planned against the
-CPU oracle, through the C ABI: the plan bit for bit (all MLA workloads, small
-ragged cases, page ids past the pool, rows past the last offset); the planned
-step bit-identical to the batch form on the same batch and within the parity
-bars of the oracle; free placements with skipped, out-of-pool and
-out-of-table entries against the oracle's planned step."""
+"""GPU parity of pkv_token_plan, mla_rope_rmsnorm_quant_planned and
+rms_norm_kv_cache_paged_planned against the CPU oracle, through the C ABI: the
+plan bit for bit (all MLA workloads, small ragged cases, page ids past the
+pool, rows past the last offset); the planned MLA step and K-cache norm
+bit-identical to their batch forms on the same batch and within the parity
+bars of the oracle; free placements and entries that are skipped, out of the
+pool or out of the freqs table against the oracle's planned forms."""
 import contextlib
 
 import numpy as np
@@ -150,3 +151,88 @@ def test_plan_reused_across_layers(orc):
     g, r = dev.results(), ref.results()
     assert np.array_equal(g[1], r[1]) and np.array_equal(g[0].view(np.uint16),
                                                          r[0].view(np.uint16))
+
+
+def _kv_planned_cases():
+    """(case, gamma width, weight offset, total, multiply_before_cast, per_head)"""
+    yield workloads.qk_generic(), 128, 0.0, None, True, True
+    small = list(oracle_pins.small_qk_cases())
+    yield small[0], 48, 0.25, -3, False, True
+    yield small[1], None, 0.0, None, True, False
+    for case in oracle_pins.small_qk_fp8_cases():
+        yield case, None, 0.0, None, True, True
+
+
+@pytest.mark.parametrize("idx", range(3 + len(list(oracle_pins.small_qk_fp8_cases()))))
+def test_kv_norm_planned_equals_batch_form(orc, idx):
+    """The K-cache norm placed by its batch's plan writes the batch form's bits
+    (bf16 both cast orders, weight offset, short total_seq_len, per-token
+    statistic, fp8 tensor and token scales), and meets the oracle's planned
+    form on the same call."""
+    import paged_kv_cache_wavefront_amd as pkv
+    case, cols, w, short, mbc, per_head = list(_kv_planned_cases())[idx]
+    D = case.k_cache.shape[-1]
+    cols = cols or (case.gamma.size if case.gamma is not None else D)
+    gamma = workloads.bf16_bits(workloads.make_rng(7000 + idx).uniform(0.5, 1.5, cols)
+                                .astype(np.float32))
+    total = case.T + short if short else case.T
+    _say(f"[kv-planned] case={case.name} T={case.T} total={total} cols={cols} w={w} "
+         f"mbc={mbc} per_head={per_head} k={case.k_scale_mode}")
+    ref, dev = gh.QkDevice(case), gh.QkDevice(case)
+    g = gh.dev_bf16(gamma)
+    ref.kv_norm(g, w, total, mbc, per_head)
+    plan = torch.zeros((case.T, 4), dtype=torch.int32, device=gh.DEV)
+    pkv.pkv_token_plan(plan, dev.offsets, dev.desc)
+    pkv.rms_norm_kv_cache_paged_planned(dev.desc, case.layer_idx, g, case.epsilon, w, total, plan,
+                                        per_head, mbc)
+    (k_r, s_r), (k_p, s_p) = ref.k_host(), dev.k_host()
+    assert int(dev.error_count.item()) == int(ref.error_count.item()) == 0
+    assert np.array_equal(k_p, k_r), "planned K norm differs from the batch form"
+    if s_r is not None:
+        assert np.array_equal(s_p.view(np.uint32), s_r.view(np.uint32))
+    # the planned form against the oracle's planned form, bit for bit where
+    # the oracle's float64 result is not within a hair of a rounding boundary
+    k_o = case.k_cache.copy()
+    s_o = None if case.k_scales is None else case.k_scales.copy()
+    orc.rms_norm_kv_cache_planned(k_o, case.layer_idx, oracle_pins.qk_token_plan(orc, case),
+                                  gamma, case.epsilon, w, total, mbc, case.k_scale_mode, s_o,
+                                  per_head)
+    rows = gh.written_k_rows(case)
+    assert np.array_equal(k_p[~rows], case.k_cache[~rows])
+    if case.k_cache.dtype == np.uint16:
+        d = gh.bf16_ulp_diff(k_p[rows], k_o[rows])
+        assert int(d.max(initial=0)) <= (1 if mbc else 2)
+        assert float((d != 0).sum() / max(d.size, 1)) <= max(gh.BF16_MAX_DIFF_FRAC, 3 / d.size)
+    else:
+        d = gh.fp8_ulp_diff(k_p[rows], k_o[rows])
+        assert int(d.max(initial=0)) <= 1
+        assert float((d != 0).sum() / max(d.size, 1)) <= max(gh.FP8_MAX_DIFF_FRAC, 3 / d.size)
+
+
+def test_kv_norm_planned_skips(orc):
+    """Entries not marked placed, or naming a page or offset outside the pool,
+    are skipped and counted; the other tokens are normalised at their cells."""
+    import paged_kv_cache_wavefront_amd as pkv
+    case = list(oracle_pins.small_qk_cases())[0]
+    dev = gh.QkDevice(case)
+    plan = torch.zeros((case.T, 4), dtype=torch.int32, device=gh.DEV)
+    pkv.pkv_token_plan(plan, dev.offsets, dev.desc)
+    L, P, S = case.k_cache.shape[:3]
+    h = plan.cpu().numpy().view(np.uint32).copy()
+    h[0, 3] = 0
+    h[1, 0] = P
+    h[2, 1] = S
+    plan.copy_(torch.from_numpy(h.view(np.int32)))
+    gamma = workloads.bf16_bits(np.linspace(0.5, 1.5, 64).astype(np.float32))
+    pkv.rms_norm_kv_cache_paged_planned(dev.desc, case.layer_idx, gh.dev_bf16(gamma),
+                                        case.epsilon, 0.0, case.T, plan)
+    k, _ = dev.k_host()
+    assert int(dev.error_count.item()) == 3
+    k_o = case.k_cache.copy()
+    try:
+        orc.rms_norm_kv_cache_planned(k_o, case.layer_idx, h, gamma, case.epsilon, 0.0, case.T)
+    except oracle.OracleError:
+        pass
+    d = gh.bf16_ulp_diff(k, k_o)
+    assert int(d.max(initial=0)) <= 1
+    assert float((d != 0).sum() / d.size) <= max(gh.BF16_MAX_DIFF_FRAC, 3 / d.size)
