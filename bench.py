@@ -19,7 +19,7 @@ again placed by a token plan built once before the timed launches
 (mla_rope_rmsnorm_quant_planned; the plan build's own time beside them), the same
 prefill batch in place on a bf16 latent cache (mla_rope_rmsnorm_inplace), the
 Llama-shaped paged-ragged Q/K RoPE with fused per-head K norm, the in-place
-K-cache RMSNorm and the paged latent gather.
+K-cache RMSNorm (also placed by a token plan) and the paged latent gather.
 
 With the CPU baseline (the oracle on the same inputs, single-threaded and on
 N host threads) the line also carries ``parity``: one launch of the timed
@@ -55,6 +55,7 @@ KERNEL_OF = {"mla_prefill": "mla_rope_rmsnorm_quant.hip", "mla_decode": "mla_rop
              "mla_prefill_inplace": "mla_rope_rmsnorm_quant.hip",
              "mla_decode_planned": "mla_rope_rmsnorm_quant.hip",
              "mla_mixed_planned": "mla_rope_rmsnorm_quant.hip",
+             "kv_norm_planned": "rms_norm_kv_cache_paged.hip",
              "qk_generic": "qk_rope_paged_ragged.hip", "kv_norm": "rms_norm_kv_cache_paged.hip",
              "gather": "mla_gather_latent_paged.hip"}
 
@@ -122,10 +123,13 @@ def gather_bytes(rows: int, batch: int, page_size: int, in_bytes=576, out_bytes=
     return rows * (in_bytes + out_bytes) + (batch + 1) * 4 + 4 * (-(-rows // page_size))
 
 
-def kv_norm_bytes(case, cols: int) -> int:
+def kv_norm_bytes(case, cols: int, planned: bool = False) -> int:
+    """The first cols columns of every K head read and written back; gamma;
+    offsets and prior lengths (planned: a 16-byte plan entry per token)."""
     T = case.T
     Hkv = case.k_cache.shape[3]
-    return T * 2 * Hkv * cols * 2 + (case.B + 1) * 4 + case.B * 4 + cols * 2
+    chain = 16 * T if planned else (case.B + 1) * 4 + case.B * 4
+    return T * 2 * Hkv * cols * 2 + chain + cols * 2
 
 
 # -- timing ------------------------------------------------------------------------------
@@ -304,7 +308,7 @@ def run_workload(name, steps, warmup):
         how = f"{n} sets of q, q_out and bf16 cache pool"
         r = measure(cycle(fns), case.T, mla_bytes(case), steps, warmup)
         label = name
-    elif name.endswith("_planned"):
+    elif name.startswith("mla_") and name.endswith("_planned"):
         # one plan per batch layout, built before the timed region (every
         # layer of a model step reuses it); the plan build is timed on its own
         case = workloads.NAMED[name[: -len("_planned")]]()
@@ -383,7 +387,8 @@ def run_workload(name, steps, warmup):
         how = f"{n} sets of q, q_out and K pool"
         r = measure(cycle(fns), case.T, qk_bytes(case, True), steps, warmup)
         label = "qk_generic (interleaved, position ids, fused per-head K norm)"
-    elif name == "kv_norm":
+    elif name in ("kv_norm", "kv_norm_planned"):
+        planned = name == "kv_norm_planned"
         case = workloads.qk_generic()
         written = int(gh.written_k_rows(case).sum()) * case.k_cache[0, 0, 0].nbytes
         n = rotation_count(written, case.k_cache.nbytes)
@@ -398,11 +403,28 @@ def run_workload(name, steps, warmup):
             return lambda: pkv.rms_norm_kv_cache_paged(dsc, case.layer_idx, base.gamma,
                                                        case.epsilon, 0.0, case.T, base.offsets,
                                                        True, True)
-        fns = [make(d) for d in descs]
-        devs = (base, pools, descs)
+        plan = torch.empty((case.T, 4), dtype=torch.int32, device="cuda")
+        pkv.pkv_token_plan(plan, base.offsets, descs[0])
+
+        def make_planned(dsc):
+            return lambda: pkv.rms_norm_kv_cache_paged_planned(dsc, case.layer_idx, base.gamma,
+                                                               case.epsilon, 0.0, case.T, plan,
+                                                               True, True)
+        fns = [(make_planned if planned else make)(d) for d in descs]
+        devs = (base, pools, descs, plan)
         how = f"{n} K pools"
-        r = measure(cycle(fns), case.T, kv_norm_bytes(case, 128), steps, warmup)
+        r = measure(cycle(fns), case.T, kv_norm_bytes(case, 128, planned), steps, warmup)
         label = "qk_generic K cache (8 heads x 128, gamma 128)"
+        if planned:
+            label += ", placed by a token plan built once"
+            batch, planned_fn = cycle([make(d) for d in descs]), cycle(fns)
+            ab = {"batch": [], "planned": []}
+            for _ in range(3):
+                ab["batch"].append(time_graph(batch, steps, warmup))
+                ab["planned"].append(time_graph(planned_fn, steps, warmup))
+            r["vs_batch_form"] = {k: round(float(np.median(v)) * 1e6, 2) for k, v in ab.items()}
+            r["vs_batch_form"]["how"] = ("graph replay, batch and planned forms alternating, "
+                                         "median of 3 x 5 replays")
     elif name == "gather":
         case = workloads.mla_decode()
         ctx = case.cache_lengths.astype(np.int64) + 1
@@ -440,6 +462,7 @@ def measure_siblings(main, steps, warmup):
                         ("mla_prefill_inplace", "mla_rope_rmsnorm_inplace"),
                         ("qk_generic", "qk_rope_paged_ragged"),
                         ("kv_norm", "rms_norm_kv_cache_paged"),
+                        ("kv_norm_planned", "rms_norm_kv_cache_paged_planned"),
                         ("gather", "mla_gather_latent_paged")):
         if name == main:
             continue
@@ -449,6 +472,7 @@ def measure_siblings(main, steps, warmup):
                      "traffic": profiled_traffic(name)}
         if "plan_build" in r:
             out[name]["plan_build"] = r["plan_build"]
+        if "vs_batch_form" in r:
             out[name]["vs_batch_form_us"] = r["vs_batch_form"]
     return out
 
@@ -621,7 +645,7 @@ def main():
     ap.add_argument("--workload", default="mla_prefill",
                     choices=["mla_prefill", "mla_decode", "mla_mixed", "mla_tiny",
                              "mla_prefill_inplace", "mla_decode_planned", "mla_mixed_planned",
-                             "qk_generic", "kv_norm", "gather"])
+                             "qk_generic", "kv_norm", "kv_norm_planned", "gather"])
     ap.add_argument("--no-siblings", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
