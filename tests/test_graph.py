@@ -113,24 +113,38 @@ def test_qk_graph_replays():
         assert np.array_equal(gh.host_bf16(dev.k), want_k), f"replay {rep}: k"
 
 
-def test_kv_norm_graph_replays():
+@pytest.mark.parametrize("planned", [False, True])
+def test_kv_norm_graph_replays(planned):
+    """The K-cache norm inside a graph (planned: the plan build and the norm
+    placed by it, both captured); K restored before every replay."""
+    import paged_kv_cache_wavefront_amd as pkv
     case = workloads.qk_generic()
     eager = gh.QkDevice(case)
     eager.kv_norm(eager.gamma, 0.25, case.T, True, per_head=False)
     want = gh.host_bf16(eager.k)
     dev = gh.QkDevice(case)
     k0 = dev.k.clone()
+    plan = torch.zeros((case.T, 4), dtype=torch.int32, device="cuda")
+
+    def step():
+        if planned:
+            pkv.pkv_token_plan(plan, dev.offsets, dev.desc)
+            pkv.rms_norm_kv_cache_paged_planned(dev.desc, case.layer_idx, dev.gamma,
+                                                case.epsilon, 0.25, case.T, plan, False, True)
+        else:
+            dev.kv_norm(dev.gamma, 0.25, case.T, True, per_head=False)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        dev.kv_norm(dev.gamma, 0.25, case.T, True, per_head=False)
+        step()
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        dev.kv_norm(dev.gamma, 0.25, case.T, True, per_head=False)
+        step()
     for rep in range(3):
         dev.k.copy_(k0)                         # normalised in place: restore it
+        plan.zero_()
         junk = torch.ones(1 << 20, device="cuda") * rep
         torch.cuda.synchronize()
         g.replay()

@@ -152,6 +152,18 @@ def test_kv_norm_random(orc, seed):
     dev.kv_norm(gh.dev_bf16(gamma), w, total, mbc, per_head)
     k, ks = dev.k_host()
     assert int(dev.error_count.item()) == 0
+    # the planned form, with the plan of this batch, writes the same bits
+    import torch
+    import paged_kv_cache_wavefront_amd as pkv
+    pdev = gh.QkDevice(case)
+    plan = torch.empty((case.T, 4), dtype=torch.int32, device=gh.DEV)
+    pkv.pkv_token_plan(plan, pdev.offsets, pdev.desc)
+    pkv.rms_norm_kv_cache_paged_planned(pdev.desc, case.layer_idx, gh.dev_bf16(gamma),
+                                        case.epsilon, w, total, plan, per_head, mbc)
+    k_p, ks_p = pdev.k_host()
+    assert np.array_equal(k_p, k), "planned K norm differs"
+    if ks is not None:
+        assert np.array_equal(ks_p.view(np.uint32), ks.view(np.uint32))
     k_o = case.k_cache.copy()
     ks_o = None if case.k_scales is None else case.k_scales.copy()
     if fp8:
