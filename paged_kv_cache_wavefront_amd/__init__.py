@@ -234,6 +234,8 @@ def mla_rope_rmsnorm_quant_planned(q_rope_output: torch.Tensor, q_rope: torch.Te
     T, H, R = q_rope.shape
     if plan.dim() != 2 or plan.shape[1] != 4 or not plan.is_contiguous():
         raise ValueError("plan must be a contiguous [tokens, 4] tensor")
+    if plan.shape[0] < T:
+        raise ValueError("plan has fewer rows than q_rope has tokens")
     st = _lib.mla_rope_rmsnorm_quant_planned(
         _ptr(q_rope_output), q_rope_output.stride(0), q_rope_output.stride(1),
         _ptr(q_rope), q_rope.stride(0), q_rope.stride(1),

@@ -196,6 +196,22 @@ def test_kv_norm_planned_validation(pkv):
     assert call_kv_planned(pkv, kcache(pkv, cache_lengths=None, page_table=None), T=0) == OK
 
 
+def test_planned_bindings_check_plan_rows(pkv):
+    """The binding refuses a plan with fewer rows than tokens (the C entry
+    points take no plan length) before any device pointer is used."""
+    import torch
+    plan = torch.zeros((3, 4), dtype=torch.int32)
+    q = torch.zeros((4, 2, 64), dtype=torch.bfloat16)
+    lat = torch.zeros((4, 576), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        pkv.mla_rope_rmsnorm_quant_planned(q, q, lat, plan, None, None, 1e-6, None, 0)
+    with pytest.raises(ValueError):
+        pkv.rms_norm_kv_cache_paged_planned(None, 0, None, 1e-6, 0.0, 4, plan)
+    with pytest.raises(ValueError):
+        pkv.mla_rope_rmsnorm_quant_planned(q, q, lat, torch.zeros((4, 3), dtype=torch.int32),
+                                           None, None, 1e-6, None, 0)
+
+
 def call_mla_planned(pkv, cache, T=16, H=4, R=64, Dn=512, plan=FAKE, q=FAKE, lat=FAKE,
                      layer=1, max_seq=64, qo_dtype=0):
     lib = pkv.library()
