@@ -260,12 +260,13 @@ class Oracle:
                                        tensor_scale=1.0, token_scales=None):
         """:meth:`mla_rope_rmsnorm_quant` with each token placed by ``plan``
         (u32 [T, 4]: page, offset, position, placed flag) instead of the
-        ragged batch and the page table."""
+        ragged batch and the page table; ``latent=None`` is the in-place form
+        on a bf16 cache."""
         T, H, R = q_in.shape
-        W = latent.shape[1]
+        W = cache.shape[4] if latent is None else latent.shape[1]
         L, P, S = cache.shape[:3]
-        if (cache.shape[3:] != (1, W) or q_out.shape != q_in.shape or latent.shape[0] != T
-                or plan.shape != (T, 4)):
+        if (cache.shape[3:] != (1, W) or q_out.shape != q_in.shape
+                or (latent is not None and latent.shape[0] != T) or plan.shape != (T, 4)):
             raise ValueError("inconsistent MLA shapes")
         cache_type = CACHE_BF16 if cache.dtype == np.uint16 else CACHE_FP8
         mode = {"per_tensor": SCALE_PER_TENSOR, "per_token": SCALE_PER_TOKEN,

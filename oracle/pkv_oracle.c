@@ -388,7 +388,8 @@ int oracle_token_plan(uint32_t* plan, int64_t T, const uint32_t* row_offsets,
  * layer layer_idx.  A token whose entry is not marked placed, whose position
  * is not below max_seq_len, or whose page or offset lies outside the pool is
  * skipped (nothing written; the return value reports it).  Other arguments
- * as for oracle_mla_rope_rmsnorm_quant with its latent buffer.
+ * as for oracle_mla_rope_rmsnorm_quant; latent = NULL is the in-place form on
+ * a bf16 cache (each row read from the cell it is written back to).
  */
 int oracle_mla_rope_rmsnorm_quant_planned(
     void* q_out, int q_out_f32, const uint16_t* q_in, const uint16_t* latent,
@@ -397,8 +398,9 @@ int oracle_mla_rope_rmsnorm_quant_planned(
     int cache_type, int64_t num_layers, int64_t num_pages, int64_t page_size,
     int64_t layer_idx, int scale_mode, float tensor_scale, float* token_scales) {
   if (R <= 0 || R % 2 || Dn <= 0 || H < 0 || T < 0 || layer_idx < 0 ||
-      layer_idx >= num_layers || page_size <= 0 || !latent)
+      layer_idx >= num_layers || page_size <= 0)
     return ORACLE_BAD_ARG;
+  if (!latent && cache_type != ORACLE_CACHE_BF16) return ORACLE_BAD_ARG;
   double g[4096];
   if (Dn + R > 4096 || R > 1024) return ORACLE_BAD_ARG;
   for (int64_t k = 0; k < Dn; ++k) g[k] = oracle_bf16_decode(gamma[k]);

@@ -676,6 +676,16 @@ def pin_mla_planned(orc):
         assert np.array_equal(q_out, q_b) and np.array_equal(cache, cache_b)
         if ts is not None:
             assert np.array_equal(ts.view(np.uint32), ts_b.view(np.uint32))
+    # in place on a bf16 cache holding the rows: equals the batch in-place form
+    for case in small_mla_inplace_cases():
+        plan = run_token_plan(orc, case)
+        cache0 = place_latent_rows(case)
+        q_p = np.zeros_like(case.q)
+        c_p = cache0.copy()
+        orc.mla_rope_rmsnorm_quant_planned(q_p, case.q, None, plan, case.freqs, case.gamma,
+                                           case.epsilon, c_p, case.layer_idx, "none")
+        q_b, c_b = run_mla_inplace(orc, case)
+        assert np.array_equal(q_p, q_b) and np.array_equal(c_p, c_b), case.name
     rng = np.random.default_rng(2020)
     for k, case in enumerate(small_mla_cases()):
         plan = free_plan(case, rng, skip_every=3 if k % 2 else 0)
