@@ -1,7 +1,7 @@
 /*
  * pkv.h -- C ABI of the paged-KV pre-attention library (gfx950 / MI355X).
  *
- * Eight entry points, each one stream-ordered kernel launch:
+ * Nine entry points, each one stream-ordered kernel launch:
  *
  *   mla_rope_rmsnorm_quant   fused MLA step: RoPE on q_rope, RMSNorm on the
  *                            latent row's non-rope part, RoPE on its rope tail,
@@ -17,10 +17,11 @@
  *                            mla_decode_branch_fp8, "mla_graph" module page).
  *   pkv_token_plan           each new token's cache placement (page, offset,
  *                            position), written once per batch layout, and
- *   mla_rope_rmsnorm_quant_planned
- *                            the fused MLA step placed by such a plan (the
- *                            same page's addressing, split so that every layer
- *                            of a model step reuses it).
+ *   mla_rope_rmsnorm_quant_planned, mla_rope_rmsnorm_inplace_planned
+ *                            the fused MLA step (buffer and in-place forms)
+ *                            placed by such a plan (the same page's
+ *                            addressing, split so that every layer of a model
+ *                            step reuses it).
  *   qk_rope_paged_ragged     RoPE on Q (out of place) and on the new K rows of a
  *                            paged cache (in place), optional per-head K
  *                            RMSNorm fused in front of the K rotation.
@@ -244,6 +245,28 @@ int mla_rope_rmsnorm_quant_planned(void* q_rope_out, int64_t qo_tok_stride,
                                    const void* gamma, float epsilon,
                                    const pkv_paged_cache* kv_cache, uint32_t layer_idx,
                                    int32_t q_out_dtype, void* stream);
+
+/*
+ * mla_rope_rmsnorm_inplace with each token placed by a token plan: the row at
+ * page token_plan[t][0], offset token_plan[t][1] of layer layer_idx is read,
+ * normalised, rotated at position token_plan[t][2] and written back there.
+ * With the plan pkv_token_plan wrote for the same batch the results equal
+ * mla_rope_rmsnorm_inplace's bit for bit.  Skipped entries as for
+ * mla_rope_rmsnorm_quant_planned (their rows are neither read nor written).
+ *
+ *   token_plan      u32 [total_tokens][4], 16-byte aligned
+ * Other arguments as for mla_rope_rmsnorm_inplace; the descriptor's
+ * cache_lengths and page_table are not read and may be NULL.
+ */
+int mla_rope_rmsnorm_inplace_planned(void* q_rope_out, int64_t qo_tok_stride,
+                                     int64_t qo_head_stride, const void* q_rope,
+                                     int64_t qi_tok_stride, int64_t qi_head_stride,
+                                     const uint32_t* token_plan, uint32_t total_tokens,
+                                     uint32_t num_heads, uint32_t rope_dim,
+                                     uint32_t kv_norm_dim, const float* freqs_cis,
+                                     uint32_t max_seq_len, const void* gamma, float epsilon,
+                                     const pkv_paged_cache* kv_cache, uint32_t layer_idx,
+                                     int32_t q_out_dtype, void* stream);
 
 /*
  * Paged-ragged fused Q/K RoPE.  Q is rotated into q_out; the K rows of the

@@ -31,7 +31,8 @@ PKV_SCALE_PER_TENSOR = 1
 PKV_SCALE_PER_TOKEN = 2
 
 EXPORTED = ("mla_rope_rmsnorm_quant", "mla_rope_rmsnorm_inplace", "pkv_token_plan",
-            "mla_rope_rmsnorm_quant_planned", "qk_rope_paged_ragged",
+            "mla_rope_rmsnorm_quant_planned", "mla_rope_rmsnorm_inplace_planned",
+            "qk_rope_paged_ragged",
             "rms_norm_kv_cache_paged", "rms_norm_kv_cache_paged_planned",
             "mla_gather_latent_paged", "pkv_status_string")
 
@@ -88,6 +89,10 @@ def _load() -> ctypes.CDLL:
     lib.mla_rope_rmsnorm_quant_planned.argtypes = [
         vp, i64, i64, vp, i64, i64, vp, i64, vp, u32, u32, u32, u32, vp, u32, vp, f32,
         cache_p, u32, ctypes.c_int32, vp]
+    lib.mla_rope_rmsnorm_inplace_planned.restype = ctypes.c_int
+    lib.mla_rope_rmsnorm_inplace_planned.argtypes = [
+        vp, i64, i64, vp, i64, i64, vp, u32, u32, u32, u32, vp, u32, vp, f32, cache_p, u32,
+        ctypes.c_int32, vp]
     lib.qk_rope_paged_ragged.restype = ctypes.c_int
     lib.qk_rope_paged_ragged.argtypes = [
         vp, i64, i64, vp, i64, i64, u32, u32, u32, vp, u32, cache_p, u32, vp, u32, vp, vp,
@@ -245,6 +250,29 @@ def mla_rope_rmsnorm_quant_planned(q_rope_output: torch.Tensor, q_rope: torch.Te
         PKV_DTYPE_F32 if q_rope_output.dtype == torch.float32 else PKV_DTYPE_BF16,
         _stream(stream))
     _check("mla_rope_rmsnorm_quant_planned", st)
+
+
+def mla_rope_rmsnorm_inplace_planned(q_rope_output: torch.Tensor, q_rope: torch.Tensor,
+                                     plan: torch.Tensor, freqs_cis: torch.Tensor,
+                                     gamma: torch.Tensor, epsilon: float, kv_cache: PagedCache,
+                                     layer_idx: int, stream=None) -> None:
+    """In-place fused MLA step placed by a token plan (C:
+    ``mla_rope_rmsnorm_inplace_planned``); arguments as for
+    :func:`mla_rope_rmsnorm_inplace` with ``plan`` in place of the row
+    offsets."""
+    T, H, R = q_rope.shape
+    if plan.dim() != 2 or plan.shape[1] != 4 or not plan.is_contiguous():
+        raise ValueError("plan must be a contiguous [tokens, 4] tensor")
+    if plan.shape[0] < T:
+        raise ValueError("plan has fewer rows than q_rope has tokens")
+    st = _lib.mla_rope_rmsnorm_inplace_planned(
+        _ptr(q_rope_output), q_rope_output.stride(0), q_rope_output.stride(1),
+        _ptr(q_rope), q_rope.stride(0), q_rope.stride(1), _ptr(plan), T, H, R,
+        kv_cache.head_dim - R, _ptr(freqs_cis), freqs_cis.shape[0], _ptr(gamma),
+        float(epsilon), ctypes.byref(kv_cache), int(layer_idx),
+        PKV_DTYPE_F32 if q_rope_output.dtype == torch.float32 else PKV_DTYPE_BF16,
+        _stream(stream))
+    _check("mla_rope_rmsnorm_inplace_planned", st)
 
 
 def qk_rope_paged_ragged(q_out: torch.Tensor, q_proj: torch.Tensor,

@@ -311,8 +311,6 @@ __global__ __launch_bounds__(256) void mla_kernel(const MlaArgs a) {
   }
 }
 
-// The planned form exists for the three buffer modes (the in-place form
-// keeps the address chain).
 template <int NI, bool QF32, bool PLANNED>
 hipError_t launch_g(const MlaArgs& a, MlaOut mode, uint32_t blocks, hipStream_t stream) {
   switch (mode) {
@@ -329,10 +327,8 @@ hipError_t launch_g(const MlaArgs& a, MlaOut mode, uint32_t blocks, hipStream_t 
                          dim3(256), 0, stream, a);
       break;
     case MlaOut::Bf16InPlace:
-      if constexpr (PLANNED) return hipErrorInvalidValue;
-      else
-        hipLaunchKernelGGL((mla_kernel<NI, MlaOut::Bf16InPlace, QF32, false>), dim3(blocks),
-                           dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((mla_kernel<NI, MlaOut::Bf16InPlace, QF32, PLANNED>), dim3(blocks),
+                         dim3(256), 0, stream, a);
       break;
   }
   return hipGetLastError();

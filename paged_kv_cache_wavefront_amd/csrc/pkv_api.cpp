@@ -225,6 +225,21 @@ int pkv_token_plan(uint32_t* token_plan, const uint32_t* input_row_offsets,
   return launch_status(pkv::launch_plan(a, static_cast<hipStream_t>(stream)));
 }
 
+int mla_rope_rmsnorm_inplace_planned(void* q_rope_out, int64_t qo_tok_stride,
+                                     int64_t qo_head_stride, const void* q_rope,
+                                     int64_t qi_tok_stride, int64_t qi_head_stride,
+                                     const uint32_t* token_plan, uint32_t total_tokens,
+                                     uint32_t num_heads, uint32_t rope_dim,
+                                     uint32_t kv_norm_dim, const float* freqs_cis,
+                                     uint32_t max_seq_len, const void* gamma, float epsilon,
+                                     const pkv_paged_cache* kv_cache, uint32_t layer_idx,
+                                     int32_t q_out_dtype, void* stream) {
+  return mla_entry(q_rope_out, qo_tok_stride, qo_head_stride, q_rope, qi_tok_stride,
+                   qi_head_stride, nullptr, 0, true, true, token_plan, nullptr, 0, total_tokens,
+                   num_heads, rope_dim, kv_norm_dim, freqs_cis, max_seq_len, gamma, epsilon,
+                   kv_cache, layer_idx, q_out_dtype, stream);
+}
+
 int mla_rope_rmsnorm_quant_planned(void* q_rope_out, int64_t qo_tok_stride,
                                    int64_t qo_head_stride, const void* q_rope,
                                    int64_t qi_tok_stride, int64_t qi_head_stride,

@@ -33,6 +33,7 @@ def pkv():
 def test_header_declares_entry_points():
     assert declared_functions() == sorted(["mla_rope_rmsnorm_quant", "mla_rope_rmsnorm_inplace",
                                            "pkv_token_plan", "mla_rope_rmsnorm_quant_planned",
+                                           "mla_rope_rmsnorm_inplace_planned",
                                            "qk_rope_paged_ragged", "rms_norm_kv_cache_paged",
                                            "rms_norm_kv_cache_paged_planned",
                                            "mla_gather_latent_paged", "pkv_status_string",
@@ -194,6 +195,24 @@ def test_kv_norm_planned_validation(pkv):
     assert call_kv_planned(pkv, kcache(pkv), layer=2) == RANGE
     # placement comes from the plan: lengths and page table may be absent
     assert call_kv_planned(pkv, kcache(pkv, cache_lengths=None, page_table=None), T=0) == OK
+
+
+def test_mla_inplace_planned_validation(pkv):
+    lib = pkv.library()
+    bf16 = dict(dtype=pkv.PKV_DTYPE_BF16, scale_mode=pkv.PKV_SCALE_NONE, scales=None,
+                cache_lengths=None, page_table=None)
+
+    def call(cache, plan=FAKE, T=16, layer=1):
+        cp = None if cache is None else ctypes.byref(cache)
+        return lib.mla_rope_rmsnorm_inplace_planned(FAKE, 4 * 64, 64, FAKE, 4 * 64, 64, plan, T,
+                                                    4, 64, 512, FAKE, 64, FAKE, 1e-6, cp, layer,
+                                                    0, None)
+    assert call(None) == NULL
+    assert call(mla_cache(pkv)) == DTYPE                 # an fp8 cache cannot hold the rows
+    assert call(mla_cache(pkv, **bf16), plan=None) == NULL
+    assert call(mla_cache(pkv, **bf16), plan=FAKE + 4) == ALIGN
+    assert call(mla_cache(pkv, **bf16), layer=2) == RANGE
+    assert call(mla_cache(pkv, **bf16), T=0) == OK
 
 
 def test_planned_bindings_check_plan_rows(pkv):
@@ -402,7 +421,11 @@ def test_headers_compile_as_c_and_cxx(tmp_path):
                    "  int (*f6)(const pkv_paged_cache*, uint32_t, const void*, uint32_t, float,"
                    " float, uint32_t, const uint32_t*, int, int, void*) ="
                    " rms_norm_kv_cache_paged_planned;\n"
-                   "  (void)f4; (void)f5; (void)f6;\n"
+                   "  int (*f7)(void*, int64_t, int64_t, const void*, int64_t, int64_t,"
+                   " const uint32_t*, uint32_t, uint32_t, uint32_t, uint32_t, const float*,"
+                   " uint32_t, const void*, float, const pkv_paged_cache*, uint32_t, int32_t,"
+                   " void*) = mla_rope_rmsnorm_inplace_planned;\n"
+                   "  (void)f4; (void)f5; (void)f6; (void)f7;\n"
                    "  int (*f3)(const void*, void*, uint64_t, uint32_t, void*) = pkv_stream_copy;\n"
                    "  (void)f1; (void)f2; (void)f3;\n"
                    "  return 0;\n}\n")

@@ -236,3 +236,30 @@ def test_kv_norm_planned_skips(orc):
     d = gh.bf16_ulp_diff(k, k_o)
     assert int(d.max(initial=0)) <= 1
     assert float((d != 0).sum() / d.size) <= max(gh.BF16_MAX_DIFF_FRAC, 3 / d.size)
+
+
+def _inplace_cases():
+    yield from oracle_pins.small_mla_inplace_cases()
+    yield workloads.mla_prefill_inplace()
+
+
+@pytest.mark.parametrize("idx", range(len(list(oracle_pins.small_mla_inplace_cases())) + 1))
+def test_inplace_planned_equals_batch_form(orc, idx):
+    """The in-place step placed by its batch's plan reads and writes exactly
+    what the batch in-place form does, and meets the oracle's parity bars."""
+    import paged_kv_cache_wavefront_amd as pkv
+    case = list(_inplace_cases())[idx]
+    _say(f"[inplace-planned] case={case.name} seed={case.seed} T={case.T} H={case.H}")
+    ref, dev = gh.MlaDevice(case), gh.MlaDevice(case)
+    ref.place_rows()
+    dev.place_rows()
+    ref.run_inplace()
+    plan = gpu_plan(dev)
+    pkv.mla_rope_rmsnorm_inplace_planned(dev.q_out, dev.q_in, plan, dev.freqs, dev.gamma,
+                                         case.epsilon, dev.desc, case.layer_idx)
+    g, r = dev.results(), ref.results()
+    assert g[3] == r[3] == 0
+    assert np.array_equal(g[0].view(np.uint16), r[0].view(np.uint16)), "q_rope_output differs"
+    assert np.array_equal(g[1], r[1]), "cache differs"
+    stats = gh.compare_mla(case, g, gh.oracle_mla_inplace(orc, case), small_case_floor=3)
+    _say(f"[inplace-planned] {case.name}: {stats}")
