@@ -16,8 +16,9 @@
 // of two, so for D = 64, 128, 256 every Q instruction moves 64 x 16
 // contiguous bytes, and for D = 80, 96 (10 or 12 chunks in a 16-lane group)
 // the idle lanes of each group neither load nor store.  An fp8 K head is read
-// as 8 codes per lane (8 bytes), decoded and scaled in registers (code x
-// scale), and re-encoded with the tensor scale or with a fresh per-(slot,
+// as 8 codes per lane (8 bytes), decoded in registers, rotated, scaled (the
+// head's scale applies to both members of every pair, so it commutes with the
+// rotation), and re-encoded with the tensor scale or with a fresh per-(slot,
 // head) scale max|y| / 448 from a DPP max over the head's lanes.
 // * interleaved: lane k holds values 8k..8k+7 = adjacent pairs 4k..4k+3.
 // * rotate-half (H = D/16 chunks per half): lane k < H holds values 8k.. of
@@ -37,6 +38,8 @@
 // as x * gamma (exact in fp32) and r is applied after it, so an fp32 rounding
 // of x * r * gamma cannot be amplified by cancellation in the rotation; a
 // pair with one normalised and one plain member takes r before the rotation.
+// An fp8 head enters the rotation as its codes (times gamma), and its scale
+// joins r after the rotation for the same reason.
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -267,9 +270,12 @@ __global__ __launch_bounds__(256) void qk_rope_kernel(const QkArgs a) {
   if (chunk != 0) return;
 
   // ---- K (in place), optional per-head RMSNorm first ------------------------
-  // bf16: 16 bytes per lane; fp8: 8 bytes per lane (code * scale on load, a
-  // per-tensor cache re-encodes with its scale, a per-token cache stores a
-  // fresh max|y| / 448 per head).
+  // bf16: 16 bytes per lane; fp8: 8 bytes per lane, decoded to the codes'
+  // exact values.  Both members of a rotation pair belong to one head and so
+  // share its scale (and its r), so the rotation runs on code x gamma (exact
+  // in fp32: 4- and 8-bit significands) and scale x r is applied once after
+  // it; a per-tensor cache re-encodes with its scale, a per-token cache
+  // stores a fresh max|y| / 448 per head.
   constexpr int64_t EB = KM == KMode::Bf16 ? 2 : 1;
   const bool knorm = a.k_gamma != nullptr;
   const int C = (int)a.k_norm_cols;
@@ -287,6 +293,7 @@ __global__ __launch_bounds__(256) void qk_rope_kernel(const QkArgs a) {
     const bool valid = h < cv.num_heads && (!Geo::kPadded || role.active);
     char* p = krow + EB * (int64_t)hbase * cv.head_stride + k_off;
     float own[8], par[8] = {};
+    float ks = 1.0f;  // the head's dequantisation scale (fp8)
     if constexpr (KM == KMode::Bf16) {
       uint4 kv = make_uint4(0, 0, 0, 0);
       if (valid) kv = load16(p);
@@ -294,40 +301,44 @@ __global__ __launch_bounds__(256) void qk_rope_kernel(const QkArgs a) {
       if constexpr (!INTER) unpack8(mirror16<LP>(kv), par);
     } else {
       uint2 kv = make_uint2(0, 0);
-      float ks = 0.0f;
+      ks = 0.0f;
       if (valid) {
         kv = *reinterpret_cast<const uint2*>(p);
         ks = KM == KMode::Fp8PerTensor ? a.k_scales[0] : a.k_scales[slot_head0 + h];
       }
       unpack8_fp8(kv.x, kv.y, own);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) own[j] *= ks;
-      if constexpr (!INTER) {  // the partner lane belongs to the same head: same scale
-        unpack8_fp8(mirror_u32<LP>(kv.x), mirror_u32<LP>(kv.y), par);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) par[j] *= ks;
-      }
+      if constexpr (!INTER) unpack8_fp8(mirror_u32<LP>(kv.x), mirror_u32<LP>(kv.y), par);
     }
     if (!knorm) {
       rotate_plain<INTER>(own, par, cs);
+      if constexpr (KM != KMode::Bf16) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) own[j] *= ks;
+      }
     } else {
+      // statistic of the head's values x = code x scale (bf16: scale 1):
+      // mean(x^2) = scale^2 mean(code^2)
       float ss = 0.0f;
 #pragma unroll
       for (int j = 0; j < 8; ++j)
         if (col + j < C) ss = fmaf(own[j], own[j], ss);
       ss = group_sum<LP>(ss);
+      if constexpr (KM != KMode::Bf16) ss = (ss * ks) * ks;
       const float r = 1.0f / sqrtf(ss / (float)C + a.epsilon);
+      const float kr = ks * r;
       float pre_own[8], pre_par[8], post[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        own[j] *= g[j];  // exact for bf16 K (bf16 x bf16); g = 1 past C
+        own[j] *= g[j];  // exact: bf16 x bf16 or code x bf16; g = 1 past C
         par[j] *= gp[j];
-        // is this value / its pair partner inside the normalised span?
+        // is this value / its pair partner inside the normalised span?  A
+        // pair with both members inside takes scale x r after the rotation,
+        // a pair with one member inside takes r on that member before it.
         const bool in_me = col + j < C;
         const bool in_other = INTER ? (col + (j ^ 1) < C) : (pcol + j < C);
         pre_own[j] = (in_me && !in_other) ? r : 1.0f;
         pre_par[j] = (in_other && !in_me) ? r : 1.0f;
-        post[j] = (in_me && in_other) ? r : 1.0f;
+        post[j] = (in_me && in_other) ? kr : ks;
       }
       rotate_scaled<INTER>(own, par, cs, pre_own, pre_par, post);
     }

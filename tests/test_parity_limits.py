@@ -60,9 +60,9 @@ def test_qk_many_requests(orc):
     orc.qk_rope_paged_ragged(q_o, case.q, case.row_offsets, case.cache_lengths, case.page_table,
                              k_o, case.layer_idx, case.freqs, case.position_ids,
                              case.interleaved, case.gamma, case.epsilon)
-    from test_parity_qk import NORM_SLACK, check_k_rows
+    from test_parity_qk import check_k_rows
     gh.check_bf16(q, q_o, "q")
-    _say(f"[limits] {check_k_rows(case, k, k_o, 'k', NORM_SLACK)}")
+    _say(f"[limits] {check_k_rows(case, k, k_o, 'k', case.gamma.size)}")
 
 
 def test_kv_norm_many_requests(orc):
@@ -155,7 +155,7 @@ def test_qk_and_kv_norm_cache_beyond_4gib(orc):
     on a bf16 K pool of more than 8 GiB (the small interleaved case's pages at
     the top)."""
     import paged_kv_cache_wavefront_amd as pkv
-    from test_parity_qk import NORM_SLACK, check_k_rows
+    from test_parity_qk import check_k_rows
     case = list(oracle_pins.small_qk_cases())[0]
     L, P, S, Hkv, D = case.k_cache.shape
     big_p = _big_pool_pages(S * Hkv * D * 2, P)
@@ -194,7 +194,7 @@ def test_qk_and_kv_norm_cache_beyond_4gib(orc):
     orc.rms_norm_kv_cache_paged(k_norm, case.layer_idx, case.row_offsets, case.cache_lengths,
                                 case.page_table, case.gamma, case.epsilon, 0.0, case.T, True)
     gh.check_bf16(q, q_o, "q")
-    _say(f"[limits] rope K {check_k_rows(case, results['rope'], k_rope, 'k', NORM_SLACK)}")
+    _say(f"[limits] rope K {check_k_rows(case, results['rope'], k_rope, 'k', case.gamma.size)}")
     rows = gh.written_k_rows(case)
     assert np.array_equal(results["norm"][~rows], case.k_cache[~rows])
     _say(f"[limits] norm K {gh.check_bf16(results['norm'][rows], k_norm[rows], 'k norm')}")

@@ -112,7 +112,7 @@ def _random_qk(rng, seed):
 
 @pytest.mark.parametrize("seed", range(N_CASES))
 def test_qk_random(orc, seed):
-    from test_parity_qk import NORM_SLACK, check_fp8_k, check_k_rows, oracle_qk
+    from test_parity_qk import check_fp8_k, check_k_rows, oracle_qk
     rng = np.random.default_rng(9100 + seed)
     case, cfg = _random_qk(rng, seed)
     with_norm = case.gamma is not None
@@ -125,10 +125,11 @@ def test_qk_random(orc, seed):
     q_o, k_o, ks_o, pre = oracle_qk(orc, case, with_norm, with_scales=True)
     stats = {"q": gh.check_bf16(q, q_o, "q", max_frac=_frac_cap(q.size))}
     if case.k_cache.dtype == np.uint8:
-        stats["k"] = check_fp8_k(case, k, ks, k_o, ks_o, pre, "k")
+        stats["k"] = check_fp8_k(case, k, ks, k_o, ks_o, pre, "k",
+                                 case.gamma.size if with_norm else None)
     else:
         n = int(gh.written_k_rows(case).sum()) * case.k_cache[0, 0, 0].size
-        stats["k"] = check_k_rows(case, k, k_o, "k", NORM_SLACK if with_norm else 0.0,
+        stats["k"] = check_k_rows(case, k, k_o, "k", case.gamma.size if with_norm else None,
                                   max_frac=_frac_cap(n))
     _say(f"[rand-qk] {stats}")
 
@@ -172,7 +173,7 @@ def test_kv_norm_random(orc, seed):
                                         case.page_table, gamma, case.epsilon, w, total, mbc,
                                         case.k_scale_mode, ks_o, per_head_norm=per_head)
         # rows of tokens past total_seq_len stay as they were on both sides
-        _say(f"[rand-kvnorm] {check_fp8_k(case, k, ks, k_o, ks_o, pre, 'k', False)}")
+        _say(f"[rand-kvnorm] {check_fp8_k(case, k, ks, k_o, ks_o, pre, 'k')}")
         return
     orc.rms_norm_kv_cache_paged(k_o, case.layer_idx, case.row_offsets, case.cache_lengths,
                                 case.page_table, gamma, case.epsilon, w, total, mbc,
