@@ -123,6 +123,24 @@ def gather_bytes(rows: int, batch: int, page_size: int, in_bytes=576, out_bytes=
     return rows * (in_bytes + out_bytes) + (batch + 1) * 4 + 4 * (-(-rows // page_size))
 
 
+def written_bytes(name: str, case, rows: int = 0) -> int:
+    """The part of a workload's algorithmic bytes that is written (the rest
+    is read): q out and the cache rows (MLA), Q out and the K rows (Q/K RoPE),
+    the normalised K columns (K norm), the dense rows (gather)."""
+    if name.startswith("mla_"):
+        T, H, R, W = case.T, case.H, case.R, case.latent.shape[1]
+        out_b = 2 if case.cache.dtype == np.uint16 else 1
+        return T * (2 * H * R + W * out_b + (4 if case.scale_mode == "per_token" else 0))
+    if name == "qk_generic":
+        T, Hq, D = case.q.shape
+        return T * (Hq * D * 2 + case.k_cache.shape[3] * D * 2)
+    if name.startswith("kv_norm"):
+        return case.T * case.k_cache.shape[3] * 128 * 2
+    if name == "gather":
+        return rows * 1152
+    raise ValueError(name)
+
+
 def kv_norm_bytes(case, cols: int, planned: bool = False) -> int:
     """The first cols columns of every K head read and written back; gamma;
     offsets and prior lengths (planned: a 16-byte plan entry per token)."""
@@ -288,6 +306,120 @@ def cycle(fns):
     return step
 
 
+def alternate(batch, planned, steps, warmup, reps: int = 7) -> dict:
+    """The batch and planned forms of one step on the same buffers, timed by
+    graph replay in turn, reps times each: the per-repetition figures, their
+    medians and spreads, and the planned form's gain with the range of the
+    per-repetition gains (a gain is settled only when that range excludes
+    zero)."""
+    ab = {"batch": [], "planned": []}
+    for _ in range(reps):
+        ab["batch"].append(time_graph(batch, steps, warmup) * 1e6)
+        ab["planned"].append(time_graph(planned, steps, warmup) * 1e6)
+    b, p = np.array(ab["batch"]), np.array(ab["planned"])
+    gain = b - p
+    return {"batch": round(float(np.median(b)), 2), "planned": round(float(np.median(p)), 2),
+            "batch_min_max": [round(float(b.min()), 2), round(float(b.max()), 2)],
+            "planned_min_max": [round(float(p.min()), 2), round(float(p.max()), 2)],
+            "gain_us_median": round(float(np.median(gain)), 2),
+            "gain_us_min_max": [round(float(gain.min()), 2), round(float(gain.max()), 2)],
+            "settled": bool(gain.min() > 0 or gain.max() < 0),
+            "how": f"graph replay, batch and planned forms alternating, {reps} repetitions "
+                   "of the median of 5 replays each"}
+
+
+def matched_stream(read_b: int, write_b: int, inplace: bool, sets: int, rotate_reads: bool,
+                   use_graph: bool, steps: int, warmup: int) -> dict:
+    """A plain stream of a workload's own traffic (pkv_stream_mix): the same
+    bytes read and written, interleaved at the same ratio (in place when the
+    workload rewrites what it reads), over the same number of rotating output
+    buffers (and input buffers, where the workload rotates its inputs too),
+    timed the same way as the workload (graph replay or eager launches); the
+    best of a sweep of grid sizes.  Its time is what moving those bytes
+    costs here with no address chain, no arithmetic and no lane geometry."""
+    import torch
+    import paged_kv_cache_wavefront_amd as pkv
+    r16 = -(-read_b // 16) * 16
+    w16 = r16 if inplace else -(-write_b // 16) * 16
+    if inplace:
+        bufs = [torch.empty(r16, dtype=torch.uint8, device="cuda") for _ in range(sets)]
+        pairs = [(b, b) for b in bufs]
+    else:
+        srcs = [torch.empty(max(r16, 16), dtype=torch.uint8, device="cuda")
+                for _ in range(sets if rotate_reads else 1)]
+        dsts = [torch.empty(max(w16, 16), dtype=torch.uint8, device="cuda") for _ in range(sets)]
+        pairs = [(srcs[i % len(srcs)], d) for i, d in enumerate(dsts)]
+    per = {}
+    for blocks in (256, 1024, 4096, 16384, 65536):
+        fn = cycle([(lambda s_, d_: lambda: pkv.pkv_stream_mix(d_, s_, r16, w16, blocks))(s_, d_)
+                    for s_, d_ in pairs])
+        if use_graph:
+            t = time_graph(fn, steps, warmup)
+        else:
+            _, t, _ = time_launches(fn, steps, warmup, spread_samples=1)
+        per[blocks] = t
+    best = min(per, key=per.get)
+    del pairs
+    return {"read_bytes": r16, "write_bytes": w16, "in_place": inplace, "buffer_sets": sets,
+            "inputs_rotate": bool(rotate_reads or inplace),
+            "us": round(per[best] * 1e6, 2), "blocks": best,
+            "GBps": round((r16 + w16) / per[best] / 1e9, 1),
+            "us_by_blocks": {b: round(v * 1e6, 2) for b, v in per.items()},
+            "timed_as": "hip graph replay" if use_graph else "eager launches"}
+
+
+_FLOOR = {}
+
+
+def launch_floor(blocks: int) -> float:
+    """Graph-replay time (us) of an almost empty launch (a 16-byte
+    pkv_stream_mix) of `blocks` blocks of 256 threads: the fixed cost of a
+    launch of that grid, below which no kernel of that grid can go."""
+    if blocks not in _FLOOR:
+        import torch
+        import paged_kv_cache_wavefront_amd as pkv
+        a = torch.empty(16, dtype=torch.uint8, device="cuda")
+        b = torch.empty(16, dtype=torch.uint8, device="cuda")
+        _FLOOR[blocks] = round(
+            time_graph(lambda: pkv.pkv_stream_mix(b, a, 16, 16, blocks), 100, 3) * 1e6, 2)
+    return _FLOOR[blocks]
+
+
+def grid_blocks(name: str, case, rows: int = 0) -> int:
+    """Blocks of 256 threads (4 waves) the entry point launches for a
+    workload, as its launch code sizes the grid: MLA one wave per token and
+    chunk of 32 heads (16 for at most 16 heads); Q/K RoPE one per token and
+    chunk of 16 heads of 128; K norm and the token plan one per token; gather
+    one per 6 rows."""
+    if name.startswith("mla_"):
+        hpw = 32 if case.H > 16 else 16
+        waves = case.T * -(-case.H // hpw)
+    elif name == "qk_generic":
+        waves = case.T * -(-int(case.q.shape[1]) // 16)
+    elif name.startswith("kv_norm"):
+        waves = case.T
+    elif name == "gather":
+        waves = -(-rows // 6)
+    else:
+        raise ValueError(name)
+    return -(-waves // 4)
+
+
+def with_references(name, r, case, steps, warmup, use_graph):
+    """The workload's figures beside a matched stream of its own traffic and
+    the empty-launch floor of its grid (both measured now, in this run)."""
+    total = r["bytes"]
+    w = written_bytes(name, case, r["T"] if name == "gather" else 0)
+    spec = r["stream_spec"]
+    ms = matched_stream(total - w, w, spec["in_place"], spec["sets"], spec["rotate_reads"],
+                        use_graph, steps, warmup)
+    t = r["graph_avg"] if use_graph and r["graph_avg"] else r["avg"]
+    blocks = grid_blocks(name, case, r["T"] if name == "gather" else 0)
+    return {"matched_stream": ms,
+            "pct_of_matched_stream": round(100.0 * ms["us"] * 1e-6 / t, 1),
+            "launch_floor_us": launch_floor(blocks), "grid_blocks": blocks}
+
+
 def run_workload(name, steps, warmup):
     """(summary, label, case) for one named workload of any entry point; the
     summary's "sets" is the number of buffer sets the steps rotate over."""
@@ -306,6 +438,7 @@ def run_workload(name, steps, warmup):
             d.place_rows()
         fns = [d.run_inplace for d in devs]
         how = f"{n} sets of q, q_out and bf16 cache pool"
+        spec = dict(in_place=False, sets=n, rotate_reads=True)
         r = measure(cycle(fns), case.T, mla_bytes(case), steps, warmup)
         label = name
     elif name.startswith("mla_") and name.endswith("_planned"):
@@ -333,6 +466,7 @@ def run_workload(name, steps, warmup):
         devs = (dev, outs, plan, plans)
         how = (f"{n} q_out buffers (one cache pool and one plan; the new rows are "
                f"{case.T * 576} bytes)")
+        spec = dict(in_place=False, sets=n, rotate_reads=False)
         r = measure(cycle(fns), case.T, mla_bytes(case, planned=True), steps, warmup)
         r["plan_build"] = {"entry_point": "pkv_token_plan", "timed_as": "hip graph replay",
                            "us": round(build["graph_avg"] * 1e6, 2),
@@ -343,13 +477,7 @@ def run_workload(name, steps, warmup):
             o, dev.q_in, dev.latent, dev.offsets, dev.freqs, dev.gamma, case.epsilon, dev.desc,
             case.layer_idx))(o) for o in outs])
         planned_fn = cycle(fns)
-        ab = {"batch": [], "planned": []}
-        for _ in range(3):
-            ab["batch"].append(time_graph(batch, steps, warmup))
-            ab["planned"].append(time_graph(planned_fn, steps, warmup))
-        r["vs_batch_form"] = {k: round(float(np.median(v)) * 1e6, 2) for k, v in ab.items()}
-        r["vs_batch_form"]["how"] = ("graph replay, batch and planned forms alternating, "
-                                     "median of 3 x 5 replays")
+        r["vs_batch_form"] = alternate(batch, planned_fn, steps, warmup)
         label = f"{name} (plan built once, outside the timed launches)"
     elif name.startswith("mla_"):
         case = workloads.NAMED[name]()
@@ -362,6 +490,7 @@ def run_workload(name, steps, warmup):
             devs = [gh.MlaDevice(case) for _ in range(n)]
             fns = [d.run for d in devs]
             how = f"{n} sets of q, q_out, latent and cache pool"
+            spec = dict(in_place=False, sets=n, rotate_reads=True)
         else:
             # the pool is large and the new rows few: rotate q_out only
             n = rotation_count(q_out_bytes, q_out_bytes, cap=256)
@@ -375,6 +504,7 @@ def run_workload(name, steps, warmup):
             fns = [make(o) for o in outs]
             devs = (dev, outs)
             how = f"{n} q_out buffers (one cache pool; its new rows are {case.T * 576} bytes)"
+            spec = dict(in_place=False, sets=n, rotate_reads=False)
         r = measure(cycle(fns), case.T, mla_bytes(case), steps, warmup)
         label = name
     elif name == "qk_generic":
@@ -385,6 +515,7 @@ def run_workload(name, steps, warmup):
         devs = [gh.QkDevice(case) for _ in range(n)]
         fns = [(lambda d: (lambda: d.rope(True)))(d) for d in devs]
         how = f"{n} sets of q, q_out and K pool"
+        spec = dict(in_place=False, sets=n, rotate_reads=True)
         r = measure(cycle(fns), case.T, qk_bytes(case, True), steps, warmup)
         label = "qk_generic (interleaved, position ids, fused per-head K norm)"
     elif name in ("kv_norm", "kv_norm_planned"):
@@ -413,18 +544,13 @@ def run_workload(name, steps, warmup):
         fns = [(make_planned if planned else make)(d) for d in descs]
         devs = (base, pools, descs, plan)
         how = f"{n} K pools"
+        spec = dict(in_place=True, sets=n, rotate_reads=True)
         r = measure(cycle(fns), case.T, kv_norm_bytes(case, 128, planned), steps, warmup)
         label = "qk_generic K cache (8 heads x 128, gamma 128)"
         if planned:
             label += ", placed by a token plan built once"
             batch, planned_fn = cycle([make(d) for d in descs]), cycle(fns)
-            ab = {"batch": [], "planned": []}
-            for _ in range(3):
-                ab["batch"].append(time_graph(batch, steps, warmup))
-                ab["planned"].append(time_graph(planned_fn, steps, warmup))
-            r["vs_batch_form"] = {k: round(float(np.median(v)) * 1e6, 2) for k, v in ab.items()}
-            r["vs_batch_form"]["how"] = ("graph replay, batch and planned forms alternating, "
-                                         "median of 3 x 5 replays")
+            r["vs_batch_form"] = alternate(batch, planned_fn, steps, warmup)
     elif name == "gather":
         case = workloads.mla_decode()
         ctx = case.cache_lengths.astype(np.int64) + 1
@@ -443,6 +569,7 @@ def run_workload(name, steps, warmup):
         fns = [make(o) for o in outs]
         devs = (cache, kv, outs, desc)
         how = f"{n} output buffers"
+        spec = dict(in_place=False, sets=n, rotate_reads=False)
         r = measure(cycle(fns), rows, gather_bytes(rows, case.B, case.meta["page_size"]), steps,
                     warmup)
         label = f"gather of {case.B} request contexts ({rows} rows) fp8 -> bf16"
@@ -450,6 +577,7 @@ def run_workload(name, steps, warmup):
         raise ValueError(name)
     r["keep"] = devs
     r["sets"] = how
+    r["stream_spec"] = spec
     return r, label, case
 
 
@@ -467,13 +595,15 @@ def measure_siblings(main, steps, warmup):
         if name == main:
             continue
         log(f"[bench] sibling {name}")
-        r, label, _ = run_workload(name, steps, warmup)
+        r, label, case = run_workload(name, steps, warmup)
         out[name] = {"entry_point": entry, **summarize(label, r, steps, use_graph=True),
-                     "traffic": profiled_traffic(name)}
+                     "traffic": profiled_traffic(name),
+                     **with_references(name, r, case, steps, warmup, use_graph=True)}
         if "plan_build" in r:
             out[name]["plan_build"] = r["plan_build"]
         if "vs_batch_form" in r:
             out[name]["vs_batch_form_us"] = r["vs_batch_form"]
+        del r
     return out
 
 
@@ -503,26 +633,51 @@ def token_chunks(case, n: int):
 
 
 def cpu_model() -> str:
+    """The host CPU's name: /proc/cpuinfo's model name, with lscpu's when that
+    is longer, and the family / model / stepping numbers (some hosts report
+    only a family name such as "AMD EPYC")."""
+    info = {}
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            k, _, v = line.partition(":")
+            k = k.strip()
+            if k in ("model name", "cpu family", "model", "stepping") and k not in info:
+                info[k] = v.strip()
     except OSError:
         pass
-    return "unknown"
+    name = info.get("model name", "unknown")
+    try:
+        import subprocess
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                alt = line.split(":", 1)[1].strip()
+                if len(alt) > len(name):
+                    name = alt
+    except (OSError, subprocess.SubprocessError):
+        pass
+    ids = ", ".join(f"{k} {info[k]}" for k in ("cpu family", "model", "stepping") if k in info)
+    return f"{name} ({ids})" if ids else name
+
+
+# Host threads for the multi-threaded oracle leg: the cores this process may
+# run on, capped at the host CPU share of one GPU on the boxes this runs on
+# (16 threads; OMP_NUM_THREADS carries the same figure there).
+CPU_SHARE = 16
 
 
 def cpu_baseline(case, budget_s=10.0):
-    """The oracle (C, binary64) on the same host arrays: single-threaded over
-    the whole workload until about budget_s has elapsed; then the same oracle
-    function called from N host threads at once on N token-balanced slices of
-    the batch (ctypes releases the GIL, so the calls run in parallel), for
-    about budget_s / 2, with its outputs checked bit for bit against the
-    single-threaded run."""
+    """The oracle (C, binary64) on the same host arrays, as it stands: called
+    from N host threads at once on N token-balanced slices of the batch
+    (ctypes releases the GIL, so the calls run in parallel) for about
+    budget_s -- the reported figure, cores = N -- and single-threaded over the
+    whole workload for about budget_s / 2 (``single_thread``); the threaded
+    outputs are checked bit for bit against the single-threaded run."""
     import oracle
     from concurrent.futures import ThreadPoolExecutor
     orc = oracle.default()
     q_out = np.zeros_like(case.q)
+    bytes_per_token = mla_bytes(case) / max(case.T, 1)  # the same byte model as the GPU line
 
     def whole(cache):
         orc.mla_rope_rmsnorm_quant(q_out, case.q, case.latent, case.row_offsets,
@@ -539,17 +694,18 @@ def cpu_baseline(case, budget_s=10.0):
         runs += 1
         tokens += case.T
         spent = time.perf_counter() - t0
-        if spent >= budget_s or (time.perf_counter() - t1) * (runs + 1) > 3 * budget_s:
+        if spent >= budget_s / 2 or (time.perf_counter() - t1) * (runs + 1) > 1.5 * budget_s:
             break
-    oracle_s = time.perf_counter() - t0
-    bytes_per_token = mla_bytes(case) / max(case.T, 1)  # the same byte model as the GPU line
-    out = {"value": round(tokens / oracle_s, 1), "unit": "tokens/s", "cores": 1,
-           "GBps": round(tokens / oracle_s * bytes_per_token / 1e9, 3),
-           "kind": "oracle", "cpu_model": cpu_model(),
-           "sample": f"whole workload ({case.T} tokens) x {runs} run(s), "
-                     f"{oracle_s:.1f} s, single thread"}
+    single_s = time.perf_counter() - t0
+    single = {"value": round(tokens / single_s, 1), "unit": "tokens/s", "cores": 1,
+              "GBps": round(tokens / single_s * bytes_per_token / 1e9, 3),
+              "sample": f"whole workload ({case.T} tokens) x {runs} run(s), {single_s:.1f} s, "
+                        "one thread"}
 
-    n = max(1, min(len(os.sched_getaffinity(0)), 16))
+    affinity = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    share = int(omp) if omp.isdigit() and int(omp) > 0 else CPU_SHARE
+    n = max(1, min(affinity, share))
     chunks = token_chunks(case, n)
     q_par = np.zeros_like(case.q)
 
@@ -567,15 +723,19 @@ def cpu_baseline(case, budget_s=10.0):
             list(ex.map(lambda c: part(c, cache_par), chunks))
             runs += 1
             tokens += case.T
-            if time.perf_counter() - t0 >= budget_s / 2:
+            if time.perf_counter() - t0 >= budget_s:
                 break
         par_s = time.perf_counter() - t0
     same = bool(np.array_equal(q_par, q_out) and np.array_equal(cache_par, cache))
-    out["threads"] = {"value": round(tokens / par_s, 1), "cores": len(chunks),
-                      "GBps": round(tokens / par_s * bytes_per_token / 1e9, 3),
-                      "sample": f"whole workload x {runs} run(s), {par_s:.1f} s, "
-                                f"{len(chunks)} threads on token-balanced slices",
-                      "same_bits_as_single_thread": same}
+    out = {"value": round(tokens / par_s, 1), "unit": "tokens/s", "cores": len(chunks),
+           "kind": "oracle",
+           "sample": f"whole workload ({case.T} tokens) x {runs} run(s), {par_s:.1f} s, "
+                     f"{len(chunks)} host threads on token-balanced slices",
+           "GBps": round(tokens / par_s * bytes_per_token / 1e9, 3),
+           "cpu_model": cpu_model(), "affinity_cores": affinity,
+           "threads_cap": f"min(affinity {affinity}, host CPU share of one GPU {share})",
+           "same_bits_as_single_thread": same,
+           "single_thread": single}
     return out, (q_out, cache)
 
 
@@ -649,6 +809,9 @@ def main():
     ap.add_argument("--no-siblings", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--no-references", action="store_true",
+                    help="skip the streaming-copy and matched-stream reference measurements "
+                         "(for profiler runs that only need the workload's own launches)")
     ap.add_argument("--source-hash", action="store_true",
                     help="print the hash of the workload's kernel sources and exit")
     args = ap.parse_args()
@@ -680,7 +843,10 @@ def main():
         cpu, oracle_out = cpu_baseline(case)
         if args.workload != "mla_prefill_inplace":
             parity = parity_stats(case, oracle_out)
-    copy_ref = measured_copy(args.steps, args.warmup)
+    copy_ref = refs = None
+    if not args.no_references:
+        copy_ref = measured_copy(args.steps, args.warmup)
+        refs = with_references(args.workload, r, case, args.steps, args.warmup, use_graph=False)
     traffic = profiled_traffic(args.workload)
     is_mla = args.workload.startswith("mla_")
     if is_mla:
@@ -720,7 +886,8 @@ def main():
         "pct_of_hbm_peak": main_sum["pct_of_hbm_peak"],
         "buffer_rotation": main_sum["buffer_rotation"],
         "measured_copy": copy_ref,
-        "pct_of_measured_copy": round(100.0 * gbps / copy_ref["GBps"], 1),
+        "pct_of_measured_copy": round(100.0 * gbps / copy_ref["GBps"], 1) if copy_ref else None,
+        **(refs or {}),
         "kernel_us": {k: main_sum[k] for k in ("kernel_us_avg", "eager_us_p10_p50_p90",
                                                "cold_us_p10_p50_p90", "graph_us_avg")},
         "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",

@@ -110,6 +110,8 @@ def _load() -> ctypes.CDLL:
     lib.pkv_status_string.argtypes = [ctypes.c_int]
     lib.pkv_stream_copy.restype = ctypes.c_int
     lib.pkv_stream_copy.argtypes = [vp, vp, ctypes.c_uint64, u32, vp]
+    lib.pkv_stream_mix.restype = ctypes.c_int
+    lib.pkv_stream_mix.argtypes = [vp, ctypes.c_uint64, vp, ctypes.c_uint64, u32, vp]
     return lib
 
 
@@ -213,14 +215,28 @@ def mla_rope_rmsnorm_inplace(q_rope_output: torch.Tensor, q_rope: torch.Tensor,
     _check("mla_rope_rmsnorm_inplace", st)
 
 
+def _check_plan(plan: torch.Tensor, rows: int, like: torch.Tensor | None, what: str) -> None:
+    """A token plan is a contiguous [>= rows, 4] int32 / uint32 tensor on the
+    device of the other tensors: the library writes or reads 16 bytes per
+    token through its raw pointer and cannot check any of this itself."""
+    if plan.dim() != 2 or plan.shape[1] != 4 or not plan.is_contiguous():
+        raise ValueError("plan must be a contiguous [tokens, 4] tensor")
+    if plan.dtype not in (torch.int32, torch.uint32):
+        raise TypeError(f"plan must be int32 or uint32, not {plan.dtype}")
+    if plan.shape[0] < rows:
+        raise ValueError(f"plan has fewer rows than {what}")
+    if not plan.is_cuda or (like is not None and plan.device != like.device):
+        where = "a ROCm device" if like is None else str(like.device)
+        raise ValueError(f"plan must live on {where}, not {plan.device}")
+
+
 def pkv_token_plan(plan: torch.Tensor, input_row_offsets: torch.Tensor, kv_cache: PagedCache,
                    stream=None) -> None:
     """Write each new token's placement (C: ``pkv_token_plan``) into ``plan``,
     a contiguous ``[tokens, 4]`` int32 / uint32 tensor: (page, offset,
     position, 1), or zeros for a token without a valid placement.  The
     token count is ``plan.shape[0]``."""
-    if plan.dim() != 2 or plan.shape[1] != 4 or not plan.is_contiguous():
-        raise ValueError("plan must be a contiguous [tokens, 4] tensor")
+    _check_plan(plan, 0, input_row_offsets, "tokens")
     st = _lib.pkv_token_plan(_ptr(plan), _ptr(input_row_offsets),
                              input_row_offsets.numel() - 1, plan.shape[0],
                              ctypes.byref(kv_cache), _stream(stream))
@@ -237,10 +253,7 @@ def mla_rope_rmsnorm_quant_planned(q_rope_output: torch.Tensor, q_rope: torch.Te
     :func:`mla_rope_rmsnorm_quant` with ``plan`` (``[tokens, 4]``, from
     :func:`pkv_token_plan`) in place of the row offsets."""
     T, H, R = q_rope.shape
-    if plan.dim() != 2 or plan.shape[1] != 4 or not plan.is_contiguous():
-        raise ValueError("plan must be a contiguous [tokens, 4] tensor")
-    if plan.shape[0] < T:
-        raise ValueError("plan has fewer rows than q_rope has tokens")
+    _check_plan(plan, T, q_rope, "q_rope has tokens")
     st = _lib.mla_rope_rmsnorm_quant_planned(
         _ptr(q_rope_output), q_rope_output.stride(0), q_rope_output.stride(1),
         _ptr(q_rope), q_rope.stride(0), q_rope.stride(1),
@@ -261,10 +274,7 @@ def mla_rope_rmsnorm_inplace_planned(q_rope_output: torch.Tensor, q_rope: torch.
     :func:`mla_rope_rmsnorm_inplace` with ``plan`` in place of the row
     offsets."""
     T, H, R = q_rope.shape
-    if plan.dim() != 2 or plan.shape[1] != 4 or not plan.is_contiguous():
-        raise ValueError("plan must be a contiguous [tokens, 4] tensor")
-    if plan.shape[0] < T:
-        raise ValueError("plan has fewer rows than q_rope has tokens")
+    _check_plan(plan, T, q_rope, "q_rope has tokens")
     st = _lib.mla_rope_rmsnorm_inplace_planned(
         _ptr(q_rope_output), q_rope_output.stride(0), q_rope_output.stride(1),
         _ptr(q_rope), q_rope.stride(0), q_rope.stride(1), _ptr(plan), T, H, R,
@@ -318,10 +328,7 @@ def rms_norm_kv_cache_paged_planned(k_cache: PagedCache, layer_idx: int, gamma: 
     """In-place K-cache RMSNorm placed by a token plan (C:
     ``rms_norm_kv_cache_paged_planned``); ``plan`` is the ``[tokens, 4]``
     tensor :func:`pkv_token_plan` wrote."""
-    if plan.dim() != 2 or plan.shape[1] != 4 or not plan.is_contiguous():
-        raise ValueError("plan must be a contiguous [tokens, 4] tensor")
-    if plan.shape[0] < total_seq_len:
-        raise ValueError("plan has fewer rows than total_seq_len")
+    _check_plan(plan, int(total_seq_len), gamma, "total_seq_len")
     st = _lib.rms_norm_kv_cache_paged_planned(
         ctypes.byref(k_cache), int(layer_idx), _ptr(gamma), gamma.numel(), float(epsilon),
         float(weight_offset), int(total_seq_len), _ptr(plan), int(bool(per_head_norm)),
@@ -352,3 +359,18 @@ def pkv_stream_copy(dst: torch.Tensor, src: torch.Tensor, blocks: int, stream=No
         raise ValueError("dst smaller than src")
     st = _lib.pkv_stream_copy(_ptr(src), _ptr(dst), nbytes, int(blocks), _stream(stream))
     _check("pkv_stream_copy", st)
+
+
+def pkv_stream_mix(dst: torch.Tensor, src: torch.Tensor, read_bytes: int, write_bytes: int,
+                   blocks: int, stream=None) -> None:
+    """Measurement helper (C: ``pkv_stream_mix``, include/pkv_bench.h): read
+    ``read_bytes`` of src and write ``write_bytes`` of dst in one streaming
+    kernel, the two interleaved at that ratio; ``dst is src`` streams in
+    place."""
+    if read_bytes > src.numel() * src.element_size():
+        raise ValueError("src smaller than read_bytes")
+    if write_bytes > dst.numel() * dst.element_size():
+        raise ValueError("dst smaller than write_bytes")
+    st = _lib.pkv_stream_mix(_ptr(src), int(read_bytes), _ptr(dst), int(write_bytes),
+                             int(blocks), _stream(stream))
+    _check("pkv_stream_mix", st)

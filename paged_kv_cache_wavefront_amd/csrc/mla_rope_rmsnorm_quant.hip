@@ -8,30 +8,32 @@
 // cache of layer layer_idx at the token's slot.
 //
 // Design (bandwidth bound; no dense contraction, so no MFMA):
-// * One wave64 per (token, chunk of heads).  Each wave instruction moves 8
-//   whole heads = 1 KiB of contiguous q: lane l serves head l/8 of the
-//   instruction and one 16-byte chunk (8 values) of it.  Within a head's 8
-//   lanes, lane k < 4 holds values 8k..8k+7 (first half) and lane k >= 4 holds
-//   values 32 + 8(7-k) .. (second half, mirrored), so the rotate-half partner
-//   of lane k is lane 7-k and arrives with one DPP row_half_mirror per dword:
-//   no LDS round trip, and every load and store covers full 128-byte lines.
+// * One wave64 per (token, chunk of heads) work item.  Each wave instruction
+//   moves 1 KiB of contiguous q: a head's rope slice of R values is R/8
+//   16-byte chunks held by a group of LP = R/8 lanes (LP = 4, 8, 16 for
+//   rope_dim 32, 64, 128), 64/LP heads per instruction.  Within a group,
+//   lane k < LP/2 holds values 8k..8k+7 (first half) and lane LP-1-k holds
+//   the second-half values of the same pairs, so the rotate-half partner of
+//   lane k is lane LP-1-k and arrives with one DPP mirror per dword (quad,
+//   half-row or row mirror): no LDS round trip, and every load and store
+//   covers full 128-byte lines.
 // * q and latent are read and q_rope_output written with non-temporal
-//   accesses (streamed once); all q loads of the wave are issued before the
-//   address chain, which takes two
-//   dependent steps ({offsets, cache lengths}, then {freqs row, page-table
-//   entry}) and hides behind the bulk traffic.
+//   accesses (streamed once); all q loads of an item are issued before the
+//   address chain, which takes two dependent steps ({offsets, cache
+//   lengths}, then {freqs row, page-table entry}) and hides behind the bulk
+//   traffic.
 // * The 16 cos/sin floats a lane needs sit contiguously in the freqs row and
 //   are the same for every head: one 64-byte load per lane per token, kept in
 //   registers.
-// * The head-chunk-0 wave also owns the latent row: lane l holds non-rope
-//   values 8l..8l+7; lanes 0..7 hold the 64-value rope tail with the q
-//   mapping.  The sum of squares (and the per-token amax) reduce across the
-//   wave with DPP inside rows and readlane across rows; the sum of squares
-//   is reduced while the second step of the address chain is in flight.
-//   The non-rope value is
-//   formed as (x * gamma) * (r / scale): x * gamma is exact in fp32 (two 8-bit
-//   significands).  The row is converted to fp8 in registers (clamp to +-448,
-//   then hardware round-to-nearest-even) and written with 8-byte
+// * The head-chunk-0 wave of a token also owns its latent row: lane l holds
+//   non-rope values 8l..8l+7 (lanes below kv_norm_dim / 8); lanes 0..LP-1
+//   hold the rope tail with the q mapping.  The sum of squares (and the
+//   per-token amax) reduce across the wave with DPP inside rows and readlane
+//   across rows; the sum of squares is reduced while the second step of the
+//   address chain is in flight.  The non-rope value is formed as
+//   (x * gamma) * (r / scale): x * gamma is exact in fp32 (two 8-bit
+//   significands).  The row is converted to fp8 in registers (clamp to
+//   +-448, then hardware round-to-nearest-even) and written with 8-byte
 //   non-temporal stores.
 // * Planned form: with a token plan (token_plan.hip) each wave reads its
 //   token's (page, offset, position, placed) entry with one scalar 16-byte
@@ -50,26 +52,24 @@
 namespace pkv {
 namespace {
 
-constexpr int kRope = 64;               // rope_dim
-constexpr int kNope = 512;              // kv_norm_dim = 64 lanes x 8
 constexpr int kWavesPerBlock = 4;
+constexpr int kMaxNope = 512;  // kv_norm_dim: at most one 16-byte chunk per lane
 
-// Lane roles inside an 8-lane head group (rotate-half, rope_dim 64).
+// Lane roles inside the LP-lane group of one head (rotate-half, rope_dim R).
+template <int R>
 struct HeadLane {
+  static constexpr int LP = R / 8;  // lanes per head
   int k;          // lane within the group
   bool first;     // holds first-half values
   int pair_block; // holds pairs 8*pair_block .. 8*pair_block+7
-  int chunk;      // 16-byte chunk of the 128-byte head row it loads/stores
+  int chunk;      // 16-byte chunk of the head's rope slice it loads/stores
+  __device__ __forceinline__ explicit HeadLane(int lane) {
+    k = lane % LP;
+    first = k < LP / 2;
+    pair_block = first ? k : LP - 1 - k;
+    chunk = first ? k : LP / 2 + pair_block;
+  }
 };
-
-__device__ __forceinline__ HeadLane head_lane(int lane) {
-  HeadLane h;
-  h.k = lane & 7;
-  h.first = h.k < 4;
-  h.pair_block = h.first ? h.k : 7 - h.k;
-  h.chunk = h.first ? h.k : 11 - h.k;
-  return h;
-}
 
 // Rotate the 8 values this lane owns, given its partner's 8 values: first
 // half  out = own*cos - partner*sin;  second half  out = own*cos + partner*sin.
@@ -81,18 +81,18 @@ __device__ __forceinline__ void rotate_own(float (&own)[8], const float (&par)[8
   for (int j = 0; j < 8; ++j) own[j] = sum_of_products(own[j], cs[2 * j], par[j], cs[2 * j + 1]);
 }
 
-// q loads / stores of one wave: NI instructions of 8 heads each.  The token
-// and chunk parts of the address are wave-uniform (scalar registers); each
-// lane adds a 32-bit offset.  GUARD masks heads past num_heads.
+// q loads / stores of one item: NI instructions of 64/LP heads each.  The
+// token and chunk parts of the address are wave-uniform (scalar registers);
+// each lane adds a 32-bit offset.  GUARD masks heads past num_heads.
 // (base and step in bytes, wave-uniform; lane_off in bytes, per lane.)
-template <int NI, bool GUARD>
+template <int NI, int HPI, bool GUARD>
 __device__ __forceinline__ void load_q(uint4 (&q)[NI], const char* base, int64_t step,
                                        uint32_t lane_off, uint32_t h_lane, uint32_t num_heads) {
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     if (GUARD) {
       q[i] = make_uint4(0, 0, 0, 0);
-      if (h_lane + 8 * i >= num_heads) continue;
+      if (h_lane + HPI * i >= num_heads) continue;
     }
     q[i] = load16_stream(base + i * step + lane_off);
   }
@@ -100,18 +100,18 @@ __device__ __forceinline__ void load_q(uint4 (&q)[NI], const char* base, int64_t
 
 // Rotate and store: bf16 output (16 bytes per lane) or fp32 output (32
 // bytes per lane: two 16-byte stores).
-template <int NI, bool GUARD, bool QF32>
+template <int NI, int HPI, int LP, bool GUARD, bool QF32>
 __device__ __forceinline__ void rotate_store_q(const uint4 (&q)[NI], const float (&cs)[16],
                                                char* base, int64_t step, uint32_t lane_off,
                                                uint32_t h_lane, uint32_t num_heads) {
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    const uint4 partner = mirror16<8>(q[i]);
+    const uint4 partner = mirror16<LP>(q[i]);
     float own[8], par[8];
     unpack8(q[i], own);
     unpack8(partner, par);
     rotate_own(own, par, cs);
-    if (GUARD && h_lane + 8 * i >= num_heads) continue;
+    if (GUARD && h_lane + HPI * i >= num_heads) continue;
     char* p = base + i * step + lane_off;
     if constexpr (QF32) {
       store16_stream(p, make_uint4(__float_as_uint(own[0]), __float_as_uint(own[1]),
@@ -125,10 +125,11 @@ __device__ __forceinline__ void rotate_store_q(const uint4 (&q)[NI], const float
 }
 
 // RMSNorm statistic of the latent row's non-rope part (lane l holds values
-// 8l..8l+7): returns r = 1/sqrt(mean(x^2) + eps), wave-uniform, and leaves
-// x * gamma in xg (exact in fp32: two 8-bit significands).
+// 8l..8l+7; lanes past kv_norm_dim / 8 hold zeros): returns
+// r = 1/sqrt(mean(x^2) + eps), wave-uniform, and leaves x * gamma in xg
+// (exact in fp32: two 8-bit significands).
 __device__ __forceinline__ float latent_rms(const uint4& xn, const uint4& gm, float (&xg)[8],
-                                            float epsilon) {
+                                            float inv_dn, float epsilon) {
   float g8[8];
   unpack8(xn, xg);
   unpack8(gm, g8);
@@ -139,44 +140,59 @@ __device__ __forceinline__ float latent_rms(const uint4& xn, const uint4& gm, fl
     xg[k] *= g8[k];
   }
   ss = wave_sum(ss);
-  return 1.0f / sqrtf(ss * (1.0f / kNope) + epsilon);
+  return 1.0f / sqrtf(ss * inv_dn + epsilon);
 }
 
-// NI = 8-head instructions per wave (heads per wave / 8).  PLANNED: each
-// token's placement comes from a token plan instead of the address chain.
-template <int NI, MlaOut MODE, bool QF32, bool PLANNED>
-__global__ __launch_bounds__(256) void mla_kernel(const MlaArgs a) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const uint32_t wave =
-      blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
-  const uint32_t t = uniform(wave / a.chunks);
-  const uint32_t chunk = uniform(wave - t * a.chunks);
-  if (t >= a.total_tokens) return;
-  const HeadLane hl = head_lane(lane);
+// The loads of one work item that need only the item's index: its q chunks,
+// and, for a token's chunk-0 wave, its latent row (buffer form) and its plan
+// entry (planned form).
+template <int NI>
+struct ItemLoads {
+  uint4 q[NI];
+  uint4 xn, tail;
+  uint4 pe;
+};
 
-  // ---- issue the bulk loads (addresses depend on t only) --------------------
-  const uint32_t h0 = chunk * (8 * NI);  // first head of this wave
-  const uint32_t h_lane = h0 + (uint32_t)(lane >> 3);
-  const bool all_heads = h0 + 8 * NI <= a.num_heads;  // wave-uniform
+template <int R, int NI, MlaOut MODE, bool PLANNED>
+__device__ __forceinline__ void issue_item(const MlaArgs& a, uint32_t t, uint32_t chunk,
+                                           int lane, ItemLoads<NI>& L) {
+  using HL = HeadLane<R>;
+  constexpr int LP = HL::LP, HPI = kWave / LP;
+  const HL hl(lane);
+  const uint32_t h0 = chunk * (HPI * NI);  // first head of this item
+  const uint32_t h_lane = h0 + (uint32_t)(lane / LP);
   const char* qsrc = reinterpret_cast<const char*>(a.q_in + (int64_t)t * a.qi_tok +
                                                     (int64_t)h0 * a.qi_head);
-  const uint32_t qi_lane = 2 * ((uint32_t)(lane >> 3) * (uint32_t)a.qi_head + 8 * hl.chunk);
-  uint4 q[NI];
-  if (all_heads)
-    load_q<NI, false>(q, qsrc, 16 * a.qi_head, qi_lane, h_lane, a.num_heads);
+  const uint32_t qi_lane = 2 * ((uint32_t)(lane / LP) * (uint32_t)a.qi_head + 8 * hl.chunk);
+  if (h0 + HPI * NI <= a.num_heads)  // wave-uniform
+    load_q<NI, HPI, false>(L.q, qsrc, 2 * HPI * a.qi_head, qi_lane, h_lane, a.num_heads);
   else
-    load_q<NI, true>(q, qsrc, 16 * a.qi_head, qi_lane, h_lane, a.num_heads);
-  constexpr bool INPLACE = MODE == MlaOut::Bf16InPlace;
-  const bool latent_wave = chunk == 0;
-  uint4 xn = {}, gm = {}, tail = {};
-  if (latent_wave) {
-    gm = load16(a.gamma + 8 * lane);
-    if constexpr (!INPLACE) {
+    load_q<NI, HPI, true>(L.q, qsrc, 2 * HPI * a.qi_head, qi_lane, h_lane, a.num_heads);
+  L.xn = L.tail = make_uint4(0, 0, 0, 0);
+  if constexpr (MODE != MlaOut::Bf16InPlace) {
+    if (chunk == 0) {
       const uint16_t* row = a.latent + (int64_t)t * a.kv_row;
-      xn = load16_stream(row + 8 * lane);
-      if (lane < 8) tail = load16_stream(row + kNope + 8 * hl.chunk);
+      if ((uint32_t)lane < a.nope_chunks) L.xn = load16_stream(row + 8 * lane);
+      if (lane < LP) L.tail = load16_stream(row + 8 * a.nope_chunks + 8 * hl.chunk);
     }
   }
+  if constexpr (PLANNED) L.pe = *reinterpret_cast<const uint4*>(a.plan + 4 * (uint64_t)t);
+}
+
+// Everything after the bulk loads: the address chain (or the plan entry),
+// the q rotation and stores, and for the chunk-0 wave the latent row's
+// normalisation, tail rotation, quantisation and paged store.
+template <int R, int NI, MlaOut MODE, bool QF32, bool PLANNED>
+__device__ __forceinline__ void finish_item(const MlaArgs& a, uint32_t t, uint32_t chunk,
+                                            int lane, const uint4& gm, ItemLoads<NI>& L) {
+  using HL = HeadLane<R>;
+  constexpr int LP = HL::LP, HPI = kWave / LP;
+  const HL hl(lane);
+  const uint32_t h0 = chunk * (HPI * NI);
+  const uint32_t h_lane = h0 + (uint32_t)(lane / LP);
+  const bool all_heads = h0 + HPI * NI <= a.num_heads;  // wave-uniform
+  constexpr bool INPLACE = MODE == MlaOut::Bf16InPlace;
+  const bool latent_wave = chunk == 0;
 
   // ---- address chain -----------------------------------------------------------
   // step 1: request and slot (= position); step 2: the freqs row and the
@@ -186,11 +202,9 @@ __global__ __launch_bounds__(256) void mla_kernel(const MlaArgs a) {
   // before anything derived from it is dereferenced.
   const CacheView& cv = a.cache;
   TokenSlot ts{};
-  uint4 pe{};
   if constexpr (PLANNED) {
-    pe = *reinterpret_cast<const uint4*>(a.plan + 4 * (uint64_t)t);
-    ts.slot = uniform(pe.z);
-    ts.ok = pe.w != 0;
+    ts.slot = uniform(L.pe.z);
+    ts.ok = L.pe.w != 0;
   } else {
     ts = find_slot(a.offsets, a.batch, cv.cache_lengths, t, lane);
   }
@@ -201,7 +215,7 @@ __global__ __launch_bounds__(256) void mla_kernel(const MlaArgs a) {
   float cs[16];
   {
     const float4* fr = reinterpret_cast<const float4*>(
-        a.freqs + (int64_t)(pos_ok ? ts.slot : 0u) * kRope + 16 * hl.pair_block);
+        a.freqs + (int64_t)(pos_ok ? ts.slot : 0u) * R + 16 * hl.pair_block);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float4 v = fr[i];
@@ -215,19 +229,19 @@ __global__ __launch_bounds__(256) void mla_kernel(const MlaArgs a) {
     col_ok = pos_ok && col < cv.pt_stride;
     if (col_ok) page = cv.page_table[(uint64_t)ts.request * cv.pt_stride + col];
   }
-  // Buffer form: the latent row arrived with the first step, so its
+  // Buffer form: the latent row arrived with the bulk loads, so its
   // statistic is reduced while the freqs row and the page-table entry are
   // still in flight.
   float xg[8];
   float r = 0.0f;
   if constexpr (!INPLACE) {
-    if (latent_wave) r = latent_rms(xn, gm, xg, a.epsilon);
+    if (latent_wave) r = latent_rms(L.xn, gm, xg, a.inv_dn, a.epsilon);
   }
   PageSlot ps{};
   bool placed;
   if constexpr (PLANNED) {
-    ps.page = uniform(pe.x);
-    ps.offset = uniform(pe.y);
+    ps.page = uniform(L.pe.x);
+    ps.offset = uniform(L.pe.y);
     placed = pos_ok && ps.page < cv.num_pages && ps.offset < cv.page_size;
   } else {
     ps.page = uniform(page);
@@ -242,8 +256,8 @@ __global__ __launch_bounds__(256) void mla_kernel(const MlaArgs a) {
   if constexpr (INPLACE) {
     if (latent_wave) {
       const uint16_t* row = static_cast<const uint16_t*>(cv.layer_base) + row_elems;
-      xn = load16_stream(row + 8 * lane);
-      if (lane < 8) tail = load16_stream(row + kNope + 8 * hl.chunk);
+      if ((uint32_t)lane < a.nope_chunks) L.xn = load16_stream(row + 8 * lane);
+      if (lane < LP) L.tail = load16_stream(row + 8 * a.nope_chunks + 8 * hl.chunk);
     }
   }
   if (hl.first) {
@@ -255,28 +269,30 @@ __global__ __launch_bounds__(256) void mla_kernel(const MlaArgs a) {
   constexpr int64_t QB = QF32 ? 4 : 2;  // bytes per q output element
   char* qdst = static_cast<char*>(a.q_out) + QB * ((int64_t)t * a.qo_tok + (int64_t)h0 * a.qo_head);
   const uint32_t qo_lane =
-      (uint32_t)QB * ((uint32_t)(lane >> 3) * (uint32_t)a.qo_head + 8 * hl.chunk);
+      (uint32_t)QB * ((uint32_t)(lane / LP) * (uint32_t)a.qo_head + 8 * hl.chunk);
   if (all_heads)
-    rotate_store_q<NI, false, QF32>(q, cs, qdst, 8 * QB * a.qo_head, qo_lane, h_lane,
-                                    a.num_heads);
+    rotate_store_q<NI, HPI, LP, false, QF32>(L.q, cs, qdst, HPI * QB * a.qo_head, qo_lane, h_lane,
+                                             a.num_heads);
   else
-    rotate_store_q<NI, true, QF32>(q, cs, qdst, 8 * QB * a.qo_head, qo_lane, h_lane,
-                                   a.num_heads);
+    rotate_store_q<NI, HPI, LP, true, QF32>(L.q, cs, qdst, HPI * QB * a.qo_head, qo_lane, h_lane,
+                                            a.num_heads);
   if (!latent_wave) return;
 
   // ---- latent row: RMSNorm (non-rope part), RoPE (tail) ---------------------
-  if constexpr (INPLACE) r = latent_rms(xn, gm, xg, a.epsilon);
+  if constexpr (INPLACE) r = latent_rms(L.xn, gm, xg, a.inv_dn, a.epsilon);
   float tv[8], tp[8];
-  unpack8(tail, tv);
-  unpack8(mirror16<8>(tail), tp);
-  rotate_own(tv, tp, cs);  // meaningful on lanes 0..7 only
+  unpack8(L.tail, tv);
+  unpack8(mirror16<LP>(L.tail), tp);
+  rotate_own(tv, tp, cs);  // meaningful on lanes 0..LP-1 only
+  const bool nope_lane = (uint32_t)lane < a.nope_chunks;
+  const uint32_t tail_off = 8 * a.nope_chunks + 8 * hl.chunk;
 
   if constexpr (MODE == MlaOut::Bf16 || INPLACE) {
     uint16_t* row = static_cast<uint16_t*>(cv.layer_base) + row_elems;
 #pragma unroll
     for (int k = 0; k < 8; ++k) xg[k] *= r;
-    store16_stream(row + 8 * lane, pack8_bf16(xg));
-    if (lane < 8) store16_stream(row + kNope + 8 * hl.chunk, pack8_bf16(tv));
+    if (nope_lane) store16_stream(row + 8 * lane, pack8_bf16(xg));
+    if (lane < LP) store16_stream(row + tail_off, pack8_bf16(tv));
     return;
   } else {
     float inv;
@@ -284,12 +300,13 @@ __global__ __launch_bounds__(256) void mla_kernel(const MlaArgs a) {
       inv = 1.0f / *a.tensor_scale;
     } else {
       // max |y| over the row: the non-rope part scales monotonically by r
+      // (lanes past the non-rope chunks hold zeros)
       float am = 0.0f;
 #pragma unroll
       for (int k = 0; k < 8; ++k) am = fmaxf(am, fabsf(xg[k]));
       am = wave_max(am) * r;
       float at = 0.0f;
-      if (lane < 8) {
+      if (lane < LP) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) at = fmaxf(at, fabsf(tv[k]));
       }
@@ -306,65 +323,106 @@ __global__ __launch_bounds__(256) void mla_kernel(const MlaArgs a) {
       tv[k] *= inv;
     }
     uint8_t* row = static_cast<uint8_t*>(cv.layer_base) + row_elems;
-    store8_stream(row + 8 * lane, pack8_fp8(xg));
-    if (lane < 8) store8_stream(row + kNope + 8 * hl.chunk, pack8_fp8(tv));
+    if (nope_lane) store8_stream(row + 8 * lane, pack8_fp8(xg));
+    if (lane < LP) store8_stream(row + tail_off, pack8_fp8(tv));
   }
 }
 
-template <int NI, bool QF32, bool PLANNED>
-hipError_t launch_g(const MlaArgs& a, MlaOut mode, uint32_t blocks, hipStream_t stream) {
-  switch (mode) {
-    case MlaOut::Fp8PerTensor:
-      hipLaunchKernelGGL((mla_kernel<NI, MlaOut::Fp8PerTensor, QF32, PLANNED>), dim3(blocks),
-                         dim3(256), 0, stream, a);
-      break;
-    case MlaOut::Fp8PerToken:
-      hipLaunchKernelGGL((mla_kernel<NI, MlaOut::Fp8PerToken, QF32, PLANNED>), dim3(blocks),
-                         dim3(256), 0, stream, a);
-      break;
-    case MlaOut::Bf16:
-      hipLaunchKernelGGL((mla_kernel<NI, MlaOut::Bf16, QF32, PLANNED>), dim3(blocks),
-                         dim3(256), 0, stream, a);
-      break;
-    case MlaOut::Bf16InPlace:
-      hipLaunchKernelGGL((mla_kernel<NI, MlaOut::Bf16InPlace, QF32, PLANNED>), dim3(blocks),
-                         dim3(256), 0, stream, a);
-      break;
-  }
+// One work item per wave (item = token * chunks + chunk).  (A persistent
+// grid -- fewer waves, each looping over items with the next item's loads
+// issued before the current one is finished -- measured slower: each wave
+// then resolves its items' address chains one after another.)
+template <int R, int NI, MlaOut MODE, bool QF32, bool PLANNED>
+__global__ __launch_bounds__(256) void mla_kernel(const MlaArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const uint32_t wave = blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
+  const uint32_t t = uniform(wave / a.chunks);
+  const uint32_t chunk = uniform(wave - t * a.chunks);
+  if (t >= a.total_tokens) return;
+  ItemLoads<NI> L;
+  issue_item<R, NI, MODE, PLANNED>(a, t, chunk, lane, L);
+  uint4 gm = make_uint4(0, 0, 0, 0);
+  if (chunk == 0 && (uint32_t)lane < a.nope_chunks) gm = load16(a.gamma + 8 * lane);
+  finish_item<R, NI, MODE, QF32, PLANNED>(a, t, chunk, lane, gm, L);
+}
+
+template <int R, int NI, MlaOut MODE, bool QF32, bool PLANNED>
+hipError_t launch_one(const MlaArgs& a, hipStream_t stream) {
+  const uint64_t items = (uint64_t)a.total_tokens * a.chunks;
+  const uint64_t blocks = (items + kWavesPerBlock - 1) / kWavesPerBlock;
+  hipLaunchKernelGGL((mla_kernel<R, NI, MODE, QF32, PLANNED>), dim3((uint32_t)blocks), dim3(256),
+                     0, stream, a);
   return hipGetLastError();
 }
 
-template <bool QF32, bool PLANNED>
-hipError_t launch_q(const MlaArgs& a, MlaOut mode, int heads_per_wave, uint32_t blocks,
-                    hipStream_t stream) {
-  switch (heads_per_wave) {
-    case 16: return launch_g<2, QF32, PLANNED>(a, mode, blocks, stream);
-    case 32: return launch_g<4, QF32, PLANNED>(a, mode, blocks, stream);
+template <int R, int NI, bool QF32, bool PLANNED>
+hipError_t launch_mode(const MlaArgs& a, MlaOut mode, hipStream_t stream) {
+  switch (mode) {
+    case MlaOut::Fp8PerTensor:
+      return launch_one<R, NI, MlaOut::Fp8PerTensor, QF32, PLANNED>(a, stream);
+    case MlaOut::Fp8PerToken:
+      return launch_one<R, NI, MlaOut::Fp8PerToken, QF32, PLANNED>(a, stream);
+    case MlaOut::Bf16:
+      return launch_one<R, NI, MlaOut::Bf16, QF32, PLANNED>(a, stream);
+    case MlaOut::Bf16InPlace:
+      return launch_one<R, NI, MlaOut::Bf16InPlace, QF32, PLANNED>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int R, bool QF32, bool PLANNED>
+hipError_t launch_ni(const MlaArgs& a, MlaOut mode, int ni, hipStream_t stream) {
+  switch (ni) {
+    case 2: return launch_mode<R, 2, QF32, PLANNED>(a, mode, stream);
+    case 4: return launch_mode<R, 4, QF32, PLANNED>(a, mode, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
+template <int R>
+hipError_t launch_r(const MlaArgs& a, MlaOut mode, int ni, hipStream_t stream) {
+  if (a.plan != nullptr)
+    return a.q_out_f32 ? launch_ni<R, true, true>(a, mode, ni, stream)
+                       : launch_ni<R, false, true>(a, mode, ni, stream);
+  return a.q_out_f32 ? launch_ni<R, true, false>(a, mode, ni, stream)
+                     : launch_ni<R, false, false>(a, mode, ni, stream);
+}
+
 }  // namespace
 
-// 32 heads (4 instructions of 8 heads) per wave measured best on 128-head
-// prefill and decode batches: small enough to keep 8 waves per SIMD resident
-// and to spread a token over 4 waves, large enough to amortise each wave's
-// address chain (rotating outputs, 17108-token prefill: 16 heads per wave
-// 104 us, 32 heads 97 us, 64 heads 98 us).  Heads beyond a multiple of 16 are
-// never padded past the next multiple of 16.
-uint32_t mla_heads_per_wave(uint32_t heads) { return heads > 16 ? 32 : 16; }
+// Heads per wave: four 1 KiB instructions of 64 / (rope_dim / 8) heads each,
+// two for head counts that fit in two (rope_dim 64: 32 heads, or 16 for at
+// most 16 heads).  32 heads per wave measured best on 128-head prefill and
+// decode batches: small enough to keep 8 waves per SIMD resident and to
+// spread a token over 4 waves, large enough to amortise each wave's address
+// chain (rotating outputs, 17108-token prefill: 16 heads per wave 104 us,
+// 32 heads 97 us, 64 heads 98 us).
+uint32_t mla_heads_per_wave(uint32_t heads, uint32_t rope_dim) {
+  const uint32_t per_instr = kWave / (rope_dim / 8);
+  return heads > 2 * per_instr ? 4 * per_instr : 2 * per_instr;
+}
+
+bool mla_rope_dim_supported(uint32_t rope_dim) {
+  return rope_dim == 32 || rope_dim == 64 || rope_dim == 128;
+}
+
+bool mla_nope_dim_supported(uint32_t kv_norm_dim) {
+  return kv_norm_dim > 0 && kv_norm_dim % 8 == 0 && kv_norm_dim <= kMaxNope;
+}
 
 hipError_t launch_mla(const MlaArgs& a, MlaOut mode, int heads_per_wave, hipStream_t stream) {
-  const uint64_t waves = (uint64_t)a.total_tokens * a.chunks;
-  const uint64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
-  if (blocks == 0) return hipSuccess;
+  const uint64_t items = (uint64_t)a.total_tokens * a.chunks;
+  if (items == 0) return hipSuccess;
   // the kernel numbers waves (block * waves per block + wave) in 32 bits
-  if (blocks * kWavesPerBlock > 0xffffffffull) return hipErrorInvalidValue;
-  if (a.plan != nullptr)
-    return a.q_out_f32 ? launch_q<true, true>(a, mode, heads_per_wave, (uint32_t)blocks, stream)
-                       : launch_q<false, true>(a, mode, heads_per_wave, (uint32_t)blocks, stream);
-  return a.q_out_f32 ? launch_q<true, false>(a, mode, heads_per_wave, (uint32_t)blocks, stream)
-                     : launch_q<false, false>(a, mode, heads_per_wave, (uint32_t)blocks, stream);
+  if (items + kWavesPerBlock > 0xffffffffull) return hipErrorInvalidValue;
+  const int R = (int)a.rope_dim;
+  const int ni = heads_per_wave / (kWave / (R / 8));
+  switch (R) {
+    case 32: return launch_r<32>(a, mode, ni, stream);
+    case 64: return launch_r<64>(a, mode, ni, stream);
+    case 128: return launch_r<128>(a, mode, ni, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace pkv

@@ -11,9 +11,6 @@ namespace {
 
 using pkv::CacheView;
 
-constexpr uint32_t kMlaRope = 64;
-constexpr uint32_t kMlaNope = 512;
-
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Head strides the kernels add to per-lane 32-bit byte offsets (up to 7
@@ -103,7 +100,8 @@ int mla_entry(void* q_rope_out, int64_t qo_tok_stride, int64_t qo_head_stride,
   if (rope_dim == 0 || rope_dim % 2 != 0 || kv_norm_dim == 0) return PKV_ERR_SHAPE;
   if (kv_cache->num_heads != 1 || kv_cache->head_dim != kv_norm_dim + rope_dim)
     return PKV_ERR_SHAPE;
-  if (rope_dim != kMlaRope || kv_norm_dim != kMlaNope) return PKV_ERR_UNSUPPORTED;
+  if (!pkv::mla_rope_dim_supported(rope_dim) || !pkv::mla_nope_dim_supported(kv_norm_dim))
+    return PKV_ERR_UNSUPPORTED;
   pkv::MlaOut mode;
   if (kv_cache->dtype == PKV_DTYPE_FP8_E4M3FN && kv_cache->scale_mode == PKV_SCALE_PER_TENSOR)
     mode = pkv::MlaOut::Fp8PerTensor;
@@ -152,8 +150,11 @@ int mla_entry(void* q_rope_out, int64_t qo_tok_stride, int64_t qo_head_stride,
   a.plan = planned ? token_plan : nullptr;
   a.total_tokens = total_tokens;
   a.num_heads = num_heads;
-  const int hpw = (int)pkv::mla_heads_per_wave(num_heads);
+  const int hpw = (int)pkv::mla_heads_per_wave(num_heads, rope_dim);
   a.chunks = num_heads == 0 ? 1u : (num_heads + (uint32_t)hpw - 1) / (uint32_t)hpw;
+  a.rope_dim = rope_dim;
+  a.nope_chunks = kv_norm_dim / 8;
+  a.inv_dn = (float)(1.0 / (double)kv_norm_dim);
   a.freqs = freqs_cis;
   a.max_seq_len = max_seq_len;
   a.gamma = static_cast<const uint16_t*>(gamma);

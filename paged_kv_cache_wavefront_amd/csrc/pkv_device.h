@@ -52,11 +52,16 @@ __device__ __forceinline__ uint4 pack8_bf16(const float (&f)[8]) {
 }
 
 // ---- fp32 -> FP8 E4M3FN (OCP), saturating, round-to-nearest-even -----------
-// Values are clamped to +-448 (the largest finite E4M3FN value) and then
-// converted by v_cvt_pk_fp8_f32, which rounds to nearest even in the OCP
-// format on gfx950; -0 keeps its sign.
+// Values are clamped to +-448 (the largest finite E4M3FN value; infinities
+// saturate too) and then converted by v_cvt_pk_fp8_f32, which rounds to
+// nearest even in the OCP format on gfx950; -0 keeps its sign.  A NaN skips
+// the clamp (min / max would replace it by a bound) and converts to the NaN
+// code, so a NaN in a row stays visible in the cache.
 
-__device__ __forceinline__ float sat448(float v) { return fminf(fmaxf(v, -448.0f), 448.0f); }
+__device__ __forceinline__ float sat448(float v) {
+  const float c = fminf(fmaxf(v, -448.0f), 448.0f);
+  return v != v ? v : c;
+}
 
 __device__ __forceinline__ uint32_t pack4_fp8(float a, float b, float c, float d) {
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(a), sat448(b), 0, false);
@@ -88,10 +93,14 @@ __device__ __forceinline__ uint2 pack8_fp8(const float (&f)[8]) {
 // recovered exactly and added back -- so the fp32 result is within 2 ulps of
 // the exact value even when the two products nearly cancel (a plain fma would
 // lose all relative accuracy there).
-// a*b + c*d with the rounding error of c*d recovered exactly.
+// a*b + c*d with the rounding error of c*d recovered exactly.  An infinite
+// c*d has no rounding error to recover: the error term is then inf - inf =
+// NaN, which fminf replaces by the largest finite float, so the sum stays
+// +-inf (or NaN when a*b is the opposite infinity), like the exact value;
+// a finite error term passes fminf unchanged (one instruction per value).
 __device__ __forceinline__ float sum_of_products(float a, float b, float c, float d) {
   const float cd = c * d;
-  const float cd_err = fmaf(c, d, -cd);     // c*d - cd, exact
+  const float cd_err = fminf(fmaf(c, d, -cd), 3.402823466e38f);  // c*d - cd, exact
   return fmaf(a, b, cd) + cd_err;
 }
 
@@ -139,6 +148,7 @@ __device__ __forceinline__ float dpp(float v) {
                             __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
 
+constexpr int kDppQuadMirror = 0x1B;   // quad_perm [3,2,1,0]
 constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7-i inside each 8 lanes
@@ -164,12 +174,13 @@ __device__ __forceinline__ float swizzle(float v) {
   return __uint_as_float(swizzle_u32<PATTERN>(__float_as_uint(v)));
 }
 
-// Lane k of an aligned group of N lanes (N = 8, 16 or 32) receives lane
+// Lane k of an aligned group of N lanes (N = 4, 8, 16 or 32) receives lane
 // (N-1-k)'s 32-bit value.
 template <int N>
 __device__ __forceinline__ uint32_t mirror_u32(uint32_t x) {
-  static_assert(N == 8 || N == 16 || N == 32, "mirror over 8, 16 or 32 lanes");
-  if constexpr (N == 8) return dpp_u32<kDppHalfMirror>(x);
+  static_assert(N == 4 || N == 8 || N == 16 || N == 32, "mirror over 4, 8, 16 or 32 lanes");
+  if constexpr (N == 4) return dpp_u32<kDppQuadMirror>(x);
+  else if constexpr (N == 8) return dpp_u32<kDppHalfMirror>(x);
   else if constexpr (N == 16) return dpp_u32<kDppMirror>(x);
   else return swizzle_u32<kSwizzleMirror32>(x);
 }

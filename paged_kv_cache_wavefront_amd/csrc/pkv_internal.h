@@ -40,6 +40,9 @@ struct MlaArgs {
   uint32_t total_tokens;
   uint32_t num_heads;
   uint32_t chunks;             // waves per token (head chunks)
+  uint32_t rope_dim;           // 32, 64 or 128
+  uint32_t nope_chunks;        // kv_norm_dim / 8 (at most 64)
+  float inv_dn;                // 1 / kv_norm_dim, rounded to fp32
   const float* freqs;
   uint32_t max_seq_len;
   const uint16_t* gamma;
@@ -51,9 +54,11 @@ struct MlaArgs {
                                // null: placement from offsets, lengths and page table
 };
 
-// Heads per MLA wave for a q with `heads` heads (16 or 32); launch_mla takes
-// that value.
-uint32_t mla_heads_per_wave(uint32_t heads);
+// Heads per MLA wave for a q with `heads` heads of rope_dim values; launch_mla
+// takes that value.  The rope and non-rope widths the kernel is built for.
+uint32_t mla_heads_per_wave(uint32_t heads, uint32_t rope_dim);
+bool mla_rope_dim_supported(uint32_t rope_dim);
+bool mla_nope_dim_supported(uint32_t kv_norm_dim);
 hipError_t launch_mla(const MlaArgs& a, MlaOut mode, int heads_per_wave, hipStream_t stream);
 
 // Per-token placement of a ragged batch (token_plan.hip).

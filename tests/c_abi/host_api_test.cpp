@@ -30,7 +30,12 @@ bool g_gather_per_token;
 PlanArgs g_plan;
 }  // namespace
 
-uint32_t mla_heads_per_wave(uint32_t heads) { return heads > 16 ? 32 : 16; }
+uint32_t mla_heads_per_wave(uint32_t heads, uint32_t rope_dim) {
+  const uint32_t per_instr = 64 / (rope_dim / 8);
+  return heads > 2 * per_instr ? 4 * per_instr : 2 * per_instr;
+}
+bool mla_rope_dim_supported(uint32_t r) { return r == 32 || r == 64 || r == 128; }
+bool mla_nope_dim_supported(uint32_t d) { return d > 0 && d % 8 == 0 && d <= 512; }
 hipError_t launch_mla(const MlaArgs& a, MlaOut mode, int hpw, hipStream_t) {
   ++g_calls; g_mla = a; g_mla_mode = mode; g_mla_hpw = hpw;
   return hipSuccess;
@@ -124,6 +129,15 @@ static int mla(const pkv_paged_cache* c, uint32_t T, uint32_t H, int32_t qdt, ui
                                 static_cast<const uint32_t*>(P(28672)), 2, T, H, 64, 512,
                                 static_cast<const float*>(P(32768)), 64, P(36864), 1e-6f, c,
                                 layer, qdt, nullptr);
+}
+
+// An MLA call with rope_dim R and kv_norm_dim Dn (q rows of H * R values).
+static int mla_dims(const pkv_paged_cache* c, uint32_t T, uint32_t H, uint32_t R, uint32_t Dn) {
+  const int64_t qs = (int64_t)H * R;
+  return mla_rope_rmsnorm_quant(P(16384), qs, R, P(20480), qs, R, P(24576), Dn + R,
+                                static_cast<const uint32_t*>(P(28672)), 2, T, H, R, Dn,
+                                static_cast<const float*>(P(32768)), 64, P(36864), 1e-6f, c, 1,
+                                PKV_DTYPE_BF16, nullptr);
 }
 
 static int mla_inplace(const pkv_paged_cache* c, uint32_t T, uint32_t H, uint32_t layer = 1) {
@@ -361,10 +375,37 @@ int main() {
     EXPECT(g_mla.token_scales == c.scales + 7 * 16);
     EXPECT(!g_mla.q_out_f32);
     EXPECT(g_mla.total_tokens == 5 && g_mla.num_heads == 40 && g_mla.batch == 2);
+    EXPECT(g_mla.rope_dim == 64 && g_mla.nope_chunks == 64 && g_mla.inv_dn == 1.0f / 512);
     EXPECT(mla(&c, 5, 40, PKV_DTYPE_F32) == PKV_OK && g_mla.q_out_f32);
     EXPECT(mla(&c, 5, 16, PKV_DTYPE_BF16) == PKV_OK && g_mla.chunks == 1 && g_mla_hpw == 16);
     EXPECT(mla(&c, 5, 40, PKV_DTYPE_BF16, 0) == PKV_OK &&
            g_mla.cache.layer_base == c.data && g_mla.token_scales == c.scales);
+  }
+  // --- MLA: other rope and non-rope widths (rows of Dn + R values)
+  {
+    struct { uint32_t R, Dn; int st; uint32_t hpw; } cases[] = {
+        {32, 256, PKV_OK, 64}, {128, 512, PKV_OK, 16}, {64, 256, PKV_OK, 32},
+        {32, 512, PKV_OK, 64}, {64, 16, PKV_OK, 32}, {128, 128, PKV_OK, 16},
+        {48, 512, PKV_ERR_UNSUPPORTED, 0}, {16, 512, PKV_ERR_UNSUPPORTED, 0},
+        {64, 520, PKV_ERR_UNSUPPORTED, 0}, {64, 100, PKV_ERR_UNSUPPORTED, 0},
+        {256, 256, PKV_ERR_UNSUPPORTED, 0}};
+    for (const auto& k : cases) {
+      pkv_paged_cache c = latent_cache(PKV_DTYPE_FP8_E4M3FN, PKV_SCALE_PER_TENSOR, 3);
+      const uint32_t W = k.Dn + k.R;
+      c.head_dim = W;
+      c.head_stride = c.slot_stride = W;
+      c.page_stride = 16 * (int64_t)W;
+      c.layer_stride = 3 * c.page_stride;
+      const int before = g_calls;
+      EXPECT(mla_dims(&c, 4, 40, k.R, k.Dn) == k.st);
+      if (k.st != PKV_OK) {
+        EXPECT(g_calls == before);
+        continue;
+      }
+      EXPECT(g_calls == before + 1 && g_mla.rope_dim == k.R && g_mla.nope_chunks == k.Dn / 8);
+      EXPECT(g_mla.inv_dn == (float)(1.0 / k.Dn) && (uint32_t)g_mla_hpw == k.hpw);
+      EXPECT(g_mla.chunks == (40 + k.hpw - 1) / k.hpw);
+    }
   }
   // --- MLA: bf16 cache (2-byte elements), per-tensor fp8, refused calls, T = 0
   {

@@ -70,7 +70,11 @@ def bf16_ulp_diff(a: np.ndarray, b: np.ndarray) -> np.ndarray:
 
 
 def fp8_ulp_diff(a: np.ndarray, b: np.ndarray) -> np.ndarray:
-    return np.abs(ord_fp8(a) - ord_fp8(b))
+    """Ordered-integer distance of E4M3FN codes; two NaN codes (S.1111.111,
+    either sign) are equal, a NaN against a number is 1000 steps apart."""
+    d = np.abs(ord_fp8(a) - ord_fp8(b))
+    na, nb = (a & 0x7F) == 0x7F, (b & 0x7F) == 0x7F
+    return np.where(na & nb, 0, np.where(na | nb, 1000, d))
 
 
 # Parity bar.  q_rope_output: every value within 1 bf16 ulp of the oracle's
@@ -287,8 +291,9 @@ def compare_mla(case, gpu, orc_res, small_case_floor: int = 0, rows=None) -> dic
         assert np.array_equal(ts_g[keep].view(np.uint32), case.token_scales[keep].view(np.uint32)), \
             "scales outside new rows changed"
         sg, so = ts_g[rows].astype(np.float64), ts_o[rows].astype(np.float64)
-        rel = np.abs(sg - so) / np.maximum(np.abs(so), 1e-30)
-        rel[(sg == 0) & (so == 0)] = 0
+        with np.errstate(invalid="ignore"):
+            rel = np.abs(sg - so) / np.maximum(np.abs(so), 1e-30)
+        rel[sg == so] = 0          # equal values, infinities included
         stats["scale_max_rel"] = float(rel.max(initial=0))
         assert stats["scale_max_rel"] <= SCALE_MAX_REL, stats
     return stats

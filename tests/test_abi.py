@@ -37,7 +37,7 @@ def test_header_declares_entry_points():
                                            "qk_rope_paged_ragged", "rms_norm_kv_cache_paged",
                                            "rms_norm_kv_cache_paged_planned",
                                            "mla_gather_latent_paged", "pkv_status_string",
-                                           "pkv_stream_copy"])
+                                           "pkv_stream_copy", "pkv_stream_mix"])
 
 
 def test_library_exports_every_declared_function(pkv):
@@ -63,6 +63,22 @@ def test_stream_copy_validation(pkv):
     assert lib.pkv_stream_copy(FAKE + 8, FAKE + 4096, 16, 1, None) == ALIGN
     assert lib.pkv_stream_copy(FAKE, FAKE + 4096, 24, 1, None) == ALIGN
     assert lib.pkv_stream_copy(FAKE, FAKE + 4096, 0, 1, None) == OK
+
+
+def test_stream_mix_validation(pkv):
+    lib = pkv.library()
+    assert lib.pkv_stream_mix(None, 16, FAKE, 16, 1, None) == NULL
+    assert lib.pkv_stream_mix(FAKE, 16, None, 16, 1, None) == NULL
+    assert lib.pkv_stream_mix(FAKE, 16, FAKE + 4096, 16, 0, None) == SHAPE
+    assert lib.pkv_stream_mix(FAKE, 32, FAKE, 16, 1, None) == SHAPE      # in place: equal counts
+    assert lib.pkv_stream_mix(FAKE + 8, 16, FAKE + 4096, 16, 1, None) == ALIGN
+    assert lib.pkv_stream_mix(FAKE, 24, FAKE + 4096, 16, 1, None) == ALIGN
+    assert lib.pkv_stream_mix(FAKE, 16, FAKE + 4096, 40, 1, None) == ALIGN
+    assert lib.pkv_stream_mix(FAKE, 4096, FAKE + 2048, 4096, 1, None) == RANGE  # overlap
+    assert lib.pkv_stream_mix(FAKE + 2048, 4096, FAKE, 4096, 1, None) == RANGE
+    assert lib.pkv_stream_mix(FAKE, 16 << 31, FAKE << 8, 16, 1, None) == RANGE
+    assert lib.pkv_stream_mix(FAKE, 0, FAKE + 4096, 0, 1, None) == OK
+    assert lib.pkv_stream_mix(FAKE, 0, FAKE, 0, 1, None) == OK
 
 
 def test_status_strings(pkv):
@@ -96,7 +112,12 @@ def test_mla_validation(pkv):
     assert call_mla(pkv, None) == NULL
     assert call_mla(pkv, mla_cache(pkv), R=63) == SHAPE
     assert call_mla(pkv, mla_cache(pkv), R=32) == SHAPE                 # head_dim != Dn + R
-    assert call_mla(pkv, mla_cache(pkv, head_dim=544), R=32) == UNSUP
+    # rope_dim 32, 64, 128 and kv_norm_dim up to 512 in steps of 8 are built
+    assert call_mla(pkv, mla_cache(pkv, head_dim=560), R=48) == UNSUP
+    assert call_mla(pkv, mla_cache(pkv, head_dim=528), R=16) == UNSUP
+    assert call_mla(pkv, mla_cache(pkv, head_dim=768), R=256) == UNSUP
+    assert call_mla(pkv, mla_cache(pkv, head_dim=584), Dn=520) == UNSUP
+    assert call_mla(pkv, mla_cache(pkv, head_dim=164), Dn=100) == UNSUP
     assert call_mla(pkv, mla_cache(pkv, num_heads=2)) == SHAPE
     assert call_mla(pkv, mla_cache(pkv, scale_mode=pkv.PKV_SCALE_NONE)) == DTYPE
     assert call_mla(pkv, mla_cache(pkv, dtype=pkv.PKV_DTYPE_BF16)) == DTYPE
@@ -229,6 +250,30 @@ def test_planned_bindings_check_plan_rows(pkv):
     with pytest.raises(ValueError):
         pkv.mla_rope_rmsnorm_quant_planned(q, q, lat, torch.zeros((4, 3), dtype=torch.int32),
                                            None, None, 1e-6, None, 0)
+
+
+def test_planned_bindings_check_plan_dtype_and_device(pkv):
+    """A plan of 1- or 2-byte elements would let the plan kernel write 16
+    bytes per token past its end, and a host tensor would hand the kernel a
+    host pointer: every plan binding refuses both before calling the
+    library."""
+    import torch
+    q = torch.zeros((4, 2, 64), dtype=torch.bfloat16)
+    lat = torch.zeros((4, 576), dtype=torch.bfloat16)
+    offs = torch.zeros(3, dtype=torch.int32)
+    calls = [
+        lambda p: pkv.pkv_token_plan(p, offs, None),
+        lambda p: pkv.mla_rope_rmsnorm_quant_planned(q, q, lat, p, None, None, 1e-6, None, 0),
+        lambda p: pkv.mla_rope_rmsnorm_inplace_planned(q, q, p, None, None, 1e-6, None, 0),
+        lambda p: pkv.rms_norm_kv_cache_paged_planned(None, 0, None, 1e-6, 0.0, 4, p),
+    ]
+    for call in calls:
+        for dt in (torch.int8, torch.int16, torch.uint8, torch.float32, torch.int64):
+            with pytest.raises(TypeError):
+                call(torch.zeros((4, 4), dtype=dt))
+        for dt in (torch.int32, torch.uint32):   # right type, host memory
+            with pytest.raises(ValueError, match="must live on"):
+                call(torch.zeros((4, 4), dtype=dt))
 
 
 def call_mla_planned(pkv, cache, T=16, H=4, R=64, Dn=512, plan=FAKE, q=FAKE, lat=FAKE,
@@ -427,7 +472,9 @@ def test_headers_compile_as_c_and_cxx(tmp_path):
                    " void*) = mla_rope_rmsnorm_inplace_planned;\n"
                    "  (void)f4; (void)f5; (void)f6; (void)f7;\n"
                    "  int (*f3)(const void*, void*, uint64_t, uint32_t, void*) = pkv_stream_copy;\n"
-                   "  (void)f1; (void)f2; (void)f3;\n"
+                   "  int (*f8)(const void*, uint64_t, void*, uint64_t, uint32_t, void*) ="
+                   " pkv_stream_mix;\n"
+                   "  (void)f1; (void)f2; (void)f3; (void)f8;\n"
                    "  return 0;\n}\n")
     inc = os.path.join(ROOT, "include")
     subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic",

@@ -68,3 +68,35 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_written_bytes_split():
+    """The read / write split of each workload's bytes, which sizes the matched
+    stream: prefill writes q (16 KiB) and the fp8 row (576 B) per token."""
+    case = workloads.mla_prefill()
+    assert bench.written_bytes("mla_prefill", case) == case.T * (2 * 128 * 64 + 576)
+    assert 0 < bench.mla_bytes(case) - bench.written_bytes("mla_prefill", case)
+    mixed = workloads.mla_mixed()
+    assert bench.written_bytes("mla_mixed", mixed) == mixed.T * (2 * 16 * 64 + 576 + 4)
+    qk = workloads.qk_generic()
+    assert bench.written_bytes("qk_generic", qk) == qk.T * (32 * 128 * 2 + 8 * 128 * 2)
+    assert bench.written_bytes("kv_norm", qk) * 2 < bench.kv_norm_bytes(qk, 128) + qk.T * 8 + 300
+    assert bench.written_bytes("gather", None, rows=10) == 11520
+
+
+def test_grid_blocks_follow_the_launch_policy():
+    """The grids the launch code sizes: 32 heads per MLA wave (16 for at most
+    16 heads), 16 Q heads of 128 per Q/K wave, one wave per K-norm token, 6
+    gather rows per wave; four waves per block."""
+    assert bench.grid_blocks("mla_prefill", workloads.mla_prefill()) == workloads.mla_prefill().T
+    assert bench.grid_blocks("mla_decode", workloads.mla_decode()) == 256
+    assert bench.grid_blocks("mla_mixed", workloads.mla_mixed()) == 2064
+    qk = workloads.qk_generic()
+    assert bench.grid_blocks("qk_generic", qk) == -(-2 * qk.T // 4)
+    assert bench.grid_blocks("kv_norm", qk) == -(-qk.T // 4)
+    assert bench.grid_blocks("gather", None, rows=1022807) == -(-170468 // 4)
+
+
+def test_cpu_model_names_the_processor():
+    name = bench.cpu_model()
+    assert name and name != "unknown"

@@ -104,6 +104,82 @@ def test_heads_not_multiple_of_16(orc):
     _run_and_compare(orc, case)
 
 
+# (rope_dim, kv_norm_dim): 4, 8 and 16 lanes per head (quad, half-row and
+# row mirrors), non-rope parts of 16 to 512 values (lanes past kv_norm_dim / 8
+# idle in the statistic, the max and the store)
+OTHER_DIMS = [(32, 256), (32, 512), (64, 256), (128, 512), (128, 128), (64, 16)]
+
+
+@pytest.mark.parametrize("R,Dn", OTHER_DIMS)
+@pytest.mark.parametrize("mode", ["per_tensor", "per_token", "bf16"])
+def test_other_dims(orc, R, Dn, mode):
+    """MLA rows of Dn + R values other than 512 + 64, every cache encoding,
+    a ragged batch with prior lengths and page crossings, 40 heads (a masked
+    head chunk at every rope_dim)."""
+    rng = workloads.make_rng(4200 + R + Dn)
+    new = rng.integers(0, 150, size=9, endpoint=True)
+    prior = rng.integers(0, 300, size=9, endpoint=True)
+    case = workloads.build_mla(f"mla_r{R}_d{Dn}_{mode}", 4200 + R + Dn, new, prior, H=40, R=R,
+                               Dn=Dn, page_size=16, max_seq_len=512, spare_pages=5,
+                               scale_mode="per_token" if mode == "per_token" else "per_tensor",
+                               tensor_scale=0.05, cache_dtype="bf16" if mode == "bf16" else "fp8",
+                               outlier_p=0.01, rng=rng)
+    _run_and_compare(orc, case)
+
+
+@pytest.mark.parametrize("R,Dn,H", [(32, 256, 128), (128, 512, 16)])
+def test_other_dims_prefill_shape(orc, R, Dn, H):
+    """A prefill-shaped batch (8 requests of U{512..4096} tokens, about 17k
+    tokens) at other widths: the persistent launch (more work items than
+    persistent waves) at rope_dim 32 and 128."""
+    rng = workloads.make_rng(4300 + R)
+    new = rng.integers(512, 4096, size=8, endpoint=True)
+    case = workloads.build_mla(f"mla_prefill_r{R}_d{Dn}", 4300 + R, new, np.zeros(8, np.int64),
+                               H=H, R=R, Dn=Dn, page_size=128, max_seq_len=4096, spare_pages=8,
+                               latent_sigma=2.0, scale_mode="per_tensor", tensor_scale=0.05,
+                               rng=rng)
+    _run_and_compare(orc, case)
+
+
+@pytest.mark.parametrize("R,Dn", [(32, 256), (128, 512)])
+def test_other_dims_inplace_and_planned(orc, R, Dn):
+    """The in-place form on a bf16 cache and the planned form at other widths."""
+    import paged_kv_cache_wavefront_amd as pkv
+    rng = workloads.make_rng(4400 + R)
+    new = rng.integers(1, 90, size=7, endpoint=True)
+    prior = rng.integers(0, 200, size=7, endpoint=True)
+    case = workloads.build_mla(f"mla_inplace_r{R}", 4400 + R, new, prior, H=24, R=R, Dn=Dn,
+                               page_size=16, max_seq_len=512, spare_pages=4, cache_dtype="bf16",
+                               rng=rng)
+    dev = gh.MlaDevice(case)
+    dev.place_rows()
+    dev.run_inplace()
+    gh.compare_mla(case, dev.results(), gh.oracle_mla_inplace(orc, case))
+    fcase = workloads.build_mla(f"mla_planned_r{R}", 4400 + R, new, prior, H=24, R=R, Dn=Dn,
+                                page_size=16, max_seq_len=512, spare_pages=4,
+                                scale_mode="per_token", rng=workloads.make_rng(4500 + R))
+    fdev = gh.MlaDevice(fcase)
+    plan = torch.empty((fcase.T, 4), dtype=torch.int32, device="cuda")
+    pkv.pkv_token_plan(plan, fdev.offsets, fdev.desc)
+    pkv.mla_rope_rmsnorm_quant_planned(fdev.q_out, fdev.q_in, fdev.latent, plan, fdev.freqs,
+                                       fdev.gamma, fcase.epsilon, fdev.desc, fcase.layer_idx)
+    _say(f"[dims] planned r{R}: "
+         f"{gh.compare_mla(fcase, fdev.results(), gh.oracle_mla(orc, fcase))}")
+
+
+def test_persistent_launch_head_chunks(orc):
+    """More work items than persistent waves with three head chunks per token
+    (80 heads of 64): the persistent grid is a whole number of token's worth
+    of chunks, every item is taken once."""
+    rng = workloads.make_rng(4600)
+    new = rng.integers(200, 700, size=6, endpoint=True)
+    prior = rng.integers(0, 100, size=6, endpoint=True)
+    case = workloads.build_mla("mla_h80", 4600, new, prior, H=80, page_size=64,
+                               max_seq_len=1024, spare_pages=4, scale_mode="per_token", rng=rng)
+    assert case.T * 3 > 4096
+    _run_and_compare(orc, case)
+
+
 def test_empty_batch(orc):
     import paged_kv_cache_wavefront_amd as pkv
     case = workloads.build_mla("mla_empty", 4003, [0, 0], [5, 0], H=4, page_size=16,
@@ -118,16 +194,17 @@ def test_empty_batch(orc):
 
 
 def test_codec_every_bf16_value(orc):
-    """Every finite bf16 value goes through the rope tail at position 0
-    (cos 1, sin 0: the value is passed through exactly) and is quantised with
+    """Every bf16 pattern goes through the rope tail at position 0 (cos 1,
+    sin 0: a finite value is passed through exactly) and is quantised with
     scale 1 and with scale 1/8: the fp8 codes must equal the oracle's (+-0
     equal) -- this pins the hardware conversion (rounding, ties, subnormals,
-    saturation)."""
+    saturation).  Infinities saturate to +-448; a NaN, and every value whose
+    rotation partner is infinite or NaN (0 x inf), becomes the NaN code, as
+    in the oracle (the NaN code's sign is not compared)."""
     bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
-    finite = bits[(bits & 0x7F80) != 0x7F80]
-    rows = -(-finite.size // 64)
+    rows = -(-bits.size // 64)
     tail = np.zeros(rows * 64, np.uint16)
-    tail[: finite.size] = finite
+    tail[: bits.size] = bits
     for scale in (1.0, 0.125):
         case = workloads.build_mla("mla_codec", 4004, [1] * rows, [0] * rows, H=1,
                                    page_size=4, max_seq_len=1, spare_pages=3,
@@ -142,10 +219,44 @@ def test_codec_every_bf16_value(orc):
         got = cache[rows_mask][:, 0, case.Dn:]
         want = cache_o[rows_mask][:, 0, case.Dn:]
         d = gh.fp8_ulp_diff(got, want)
-        _say(f"[codec] scale={scale}: {int((d != 0).sum())} of {d.size} tail codes differ")
+        nan = (want & 0x7F) == 0x7F
+        _say(f"[codec] scale={scale}: {int((d != 0).sum())} of {d.size} tail codes differ; "
+             f"{int(nan.sum())} NaN codes")
         assert int(d.max()) == 0
+        # 254 NaN patterns, each with its rotation partner (and the infinities'
+        # partners) in the same 64-value tail: four whole tails of NaN codes
+        assert int(nan.sum()) == 256, "a NaN input gives the NaN code"
         stats = gh.compare_mla(case, (q, cache, None, 0), gh.oracle_mla(orc, case))
         _say(f"[codec] scale={scale}: {stats}")
+
+
+@pytest.mark.parametrize("scale_mode", ["per_tensor", "per_token"])
+def test_non_finite_latent_values(orc, scale_mode):
+    """A NaN or an infinity in the latent row's non-rope part reaches the
+    statistic: a NaN makes every normalised value NaN; an infinity makes r = 0,
+    so the infinite value becomes NaN (inf x 0) and the others +-0.  The rope
+    tail is rotated as usual.  Codes (NaN codes by NaN-ness), and per-token
+    scales (which ignore NaN values, as a max over the row does), match the
+    oracle."""
+    case = workloads.build_mla(f"mla_nonfinite_{scale_mode}", 4010, [3, 5], [2, 7], H=4,
+                               page_size=8, max_seq_len=64, spare_pages=2,
+                               scale_mode=scale_mode, tensor_scale=0.05)
+    nan, inf, ninf = np.uint16(0x7FC0), np.uint16(0x7F80), np.uint16(0xFF80)
+    case.latent[0, 17] = nan                 # NaN in the normalised part
+    case.latent[1, 300] = inf                # +inf in the normalised part
+    case.latent[2, 5] = ninf                 # -inf in the normalised part
+    case.latent[3, case.Dn + 3] = nan        # NaN in the rope tail
+    case.latent[4, case.Dn + 40] = inf       # +inf in the rope tail
+    case.latent[5, :case.Dn] = nan           # every normalised value NaN
+    dev = gh.MlaDevice(case)
+    dev.run()
+    res = dev.results()
+    assert res[3] == 0
+    stats = gh.compare_mla(case, res, gh.oracle_mla(orc, case), small_case_floor=3)
+    _say(f"[nonfinite] {scale_mode}: {stats}")
+    rows = gh.written_rows(case)
+    codes = res[1][rows][:, 0]
+    assert ((codes & 0x7F) == 0x7F).any(axis=1).sum() >= 5
 
 
 def test_skipped_tokens_are_counted(orc):
