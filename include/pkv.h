@@ -159,8 +159,11 @@ typedef struct pkv_paged_cache {
  *                   PER_TENSOR or PER_TOKEN, or BF16 with scale mode NONE;
  *                   num_heads 1, head_dim kv_norm_dim + rope_dim
  *   stream          hipStream_t to enqueue on (NULL = default stream)
- * Supported here: rope_dim 64, kv_norm_dim 512, any num_heads >= 0, q head
- * strides up to 2^27 elements (else PKV_ERR_UNSUPPORTED).
+ * Supported here: rope_dim 32, 64 or 128; kv_norm_dim a multiple of 8 up to
+ * 512 (the pages leave both open: gamma [kv_norm_dim], q_rope [..,
+ * rope_dim]); any num_heads >= 0; q head strides up to 2^27 elements.  Other
+ * sizes return PKV_ERR_UNSUPPORTED.  The cache row (kv_norm_dim + rope_dim
+ * elements) must keep the descriptor's strides 16-byte multiples.
  */
 int mla_rope_rmsnorm_quant(void* q_rope_out, int64_t qo_tok_stride, int64_t qo_head_stride,
                            const void* q_rope, int64_t qi_tok_stride, int64_t qi_head_stride,

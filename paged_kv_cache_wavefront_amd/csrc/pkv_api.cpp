@@ -85,6 +85,7 @@ float* k_scales_of(const pkv_paged_cache* c, uint32_t layer_idx, pkv::KMode km) 
 // Both MLA entry points and the planned form: placement from the ragged
 // batch (input_row_offsets, the cache's lengths and page table) or, when
 // `planned`, from token_plan alone.
+// With `prepared` set, the call only validates and fills *prepared (no launch).
 int mla_entry(void* q_rope_out, int64_t qo_tok_stride, int64_t qo_head_stride,
               const void* q_rope, int64_t qi_tok_stride, int64_t qi_head_stride,
               const void* kv_latent, int64_t kv_row_stride, bool in_place, bool planned,
@@ -93,7 +94,8 @@ int mla_entry(void* q_rope_out, int64_t qo_tok_stride, int64_t qo_head_stride,
               uint32_t num_heads, uint32_t rope_dim, uint32_t kv_norm_dim,
               const float* freqs_cis, uint32_t max_seq_len, const void* gamma, float epsilon,
               const pkv_paged_cache* kv_cache, uint32_t layer_idx, int32_t q_out_dtype,
-              void* stream) {
+              void* stream, pkv::MlaLaunch* prepared = nullptr) {
+  if (prepared != nullptr) prepared->empty = true;
   if (kv_cache == nullptr) return PKV_ERR_NULL;
   if (q_out_dtype != PKV_DTYPE_BF16 && q_out_dtype != PKV_DTYPE_F32) return PKV_ERR_DTYPE;
   const int64_t qo_align = q_out_dtype == PKV_DTYPE_F32 ? 4 : 8;  // 16 bytes in elements
@@ -165,10 +167,64 @@ int mla_entry(void* q_rope_out, int64_t qo_tok_stride, int64_t qo_head_stride,
     a.token_scales = kv_cache->scales + (int64_t)layer_idx * kv_cache->num_pages *
                                             kv_cache->page_size * kv_cache->num_heads;
   a.cache = view;
+  if (prepared != nullptr) {
+    *prepared = pkv::MlaLaunch{a, mode, hpw, false};
+    return PKV_OK;
+  }
   return launch_status(pkv::launch_mla(a, mode, hpw, static_cast<hipStream_t>(stream)));
 }
 
+// pkv_token_plan's checks; fills *out.
+int plan_entry(uint32_t* token_plan, const uint32_t* input_row_offsets, uint32_t batch_size,
+               uint32_t total_tokens, const pkv_paged_cache* cache, pkv::PlanArgs* out) {
+  if (cache == nullptr) return PKV_ERR_NULL;
+  if (cache->num_pages == 0 || cache->page_size == 0 || cache->page_table_stride == 0)
+    return PKV_ERR_SHAPE;
+  if (total_tokens > 0 && batch_size == 0) return PKV_ERR_SHAPE;
+  *out = pkv::PlanArgs{};
+  if (total_tokens == 0) return PKV_OK;
+  if (token_plan == nullptr || input_row_offsets == nullptr || cache->cache_lengths == nullptr ||
+      cache->page_table == nullptr)
+    return PKV_ERR_NULL;
+  if (!aligned16(token_plan)) return PKV_ERR_ALIGN;
+  out->plan = token_plan;
+  out->offsets = input_row_offsets;
+  out->batch = batch_size;
+  out->total_tokens = total_tokens;
+  out->cache_lengths = cache->cache_lengths;
+  out->page_table = cache->page_table;
+  out->pt_stride = cache->page_table_stride;
+  out->num_pages = cache->num_pages;
+  out->page_size = cache->page_size;
+  return PKV_OK;
+}
+
 }  // namespace
+
+namespace pkv {
+
+int mla_prepare_planned(void* q_rope_out, int64_t qo_tok_stride, int64_t qo_head_stride,
+                        const void* q_rope, int64_t qi_tok_stride, int64_t qi_head_stride,
+                        const void* kv_latent, int64_t kv_row_stride,
+                        const uint32_t* token_plan, uint32_t total_tokens, uint32_t num_heads,
+                        uint32_t rope_dim, uint32_t kv_norm_dim, const float* freqs_cis,
+                        uint32_t max_seq_len, const void* gamma, float epsilon,
+                        const pkv_paged_cache* kv_cache, uint32_t layer_idx,
+                        int32_t q_out_dtype, MlaLaunch* out) {
+  return mla_entry(q_rope_out, qo_tok_stride, qo_head_stride, q_rope, qi_tok_stride,
+                   qi_head_stride, kv_latent, kv_row_stride, false, true, token_plan, nullptr,
+                   0, total_tokens, num_heads, rope_dim, kv_norm_dim, freqs_cis, max_seq_len,
+                   gamma, epsilon, kv_cache, layer_idx, q_out_dtype, nullptr, out);
+}
+
+int plan_prepare(uint32_t* token_plan, const uint32_t* input_row_offsets, uint32_t batch_size,
+                 uint32_t total_tokens, const pkv_paged_cache* cache, PlanArgs* out) {
+  return plan_entry(token_plan, input_row_offsets, batch_size, total_tokens, cache, out);
+}
+
+int status_of(hipError_t e) { return launch_status(e); }
+
+}  // namespace pkv
 
 extern "C" {
 
@@ -204,25 +260,9 @@ int mla_rope_rmsnorm_quant(void* q_rope_out, int64_t qo_tok_stride, int64_t qo_h
 int pkv_token_plan(uint32_t* token_plan, const uint32_t* input_row_offsets,
                    uint32_t batch_size, uint32_t total_tokens, const pkv_paged_cache* cache,
                    void* stream) {
-  if (cache == nullptr) return PKV_ERR_NULL;
-  if (cache->num_pages == 0 || cache->page_size == 0 || cache->page_table_stride == 0)
-    return PKV_ERR_SHAPE;
-  if (total_tokens > 0 && batch_size == 0) return PKV_ERR_SHAPE;
-  if (total_tokens == 0) return PKV_OK;
-  if (token_plan == nullptr || input_row_offsets == nullptr || cache->cache_lengths == nullptr ||
-      cache->page_table == nullptr)
-    return PKV_ERR_NULL;
-  if (!aligned16(token_plan)) return PKV_ERR_ALIGN;
-  pkv::PlanArgs a{};
-  a.plan = token_plan;
-  a.offsets = input_row_offsets;
-  a.batch = batch_size;
-  a.total_tokens = total_tokens;
-  a.cache_lengths = cache->cache_lengths;
-  a.page_table = cache->page_table;
-  a.pt_stride = cache->page_table_stride;
-  a.num_pages = cache->num_pages;
-  a.page_size = cache->page_size;
+  pkv::PlanArgs a;
+  const int st = plan_entry(token_plan, input_row_offsets, batch_size, total_tokens, cache, &a);
+  if (st != PKV_OK || total_tokens == 0) return st;
   return launch_status(pkv::launch_plan(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+struct pkv_paged_cache;  // include/pkv.h
+
 namespace pkv {
 
 // K cache element encoding of the sibling entry points.
@@ -60,6 +62,15 @@ uint32_t mla_heads_per_wave(uint32_t heads, uint32_t rope_dim);
 bool mla_rope_dim_supported(uint32_t rope_dim);
 bool mla_nope_dim_supported(uint32_t kv_norm_dim);
 hipError_t launch_mla(const MlaArgs& a, MlaOut mode, int heads_per_wave, hipStream_t stream);
+
+// A validated MLA launch (pkv_api.cpp): its argument block, cache encoding
+// and heads per wave; `empty` when there is nothing to launch.
+struct MlaLaunch {
+  MlaArgs args;
+  MlaOut mode;
+  int heads_per_wave;
+  bool empty;
+};
 
 // Per-token placement of a ragged batch (token_plan.hip).
 struct PlanArgs {
@@ -136,5 +147,21 @@ struct GatherArgs {
 enum class GatherKind : int { Fp8ToFp8 = 0, Fp8ToBf16 = 1, Bf16ToBf16 = 2, Bf16ToFp8 = 3 };
 
 hipError_t launch_gather(const GatherArgs& a, GatherKind kind, bool per_token, hipStream_t stream);
+
+// The planned MLA step's and the token plan's host checks, filling their
+// argument blocks without launching (pkv_api.cpp); each returns the status the
+// corresponding entry point would return before enqueueing anything.
+int mla_prepare_planned(void* q_rope_out, int64_t qo_tok_stride, int64_t qo_head_stride,
+                        const void* q_rope, int64_t qi_tok_stride, int64_t qi_head_stride,
+                        const void* kv_latent, int64_t kv_row_stride,
+                        const uint32_t* token_plan, uint32_t total_tokens, uint32_t num_heads,
+                        uint32_t rope_dim, uint32_t kv_norm_dim, const float* freqs_cis,
+                        uint32_t max_seq_len, const void* gamma, float epsilon,
+                        const ::pkv_paged_cache* kv_cache, uint32_t layer_idx,
+                        int32_t q_out_dtype, MlaLaunch* out);
+int plan_prepare(uint32_t* token_plan, const uint32_t* input_row_offsets, uint32_t batch_size,
+                 uint32_t total_tokens, const ::pkv_paged_cache* cache, PlanArgs* out);
+// A launch's status code (PKV_OK or PKV_ERR_LAUNCH).
+int status_of(hipError_t e);
 
 }  // namespace pkv
