@@ -1,7 +1,7 @@
 /*
  * pkv.h -- C ABI of the paged-KV pre-attention library (gfx950 / MI355X).
  *
- * Nine entry points, each one stream-ordered kernel launch:
+ * Ten entry points, each one stream-ordered kernel launch (but one, below):
  *
  *   mla_rope_rmsnorm_quant   fused MLA step: RoPE on q_rope, RMSNorm on the
  *                            latent row's non-rope part, RoPE on its rope tail,
@@ -22,6 +22,10 @@
  *                            placed by such a plan (the same page's
  *                            addressing, split so that every layer of a model
  *                            step reuses it).
+ *   mla_rope_rmsnorm_quant_noalloc
+ *                            the planned step with its plan in a static device
+ *                            array, for callers that cannot allocate (two
+ *                            launches when it builds the plan).
  *   qk_rope_paged_ragged     RoPE on Q (out of place) and on the new K rows of a
  *                            paged cache (in place), optional per-head K
  *                            RMSNorm fused in front of the K rotation.
@@ -56,8 +60,9 @@
  * column 2i and the sine in column 2i+1 of the angle p * theta_i.
  *
  * Ownership: the caller allocates and frees every buffer.  The library
- * allocates nothing, keeps no state between calls, never synchronises and may
- * be called from several host threads.  Outputs may alias their inputs only
+ * allocates nothing, keeps no state between calls (except the plan array of
+ * mla_rope_rmsnorm_quant_noalloc), never synchronises and may be called from
+ * several host threads.  Outputs may alias their inputs only
  * exactly (q_out == q_in); partial overlap is undefined.
  *
  * Errors: every entry point returns PKV_OK (0) or a pkv_status.  All argument
@@ -270,6 +275,46 @@ int mla_rope_rmsnorm_inplace_planned(void* q_rope_out, int64_t qo_tok_stride,
                                      uint32_t max_seq_len, const void* gamma, float epsilon,
                                      const pkv_paged_cache* kv_cache, uint32_t layer_idx,
                                      int32_t q_out_dtype, void* stream);
+
+/*
+ * mla_rope_rmsnorm_quant_planned without a caller-allocated plan, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  The token plan lives in a
+ * static array the library holds on every device it runs on (2^18 entries of
+ * 16 bytes = 4 MiB per device, kept until the process ends); the call
+ * allocates nothing and calls no allocating routine.
+ *
+ *   build_plan != 0  write the plan of this batch (input_row_offsets,
+ *                    batch_size and the descriptor's cache_lengths and
+ *                    page_table, as pkv_token_plan would) into the array of
+ *                    the stream's device, then run the planned step from it:
+ *                    two stream-ordered launches.
+ *   build_plan == 0  run the planned step from the plan the last call with
+ *                    build_plan != 0 built on that device (for the other
+ *                    layers of the same batch layout); input_row_offsets and
+ *                    batch_size are not read.  PKV_ERR_SHAPE when that plan
+ *                    has fewer tokens than total_tokens (or none was built).
+ * Results equal mla_rope_rmsnorm_quant_planned's with the plan pkv_token_plan
+ * writes for the same batch, bit for bit.  Other arguments, shapes and
+ * supported sizes as for mla_rope_rmsnorm_quant.  total_tokens above 2^18
+ * returns PKV_ERR_UNSUPPORTED.  A call with total_tokens = 0 enqueues nothing
+ * but resolves the array's address on the stream's device, so that a caller
+ * can make it before capturing a graph.
+ * Every call on one device shares that device's array and it keeps the last
+ * build's contents: calls that overlap on one device (other streams, other
+ * host threads) race, and a build_plan == 0 call reads whatever the last
+ * build on that device wrote.
+ */
+int mla_rope_rmsnorm_quant_noalloc(void* q_rope_out, int64_t qo_tok_stride,
+                                   int64_t qo_head_stride, const void* q_rope,
+                                   int64_t qi_tok_stride, int64_t qi_head_stride,
+                                   const void* kv_latent, int64_t kv_row_stride,
+                                   const uint32_t* input_row_offsets, uint32_t batch_size,
+                                   uint32_t total_tokens, uint32_t num_heads, uint32_t rope_dim,
+                                   uint32_t kv_norm_dim, const float* freqs_cis,
+                                   uint32_t max_seq_len, const void* gamma, float epsilon,
+                                   const pkv_paged_cache* kv_cache, uint32_t layer_idx,
+                                   int32_t q_out_dtype, int build_plan, void* stream);
 
 /*
  * Paged-ragged fused Q/K RoPE.  Q is rotated into q_out; the K rows of the

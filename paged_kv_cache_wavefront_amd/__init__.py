@@ -34,7 +34,7 @@ EXPORTED = ("mla_rope_rmsnorm_quant", "mla_rope_rmsnorm_inplace", "pkv_token_pla
             "mla_rope_rmsnorm_quant_planned", "mla_rope_rmsnorm_inplace_planned",
             "qk_rope_paged_ragged",
             "rms_norm_kv_cache_paged", "rms_norm_kv_cache_paged_planned",
-            "mla_gather_latent_paged", "pkv_status_string")
+            "mla_gather_latent_paged", "mla_rope_rmsnorm_quant_noalloc", "pkv_status_string")
 
 
 class PkvError(RuntimeError):
@@ -106,6 +106,10 @@ def _load() -> ctypes.CDLL:
     lib.mla_gather_latent_paged.restype = ctypes.c_int
     lib.mla_gather_latent_paged.argtypes = [
         vp, ctypes.c_int32, i64, vp, vp, vp, u32, u32, cache_p, u32, vp]
+    lib.mla_rope_rmsnorm_quant_noalloc.restype = ctypes.c_int
+    lib.mla_rope_rmsnorm_quant_noalloc.argtypes = [
+        vp, i64, i64, vp, i64, i64, vp, i64, vp, u32, u32, u32, u32, u32, vp, u32, vp, f32,
+        cache_p, u32, ctypes.c_int32, ctypes.c_int, vp]
     lib.pkv_status_string.restype = ctypes.c_char_p
     lib.pkv_status_string.argtypes = [ctypes.c_int]
     lib.pkv_stream_copy.restype = ctypes.c_int
@@ -283,6 +287,29 @@ def mla_rope_rmsnorm_inplace_planned(q_rope_output: torch.Tensor, q_rope: torch.
         PKV_DTYPE_F32 if q_rope_output.dtype == torch.float32 else PKV_DTYPE_BF16,
         _stream(stream))
     _check("mla_rope_rmsnorm_inplace_planned", st)
+
+
+def mla_rope_rmsnorm_quant_noalloc(q_rope_output: torch.Tensor, q_rope: torch.Tensor,
+                                   kv_latent: torch.Tensor, input_row_offsets: torch.Tensor,
+                                   freqs_cis: torch.Tensor, gamma: torch.Tensor, epsilon: float,
+                                   kv_cache: PagedCache, layer_idx: int, build_plan: bool = True,
+                                   stream=None) -> None:
+    """The planned MLA step with its token plan in the library's static
+    device array (C: ``mla_rope_rmsnorm_quant_noalloc``): ``build_plan``
+    writes this batch's plan there first; without it the plan the last
+    building call left on the device is used.  Arguments as for
+    :func:`mla_rope_rmsnorm_quant`; nothing is allocated."""
+    T, H, R = q_rope.shape
+    st = _lib.mla_rope_rmsnorm_quant_noalloc(
+        _ptr(q_rope_output), q_rope_output.stride(0), q_rope_output.stride(1),
+        _ptr(q_rope), q_rope.stride(0), q_rope.stride(1),
+        _ptr(kv_latent), kv_latent.stride(0),
+        _ptr(input_row_offsets), input_row_offsets.numel() - 1, T, H, R,
+        kv_latent.shape[1] - R, _ptr(freqs_cis), freqs_cis.shape[0], _ptr(gamma),
+        float(epsilon), ctypes.byref(kv_cache), int(layer_idx),
+        PKV_DTYPE_F32 if q_rope_output.dtype == torch.float32 else PKV_DTYPE_BF16,
+        int(bool(build_plan)), _stream(stream))
+    _check("mla_rope_rmsnorm_quant_noalloc", st)
 
 
 def qk_rope_paged_ragged(q_out: torch.Tensor, q_proj: torch.Tensor,

@@ -37,6 +37,7 @@ def test_header_declares_entry_points():
                                            "qk_rope_paged_ragged", "rms_norm_kv_cache_paged",
                                            "rms_norm_kv_cache_paged_planned",
                                            "mla_gather_latent_paged", "pkv_status_string",
+                                           "mla_rope_rmsnorm_quant_noalloc",
                                            "pkv_stream_copy", "pkv_stream_mix"])
 
 
@@ -276,6 +277,30 @@ def test_planned_bindings_check_plan_dtype_and_device(pkv):
                 call(torch.zeros((4, 4), dtype=dt))
 
 
+def call_noalloc(pkv, cache, T=16, H=4, R=64, Dn=512, offs=FAKE, batch=2, build=1, layer=1):
+    lib = pkv.library()
+    cp = None if cache is None else ctypes.byref(cache)
+    return lib.mla_rope_rmsnorm_quant_noalloc(FAKE, 4 * 64, R, FAKE, 4 * 64, R, FAKE, Dn + R,
+                                              offs, batch, T, H, R, Dn, FAKE, 64, FAKE, 1e-6,
+                                              cp, layer, 0, build, None)
+
+
+def test_noalloc_validation(pkv):
+    """The allocation-free entry point refuses on the host, before it touches
+    any device: too many tokens for its plan array, and every refusal of the
+    planned step and of the plan build."""
+    assert call_noalloc(pkv, mla_cache(pkv), T=(1 << 18) + 1) == UNSUP
+    assert call_noalloc(pkv, None) == NULL
+    assert call_noalloc(pkv, mla_cache(pkv), R=48) == SHAPE
+    assert call_noalloc(pkv, mla_cache(pkv, head_dim=560), R=48) == UNSUP
+    assert call_noalloc(pkv, mla_cache(pkv), layer=2) == RANGE
+    assert call_noalloc(pkv, mla_cache(pkv, dtype=pkv.PKV_DTYPE_BF16)) == DTYPE
+    assert call_noalloc(pkv, mla_cache(pkv), offs=None) == NULL        # building needs offsets
+    assert call_noalloc(pkv, mla_cache(pkv), batch=0) == SHAPE
+    assert call_noalloc(pkv, mla_cache(pkv, page_table=None)) == NULL
+    assert call_noalloc(pkv, mla_cache(pkv, cache_lengths=None)) == NULL
+
+
 def call_mla_planned(pkv, cache, T=16, H=4, R=64, Dn=512, plan=FAKE, q=FAKE, lat=FAKE,
                      layer=1, max_seq=64, qo_dtype=0):
     lib = pkv.library()
@@ -470,7 +495,12 @@ def test_headers_compile_as_c_and_cxx(tmp_path):
                    " const uint32_t*, uint32_t, uint32_t, uint32_t, uint32_t, const float*,"
                    " uint32_t, const void*, float, const pkv_paged_cache*, uint32_t, int32_t,"
                    " void*) = mla_rope_rmsnorm_inplace_planned;\n"
-                   "  (void)f4; (void)f5; (void)f6; (void)f7;\n"
+                   "  int (*f9)(void*, int64_t, int64_t, const void*, int64_t, int64_t,"
+                   " const void*, int64_t, const uint32_t*, uint32_t, uint32_t, uint32_t,"
+                   " uint32_t, uint32_t, const float*, uint32_t, const void*, float,"
+                   " const pkv_paged_cache*, uint32_t, int32_t, int, void*) ="
+                   " mla_rope_rmsnorm_quant_noalloc;\n"
+                   "  (void)f4; (void)f5; (void)f6; (void)f7; (void)f9;\n"
                    "  int (*f3)(const void*, void*, uint64_t, uint32_t, void*) = pkv_stream_copy;\n"
                    "  int (*f8)(const void*, uint64_t, void*, uint64_t, uint32_t, void*) ="
                    " pkv_stream_mix;\n"
