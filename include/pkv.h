@@ -323,7 +323,9 @@ int mla_rope_rmsnorm_quant_noalloc(void* q_rope_out, int64_t qo_tok_stride,
  * Multimodal RoPE (mrope_section != NULL, three host values summing to
  * head_dim/2: temporal, height, width pair counts): position_ids is
  * [3][total_tokens] and pair i is rotated by the angle of the row of its
- * section (page "generic_fused_qk_rope_bshd_paged_ragged", Parameters).
+ * section (page "generic_fused_qk_rope_bshd_paged_ragged", Parameters, names
+ * mrope_section but gives no position layout: the three-row layout, and the
+ * sections taken in that order over the pairs, are the reading taken).
  * interleaved != 0 rotates adjacent pairs (2i, 2i+1), otherwise pairs
  * (i, i + head_dim/2); pair i always uses freqs_cis columns 2i, 2i+1.
  * With k_norm_gamma != NULL, each K head's first k_norm_cols columns are
@@ -374,8 +376,8 @@ int qk_rope_paged_ragged(void* q_out, int64_t qo_tok_stride, int64_t qo_head_str
  *                  token over the first gamma_len columns of all its heads
  *                  (the page lists the flag without describing it; this is
  *                  the reading taken)
- * Supported here: head_dim 64, 80, 96, 128 or 256; per_head_norm 0 with at
- * most 32 heads of 64, 16 heads of 80, 96 or 128, 8 heads of 256.
+ * Supported here: head_dim 64, 80, 96, 128 or 256, any number of heads with
+ * either statistic.
  */
 int rms_norm_kv_cache_paged(const pkv_paged_cache* k_cache, uint32_t layer_idx,
                             const void* gamma, uint32_t gamma_len, float epsilon,

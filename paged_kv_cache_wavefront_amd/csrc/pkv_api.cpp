@@ -395,8 +395,6 @@ int kv_norm_entry(const pkv_paged_cache* k_cache, uint32_t layer_idx, const void
   if (km != pkv::KMode::Bf16 && !multiply_before_cast) return PKV_ERR_UNSUPPORTED;
   if (!sibling_head_dim(k_cache->head_dim))
     return PKV_ERR_UNSUPPORTED;
-  if (!per_head_norm && k_cache->num_heads > pkv::kv_norm_max_heads(k_cache->head_dim))
-    return PKV_ERR_UNSUPPORTED;
   if (!planned && total_seq_len > 0 && batch_size == 0) return PKV_ERR_SHAPE;
   CacheView view{};
   int st = check_cache(k_cache, layer_idx, planned ? 0u : batch_size, &view);

@@ -126,8 +126,6 @@ struct KvNormArgs {
                                  // from offsets, lengths and page table
 };
 
-// Most KV heads per token the per-token K-norm statistic handles.
-uint32_t kv_norm_max_heads(uint32_t head_dim);
 hipError_t launch_kv_norm(const KvNormArgs& a, bool multiply_before_cast, KMode kmode,
                           hipStream_t stream);
 

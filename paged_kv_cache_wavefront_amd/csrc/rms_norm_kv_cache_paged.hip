@@ -11,8 +11,10 @@
 // Per-token statistic (per_head_norm = 0, a reading: the page lists the flag
 // without describing it): one r over the first len(gamma) columns of every
 // head of the token, from a wave-wide sum.  Both forms load a chunk of up to
-// 4 head groups first (phase 1, sums), then normalise and store it (phase 2);
-// the per-token form needs all heads in one chunk.
+// 4 head groups first (phase 1, sums), then normalise and store it (phase 2).
+// A token whose heads fill more than one chunk first sums the statistic over
+// all of them (ordinary loads, so that the lines stay in L2 for phase 1 of
+// each chunk, which then only reloads and normalises).
 //
 // Planned form: with a token plan (token_plan.hip) the token's (page,
 // offset) is one checked plan entry instead of the address chain, which in
@@ -96,9 +98,39 @@ __global__ __launch_bounds__(256) void kv_norm_kernel(const KvNormArgs a) {
     tensor_scale = a.k_scales[0];
     tensor_inv = 1.0f / tensor_scale;
   }
-  // head groups of HPI heads; the per-token statistic needs them all in one
-  // chunk (host-checked), per-head statistics go kMaxIter groups at a time
+  // head groups of HPI heads, kMaxIter groups at a time
   const uint32_t nit = (cv.num_heads + HPI - 1) / HPI;
+  // per-token statistic over more than one chunk: summed in a pass of its own
+  const bool presum = !PER_HEAD && nit > (uint32_t)kMaxIter;
+  float r_presum = 0.0f;
+  if (!PER_HEAD && presum) {
+    float ss_all = 0.0f;
+    for (uint32_t it = 0; it < nit; ++it) {
+      const uint32_t h = it * HPI + hl;
+      const bool valid = h < cv.num_heads && touches;
+      const char* p = krow + EB * (int64_t)h * cv.head_stride;
+      float y[8];
+      if constexpr (KM == KMode::Bf16) {
+        uint4 raw = make_uint4(0, 0, 0, 0);
+        if (valid) raw = load16(p);
+        unpack8(raw, y);
+      } else {
+        uint2 raw = make_uint2(0, 0);
+        float ks = 0.0f;
+        if (valid) {
+          raw = *reinterpret_cast<const uint2*>(p);
+          ks = KM == KMode::Fp8PerTensor ? tensor_scale : a.k_scales[slot_head0 + h];
+        }
+        unpack8_fp8(raw.x, raw.y, y);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) y[k] *= ks;
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (col0 + k < C) ss_all = fmaf(y[k], y[k], ss_all);
+    }
+    r_presum = 1.0f / sqrtf(wave_sum(ss_all) / (float)(C * cv.num_heads) + a.epsilon);
+  }
   for (uint32_t base = 0; base < nit; base += kMaxIter) {
     // phase 1: load the chunk's heads this lane serves, sums of squares
     float x[kMaxIter][8], rh[kMaxIter];
@@ -135,9 +167,11 @@ __global__ __launch_bounds__(256) void kv_norm_kernel(const KvNormArgs a) {
         ss_token += ss;
       }
     }
-    float r_token = 0.0f;
-    if constexpr (!PER_HEAD)
-      r_token = 1.0f / sqrtf(wave_sum(ss_token) / (float)(C * cv.num_heads) + a.epsilon);
+    float r_token = r_presum;
+    if constexpr (!PER_HEAD) {
+      if (!presum)
+        r_token = 1.0f / sqrtf(wave_sum(ss_token) / (float)(C * cv.num_heads) + a.epsilon);
+    }
 
     // phase 2: normalise, re-encode, store
 #pragma unroll
@@ -233,14 +267,8 @@ hipError_t launch_d(const KvNormArgs& a, bool mbc, KMode km, uint32_t blocks, hi
 
 }  // namespace
 
-uint32_t kv_norm_max_heads(uint32_t head_dim) {
-  return kMaxIter * (uint32_t)(kWave / pow2_at_least((int)head_dim / 8));
-}
-
 hipError_t launch_kv_norm(const KvNormArgs& a, bool multiply_before_cast, KMode kmode,
                           hipStream_t stream) {
-  if (!a.per_head && a.cache.num_heads > kv_norm_max_heads(a.head_dim))
-    return hipErrorInvalidValue;
   const uint64_t blocks = ((uint64_t)a.total_tokens + kWavesPerBlock - 1) / kWavesPerBlock;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffull) return hipErrorInvalidValue;

@@ -50,7 +50,6 @@ hipError_t launch_qk_rope(const QkArgs& a, int head_dim, bool inter, KMode km, h
   ++g_calls; g_qk = a; g_qk_dim = head_dim; g_qk_inter = inter; g_qk_mode = km;
   return hipSuccess;
 }
-uint32_t kv_norm_max_heads(uint32_t head_dim) { return 4u * (64u / lanes_per_head(head_dim)); }
 hipError_t launch_kv_norm(const KvNormArgs& a, bool mbc, KMode km, hipStream_t) {
   ++g_calls; g_norm = a; g_norm_mbc = mbc; g_norm_mode = km;
   return hipSuccess;
@@ -481,10 +480,11 @@ int main() {
     EXPECT(!g_norm.per_head && !g_norm_mbc && g_norm_mode == KMode::Bf16);
     EXPECT(g_norm.total_tokens == 7 && g_norm.gamma_len == 100 && g_norm.weight_offset == 0.5f);
     EXPECT(g_norm.head_dim == 128);
+    // the per-token statistic over more heads than one register chunk holds
     pkv_paged_cache big = k_cache(PKV_DTYPE_BF16, PKV_SCALE_NONE, 17, 128);
     EXPECT(rms_norm_kv_cache_paged(&big, 1, P(40960), 128, 1e-6f, 0.f, 7,
                                    static_cast<const uint32_t*>(P(28672)), 2, 0, 1, nullptr) ==
-           PKV_ERR_UNSUPPORTED);
+           PKV_OK && !g_norm.per_head && g_norm.cache.num_heads == 17);
     EXPECT(rms_norm_kv_cache_paged(&big, 1, P(40960), 128, 1e-6f, 0.f, 7,
                                    static_cast<const uint32_t*>(P(28672)), 2, 1, 1, nullptr) ==
            PKV_OK && g_norm.per_head);

@@ -391,15 +391,16 @@ def test_kv_norm_validation(pkv):
     assert call_norm(pkv, kcache(pkv), gamma_len=129) == SHAPE
     # one statistic per token: every head of the token in one wave's registers
     assert call_norm(pkv, kcache(pkv), per_head=0, T=0) == OK
+    # the per-token statistic takes any head count (17 heads: two register chunks)
     assert call_norm(pkv, kcache(pkv, num_heads=17, slot_stride=17 * 128, page_stride=16 * 17 * 128,
-                                  layer_stride=8 * 16 * 17 * 128), per_head=0) == UNSUP
+                                  layer_stride=8 * 16 * 17 * 128), per_head=0, T=0) == OK
     assert call_norm(pkv, kcache(pkv, num_heads=17, slot_stride=17 * 128, page_stride=16 * 17 * 128,
                                   layer_stride=8 * 16 * 17 * 128), per_head=1, T=0) == OK
     assert call_norm(pkv, kcache(pkv, head_dim=512), gamma_len=128) == UNSUP
     assert call_norm(pkv, kcache(pkv, head_dim=112), gamma_len=64) == UNSUP
     d96 = dict(head_dim=96, head_stride=96, slot_stride=17 * 96, page_stride=16 * 17 * 96,
                layer_stride=8 * 16 * 17 * 96, num_heads=17)
-    assert call_norm(pkv, kcache(pkv, **d96), gamma_len=96, per_head=0) == UNSUP  # > 16 heads
+    assert call_norm(pkv, kcache(pkv, **d96), gamma_len=96, per_head=0, T=0) == OK
     assert call_norm(pkv, kcache(pkv, **d96), gamma_len=96, per_head=1, T=0) == OK
     assert call_norm(pkv, kcache(pkv), gamma=None) == NULL
     assert call_norm(pkv, kcache(pkv), gamma=FAKE + 2) == ALIGN

@@ -5,6 +5,7 @@ and without position ids, head_dim 64 and 128, partial norm widths,
 weight_offset, both cast orders, and determinism."""
 import numpy as np
 import pytest
+import torch
 
 import gpu_helpers as gh
 import oracle_pins
@@ -307,6 +308,63 @@ def test_kv_norm_per_token_statistic(orc, kind):
     d = gh.bf16_ulp_diff(k[rows], k_o[rows])
     frac = float((d != 0).sum() / max(d.size, 1))
     _say(f"[kvnorm-tok] max_ulp={int(d.max())} diff_frac={frac}")
+    assert int(d.max()) <= (1 if mbc else 2)
+    assert frac <= gh.BF16_MAX_DIFF_FRAC
+    assert np.array_equal(k[rows][..., cols:], case.k_cache[rows][..., cols:])
+
+
+@pytest.mark.parametrize("D,Hkv,kmode,mbc,planned",
+                         [(128, 64, "bf16", True, False), (128, 32, "bf16", False, False),
+                          (64, 48, "bf16", True, True), (256, 12, "bf16", True, False),
+                          (96, 20, "bf16", False, False), (128, 40, "per_tensor", True, False),
+                          (128, 40, "per_token", True, True), (80, 33, "per_token", True, False)])
+def test_kv_norm_per_token_statistic_many_heads(orc, D, Hkv, kmode, mbc, planned):
+    """per_head_norm=False on tokens with more heads than one register chunk
+    of the kernel holds (64 / (D/8) x 4 heads): the statistic is summed over
+    every head first, then each chunk is normalised; every encoding, both
+    cast orders, partial gamma, the planned form."""
+    import paged_kv_cache_wavefront_amd as pkv
+    rng = workloads.make_rng(6300 + D + Hkv)
+    new = rng.integers(1, 70, size=9, endpoint=True)
+    prior = rng.integers(0, 90, size=9, endpoint=True)
+    fp8 = kmode != "bf16"
+    case = workloads.build_qk(f"kvnorm_h{Hkv}_d{D}_{kmode}", 6300 + D + Hkv, new, prior, Hq=2,
+                              Hkv=Hkv, D=D, page_size=8, max_seq_len=256, theta=10000.0,
+                              interleaved=False, with_position_ids=False, norm_cols=None, rng=rng,
+                              k_dtype="fp8" if fp8 else "bf16",
+                              k_scale_mode=kmode if fp8 else "per_tensor")
+    cols = D - 8 if D != 80 else D
+    gamma = workloads.bf16_bits(rng.uniform(0.5, 1.5, cols).astype(np.float32))
+    total = case.T - 1
+    _say(f"[kvnorm-many] {case.name} T={case.T} cols={cols} mbc={mbc} planned={planned}")
+    dev = gh.QkDevice(case)
+    if planned:
+        plan = torch.empty((case.T, 4), dtype=torch.int32, device="cuda")
+        pkv.pkv_token_plan(plan, dev.offsets, dev.desc)
+        pkv.rms_norm_kv_cache_paged_planned(dev.desc, case.layer_idx, gh.dev_bf16(gamma),
+                                            case.epsilon, 0.125, total, plan, False, mbc)
+    else:
+        dev.kv_norm(gh.dev_bf16(gamma), 0.125, total, mbc, per_head=False)
+    k, ks = dev.k_host()
+    assert int(dev.error_count.item()) == 0
+    k_o = case.k_cache.copy()
+    ks_o = None if case.k_scales is None else case.k_scales.copy()
+    if fp8:
+        with orc.fp8_probe(k_o) as pre:
+            orc.rms_norm_kv_cache_paged(k_o, case.layer_idx, case.row_offsets,
+                                        case.cache_lengths, case.page_table, gamma, case.epsilon,
+                                        0.125, total, mbc, case.k_scale_mode, ks_o,
+                                        per_head_norm=False)
+        _say(f"[kvnorm-many] {check_fp8_k(case, k, ks, k_o, ks_o, pre, 'k')}")
+        return
+    orc.rms_norm_kv_cache_paged(k_o, case.layer_idx, case.row_offsets, case.cache_lengths,
+                                case.page_table, gamma, case.epsilon, 0.125, total, mbc,
+                                per_head_norm=False)
+    rows = gh.written_k_rows(case)
+    assert np.array_equal(k[~rows], case.k_cache[~rows])
+    d = gh.bf16_ulp_diff(k[rows], k_o[rows])
+    frac = float((d != 0).sum() / max(d.size, 1))
+    _say(f"[kvnorm-many] max_ulp={int(d.max())} diff_frac={frac}")
     assert int(d.max()) <= (1 if mbc else 2)
     assert frac <= gh.BF16_MAX_DIFF_FRAC
     assert np.array_equal(k[rows][..., cols:], case.k_cache[rows][..., cols:])

@@ -144,7 +144,7 @@ def test_kv_norm_random(orc, seed):
     w = float(rng.choice([0.0, 0.25, -0.5, 1.0]))
     fp8 = case.k_cache.dtype == np.uint8
     mbc = True if fp8 else bool(rng.random() < 0.5)
-    per_head = bool(rng.random() < 0.6) or Hkv * D > 2048
+    per_head = bool(rng.random() < 0.6)
     total = case.T - int(rng.integers(0, min(3, case.T - 1), endpoint=True))
     _say(f"[rand-kvnorm] seed={seed} {cfg} C={C} w={w} mbc={mbc} per_head={per_head} "
          f"total={total}")
