@@ -26,8 +26,12 @@
 //   are the same for every head: one 64-byte load per lane per token, kept in
 //   registers.
 // * The head-chunk-0 wave of a token also owns its latent row: lane l holds
-//   non-rope values 8l..8l+7 (lanes below kv_norm_dim / 8); lanes 0..LP-1
-//   hold the rope tail with the q mapping.  The sum of squares (and the
+//   non-rope values 8l..8l+7 (lanes below kv_norm_dim / 8) and rope-tail
+//   value l (and l + 64 for rope_dim 128): one tail value per lane instead
+//   of eight on a few lanes, since every lane of a wave pays for every
+//   instruction.  A tail pair's partner comes from lane l +- R/2 (a
+//   cross-lane permute; in the same lane for rope_dim 128), and its cos/sin
+//   with one 8-byte load from the freqs row.  The sum of squares (and the
 //   per-token amax) reduce across the wave with DPP inside rows and readlane
 //   across rows; the sum of squares is reduced while the second step of the
 //   address chain is in flight.  The non-rope value is formed as
@@ -70,6 +74,52 @@ struct HeadLane {
     chunk = first ? k : LP / 2 + pair_block;
   }
 };
+
+// The latent row's rope tail, one value per lane (two for rope_dim 128): lane
+// l holds tail value l (rope_dim 32: lanes 0..31 only) and, for rope_dim 128,
+// value l + 64 in the upper half of its word.  Value i belongs to pair
+// i mod R/2; for rope_dim 32 and 64 the pair's other member sits in lane
+// l ^ R/2, for 128 in the same lane.
+template <int R>
+struct TailLane {
+  bool active;  // holds tail values
+  int pair;     // rotation pair of its (first) value
+  bool first;   // its (first) value is the pair's first member
+  __device__ __forceinline__ explicit TailLane(int lane) {
+    active = R == 128 || lane < R;
+    pair = R == 128 ? lane : lane % (R / 2);
+    first = R == 128 || lane % R < R / 2;
+  }
+};
+
+__device__ __forceinline__ uint32_t load2_stream(const uint16_t* p) {
+  return __builtin_nontemporal_load(p);
+}
+
+template <int R>
+__device__ __forceinline__ uint32_t load_tail(const uint16_t* tail_row, int lane) {
+  if constexpr (R == 128)
+    return load2_stream(tail_row + lane) | (load2_stream(tail_row + 64 + lane) << 16);
+  else
+    return lane < R ? load2_stream(tail_row + lane) : 0u;
+}
+
+// Rotated tail values of this lane (tv[1] only for rope_dim 128); tcs is the
+// (cos, sin) of the lane's pair.
+template <int R>
+__device__ __forceinline__ void rotate_tail(uint32_t raw, const float2& tcs,
+                                            const TailLane<R>& tl, float (&tv)[2]) {
+  const float own = bf16_lo(raw);
+  if constexpr (R == 128) {
+    const float hi = bf16_hi(raw);
+    tv[0] = sum_of_products(own, tcs.x, hi, -tcs.y);
+    tv[1] = sum_of_products(hi, tcs.x, own, tcs.y);
+  } else {
+    const float par = R == 64 ? __shfl_xor(own, 32) : swizzle<kSwizzleXor16>(own);
+    tv[0] = sum_of_products(own, tcs.x, par, tl.first ? -tcs.y : tcs.y);
+    tv[1] = 0.0f;
+  }
+}
 
 // Rotate the 8 values this lane owns, given its partner's 8 values: first
 // half  out = own*cos - partner*sin;  second half  out = own*cos + partner*sin.
@@ -149,7 +199,8 @@ __device__ __forceinline__ float latent_rms(const uint4& xn, const uint4& gm, fl
 template <int NI>
 struct ItemLoads {
   uint4 q[NI];
-  uint4 xn, tail;
+  uint4 xn;
+  uint32_t tail;
   uint4 pe;
 };
 
@@ -168,12 +219,13 @@ __device__ __forceinline__ void issue_item(const MlaArgs& a, uint32_t t, uint32_
     load_q<NI, HPI, false>(L.q, qsrc, 2 * HPI * a.qi_head, qi_lane, h_lane, a.num_heads);
   else
     load_q<NI, HPI, true>(L.q, qsrc, 2 * HPI * a.qi_head, qi_lane, h_lane, a.num_heads);
-  L.xn = L.tail = make_uint4(0, 0, 0, 0);
+  L.xn = make_uint4(0, 0, 0, 0);
+  L.tail = 0;
   if constexpr (MODE != MlaOut::Bf16InPlace) {
     if (chunk == 0) {
       const uint16_t* row = a.latent + (int64_t)t * a.kv_row;
       if ((uint32_t)lane < a.nope_chunks) L.xn = load16_stream(row + 8 * lane);
-      if (lane < LP) L.tail = load16_stream(row + 8 * a.nope_chunks + 8 * hl.chunk);
+      L.tail = load_tail<R>(row + 8 * a.nope_chunks, lane);
     }
   }
   if constexpr (PLANNED) L.pe = *reinterpret_cast<const uint4*>(a.plan + 4 * (uint64_t)t);
@@ -212,15 +264,18 @@ __device__ __forceinline__ void finish_item(const MlaArgs& a, uint32_t t, uint32
   // The freqs row is loaded without a branch (a skipped token reads row 0,
   // which always exists, and returns before using it), so that nothing
   // issued after the latent row has to complete before the statistic below.
+  const TailLane<R> tl(lane);
   float cs[16];
+  float2 tcs;
   {
-    const float4* fr = reinterpret_cast<const float4*>(
-        a.freqs + (int64_t)(pos_ok ? ts.slot : 0u) * R + 16 * hl.pair_block);
+    const float* frow = a.freqs + (int64_t)(pos_ok ? ts.slot : 0u) * R;
+    const float4* fr = reinterpret_cast<const float4*>(frow + 16 * hl.pair_block);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float4 v = fr[i];
       cs[4 * i] = v.x; cs[4 * i + 1] = v.y; cs[4 * i + 2] = v.z; cs[4 * i + 3] = v.w;
     }
+    tcs = *reinterpret_cast<const float2*>(frow + 2 * tl.pair);
   }
   uint32_t col = 0, page = 0;
   bool col_ok = pos_ok;
@@ -257,7 +312,7 @@ __device__ __forceinline__ void finish_item(const MlaArgs& a, uint32_t t, uint32
     if (latent_wave) {
       const uint16_t* row = static_cast<const uint16_t*>(cv.layer_base) + row_elems;
       if ((uint32_t)lane < a.nope_chunks) L.xn = load16_stream(row + 8 * lane);
-      if (lane < LP) L.tail = load16_stream(row + 8 * a.nope_chunks + 8 * hl.chunk);
+      L.tail = load_tail<R>(row + 8 * a.nope_chunks, lane);
     }
   }
   if (hl.first) {
@@ -280,19 +335,19 @@ __device__ __forceinline__ void finish_item(const MlaArgs& a, uint32_t t, uint32
 
   // ---- latent row: RMSNorm (non-rope part), RoPE (tail) ---------------------
   if constexpr (INPLACE) r = latent_rms(L.xn, gm, xg, a.inv_dn, a.epsilon);
-  float tv[8], tp[8];
-  unpack8(L.tail, tv);
-  unpack8(mirror16<LP>(L.tail), tp);
-  rotate_own(tv, tp, cs);  // meaningful on lanes 0..LP-1 only
+  float tv[2];
+  rotate_tail<R>(L.tail, tcs, tl, tv);  // meaningful on active tail lanes only
   const bool nope_lane = (uint32_t)lane < a.nope_chunks;
-  const uint32_t tail_off = 8 * a.nope_chunks + 8 * hl.chunk;
+  const uint32_t tail0 = 8 * a.nope_chunks + lane;  // element of the lane's (first) tail value
 
   if constexpr (MODE == MlaOut::Bf16 || INPLACE) {
     uint16_t* row = static_cast<uint16_t*>(cv.layer_base) + row_elems;
 #pragma unroll
     for (int k = 0; k < 8; ++k) xg[k] *= r;
     if (nope_lane) store16_stream(row + 8 * lane, pack8_bf16(xg));
-    if (lane < LP) store16_stream(row + tail_off, pack8_bf16(tv));
+    const uint32_t w = pack_bf16x2(tv[0], tv[1]);
+    if (tl.active) __builtin_nontemporal_store((uint16_t)w, row + tail0);
+    if (R == 128) __builtin_nontemporal_store((uint16_t)(w >> 16), row + tail0 + 64);
     return;
   } else {
     float inv;
@@ -300,17 +355,14 @@ __device__ __forceinline__ void finish_item(const MlaArgs& a, uint32_t t, uint32
       inv = 1.0f / *a.tensor_scale;
     } else {
       // max |y| over the row: the non-rope part scales monotonically by r
-      // (lanes past the non-rope chunks hold zeros)
+      // (lanes past the non-rope chunks hold zeros), so the lane's largest
+      // |x * gamma| times r is its largest normalised value
       float am = 0.0f;
 #pragma unroll
       for (int k = 0; k < 8; ++k) am = fmaxf(am, fabsf(xg[k]));
-      am = wave_max(am) * r;
-      float at = 0.0f;
-      if (lane < LP) {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) at = fmaxf(at, fabsf(tv[k]));
-      }
-      am = fmaxf(am, wave_max(at));
+      am *= r;
+      if (tl.active) am = fmaxf(am, fmaxf(fabsf(tv[0]), fabsf(tv[1])));
+      am = wave_max(am);
       const float st = am / 448.0f;
       inv = st > 0.0f ? 1.0f / st : 0.0f;
       if (lane == 0)
@@ -318,13 +370,12 @@ __device__ __forceinline__ void finish_item(const MlaArgs& a, uint32_t t, uint32
     }
     const float rs = r * inv;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      xg[k] *= rs;
-      tv[k] *= inv;
-    }
+    for (int k = 0; k < 8; ++k) xg[k] *= rs;
     uint8_t* row = static_cast<uint8_t*>(cv.layer_base) + row_elems;
     if (nope_lane) store8_stream(row + 8 * lane, pack8_fp8(xg));
-    if (lane < LP) store8_stream(row + tail_off, pack8_fp8(tv));
+    const uint32_t codes = pack4_fp8(tv[0] * inv, tv[1] * inv, 0.0f, 0.0f);
+    if (tl.active) __builtin_nontemporal_store((uint8_t)codes, row + tail0);
+    if (R == 128) __builtin_nontemporal_store((uint8_t)(codes >> 8), row + tail0 + 64);
   }
 }
 
