@@ -20,8 +20,13 @@ point of the method:
   it;
 * :func:`mla_gather_latent_paged` -- the paged-to-contiguous latent copy and
   fp8 (de)quantisation step of mla_prefill_branch_fp8 ("mla_graph" page);
-* the bf16 and FP8 E4M3FN codecs and the RoPE / RMSNorm row steps, exposed so
-  that tests can pin each step on its own.
+* the bf16, binary16 and FP8 E4M3FN codecs and the RoPE / RMSNorm row steps,
+  exposed so that tests can pin each step on its own.
+
+Element types: q (and q_out), freqs_cis and gamma arrays may be bf16 (bits in
+a uint16 array), fp16 (numpy float16) or fp32, the dtype / out_rope_dtype /
+freq_dtype / gamma_dtype parameters of the pages; the latent row is bf16 (the
+MLA page's kv_input_fn yields bfloat16).
 
 Parity status of each function: pinned by ``tests/test_oracle_*.py`` against
 closed forms, invariants, brute force and library special cases (no page
@@ -49,6 +54,21 @@ SCALE_PER_TENSOR = 1
 SCALE_PER_TOKEN = 2
 CACHE_FP8 = 0
 CACHE_BF16 = 1
+# element types of q, freqs and gamma arrays, from their numpy dtype: uint16
+# holds bf16 bits, float16 holds fp16 values (the same bits), float32 fp32
+ELEM_BF16 = 0
+ELEM_F32 = 2
+ELEM_F16 = 3
+
+
+def _elem_type(a: np.ndarray) -> int:
+    if a.dtype == np.uint16:
+        return ELEM_BF16
+    if a.dtype == np.float16:
+        return ELEM_F16
+    if a.dtype == np.float32:
+        return ELEM_F32
+    raise TypeError(f"element type {a.dtype} is not bf16 (uint16), fp16 or fp32")
 
 
 def build() -> str:
@@ -67,6 +87,10 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.oracle_bf16_decode.argtypes = [ctypes.c_uint16]
     lib.oracle_bf16_encode.restype = ctypes.c_uint16
     lib.oracle_bf16_encode.argtypes = [ctypes.c_double]
+    lib.oracle_f16_decode.restype = ctypes.c_double
+    lib.oracle_f16_decode.argtypes = [ctypes.c_uint16]
+    lib.oracle_f16_encode.restype = ctypes.c_uint16
+    lib.oracle_f16_encode.argtypes = [ctypes.c_double]
     lib.oracle_e4m3fn_decode.restype = ctypes.c_double
     lib.oracle_e4m3fn_decode.argtypes = [ctypes.c_uint8]
     lib.oracle_e4m3fn_encode_sat.restype = ctypes.c_uint8
@@ -79,28 +103,29 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.oracle_rmsnorm_row.argtypes = [_vp, _vp, _i64, _vp, ctypes.c_double]
     lib.oracle_mla_rope_rmsnorm_quant.restype = ctypes.c_int
     lib.oracle_mla_rope_rmsnorm_quant.argtypes = [
-        _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
-        ctypes.c_float, _i64, _i64, _i64, _vp, ctypes.c_int, _i64, _i64, _i64,
-        _i64, ctypes.c_int, ctypes.c_float, _vp]
+        _vp, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp, _vp, _i64, _vp, _i64, _vp,
+        ctypes.c_int, _i64, _vp, ctypes.c_int, ctypes.c_float, _i64, _i64, _i64, _vp,
+        ctypes.c_int, _i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_float, _vp]
     lib.oracle_token_plan.restype = ctypes.c_int
     lib.oracle_token_plan.argtypes = [_vp, _i64, _vp, _vp, _i64, _vp, _i64, _i64, _i64]
     lib.oracle_mla_rope_rmsnorm_quant_planned.restype = ctypes.c_int
     lib.oracle_mla_rope_rmsnorm_quant_planned.argtypes = [
-        _vp, ctypes.c_int, _vp, _vp, _vp, _i64, _vp, _i64, _vp, ctypes.c_float, _i64, _i64,
-        _i64, _vp, ctypes.c_int, _i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_float, _vp]
+        _vp, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp, _i64, _vp, ctypes.c_int, _i64, _vp,
+        ctypes.c_int, ctypes.c_float, _i64, _i64, _i64, _vp, ctypes.c_int, _i64, _i64, _i64,
+        _i64, ctypes.c_int, ctypes.c_float, _vp]
     lib.oracle_rms_norm_kv_cache_planned.restype = ctypes.c_int
     lib.oracle_rms_norm_kv_cache_planned.argtypes = [
         _vp, ctypes.c_int, ctypes.c_int, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _vp, _vp,
-        _i64, ctypes.c_float, ctypes.c_float, _i64, ctypes.c_int, ctypes.c_int]
+        ctypes.c_int, _i64, ctypes.c_float, ctypes.c_float, _i64, ctypes.c_int, ctypes.c_int]
     lib.oracle_mla_rope_rmsnorm_inplace.restype = ctypes.c_int
     lib.oracle_mla_rope_rmsnorm_inplace.argtypes = [
-        _vp, ctypes.c_int, _vp, _vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp, ctypes.c_float,
-        _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i64]
+        _vp, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp, _i64, _vp, _i64, _vp, ctypes.c_int,
+        _i64, _vp, ctypes.c_int, ctypes.c_float, _i64, _i64, _i64, _vp, _i64, _i64, _i64, _i64]
     lib.oracle_qk_rope_paged_ragged.restype = ctypes.c_int
     lib.oracle_qk_rope_paged_ragged.argtypes = [
-        _vp, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _i64, _vp, ctypes.c_int, ctypes.c_int,
-        _vp, _i64, _i64, _i64, _i64, _i64, _vp, _i64, _vp, _vp, ctypes.c_int, _vp, _i64,
-        ctypes.c_float]
+        _vp, _vp, ctypes.c_int, _i64, _i64, _vp, _vp, _i64, _vp, _i64, _vp, ctypes.c_int,
+        ctypes.c_int, _vp, _i64, _i64, _i64, _i64, _i64, _vp, ctypes.c_int, _i64, _vp, _vp,
+        ctypes.c_int, _vp, _i64, ctypes.c_float]
     lib.oracle_mla_gather_latent_paged.restype = ctypes.c_int
     lib.oracle_mla_gather_latent_paged.argtypes = [
         _vp, ctypes.c_int, _vp, ctypes.c_float, _vp, _i64, _vp, _i64, _vp, ctypes.c_int,
@@ -108,7 +133,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.oracle_rms_norm_kv_cache_paged.restype = ctypes.c_int
     lib.oracle_rms_norm_kv_cache_paged.argtypes = [
         _vp, ctypes.c_int, ctypes.c_int, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _vp, _vp,
-        _i64, _vp, _i64, _vp, _i64, ctypes.c_float, ctypes.c_float, _i64, ctypes.c_int]
+        _i64, _vp, _i64, _vp, ctypes.c_int, _i64, ctypes.c_float, ctypes.c_float, _i64,
+        ctypes.c_int, ctypes.c_int]
     _declare_probe(lib)
     return lib
 
@@ -166,6 +192,18 @@ class Oracle:
     def bf16_encode(self, v: float) -> int:
         return self.lib.oracle_bf16_encode(float(v))
 
+    def f16_decode(self, bits: int) -> float:
+        return self.lib.oracle_f16_decode(int(bits))
+
+    def f16_encode(self, v: float) -> int:
+        return self.lib.oracle_f16_encode(float(v))
+
+    def f16_encode_array(self, v) -> np.ndarray:
+        f = self.lib.oracle_f16_encode
+        v = np.asarray(v, np.float64)
+        return np.fromiter((f(float(x)) for x in v.ravel()), np.uint16,
+                           count=v.size).reshape(v.shape)
+
     def e4m3fn_decode(self, code: int) -> float:
         return self.lib.oracle_e4m3fn_decode(int(code))
 
@@ -213,12 +251,13 @@ class Oracle:
                                token_scales=None):
         """Fill ``q_out`` and the new rows of ``cache`` (and ``token_scales``).
 
-        Shapes: q_in [T,H,R] u16; q_out the same shape, u16 (bf16) or f32;
-        latent [T,Dn+R] u16; row_offsets [B+1] u32;
-        cache_lengths [B] u32; page_table [B,stride] u32; freqs [max_seq,R]
-        f32; gamma [Dn] u16; cache [L,P,S,1,Dn+R] u8 (fp8) or u16 (bf16);
-        token_scales [L,P,S,1] f32.  ``scale_mode``: "per_tensor" |
-        "per_token" (ignored for a bf16 cache).
+        Shapes: q_in [T,H,R]; q_out the same shape; latent [T,Dn+R] u16
+        (bf16); row_offsets [B+1] u32; cache_lengths [B] u32; page_table
+        [B,stride] u32; freqs [max_seq,R]; gamma [Dn]; cache [L,P,S,1,Dn+R] u8
+        (fp8) or u16 (bf16); token_scales [L,P,S,1] f32.  q_in, q_out, freqs
+        and gamma may each be u16 (bf16 bits), float16 or float32 (q_in:
+        bf16 or fp16).  ``scale_mode``: "per_tensor" | "per_token" (ignored
+        for a bf16 cache).
         """
         T, H, R = q_in.shape
         W = latent.shape[1]
@@ -231,13 +270,13 @@ class Oracle:
         cache_type = CACHE_BF16 if cache.dtype == np.uint16 else CACHE_FP8
         mode = {"per_tensor": SCALE_PER_TENSOR, "per_token": SCALE_PER_TOKEN,
                 "none": 0}[scale_mode]
-        q_f32 = q_out.dtype == np.float32
         rc = self.lib.oracle_mla_rope_rmsnorm_quant(
-            _ptr(q_out, np.float32 if q_f32 else np.uint16), int(q_f32),
-            _ptr(q_in, np.uint16), _ptr(latent, np.uint16),
+            _ptr(q_out, q_out.dtype), _elem_type(q_out), _ptr(q_in, q_in.dtype),
+            _elem_type(q_in), _ptr(latent, np.uint16),
             _ptr(row_offsets, np.uint32), _ptr(cache_lengths, np.uint32), B,
             _ptr(page_table, np.uint32), page_table.shape[1],
-            _ptr(freqs, np.float32), freqs.shape[0], _ptr(gamma, np.uint16),
+            _ptr(freqs, freqs.dtype), _elem_type(freqs), freqs.shape[0],
+            _ptr(gamma, gamma.dtype), _elem_type(gamma),
             float(epsilon), H, R, Dn, _ptr(cache, cache.dtype), cache_type, L, P, S,
             int(layer_idx), mode, float(tensor_scale),
             _ptr(token_scales, np.float32))
@@ -271,11 +310,11 @@ class Oracle:
         cache_type = CACHE_BF16 if cache.dtype == np.uint16 else CACHE_FP8
         mode = {"per_tensor": SCALE_PER_TENSOR, "per_token": SCALE_PER_TOKEN,
                 "none": 0}[scale_mode]
-        q_f32 = q_out.dtype == np.float32
         rc = self.lib.oracle_mla_rope_rmsnorm_quant_planned(
-            _ptr(q_out, np.float32 if q_f32 else np.uint16), int(q_f32),
-            _ptr(q_in, np.uint16), _ptr(latent, np.uint16), _ptr(plan, np.uint32), T,
-            _ptr(freqs, np.float32), freqs.shape[0], _ptr(gamma, np.uint16), float(epsilon),
+            _ptr(q_out, q_out.dtype), _elem_type(q_out), _ptr(q_in, q_in.dtype),
+            _elem_type(q_in), _ptr(latent, np.uint16), _ptr(plan, np.uint32), T,
+            _ptr(freqs, freqs.dtype), _elem_type(freqs), freqs.shape[0],
+            _ptr(gamma, gamma.dtype), _elem_type(gamma), float(epsilon),
             H, R, W - R, _ptr(cache, cache.dtype), cache_type, L, P, S, int(layer_idx), mode,
             float(tensor_scale), _ptr(token_scales, np.float32))
         _check(rc, "mla_rope_rmsnorm_quant_planned")
@@ -290,13 +329,13 @@ class Oracle:
         if cache.dtype != np.uint16 or one != 1 or q_out.shape != q_in.shape:
             raise ValueError("inconsistent in-place MLA arguments")
         B = row_offsets.size - 1
-        q_f32 = q_out.dtype == np.float32
         rc = self.lib.oracle_mla_rope_rmsnorm_inplace(
-            _ptr(q_out, np.float32 if q_f32 else np.uint16), int(q_f32),
-            _ptr(q_in, np.uint16), _ptr(row_offsets, np.uint32),
+            _ptr(q_out, q_out.dtype), _elem_type(q_out), _ptr(q_in, q_in.dtype),
+            _elem_type(q_in), _ptr(row_offsets, np.uint32),
             _ptr(cache_lengths, np.uint32), B, _ptr(page_table, np.uint32),
-            page_table.shape[1], _ptr(freqs, np.float32), freqs.shape[0],
-            _ptr(gamma, np.uint16), float(epsilon), H, R, W - R, _ptr(cache, np.uint16),
+            page_table.shape[1], _ptr(freqs, freqs.dtype), _elem_type(freqs), freqs.shape[0],
+            _ptr(gamma, gamma.dtype), _elem_type(gamma), float(epsilon), H, R, W - R,
+            _ptr(cache, np.uint16),
             L, P, S, int(layer_idx))
         _check(rc, "mla_rope_rmsnorm_inplace")
 
@@ -306,16 +345,18 @@ class Oracle:
                              k_scales=None, mrope_section=None):
         """Fill ``q_out``; rotate (and optionally K-normalise) ``k_cache``.
 
-        Shapes: q [T,Hq,D] u16; k_cache [L,P,S,Hkv,D] u16 (bf16) or u8 (fp8,
+        Shapes: q [T,Hq,D] u16 (bf16 bits) or float16 (q_out of the same
+        type); k_cache [L,P,S,Hkv,D] u16 (bf16) or u8 (fp8,
         with k_scale_mode "per_tensor" -> k_scales f32 [1], "per_token" ->
-        k_scales f32 [L,P,S,Hkv], rewritten); freqs [max_seq,D] f32;
+        k_scales f32 [L,P,S,Hkv], rewritten); freqs [max_seq,D] f32, float16
+        or u16 (bf16);
         position_ids [T] u32 or None, or [3, T] u32 with mrope_section =
         (temporal, height, width) pair counts summing to D/2; k_gamma [C]
         u16 or None.
         """
         T, Hq, D = q_in.shape
         L, P, S, Hkv, Dk = k_cache.shape
-        if Dk != D or q_out.shape != q_in.shape:
+        if Dk != D or q_out.shape != q_in.shape or q_out.dtype != q_in.dtype:
             raise ValueError("inconsistent QK shapes")
         B = row_offsets.size - 1
         k_type = CACHE_BF16 if k_cache.dtype == np.uint16 else CACHE_FP8
@@ -324,11 +365,12 @@ class Oracle:
         if sec is not None and (position_ids is None or position_ids.shape != (3, T)):
             raise ValueError("multimodal RoPE needs position ids of shape [3, T]")
         rc = self.lib.oracle_qk_rope_paged_ragged(
-            _ptr(q_out, np.uint16), _ptr(q_in, np.uint16), Hq, D,
+            _ptr(q_out, q_out.dtype), _ptr(q_in, q_in.dtype), _elem_type(q_in), Hq, D,
             _ptr(row_offsets, np.uint32), _ptr(cache_lengths, np.uint32), B,
             _ptr(page_table, np.uint32), page_table.shape[1], _ptr(k_cache, k_cache.dtype),
             k_type, mode, _ptr(k_scales, np.float32), L, P, S, Hkv, int(layer_idx),
-            _ptr(freqs, np.float32), freqs.shape[0], _ptr(position_ids, np.uint32),
+            _ptr(freqs, freqs.dtype), _elem_type(freqs), freqs.shape[0],
+            _ptr(position_ids, np.uint32),
             None if sec is None else sec.ctypes.data,
             int(bool(interleaved)), _ptr(k_gamma, np.uint16),
             0 if k_gamma is None else k_gamma.size, float(epsilon))
@@ -371,7 +413,7 @@ class Oracle:
             L, P, S, Hkv, D, int(layer_idx),
             _ptr(row_offsets, np.uint32), _ptr(cache_lengths, np.uint32), B,
             _ptr(page_table, np.uint32), page_table.shape[1],
-            _ptr(gamma, np.uint16), gamma.size, float(epsilon),
+            _ptr(gamma, gamma.dtype), _elem_type(gamma), gamma.size, float(epsilon),
             float(weight_offset), int(total_seq_len),
             int(bool(multiply_before_cast)), int(bool(per_head_norm)))
         _check(rc, "rms_norm_kv_cache_paged")
@@ -389,7 +431,8 @@ class Oracle:
         rc = self.lib.oracle_rms_norm_kv_cache_planned(
             _ptr(k_cache, k_cache.dtype), k_type, mode, _ptr(k_scales, np.float32),
             L, P, S, Hkv, D, int(layer_idx), _ptr(plan, np.uint32),
-            _ptr(gamma, np.uint16), gamma.size, float(epsilon), float(weight_offset),
+            _ptr(gamma, gamma.dtype), _elem_type(gamma), gamma.size, float(epsilon),
+            float(weight_offset),
             int(total_seq_len), int(bool(multiply_before_cast)), int(bool(per_head_norm)))
         _check(rc, "rms_norm_kv_cache_planned")
 

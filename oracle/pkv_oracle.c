@@ -92,6 +92,74 @@ uint16_t oracle_bf16_encode(double v) {
   return (uint16_t)(sign | (uint16_t)(u >> 16));
 }
 
+/* IEEE 754 binary16: 1 sign bit, 5 exponent bits with bias 15, 10 fraction
+ * bits; exponent field 0 holds zero and the subnormals m * 2^-24, field 31
+ * the infinities (fraction 0) and NaNs. */
+double oracle_f16_decode(uint16_t bits) {
+  const int e = (bits >> 10) & 0x1F;
+  const int m = bits & 0x3FF;
+  double mag;
+  if (e == 0x1F) mag = m ? NAN : INFINITY;
+  else if (e == 0) mag = ldexp((double)m, -24);
+  else mag = ldexp(1.0 + m / 1024.0, e - 15);
+  return (bits & 0x8000u) ? -mag : mag;
+}
+
+/* Nearest binary16 to v, ties to the even significand, in one step from
+ * binary64; magnitudes that round past the largest finite value (65504)
+ * become infinity, as IEEE rounding to nearest prescribes. */
+uint16_t oracle_f16_encode(double v) {
+  uint16_t sign = signbit(v) ? 0x8000u : 0u;
+  if (isnan(v)) return 0x7E00u;
+  double a = fabs(v);
+  if (a == 0.0) return sign;
+  if (isinf(a)) return (uint16_t)(sign | 0x7C00u);
+  int e;
+  frexp(a, &e);                 /* a = f * 2^e with 0.5 <= f < 1 */
+  int qexp = e - 11;            /* keep 11 significant bits */
+  if (qexp < -24) qexp = -24;   /* subnormal range: fixed quantum 2^-24 */
+  double n = nearbyint(ldexp(a, -qexp));
+  double r = ldexp(n, qexp);
+  if (r > 65504.0) return (uint16_t)(sign | 0x7C00u);
+  if (r < ldexp(1.0, -14)) return (uint16_t)(sign | (uint16_t)ldexp(r, 24)); /* subnormal */
+  int er;
+  frexp(r, &er);
+  const int E = er - 1;         /* r = 1.f * 2^E, -14 <= E <= 15 */
+  const int m = (int)((ldexp(r, -E) - 1.0) * 1024.0);
+  return (uint16_t)(sign | ((E + 15) << 10) | m);
+}
+
+/* Element types of the q, freqs and gamma arrays ([MLA] Parameters: dtype,
+ * freq_dtype, gamma_dtype, out_rope_dtype; [QK] Parameters: dtype and
+ * freq_dtype; [NORM]: the dtype of gamma and weight_offset). */
+#define ORACLE_BF16 0
+#define ORACLE_F32 2
+#define ORACLE_F16 3
+
+/* Element i of an array of the given type, widened exactly to binary64. */
+static double elem(const void* base, int64_t i, int type) {
+  if (type == ORACLE_F32) return (double)((const float*)base)[i];
+  const uint16_t bits = ((const uint16_t*)base)[i];
+  return type == ORACLE_F16 ? oracle_f16_decode(bits) : oracle_bf16_decode(bits);
+}
+
+/* v rounded once into element i of an array of the given type. */
+static void put_elem(void* base, int64_t i, int type, double v) {
+  if (type == ORACLE_F32) ((float*)base)[i] = (float)v;  /* RNE */
+  else if (type == ORACLE_F16) ((uint16_t*)base)[i] = oracle_f16_encode(v);
+  else ((uint16_t*)base)[i] = oracle_bf16_encode(v);
+}
+
+/* Row p of a freqs_cis table of `dim` columns as fp32 values (bf16 and fp16
+ * values are exactly fp32 values): a pointer into the table itself when it
+ * is fp32, else into buf, filled. */
+static const float* freqs_row_at(const void* freqs, int type, int64_t p, int64_t dim,
+                                 float* buf) {
+  if (type == ORACLE_F32) return (const float*)freqs + p * dim;
+  for (int64_t i = 0; i < dim; ++i) buf[i] = (float)elem(freqs, p * dim + i, type);
+  return buf;
+}
+
 /* FP8 E4M3FN (OCP): 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits,
  * no infinities, S.1111.111 is NaN, largest finite 0x7E = 448, exponent field
  * 0 holds subnormals m * 2^-9. */
@@ -229,14 +297,15 @@ static int64_t page_of(const uint32_t* page_table, int64_t pt_stride,
  * quantise at the end, write into the cache).
  *
  * Host arrays, all dense and row-major:
- *   q_out         [T][H][R] bf16 bits, or fp32 when q_out_f32 (q_rope_output)
- *   q_in          bf16 bits [T][H][R]            (q_rope)
+ *   q_out         [T][H][R] of q_out_type (q_rope_output; out_rope_dtype)
+ *   q_in          [T][H][R] of q_in_type         (q_rope; dtype)
  *   latent        bf16 bits [T][Dn + R]          (the KV latent input)
  *   row_offsets   u32 [B + 1]                    (input_row_offsets)
  *   cache_lengths u32 [B]  length of each request's cache before this step
  *   page_table    u32 [B][pt_stride]
- *   freqs         f32 [max_seq_len][R]           (freqs_cis)
- *   gamma         bf16 bits [Dn]
+ *   freqs         [max_seq_len][R] of freq_type  (freqs_cis; freq_dtype)
+ *   gamma         [Dn] of gamma_type             (gamma_dtype)
+ * Element types: ORACLE_BF16 (bits), ORACLE_F16 (bits), ORACLE_F32.
  *   cache         [L][P][S][Dn + R] of u8 (fp8 codes) or u16 (bf16 bits)
  *   token_scales  f32 [L][P][S]  (written in per-token mode only)
  * Only layer `layer_idx` and only the new tokens' slots are written.
@@ -251,9 +320,10 @@ static int plan_entry_placed(const uint32_t* e, int64_t num_pages, int64_t page_
 
 /* gamma + weight_offset of the K-cache norm, widened ([NORM]: weight_offset
  * is added to gamma). */
-static void kv_norm_gamma(const uint16_t* gamma, int64_t n, float weight_offset, double* g) {
+static void kv_norm_gamma(const void* gamma, int gamma_type, int64_t n, float weight_offset,
+                          double* g) {
   for (int64_t k = 0; k < n; ++k)
-    g[k] = oracle_bf16_decode(gamma[k]) + (double)weight_offset;
+    g[k] = elem(gamma, k, gamma_type) + (double)weight_offset;
 }
 
 /* One token of the fused MLA step: q of token t rotated at position pos into
@@ -261,27 +331,26 @@ static void kv_norm_gamma(const uint16_t* gamma, int64_t n, float weight_offset,
  * row `row`) normalised, rotated and written to cache row `row` (row counts
  * latent rows of W = Dn + R elements from the start of the cache, layer
  * included). */
-static int mla_token(void* q_out, int q_out_f32, const uint16_t* q_in, const uint16_t* latent,
-                     int64_t t, int64_t pos, int64_t row, const float* freqs, const double* g,
-                     double eps, int64_t H, int64_t R, int64_t Dn, void* cache,
-                     int cache_type, int scale_mode, float tensor_scale,
-                     float* token_scales) {
+static int mla_token(void* q_out, int q_out_type, const void* q_in, int q_in_type,
+                     const uint16_t* latent, int64_t t, int64_t pos, int64_t row,
+                     const void* freqs, int freq_type, const double* g, double eps, int64_t H,
+                     int64_t R, int64_t Dn, void* cache, int cache_type, int scale_mode,
+                     float tensor_scale, float* token_scales) {
   const int64_t W = Dn + R;
   double x[4096], y[4096], qa[1024], qb[1024];
-  const float* fr = freqs + pos * R;
+  float frow[1024];
+  const float* fr = freqs_row_at(freqs, freq_type, pos, R, frow);
 
   /* q: RoPE on every head, one rounding per value into the output type
-   * ([MLA] Parameters: out_rope_dtype; bf16 or fp32 here). */
+   * ([MLA] Parameters: dtype of q_rope, out_rope_dtype of q_rope_output). */
   for (int64_t h = 0; h < H; ++h) {
-    const uint16_t* src = q_in + (t * H + h) * R;
-    for (int64_t i = 0; i < R; ++i) qa[i] = oracle_bf16_decode(src[i]);
+    for (int64_t i = 0; i < R; ++i) qa[i] = elem(q_in, (t * H + h) * R + i, q_in_type);
     oracle_rope_row(qa, qb, R, fr, 0);
-    if (q_out_f32) {
+    if (q_out_type == ORACLE_F32) {
       float* dst = (float*)q_out + (t * H + h) * R;
       for (int64_t i = 0; i < R; ++i) dst[i] = (float)qb[i];  /* RNE */
     } else {
-      uint16_t* dst = (uint16_t*)q_out + (t * H + h) * R;
-      for (int64_t i = 0; i < R; ++i) dst[i] = oracle_bf16_encode(qb[i]);
+      for (int64_t i = 0; i < R; ++i) put_elem(q_out, (t * H + h) * R + i, q_out_type, qb[i]);
     }
   }
 
@@ -316,10 +385,10 @@ static int mla_token(void* q_out, int q_out_f32, const uint16_t* q_in, const uin
 }
 
 int oracle_mla_rope_rmsnorm_quant(
-    void* q_out, int q_out_f32, const uint16_t* q_in, const uint16_t* latent,
+    void* q_out, int q_out_type, const void* q_in, int q_in_type, const uint16_t* latent,
     const uint32_t* row_offsets, const uint32_t* cache_lengths, int64_t B,
-    const uint32_t* page_table, int64_t pt_stride, const float* freqs,
-    int64_t max_seq_len, const uint16_t* gamma, float epsilon, int64_t H,
+    const uint32_t* page_table, int64_t pt_stride, const void* freqs, int freq_type,
+    int64_t max_seq_len, const void* gamma, int gamma_type, float epsilon, int64_t H,
     int64_t R, int64_t Dn, void* cache, int cache_type, int64_t num_layers,
     int64_t num_pages, int64_t page_size, int64_t layer_idx, int scale_mode,
     float tensor_scale, float* token_scales) {
@@ -329,7 +398,7 @@ int oracle_mla_rope_rmsnorm_quant(
   if (!latent && cache_type != ORACLE_CACHE_BF16) return ORACLE_BAD_ARG;
   double g[4096];
   if (Dn + R > 4096 || R > 1024) return ORACLE_BAD_ARG;
-  for (int64_t k = 0; k < Dn; ++k) g[k] = oracle_bf16_decode(gamma[k]);
+  for (int64_t k = 0; k < Dn; ++k) g[k] = elem(gamma, k, gamma_type);
   const double eps = (double)epsilon; /* the fp32 value, widened exactly */
   int status = ORACLE_OK;
 
@@ -344,9 +413,9 @@ int oracle_mla_rope_rmsnorm_quant(
       if (page < 0) { status = ORACLE_BAD_PAGE; continue; }
       const int64_t off = slot % page_size;
       const int64_t row = ((layer_idx * num_pages + page) * page_size + off);
-      const int rc = mla_token(q_out, q_out_f32, q_in, latent, t, pos, row, freqs, g, eps,
-                               H, R, Dn, cache, cache_type, scale_mode, tensor_scale,
-                               token_scales);
+      const int rc = mla_token(q_out, q_out_type, q_in, q_in_type, latent, t, pos, row,
+                               freqs, freq_type, g, eps, H, R, Dn, cache, cache_type,
+                               scale_mode, tensor_scale, token_scales);
       if (rc != ORACLE_OK) return rc;
     }
   }
@@ -392,9 +461,10 @@ int oracle_token_plan(uint32_t* plan, int64_t T, const uint32_t* row_offsets,
  * a bf16 cache (each row read from the cell it is written back to).
  */
 int oracle_mla_rope_rmsnorm_quant_planned(
-    void* q_out, int q_out_f32, const uint16_t* q_in, const uint16_t* latent,
-    const uint32_t* plan, int64_t T, const float* freqs, int64_t max_seq_len,
-    const uint16_t* gamma, float epsilon, int64_t H, int64_t R, int64_t Dn, void* cache,
+    void* q_out, int q_out_type, const void* q_in, int q_in_type, const uint16_t* latent,
+    const uint32_t* plan, int64_t T, const void* freqs, int freq_type, int64_t max_seq_len,
+    const void* gamma, int gamma_type, float epsilon, int64_t H, int64_t R, int64_t Dn,
+    void* cache,
     int cache_type, int64_t num_layers, int64_t num_pages, int64_t page_size,
     int64_t layer_idx, int scale_mode, float tensor_scale, float* token_scales) {
   if (R <= 0 || R % 2 || Dn <= 0 || H < 0 || T < 0 || layer_idx < 0 ||
@@ -403,7 +473,7 @@ int oracle_mla_rope_rmsnorm_quant_planned(
   if (!latent && cache_type != ORACLE_CACHE_BF16) return ORACLE_BAD_ARG;
   double g[4096];
   if (Dn + R > 4096 || R > 1024) return ORACLE_BAD_ARG;
-  for (int64_t k = 0; k < Dn; ++k) g[k] = oracle_bf16_decode(gamma[k]);
+  for (int64_t k = 0; k < Dn; ++k) g[k] = elem(gamma, k, gamma_type);
   const double eps = (double)epsilon;
   int status = ORACLE_OK;
   for (int64_t t = 0; t < T; ++t) {
@@ -411,9 +481,9 @@ int oracle_mla_rope_rmsnorm_quant_planned(
     if (!plan_entry_placed(e, num_pages, page_size)) { status = ORACLE_BAD_PAGE; continue; }
     if ((int64_t)e[2] >= max_seq_len) { status = ORACLE_BAD_POSITION; continue; }
     const int64_t row = ((layer_idx * num_pages + e[0]) * page_size + e[1]);
-    const int rc = mla_token(q_out, q_out_f32, q_in, latent, t, (int64_t)e[2], row, freqs, g,
-                             eps, H, R, Dn, cache, cache_type, scale_mode, tensor_scale,
-                             token_scales);
+    const int rc = mla_token(q_out, q_out_type, q_in, q_in_type, latent, t, (int64_t)e[2], row,
+                             freqs, freq_type, g, eps, H, R, Dn, cache, cache_type, scale_mode,
+                             tensor_scale, token_scales);
     if (rc != ORACLE_OK) return rc;
   }
   return status;
@@ -426,14 +496,15 @@ int oracle_mla_rope_rmsnorm_quant_planned(
  * and is replaced by its normalised, rotated value; q as above.
  */
 int oracle_mla_rope_rmsnorm_inplace(
-    void* q_out, int q_out_f32, const uint16_t* q_in, const uint32_t* row_offsets,
+    void* q_out, int q_out_type, const void* q_in, int q_in_type, const uint32_t* row_offsets,
     const uint32_t* cache_lengths, int64_t B, const uint32_t* page_table, int64_t pt_stride,
-    const float* freqs, int64_t max_seq_len, const uint16_t* gamma, float epsilon, int64_t H,
-    int64_t R, int64_t Dn, uint16_t* cache, int64_t num_layers, int64_t num_pages,
-    int64_t page_size, int64_t layer_idx) {
-  return oracle_mla_rope_rmsnorm_quant(q_out, q_out_f32, q_in, NULL, row_offsets,
+    const void* freqs, int freq_type, int64_t max_seq_len, const void* gamma, int gamma_type,
+    float epsilon, int64_t H, int64_t R, int64_t Dn, uint16_t* cache, int64_t num_layers,
+    int64_t num_pages, int64_t page_size, int64_t layer_idx) {
+  return oracle_mla_rope_rmsnorm_quant(q_out, q_out_type, q_in, q_in_type, NULL, row_offsets,
                                        cache_lengths, B, page_table, pt_stride, freqs,
-                                       max_seq_len, gamma, epsilon, H, R, Dn, cache,
+                                       freq_type, max_seq_len, gamma, gamma_type, epsilon, H,
+                                       R, Dn, cache,
                                        ORACLE_CACHE_BF16, num_layers, num_pages, page_size,
                                        layer_idx, 0, 1.0f, NULL);
 }
@@ -445,9 +516,10 @@ int oracle_mla_rope_rmsnorm_inplace(
  * every head is first RMS-normalised over its first k_norm_cols columns (the
  * optional per-head K norm), still unrounded, then rotated, then rounded once.
  *
- *   q_out, q_in   bf16 bits [T][Hq][D]
- *   k_cache       bf16 bits [L][P][S][Hkv][D]
- *   freqs         f32 [max_seq_len][D]
+ *   q_out, q_in   [T][Hq][D] of q_type ([QK] Parameters: dtype; bf16 or
+ *                 fp16 bits, or fp32)
+ *   k_cache       bf16 bits [L][P][S][Hkv][D], or fp8 codes (k_type)
+ *   freqs         [max_seq_len][D] of freq_type ([QK] Parameters: freq_dtype)
  *   position_ids  u32 [T] or NULL (then position = cache length + index)
  *   k_gamma       bf16 bits [k_norm_cols] or NULL
  */
@@ -486,11 +558,11 @@ static void store_k_row(void* k_cache, int k_type, int scale_mode, int64_t elem,
 }
 
 int oracle_qk_rope_paged_ragged(
-    uint16_t* q_out, const uint16_t* q_in, int64_t Hq, int64_t D,
+    void* q_out, const void* q_in, int q_type, int64_t Hq, int64_t D,
     const uint32_t* row_offsets, const uint32_t* cache_lengths, int64_t B,
     const uint32_t* page_table, int64_t pt_stride, void* k_cache, int k_type,
     int scale_mode, float* k_scales, int64_t num_layers, int64_t num_pages,
-    int64_t page_size, int64_t Hkv, int64_t layer_idx, const float* freqs,
+    int64_t page_size, int64_t Hkv, int64_t layer_idx, const void* freqs, int freq_type,
     int64_t max_seq_len, const uint32_t* position_ids, const int64_t* mrope_section,
     int interleaved, const uint16_t* k_gamma, int64_t k_norm_cols, float epsilon) {
   if (D <= 0 || D % 2 || D > 1024 || layer_idx < 0 || layer_idx >= num_layers ||
@@ -501,6 +573,7 @@ int oracle_qk_rope_paged_ragged(
                         mrope_section[0] + mrope_section[1] + mrope_section[2] != D / 2))
     return ORACLE_BAD_ARG;
   double a[1024], r[1024], g[1024];
+  float frow[1024];
   float mixed[1024];  /* multimodal: per-pair cos/sin gathered from three rows */
   int64_t T = row_offsets[B];
   if (k_gamma)
@@ -518,7 +591,7 @@ int oracle_qk_rope_paged_ragged(
                                    page_size, b, slot);
       if (page < 0) { status = ORACLE_BAD_PAGE; continue; }
       const int64_t off = slot % page_size;
-      const float* fr = freqs + pos * D;
+      const float* fr = freqs_row_at(freqs, freq_type, pos, D, frow);
       if (mrope_section) {
         /* [QK] Parameters, mrope_section: pair i of section k (temporal,
          * height, width) is rotated by the angle of position row k. */
@@ -528,19 +601,18 @@ int oracle_qk_rope_paged_ragged(
                             : i < mrope_section[0] + mrope_section[1] ? 1 : 2;
           const int64_t pk = (int64_t)position_ids[k * T + t];
           if (pk >= max_seq_len) { bad = 1; break; }
-          mixed[2 * i] = freqs[pk * D + 2 * i];
-          mixed[2 * i + 1] = freqs[pk * D + 2 * i + 1];
+          mixed[2 * i] = (float)elem(freqs, pk * D + 2 * i, freq_type);
+          mixed[2 * i + 1] = (float)elem(freqs, pk * D + 2 * i + 1, freq_type);
         }
         if (bad) { status = ORACLE_BAD_POSITION; continue; }
         fr = mixed;
       }
 
       for (int64_t h = 0; h < Hq; ++h) {
-        const uint16_t* src = q_in + (t * Hq + h) * D;
-        uint16_t* dst = q_out + (t * Hq + h) * D;
-        for (int64_t i = 0; i < D; ++i) a[i] = oracle_bf16_decode(src[i]);
+        const int64_t base = (t * Hq + h) * D;
+        for (int64_t i = 0; i < D; ++i) a[i] = elem(q_in, base + i, q_type);
         oracle_rope_row(a, r, D, fr, interleaved);
-        for (int64_t i = 0; i < D; ++i) dst[i] = oracle_bf16_encode(r[i]);
+        for (int64_t i = 0; i < D; ++i) put_elem(q_out, base + i, q_type, r[i]);
       }
       for (int64_t h = 0; h < Hkv; ++h) {
         const int64_t head = ((layer_idx * num_pages + page) * page_size + off) * Hkv + h;
@@ -630,8 +702,9 @@ int oracle_mla_gather_latent_paged(
  * then multiplies by (gamma + weight_offset) and rounds again.
  * per_head_norm = 1: one statistic per head; 0: one per token over all heads.
  *
- *   k_cache   bf16 bits [L][P][S][Hkv][D]
- *   gamma     bf16 bits [gamma_len]
+ *   k_cache   bf16 bits [L][P][S][Hkv][D], or fp8 codes (k_type)
+ *   gamma     [gamma_len] of gamma_type ([NORM]: the dtype of gamma and
+ *             weight_offset; bf16 or fp16 bits, or fp32)
  */
 /* The K-cache RMSNorm of one token whose rows sit at (page, off) of layer
  * layer_idx: every head's first gamma_len columns normalised with g (gamma
@@ -685,7 +758,7 @@ int oracle_rms_norm_kv_cache_paged(
     void* k_cache, int k_type, int scale_mode, float* k_scales, int64_t num_layers,
     int64_t num_pages, int64_t page_size, int64_t Hkv, int64_t D, int64_t layer_idx,
     const uint32_t* row_offsets, const uint32_t* cache_lengths, int64_t B,
-    const uint32_t* page_table, int64_t pt_stride, const uint16_t* gamma,
+    const uint32_t* page_table, int64_t pt_stride, const void* gamma, int gamma_type,
     int64_t gamma_len, float epsilon, float weight_offset, int64_t total_seq_len,
     int multiply_before_cast, int per_head_norm) {
   if (gamma_len <= 0 || gamma_len > D || D > 1024 || layer_idx < 0 ||
@@ -693,7 +766,7 @@ int oracle_rms_norm_kv_cache_paged(
     return ORACLE_BAD_ARG;
   double g[1024];
   if (k_type == ORACLE_CACHE_FP8 && !multiply_before_cast) return ORACLE_BAD_ARG;
-  kv_norm_gamma(gamma, gamma_len, weight_offset, g);
+  kv_norm_gamma(gamma, gamma_type, gamma_len, weight_offset, g);
   const double eps = (double)epsilon;
   int status = ORACLE_OK;
 
@@ -723,14 +796,14 @@ int oracle_rms_norm_kv_cache_paged(
 int oracle_rms_norm_kv_cache_planned(
     void* k_cache, int k_type, int scale_mode, float* k_scales, int64_t num_layers,
     int64_t num_pages, int64_t page_size, int64_t Hkv, int64_t D, int64_t layer_idx,
-    const uint32_t* plan, const uint16_t* gamma, int64_t gamma_len, float epsilon,
+    const uint32_t* plan, const void* gamma, int gamma_type, int64_t gamma_len, float epsilon,
     float weight_offset, int64_t total_seq_len, int multiply_before_cast, int per_head_norm) {
   if (gamma_len <= 0 || gamma_len > D || D > 1024 || layer_idx < 0 ||
       layer_idx >= num_layers || page_size <= 0 || total_seq_len < 0)
     return ORACLE_BAD_ARG;
   double g[1024];
   if (k_type == ORACLE_CACHE_FP8 && !multiply_before_cast) return ORACLE_BAD_ARG;
-  kv_norm_gamma(gamma, gamma_len, weight_offset, g);
+  kv_norm_gamma(gamma, gamma_type, gamma_len, weight_offset, g);
   const double eps = (double)epsilon;
   int status = ORACLE_OK;
   for (int64_t t = 0; t < total_seq_len; ++t) {

@@ -114,6 +114,19 @@ def round_f32(v: Decimal):
     return code | (0x80000000 if v.is_signed() else 0), kind
 
 
+def f16_value(p: int) -> Decimal:
+    return Decimal(float(np.array([int(p) & 0xFFFF], np.uint16).view(np.float16)[0]))
+
+
+def round_f16(v: Decimal):
+    """binary16 (11 significant bits) by exact comparison with the patterns
+    around numpy's rounding of the value (finite range only)."""
+    m = abs(v)
+    t = int(np.array([float(m)]).astype(np.float16).view(np.uint16)[0])
+    code, kind = _pick(m, [(f16_value(p), p) for p in range(t - 1, t + 2) if 0 <= p <= 0x7BFF])
+    return code | (0x8000 if v.is_signed() else 0), kind
+
+
 def round_fp8(v: Decimal):
     m = min(abs(v), Decimal(448))
     i = bisect.bisect_left(FP8_MAGS, m)
@@ -268,6 +281,54 @@ def pin_mla_exact(orc):
                                  None if ts is None else ts[L, page, off, 0], (case.name, t))
     tq.done()
     tq32.done(min_ties=50)
+    tc.done()
+    ts_t.done()
+
+
+def pin_mla_types_exact(orc):
+    """The fused MLA step over the element types the pages parameterise (q
+    input bf16 / fp16, freqs_cis fp32 / bf16 / fp16, gamma bf16 / fp16 /
+    fp32): fp16 and fp32 q outputs and every cache row equal the exact value
+    of the widened inputs rounded once."""
+    tq = Tally("mla q fp16 (element types)")
+    tq32 = Tally("mla q fp32 (element types)")
+    tc = Tally("mla cache (element types)")
+    ts_t = Tally("mla token scale (element types)")
+    with localcontext() as ctx:
+        ctx.prec = PREC
+        for case in op.dtype_mla_cases():
+            q16, cache, ts = op.run_mla(orc, case, np.float16)
+            q32, _, _ = op.run_mla(orc, case, np.float32)
+            S = case.meta["page_size"]
+            owners = op.slot_owners(case.row_offsets, case.cache_lengths, case.page_table, S)
+            H, R = case.q.shape[1:]
+            Dn = case.Dn
+            g = [dec(v) for v in op.elem_to_f64(case.gamma)]
+            eps = dec(np.float32(case.epsilon))
+            L = case.layer_idx
+            for (page, off), (t, slot) in owners.items():
+                row_f = op.elem_to_f64(case.freqs[slot])
+                cs, sn = [dec(v) for v in row_f[0::2]], [dec(v) for v in row_f[1::2]]
+                for h in range(H):
+                    x = [dec(v) for v in op.elem_to_f64(case.q[t, h])]
+                    y = rope_exact(x, cs, sn, False)
+                    for i in range(R):
+                        tq.check(int(q16[t, h, i:i + 1].view(np.uint16)[0]), round_f16(y[i]),
+                                 (case.name, t, h, i))
+                        tq32.check(int(q32[t, h, i:i + 1].view(np.uint32)[0]), round_f32(y[i]),
+                                   (case.name, t, h, i))
+                x = [dec(v) for v in op.bf16_to_f64(case.latent[t])]
+                r = inv_rms_exact(x[:Dn], Dn, eps)
+                y = [x[k] * g[k] * r for k in range(Dn)] + rope_exact(x[Dn:], cs, sn, False)
+                row = cache[L, page, off, 0]
+                if case.cache.dtype == np.uint16:
+                    for k in range(Dn + R):
+                        tc.check(row[k], round_bf16(y[k]), (case.name, t, k))
+                else:
+                    quantise_row(y, case.scale_mode, case.tensor_scale, tc, ts_t, row,
+                                 None if ts is None else ts[L, page, off, 0], (case.name, t))
+    tq.done()
+    tq32.done()
     tc.done()
     ts_t.done()
 
@@ -453,4 +514,5 @@ def pin_gather_exact(orc):
     t.done()
 
 
-ALL_EXACT_PINS = [pin_mla_exact, pin_qk_exact, pin_rms_norm_kv_exact, pin_gather_exact]
+ALL_EXACT_PINS = [pin_mla_exact, pin_qk_exact, pin_rms_norm_kv_exact, pin_gather_exact,
+                  pin_mla_types_exact]

@@ -61,6 +61,37 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
         return b.view(np.float32).astype(np.float64)
 
 
+def f16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """binary16 bit patterns decoded by numpy's float16 (a library routine)."""
+    return np.asarray(bits, np.uint16).view(np.float16).astype(np.float64)
+
+
+def elem_to_f64(a: np.ndarray) -> np.ndarray:
+    """An element-typed array as float64: uint16 holds bf16 bits, float16 and
+    float32 are numpy's own."""
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return bf16_to_f64(a)
+    return a.astype(np.float64)
+
+
+def ulp_f16(v: np.ndarray) -> np.ndarray:
+    """Spacing of binary16 values at |v| (11 significant bits, quantum >= 2^-24)."""
+    _, e = np.frexp(np.maximum(np.abs(v), 2.0 ** -14))
+    return np.ldexp(1.0, e - 1 - 10)
+
+
+def ulp_f32(v: np.ndarray) -> np.ndarray:
+    _, e = np.frexp(np.maximum(np.abs(v), 2.0 ** -126))
+    return np.ldexp(1.0, e - 1 - 23)
+
+
+def ulp_of(a: np.ndarray):
+    """The spacing function of an element-typed array's type."""
+    return {np.dtype(np.uint16): ulp_bf16, np.dtype(np.float16): ulp_f16,
+            np.dtype(np.float32): ulp_f32}[np.asarray(a).dtype]
+
+
 def fp8_to_f64(codes: np.ndarray) -> np.ndarray:
     return fp8_values_torch()[np.asarray(codes, np.uint8)]
 
@@ -259,6 +290,60 @@ def pin_bf16_encode_bruteforce(orc):
                              f"v={v[i]!r} got={got[i]:#06x} ref={ref[i]:#06x}")
 
 
+def pin_f16_decode(orc):
+    """Every binary16 pattern decodes as numpy's float16 does (NaN patterns
+    to NaN), signed zeros included."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = f16_to_f64(bits)
+    got = np.array([orc.f16_decode(int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan), "f16 NaN patterns"
+    assert np.array_equal(got[~nan], ref[~nan]), "f16 decode values"
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan])), "f16 decode signs"
+
+
+def pin_f16_landmarks(orc):
+    for row in read_golden("f16_landmarks.txt"):
+        if row[0] == "decode":
+            code, val = int(row[1], 16), float(row[2])
+            d = orc.f16_decode(code)
+            assert d == val and math.copysign(1, d) == math.copysign(1, val), row
+        else:
+            val, code = float(row[1]), int(row[2], 16)
+            assert orc.f16_encode(val) == code, (row, hex(orc.f16_encode(val)))
+
+
+def pin_f16_encode_numpy(orc):
+    """For fp64 inputs over the whole range (subnormals, overflow to
+    infinity included) the oracle equals numpy's float64 -> float16 cast,
+    which rounds to nearest even in one step."""
+    rng = np.random.Generator(np.random.PCG64(11))
+    v = rng.standard_normal(40000) * np.exp(rng.uniform(-22, 13, 40000))
+    with np.errstate(over="ignore"):
+        ref = v.astype(np.float16).view(np.uint16)
+    got = orc.f16_encode_array(v)
+    bad = got != ref
+    assert not bad.any(), f"f16 vs numpy: {int(bad.sum())} differ, first v={v[bad][0]!r}"
+
+
+def pin_f16_encode_bruteforce(orc):
+    """At every midpoint between adjacent finite binary16 values (and one
+    fp64 step either side of it) the oracle returns the nearest pattern, ties
+    to the even pattern, by direct comparison with both neighbours."""
+    lo_bits = np.arange(0, 0x7BFF, dtype=np.uint16)          # finite, next one finite
+    lo, hi = f16_to_f64(lo_bits), f16_to_f64(lo_bits + np.uint16(1))
+    mid = (lo + hi) / 2.0
+    for v, want in ((mid, np.where(lo_bits % 2 == 0, lo_bits, lo_bits + 1)),
+                    (np.nextafter(mid, 0), lo_bits), (np.nextafter(mid, np.inf), lo_bits + 1)):
+        got = orc.f16_encode_array(v)
+        assert np.array_equal(got, want.astype(np.uint16)), "f16 positive midpoints"
+        got_n = orc.f16_encode_array(-v)
+        assert np.array_equal(got_n, (want | 0x8000).astype(np.uint16)), "f16 negative midpoints"
+    # past the largest finite value: below 65520 stays 65504, from 65520 on infinity
+    assert orc.f16_encode(np.nextafter(65520.0, 0)) == 0x7BFF
+    assert orc.f16_encode(65520.0) == 0x7C00 and orc.f16_encode(-1e300) == 0xFC00
+
+
 # -- RoPE row pins -------------------------------------------------------------------
 
 
@@ -450,21 +535,21 @@ def mla_reference(case):
     pos = np.empty(case.T, np.int64)
     for (page, off), (t, slot) in owners.items():
         pos[t] = slot
-    fr = case.freqs[pos].astype(np.float64)
+    fr = elem_to_f64(case.freqs[pos])
     cs, sn = fr[:, 0::2], fr[:, 1::2]
-    q_ref = _complex_rope(bf16_to_f64(case.q), cs[:, None, :], sn[:, None, :], False)
+    q_ref = _complex_rope(elem_to_f64(case.q), cs[:, None, :], sn[:, None, :], False)
     x = bf16_to_f64(case.latent)
     Dn = case.Dn
     y_ref = np.empty_like(x)
     y_ref[:, :Dn] = torch.nn.functional.rms_norm(
         torch.from_numpy(x[:, :Dn].copy()), (Dn,),
-        weight=torch.from_numpy(bf16_to_f64(case.gamma)), eps=case.epsilon).numpy()
+        weight=torch.from_numpy(elem_to_f64(case.gamma)), eps=case.epsilon).numpy()
     y_ref[:, Dn:] = _complex_rope(x[:, Dn:], cs, sn, False)
     return q_ref, y_ref, owners
 
 
-def run_mla(orc, case):
-    q_out = np.zeros_like(case.q)
+def run_mla(orc, case, q_out_dtype=None):
+    q_out = np.zeros(case.q.shape, case.q.dtype if q_out_dtype is None else q_out_dtype)
     cache = case.cache.copy()
     ts = None if case.token_scales is None else case.token_scales.copy()
     orc.mla_rope_rmsnorm_quant(q_out, case.q, case.latent, case.row_offsets,
@@ -476,7 +561,7 @@ def run_mla(orc, case):
 
 def check_mla_against_reference(case, q_out, cache, ts):
     q_ref, y_ref, owners = mla_reference(case)
-    assert_correctly_rounded(bf16_to_f64(q_out), q_ref, ulp_bf16, "q_rope_output")
+    assert_correctly_rounded(elem_to_f64(q_out), q_ref, ulp_of(q_out), "q_rope_output")
     L = case.layer_idx
     expect = case.cache.copy()
     written = np.zeros(case.cache.shape[:3], bool)
@@ -532,6 +617,36 @@ def pin_mla_composite(orc):
     for case in small_mla_cases():
         q_out, cache, ts = run_mla(orc, case)
         check_mla_against_reference(case, q_out, cache, ts)
+
+
+def dtype_mla_cases():
+    """Small MLA cases over the element types the pages parameterise: q_rope
+    (dtype) bf16 / fp16, freqs_cis (freq_dtype) fp32 / bf16 / fp16, gamma
+    (gamma_dtype) bf16 / fp16 / fp32, with an fp8 (tensor and token scale)
+    or bf16 cache; each with its q output types."""
+    specs = [("f16", "f32", "bf16", "per_tensor", "fp8"), ("bf16", "bf16", "f32", "per_token", "fp8"),
+             ("f16", "f16", "f16", "none", "bf16"), ("bf16", "f16", "bf16", "per_tensor", "fp8"),
+             ("f16", "bf16", "f32", "per_token", "fp8")]
+    for k, (qd, fd, gd, mode, cache) in enumerate(specs):
+        yield workloads.build_mla(f"mla_types_{qd}_{fd}_{gd}", 2100 + k, [5, 0, 9, 3], [2, 7, 0, 30],
+                                  H=6, page_size=8, max_seq_len=64, spare_pages=3,
+                                  outlier_p=0.02, scale_mode=mode, tensor_scale=0.05,
+                                  cache_dtype=cache, q_dtype=qd, freq_dtype=fd, gamma_dtype=gd)
+
+
+def pin_mla_types(orc):
+    """Every q input / q output / freqs / gamma element type: q_rope_output is
+    the correctly rounded value of the exact rotation in its own type (bf16,
+    fp16 or fp32), the cache rows as in the bf16 case (the exact values of
+    the widened inputs), and the cache rows do not depend on q's output type."""
+    for case in dtype_mla_cases():
+        outs = (np.uint16, np.float16, np.float32)
+        caches = []
+        for od in outs:
+            q_out, cache, ts = run_mla(orc, case, od)
+            check_mla_against_reference(case, q_out, cache, ts)
+            caches.append(cache)
+        assert all(np.array_equal(c, caches[0]) for c in caches), case.name
 
 
 def pin_mla_f32_q(orc):
@@ -790,9 +905,9 @@ def qk_reference(case, k_norm: bool):
     for (page, off), (t, slot) in owners.items():
         slot_of[t] = slot
     pos = case.position_ids.astype(np.int64) if case.position_ids is not None else slot_of
-    fr = case.freqs[pos].astype(np.float64)
+    fr = elem_to_f64(case.freqs[pos])
     cs, sn = fr[:, 0::2], fr[:, 1::2]
-    q_ref = _complex_rope(bf16_to_f64(case.q), cs[:, None, :], sn[:, None, :],
+    q_ref = _complex_rope(elem_to_f64(case.q), cs[:, None, :], sn[:, None, :],
                           case.interleaved)
     L = case.layer_idx
     k_ref = {}
@@ -807,6 +922,63 @@ def qk_reference(case, k_norm: bool):
         k_ref[(page, off)] = _complex_rope(x, cs[t][None, :], sn[t][None, :],
                                            case.interleaved)
     return q_ref, k_ref
+
+
+def dtype_qk_cases():
+    """Q/K cases with fp16 Q (the pages' dtype of q_proj and the output) and
+    bf16 / fp16 / fp32 freqs_cis (freq_dtype), both rope styles."""
+    yield workloads.build_qk("qk_types_f16_bf16", 3101, [5, 0, 17, 1], [0, 4, 11, 31],
+                             Hq=4, Hkv=2, D=128, page_size=16, max_seq_len=4096,
+                             theta=500000.0, interleaved=True, with_position_ids=True,
+                             norm_cols=128, spare_pages=3, q_dtype="f16", freq_dtype="bf16")
+    yield workloads.build_qk("qk_types_f16_f16", 3102, [3, 9], [14, 0], Hq=3, Hkv=1, D=64,
+                             page_size=4, max_seq_len=64, theta=10000.0,
+                             interleaved=False, with_position_ids=False,
+                             norm_cols=40, spare_pages=2, q_dtype="f16", freq_dtype="f16")
+    yield workloads.build_qk("qk_types_bf16_f16", 3103, [6, 2], [1, 7], Hq=2, Hkv=2, D=96,
+                             page_size=8, max_seq_len=64, theta=10000.0,
+                             interleaved=False, with_position_ids=True,
+                             norm_cols=96, spare_pages=1, q_dtype="bf16", freq_dtype="f16")
+
+
+def pin_qk_types(orc):
+    for case in dtype_qk_cases():
+        q_out = np.zeros_like(case.q)
+        k = case.k_cache.copy()
+        orc.qk_rope_paged_ragged(q_out, case.q, case.row_offsets, case.cache_lengths,
+                                 case.page_table, k, case.layer_idx, case.freqs,
+                                 case.position_ids, case.interleaved, case.gamma, case.epsilon)
+        q_ref, k_ref = qk_reference(case, True)
+        assert_correctly_rounded(elem_to_f64(q_out), q_ref, ulp_of(q_out), f"{case.name} q")
+        L = case.layer_idx
+        for (page, off), ref in k_ref.items():
+            assert_correctly_rounded(bf16_to_f64(k[L, page, off]), ref, ulp_bf16,
+                                     f"{case.name} k {page},{off}")
+
+
+def pin_rms_norm_kv_gamma_types(orc):
+    """The K-cache norm with gamma (and weight_offset) in fp16 or fp32 ([NORM]:
+    gamma and weight_offset share a dtype): torch rms_norm (fp64) with the
+    widened gamma + offset, each written value correctly rounded."""
+    case = list(small_qk_cases())[0]
+    S = case.meta["page_size"]
+    owners = slot_owners(case.row_offsets, case.cache_lengths, case.page_table, S)
+    L = case.layer_idx
+    rng = np.random.Generator(np.random.PCG64(77))
+    g32 = rng.uniform(0.5, 1.5, 100).astype(np.float32)
+    for gamma in (g32.astype(np.float16), g32):
+        k = case.k_cache.copy()
+        orc.rms_norm_kv_cache_paged(k, L, case.row_offsets, case.cache_lengths, case.page_table,
+                                    gamma, case.epsilon, 0.25, case.T, True)
+        g = gamma.astype(np.float64) + 0.25
+        for (page, off), (t, slot) in owners.items():
+            x = bf16_to_f64(case.k_cache[L, page, off])[:, :100]
+            ref = torch.nn.functional.rms_norm(torch.from_numpy(x.copy()), (100,),
+                                               weight=torch.from_numpy(g),
+                                               eps=case.epsilon).numpy()
+            assert_correctly_rounded(bf16_to_f64(k[L, page, off][:, :100]), ref, ulp_bf16,
+                                     f"kvnorm gamma {gamma.dtype}")
+            assert np.array_equal(k[L, page, off][:, 100:], case.k_cache[L, page, off][:, 100:])
 
 
 def small_qk_cases():
@@ -846,7 +1018,7 @@ def pin_qk_composite(orc):
                                      case.position_ids, case.interleaved,
                                      case.gamma if use_norm else None, case.epsilon)
             q_ref, k_ref = qk_reference(case, use_norm)
-            assert_correctly_rounded(bf16_to_f64(q_out), q_ref, ulp_bf16, "qk q")
+            assert_correctly_rounded(elem_to_f64(q_out), q_ref, ulp_of(q_out), "qk q")
             expect = case.k_cache.copy()
             L = case.layer_idx
             for (page, off), ref in k_ref.items():
@@ -1255,5 +1427,6 @@ ALL_PINS = [
     pin_mla_position0, pin_mla_zero_row_per_token, pin_qk_composite,
     pin_rms_norm_kv, pin_gather, pin_qk_fp8, pin_rms_norm_kv_fp8, pin_mrope,
     pin_mla_f32_q, pin_rms_norm_kv_token, pin_mla_inplace, pin_token_plan, pin_mla_planned,
-    pin_rms_norm_kv_planned,
+    pin_rms_norm_kv_planned, pin_f16_decode, pin_f16_landmarks, pin_f16_encode_numpy,
+    pin_f16_encode_bruteforce, pin_mla_types, pin_qk_types, pin_rms_norm_kv_gamma_types,
 ]

@@ -73,8 +73,8 @@ MUTANTS = [
      "for (int64_t i = 0; i < k_norm_cols; ++i) a[i] = a[i] * inv;"),
     ("qk_norm_all_columns", "double inv = oracle_inv_rms(a, k_norm_cols, eps);",
      "double inv = oracle_inv_rms(a, D, eps);"),
-    ("kvnorm_no_offset", "g[k] = oracle_bf16_decode(gamma[k]) + (double)weight_offset;",
-     "g[k] = oracle_bf16_decode(gamma[k]);"),
+    ("kvnorm_no_offset", "g[k] = elem(gamma, k, gamma_type) + (double)weight_offset;",
+     "g[k] = elem(gamma, k, gamma_type);"),
     ("kvnorm_cast_order", "if (multiply_before_cast) {", "if (!multiply_before_cast) {"),
     ("kvnorm_ignores_total", "if (t >= total_seq_len) break;", "(void)total_seq_len;"),
     ("gather_slot_shift", "const int64_t slot = row - (int64_t)kv_row_offsets[b];",
@@ -121,9 +121,29 @@ MUTANTS = [
      "for (int64_t t = 0; t + 1 < total_seq_len; ++t) {"),
     ("planned_kvnorm_next_slot", "layer_idx, (int64_t)e[0], (int64_t)e[1], g, gamma_len, eps,",
      "layer_idx, (int64_t)e[0], (int64_t)(e[1] ^ 1u), g, gamma_len, eps,"),
+    # the element types: binary16 codec, typed reads and writes, freqs and gamma types
+    ("f16_decode_subnormal", "else if (e == 0) mag = ldexp((double)m, -24);",
+     "else if (e == 0) mag = ldexp((double)m, -25);"),
+    ("f16_bias", "return (uint16_t)(sign | ((E + 15) << 10) | m);",
+     "return (uint16_t)(sign | ((E + 16) << 10) | m);"),
+    ("f16_precision", "int qexp = e - 11;            /* keep 11 significant bits */",
+     "int qexp = e - 10;"),
+    ("f16_ties_away", "double n = nearbyint(ldexp(a, -qexp));\n  double r = ldexp(n, qexp);\n  if (r > 65504.0)",
+     "double n = round(ldexp(a, -qexp));\n  double r = ldexp(n, qexp);\n  if (r > 65504.0)"),
+    ("elem_f16_read_as_bf16",
+     "return type == ORACLE_F16 ? oracle_f16_decode(bits) : oracle_bf16_decode(bits);",
+     "return oracle_bf16_decode(bits);"),
+    ("elem_f16_written_as_bf16",
+     "else if (type == ORACLE_F16) ((uint16_t*)base)[i] = oracle_f16_encode(v);",
+     "else if (type == ORACLE_F16) ((uint16_t*)base)[i] = oracle_bf16_encode(v);"),
+    ("freqs_type_ignored", "buf[i] = (float)elem(freqs, p * dim + i, type);",
+     "buf[i] = (float)elem(freqs, p * dim + i, ORACLE_BF16);"),
+    ("mla_gamma_type_ignored",
+     "g[k] = elem(gamma, k, gamma_type);\n  const double eps = (double)epsilon; /* the fp32",
+     "g[k] = elem(gamma, k, ORACLE_BF16);\n  const double eps = (double)epsilon; /* the fp32"),
     ("planned_offset_as_position",
-     "mla_token(q_out, q_out_f32, q_in, latent, t, (int64_t)e[2], row,",
-     "mla_token(q_out, q_out_f32, q_in, latent, t, (int64_t)e[1], row,"),
+     "mla_token(q_out, q_out_type, q_in, q_in_type, latent, t, (int64_t)e[2], row,",
+     "mla_token(q_out, q_out_type, q_in, q_in_type, latent, t, (int64_t)e[1], row,"),
 ]
 
 RUNNER = r"""

@@ -37,6 +37,10 @@ def test_exact_rounding_helpers(orc):
     assert E.round_f32(Decimal(1) + Decimal(2) ** -24) == (0x3F800000, E.TIE)
     assert E.round_f32(Decimal(-1) - Decimal(2) ** -23) == (0xBF800001, E.OK)
     assert E.fp8_value(0x80).is_signed() and E.fp8_value(0x7E) == 448
+    assert E.round_f16(Decimal(1) + Decimal(2) ** -11) == (0x3C00, E.TIE)
+    assert E.round_f16(Decimal(1) + Decimal(3) * Decimal(2) ** -11) == (0x3C02, E.TIE)
+    assert E.round_f16(Decimal(-1) - Decimal(2) ** -10) == (0xBC01, E.OK)
+    assert E.round_f16(Decimal(2) ** -25) == (0x0000, E.TIE)      # halfway to 2^-24
     rng = np.random.default_rng(5)
     for v in rng.standard_normal(300) * 50:
         d = Decimal(float(v))

@@ -39,28 +39,43 @@ def bf16_bits(x: np.ndarray) -> np.ndarray:
     return t.view(torch.int16).numpy().view(np.uint16)
 
 
-def freqs_table(max_seq_len: int, dim: int, theta: float) -> np.ndarray:
-    """RoPE table [max_seq_len, dim] fp32: column 2i = cos, 2i+1 = sin of
-    position * theta^(-2i/dim), computed in float64 and rounded once."""
+def as_elem(x: np.ndarray, dtype: str) -> np.ndarray:
+    """float32 values in an element type: "bf16" (bits as uint16, torch's
+    round-to-nearest-even cast), "f16" (numpy float16, round-to-nearest-even)
+    or "f32" (unchanged)."""
+    x = np.ascontiguousarray(x, np.float32)
+    if dtype == "bf16":
+        return bf16_bits(x)
+    if dtype == "f16":
+        return x.astype(np.float16)
+    if dtype == "f32":
+        return x
+    raise ValueError(dtype)
+
+
+def freqs_table(max_seq_len: int, dim: int, theta: float, dtype: str = "f32") -> np.ndarray:
+    """RoPE table [max_seq_len, dim]: column 2i = cos, 2i+1 = sin of
+    position * theta^(-2i/dim), computed in float64 and rounded once to fp32
+    (and from there to bf16 or fp16 for those dtypes)."""
     i = np.arange(dim // 2, dtype=np.float64)
     inv_freq = theta ** (-2.0 * i / dim)
     ang = np.arange(max_seq_len, dtype=np.float64)[:, None] * inv_freq[None, :]
     out = np.empty((max_seq_len, dim), np.float64)
     out[:, 0::2] = np.cos(ang)
     out[:, 1::2] = np.sin(ang)
-    return out.astype(np.float32)
+    return as_elem(out.astype(np.float32), dtype)
 
 
-def _normal_bf16(rng, shape, sigma=1.0, outlier_p=0.0, outlier_mult=50.0):
+def _normal_bf16(rng, shape, sigma=1.0, outlier_p=0.0, outlier_mult=50.0, dtype="bf16"):
     x = rng.standard_normal(size=shape, dtype=np.float32) * np.float32(sigma)
     if outlier_p > 0.0:
         hit = rng.random(size=shape) < outlier_p
         x = np.where(hit, x * np.float32(outlier_mult), x)
-    return bf16_bits(x)
+    return as_elem(x, dtype)
 
 
-def _uniform_bf16(rng, shape, lo, hi):
-    return bf16_bits(rng.uniform(lo, hi, size=shape).astype(np.float32))
+def _uniform_bf16(rng, shape, lo, hi, dtype="bf16"):
+    return as_elem(rng.uniform(lo, hi, size=shape).astype(np.float32), dtype)
 
 
 _SENTINEL_PERIOD = (16 << 20) + 7  # odd period: no two pages see the same bytes
@@ -104,10 +119,10 @@ class MlaCase:
     row_offsets: np.ndarray      # u32 [B+1]
     cache_lengths: np.ndarray    # u32 [B]
     page_table: np.ndarray       # u32 [B, stride]
-    q: np.ndarray                # bf16 bits [T, H, R]
+    q: np.ndarray                # bf16 bits [T, H, R] (or float16)
     latent: np.ndarray           # bf16 bits [T, Dn + R]
-    gamma: np.ndarray            # bf16 bits [Dn]
-    freqs: np.ndarray            # f32 [max_seq_len, R]
+    gamma: np.ndarray            # bf16 bits [Dn] (or float16, float32)
+    freqs: np.ndarray            # f32 [max_seq_len, R] (or bf16 bits, float16)
     epsilon: float
     cache: np.ndarray            # u8 [L, P, S, 1, Dn + R] (fp8) or u16 (bf16)
     layer_idx: int
@@ -145,17 +160,21 @@ def build_mla(name, seed, new_lens, prior_lens, H, R=64, Dn=512, *,
               page_size, max_seq_len, theta=10000.0, spare_pages=16,
               q_sigma=1.0, latent_sigma=1.0, outlier_p=0.0, eps=1e-6,
               scale_mode="per_tensor", tensor_scale=1.0, cache_dtype="fp8",
-              num_layers=2, layer_idx=1, rng=None):
-    """Generic MLA case; ``rng`` continues a preset's stream if given."""
+              num_layers=2, layer_idx=1, rng=None, q_dtype="bf16", freq_dtype="f32",
+              gamma_dtype="bf16"):
+    """Generic MLA case; ``rng`` continues a preset's stream if given.
+    q_dtype ("bf16" | "f16"), freq_dtype ("f32" | "bf16" | "f16") and
+    gamma_dtype ("bf16" | "f16" | "f32") pick the element types of q_rope,
+    freqs_cis and gamma (the same draws, rounded into that type)."""
     rng = make_rng(seed) if rng is None else rng
     offsets, clens, pt, P = ragged_batch(new_lens, prior_lens, page_size,
                                          spare_pages, rng)
     T = int(offsets[-1])
     W = Dn + R
-    q = _normal_bf16(rng, (T, H, R), q_sigma, outlier_p)
+    q = _normal_bf16(rng, (T, H, R), q_sigma, outlier_p, dtype=q_dtype)
     latent = _normal_bf16(rng, (T, W), latent_sigma, outlier_p)
-    gamma = _uniform_bf16(rng, (Dn,), 0.5, 1.5)
-    freqs = freqs_table(max_seq_len, R, theta)
+    gamma = _uniform_bf16(rng, (Dn,), 0.5, 1.5, dtype=gamma_dtype)
+    freqs = freqs_table(max_seq_len, R, theta, freq_dtype)
     if cache_dtype == "fp8":
         cache = _random_bytes(rng, num_layers * P * page_size * W).reshape(
             num_layers, P, page_size, 1, W)
@@ -277,16 +296,18 @@ def build_qk(name, seed, new_lens, prior_lens, Hq, Hkv, D, *, page_size,
              max_seq_len, theta, interleaved, with_position_ids,
              norm_cols=None, eps=1e-6, spare_pages=64, num_layers=2, layer_idx=1,
              rng=None, k_dtype="bf16", k_scale_mode="per_tensor", k_scale=0.05,
-             mrope_section=None):
+             mrope_section=None, q_dtype="bf16", freq_dtype="f32"):
     """Generic Q/K RoPE case; ``rng`` continues a preset's stream if given.
     k_dtype "fp8": the K pool holds E4M3FN codes of N(0,1) values divided by
     the scale -- one tensor scale, or per (slot, head) scales ~U(0.5, 1.5) x
-    k_scale (k_scale_mode "per_token")."""
+    k_scale (k_scale_mode "per_token").  q_dtype ("bf16" | "f16") and
+    freq_dtype ("f32" | "bf16" | "f16") pick the element types of Q and of
+    freqs_cis."""
     rng = make_rng(seed) if rng is None else rng
     offsets, clens, pt, P = ragged_batch(new_lens, prior_lens, page_size,
                                          spare_pages, rng)
     T = int(offsets[-1])
-    q = _normal_bf16(rng, (T, Hq, D))
+    q = _normal_bf16(rng, (T, Hq, D), dtype=q_dtype)
     # The whole pool holds N(0,1) bf16 values, so the new K rows (written by a
     # preceding projection) are normal draws wherever they sit, and every other
     # slot is a finite value whose bits must survive the call unchanged.
@@ -303,7 +324,7 @@ def build_qk(name, seed, new_lens, prior_lens, Hq, Hkv, D, *, page_size,
         else:
             k_scales = np.array([k_scale], np.float32)
             k_cache = fp8_codes(x / k_scales[0])
-    freqs = freqs_table(max_seq_len, D, theta)
+    freqs = freqs_table(max_seq_len, D, theta, freq_dtype)
     pos = None
     if mrope_section is not None:
         pos = rng.integers(0, max_seq_len - 1, size=(3, T), endpoint=True).astype(np.uint32)
