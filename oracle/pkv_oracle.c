@@ -4,7 +4,7 @@
  * TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only the test-suite, the smoke check
  * and the CPU-baseline leg of the benchmark load this library.  It shares no
  * source, header, table or helper with the HIP library; it includes nothing but
- * the C standard library.
+ * the C standard library and its own pkv_oracle.h.
  *
  * Style: plain scalar loops, every intermediate in IEEE binary64 (built with
  * -ffp-contract=off, no fast-math), and exactly one rounding into each output
@@ -14,8 +14,11 @@
  * rounded value of the plain definition, exact ties included.  Values that
  * pass through the square root and divisions of the norm carry a binary64
  * error well under 2^-43 relative, so they are correctly rounded except within
- * that distance of a rounding boundary.  (tests/exact_pins.py checks both
- * statements against 120-digit decimal arithmetic.)
+ * that distance of a rounding boundary.  The fused K norm of the Q/K RoPE
+ * applies r after rotating a pair whose members it both scales (the rotation
+ * is linear), so that a pair which cancels keeps the exactness above.
+ * (tests/exact_pins.py checks both statements against 120-digit decimal
+ * arithmetic.)
  *
  * Sources (Modular MAX / Mojo API reference pages):
  *   [MLA]   "mla_fused_rope_rmsnorm_quantization" -- summary, Parameters, Args
@@ -50,6 +53,8 @@
 #include <stddef.h>
 #include <stdint.h>
 #include <string.h>
+
+#include "pkv_oracle.h"
 
 /* Return codes: 0 = done; negative = a precondition on the data does not hold
  * (nothing is guaranteed about the outputs then). */
@@ -573,6 +578,7 @@ int oracle_qk_rope_paged_ragged(
                         mrope_section[0] + mrope_section[1] + mrope_section[2] != D / 2))
     return ORACLE_BAD_ARG;
   double a[1024], r[1024], g[1024];
+  int both[1024];     /* K norm: both members of the value's pair normalised */
   float frow[1024];
   float mixed[1024];  /* multimodal: per-pair cos/sin gathered from three rows */
   int64_t T = row_offsets[B];
@@ -621,10 +627,25 @@ int oracle_qk_rope_paged_ragged(
             : 1.0;
         load_k_row(k_cache, k_type, head * D, D, ks, a);
         if (k_gamma) {
-          double inv = oracle_inv_rms(a, k_norm_cols, eps);
-          for (int64_t i = 0; i < k_norm_cols; ++i) a[i] = a[i] * inv * g[i];
+          /* [QK] the K norm, then the rotation.  The rotation is linear, so
+           * a pair whose members are both normalised is rotated as x * gamma
+           * and scaled by inv after it: the same value, and an exact
+           * cancellation in the pair gives an exact zero, as the definition
+           * does (scaling each member by its own rounded product first would
+           * leave a binary64 residue there).  A pair with one normalised
+           * member takes inv on that member before the rotation. */
+          const double inv = oracle_inv_rms(a, k_norm_cols, eps);
+          for (int64_t i = 0; i < D; ++i) {
+            const int64_t partner = interleaved ? (i ^ 1) : (i + D / 2) % D;
+            both[i] = i < k_norm_cols && partner < k_norm_cols;
+            if (i < k_norm_cols) a[i] = both[i] ? a[i] * g[i] : a[i] * inv * g[i];
+          }
+          oracle_rope_row(a, r, D, fr, interleaved);
+          for (int64_t i = 0; i < D; ++i)
+            if (both[i]) r[i] *= inv;
+        } else {
+          oracle_rope_row(a, r, D, fr, interleaved);
         }
-        oracle_rope_row(a, r, D, fr, interleaved);
         store_k_row(k_cache, k_type, scale_mode, head * D, D, r,
                     k_type == ORACLE_CACHE_FP8 ? k_scales[0] : 1.0f,
                     scale_mode == ORACLE_SCALE_PER_TOKEN ? &k_scales[head] : NULL, 0, D);

@@ -109,17 +109,20 @@ def ulp_fp8(v: np.ndarray) -> np.ndarray:
 
 
 def assert_correctly_rounded(got: np.ndarray, ref: np.ndarray, ulp_fn, what: str,
-                             sat: float | None = None) -> None:
+                             sat: float | None = None, abs_tol=None) -> None:
     """|got - ref| <= ulp(ref)/2: got is a nearest representable value of ref.
-    With ``sat``, references beyond +-sat must come back as +-sat."""
+    With ``sat``, references beyond +-sat must come back as +-sat.  abs_tol
+    (same shape as ref): the reference's own binary64 error, added to the
+    bound (where a cancellation leaves the reference a residue near zero)."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
+    tol = np.zeros_like(ref) if abs_tol is None else np.broadcast_to(abs_tol, ref.shape)
     if sat is not None:
         over = np.abs(ref) > sat
         assert np.all(got[over] == np.sign(ref[over]) * sat), f"{what}: saturation"
-        got, ref = got[~over], ref[~over]
+        got, ref, tol = got[~over], ref[~over], tol[~over]
     err = np.abs(got - ref)
-    bound = 0.5 * ulp_fn(ref) * (1.0 + 1e-12)
+    bound = 0.5 * ulp_fn(ref) * (1.0 + 1e-12) + tol
     bad = err > bound
     if bad.any():
         i = int(np.flatnonzero(bad)[0])
@@ -897,6 +900,35 @@ def pin_mla_zero_row_per_token(orc):
     assert np.array_equal(row[:Dn] >> 7, (case.latent[0, :Dn] >> 15).astype(np.uint8))
 
 
+# The K reference's own error with the norm: torch's rms_norm (a square
+# root, a division and two products, each rounded in binary64) and the
+# complex product that rotates it leave an absolute error of a few 2^-53 of
+# the pair's magnitude; where the pair cancels, that is all the reference
+# holds.  2^-49 x the pair magnitude bounds it with margin.
+QK_REF_NORM_TOL = 2.0 ** -49
+
+
+def pair_magnitude_of(v: np.ndarray, interleaved: bool) -> np.ndarray:
+    """|(a, b)| of the rotation pair each element of the last axis is in."""
+    out = np.empty_like(v)
+    if interleaved:
+        m = np.hypot(v[..., 0::2], v[..., 1::2])
+        out[..., 0::2], out[..., 1::2] = m, m
+    else:
+        h = v.shape[-1] // 2
+        m = np.hypot(v[..., :h], v[..., h:])
+        out[..., :h], out[..., h:] = m, m
+    return out
+
+
+def qk_k_tolerance(ref: np.ndarray, case, k_norm: bool):
+    """abs_tol for a K reference row (None without the norm: the rotation of
+    bf16 values by fp32 / 16-bit cos and sin is exact in binary64)."""
+    if not k_norm:
+        return None
+    return QK_REF_NORM_TOL * pair_magnitude_of(ref, case.interleaved)
+
+
 def qk_reference(case, k_norm: bool):
     S = case.meta["page_size"]
     owners = slot_owners(case.row_offsets, case.cache_lengths, case.page_table, S)
@@ -953,7 +985,51 @@ def pin_qk_types(orc):
         L = case.layer_idx
         for (page, off), ref in k_ref.items():
             assert_correctly_rounded(bf16_to_f64(k[L, page, off]), ref, ulp_bf16,
-                                     f"{case.name} k {page},{off}")
+                                     f"{case.name} k {page},{off}",
+                                     abs_tol=qk_k_tolerance(ref, case, True))
+
+
+def pin_qk_norm_exact_cancellation(orc):
+    """The fused K norm where a rotation pair cancels exactly ([QK]: the K
+    norm, then RoPE): with cos = sin in every row and x_a g_a = x_b g_b for
+    every pair (x_b / x_a = 1.2, not a power of two), the first output of each
+    pair is exactly zero -- r is common to both members, so the definition's
+    value is r (x_a g_a c - x_b g_b s) = 0 -- and every other value is
+    correctly rounded.  Both rope styles; bf16 freqs_cis."""
+    D, h = 64, 32
+    for inter in (True, False):
+        case = workloads.build_qk(f"qk_cancel_{int(inter)}", 3201, [4, 3], [2, 9], Hq=1, Hkv=2,
+                                  D=D, page_size=4, max_seq_len=32, theta=10000.0,
+                                  interleaved=inter, with_position_ids=False, norm_cols=D,
+                                  spare_pages=1, freq_dtype="bf16")
+        ia = np.arange(0, D, 2) if inter else np.arange(h)
+        ib = ia + 1 if inter else ia + h
+        case.freqs[:] = workloads.bf16_bits(np.float32(0.70703125))   # cos = sin
+        case.gamma[ia] = workloads.bf16_bits(np.float32(1.5))
+        case.gamma[ib] = workloads.bf16_bits(np.float32(1.25))
+        rng = np.random.Generator(np.random.PCG64(3202))
+        L = case.layer_idx
+        owners = slot_owners(case.row_offsets, case.cache_lengths, case.page_table,
+                             case.meta["page_size"])
+        for (page, off) in owners:
+            for head in range(2):
+                kk = (rng.integers(8, 16, size=h) * 2.0 ** rng.integers(-5, 0, size=h) *
+                      rng.choice([-1.0, 1.0], size=h))
+                x = np.zeros(D, np.float32)
+                x[ia], x[ib] = 1.25 * kk, 1.5 * kk                  # both exact in bf16
+                case.k_cache[L, page, off, head] = workloads.bf16_bits(x)
+        q_out = np.zeros_like(case.q)
+        k = case.k_cache.copy()
+        orc.qk_rope_paged_ragged(q_out, case.q, case.row_offsets, case.cache_lengths,
+                                 case.page_table, k, L, case.freqs, None, inter, case.gamma,
+                                 case.epsilon)
+        _, k_ref = qk_reference(case, True)
+        for (page, off), ref in k_ref.items():
+            row = k[L, page, off]
+            assert np.all(row[:, ia] & 0x7FFF == 0), f"cancelling pair not zero ({inter})"
+            assert np.all(row[:, ib] & 0x7FFF != 0)
+            assert_correctly_rounded(bf16_to_f64(row), ref, ulp_bf16, "cancel k",
+                                     abs_tol=qk_k_tolerance(ref, case, True))
 
 
 def pin_rms_norm_kv_gamma_types(orc):
@@ -1023,7 +1099,8 @@ def pin_qk_composite(orc):
             L = case.layer_idx
             for (page, off), ref in k_ref.items():
                 assert_correctly_rounded(bf16_to_f64(k[L, page, off]), ref, ulp_bf16,
-                                         f"qk k {page},{off}")
+                                         f"qk k {page},{off}",
+                                         abs_tol=qk_k_tolerance(ref, case, use_norm))
                 expect[L, page, off] = k[L, page, off]
             assert np.array_equal(k, expect), "K elements outside the new rows changed"
 
@@ -1429,4 +1506,5 @@ ALL_PINS = [
     pin_mla_f32_q, pin_rms_norm_kv_token, pin_mla_inplace, pin_token_plan, pin_mla_planned,
     pin_rms_norm_kv_planned, pin_f16_decode, pin_f16_landmarks, pin_f16_encode_numpy,
     pin_f16_encode_bruteforce, pin_mla_types, pin_qk_types, pin_rms_norm_kv_gamma_types,
+    pin_qk_norm_exact_cancellation,
 ]

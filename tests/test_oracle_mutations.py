@@ -69,10 +69,23 @@ MUTANTS = [
     ("qk_ignores_position_ids",
      "const int64_t pos = position_ids ? (int64_t)position_ids[t] : slot;",
      "const int64_t pos = slot;"),
-    ("qk_norm_skips_gamma", "for (int64_t i = 0; i < k_norm_cols; ++i) a[i] = a[i] * inv * g[i];",
-     "for (int64_t i = 0; i < k_norm_cols; ++i) a[i] = a[i] * inv;"),
-    ("qk_norm_all_columns", "double inv = oracle_inv_rms(a, k_norm_cols, eps);",
-     "double inv = oracle_inv_rms(a, D, eps);"),
+    ("qk_norm_skips_gamma",
+     "if (i < k_norm_cols) a[i] = both[i] ? a[i] * g[i] : a[i] * inv * g[i];",
+     "if (i < k_norm_cols) a[i] = both[i] ? a[i] : a[i] * inv;"),
+    ("qk_norm_all_columns", "const double inv = oracle_inv_rms(a, k_norm_cols, eps);",
+     "const double inv = oracle_inv_rms(a, D, eps);"),
+    ("qk_norm_inv_not_applied_after", "if (both[i]) r[i] *= inv;", "if (both[i]) r[i] *= 1.0;"),
+    ("qk_norm_mixed_pair_unnormalised",
+     "if (i < k_norm_cols) a[i] = both[i] ? a[i] * g[i] : a[i] * inv * g[i];",
+     "if (i < k_norm_cols) a[i] = a[i] * g[i];"),
+    # the per-member order before the rotation: a binary64 residue where a
+    # pair cancels exactly (only the exact-cancellation pin sees it)
+    ("qk_norm_inv_before_rotation",
+     "if (i < k_norm_cols) a[i] = both[i] ? a[i] * g[i] : a[i] * inv * g[i];\n"
+     "          }\n          oracle_rope_row(a, r, D, fr, interleaved);\n"
+     "          for (int64_t i = 0; i < D; ++i)\n            if (both[i]) r[i] *= inv;",
+     "if (i < k_norm_cols) a[i] = a[i] * inv * g[i];\n"
+     "          }\n          oracle_rope_row(a, r, D, fr, interleaved);"),
     ("kvnorm_no_offset", "g[k] = elem(gamma, k, gamma_type) + (double)weight_offset;",
      "g[k] = elem(gamma, k, gamma_type);"),
     ("kvnorm_cast_order", "if (multiply_before_cast) {", "if (!multiply_before_cast) {"),
@@ -169,7 +182,8 @@ def _run_mutant(name, old, new, tmp):
         f.write(src.replace(old, new))
     lib = os.path.join(tmp, f"lib_{name}.so")
     subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-ffp-contract=off", "-shared",
-                    "-o", lib, path, "-lm"], check=True, capture_output=True)
+                    "-I", os.path.dirname(SRC), "-o", lib, path, "-lm"], check=True,
+                   capture_output=True)
     code = RUNNER.format(root=ROOT, tests=os.path.dirname(os.path.abspath(__file__)), lib=lib)
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
                        timeout=600)
