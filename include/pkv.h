@@ -101,8 +101,30 @@ typedef enum pkv_status {
 typedef enum pkv_dtype {
   PKV_DTYPE_BF16 = 0,
   PKV_DTYPE_FP8_E4M3FN = 1, /* OCP FP8 E4M3FN: bias 7, max 448, no inf */
-  PKV_DTYPE_F32 = 2         /* IEEE binary32 (MLA q output only) */
+  PKV_DTYPE_F32 = 2,        /* IEEE binary32 */
+  PKV_DTYPE_F16 = 3         /* IEEE binary16 */
 } pkv_dtype;
+
+/*
+ * Element types of a call's q, q output, freqs_cis and gamma tensors (the
+ * pages' dtype, out_rope_dtype, freq_dtype and gamma_dtype parameters).  A
+ * NULL pointer in place of the struct means the defaults in brackets.
+ *   q       q_rope of the MLA step, q_proj and the Q output of the Q/K RoPE:
+ *           PKV_DTYPE_BF16 or PKV_DTYPE_F16 [BF16]
+ *   q_out   q_rope_output of the MLA step: BF16, F16 or F32 [BF16]
+ *           (the Q/K RoPE writes its output in the type of q)
+ *   freqs   freqs_cis: F32, BF16 or F16 [F32]
+ *   gamma   gamma of the MLA step and of the K-cache RMSNorm: BF16, F16 or
+ *           F32 [BF16] (the Q/K RoPE's optional K-norm gamma is BF16 only)
+ * Another value returns PKV_ERR_DTYPE.  The latent row is always bf16 (the
+ * MLA page's latent input yields bfloat16 values).
+ */
+typedef struct pkv_elem_types {
+  int32_t q;
+  int32_t q_out;
+  int32_t freqs;
+  int32_t gamma;
+} pkv_elem_types;
 
 typedef enum pkv_scale_mode {
   PKV_SCALE_NONE = 0,       /* bf16 cache, no quantisation */
@@ -140,7 +162,8 @@ typedef struct pkv_paged_cache {
  * Fused MLA pre-attention step.  For every token t (request b, index j,
  * position p = cache_lengths[b] + j):
  *   q_rope_out[t,h,:] = RoPE_p(q_rope[t,h,:]) for every head h, rotate-half
- *                       pairs (i, i + rope_dim/2), fp32 math, one bf16 RNE;
+ *                       pairs (i, i + rope_dim/2), fp32 math, one rounding
+ *                       into the output type;
  *   y[0:kv_norm_dim]  = x * r * gamma,  r = 1/sqrt(mean(x^2) + epsilon),
  *                       x = kv_latent[t, 0:kv_norm_dim];
  *   y[kv_norm_dim: ]  = RoPE_p(kv_latent[t, kv_norm_dim:kv_norm_dim+rope_dim]);
@@ -148,18 +171,20 @@ typedef struct pkv_paged_cache {
  *                                        bf16_rne(y)                  (bf16).
  * Per-token scale mode writes scale = fp32(max|y| / 448) beside the row.
  *
- *   q_rope_out      [total_tokens][num_heads][rope_dim] of q_out_dtype
- *                   (PKV_DTYPE_BF16, or PKV_DTYPE_F32: the rotation rounded
- *                   to fp32 instead of bf16 -- the pages' out_rope_dtype),
- *                   strides qo_tok_stride / qo_head_stride (elements,
- *                   16-byte multiples)
- *   q_rope          bf16, same shape, strides qi_tok_stride / qi_head_stride
+ *   q_rope_out      [total_tokens][num_heads][rope_dim] of types->q_out (bf16,
+ *                   fp16 or fp32: the pages' out_rope_dtype), strides
+ *                   qo_tok_stride / qo_head_stride (elements, 16-byte
+ *                   multiples)
+ *   q_rope          types->q (bf16 or fp16), same shape, strides
+ *                   qi_tok_stride / qi_head_stride
  *   kv_latent       bf16 [total_tokens][kv_norm_dim + rope_dim], row stride
  *                   kv_row_stride (multiple of 8)
  *   input_row_offsets u32 [batch_size + 1]
  *   total_tokens    (host) number of new tokens = input_row_offsets[batch_size]
- *   freqs_cis       fp32 [max_seq_len][rope_dim]
- *   gamma           bf16 [kv_norm_dim]
+ *   freqs_cis       [max_seq_len][rope_dim] of types->freqs (fp32, bf16, fp16)
+ *   gamma           [kv_norm_dim] of types->gamma (bf16, fp16, fp32)
+ *   types           (host) element types, or NULL (bf16 q and q output, fp32
+ *                   freqs_cis, bf16 gamma); see pkv_elem_types
  *   kv_cache        (host) descriptor: dtype FP8_E4M3FN with scale mode
  *                   PER_TENSOR or PER_TOKEN, or BF16 with scale mode NONE;
  *                   num_heads 1, head_dim kv_norm_dim + rope_dim
@@ -175,9 +200,9 @@ int mla_rope_rmsnorm_quant(void* q_rope_out, int64_t qo_tok_stride, int64_t qo_h
                            const void* kv_latent, int64_t kv_row_stride,
                            const uint32_t* input_row_offsets, uint32_t batch_size,
                            uint32_t total_tokens, uint32_t num_heads, uint32_t rope_dim,
-                           uint32_t kv_norm_dim, const float* freqs_cis, uint32_t max_seq_len,
+                           uint32_t kv_norm_dim, const void* freqs_cis, uint32_t max_seq_len,
                            const void* gamma, float epsilon, const pkv_paged_cache* kv_cache,
-                           uint32_t layer_idx, int32_t q_out_dtype, void* stream);
+                           uint32_t layer_idx, const pkv_elem_types* types, void* stream);
 
 /*
  * Fused MLA pre-attention step in place on a bf16 latent cache ("mla_graph"
@@ -197,9 +222,9 @@ int mla_rope_rmsnorm_inplace(void* q_rope_out, int64_t qo_tok_stride, int64_t qo
                              const void* q_rope, int64_t qi_tok_stride, int64_t qi_head_stride,
                              const uint32_t* input_row_offsets, uint32_t batch_size,
                              uint32_t total_tokens, uint32_t num_heads, uint32_t rope_dim,
-                             uint32_t kv_norm_dim, const float* freqs_cis, uint32_t max_seq_len,
+                             uint32_t kv_norm_dim, const void* freqs_cis, uint32_t max_seq_len,
                              const void* gamma, float epsilon, const pkv_paged_cache* kv_cache,
-                             uint32_t layer_idx, int32_t q_out_dtype, void* stream);
+                             uint32_t layer_idx, const pkv_elem_types* types, void* stream);
 
 /*
  * Token plan: the placement of every new token of a ragged batch, written
@@ -249,10 +274,10 @@ int mla_rope_rmsnorm_quant_planned(void* q_rope_out, int64_t qo_tok_stride,
                                    const void* kv_latent, int64_t kv_row_stride,
                                    const uint32_t* token_plan, uint32_t total_tokens,
                                    uint32_t num_heads, uint32_t rope_dim, uint32_t kv_norm_dim,
-                                   const float* freqs_cis, uint32_t max_seq_len,
+                                   const void* freqs_cis, uint32_t max_seq_len,
                                    const void* gamma, float epsilon,
                                    const pkv_paged_cache* kv_cache, uint32_t layer_idx,
-                                   int32_t q_out_dtype, void* stream);
+                                   const pkv_elem_types* types, void* stream);
 
 /*
  * mla_rope_rmsnorm_inplace with each token placed by a token plan: the row at
@@ -271,10 +296,10 @@ int mla_rope_rmsnorm_inplace_planned(void* q_rope_out, int64_t qo_tok_stride,
                                      int64_t qi_tok_stride, int64_t qi_head_stride,
                                      const uint32_t* token_plan, uint32_t total_tokens,
                                      uint32_t num_heads, uint32_t rope_dim,
-                                     uint32_t kv_norm_dim, const float* freqs_cis,
+                                     uint32_t kv_norm_dim, const void* freqs_cis,
                                      uint32_t max_seq_len, const void* gamma, float epsilon,
                                      const pkv_paged_cache* kv_cache, uint32_t layer_idx,
-                                     int32_t q_out_dtype, void* stream);
+                                     const pkv_elem_types* types, void* stream);
 
 /*
  * mla_rope_rmsnorm_quant_planned without a caller-allocated plan, for callers
@@ -311,10 +336,10 @@ int mla_rope_rmsnorm_quant_noalloc(void* q_rope_out, int64_t qo_tok_stride,
                                    const void* kv_latent, int64_t kv_row_stride,
                                    const uint32_t* input_row_offsets, uint32_t batch_size,
                                    uint32_t total_tokens, uint32_t num_heads, uint32_t rope_dim,
-                                   uint32_t kv_norm_dim, const float* freqs_cis,
+                                   uint32_t kv_norm_dim, const void* freqs_cis,
                                    uint32_t max_seq_len, const void* gamma, float epsilon,
                                    const pkv_paged_cache* kv_cache, uint32_t layer_idx,
-                                   int32_t q_out_dtype, int build_plan, void* stream);
+                                   const pkv_elem_types* types, int build_plan, void* stream);
 
 /*
  * Paged-ragged fused Q/K RoPE.  Q is rotated into q_out; the K rows of the
@@ -332,18 +357,23 @@ int mla_rope_rmsnorm_quant_noalloc(void* q_rope_out, int64_t qo_tok_stride,
  * first RMS-normalised with gamma (fp32, unrounded), then the row is
  * rotated and rounded to bf16 once.
  *
- *   q_out, q_proj   bf16 [total_tokens][num_q_heads][head_dim] with strides
+ *   q_out, q_proj   types->q (bf16 or fp16) [total_tokens][num_q_heads]
+ *                   [head_dim] with strides
  *   k_cache         (host) descriptor, head_dim == the q head_dim: dtype
  *                   BF16 with scale mode NONE, or FP8_E4M3FN with
  *                   PER_TENSOR (K = code * scales[0], re-encoded with the
  *                   same scale) or PER_TOKEN (K = code * the slot/head
  *                   scale; after the rotation the head's scale is replaced
  *                   by max|y| / 448 and the head re-encoded with it)
- *   freqs_cis       fp32 [max_seq_len][head_dim]
+ *   freqs_cis       [max_seq_len][head_dim] of types->freqs (fp32, bf16, fp16)
  *   position_ids    u32 [total_tokens] or NULL ([3][total_tokens] with
  *                   mrope_section)
  *   mrope_section   (host) u32 [3] or NULL
  *   k_norm_gamma    bf16 [k_norm_cols] or NULL; 0 < k_norm_cols <= head_dim
+ *   types           (host) element types or NULL (bf16 q, fp32 freqs_cis);
+ *                   types->q_out must equal types->q, and types->gamma must
+ *                   be bf16 when k_norm_gamma is given (PKV_ERR_DTYPE
+ *                   otherwise)
  * Supported here: head_dim 64, 80, 96, 128 or 256; q and K head strides up
  * to 2^27 elements (else PKV_ERR_UNSUPPORTED).
  */
@@ -352,10 +382,10 @@ int qk_rope_paged_ragged(void* q_out, int64_t qo_tok_stride, int64_t qo_head_str
                          uint32_t total_tokens, uint32_t num_q_heads, uint32_t head_dim,
                          const uint32_t* input_row_offsets, uint32_t batch_size,
                          const pkv_paged_cache* k_cache, uint32_t layer_idx,
-                         const float* freqs_cis, uint32_t max_seq_len,
+                         const void* freqs_cis, uint32_t max_seq_len,
                          const uint32_t* position_ids, const uint32_t* mrope_section,
                          int interleaved, const void* k_norm_gamma, uint32_t k_norm_cols,
-                         float epsilon, void* stream);
+                         float epsilon, const pkv_elem_types* types, void* stream);
 
 /*
  * In-place RMSNorm of the new K-cache rows.  Tokens t < total_seq_len (host
@@ -371,7 +401,9 @@ int qk_rope_paged_ragged(void* q_out, int64_t qo_tok_stride, int64_t qo_head_str
  *                  scale) or PER_TOKEN (the head's scale becomes max|y| / 448
  *                  and the whole head is re-encoded with it); fp8 caches
  *                  need multiply_before_cast != 0
- *   gamma          bf16 [gamma_len], 0 < gamma_len <= head_dim
+ *   gamma          [gamma_len] of types->gamma (bf16, fp16, fp32),
+ *                  0 < gamma_len <= head_dim
+ *   types          (host) element types or NULL; only types->gamma is read
  *   per_head_norm  non-zero: one statistic per head; 0: one statistic per
  *                  token over the first gamma_len columns of all its heads
  *                  (the page lists the flag without describing it; this is
@@ -383,7 +415,8 @@ int rms_norm_kv_cache_paged(const pkv_paged_cache* k_cache, uint32_t layer_idx,
                             const void* gamma, uint32_t gamma_len, float epsilon,
                             float weight_offset, uint32_t total_seq_len,
                             const uint32_t* input_row_offsets, uint32_t batch_size,
-                            int per_head_norm, int multiply_before_cast, void* stream);
+                            int per_head_norm, int multiply_before_cast,
+                            const pkv_elem_types* types, void* stream);
 
 /*
  * rms_norm_kv_cache_paged with each token placed by a token plan (see
@@ -402,7 +435,8 @@ int rms_norm_kv_cache_paged_planned(const pkv_paged_cache* k_cache, uint32_t lay
                                     const void* gamma, uint32_t gamma_len, float epsilon,
                                     float weight_offset, uint32_t total_seq_len,
                                     const uint32_t* token_plan, int per_head_norm,
-                                    int multiply_before_cast, void* stream);
+                                    int multiply_before_cast, const pkv_elem_types* types,
+                                    void* stream);
 
 /*
  * Gather of request contexts from the paged latent cache.  For request b and

@@ -7,7 +7,11 @@ non-zero status.  All computation happens in the HIP kernels of ``libpkv.so``
 (built for gfx950 by ``paged_kv_cache_wavefront_amd.build``); there is no
 fallback: importing the module without the built library raises.
 
-Tensor conventions: bf16 data is ``torch.bfloat16``; the FP8 cache is
+Tensor conventions: bf16 data is ``torch.bfloat16``; q, its output,
+freqs_cis and gamma may also be ``torch.float16`` or ``torch.float32`` where
+the C entry point accepts that type (their ``pkv_elem_types`` is built from
+the tensors' dtypes, any other dtype passing a code the library refuses with
+PKV_ERR_DTYPE); the FP8 cache is
 ``torch.uint8`` (or ``torch.float8_e4m3fn``) holding E4M3FN codes; index
 arrays are ``torch.int32`` or ``torch.uint32`` holding unsigned values; all of
 them live on the same ROCm device.  Kernels are enqueued on ``stream`` (a
@@ -26,6 +30,7 @@ LIB_PATH = os.path.join(_PKG, "libpkv.so")
 PKV_DTYPE_BF16 = 0
 PKV_DTYPE_FP8_E4M3FN = 1
 PKV_DTYPE_F32 = 2
+PKV_DTYPE_F16 = 3
 PKV_SCALE_NONE = 0
 PKV_SCALE_PER_TENSOR = 1
 PKV_SCALE_PER_TOKEN = 2
@@ -67,6 +72,30 @@ class PagedCache(ctypes.Structure):
     ]
 
 
+class ElemTypes(ctypes.Structure):
+    """Mirror of ``pkv_elem_types``."""
+
+    _fields_ = [("q", ctypes.c_int32), ("q_out", ctypes.c_int32), ("freqs", ctypes.c_int32),
+                ("gamma", ctypes.c_int32)]
+
+
+_ELEM_CODES = {torch.bfloat16: PKV_DTYPE_BF16, torch.float16: PKV_DTYPE_F16,
+               torch.float32: PKV_DTYPE_F32}
+
+
+def _code(t: torch.Tensor | None, default: int) -> int:
+    if t is None:
+        return default
+    return _ELEM_CODES.get(t.dtype, -1)  # -1: refused by the library
+
+
+def _types(q=None, q_out=None, freqs=None, gamma=None) -> ElemTypes:
+    """The pkv_elem_types of a call, from its tensors' dtypes (a missing tensor
+    takes the library's default)."""
+    return ElemTypes(_code(q, PKV_DTYPE_BF16), _code(q_out, PKV_DTYPE_BF16),
+                     _code(freqs, PKV_DTYPE_F32), _code(gamma, PKV_DTYPE_BF16))
+
+
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
@@ -75,41 +104,42 @@ def _load() -> ctypes.CDLL:
     lib = ctypes.CDLL(LIB_PATH)
     i64, u32, vp, f32 = ctypes.c_int64, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_float
     cache_p = ctypes.POINTER(PagedCache)
+    types_p = ctypes.POINTER(ElemTypes)
     lib.mla_rope_rmsnorm_quant.restype = ctypes.c_int
     lib.mla_rope_rmsnorm_quant.argtypes = [
         vp, i64, i64, vp, i64, i64, vp, i64, vp, u32, u32, u32, u32, u32, vp, u32, vp, f32,
-        cache_p, u32, ctypes.c_int32, vp]
+        cache_p, u32, types_p, vp]
     lib.mla_rope_rmsnorm_inplace.restype = ctypes.c_int
     lib.mla_rope_rmsnorm_inplace.argtypes = [
         vp, i64, i64, vp, i64, i64, vp, u32, u32, u32, u32, u32, vp, u32, vp, f32,
-        cache_p, u32, ctypes.c_int32, vp]
+        cache_p, u32, types_p, vp]
     lib.pkv_token_plan.restype = ctypes.c_int
     lib.pkv_token_plan.argtypes = [vp, vp, u32, u32, cache_p, vp]
     lib.mla_rope_rmsnorm_quant_planned.restype = ctypes.c_int
     lib.mla_rope_rmsnorm_quant_planned.argtypes = [
         vp, i64, i64, vp, i64, i64, vp, i64, vp, u32, u32, u32, u32, vp, u32, vp, f32,
-        cache_p, u32, ctypes.c_int32, vp]
+        cache_p, u32, types_p, vp]
     lib.mla_rope_rmsnorm_inplace_planned.restype = ctypes.c_int
     lib.mla_rope_rmsnorm_inplace_planned.argtypes = [
         vp, i64, i64, vp, i64, i64, vp, u32, u32, u32, u32, vp, u32, vp, f32, cache_p, u32,
-        ctypes.c_int32, vp]
+        types_p, vp]
     lib.qk_rope_paged_ragged.restype = ctypes.c_int
     lib.qk_rope_paged_ragged.argtypes = [
         vp, i64, i64, vp, i64, i64, u32, u32, u32, vp, u32, cache_p, u32, vp, u32, vp, vp,
-        ctypes.c_int, vp, u32, f32, vp]
+        ctypes.c_int, vp, u32, f32, types_p, vp]
     lib.rms_norm_kv_cache_paged.restype = ctypes.c_int
     lib.rms_norm_kv_cache_paged.argtypes = [
-        cache_p, u32, vp, u32, f32, f32, u32, vp, u32, ctypes.c_int, ctypes.c_int, vp]
+        cache_p, u32, vp, u32, f32, f32, u32, vp, u32, ctypes.c_int, ctypes.c_int, types_p, vp]
     lib.rms_norm_kv_cache_paged_planned.restype = ctypes.c_int
     lib.rms_norm_kv_cache_paged_planned.argtypes = [
-        cache_p, u32, vp, u32, f32, f32, u32, vp, ctypes.c_int, ctypes.c_int, vp]
+        cache_p, u32, vp, u32, f32, f32, u32, vp, ctypes.c_int, ctypes.c_int, types_p, vp]
     lib.mla_gather_latent_paged.restype = ctypes.c_int
     lib.mla_gather_latent_paged.argtypes = [
         vp, ctypes.c_int32, i64, vp, vp, vp, u32, u32, cache_p, u32, vp]
     lib.mla_rope_rmsnorm_quant_noalloc.restype = ctypes.c_int
     lib.mla_rope_rmsnorm_quant_noalloc.argtypes = [
         vp, i64, i64, vp, i64, i64, vp, i64, vp, u32, u32, u32, u32, u32, vp, u32, vp, f32,
-        cache_p, u32, ctypes.c_int32, ctypes.c_int, vp]
+        cache_p, u32, types_p, ctypes.c_int, vp]
     lib.pkv_status_string.restype = ctypes.c_char_p
     lib.pkv_status_string.argtypes = [ctypes.c_int]
     lib.pkv_stream_copy.restype = ctypes.c_int
@@ -182,10 +212,10 @@ def mla_rope_rmsnorm_quant(q_rope_output: torch.Tensor, q_rope: torch.Tensor,
                            freqs_cis: torch.Tensor, gamma: torch.Tensor, epsilon: float,
                            kv_cache: PagedCache, layer_idx: int, stream=None) -> None:
     """Fused MLA step (C: ``mla_rope_rmsnorm_quant``).  q tensors are
-    ``[tokens, heads, rope_dim]`` (rope_dim axis contiguous; q_rope bf16,
-    q_rope_output bf16 or float32), kv_latent
+    ``[tokens, heads, rope_dim]`` (rope_dim axis contiguous; q_rope bf16 or
+    float16, q_rope_output bf16, float16 or float32), kv_latent
     ``[tokens, kv_norm_dim + rope_dim]`` bf16, freqs_cis ``[max_seq_len,
-    rope_dim]`` fp32, gamma ``[kv_norm_dim]`` bf16."""
+    rope_dim]`` and gamma ``[kv_norm_dim]`` float32, bf16 or float16."""
     T, H, R = q_rope.shape
     st = _lib.mla_rope_rmsnorm_quant(
         _ptr(q_rope_output), q_rope_output.stride(0), q_rope_output.stride(1),
@@ -194,7 +224,7 @@ def mla_rope_rmsnorm_quant(q_rope_output: torch.Tensor, q_rope: torch.Tensor,
         _ptr(input_row_offsets), input_row_offsets.numel() - 1, T, H, R,
         kv_latent.shape[1] - R, _ptr(freqs_cis), freqs_cis.shape[0], _ptr(gamma),
         float(epsilon), ctypes.byref(kv_cache), int(layer_idx),
-        PKV_DTYPE_F32 if q_rope_output.dtype == torch.float32 else PKV_DTYPE_BF16,
+        ctypes.byref(_types(q_rope, q_rope_output, freqs_cis, gamma)),
         _stream(stream))
     _check("mla_rope_rmsnorm_quant", st)
 
@@ -214,7 +244,7 @@ def mla_rope_rmsnorm_inplace(q_rope_output: torch.Tensor, q_rope: torch.Tensor,
         _ptr(input_row_offsets), input_row_offsets.numel() - 1, T, H, R,
         kv_cache.head_dim - R, _ptr(freqs_cis), freqs_cis.shape[0], _ptr(gamma),
         float(epsilon), ctypes.byref(kv_cache), int(layer_idx),
-        PKV_DTYPE_F32 if q_rope_output.dtype == torch.float32 else PKV_DTYPE_BF16,
+        ctypes.byref(_types(q_rope, q_rope_output, freqs_cis, gamma)),
         _stream(stream))
     _check("mla_rope_rmsnorm_inplace", st)
 
@@ -264,7 +294,7 @@ def mla_rope_rmsnorm_quant_planned(q_rope_output: torch.Tensor, q_rope: torch.Te
         _ptr(kv_latent), kv_latent.stride(0), _ptr(plan), T, H, R,
         kv_latent.shape[1] - R, _ptr(freqs_cis), freqs_cis.shape[0], _ptr(gamma),
         float(epsilon), ctypes.byref(kv_cache), int(layer_idx),
-        PKV_DTYPE_F32 if q_rope_output.dtype == torch.float32 else PKV_DTYPE_BF16,
+        ctypes.byref(_types(q_rope, q_rope_output, freqs_cis, gamma)),
         _stream(stream))
     _check("mla_rope_rmsnorm_quant_planned", st)
 
@@ -284,7 +314,7 @@ def mla_rope_rmsnorm_inplace_planned(q_rope_output: torch.Tensor, q_rope: torch.
         _ptr(q_rope), q_rope.stride(0), q_rope.stride(1), _ptr(plan), T, H, R,
         kv_cache.head_dim - R, _ptr(freqs_cis), freqs_cis.shape[0], _ptr(gamma),
         float(epsilon), ctypes.byref(kv_cache), int(layer_idx),
-        PKV_DTYPE_F32 if q_rope_output.dtype == torch.float32 else PKV_DTYPE_BF16,
+        ctypes.byref(_types(q_rope, q_rope_output, freqs_cis, gamma)),
         _stream(stream))
     _check("mla_rope_rmsnorm_inplace_planned", st)
 
@@ -307,7 +337,7 @@ def mla_rope_rmsnorm_quant_noalloc(q_rope_output: torch.Tensor, q_rope: torch.Te
         _ptr(input_row_offsets), input_row_offsets.numel() - 1, T, H, R,
         kv_latent.shape[1] - R, _ptr(freqs_cis), freqs_cis.shape[0], _ptr(gamma),
         float(epsilon), ctypes.byref(kv_cache), int(layer_idx),
-        PKV_DTYPE_F32 if q_rope_output.dtype == torch.float32 else PKV_DTYPE_BF16,
+        ctypes.byref(_types(q_rope, q_rope_output, freqs_cis, gamma)),
         int(bool(build_plan)), _stream(stream))
     _check("mla_rope_rmsnorm_quant_noalloc", st)
 
@@ -319,7 +349,8 @@ def qk_rope_paged_ragged(q_out: torch.Tensor, q_proj: torch.Tensor,
                          k_norm_gamma: torch.Tensor | None = None, epsilon: float = 1e-6,
                          stream=None, mrope_section=None) -> None:
     """Paged-ragged fused Q/K RoPE (C: ``qk_rope_paged_ragged``).  Q tensors
-    are ``[tokens, heads, head_dim]`` bf16; K is rotated in place.
+    are ``[tokens, heads, head_dim]`` bf16 or float16 (both the same);
+    freqs_cis float32, bf16 or float16; K is rotated in place.
     ``mrope_section``: three ints (temporal, height, width pair counts) with
     ``position_ids`` of shape [3, tokens]."""
     T, Hq, D = q_proj.shape
@@ -331,7 +362,8 @@ def qk_rope_paged_ragged(q_out: torch.Tensor, q_proj: torch.Tensor,
         q_proj.stride(1), T, Hq, D, _ptr(input_row_offsets), input_row_offsets.numel() - 1,
         ctypes.byref(k_cache), int(layer_idx), _ptr(freqs_cis), freqs_cis.shape[0],
         _ptr(position_ids), sec, int(bool(interleaved)), _ptr(k_norm_gamma),
-        0 if k_norm_gamma is None else k_norm_gamma.numel(), float(epsilon), _stream(stream))
+        0 if k_norm_gamma is None else k_norm_gamma.numel(), float(epsilon),
+        ctypes.byref(_types(q_proj, q_out, freqs_cis, k_norm_gamma)), _stream(stream))
     _check("qk_rope_paged_ragged", st)
 
 
@@ -339,12 +371,13 @@ def rms_norm_kv_cache_paged(k_cache: PagedCache, layer_idx: int, gamma: torch.Te
                             epsilon: float, weight_offset: float, total_seq_len: int,
                             input_row_offsets: torch.Tensor, per_head_norm: bool = True,
                             multiply_before_cast: bool = True, stream=None) -> None:
-    """In-place K-cache RMSNorm (C: ``rms_norm_kv_cache_paged``)."""
+    """In-place K-cache RMSNorm (C: ``rms_norm_kv_cache_paged``); gamma bf16,
+    float16 or float32."""
     st = _lib.rms_norm_kv_cache_paged(
         ctypes.byref(k_cache), int(layer_idx), _ptr(gamma), gamma.numel(), float(epsilon),
         float(weight_offset), int(total_seq_len), _ptr(input_row_offsets),
         input_row_offsets.numel() - 1, int(bool(per_head_norm)),
-        int(bool(multiply_before_cast)), _stream(stream))
+        int(bool(multiply_before_cast)), ctypes.byref(_types(gamma=gamma)), _stream(stream))
     _check("rms_norm_kv_cache_paged", st)
 
 
@@ -359,7 +392,7 @@ def rms_norm_kv_cache_paged_planned(k_cache: PagedCache, layer_idx: int, gamma: 
     st = _lib.rms_norm_kv_cache_paged_planned(
         ctypes.byref(k_cache), int(layer_idx), _ptr(gamma), gamma.numel(), float(epsilon),
         float(weight_offset), int(total_seq_len), _ptr(plan), int(bool(per_head_norm)),
-        int(bool(multiply_before_cast)), _stream(stream))
+        int(bool(multiply_before_cast)), ctypes.byref(_types(gamma=gamma)), _stream(stream))
     _check("rms_norm_kv_cache_paged_planned", st)
 
 

@@ -70,9 +70,9 @@ extern "C" int mla_rope_rmsnorm_quant_noalloc(
     void* q_rope_out, int64_t qo_tok_stride, int64_t qo_head_stride, const void* q_rope,
     int64_t qi_tok_stride, int64_t qi_head_stride, const void* kv_latent, int64_t kv_row_stride,
     const uint32_t* input_row_offsets, uint32_t batch_size, uint32_t total_tokens,
-    uint32_t num_heads, uint32_t rope_dim, uint32_t kv_norm_dim, const float* freqs_cis,
+    uint32_t num_heads, uint32_t rope_dim, uint32_t kv_norm_dim, const void* freqs_cis,
     uint32_t max_seq_len, const void* gamma, float epsilon, const pkv_paged_cache* kv_cache,
-    uint32_t layer_idx, int32_t q_out_dtype, int build_plan, void* stream) {
+    uint32_t layer_idx, const pkv_elem_types* types, int build_plan, void* stream) {
   if (total_tokens > kScratchTokens) return PKV_ERR_UNSUPPORTED;
   // Host checks first, against a stand-in plan address (16-byte aligned,
   // never dereferenced): a refused call touches no device.
@@ -82,7 +82,7 @@ extern "C" int mla_rope_rmsnorm_quant_noalloc(
                                     qi_tok_stride, qi_head_stride, kv_latent, kv_row_stride,
                                     stand_in, total_tokens, num_heads, rope_dim, kv_norm_dim,
                                     freqs_cis, max_seq_len, gamma, epsilon, kv_cache, layer_idx,
-                                    q_out_dtype, &m);
+                                    types, &m);
   if (st != PKV_OK) return st;
   pkv::PlanArgs pa{};
   if (build_plan) {

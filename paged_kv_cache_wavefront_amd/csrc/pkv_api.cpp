@@ -55,6 +55,24 @@ int check_cache(const pkv_paged_cache* c, uint32_t layer_idx, uint32_t batch_siz
 
 int launch_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH; }
 
+// A call's element types, NULL standing for the defaults.
+pkv_elem_types types_or_default(const pkv_elem_types* t) {
+  if (t != nullptr) return *t;
+  return pkv_elem_types{PKV_DTYPE_BF16, PKV_DTYPE_BF16, PKV_DTYPE_F32, PKV_DTYPE_BF16};
+}
+bool is_16bit_float(int32_t t) { return t == PKV_DTYPE_BF16 || t == PKV_DTYPE_F16; }
+bool is_float(int32_t t) { return is_16bit_float(t) || t == PKV_DTYPE_F32; }
+
+// The MLA kernel's q input / output pair; false if it is not one it is built for.
+bool qio_of(int32_t q, int32_t q_out, pkv::QIO* out) {
+  if (!is_16bit_float(q) || !is_float(q_out)) return false;
+  const bool h = q == PKV_DTYPE_F16;
+  if (q_out == PKV_DTYPE_BF16) *out = h ? pkv::QIO::H_B : pkv::QIO::B_B;
+  else if (q_out == PKV_DTYPE_F16) *out = h ? pkv::QIO::H_H : pkv::QIO::B_H;
+  else *out = h ? pkv::QIO::H_F : pkv::QIO::B_F;
+  return true;
+}
+
 // Head dims the Q/K RoPE and K-norm kernels are built for.
 bool sibling_head_dim(uint32_t d) { return d == 64 || d == 80 || d == 96 || d == 128 || d == 256; }
 
@@ -92,13 +110,16 @@ int mla_entry(void* q_rope_out, int64_t qo_tok_stride, int64_t qo_head_stride,
               const uint32_t* token_plan,
               const uint32_t* input_row_offsets, uint32_t batch_size, uint32_t total_tokens,
               uint32_t num_heads, uint32_t rope_dim, uint32_t kv_norm_dim,
-              const float* freqs_cis, uint32_t max_seq_len, const void* gamma, float epsilon,
-              const pkv_paged_cache* kv_cache, uint32_t layer_idx, int32_t q_out_dtype,
+              const void* freqs_cis, uint32_t max_seq_len, const void* gamma, float epsilon,
+              const pkv_paged_cache* kv_cache, uint32_t layer_idx, const pkv_elem_types* types,
               void* stream, pkv::MlaLaunch* prepared = nullptr) {
   if (prepared != nullptr) prepared->empty = true;
   if (kv_cache == nullptr) return PKV_ERR_NULL;
-  if (q_out_dtype != PKV_DTYPE_BF16 && q_out_dtype != PKV_DTYPE_F32) return PKV_ERR_DTYPE;
-  const int64_t qo_align = q_out_dtype == PKV_DTYPE_F32 ? 4 : 8;  // 16 bytes in elements
+  const pkv_elem_types ty = types_or_default(types);
+  pkv::QIO qio;
+  if (!qio_of(ty.q, ty.q_out, &qio) || !is_float(ty.freqs) || !is_float(ty.gamma))
+    return PKV_ERR_DTYPE;
+  const int64_t qo_align = ty.q_out == PKV_DTYPE_F32 ? 4 : 8;  // 16 bytes in elements
   if (rope_dim == 0 || rope_dim % 2 != 0 || kv_norm_dim == 0) return PKV_ERR_SHAPE;
   if (kv_cache->num_heads != 1 || kv_cache->head_dim != kv_norm_dim + rope_dim)
     return PKV_ERR_SHAPE;
@@ -139,7 +160,9 @@ int mla_entry(void* q_rope_out, int64_t qo_tok_stride, int64_t qo_head_stride,
 
   pkv::MlaArgs a{};
   a.q_out = q_rope_out;
-  a.q_out_f32 = q_out_dtype == PKV_DTYPE_F32;
+  a.qio = qio;
+  a.freq_type = ty.freqs;
+  a.gamma_type = ty.gamma;
   a.qo_tok = qo_tok_stride;
   a.qo_head = qo_head_stride;
   a.q_in = static_cast<const uint16_t*>(q_rope);
@@ -159,7 +182,7 @@ int mla_entry(void* q_rope_out, int64_t qo_tok_stride, int64_t qo_head_stride,
   a.inv_dn = (float)(1.0 / (double)kv_norm_dim);
   a.freqs = freqs_cis;
   a.max_seq_len = max_seq_len;
-  a.gamma = static_cast<const uint16_t*>(gamma);
+  a.gamma = gamma;
   a.epsilon = epsilon;
   a.tensor_scale = kv_cache->scales;
   a.token_scales = nullptr;
@@ -207,14 +230,14 @@ int mla_prepare_planned(void* q_rope_out, int64_t qo_tok_stride, int64_t qo_head
                         const void* q_rope, int64_t qi_tok_stride, int64_t qi_head_stride,
                         const void* kv_latent, int64_t kv_row_stride,
                         const uint32_t* token_plan, uint32_t total_tokens, uint32_t num_heads,
-                        uint32_t rope_dim, uint32_t kv_norm_dim, const float* freqs_cis,
+                        uint32_t rope_dim, uint32_t kv_norm_dim, const void* freqs_cis,
                         uint32_t max_seq_len, const void* gamma, float epsilon,
                         const pkv_paged_cache* kv_cache, uint32_t layer_idx,
-                        int32_t q_out_dtype, MlaLaunch* out) {
+                        const pkv_elem_types* types, MlaLaunch* out) {
   return mla_entry(q_rope_out, qo_tok_stride, qo_head_stride, q_rope, qi_tok_stride,
                    qi_head_stride, kv_latent, kv_row_stride, false, true, token_plan, nullptr,
                    0, total_tokens, num_heads, rope_dim, kv_norm_dim, freqs_cis, max_seq_len,
-                   gamma, epsilon, kv_cache, layer_idx, q_out_dtype, nullptr, out);
+                   gamma, epsilon, kv_cache, layer_idx, types, nullptr, out);
 }
 
 int plan_prepare(uint32_t* token_plan, const uint32_t* input_row_offsets, uint32_t batch_size,
@@ -247,14 +270,14 @@ int mla_rope_rmsnorm_quant(void* q_rope_out, int64_t qo_tok_stride, int64_t qo_h
                            const void* kv_latent, int64_t kv_row_stride,
                            const uint32_t* input_row_offsets, uint32_t batch_size,
                            uint32_t total_tokens, uint32_t num_heads, uint32_t rope_dim,
-                           uint32_t kv_norm_dim, const float* freqs_cis, uint32_t max_seq_len,
+                           uint32_t kv_norm_dim, const void* freqs_cis, uint32_t max_seq_len,
                            const void* gamma, float epsilon, const pkv_paged_cache* kv_cache,
-                           uint32_t layer_idx, int32_t q_out_dtype, void* stream) {
+                           uint32_t layer_idx, const pkv_elem_types* types, void* stream) {
   return mla_entry(q_rope_out, qo_tok_stride, qo_head_stride, q_rope, qi_tok_stride,
                    qi_head_stride, kv_latent, kv_row_stride, false, false, nullptr,
                    input_row_offsets, batch_size, total_tokens, num_heads, rope_dim,
                    kv_norm_dim, freqs_cis, max_seq_len, gamma, epsilon, kv_cache, layer_idx,
-                   q_out_dtype, stream);
+                   types, stream);
 }
 
 int pkv_token_plan(uint32_t* token_plan, const uint32_t* input_row_offsets,
@@ -271,14 +294,14 @@ int mla_rope_rmsnorm_inplace_planned(void* q_rope_out, int64_t qo_tok_stride,
                                      int64_t qi_tok_stride, int64_t qi_head_stride,
                                      const uint32_t* token_plan, uint32_t total_tokens,
                                      uint32_t num_heads, uint32_t rope_dim,
-                                     uint32_t kv_norm_dim, const float* freqs_cis,
+                                     uint32_t kv_norm_dim, const void* freqs_cis,
                                      uint32_t max_seq_len, const void* gamma, float epsilon,
                                      const pkv_paged_cache* kv_cache, uint32_t layer_idx,
-                                     int32_t q_out_dtype, void* stream) {
+                                     const pkv_elem_types* types, void* stream) {
   return mla_entry(q_rope_out, qo_tok_stride, qo_head_stride, q_rope, qi_tok_stride,
                    qi_head_stride, nullptr, 0, true, true, token_plan, nullptr, 0, total_tokens,
                    num_heads, rope_dim, kv_norm_dim, freqs_cis, max_seq_len, gamma, epsilon,
-                   kv_cache, layer_idx, q_out_dtype, stream);
+                   kv_cache, layer_idx, types, stream);
 }
 
 int mla_rope_rmsnorm_quant_planned(void* q_rope_out, int64_t qo_tok_stride,
@@ -287,27 +310,27 @@ int mla_rope_rmsnorm_quant_planned(void* q_rope_out, int64_t qo_tok_stride,
                                    const void* kv_latent, int64_t kv_row_stride,
                                    const uint32_t* token_plan, uint32_t total_tokens,
                                    uint32_t num_heads, uint32_t rope_dim, uint32_t kv_norm_dim,
-                                   const float* freqs_cis, uint32_t max_seq_len,
+                                   const void* freqs_cis, uint32_t max_seq_len,
                                    const void* gamma, float epsilon,
                                    const pkv_paged_cache* kv_cache, uint32_t layer_idx,
-                                   int32_t q_out_dtype, void* stream) {
+                                   const pkv_elem_types* types, void* stream) {
   return mla_entry(q_rope_out, qo_tok_stride, qo_head_stride, q_rope, qi_tok_stride,
                    qi_head_stride, kv_latent, kv_row_stride, false, true, token_plan, nullptr,
                    0, total_tokens, num_heads, rope_dim, kv_norm_dim, freqs_cis, max_seq_len,
-                   gamma, epsilon, kv_cache, layer_idx, q_out_dtype, stream);
+                   gamma, epsilon, kv_cache, layer_idx, types, stream);
 }
 
 int mla_rope_rmsnorm_inplace(void* q_rope_out, int64_t qo_tok_stride, int64_t qo_head_stride,
                              const void* q_rope, int64_t qi_tok_stride, int64_t qi_head_stride,
                              const uint32_t* input_row_offsets, uint32_t batch_size,
                              uint32_t total_tokens, uint32_t num_heads, uint32_t rope_dim,
-                             uint32_t kv_norm_dim, const float* freqs_cis, uint32_t max_seq_len,
+                             uint32_t kv_norm_dim, const void* freqs_cis, uint32_t max_seq_len,
                              const void* gamma, float epsilon, const pkv_paged_cache* kv_cache,
-                             uint32_t layer_idx, int32_t q_out_dtype, void* stream) {
+                             uint32_t layer_idx, const pkv_elem_types* types, void* stream) {
   return mla_entry(q_rope_out, qo_tok_stride, qo_head_stride, q_rope, qi_tok_stride,
                    qi_head_stride, nullptr, 0, true, false, nullptr, input_row_offsets,
                    batch_size, total_tokens, num_heads, rope_dim, kv_norm_dim, freqs_cis,
-                   max_seq_len, gamma, epsilon, kv_cache, layer_idx, q_out_dtype, stream);
+                   max_seq_len, gamma, epsilon, kv_cache, layer_idx, types, stream);
 }
 
 int qk_rope_paged_ragged(void* q_out, int64_t qo_tok_stride, int64_t qo_head_stride,
@@ -315,11 +338,15 @@ int qk_rope_paged_ragged(void* q_out, int64_t qo_tok_stride, int64_t qo_head_str
                          uint32_t total_tokens, uint32_t num_q_heads, uint32_t head_dim,
                          const uint32_t* input_row_offsets, uint32_t batch_size,
                          const pkv_paged_cache* k_cache, uint32_t layer_idx,
-                         const float* freqs_cis, uint32_t max_seq_len,
+                         const void* freqs_cis, uint32_t max_seq_len,
                          const uint32_t* position_ids, const uint32_t* mrope_section,
                          int interleaved, const void* k_norm_gamma, uint32_t k_norm_cols,
-                         float epsilon, void* stream) {
+                         float epsilon, const pkv_elem_types* types, void* stream) {
   if (k_cache == nullptr) return PKV_ERR_NULL;
+  const pkv_elem_types ty = types_or_default(types);
+  if (!is_16bit_float(ty.q) || ty.q_out != ty.q || !is_float(ty.freqs) ||
+      (k_norm_gamma != nullptr && ty.gamma != PKV_DTYPE_BF16))
+    return PKV_ERR_DTYPE;
   if (mrope_section != nullptr &&
       (uint64_t)mrope_section[0] + mrope_section[1] + mrope_section[2] != head_dim / 2)
     return PKV_ERR_SHAPE;
@@ -361,6 +388,7 @@ int qk_rope_paged_ragged(void* q_out, int64_t qo_tok_stride, int64_t qo_head_str
   a.offsets = input_row_offsets;
   a.batch = batch_size;
   a.freqs = freqs_cis;
+  a.freq_type = ty.freqs;
   a.max_seq_len = max_seq_len;
   a.position_ids = position_ids;
   a.mrope = mrope_section != nullptr;
@@ -373,7 +401,8 @@ int qk_rope_paged_ragged(void* q_out, int64_t qo_tok_stride, int64_t qo_head_str
   a.epsilon = epsilon;
   a.k_scales = k_scales_of(k_cache, layer_idx, km);
   a.cache = view;
-  return launch_status(pkv::launch_qk_rope(a, (int)head_dim, interleaved != 0, km,
+  return launch_status(pkv::launch_qk_rope(a, (int)head_dim, interleaved != 0,
+                                           ty.q == PKV_DTYPE_F16, km,
                                            static_cast<hipStream_t>(stream)));
 }
 
@@ -387,8 +416,10 @@ int kv_norm_entry(const pkv_paged_cache* k_cache, uint32_t layer_idx, const void
                   uint32_t gamma_len, float epsilon, float weight_offset,
                   uint32_t total_seq_len, bool planned, const uint32_t* token_plan,
                   const uint32_t* input_row_offsets, uint32_t batch_size, int per_head_norm,
-                  int multiply_before_cast, void* stream) {
+                  int multiply_before_cast, const pkv_elem_types* types, void* stream) {
   if (k_cache == nullptr) return PKV_ERR_NULL;
+  const int32_t gamma_type = types_or_default(types).gamma;
+  if (!is_float(gamma_type)) return PKV_ERR_DTYPE;
   pkv::KMode km;
   if (!k_mode_of(k_cache, &km)) return PKV_ERR_DTYPE;
   if (gamma_len == 0 || gamma_len > k_cache->head_dim) return PKV_ERR_SHAPE;
@@ -410,7 +441,8 @@ int kv_norm_entry(const pkv_paged_cache* k_cache, uint32_t layer_idx, const void
   a.offsets = planned ? nullptr : input_row_offsets;
   a.batch = planned ? 0u : batch_size;
   a.plan = planned ? token_plan : nullptr;
-  a.gamma = static_cast<const uint16_t*>(gamma);
+  a.gamma = gamma;
+  a.gamma_type = gamma_type;
   a.gamma_len = gamma_len;
   a.per_head = per_head_norm != 0;
   a.epsilon = epsilon;
@@ -430,20 +462,22 @@ int rms_norm_kv_cache_paged(const pkv_paged_cache* k_cache, uint32_t layer_idx,
                             const void* gamma, uint32_t gamma_len, float epsilon,
                             float weight_offset, uint32_t total_seq_len,
                             const uint32_t* input_row_offsets, uint32_t batch_size,
-                            int per_head_norm, int multiply_before_cast, void* stream) {
+                            int per_head_norm, int multiply_before_cast,
+                            const pkv_elem_types* types, void* stream) {
   return kv_norm_entry(k_cache, layer_idx, gamma, gamma_len, epsilon, weight_offset,
                        total_seq_len, false, nullptr, input_row_offsets, batch_size,
-                       per_head_norm, multiply_before_cast, stream);
+                       per_head_norm, multiply_before_cast, types, stream);
 }
 
 int rms_norm_kv_cache_paged_planned(const pkv_paged_cache* k_cache, uint32_t layer_idx,
                                     const void* gamma, uint32_t gamma_len, float epsilon,
                                     float weight_offset, uint32_t total_seq_len,
                                     const uint32_t* token_plan, int per_head_norm,
-                                    int multiply_before_cast, void* stream) {
+                                    int multiply_before_cast, const pkv_elem_types* types,
+                                    void* stream) {
   return kv_norm_entry(k_cache, layer_idx, gamma, gamma_len, epsilon, weight_offset,
                        total_seq_len, true, token_plan, nullptr, 0, per_head_norm,
-                       multiply_before_cast, stream);
+                       multiply_before_cast, types, stream);
 }
 
 int mla_gather_latent_paged(void* out, int32_t out_dtype, int64_t out_row_stride,

@@ -38,6 +38,7 @@ __device__ __forceinline__ void unpack8(const uint4& v, float (&f)[8]) {
 
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 // Two fp32 -> two bf16 in one dword, round-to-nearest-even
 // (v_cvt_pk_bf16_f32 on gfx950).
@@ -49,6 +50,81 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ uint4 pack8_bf16(const float (&f)[8]) {
   return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
                     pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
+}
+
+// ---- fp16 (IEEE binary16) <-> fp32 -------------------------------------------
+// Widening is exact; narrowing rounds to nearest even (the default mode),
+// overflowing to infinity, subnormals kept.
+
+__device__ __forceinline__ f32x2_t f16x2_to_f32(uint32_t w) {
+  return __builtin_convertvector(__builtin_bit_cast(f16x2_t, w), f32x2_t);
+}
+
+__device__ __forceinline__ void unpack8_f16(const uint4& v, float (&f)[8]) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f32x2_t p = f16x2_to_f32(w[i]);
+    f[2 * i] = p[0];
+    f[2 * i + 1] = p[1];
+  }
+}
+
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  f32x2_t f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2_t));
+}
+
+__device__ __forceinline__ uint4 pack8_f16(const float (&f)[8]) {
+  return make_uint4(pack_f16x2(f[0], f[1]), pack_f16x2(f[2], f[3]),
+                    pack_f16x2(f[4], f[5]), pack_f16x2(f[6], f[7]));
+}
+
+// Element types of q, freqs and gamma arrays (the values of pkv_dtype).
+enum ElemType : int { kBf16 = 0, kF32 = 2, kF16 = 3 };
+
+// 8 values of a 16-bit type (bf16 or fp16) from one 16-byte chunk.
+__device__ __forceinline__ void unpack8_16(const uint4& v, bool f16, float (&f)[8]) {
+  if (f16) unpack8_f16(v, f);
+  else unpack8(v, f);
+}
+
+// Value k (0 or 1) of a dword holding two 16-bit values of either type.
+__device__ __forceinline__ float half_of(uint32_t w, int k, bool f16) {
+  if (f16) return f16x2_to_f32(w)[k];
+  return k ? bf16_hi(w) : bf16_lo(w);
+}
+
+// Element i of an fp32 / bf16 / fp16 array, widened to fp32 (exact).
+__device__ __forceinline__ float load_elem(const void* p, int64_t i, int type) {
+  if (type == kF32) return static_cast<const float*>(p)[i];
+  const uint16_t b = static_cast<const uint16_t*>(p)[i];
+  if (type == kF16) return (float)__builtin_bit_cast(_Float16, b);
+  return __uint_as_float((uint32_t)b << 16);
+}
+
+// n consecutive values of an fp32 / bf16 / fp16 array, widened to fp32
+// (n a multiple of 8; p 16-byte aligned for 16-bit types, 32-byte for fp32).
+template <int N>
+__device__ __forceinline__ void load_typed(const void* p, int type, float (&f)[N]) {
+  static_assert(N % 8 == 0, "whole 16-byte chunks");
+  if (type == kF32) {
+    const float4* q = static_cast<const float4*>(p);
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) {
+      const float4 v = q[i];
+      f[4 * i] = v.x; f[4 * i + 1] = v.y; f[4 * i + 2] = v.z; f[4 * i + 3] = v.w;
+    }
+  } else {
+    const uint4* q = static_cast<const uint4*>(p);
+#pragma unroll
+    for (int i = 0; i < N / 8; ++i) {
+      float t[8];
+      unpack8_16(q[i], type == kF16, t);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) f[8 * i + j] = t[j];
+    }
+  }
 }
 
 // ---- fp32 -> FP8 E4M3FN (OCP), saturating, round-to-nearest-even -----------

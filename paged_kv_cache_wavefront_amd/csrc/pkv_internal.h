@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 struct pkv_paged_cache;  // include/pkv.h
+struct pkv_elem_types;   // include/pkv.h
 
 namespace pkv {
 
@@ -29,11 +30,16 @@ struct CacheView {
 // bf16 cache that already holds the row.
 enum class MlaOut : int { Fp8PerTensor = 0, Fp8PerToken = 1, Bf16 = 2, Bf16InPlace = 3 };
 
+// q_rope / q_rope_output element types of the MLA kernel (a template
+// parameter): bf16 or fp16 in, bf16, fp16 or fp32 out.
+enum class QIO : int { B_B = 0, B_H, B_F, H_H, H_B, H_F };
+
 struct MlaArgs {
-  void* q_out;                 // bf16, or fp32 when q_out_f32
-  bool q_out_f32;
+  void* q_out;                 // of the QIO output type
+  QIO qio;
+  int freq_type, gamma_type;   // ElemType of freqs_cis and gamma
   int64_t qo_tok, qo_head;
-  const uint16_t* q_in;
+  const uint16_t* q_in;        // bf16 or fp16 bits
   int64_t qi_tok, qi_head;
   const uint16_t* latent;      // unused in place
   int64_t kv_row;
@@ -45,9 +51,9 @@ struct MlaArgs {
   uint32_t rope_dim;           // 32, 64 or 128
   uint32_t nope_chunks;        // kv_norm_dim / 8 (at most 64)
   float inv_dn;                // 1 / kv_norm_dim, rounded to fp32
-  const float* freqs;
+  const void* freqs;           // [max_seq_len][rope_dim] of freq_type
   uint32_t max_seq_len;
-  const uint16_t* gamma;
+  const void* gamma;           // [kv_norm_dim] of gamma_type
   float epsilon;
   const float* tensor_scale;   // per-tensor mode: device scalar
   float* token_scales;         // per-token mode: this layer's [pages][page_size][heads]
@@ -86,7 +92,7 @@ struct PlanArgs {
 hipError_t launch_plan(const PlanArgs& a, hipStream_t stream);
 
 struct QkArgs {
-  uint16_t* q_out;
+  uint16_t* q_out;               // bf16 or fp16 bits, the type of q_in
   int64_t qo_tok, qo_head;
   const uint16_t* q_in;
   int64_t qi_tok, qi_head;
@@ -94,7 +100,8 @@ struct QkArgs {
   uint32_t chunks;               // waves per token (Q head chunks)
   const uint32_t* offsets;
   uint32_t batch;
-  const float* freqs;
+  const void* freqs;             // [max_seq_len][head_dim] of freq_type
+  int freq_type;                 // ElemType
   uint32_t max_seq_len;
   const uint32_t* position_ids;  // may be null; [3][total_tokens] with mrope
   uint32_t mrope;                // 1: multimodal RoPE with the two section ends below
@@ -108,14 +115,15 @@ struct QkArgs {
 
 // Q heads one wave of the Q/K kernel handles (head_dim 64, 80, 96, 128, 256).
 uint32_t qk_heads_per_wave(int head_dim);
-hipError_t launch_qk_rope(const QkArgs& a, int head_dim, bool interleaved, KMode kmode,
-                          hipStream_t stream);
+hipError_t launch_qk_rope(const QkArgs& a, int head_dim, bool interleaved, bool q_f16,
+                          KMode kmode, hipStream_t stream);
 
 struct KvNormArgs {
   uint32_t total_tokens;
   const uint32_t* offsets;
   uint32_t batch;
-  const uint16_t* gamma;
+  const void* gamma;             // [gamma_len] of gamma_type
+  int gamma_type;                // ElemType
   uint32_t gamma_len;
   bool per_head;                 // false: one statistic per token over all heads
   float epsilon, weight_offset;
@@ -153,10 +161,10 @@ int mla_prepare_planned(void* q_rope_out, int64_t qo_tok_stride, int64_t qo_head
                         const void* q_rope, int64_t qi_tok_stride, int64_t qi_head_stride,
                         const void* kv_latent, int64_t kv_row_stride,
                         const uint32_t* token_plan, uint32_t total_tokens, uint32_t num_heads,
-                        uint32_t rope_dim, uint32_t kv_norm_dim, const float* freqs_cis,
+                        uint32_t rope_dim, uint32_t kv_norm_dim, const void* freqs_cis,
                         uint32_t max_seq_len, const void* gamma, float epsilon,
                         const ::pkv_paged_cache* kv_cache, uint32_t layer_idx,
-                        int32_t q_out_dtype, MlaLaunch* out);
+                        const ::pkv_elem_types* types, MlaLaunch* out);
 int plan_prepare(uint32_t* token_plan, const uint32_t* input_row_offsets, uint32_t batch_size,
                  uint32_t total_tokens, const ::pkv_paged_cache* cache, PlanArgs* out);
 // A launch's status code (PKV_OK or PKV_ERR_LAUNCH).

@@ -26,9 +26,10 @@
 //   pairs 8k..8k+7, so the partner of lane k is lane LP-1-k, reached by one
 //   DPP mirror per dword (a ds_swizzle for D = 256, whose heads span 32
 //   lanes).
-// Pair i needs freqs columns 2i, 2i+1: 8 or 16 consecutive floats per lane,
-// loaded once per token.  Q is read, and Q and K are written, with
-// non-temporal accesses.
+// Pair i needs freqs columns 2i, 2i+1: 8 or 16 consecutive values per lane
+// (fp32, or bf16 / fp16 widened exactly), loaded once per token.  Q (bf16 or
+// fp16, a template parameter; the output takes q's type) is read, and Q and K
+// are written, with non-temporal accesses.
 //
 // Multimodal RoPE: three position rows; pair i uses the row of its section
 // (temporal / height / width pair ranges), cos/sin fetched per pair.
@@ -157,8 +158,8 @@ __device__ __forceinline__ void rotate_scaled(float (&own)[8], const float (&par
 
 // Q of one wave: NI instructions of HPI heads.  Base and step are wave-uniform
 // byte addresses; lane_off is the lane's byte offset.  GUARD masks heads past
-// num_heads.
-template <int D, bool INTER, int NI, bool GUARD>
+// num_heads.  QF16: q and its output are fp16, else bf16.
+template <int D, bool INTER, int NI, bool GUARD, bool QF16>
 __device__ __forceinline__ void q_rope(const char* src, char* dst, int64_t in_step,
                                        int64_t out_step, uint32_t in_off, uint32_t out_off,
                                        uint32_t h_lane, uint32_t num_heads, bool active,
@@ -177,18 +178,18 @@ __device__ __forceinline__ void q_rope(const char* src, char* dst, int64_t in_st
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     float own[8], par[8] = {};
-    unpack8(v[i], own);
-    if constexpr (!INTER) unpack8(mirror16<LP>(v[i]), par);
+    unpack8_16(v[i], QF16, own);
+    if constexpr (!INTER) unpack8_16(mirror16<LP>(v[i]), QF16, par);
     rotate_plain<INTER>(own, par, cs);
     if (GUARD && h_lane + HPI * i >= num_heads) continue;
     if (Geo::kPadded && !active) continue;
-    store16_stream(dst + i * out_step + out_off, pack8_bf16(own));
+    store16_stream(dst + i * out_step + out_off, QF16 ? pack8_f16(own) : pack8_bf16(own));
   }
 }
 
 // One wave per (token, chunk of Q heads); chunk 0 also rotates (and
 // optionally normalises) the token's K heads.
-template <int D, bool INTER, int NI, KMode KM>
+template <int D, bool INTER, int NI, KMode KM, bool QF16>
 __global__ __launch_bounds__(256) void qk_rope_kernel(const QkArgs a) {
   using Geo = Geometry<D, INTER>;
   constexpr int LP = Geo::kLanesPerHead, HPI = Geo::kHeadsPerInstr;
@@ -230,22 +231,27 @@ __global__ __launch_bounds__(256) void qk_rope_kernel(const QkArgs a) {
   bool pos_ok = ts.ok && pos < a.max_seq_len;
   if (a.mrope) pos_ok = pos_ok && pid[1] < a.max_seq_len && pid[2] < a.max_seq_len;
   float cs[Geo::kCs];
+  const bool f32 = a.freq_type == kF32, f16 = a.freq_type == kF16;
+  const int64_t feb = f32 ? 4 : 2;  // freqs element bytes
+  const char* freqs = static_cast<const char*>(a.freqs);
   if (pos_ok && !a.mrope) {
-    const float4* fr = reinterpret_cast<const float4*>(a.freqs + (int64_t)pos * D + role.cs_base);
-#pragma unroll
-    for (int i = 0; i < Geo::kCs / 4; ++i) {
-      const float4 v = fr[i];
-      cs[4 * i] = v.x; cs[4 * i + 1] = v.y; cs[4 * i + 2] = v.z; cs[4 * i + 3] = v.w;
-    }
+    load_typed<Geo::kCs>(freqs + feb * ((int64_t)pos * D + role.cs_base), a.freq_type, cs);
   } else if (pos_ok) {
     // multimodal RoPE: pair i takes cos/sin from the row of its section
 #pragma unroll
     for (int j = 0; j < Geo::kCs / 2; ++j) {
       const uint32_t i = (uint32_t)role.cs_base / 2 + j;
       const uint32_t p = i < a.mrope_end0 ? pid[0] : (i < a.mrope_end1 ? pid[1] : pid[2]);
-      const float2 v = *reinterpret_cast<const float2*>(a.freqs + (int64_t)p * D + 2 * i);
-      cs[2 * j] = v.x;
-      cs[2 * j + 1] = v.y;
+      const char* e = freqs + feb * ((int64_t)p * D + 2 * i);
+      if (f32) {
+        const float2 v = *reinterpret_cast<const float2*>(e);
+        cs[2 * j] = v.x;
+        cs[2 * j + 1] = v.y;
+      } else {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(e);
+        cs[2 * j] = half_of(w, 0, f16);
+        cs[2 * j + 1] = half_of(w, 1, f16);
+      }
     }
   }
   PageSlot ps{};
@@ -262,10 +268,10 @@ __global__ __launch_bounds__(256) void qk_rope_kernel(const QkArgs a) {
 
   // ---- Q ------------------------------------------------------------------------
   if (all_heads)
-    q_rope<D, INTER, NI, false>(qsrc, qdst, qi_step, qo_step, qi_off, qo_off, h_lane,
+    q_rope<D, INTER, NI, false, QF16>(qsrc, qdst, qi_step, qo_step, qi_off, qo_off, h_lane,
                                 a.num_q_heads, role.active, cs);
   else if (h0 < a.num_q_heads)
-    q_rope<D, INTER, NI, true>(qsrc, qdst, qi_step, qo_step, qi_off, qo_off, h_lane,
+    q_rope<D, INTER, NI, true, QF16>(qsrc, qdst, qi_step, qo_step, qi_off, qo_off, h_lane,
                                a.num_q_heads, role.active, cs);
   if (chunk != 0) return;
 
@@ -363,27 +369,33 @@ __global__ __launch_bounds__(256) void qk_rope_kernel(const QkArgs a) {
 }
 
 template <int D, bool INTER, KMode KM>
-hipError_t launch_one(const QkArgs& a, uint32_t blocks, hipStream_t stream) {
-  hipLaunchKernelGGL((qk_rope_kernel<D, INTER, kQInstrPerWave, KM>), dim3(blocks), dim3(256), 0,
-                     stream, a);
+hipError_t launch_one(const QkArgs& a, bool q_f16, uint32_t blocks, hipStream_t stream) {
+  if (q_f16)
+    hipLaunchKernelGGL((qk_rope_kernel<D, INTER, kQInstrPerWave, KM, true>), dim3(blocks),
+                       dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((qk_rope_kernel<D, INTER, kQInstrPerWave, KM, false>), dim3(blocks),
+                       dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
 template <int D, bool INTER>
-hipError_t launch_k(const QkArgs& a, KMode km, uint32_t blocks, hipStream_t stream) {
+hipError_t launch_k(const QkArgs& a, bool q_f16, KMode km, uint32_t blocks, hipStream_t stream) {
   switch (km) {
-    case KMode::Bf16: return launch_one<D, INTER, KMode::Bf16>(a, blocks, stream);
-    case KMode::Fp8PerTensor: return launch_one<D, INTER, KMode::Fp8PerTensor>(a, blocks, stream);
-    case KMode::Fp8PerToken: return launch_one<D, INTER, KMode::Fp8PerToken>(a, blocks, stream);
+    case KMode::Bf16: return launch_one<D, INTER, KMode::Bf16>(a, q_f16, blocks, stream);
+    case KMode::Fp8PerTensor:
+      return launch_one<D, INTER, KMode::Fp8PerTensor>(a, q_f16, blocks, stream);
+    case KMode::Fp8PerToken:
+      return launch_one<D, INTER, KMode::Fp8PerToken>(a, q_f16, blocks, stream);
   }
   return hipErrorInvalidValue;
 }
 
 template <int D>
-hipError_t launch_d(const QkArgs& a, bool interleaved, KMode km, uint32_t blocks,
+hipError_t launch_d(const QkArgs& a, bool interleaved, bool q_f16, KMode km, uint32_t blocks,
                     hipStream_t stream) {
-  return interleaved ? launch_k<D, true>(a, km, blocks, stream)
-                     : launch_k<D, false>(a, km, blocks, stream);
+  return interleaved ? launch_k<D, true>(a, q_f16, km, blocks, stream)
+                     : launch_k<D, false>(a, q_f16, km, blocks, stream);
 }
 
 }  // namespace
@@ -395,8 +407,8 @@ uint32_t qk_heads_per_wave(int head_dim) {
   return (uint32_t)kQInstrPerWave * (uint32_t)(kWave / pow2_at_least(head_dim / 8));
 }
 
-hipError_t launch_qk_rope(const QkArgs& a, int head_dim, bool interleaved, KMode kmode,
-                          hipStream_t stream) {
+hipError_t launch_qk_rope(const QkArgs& a, int head_dim, bool interleaved, bool q_f16,
+                          KMode kmode, hipStream_t stream) {
   const uint64_t waves = (uint64_t)a.total_tokens * a.chunks;
   const uint64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
   if (blocks == 0) return hipSuccess;
@@ -404,11 +416,11 @@ hipError_t launch_qk_rope(const QkArgs& a, int head_dim, bool interleaved, KMode
   if (blocks * kWavesPerBlock > 0xffffffffull) return hipErrorInvalidValue;
   const uint32_t nb = (uint32_t)blocks;
   switch (head_dim) {
-    case 64: return launch_d<64>(a, interleaved, kmode, nb, stream);
-    case 80: return launch_d<80>(a, interleaved, kmode, nb, stream);
-    case 96: return launch_d<96>(a, interleaved, kmode, nb, stream);
-    case 128: return launch_d<128>(a, interleaved, kmode, nb, stream);
-    case 256: return launch_d<256>(a, interleaved, kmode, nb, stream);
+    case 64: return launch_d<64>(a, interleaved, q_f16, kmode, nb, stream);
+    case 80: return launch_d<80>(a, interleaved, q_f16, kmode, nb, stream);
+    case 96: return launch_d<96>(a, interleaved, q_f16, kmode, nb, stream);
+    case 128: return launch_d<128>(a, interleaved, q_f16, kmode, nb, stream);
+    case 256: return launch_d<256>(a, interleaved, q_f16, kmode, nb, stream);
     default: return hipErrorInvalidValue;
   }
 }

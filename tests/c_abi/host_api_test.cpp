@@ -20,6 +20,7 @@ int g_mla_hpw;
 QkArgs g_qk;
 int g_qk_dim;
 bool g_qk_inter;
+bool g_qk_f16;
 KMode g_qk_mode;
 KvNormArgs g_norm;
 bool g_norm_mbc;
@@ -46,8 +47,9 @@ static uint32_t lanes_per_head(uint32_t head_dim) {
   return p;
 }
 uint32_t qk_heads_per_wave(int head_dim) { return 4u * (64u / lanes_per_head((uint32_t)head_dim)); }
-hipError_t launch_qk_rope(const QkArgs& a, int head_dim, bool inter, KMode km, hipStream_t) {
-  ++g_calls; g_qk = a; g_qk_dim = head_dim; g_qk_inter = inter; g_qk_mode = km;
+hipError_t launch_qk_rope(const QkArgs& a, int head_dim, bool inter, bool f16, KMode km,
+                          hipStream_t) {
+  ++g_calls; g_qk = a; g_qk_dim = head_dim; g_qk_inter = inter; g_qk_f16 = f16; g_qk_mode = km;
   return hipSuccess;
 }
 hipError_t launch_kv_norm(const KvNormArgs& a, bool mbc, KMode km, hipStream_t) {
@@ -122,12 +124,22 @@ static pkv_paged_cache k_cache(int32_t dtype, int32_t mode, uint32_t heads, uint
   return c;
 }
 
+// An MLA call whose q output has element type qdt (bf16 q, fp32 freqs, bf16 gamma).
 static int mla(const pkv_paged_cache* c, uint32_t T, uint32_t H, int32_t qdt, uint32_t layer = 1) {
   const int64_t qs = (int64_t)H * 64;
+  const pkv_elem_types types = {PKV_DTYPE_BF16, qdt, PKV_DTYPE_F32, PKV_DTYPE_BF16};
   return mla_rope_rmsnorm_quant(P(16384), qs, 64, P(20480), qs, 64, P(24576), 576,
                                 static_cast<const uint32_t*>(P(28672)), 2, T, H, 64, 512,
-                                static_cast<const float*>(P(32768)), 64, P(36864), 1e-6f, c,
-                                layer, qdt, nullptr);
+                                P(32768), 64, P(36864), 1e-6f, c, layer, &types, nullptr);
+}
+
+// An MLA call of 5 tokens of 40 heads with the given element types and q
+// output token stride (elements).
+static int mla_types(const pkv_paged_cache* c, const pkv_elem_types* t,
+                     int64_t qo_stride = 40 * 64) {
+  return mla_rope_rmsnorm_quant(P(16384), qo_stride, 64, P(20480), 40 * 64, 64, P(24576), 576,
+                                static_cast<const uint32_t*>(P(28672)), 2, 5, 40, 64, 512,
+                                P(32768), 64, P(36864), 1e-6f, c, 1, t, nullptr);
 }
 
 // An MLA call with rope_dim R and kv_norm_dim Dn (q rows of H * R values).
@@ -135,16 +147,14 @@ static int mla_dims(const pkv_paged_cache* c, uint32_t T, uint32_t H, uint32_t R
   const int64_t qs = (int64_t)H * R;
   return mla_rope_rmsnorm_quant(P(16384), qs, R, P(20480), qs, R, P(24576), Dn + R,
                                 static_cast<const uint32_t*>(P(28672)), 2, T, H, R, Dn,
-                                static_cast<const float*>(P(32768)), 64, P(36864), 1e-6f, c, 1,
-                                PKV_DTYPE_BF16, nullptr);
+                                P(32768), 64, P(36864), 1e-6f, c, 1, nullptr, nullptr);
 }
 
 static int mla_inplace(const pkv_paged_cache* c, uint32_t T, uint32_t H, uint32_t layer = 1) {
   const int64_t qs = (int64_t)H * 64;
   return mla_rope_rmsnorm_inplace(P(16384), qs, 64, P(20480), qs, 64,
                                   static_cast<const uint32_t*>(P(28672)), 2, T, H, 64, 512,
-                                  static_cast<const float*>(P(32768)), 64, P(36864), 1e-6f, c,
-                                  layer, PKV_DTYPE_BF16, nullptr);
+                                  P(32768), 64, P(36864), 1e-6f, c, layer, nullptr, nullptr);
 }
 
 // Randomised sweep of the validation: descriptors and arguments drawn from
@@ -205,26 +215,31 @@ static void fuzz(int iters) {
     const uint32_t layer = frand() % 4;
     void* q = coin(30) ? nullptr : (coin(20) ? P(16384 + 4) : P(16384));
     const uint32_t H = frand() % 200;
+    // element types: mostly the defaults, sometimes any code in -1..4
+    pkv_elem_types ty = {PKV_DTYPE_BF16, PKV_DTYPE_BF16, PKV_DTYPE_F32, PKV_DTYPE_BF16};
+    int32_t* fields[4] = {&ty.q, &ty.q_out, &ty.freqs, &ty.gamma};
+    for (int32_t* f : fields)
+      if (coin(8)) *f = (int32_t)(frand() % 6) - 1;
+    const pkv_elem_types* tp = coin(3) ? nullptr : &ty;
     const int before = g_calls;
     int st = -1;
     switch (entry) {
       case 0:
       case 1: {
         const int64_t ts = (int64_t)H * 64 + (coin(10) ? 4 : 0);
-        const int32_t qdt = coin(10) ? (int32_t)(frand() % 4) : PKV_DTYPE_BF16;
         if (entry == 0)
           st = mla_rope_rmsnorm_quant(P(20480), ts, 64, q, ts, 64, coin(20) ? nullptr : P(24576),
                                       coin(10) ? 580 : 576, static_cast<const uint32_t*>(P(28672)),
                                       B, T, H, coin(10) ? 32 : 64, coin(10) ? 256 : 512,
-                                      static_cast<const float*>(P(32768)), 1 + frand() % 9000,
-                                      coin(30) ? nullptr : P(36864), 1e-6f, cp, layer, qdt,
+                                      P(32768), 1 + frand() % 9000,
+                                      coin(30) ? nullptr : P(36864), 1e-6f, cp, layer, tp,
                                       nullptr);
         else
           st = mla_rope_rmsnorm_inplace(P(20480), ts, 64, q, ts, 64,
                                         static_cast<const uint32_t*>(P(28672)), B, T, H,
                                         coin(10) ? 32 : 64, 512,
-                                        static_cast<const float*>(P(32768)), 1 + frand() % 9000,
-                                        coin(30) ? nullptr : P(36864), 1e-6f, cp, layer, qdt,
+                                        P(32768), 1 + frand() % 9000,
+                                        coin(30) ? nullptr : P(36864), 1e-6f, cp, layer, tp,
                                         nullptr);
         break;
       }
@@ -236,10 +251,10 @@ static void fuzz(int iters) {
         const uint32_t cols = coin(3) ? 0u : frand() % (D + 2);
         st = qk_rope_paged_ragged(P(20480), (int64_t)H * D, D, q, (int64_t)H * D, D, T, H, D,
                                   static_cast<const uint32_t*>(P(28672)), B, cp, layer,
-                                  static_cast<const float*>(P(32768)), 4096,
+                                  P(32768), 4096,
                                   coin(2) ? static_cast<const uint32_t*>(P(40960)) : nullptr, sec,
                                   (int)(frand() % 2), cols ? P(45056) : nullptr, cols, 1e-6f,
-                                  nullptr);
+                                  tp, nullptr);
         break;
       }
       case 3: {
@@ -247,20 +262,19 @@ static void fuzz(int iters) {
         st = rms_norm_kv_cache_paged(cp, layer, coin(20) ? nullptr : P(45056),
                                      coin(10) ? 0u : 1 + frand() % (D + 1), 1e-6f, 0.25f, T,
                                      static_cast<const uint32_t*>(P(28672)), B,
-                                     (int)(frand() % 2), (int)(frand() % 2), nullptr);
+                                     (int)(frand() % 2), (int)(frand() % 2), tp, nullptr);
         break;
       }
       case 5: {
         const int64_t ts = (int64_t)H * 64 + (coin(10) ? 4 : 0);
-        const int32_t qdt = coin(10) ? (int32_t)(frand() % 4) : PKV_DTYPE_BF16;
         const uint32_t* plan = coin(20) ? nullptr
                                         : static_cast<const uint32_t*>(P(coin(20) ? 40964 : 40960));
         st = mla_rope_rmsnorm_quant_planned(P(20480), ts, 64, q, ts, 64,
                                             coin(20) ? nullptr : P(24576), coin(10) ? 580 : 576,
                                             plan, T, H, coin(10) ? 32 : 64, coin(10) ? 256 : 512,
-                                            static_cast<const float*>(P(32768)),
-                                            1 + frand() % 9000, coin(30) ? nullptr : P(36864),
-                                            1e-6f, cp, layer, qdt, nullptr);
+                                            P(32768), 1 + frand() % 9000,
+                                            coin(30) ? nullptr : P(36864), 1e-6f, cp, layer, tp,
+                                            nullptr);
         break;
       }
       case 6: {
@@ -334,17 +348,16 @@ int main() {
     c.page_table = nullptr;
     EXPECT(mla_rope_rmsnorm_quant_planned(P(16384), 40 * 64, 64, P(20480), 40 * 64, 64,
                                           P(24576), 576, plan, 5, 40, 64, 512,
-                                          static_cast<const float*>(P(32768)), 64, P(36864),
-                                          1e-6f, &c, 1, PKV_DTYPE_BF16, nullptr) == PKV_OK);
+                                          P(32768), 64, P(36864), 1e-6f, &c, 1, nullptr,
+                                          nullptr) == PKV_OK);
     EXPECT(g_calls == before + 1 && g_mla.plan == plan && g_mla.offsets == nullptr);
     EXPECT(g_mla.batch == 0 && g_mla.total_tokens == 5 && g_mla.chunks == 2);
     EXPECT(g_mla_mode == MlaOut::Fp8PerTensor);
     EXPECT(g_mla.cache.layer_base == static_cast<char*>(c.data) + c.layer_stride);
     EXPECT(mla_rope_rmsnorm_quant_planned(P(16384), 40 * 64, 64, P(20480), 40 * 64, 64,
                                           P(24576), 576, plan + 2, 5, 40, 64, 512,
-                                          static_cast<const float*>(P(32768)), 64, P(36864),
-                                          1e-6f, &c, 1, PKV_DTYPE_BF16, nullptr) ==
-           PKV_ERR_ALIGN);
+                                          P(32768), 64, P(36864), 1e-6f, &c, 1, nullptr,
+                                          nullptr) == PKV_ERR_ALIGN);
     // the batch form never carries a plan
     pkv_paged_cache b = latent_cache(PKV_DTYPE_FP8_E4M3FN, PKV_SCALE_PER_TENSOR, 7);
     EXPECT(mla(&b, 5, 40, PKV_DTYPE_BF16) == PKV_OK && g_mla.plan == nullptr);
@@ -354,12 +367,12 @@ int main() {
     k.page_table = nullptr;
     before = g_calls;
     EXPECT(rms_norm_kv_cache_paged_planned(&k, 2, P(45056), 128, 1e-6f, 0.0f, 7, plan, 1, 1,
-                                           nullptr) == PKV_OK);
+                                           nullptr, nullptr) == PKV_OK);
     EXPECT(g_calls == before + 1 && g_norm.plan == plan && g_norm.offsets == nullptr);
     EXPECT(g_norm.total_tokens == 7 && g_norm.batch == 0);
     EXPECT(g_norm.cache.layer_base == static_cast<char*>(k.data) + 2 * 2 * k.layer_stride);
     EXPECT(rms_norm_kv_cache_paged_planned(&k, 2, P(45056), 128, 1e-6f, 0.0f, 7, plan + 1, 1, 1,
-                                           nullptr) == PKV_ERR_ALIGN);
+                                           nullptr, nullptr) == PKV_ERR_ALIGN);
   }
   // --- MLA: per-token fp8, 40 heads, layer 1 of 2
   {
@@ -372,10 +385,11 @@ int main() {
     EXPECT(g_mla.chunks == 2);
     EXPECT(g_mla.cache.layer_base == static_cast<char*>(c.data) + c.layer_stride);
     EXPECT(g_mla.token_scales == c.scales + 7 * 16);
-    EXPECT(!g_mla.q_out_f32);
+    EXPECT(g_mla.qio == QIO::B_B && g_mla.freq_type == PKV_DTYPE_F32);
+    EXPECT(g_mla.gamma_type == PKV_DTYPE_BF16);
     EXPECT(g_mla.total_tokens == 5 && g_mla.num_heads == 40 && g_mla.batch == 2);
     EXPECT(g_mla.rope_dim == 64 && g_mla.nope_chunks == 64 && g_mla.inv_dn == 1.0f / 512);
-    EXPECT(mla(&c, 5, 40, PKV_DTYPE_F32) == PKV_OK && g_mla.q_out_f32);
+    EXPECT(mla(&c, 5, 40, PKV_DTYPE_F32) == PKV_OK && g_mla.qio == QIO::B_F);
     EXPECT(mla(&c, 5, 16, PKV_DTYPE_BF16) == PKV_OK && g_mla.chunks == 1 && g_mla_hpw == 16);
     EXPECT(mla(&c, 5, 40, PKV_DTYPE_BF16, 0) == PKV_OK &&
            g_mla.cache.layer_base == c.data && g_mla.token_scales == c.scales);
@@ -443,11 +457,12 @@ int main() {
     const uint32_t sec[3] = {16, 24, 24};
     const int st = qk_rope_paged_ragged(P(16384), 40 * 128, 128, P(20480), 40 * 128, 128, 9, 40, 128,
                                         static_cast<const uint32_t*>(P(28672)), 2, &c, 2,
-                                        static_cast<const float*>(P(32768)), 512,
+                                        P(32768), 512,
                                         static_cast<const uint32_t*>(P(36864)), sec, 0, P(40960), 96,
-                                        1e-6f, nullptr);
+                                        1e-6f, nullptr, nullptr);
     EXPECT(st == PKV_OK);
-    EXPECT(g_qk_mode == KMode::Fp8PerToken && g_qk_dim == 128 && !g_qk_inter);
+    EXPECT(g_qk_mode == KMode::Fp8PerToken && g_qk_dim == 128 && !g_qk_inter && !g_qk_f16);
+    EXPECT(g_qk.freq_type == PKV_DTYPE_F32);
     EXPECT(g_qk.chunks == 3);                                      // 40 heads, 16 per wave
     EXPECT(g_qk.mrope && g_qk.mrope_end0 == 16 && g_qk.mrope_end1 == 40);
     EXPECT(g_qk.k_norm_cols == 96);
@@ -457,9 +472,9 @@ int main() {
     const int before = g_calls;
     EXPECT(qk_rope_paged_ragged(P(16384), 40 * 128, 128, P(20480), 40 * 128, 128, 9, 40, 128,
                                 static_cast<const uint32_t*>(P(28672)), 2, &c, 2,
-                                static_cast<const float*>(P(32768)), 512,
+                                P(32768), 512,
                                 static_cast<const uint32_t*>(P(36864)), bad, 0, nullptr, 0, 1e-6f,
-                                nullptr) == PKV_ERR_SHAPE);
+                                nullptr, nullptr) == PKV_ERR_SHAPE);
     EXPECT(g_calls == before);
   }
   // --- Q/K RoPE with 96-wide heads: 16-lane groups, 16 heads per wave
@@ -467,27 +482,80 @@ int main() {
     pkv_paged_cache c = k_cache(PKV_DTYPE_BF16, PKV_SCALE_NONE, 2, 96);
     EXPECT(qk_rope_paged_ragged(P(16384), 40 * 96, 96, P(20480), 40 * 96, 96, 9, 40, 96,
                                 static_cast<const uint32_t*>(P(28672)), 2, &c, 1,
-                                static_cast<const float*>(P(32768)), 512, nullptr, nullptr, 1,
-                                nullptr, 0, 1e-6f, nullptr) == PKV_OK);
+                                P(32768), 512, nullptr, nullptr, 1,
+                                nullptr, 0, 1e-6f, nullptr, nullptr) == PKV_OK);
     EXPECT(g_qk_dim == 96 && g_qk_inter && g_qk.chunks == 3);
   }
   // --- K-cache norm: per-token statistic, bf16 two roundings
   {
     pkv_paged_cache c = k_cache(PKV_DTYPE_BF16, PKV_SCALE_NONE, 8, 128);
     EXPECT(rms_norm_kv_cache_paged(&c, 1, P(40960), 100, 1e-6f, 0.5f, 7,
-                                   static_cast<const uint32_t*>(P(28672)), 2, 0, 0, nullptr) ==
-           PKV_OK);
+                                   static_cast<const uint32_t*>(P(28672)), 2, 0, 0, nullptr,
+                                   nullptr) == PKV_OK);
     EXPECT(!g_norm.per_head && !g_norm_mbc && g_norm_mode == KMode::Bf16);
     EXPECT(g_norm.total_tokens == 7 && g_norm.gamma_len == 100 && g_norm.weight_offset == 0.5f);
     EXPECT(g_norm.head_dim == 128);
     // the per-token statistic over more heads than one register chunk holds
     pkv_paged_cache big = k_cache(PKV_DTYPE_BF16, PKV_SCALE_NONE, 17, 128);
     EXPECT(rms_norm_kv_cache_paged(&big, 1, P(40960), 128, 1e-6f, 0.f, 7,
-                                   static_cast<const uint32_t*>(P(28672)), 2, 0, 1, nullptr) ==
-           PKV_OK && !g_norm.per_head && g_norm.cache.num_heads == 17);
+                                   static_cast<const uint32_t*>(P(28672)), 2, 0, 1, nullptr,
+                                   nullptr) == PKV_OK && !g_norm.per_head &&
+           g_norm.cache.num_heads == 17);
     EXPECT(rms_norm_kv_cache_paged(&big, 1, P(40960), 128, 1e-6f, 0.f, 7,
-                                   static_cast<const uint32_t*>(P(28672)), 2, 1, 1, nullptr) ==
-           PKV_OK && g_norm.per_head);
+                                   static_cast<const uint32_t*>(P(28672)), 2, 1, 1, nullptr,
+                                   nullptr) == PKV_OK && g_norm.per_head);
+  }
+  // --- element types: the six q / q-output pairs, freqs and gamma types, refusals
+  {
+    const int32_t BF = PKV_DTYPE_BF16, H = PKV_DTYPE_F16, F = PKV_DTYPE_F32;
+    const int32_t E8 = PKV_DTYPE_FP8_E4M3FN;
+    pkv_paged_cache c = latent_cache(PKV_DTYPE_FP8_E4M3FN, PKV_SCALE_PER_TENSOR, 7);
+    struct { int32_t q, qo; QIO qio; } pairs[] = {{BF, BF, QIO::B_B}, {BF, H, QIO::B_H},
+                                                  {BF, F, QIO::B_F},  {H, H, QIO::H_H},
+                                                  {H, BF, QIO::H_B},  {H, F, QIO::H_F}};
+    for (const auto& p : pairs) {
+      const pkv_elem_types t = {p.q, p.qo, H, F};
+      EXPECT(mla_types(&c, &t) == PKV_OK && g_mla.qio == p.qio);
+      EXPECT(g_mla.freq_type == PKV_DTYPE_F16 && g_mla.gamma_type == PKV_DTYPE_F32);
+    }
+    const int before = g_calls;
+    const pkv_elem_types refused[] = {{F, BF, F, BF}, {E8, BF, F, BF}, {BF, E8, F, BF},
+                                      {BF, BF, E8, BF}, {BF, BF, F, E8}, {BF, BF, F, 7},
+                                      {-1, BF, F, BF}};
+    for (const auto& t : refused) EXPECT(mla_types(&c, &t) == PKV_ERR_DTYPE);
+    // the q output's strides are 16-byte multiples of its own element size
+    const pkv_elem_types f32_out = {BF, F, F, BF}, f16_out = {BF, H, F, BF};
+    EXPECT(mla_types(&c, &f16_out, 40 * 64 + 4) == PKV_ERR_ALIGN);
+    EXPECT(g_calls == before);
+    EXPECT(mla_types(&c, &f32_out, 40 * 64 + 4) == PKV_OK);
+    // Q/K RoPE: q and its output share a 16-bit type; the K-norm gamma is bf16
+    pkv_paged_cache k = k_cache(PKV_DTYPE_BF16, PKV_SCALE_NONE, 2, 128);
+    auto qk = [&](const pkv_elem_types* t, const void* gamma) {
+      return qk_rope_paged_ragged(P(16384), 40 * 128, 128, P(20480), 40 * 128, 128, 9, 40, 128,
+                                  static_cast<const uint32_t*>(P(28672)), 2, &k, 1, P(32768), 512,
+                                  nullptr, nullptr, 0, gamma, gamma ? 128 : 0, 1e-6f, t, nullptr);
+    };
+    const pkv_elem_types hh = {H, H, BF, BF};
+    EXPECT(qk(&hh, P(40960)) == PKV_OK && g_qk_f16 && g_qk.freq_type == PKV_DTYPE_BF16);
+    EXPECT(qk(nullptr, nullptr) == PKV_OK && !g_qk_f16 && g_qk.freq_type == PKV_DTYPE_F32);
+    const pkv_elem_types f32_gamma = {BF, BF, F, F};
+    EXPECT(qk(&f32_gamma, nullptr) == PKV_OK);  // gamma type unused without a K norm
+    const int before_qk = g_calls;
+    EXPECT(qk(&f32_gamma, P(40960)) == PKV_ERR_DTYPE);
+    const pkv_elem_types mixed = {H, BF, F, BF}, f32_q = {F, F, F, BF}, fp8_freqs = {BF, BF, E8, BF};
+    EXPECT(qk(&mixed, nullptr) == PKV_ERR_DTYPE && qk(&f32_q, nullptr) == PKV_ERR_DTYPE);
+    EXPECT(qk(&fp8_freqs, nullptr) == PKV_ERR_DTYPE && g_calls == before_qk);
+    // K-cache norm: bf16, fp16 or fp32 gamma
+    auto norm = [&](const pkv_elem_types* t) {
+      return rms_norm_kv_cache_paged(&k, 1, P(40960), 100, 1e-6f, 0.f, 7,
+                                     static_cast<const uint32_t*>(P(28672)), 2, 1, 1, t, nullptr);
+    };
+    const pkv_elem_types g16 = {BF, BF, F, H}, g32 = {BF, BF, F, F}, g8 = {BF, BF, F, E8};
+    EXPECT(norm(&g16) == PKV_OK && g_norm.gamma_type == PKV_DTYPE_F16);
+    EXPECT(norm(&g32) == PKV_OK && g_norm.gamma_type == PKV_DTYPE_F32);
+    EXPECT(norm(nullptr) == PKV_OK && g_norm.gamma_type == PKV_DTYPE_BF16);
+    const int before_norm = g_calls;
+    EXPECT(norm(&g8) == PKV_ERR_DTYPE && g_calls == before_norm);
   }
   // --- gather: fp8 per-token cache -> bf16 rows with a padded stride
   {

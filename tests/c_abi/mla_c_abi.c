@@ -19,24 +19,7 @@
 #include <string.h>
 
 #include "pkv.h"
-
-/* the oracle's entry point (liboracle.so) */
-int oracle_mla_rope_rmsnorm_quant(void* q_out, int q_out_f32, const uint16_t* q_in,
-                                  const uint16_t* latent, const uint32_t* row_offsets,
-                                  const uint32_t* cache_lengths, int64_t B,
-                                  const uint32_t* page_table, int64_t pt_stride,
-                                  const float* freqs, int64_t max_seq_len,
-                                  const uint16_t* gamma, float epsilon, int64_t H, int64_t R,
-                                  int64_t Dn, void* cache, int cache_type, int64_t num_layers,
-                                  int64_t num_pages, int64_t page_size, int64_t layer_idx,
-                                  int scale_mode, float tensor_scale, float* token_scales);
-int oracle_mla_rope_rmsnorm_inplace(void* q_out, int q_out_f32, const uint16_t* q_in,
-                                    const uint32_t* row_offsets, const uint32_t* cache_lengths,
-                                    int64_t B, const uint32_t* page_table, int64_t pt_stride,
-                                    const float* freqs, int64_t max_seq_len,
-                                    const uint16_t* gamma, float epsilon, int64_t H, int64_t R,
-                                    int64_t Dn, uint16_t* cache, int64_t num_layers,
-                                    int64_t num_pages, int64_t page_size, int64_t layer_idx);
+#include "pkv_oracle.h" /* the oracle's entry points (liboracle.so) */
 
 enum { B = 3, H = 5, R = 64, DN = 512, W = DN + R, S = 8, L = 2, LAYER = 1, MAXSEQ = 32 };
 
@@ -141,7 +124,7 @@ int main(void) {
 
   const int st = mla_rope_rmsnorm_quant(d_qo, (int64_t)H * R, R, d_q, (int64_t)H * R, R, d_lat, W,
                                         d_off, B, (uint32_t)T, H, R, DN, d_freqs, MAXSEQ, d_gamma,
-                                        eps, &c, LAYER, PKV_DTYPE_BF16, NULL);
+                                        eps, &c, LAYER, NULL, NULL);
   if (st != PKV_OK) {
     fprintf(stderr, "mla_rope_rmsnorm_quant: %s\n", pkv_status_string(st));
     return 1;
@@ -155,10 +138,10 @@ int main(void) {
   uint16_t* q_ref = malloc(sizeof(uint16_t) * T * H * R);
   uint8_t* cache_ref = malloc(cache_bytes);
   memcpy(cache_ref, cache0, cache_bytes);
-  const int orc = oracle_mla_rope_rmsnorm_quant(q_ref, 0, q, latent, offsets, prior, B, page_table,
-                                                PT_STRIDE, freqs, MAXSEQ, gamma, eps, H, R, DN,
-                                                cache_ref, 0 /* fp8 */, L, P, S, LAYER,
-                                                1 /* per-tensor */, scale, NULL);
+  const int orc = oracle_mla_rope_rmsnorm_quant(q_ref, 0, q, 0, latent, offsets, prior, B,
+                                                page_table, PT_STRIDE, freqs, 2, MAXSEQ, gamma,
+                                                0, eps, H, R, DN, cache_ref, 0 /* fp8 */, L, P,
+                                                S, LAYER, 1 /* per-tensor */, scale, NULL);
   if (orc != 0) {
     fprintf(stderr, "oracle: precondition failed (%d)\n", orc);
     return 1;
@@ -191,7 +174,7 @@ int main(void) {
     st3 = mla_rope_rmsnorm_quant_planned(d_qo_p, (int64_t)H * R, R, d_q, (int64_t)H * R, R,
                                          d_lat, W, (const uint32_t*)d_plan, (uint32_t)T, H, R,
                                          DN, d_freqs, MAXSEQ, d_gamma, eps, &c, LAYER,
-                                         PKV_DTYPE_BF16, NULL);
+                                         NULL, NULL);
   if (st3 != PKV_OK) {
     fprintf(stderr, "planned: %s\n", pkv_status_string(st3));
     return 1;
@@ -224,9 +207,11 @@ int main(void) {
   c.dtype = PKV_DTYPE_BF16;
   c.scale_mode = PKV_SCALE_NONE;
   c.scales = NULL;
+  /* the element types spelled out (the same as the NULL defaults) */
+  const pkv_elem_types types = {PKV_DTYPE_BF16, PKV_DTYPE_BF16, PKV_DTYPE_F32, PKV_DTYPE_BF16};
   const int st2 = mla_rope_rmsnorm_inplace(d_qo, (int64_t)H * R, R, d_q, (int64_t)H * R, R, d_off,
                                            B, (uint32_t)T, H, R, DN, d_freqs, MAXSEQ, d_gamma, eps,
-                                           &c, LAYER, PKV_DTYPE_BF16, NULL);
+                                           &c, LAYER, &types, NULL);
   if (st2 != PKV_OK) {
     fprintf(stderr, "mla_rope_rmsnorm_inplace: %s\n", pkv_status_string(st2));
     return 1;
@@ -237,9 +222,9 @@ int main(void) {
   CHECK(hipMemcpy(cache16_gpu, d_cache16, sizeof(uint16_t) * n16, hipMemcpyDeviceToHost));
   uint16_t* cache16_ref = malloc(sizeof(uint16_t) * n16);
   memcpy(cache16_ref, cache16, sizeof(uint16_t) * n16);
-  if (oracle_mla_rope_rmsnorm_inplace(q_ref, 0, q, offsets, prior, B, page_table, PT_STRIDE, freqs,
-                                      MAXSEQ, gamma, eps, H, R, DN, cache16_ref, L, P, S,
-                                      LAYER) != 0) {
+  if (oracle_mla_rope_rmsnorm_inplace(q_ref, 0, q, 0, offsets, prior, B, page_table, PT_STRIDE,
+                                      freqs, 2, MAXSEQ, gamma, 0, eps, H, R, DN, cache16_ref, L,
+                                      P, S, LAYER) != 0) {
     fprintf(stderr, "oracle (in place): precondition failed\n");
     return 1;
   }

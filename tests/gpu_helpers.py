@@ -29,6 +29,25 @@ def dev_f32(a: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(DEV)
 
 
+# numpy representation of each element type (bf16 as its uint16 bits) -> torch dtype
+TORCH_OF = {np.dtype(np.uint16): torch.bfloat16, np.dtype(np.float16): torch.float16,
+            np.dtype(np.float32): torch.float32}
+
+
+def dev_elem(a: np.ndarray) -> torch.Tensor:
+    """A bf16 (uint16 bits), fp16 or fp32 array on the device, in its type."""
+    if a.dtype == np.uint16:
+        return dev_bf16(a)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host_elem(t: torch.Tensor) -> np.ndarray:
+    """Inverse of dev_elem."""
+    if t.dtype == torch.bfloat16:
+        return host_bf16(t)
+    return t.contiguous().cpu().numpy()
+
+
 def host_bf16(t: torch.Tensor) -> np.ndarray:
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
@@ -59,6 +78,16 @@ def ord_f32(a: np.ndarray) -> np.ndarray:
     u = np.ascontiguousarray(a, np.float32).view(np.uint32).astype(np.int64)
     mag = u & 0x7FFFFFFF
     return np.where(u & 0x80000000, -mag, mag)
+
+
+def ord_f16(a: np.ndarray) -> np.ndarray:
+    u = np.ascontiguousarray(a, np.float16).view(np.uint16).astype(np.int64)
+    mag = u & 0x7FFF
+    return np.where(u & 0x8000, -mag, mag)
+
+
+def f16_ulp_diff(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    return np.abs(ord_f16(a) - ord_f16(b))
 
 
 def f32_ulp_diff(a: np.ndarray, b: np.ndarray) -> np.ndarray:
@@ -105,6 +134,11 @@ FP8_TIE_REL = 2.0 ** -18
 # two products with Kahan's FMA algorithm (within 1.5 ulp of the exact value);
 # the oracle rounds the exact value once (within 0.5 ulp): at most 2 fp32 ulps.
 F32_MAX_ULP = 2
+# fp16 q output: within 1 fp16 ulp; a value differs from the correctly rounded
+# one only where the exact value lies within the kernel's ~1.5 fp32 ulps of an
+# fp16 rounding midpoint, about 3 x 2^-13 = 3.7e-4 of values: bar 10x that.
+F16_MAX_ULP = 1
+F16_MAX_DIFF_FRAC = 4e-3
 
 
 def check_fp8(got: np.ndarray, want: np.ndarray, pre, what: str, abs_slack=None,
@@ -132,6 +166,23 @@ def check_fp8(got: np.ndarray, want: np.ndarray, pre, what: str, abs_slack=None,
     return stats
 
 
+def check_q(got: np.ndarray, want: np.ndarray, what: str, floor: int = 0) -> dict:
+    """A q output of any element type against the oracle's under its type's
+    bar (floor: differing values always allowed, for cases of a few hundred
+    values)."""
+    n = max(want.size, 1)
+    if want.dtype == np.uint16:
+        return check_bf16(got, want, what, max_frac=max(BF16_MAX_DIFF_FRAC, floor / n))
+    if want.dtype == np.float16:
+        d, max_ulp, frac = f16_ulp_diff(got, want), F16_MAX_ULP, max(F16_MAX_DIFF_FRAC, floor / n)
+    else:
+        d, max_ulp, frac = f32_ulp_diff(got, want), F32_MAX_ULP, 1.0
+    stats = dict(max_ulp=int(d.max(initial=0)), diff_frac=float((d != 0).sum() / n), n=d.size)
+    assert stats["max_ulp"] <= max_ulp, f"{what}: {stats}"
+    assert stats["diff_frac"] <= frac, f"{what}: {stats}"
+    return stats
+
+
 def check_bf16(got: np.ndarray, want: np.ndarray, what: str, max_ulp=BF16_MAX_ULP,
                max_frac=BF16_MAX_DIFF_FRAC) -> dict:
     d = bf16_ulp_diff(got, want)
@@ -147,31 +198,34 @@ def check_bf16(got: np.ndarray, want: np.ndarray, what: str, max_ulp=BF16_MAX_UL
 class MlaDevice:
     """Device copies of an MlaCase plus the cache descriptor."""
 
-    def __init__(self, case: workloads.MlaCase, q_layout: str = "dense", q_f32: bool = False):
+    def __init__(self, case: workloads.MlaCase, q_layout: str = "dense", q_f32: bool = False,
+                 q_out_dtype=None):
+        """q_out_dtype: numpy type of the q output (np.uint16 = bf16,
+        np.float16, np.float32); default q's own type (q_f32: np.float32)."""
         import paged_kv_cache_wavefront_amd as pkv
         self.case = case
-        self.q_f32 = q_f32
         T, H, R = case.q.shape
-        if q_f32:
-            if q_layout != "dense":
-                raise ValueError("fp32 q output is tested dense")
-            self.q_in = dev_bf16(case.q)
-            self.q_out = torch.full((T, H, R), float("nan"), dtype=torch.float32, device=DEV)
-        elif q_layout == "dense":
-            self.q_in = dev_bf16(case.q)
-            self.q_out = torch.empty_like(self.q_in)
+        out_np = np.dtype(np.float32 if q_f32 else (case.q.dtype if q_out_dtype is None
+                                                     else q_out_dtype))
+        out_t = TORCH_OF[out_np]
+        if q_layout == "dense":
+            self.q_in = dev_elem(case.q)
+            self.q_out = torch.full((T, H, R), float("nan"), dtype=out_t, device=DEV)
         elif q_layout == "strided":
-            # q and q_out live inside wider buffers: token stride 2*H*R + 8,
-            # head stride 2*R (the rope slice of a [T, H, nope+rope] tensor).
-            big = torch.zeros((T, 2 * H * R + 8), dtype=torch.bfloat16, device=DEV)
+            # q and q_out live inside wider buffers: token stride 2*H*R + 8
+            # (+ 16 for the output), head stride 2*R (the rope slice of a
+            # [T, H, nope+rope] tensor).
+            big = torch.zeros((T, 2 * H * R + 8), dtype=TORCH_OF[case.q.dtype], device=DEV)
             view = big[:, : 2 * H * R].view(T, H, 2 * R)[:, :, R:]
-            view.copy_(dev_bf16(case.q))
+            view.copy_(dev_elem(case.q))
             self.q_in = view
-            big_o = torch.zeros((T, 2 * H * R + 16), dtype=torch.bfloat16, device=DEV)
+            big_o = torch.zeros((T, 2 * H * R + 16), dtype=out_t, device=DEV)
             self.q_out = big_o[:, : 2 * H * R].view(T, H, 2 * R)[:, :, :R]
             self._keep = (big, big_o)
         elif q_layout == "inplace":
-            self.q_in = dev_bf16(case.q)
+            if out_np != case.q.dtype:
+                raise ValueError("in-place q needs one element type")
+            self.q_in = dev_elem(case.q)
             self.q_out = self.q_in
         else:
             raise ValueError(q_layout)
@@ -179,8 +233,8 @@ class MlaDevice:
         self.offsets = dev_u32(case.row_offsets)
         self.cache_lengths = dev_u32(case.cache_lengths)
         self.page_table = dev_u32(case.page_table)
-        self.freqs = dev_f32(case.freqs)
-        self.gamma = dev_bf16(case.gamma)
+        self.freqs = dev_elem(case.freqs)
+        self.gamma = dev_elem(case.gamma)
         if case.cache.dtype == np.uint16:
             self.cache = dev_bf16(case.cache)
             mode, self.scales = pkv.PKV_SCALE_NONE, None
@@ -216,17 +270,19 @@ class MlaDevice:
 
     def results(self):
         torch.cuda.synchronize()
-        q = host_f32(self.q_out) if self.q_f32 else host_bf16(self.q_out)
+        q = host_elem(self.q_out)
         cache = host_bf16(self.cache) if self.case.cache.dtype == np.uint16 else host_u8(self.cache)
         ts = host_f32(self.scales) if self.case.scale_mode == "per_token" else None
         return q, cache, ts, int(self.error_count.item())
 
 
-def oracle_mla(orc, case, q_f32=False):
+def oracle_mla(orc, case, q_f32=False, q_out_dtype=None):
     """Oracle results (q_out, cache, token_scales, pre): ``pre`` holds the
-    binary64 value each fp8 cache code was rounded from (None: bf16 cache)."""
+    binary64 value each fp8 cache code was rounded from (None: bf16 cache).
+    The q output has q_out_dtype (default q's type; q_f32: np.float32)."""
     import contextlib
-    q_out = np.zeros(case.q.shape, np.float32) if q_f32 else np.zeros_like(case.q)
+    out_np = np.float32 if q_f32 else (case.q.dtype if q_out_dtype is None else q_out_dtype)
+    q_out = np.zeros(case.q.shape, out_np)
     cache = case.cache.copy()
     ts = None if case.token_scales is None else case.token_scales.copy()
     probe = orc.fp8_probe(cache) if cache.dtype == np.uint8 else contextlib.nullcontext()
@@ -267,14 +323,8 @@ def compare_mla(case, gpu, orc_res, small_case_floor: int = 0, rows=None) -> dic
 
     def cap(frac, n):
         return max(frac, small_case_floor / max(n, 1))
-    if q_o.dtype == np.float32:
-        d = f32_ulp_diff(q_g, q_o)
-        stats = {"q": dict(max_ulp=int(d.max(initial=0)),
-                           diff_frac=float((d != 0).sum() / max(d.size, 1)), n=d.size)}
-        assert stats["q"]["max_ulp"] <= F32_MAX_ULP, f"fp32 q_rope_output: {stats}"
-    else:
-        stats = {"q": check_bf16(q_g, q_o, "q_rope_output",
-                                 max_frac=cap(BF16_MAX_DIFF_FRAC, q_g.size))}
+    assert q_g.dtype == q_o.dtype, (q_g.dtype, q_o.dtype)
+    stats = {"q": check_q(q_g, q_o, f"q_rope_output ({q_o.dtype})", small_case_floor)}
     rows = written_rows(case) if rows is None else rows
     # untouched rows: bit-exact against the starting pool (and the oracle's)
     assert np.array_equal(cache_g[~rows], case.cache[~rows]), "cache bytes outside new rows changed"
@@ -305,12 +355,12 @@ class QkDevice:
     def __init__(self, case: workloads.QkCase):
         import paged_kv_cache_wavefront_amd as pkv
         self.case = case
-        self.q_in = dev_bf16(case.q)
+        self.q_in = dev_elem(case.q)
         self.q_out = torch.empty_like(self.q_in)
         self.offsets = dev_u32(case.row_offsets)
         self.cache_lengths = dev_u32(case.cache_lengths)
         self.page_table = dev_u32(case.page_table)
-        self.freqs = dev_f32(case.freqs)
+        self.freqs = dev_elem(case.freqs)
         self.pos = None if case.position_ids is None else dev_u32(case.position_ids)
         self.gamma = None if case.gamma is None else dev_bf16(case.gamma)
         self.error_count = torch.zeros(1, dtype=torch.int32, device=DEV)

@@ -99,14 +99,23 @@ def mla_cache(pkv, **kw):
     return pkv.PagedCache(**base)
 
 
+def elem_types(pkv, q=0, q_out=0, freqs=2, gamma=0):
+    """A pkv_elem_types by reference (defaults: bf16 q and output, fp32 freqs,
+    bf16 gamma)."""
+    return ctypes.byref(pkv.ElemTypes(q, q_out, freqs, gamma))
+
+
 def call_mla(pkv, cache, T=16, H=4, R=64, Dn=512, q=FAKE, qo=FAKE, lat=FAKE, qstride=4 * 64,
-             layer=1, batch=2, freqs=FAKE, gamma=FAKE, max_seq=64, qo_dtype=0, qostride=None):
+             layer=1, batch=2, freqs=FAKE, gamma=FAKE, max_seq=64, qo_dtype=None, qostride=None,
+             types=None):
     lib = pkv.library()
     cp = None if cache is None else ctypes.byref(cache)
     qos = qstride if qostride is None else qostride
+    if qo_dtype is not None:
+        types = elem_types(pkv, q_out=qo_dtype)
     return lib.mla_rope_rmsnorm_quant(qo, qos, R, q, qstride, R, lat, Dn + R, FAKE, batch,
                                       T, H, R, Dn, freqs, max_seq, gamma, 1e-6, cp, layer,
-                                      qo_dtype, None)
+                                      types, None)
 
 
 def test_mla_validation(pkv):
@@ -135,7 +144,7 @@ def test_mla_validation(pkv):
     assert call_mla(pkv, mla_cache(pkv), q=FAKE + 8) == ALIGN
     assert call_mla(pkv, mla_cache(pkv), qstride=4 * 64 + 4) == ALIGN
     assert call_mla(pkv, mla_cache(pkv), gamma=FAKE + 2) == ALIGN
-    # q output dtype: bf16 or fp32 (16-byte strides: multiples of 4 fp32)
+    # q output dtype: bf16, fp16 or fp32 (16-byte strides: multiples of 4 fp32)
     assert call_mla(pkv, mla_cache(pkv), qo_dtype=pkv.PKV_DTYPE_FP8_E4M3FN) == DTYPE
     assert call_mla(pkv, mla_cache(pkv), qo_dtype=9) == DTYPE
     assert call_mla(pkv, mla_cache(pkv), T=0, qo_dtype=pkv.PKV_DTYPE_F32,
@@ -146,7 +155,7 @@ def test_mla_validation(pkv):
     big = (1 << 27) + 8
     assert lib.mla_rope_rmsnorm_quant(FAKE, 4 * big, big, FAKE, 4 * big, big, FAKE, 576, FAKE, 2,
                                       16, 4, 64, 512, FAKE, 64, FAKE, 1e-6,
-                                      ctypes.byref(mla_cache(pkv)), 1, 0, None) == UNSUP
+                                      ctypes.byref(mla_cache(pkv)), 1, None, None) == UNSUP
     assert call_mla(pkv, mla_cache(pkv, slot_stride=584)) == ALIGN
     assert call_mla(pkv, mla_cache(pkv, data=FAKE + 8)) == ALIGN
     # nothing to do: accepted without a launch
@@ -158,7 +167,8 @@ def call_mla_inplace(pkv, cache, T=16, H=4, R=64, Dn=512, q=FAKE, qo=FAKE, layer
     lib = pkv.library()
     cp = None if cache is None else ctypes.byref(cache)
     return lib.mla_rope_rmsnorm_inplace(qo, 4 * 64, R, q, 4 * 64, R, FAKE, batch, T, H, R, Dn,
-                                        FAKE, 64, gamma, 1e-6, cp, layer, qo_dtype, None)
+                                        FAKE, 64, gamma, 1e-6, cp, layer,
+                                        elem_types(pkv, q_out=qo_dtype), None)
 
 
 def test_mla_inplace_validation(pkv):
@@ -204,7 +214,7 @@ def call_kv_planned(pkv, cache, plan=FAKE, T=16, gamma=FAKE, glen=128, layer=1):
     lib = pkv.library()
     cp = None if cache is None else ctypes.byref(cache)
     return lib.rms_norm_kv_cache_paged_planned(cp, layer, gamma, glen, 1e-6, 0.0, T, plan, 1, 1,
-                                               None)
+                                               None, None)
 
 
 def test_kv_norm_planned_validation(pkv):
@@ -228,7 +238,7 @@ def test_mla_inplace_planned_validation(pkv):
         cp = None if cache is None else ctypes.byref(cache)
         return lib.mla_rope_rmsnorm_inplace_planned(FAKE, 4 * 64, 64, FAKE, 4 * 64, 64, plan, T,
                                                     4, 64, 512, FAKE, 64, FAKE, 1e-6, cp, layer,
-                                                    0, None)
+                                                    None, None)
     assert call(None) == NULL
     assert call(mla_cache(pkv)) == DTYPE                 # an fp8 cache cannot hold the rows
     assert call(mla_cache(pkv, **bf16), plan=None) == NULL
@@ -282,7 +292,7 @@ def call_noalloc(pkv, cache, T=16, H=4, R=64, Dn=512, offs=FAKE, batch=2, build=
     cp = None if cache is None else ctypes.byref(cache)
     return lib.mla_rope_rmsnorm_quant_noalloc(FAKE, 4 * 64, R, FAKE, 4 * 64, R, FAKE, Dn + R,
                                               offs, batch, T, H, R, Dn, FAKE, 64, FAKE, 1e-6,
-                                              cp, layer, 0, build, None)
+                                              cp, layer, None, build, None)
 
 
 def test_noalloc_validation(pkv):
@@ -307,7 +317,7 @@ def call_mla_planned(pkv, cache, T=16, H=4, R=64, Dn=512, plan=FAKE, q=FAKE, lat
     cp = None if cache is None else ctypes.byref(cache)
     return lib.mla_rope_rmsnorm_quant_planned(FAKE, 4 * 64, R, q, 4 * 64, R, lat, Dn + R, plan,
                                               T, H, R, Dn, FAKE, max_seq, FAKE, 1e-6, cp, layer,
-                                              qo_dtype, None)
+                                              elem_types(pkv, q_out=qo_dtype), None)
 
 
 def test_mla_planned_validation(pkv):
@@ -338,12 +348,12 @@ def kcache(pkv, **kw):
 
 
 def call_qk(pkv, cache, T=16, Hq=32, D=128, gamma=None, cols=0, layer=1, q=FAKE, pos=None,
-            mrope=None):
+            mrope=None, types=None):
     lib = pkv.library()
     cp = None if cache is None else ctypes.byref(cache)
     sec = None if mrope is None else (ctypes.c_uint32 * 3)(*mrope)
     return lib.qk_rope_paged_ragged(FAKE, Hq * D, D, q, Hq * D, D, T, Hq, D, FAKE, 2, cp, layer,
-                                    FAKE, 4096, pos, sec, 1, gamma, cols, 1e-6, None)
+                                    FAKE, 4096, pos, sec, 1, gamma, cols, 1e-6, types, None)
 
 
 def test_qk_validation(pkv):
@@ -377,11 +387,11 @@ def test_qk_validation(pkv):
     assert call_qk(pkv, kcache(pkv), mrope=(16, 24, 24), pos=FAKE, T=0) == OK
 
 
-def call_norm(pkv, cache, gamma_len=128, per_head=1, T=16, gamma=FAKE):
+def call_norm(pkv, cache, gamma_len=128, per_head=1, T=16, gamma=FAKE, types=None):
     lib = pkv.library()
     cp = None if cache is None else ctypes.byref(cache)
     return lib.rms_norm_kv_cache_paged(cp, 1, gamma, gamma_len, 1e-6, 0.0, T, FAKE, 2,
-                                       per_head, 1, None)
+                                       per_head, 1, types, None)
 
 
 def test_kv_norm_validation(pkv):
@@ -410,7 +420,56 @@ def test_kv_norm_validation(pkv):
     lib = pkv.library()
     c8 = kcache(pkv, scales=FAKE, **fp8)
     assert lib.rms_norm_kv_cache_paged(ctypes.byref(c8), 1, FAKE, 128, 1e-6, 0.0, 16, FAKE, 2,
-                                       1, 0, None) == UNSUP                # fp8 needs mbc
+                                       1, 0, None, None) == UNSUP          # fp8 needs mbc
+
+
+def test_element_types_validation(pkv):
+    """pkv_elem_types: the accepted q / q-output pairs, freqs and gamma types
+    of each entry point, and PKV_ERR_DTYPE for every other code (checked
+    before anything else about the call, so T = 0 calls show it)."""
+    BF, E8, F, H = pkv.PKV_DTYPE_BF16, pkv.PKV_DTYPE_FP8_E4M3FN, pkv.PKV_DTYPE_F32, pkv.PKV_DTYPE_F16
+    for q in (BF, H):
+        for qo in (BF, H, F):
+            for fr in (BF, H, F):
+                for g in (BF, H, F):
+                    t = elem_types(pkv, q, qo, fr, g)
+                    assert call_mla(pkv, mla_cache(pkv), T=0, types=t) == OK
+    for bad in ((F, BF, F, BF), (E8, BF, F, BF), (BF, E8, F, BF), (BF, BF, E8, BF),
+                (BF, BF, F, E8), (-1, BF, F, BF), (BF, BF, 5, BF), (BF, BF, F, 4)):
+        assert call_mla(pkv, mla_cache(pkv), T=0, types=elem_types(pkv, *bad)) == DTYPE
+    # fp16 output rows: strides in multiples of 8 elements
+    assert call_mla(pkv, mla_cache(pkv), T=0, types=elem_types(pkv, q_out=H),
+                    qostride=4 * 64 + 4) == OK
+    assert call_mla(pkv, mla_cache(pkv), types=elem_types(pkv, q_out=H),
+                    qostride=4 * 64 + 4) == ALIGN
+    # Q/K RoPE: q and its output one 16-bit type; a K-norm gamma bf16
+    for q in (BF, H):
+        for fr in (BF, H, F):
+            assert call_qk(pkv, kcache(pkv), T=0, types=elem_types(pkv, q, q, fr)) == OK
+    assert call_qk(pkv, kcache(pkv), T=0, types=elem_types(pkv, H, BF)) == DTYPE
+    assert call_qk(pkv, kcache(pkv), T=0, types=elem_types(pkv, F, F)) == DTYPE
+    assert call_qk(pkv, kcache(pkv), T=0, types=elem_types(pkv, freqs=E8)) == DTYPE
+    assert call_qk(pkv, kcache(pkv), T=0, types=elem_types(pkv, gamma=F)) == OK
+    assert call_qk(pkv, kcache(pkv), T=0, gamma=FAKE, cols=128,
+                   types=elem_types(pkv, gamma=F)) == DTYPE
+    # K-cache norm: any of the three gamma types
+    for g in (BF, H, F):
+        assert call_norm(pkv, kcache(pkv), T=0, types=elem_types(pkv, gamma=g)) == OK
+    assert call_norm(pkv, kcache(pkv), T=0, types=elem_types(pkv, gamma=E8)) == DTYPE
+
+
+def test_binding_element_type_codes(pkv):
+    """The binding's pkv_elem_types from tensor dtypes: bf16, fp16, fp32
+    codes, the defaults for an absent tensor, -1 (refused by the library)
+    for any other dtype."""
+    import torch
+    t = pkv._types(torch.zeros(1, dtype=torch.float16), torch.zeros(1, dtype=torch.float32),
+                   torch.zeros(1, dtype=torch.bfloat16), torch.zeros(1, dtype=torch.int16))
+    assert (t.q, t.q_out, t.freqs, t.gamma) == (pkv.PKV_DTYPE_F16, pkv.PKV_DTYPE_F32,
+                                                pkv.PKV_DTYPE_BF16, -1)
+    d = pkv._types()
+    assert (d.q, d.q_out, d.freqs, d.gamma) == (pkv.PKV_DTYPE_BF16, pkv.PKV_DTYPE_BF16,
+                                                pkv.PKV_DTYPE_F32, pkv.PKV_DTYPE_BF16)
 
 
 def call_gather(pkv, cache, out_dtype=None, stride=576, rows=32, out=FAKE, oscales=FAKE,
@@ -472,36 +531,54 @@ def test_headers_compile_as_c_and_cxx(tmp_path):
     """The public headers are plain C (C99) and C++ (17), warning-free, and
     declare the entry points with the argument lists the binding uses."""
     src = tmp_path / "use.c"
+    T = "const pkv_elem_types*"
     src.write_text('#include <string.h>\n#include "pkv.h"\n#include "pkv_bench.h"\n'
                    "int main(void) {\n"
                    "  pkv_paged_cache c;\n"
                    "  memset(&c, 0, sizeof c);\n"
-                   "  (void)c;\n"
+                   "  pkv_elem_types t = {PKV_DTYPE_F16, PKV_DTYPE_F32, PKV_DTYPE_BF16,"
+                   " PKV_DTYPE_F16};\n"
+                   "  (void)c; (void)t;\n"
                    "  int (*f1)(void*, int64_t, int64_t, const void*, int64_t, int64_t, const void*,"
                    " int64_t, const uint32_t*, uint32_t, uint32_t, uint32_t, uint32_t, uint32_t,"
-                   " const float*, uint32_t, const void*, float, const pkv_paged_cache*, uint32_t,"
-                   " int32_t, void*) = mla_rope_rmsnorm_quant;\n"
+                   " const void*, uint32_t, const void*, float, const pkv_paged_cache*, uint32_t,"
+                   f" {T}, void*) = mla_rope_rmsnorm_quant;\n"
+                   "  int (*f10)(void*, int64_t, int64_t, const void*, int64_t, int64_t,"
+                   " const uint32_t*, uint32_t, uint32_t, uint32_t, uint32_t, uint32_t,"
+                   " const void*, uint32_t, const void*, float, const pkv_paged_cache*, uint32_t,"
+                   f" {T}, void*) = mla_rope_rmsnorm_inplace;\n"
                    "  const char* (*f2)(int) = pkv_status_string;\n"
                    "  int (*f4)(uint32_t*, const uint32_t*, uint32_t, uint32_t,"
                    " const pkv_paged_cache*, void*) = pkv_token_plan;\n"
                    "  int (*f5)(void*, int64_t, int64_t, const void*, int64_t, int64_t,"
                    " const void*, int64_t, const uint32_t*, uint32_t, uint32_t, uint32_t,"
-                   " uint32_t, const float*, uint32_t, const void*, float,"
-                   " const pkv_paged_cache*, uint32_t, int32_t, void*) ="
+                   " uint32_t, const void*, uint32_t, const void*, float,"
+                   f" const pkv_paged_cache*, uint32_t, {T}, void*) ="
                    " mla_rope_rmsnorm_quant_planned;\n"
                    "  int (*f6)(const pkv_paged_cache*, uint32_t, const void*, uint32_t, float,"
-                   " float, uint32_t, const uint32_t*, int, int, void*) ="
+                   f" float, uint32_t, const uint32_t*, int, int, {T}, void*) ="
                    " rms_norm_kv_cache_paged_planned;\n"
+                   "  int (*f11)(const pkv_paged_cache*, uint32_t, const void*, uint32_t, float,"
+                   f" float, uint32_t, const uint32_t*, uint32_t, int, int, {T}, void*) ="
+                   " rms_norm_kv_cache_paged;\n"
+                   "  int (*f12)(void*, int64_t, int64_t, const void*, int64_t, int64_t, uint32_t,"
+                   " uint32_t, uint32_t, const uint32_t*, uint32_t, const pkv_paged_cache*,"
+                   " uint32_t, const void*, uint32_t, const uint32_t*, const uint32_t*, int,"
+                   f" const void*, uint32_t, float, {T}, void*) = qk_rope_paged_ragged;\n"
+                   "  int (*f13)(void*, int32_t, int64_t, float*, const float*, const uint32_t*,"
+                   " uint32_t, uint32_t, const pkv_paged_cache*, uint32_t, void*) ="
+                   " mla_gather_latent_paged;\n"
                    "  int (*f7)(void*, int64_t, int64_t, const void*, int64_t, int64_t,"
-                   " const uint32_t*, uint32_t, uint32_t, uint32_t, uint32_t, const float*,"
-                   " uint32_t, const void*, float, const pkv_paged_cache*, uint32_t, int32_t,"
+                   " const uint32_t*, uint32_t, uint32_t, uint32_t, uint32_t, const void*,"
+                   f" uint32_t, const void*, float, const pkv_paged_cache*, uint32_t, {T},"
                    " void*) = mla_rope_rmsnorm_inplace_planned;\n"
                    "  int (*f9)(void*, int64_t, int64_t, const void*, int64_t, int64_t,"
                    " const void*, int64_t, const uint32_t*, uint32_t, uint32_t, uint32_t,"
-                   " uint32_t, uint32_t, const float*, uint32_t, const void*, float,"
-                   " const pkv_paged_cache*, uint32_t, int32_t, int, void*) ="
+                   " uint32_t, uint32_t, const void*, uint32_t, const void*, float,"
+                   f" const pkv_paged_cache*, uint32_t, {T}, int, void*) ="
                    " mla_rope_rmsnorm_quant_noalloc;\n"
-                   "  (void)f4; (void)f5; (void)f6; (void)f7; (void)f9;\n"
+                   "  (void)f4; (void)f5; (void)f6; (void)f7; (void)f9; (void)f10; (void)f11;\n"
+                   "  (void)f12; (void)f13;\n"
                    "  int (*f3)(const void*, void*, uint64_t, uint32_t, void*) = pkv_stream_copy;\n"
                    "  int (*f8)(const void*, uint64_t, void*, uint64_t, uint32_t, void*) ="
                    " pkv_stream_mix;\n"

@@ -130,8 +130,8 @@ def test_other_dims(orc, R, Dn, mode):
 @pytest.mark.parametrize("R,Dn,H", [(32, 256, 128), (128, 512, 16)])
 def test_other_dims_prefill_shape(orc, R, Dn, H):
     """A prefill-shaped batch (8 requests of U{512..4096} tokens, about 17k
-    tokens) at other widths: the persistent launch (more work items than
-    persistent waves) at rope_dim 32 and 128."""
+    tokens) at other widths: a grid of many thousand waves at rope_dim 32
+    (two head chunks per token) and 128."""
     rng = workloads.make_rng(4300 + R)
     new = rng.integers(512, 4096, size=8, endpoint=True)
     case = workloads.build_mla(f"mla_prefill_r{R}_d{Dn}", 4300 + R, new, np.zeros(8, np.int64),
@@ -167,10 +167,10 @@ def test_other_dims_inplace_and_planned(orc, R, Dn):
          f"{gh.compare_mla(fcase, fdev.results(), gh.oracle_mla(orc, fcase))}")
 
 
-def test_persistent_launch_head_chunks(orc):
-    """More work items than persistent waves with three head chunks per token
-    (80 heads of 64): the persistent grid is a whole number of token's worth
-    of chunks, every item is taken once."""
+def test_three_head_chunks_per_token(orc):
+    """Three head chunks per token (80 heads of 64: 32 + 32 + a masked 16),
+    over more than 4096 work items: every (token, chunk) item is written once
+    and only chunk 0 stores the latent row."""
     rng = workloads.make_rng(4600)
     new = rng.integers(200, 700, size=6, endpoint=True)
     prior = rng.integers(0, 100, size=6, endpoint=True)

@@ -134,11 +134,11 @@ def run_qk_fp8(orc, case, with_norm):
     _say(f"[qk8] case={case.name} T={case.T} mode={case.k_scale_mode} norm={with_norm}")
     dev = gh.QkDevice(case)
     dev.rope(with_norm)
-    q = gh.host_bf16(dev.q_out)
+    q = gh.host_elem(dev.q_out)
     k, ks = dev.k_host()
     assert int(dev.error_count.item()) == 0
     q_o, k_o, ks_o, pre = oracle_qk(orc, case, with_norm, with_scales=True)
-    stats = {"q": gh.check_bf16(q, q_o, "q"),
+    stats = {"q": gh.check_q(q, q_o, f"q ({q_o.dtype})"),
              "k": check_fp8_k(case, k, ks, k_o, ks_o, pre, "k",
                               case.gamma.size if with_norm else None)}
     _say(f"[qk8] {case.name}: {stats}")
@@ -393,11 +393,11 @@ def run_qk(orc, case, with_norm):
          f"pos_ids={case.position_ids is not None} norm={with_norm}")
     dev = gh.QkDevice(case)
     dev.rope(with_norm)
-    q = gh.host_bf16(dev.q_out)
+    q = gh.host_elem(dev.q_out)
     k, _ = dev.k_host()
     assert int(dev.error_count.item()) == 0
     q_o, k_o = oracle_qk(orc, case, with_norm)
-    stats = {"q": gh.check_bf16(q, q_o, "q")}
+    stats = {"q": gh.check_q(q, q_o, f"q ({q_o.dtype})")}
     stats["k"] = check_k_rows(case, k, k_o, "k", case.gamma.size if with_norm else None)
     _say(f"[qk] {case.name}: {stats}")
     return q, k

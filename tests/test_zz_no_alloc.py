@@ -94,11 +94,11 @@ def test_noalloc_refusals():
     st = lib.mla_rope_rmsnorm_quant_noalloc(
         dev.q_out.data_ptr(), 0, 64, dev.q_in.data_ptr(), 0, 64, dev.latent.data_ptr(), 576,
         dev.offsets.data_ptr(), 2, (1 << 18) + 1, 8, 64, 512, dev.freqs.data_ptr(), 64,
-        dev.gamma.data_ptr(), 1e-6, dev.desc, 1, 0, 1, None)
+        dev.gamma.data_ptr(), 1e-6, dev.desc, 1, None, 1, None)
     assert st == 5
     # zero tokens: nothing enqueued
     st = lib.mla_rope_rmsnorm_quant_noalloc(
         dev.q_out.data_ptr(), 0, 64, dev.q_in.data_ptr(), 0, 64, dev.latent.data_ptr(), 576,
         dev.offsets.data_ptr(), 2, 0, 8, 64, 512, dev.freqs.data_ptr(), 64,
-        dev.gamma.data_ptr(), 1e-6, dev.desc, 1, 0, 1, None)
+        dev.gamma.data_ptr(), 1e-6, dev.desc, 1, None, 1, None)
     assert st == 0
