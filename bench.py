@@ -12,17 +12,24 @@ writes at least 1 GiB of distinct memory, so no step rewrites lines the
 previous one left dirty in the Infinity Cache (``buffer_rotation`` names the
 sets).  Also reported: 20 isolated launches after a 512 MiB read that
 flushes the caches (``cold_us_p10_p50_p90``); a plain streaming copy timed in
-the same run (``measured_copy``); and (``siblings``) the other workloads and
-entry points, each timed the same way -- MLA decode (256 x 1 token, 128
-heads), mixed prefill + decode with per-token scales (16 heads), both of them
-again placed by a token plan built once before the timed launches
-(mla_rope_rmsnorm_quant_planned; the plan build's own time beside them), the same
-prefill batch in place on a bf16 latent cache (mla_rope_rmsnorm_inplace), the
-Llama-shaped paged-ragged Q/K RoPE with fused per-head K norm, the in-place
-K-cache RMSNorm (also placed by a token plan) and the paged latent gather.
+the same run (``measured_copy``); a stream of the workload's own read and
+written bytes, rotated and timed the same way (``matched_stream``, with the
+workload's fraction of it in ``pct_of_matched_stream``); the cost of an empty
+launch on the workload's grid (``launch_floor_us``); and (``siblings``) the
+other workloads and entry points, each timed the same way with the same
+fields -- MLA decode (256 x 1 token, 128 heads), mixed prefill + decode with
+per-token scales (16 heads), both of them again placed by a token plan built
+once before the timed launches (mla_rope_rmsnorm_quant_planned; the plan
+build's own time beside them, and seven alternating repetitions against the
+batch form in ``vs_batch_form_us``), the same prefill batch in place on a
+bf16 latent cache (mla_rope_rmsnorm_inplace), the Llama-shaped paged-ragged
+Q/K RoPE with fused per-head K norm, the in-place K-cache RMSNorm (also placed
+by a token plan) and the paged latent gather.
 
-With the CPU baseline (the oracle on the same inputs, single-threaded and on
-N host threads) the line also carries ``parity``: one launch of the timed
+``cpu_baseline`` is the oracle on the same inputs on N host threads (N = the
+cores in the process's affinity mask, at most the 16 a GPU's share of the
+host holds), checked bit for bit against a single-threaded run whose rate is
+reported beside it; the line also carries ``parity``: one launch of the timed
 entry point compared with the oracle's outputs of that run.
 
 ``--calibrate-copy`` runs a plain elementwise copy of known size instead (the

@@ -22,9 +22,9 @@
 //   address chain, which takes two dependent steps ({offsets, cache
 //   lengths}, then {freqs row, page-table entry}) and hides behind the bulk
 //   traffic.
-// * The 16 cos/sin floats a lane needs sit contiguously in the freqs row and
-//   are the same for every head: one 64-byte load per lane per token, kept in
-//   registers.
+// * The 16 cos/sin values a lane needs sit contiguously in the freqs row and
+//   are the same for every head: one 64-byte load per lane per token (32
+//   bytes for a 16-bit table), kept in registers.
 // * The head-chunk-0 wave of a token also owns its latent row: lane l holds
 //   non-rope values 8l..8l+7 (lanes below kv_norm_dim / 8) and rope-tail
 //   value l (and l + 64 for rope_dim 128): one tail value per lane instead
@@ -35,10 +35,16 @@
 //   per-token amax) reduce across the wave with DPP inside rows and readlane
 //   across rows; the sum of squares is reduced while the second step of the
 //   address chain is in flight.  The non-rope value is formed as
-//   (x * gamma) * (r / scale): x * gamma is exact in fp32 (two 8-bit
-//   significands).  The row is converted to fp8 in registers (clamp to
+//   (x * gamma) * (r / scale): x * gamma is exact in fp32 for a bf16 or fp16
+//   gamma (8 + 8 or 8 + 11 significant bits).  The row is converted to fp8 in registers (clamp to
 //   +-448, then hardware round-to-nearest-even) and written with 8-byte
 //   non-temporal stores.
+// * Element types ("mla_fused_rope_rmsnorm_quantization", Parameters: dtype,
+//   out_rope_dtype, freq_dtype, gamma_dtype): q in bf16 or fp16 and
+//   q_rope_output in bf16, fp16 or fp32 are a template pair (QIO); freqs_cis
+//   and gamma in fp32, bf16 or fp16 widen exactly to fp32 behind uniform
+//   branches that only the GT instances carry, so that the default fp32 freqs
+//   and bf16 gamma run without them.
 // * Planned form: with a token plan (token_plan.hip) each wave reads its
 //   token's (page, offset, position, placed) entry with one scalar 16-byte
 //   load instead of the two-step chain; the entry is checked against the
