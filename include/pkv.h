@@ -43,9 +43,11 @@
  *
  * Conventions shared by all entry points
  * --------------------------------------
- * Pointers are DEVICE pointers unless marked (host).  Element types: bf16 is
- * stored as its 16-bit pattern, fp8 as its byte; "stride" arguments count
- * elements, not bytes, and the innermost dimension is always contiguous.
+ * Pointers are DEVICE pointers unless marked (host).  Element types: bf16 and
+ * fp16 are stored as their 16-bit patterns, fp8 as its byte; which type a q,
+ * freqs_cis or gamma array holds is given by the call's pkv_elem_types (NULL:
+ * the defaults); "stride" arguments count elements, not bytes, and the
+ * innermost dimension is always contiguous.
  *
  * Ragged batch: input_row_offsets[0..batch] (device, u32) is non-decreasing
  * with input_row_offsets[0] = 0 and input_row_offsets[batch] = total tokens;
@@ -56,8 +58,9 @@
  * at offset s % page_size.  Without explicit position ids the token's RoPE
  * position equals its slot.
  *
- * freqs_cis: [max_seq_len][dim] fp32, row p holds for pair i the cosine in
- * column 2i and the sine in column 2i+1 of the angle p * theta_i.
+ * freqs_cis: [max_seq_len][dim] (fp32 unless the call's types say bf16 or
+ * fp16), row p holds for pair i the cosine in column 2i and the sine in
+ * column 2i+1 of the angle p * theta_i.
  *
  * Ownership: the caller allocates and frees every buffer.  The library
  * allocates nothing, keeps no state between calls (except the plan array of
