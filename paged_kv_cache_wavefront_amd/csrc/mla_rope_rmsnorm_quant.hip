@@ -233,7 +233,7 @@ __device__ __forceinline__ float latent_rms(const uint4& xn, const Gamma8& gm, i
     xg[k] *= g8[k];
   }
   ss = wave_sum(ss);
-  return 1.0f / sqrtf(ss * inv_dn + epsilon);
+  return rsqrt_hw(ss * inv_dn + epsilon);
 }
 
 // The loads of one work item that need only the item's index: its q chunks,
@@ -408,7 +408,7 @@ __device__ __forceinline__ void finish_item(const MlaArgs& a, uint32_t t, uint32
   } else {
     float inv;
     if constexpr (MODE == MlaOut::Fp8PerTensor) {
-      inv = 1.0f / *a.tensor_scale;
+      inv = rcp_hw(*a.tensor_scale);
     } else {
       // max |y| over the row: the non-rope part scales monotonically by r
       // (lanes past the non-rope chunks hold zeros), so the lane's largest
@@ -420,7 +420,7 @@ __device__ __forceinline__ void finish_item(const MlaArgs& a, uint32_t t, uint32
       if (tl.active) am = fmaxf(am, fmaxf(fabsf(tv[0]), fabsf(tv[1])));
       am = wave_max(am);
       const float st = am / 448.0f;
-      inv = st > 0.0f ? 1.0f / st : 0.0f;
+      inv = st > 0.0f ? rcp_hw(st) : 0.0f;
       if (lane == 0)
         a.token_scales[((int64_t)ps.page * cv.page_size + ps.offset) * cv.num_heads] = st;
     }

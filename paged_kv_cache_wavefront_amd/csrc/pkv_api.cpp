@@ -398,6 +398,7 @@ int qk_rope_paged_ragged(void* q_out, int64_t qo_tok_stride, int64_t qo_head_str
   }
   a.k_gamma = static_cast<const uint16_t*>(k_norm_gamma);
   a.k_norm_cols = k_norm_gamma ? k_norm_cols : 0;
+  a.inv_norm_cols = k_norm_gamma ? (float)(1.0 / (double)k_norm_cols) : 0.0f;
   a.epsilon = epsilon;
   a.k_scales = k_scales_of(k_cache, layer_idx, km);
   a.cache = view;
@@ -444,6 +445,8 @@ int kv_norm_entry(const pkv_paged_cache* k_cache, uint32_t layer_idx, const void
   a.gamma = gamma;
   a.gamma_type = gamma_type;
   a.gamma_len = gamma_len;
+  a.inv_cols = (float)(1.0 / (double)gamma_len);
+  a.inv_token_cols = (float)(1.0 / ((double)gamma_len * (double)k_cache->num_heads));
   a.per_head = per_head_norm != 0;
   a.epsilon = epsilon;
   a.weight_offset = weight_offset;

@@ -108,6 +108,7 @@ struct QkArgs {
   uint32_t mrope_end0, mrope_end1;  // pairs [0,end0) temporal, [end0,end1) height, rest width
   const uint16_t* k_gamma;       // may be null
   uint32_t k_norm_cols;
+  float inv_norm_cols;           // 1 / k_norm_cols, rounded to fp32 (0 without a norm)
   float epsilon;
   float* k_scales;               // fp8 K: tensor scale [1] or this layer's per-token scales
   CacheView cache;               // K cache
@@ -125,6 +126,8 @@ struct KvNormArgs {
   const void* gamma;             // [gamma_len] of gamma_type
   int gamma_type;                // ElemType
   uint32_t gamma_len;
+  float inv_cols;                // 1 / gamma_len, rounded to fp32
+  float inv_token_cols;          // 1 / (gamma_len * heads): the per-token mean
   bool per_head;                 // false: one statistic per token over all heads
   float epsilon, weight_offset;
   float* k_scales;               // fp8 K: tensor scale [1] or this layer's per-token scales

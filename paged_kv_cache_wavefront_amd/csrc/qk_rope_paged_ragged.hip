@@ -293,7 +293,7 @@ __global__ __launch_bounds__(256) void qk_rope_kernel(const QkArgs a) {
   const uint32_t k_off = (uint32_t)EB * (hl * (uint32_t)cv.head_stride + (uint32_t)col);
   const int64_t slot_head0 = ((int64_t)ps.page * cv.page_size + ps.offset) * cv.num_heads;
   float tensor_inv = 1.0f;
-  if constexpr (KM == KMode::Fp8PerTensor) tensor_inv = 1.0f / a.k_scales[0];
+  if constexpr (KM == KMode::Fp8PerTensor) tensor_inv = rcp_hw(a.k_scales[0]);
   for (uint32_t hbase = 0; hbase < cv.num_heads; hbase += HPI) {
     const uint32_t h = hbase + hl;
     const bool valid = h < cv.num_heads && (!Geo::kPadded || role.active);
@@ -330,7 +330,7 @@ __global__ __launch_bounds__(256) void qk_rope_kernel(const QkArgs a) {
         if (col + j < C) ss = fmaf(own[j], own[j], ss);
       ss = group_sum<LP>(ss);
       if constexpr (KM != KMode::Bf16) ss = (ss * ks) * ks;
-      const float r = 1.0f / sqrtf(ss / (float)C + a.epsilon);
+      const float r = rsqrt_hw(ss * a.inv_norm_cols + a.epsilon);
       const float kr = ks * r;
       float pre_own[8], pre_par[8], post[8];
 #pragma unroll
@@ -358,7 +358,7 @@ __global__ __launch_bounds__(256) void qk_rope_kernel(const QkArgs a) {
         for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(own[j]));
         am = group_max<LP>(am);
         const float st = am / 448.0f;
-        inv = st > 0.0f ? 1.0f / st : 0.0f;
+        inv = st > 0.0f ? rcp_hw(st) : 0.0f;
         if (valid && role.k == 0) a.k_scales[slot_head0 + h] = st;
       }
 #pragma unroll

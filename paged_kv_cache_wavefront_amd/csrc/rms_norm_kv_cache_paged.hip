@@ -100,7 +100,7 @@ __global__ __launch_bounds__(256) void kv_norm_kernel(const KvNormArgs a) {
   float tensor_scale = 1.0f, tensor_inv = 1.0f;
   if constexpr (KM == KMode::Fp8PerTensor) {
     tensor_scale = a.k_scales[0];
-    tensor_inv = 1.0f / tensor_scale;
+    tensor_inv = rcp_hw(tensor_scale);
   }
   // head groups of HPI heads, kMaxIter groups at a time
   const uint32_t nit = (cv.num_heads + HPI - 1) / HPI;
@@ -133,7 +133,7 @@ __global__ __launch_bounds__(256) void kv_norm_kernel(const KvNormArgs a) {
       for (int k = 0; k < 8; ++k)
         if (col0 + k < C) ss_all = fmaf(y[k], y[k], ss_all);
     }
-    r_presum = 1.0f / sqrtf(wave_sum(ss_all) / (float)(C * cv.num_heads) + a.epsilon);
+    r_presum = rsqrt_hw(wave_sum(ss_all) * a.inv_token_cols + a.epsilon);
   }
   for (uint32_t base = 0; base < nit; base += kMaxIter) {
     // phase 1: load the chunk's heads this lane serves, sums of squares
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(256) void kv_norm_kernel(const KvNormArgs a) {
         if (col0 + k < C) ss = fmaf(x[it][k], x[it][k], ss);
       if constexpr (PER_HEAD) {
         ss = group_sum<LP>(ss);
-        rh[it] = 1.0f / sqrtf(ss / (float)C + a.epsilon);
+        rh[it] = rsqrt_hw(ss * a.inv_cols + a.epsilon);
       } else {
         ss_token += ss;
       }
@@ -174,7 +174,7 @@ __global__ __launch_bounds__(256) void kv_norm_kernel(const KvNormArgs a) {
     float r_token = r_presum;
     if constexpr (!PER_HEAD) {
       if (!presum)
-        r_token = 1.0f / sqrtf(wave_sum(ss_token) / (float)(C * cv.num_heads) + a.epsilon);
+        r_token = rsqrt_hw(wave_sum(ss_token) * a.inv_token_cols + a.epsilon);
     }
 
     // phase 2: normalise, re-encode, store
@@ -214,7 +214,7 @@ __global__ __launch_bounds__(256) void kv_norm_kernel(const KvNormArgs a) {
           for (int k = 0; k < 8; ++k) am = fmaxf(am, fabsf(v[k]));
           am = group_max<LP>(am);
           const float st = am / 448.0f;
-          inv = st > 0.0f ? 1.0f / st : 0.0f;
+          inv = st > 0.0f ? rcp_hw(st) : 0.0f;
           if (valid && m == 0) a.k_scales[slot_head0 + h] = st;
         }
 #pragma unroll

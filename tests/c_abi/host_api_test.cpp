@@ -465,7 +465,7 @@ int main() {
     EXPECT(g_qk.freq_type == PKV_DTYPE_F32);
     EXPECT(g_qk.chunks == 3);                                      // 40 heads, 16 per wave
     EXPECT(g_qk.mrope && g_qk.mrope_end0 == 16 && g_qk.mrope_end1 == 40);
-    EXPECT(g_qk.k_norm_cols == 96);
+    EXPECT(g_qk.k_norm_cols == 96 && g_qk.inv_norm_cols == (float)(1.0 / 96));
     EXPECT(g_qk.k_scales == c.scales + 2 * 10 * 8 * 4);
     EXPECT(g_qk.cache.layer_base == static_cast<char*>(c.data) + 2 * c.layer_stride);
     const uint32_t bad[3] = {16, 24, 23};
@@ -494,6 +494,7 @@ int main() {
                                    nullptr) == PKV_OK);
     EXPECT(!g_norm.per_head && !g_norm_mbc && g_norm_mode == KMode::Bf16);
     EXPECT(g_norm.total_tokens == 7 && g_norm.gamma_len == 100 && g_norm.weight_offset == 0.5f);
+    EXPECT(g_norm.inv_cols == (float)(1.0 / 100) && g_norm.inv_token_cols == (float)(1.0 / 800));
     EXPECT(g_norm.head_dim == 128);
     // the per-token statistic over more heads than one register chunk holds
     pkv_paged_cache big = k_cache(PKV_DTYPE_BF16, PKV_SCALE_NONE, 17, 128);
