@@ -60,6 +60,8 @@ COMMON_SOURCES = ("pkv_device.h", "pkv_internal.h")
 KERNEL_OF = {"mla_prefill": "mla_rope_rmsnorm_quant.hip", "mla_decode": "mla_rope_rmsnorm_quant.hip",
              "mla_mixed": "mla_rope_rmsnorm_quant.hip", "mla_tiny": "mla_rope_rmsnorm_quant.hip",
              "mla_prefill_inplace": "mla_rope_rmsnorm_quant.hip",
+             "mla_prefill_f16": "mla_rope_rmsnorm_quant.hip",
+             "qk_generic_f16": "qk_rope_paged_ragged.hip",
              "mla_decode_planned": "mla_rope_rmsnorm_quant.hip",
              "mla_mixed_planned": "mla_rope_rmsnorm_quant.hip",
              "kv_norm_planned": "rms_norm_kv_cache_paged.hip",
@@ -81,15 +83,17 @@ def log(*a):
 # -- algorithmic bytes (what the method must move, read + written) ---------------------
 
 def mla_bytes(case, planned: bool = False) -> int:
-    """q in + q out (2 x H x R x 2) + latent row in (W x 2, from its buffer or,
-    in place, from the cache) + cache row out (W x 1 fp8 / W x 2 bf16, + 4 for
-    a per-token scale) per token; once per launch: freqs rows of the distinct
-    positions (R x 4 each), gamma, offsets, prior lengths, the page-table
+    """q in + q out (H x R x 2 each for bf16 or fp16; the output takes q's
+    type) + latent row in (W x 2, from its buffer or, in place, from the
+    cache) + cache row out (W x 1 fp8 / W x 2 bf16, + 4 for a per-token scale)
+    per token; once per launch: freqs rows of the distinct positions (R
+    values each, 4 or 2 bytes), gamma, offsets, prior lengths, the page-table
     entries read, the per-tensor scale.  Planned: a 16-byte plan entry per
     token replaces the offsets, prior lengths and page-table entries."""
     T, H, R, W = case.T, case.H, case.R, case.latent.shape[1]
     out_b = 2 if case.cache.dtype == np.uint16 else 1
-    per_tok = 2 * H * R * 2 + W * 2 + W * out_b + (4 if case.scale_mode == "per_token" else 0)
+    qb = case.q.itemsize
+    per_tok = 2 * H * R * qb + W * 2 + W * out_b + (4 if case.scale_mode == "per_token" else 0)
     pos = np.concatenate([np.arange(c, c + n) for c, n in
                           zip(case.cache_lengths.astype(np.int64),
                               np.diff(case.row_offsets.astype(np.int64)))]) if T else np.zeros(0)
@@ -98,7 +102,7 @@ def mla_bytes(case, planned: bool = False) -> int:
         zip(case.cache_lengths, np.diff(case.row_offsets.astype(np.int64))))
         for p in range(int(c), int(c) + int(n))})
     chain = 16 * T if planned else (case.B + 1) * 4 + case.B * 4 + 4 * pages_read
-    shared = (len(np.unique(pos)) * R * 4 + case.Dn * 2 + chain
+    shared = (len(np.unique(pos)) * R * case.freqs.itemsize + case.Dn * case.gamma.itemsize + chain
               + (4 if case.scale_mode == "per_tensor" else 0))
     return T * per_tok + shared
 
@@ -118,7 +122,8 @@ def qk_bytes(case, with_norm: bool) -> int:
     row per token; gamma, offsets, prior lengths and page-table entries once."""
     T, Hq, D = case.q.shape
     Hkv = case.k_cache.shape[3]
-    per_tok = 2 * Hq * D * 2 + 2 * Hkv * D * 2 + D * 4 + (4 if case.position_ids is not None else 0)
+    per_tok = (2 * Hq * D * case.q.itemsize + 2 * Hkv * D * 2 + D * case.freqs.itemsize
+               + (4 if case.position_ids is not None else 0))
     shared = (case.B + 1) * 4 + case.B * 4 + T * 4 // case.meta["page_size"] + \
         (case.gamma.size * 2 if with_norm else 0)
     return T * per_tok + shared
@@ -137,10 +142,10 @@ def written_bytes(name: str, case, rows: int = 0) -> int:
     if name.startswith("mla_"):
         T, H, R, W = case.T, case.H, case.R, case.latent.shape[1]
         out_b = 2 if case.cache.dtype == np.uint16 else 1
-        return T * (2 * H * R + W * out_b + (4 if case.scale_mode == "per_token" else 0))
-    if name == "qk_generic":
+        return T * (case.q.itemsize * H * R + W * out_b + (4 if case.scale_mode == "per_token" else 0))
+    if name.startswith("qk_generic"):
         T, Hq, D = case.q.shape
-        return T * (Hq * D * 2 + case.k_cache.shape[3] * D * 2)
+        return T * (Hq * D * case.q.itemsize + case.k_cache.shape[3] * D * 2)
     if name.startswith("kv_norm"):
         return case.T * case.k_cache.shape[3] * 128 * 2
     if name == "gather":
@@ -401,7 +406,7 @@ def grid_blocks(name: str, case, rows: int = 0) -> int:
     if name.startswith("mla_"):
         hpw = 32 if case.H > 16 else 16
         waves = case.T * -(-case.H // hpw)
-    elif name == "qk_generic":
+    elif name.startswith("qk_generic"):
         waves = case.T * -(-int(case.q.shape[1]) // 16)
     elif name.startswith("kv_norm"):
         waves = case.T
@@ -488,7 +493,7 @@ def run_workload(name, steps, warmup):
         label = f"{name} (plan built once, outside the timed launches)"
     elif name.startswith("mla_"):
         case = workloads.NAMED[name]()
-        q_out_bytes = case.q.size * 2
+        q_out_bytes = case.q.nbytes
         written = q_out_bytes + case.T * case.latent.shape[1]
         set_bytes = 2 * q_out_bytes + case.latent.nbytes + case.cache.nbytes
         n = rotation_count(written, set_bytes)
@@ -514,9 +519,9 @@ def run_workload(name, steps, warmup):
             spec = dict(in_place=False, sets=n, rotate_reads=False)
         r = measure(cycle(fns), case.T, mla_bytes(case), steps, warmup)
         label = name
-    elif name == "qk_generic":
-        case = workloads.qk_generic()
-        written = case.q.size * 2 + int(gh.written_k_rows(case).sum()) * case.k_cache[0, 0, 0].nbytes
+    elif name.startswith("qk_generic"):
+        case = workloads.NAMED[name]()
+        written = case.q.nbytes + int(gh.written_k_rows(case).sum()) * case.k_cache[0, 0, 0].nbytes
         set_bytes = 2 * case.q.nbytes + case.k_cache.nbytes
         n = rotation_count(written, set_bytes)
         devs = [gh.QkDevice(case) for _ in range(n)]
@@ -524,7 +529,7 @@ def run_workload(name, steps, warmup):
         how = f"{n} sets of q, q_out and K pool"
         spec = dict(in_place=False, sets=n, rotate_reads=True)
         r = measure(cycle(fns), case.T, qk_bytes(case, True), steps, warmup)
-        label = "qk_generic (interleaved, position ids, fused per-head K norm)"
+        label = f"{name} (interleaved, position ids, fused per-head K norm; Q {case.q.dtype}, freqs {case.freqs.dtype})"
     elif name in ("kv_norm", "kv_norm_planned"):
         planned = name == "kv_norm_planned"
         case = workloads.qk_generic()
@@ -595,7 +600,9 @@ def measure_siblings(main, steps, warmup):
                         ("mla_decode_planned", "mla_rope_rmsnorm_quant_planned"),
                         ("mla_mixed_planned", "mla_rope_rmsnorm_quant_planned"),
                         ("mla_prefill_inplace", "mla_rope_rmsnorm_inplace"),
+                        ("mla_prefill_f16", "mla_rope_rmsnorm_quant"),
                         ("qk_generic", "qk_rope_paged_ragged"),
+                        ("qk_generic_f16", "qk_rope_paged_ragged"),
                         ("kv_norm", "rms_norm_kv_cache_paged"),
                         ("kv_norm_planned", "rms_norm_kv_cache_paged_planned"),
                         ("gather", "mla_gather_latent_paged")):
@@ -746,6 +753,23 @@ def cpu_baseline(case, budget_s=10.0):
     return out, (q_out, cache)
 
 
+ELEM_NAME = {np.dtype(np.uint16): "bf16", np.dtype(np.float16): "fp16", np.dtype(np.float32): "fp32"}
+
+
+def io_dtypes(name: str, case) -> str:
+    """The element types a workload's launch reads and writes."""
+    if name == "gather":
+        return "fp8 e4m3fn cache rows in, bf16 rows out"
+    q, fr = ELEM_NAME[case.q.dtype], ELEM_NAME[case.freqs.dtype]
+    if not name.startswith("mla_"):
+        return f"{q} Q in and out, bf16 K rows in place, {fr} freqs" if name.startswith("qk_") \
+            else "bf16 K rows in place, bf16 gamma"
+    g = ELEM_NAME[case.gamma.dtype]
+    if name == "mla_prefill_inplace":
+        return f"{q} q in and out; bf16 latent rows read and rewritten in the cache; {fr} freqs, {g} gamma"
+    return f"{q} q in and out; bf16 latent in; fp8 e4m3fn cache rows out; {fr} freqs, {g} gamma"
+
+
 def parity_stats(case, oracle_out):
     """One launch of the timed entry point on fresh device copies of the
     workload, compared with the oracle's outputs from the CPU baseline (same
@@ -759,7 +783,7 @@ def parity_stats(case, oracle_out):
     q, cache, _, skipped = dev.results()
     q_o, cache_o = oracle_out
     rows = gh.written_rows(case)
-    dq = gh.bf16_ulp_diff(q, q_o)
+    dq = gh.f16_ulp_diff(q, q_o) if q_o.dtype == np.float16 else gh.bf16_ulp_diff(q, q_o)
     dc = gh.fp8_ulp_diff(cache[rows], cache_o[rows]) if cache.dtype == np.uint8 else \
         gh.bf16_ulp_diff(cache[rows], cache_o[rows])
     return {"q_max_ulp": int(dq.max(initial=0)),
@@ -812,7 +836,8 @@ def main():
     ap.add_argument("--workload", default="mla_prefill",
                     choices=["mla_prefill", "mla_decode", "mla_mixed", "mla_tiny",
                              "mla_prefill_inplace", "mla_decode_planned", "mla_mixed_planned",
-                             "qk_generic", "kv_norm", "kv_norm_planned", "gather"])
+                             "mla_prefill_f16", "qk_generic", "qk_generic_f16", "kv_norm",
+                             "kv_norm_planned", "gather"])
     ap.add_argument("--no-siblings", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
@@ -882,11 +907,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
-        "io_dtypes": ("bf16 q in and out; bf16 latent rows read and rewritten in the cache"
-                      if args.workload == "mla_prefill_inplace"
-                      else "bf16 q and latent in; bf16 q out; fp8 e4m3fn cache rows out" if is_mla
-                      else "bf16 in, bf16 out" if args.workload != "gather"
-                      else "fp8 e4m3fn cache rows in, bf16 rows out"),
+        "io_dtypes": io_dtypes(args.workload, case),
         "data": "synthetic (seeded; DeepSeek-V3-shaped random tensors, no weights)",
         "config": config,
         "effective_GBps": gbps,

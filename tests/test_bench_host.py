@@ -100,3 +100,20 @@ def test_grid_blocks_follow_the_launch_policy():
 def test_cpu_model_names_the_processor():
     name = bench.cpu_model()
     assert name and name != "unknown"
+
+
+def test_typed_workloads_byte_model():
+    """The fp16-q prefill and fp16-Q Q/K siblings move the same q bytes as
+    their bf16 twins; only the freqs rows (bf16: half the bytes) and gamma
+    (fp32: twice) differ, and the written bytes are the same."""
+    a, b = workloads.mla_prefill(), workloads.mla_prefill_f16()
+    R, Dn = a.R, a.Dn
+    pos = len({int(p) for c, n in zip(a.cache_lengths, np.diff(a.row_offsets.astype(np.int64)))
+               for p in range(int(c), int(c) + int(n))})
+    assert bench.mla_bytes(b) - bench.mla_bytes(a) == -pos * R * 2 + Dn * 2
+    assert bench.written_bytes("mla_prefill_f16", b) == bench.written_bytes("mla_prefill", a)
+    assert bench.grid_blocks("mla_prefill_f16", b) == bench.grid_blocks("mla_prefill", a)
+    q, qh = workloads.qk_generic(), workloads.qk_generic_f16()
+    assert bench.qk_bytes(q, True) - bench.qk_bytes(qh, True) == q.T * 128 * 2
+    assert bench.written_bytes("qk_generic_f16", qh) == bench.written_bytes("qk_generic", q)
+    assert "fp16 q" in bench.io_dtypes("mla_prefill_f16", b)

@@ -230,6 +230,18 @@ def mla_prefill(seed: int = 1003) -> MlaCase:
                      rng=rng)
 
 
+def mla_prefill_f16(seed: int = 1003) -> MlaCase:
+    """The prefill batch of :func:`mla_prefill` (same lengths and latent
+    draws) with fp16 q (q_rope and q_rope_output), bf16 freqs_cis and fp32
+    gamma: the element-type variants the MLA page parameterises."""
+    rng = make_rng(seed)
+    new = rng.integers(512, 4096, size=8, endpoint=True)
+    return build_mla("mla_prefill_f16", seed, new, np.zeros(8, np.int64), H=128,
+                     page_size=128, max_seq_len=16384, spare_pages=16,
+                     latent_sigma=2.0, scale_mode="per_tensor", tensor_scale=0.05,
+                     rng=rng, q_dtype="f16", freq_dtype="bf16", gamma_dtype="f32")
+
+
 def mla_prefill_inplace(seed: int = 1003) -> MlaCase:
     """The DeepSeek-V3-shaped prefill batch of :func:`mla_prefill` over a bf16
     latent cache, for the in-place form (the rows are placed at their slots
@@ -358,11 +370,25 @@ def qk_generic(seed: int = 1005) -> QkCase:
                     rng=rng)
 
 
+def qk_generic_f16(seed: int = 1005) -> QkCase:
+    """The Llama-style batch of :func:`qk_generic` (same lengths, positions and
+    K pool) with fp16 Q and bf16 freqs_cis."""
+    rng = make_rng(seed)
+    new = rng.integers(1, 1024, size=32, endpoint=True)
+    prior = rng.integers(0, 1023, size=32, endpoint=True)
+    return build_qk("qk_generic_f16", seed, new, prior, Hq=32, Hkv=8, D=128,
+                    page_size=16, max_seq_len=131072, theta=500000.0,
+                    interleaved=True, with_position_ids=True, norm_cols=128,
+                    rng=rng, q_dtype="f16", freq_dtype="bf16")
+
+
 NAMED = {
     "mla_tiny": mla_tiny,
     "mla_decode": mla_decode,
     "mla_prefill": mla_prefill,
     "mla_mixed": mla_mixed,
     "mla_prefill_inplace": mla_prefill_inplace,
+    "mla_prefill_f16": mla_prefill_f16,
     "qk_generic": qk_generic,
+    "qk_generic_f16": qk_generic_f16,
 }
