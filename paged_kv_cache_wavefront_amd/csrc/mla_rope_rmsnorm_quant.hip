@@ -192,22 +192,17 @@ __device__ __forceinline__ void rotate_store_q(const uint4 (&q)[NI], const float
   }
 }
 
-// The 8 gamma values of a lane (values 8l..8l+7), raw: one 16-byte chunk of
-// a 16-bit type, or two of fp32.
+// The 8 gamma values of a lane (values 8l..8l+7), raw: two 16-byte chunks of
+// fp32, or one of a 16-bit type (loaded twice: the loads do not depend on
+// the type, so that no wait for them sits under a branch).
 struct Gamma8 {
   uint4 lo, hi;
 };
 
 __device__ __forceinline__ Gamma8 load_gamma8(const void* gamma, int type, int lane) {
-  Gamma8 g{make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
-  if (type == kF32) {
-    const uint4* p = static_cast<const uint4*>(gamma) + 2 * lane;
-    g.lo = load16(p);
-    g.hi = load16(p + 1);
-  } else {
-    g.lo = load16(static_cast<const uint16_t*>(gamma) + 8 * lane);
-  }
-  return g;
+  const bool f32 = type == kF32;
+  const uint4* p = static_cast<const uint4*>(gamma) + (f32 ? 2 * lane : lane);
+  return Gamma8{load16(p), load16(p + (f32 ? 1 : 0))};
 }
 
 // RMSNorm statistic of the latent row's non-rope part (lane l holds values
@@ -316,7 +311,7 @@ __device__ __forceinline__ void finish_item(const MlaArgs& a, uint32_t t, uint32
   float2 tcs;
   {
     const int64_t first = (int64_t)(pos_ok ? ts.slot : 0u) * R;  // row's first element
-    if (freq_type == kF32) {
+    if constexpr (!GT) {
       const float* frow = static_cast<const float*>(a.freqs) + first;
       const float4* fr = reinterpret_cast<const float4*>(frow + 16 * hl.pair_block);
 #pragma unroll
@@ -326,11 +321,35 @@ __device__ __forceinline__ void finish_item(const MlaArgs& a, uint32_t t, uint32
       }
       tcs = *reinterpret_cast<const float2*>(frow + 2 * tl.pair);
     } else {
-      const bool f16 = freq_type == kF16;
-      const uint16_t* frow = static_cast<const uint16_t*>(a.freqs) + first;
-      load_typed<16>(frow + 16 * hl.pair_block, freq_type, cs);
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(frow + 2 * tl.pair);
-      tcs = make_float2(half_of(w, 0, f16), half_of(w, 1, f16));
+      // Any type, with the same loads for each (a load under a branch would
+      // put a wait for it in front of the latent statistic): the lane's 16
+      // values are four 16-byte chunks of fp32, or two of a 16-bit type,
+      // loaded twice; the tail's (cos, sin) two 4-byte words, or one.
+      const bool f32 = freq_type == kF32, f16 = freq_type == kF16;
+      const char* row = static_cast<const char*>(a.freqs) + (f32 ? 4 : 2) * first;
+      const uint4* p = reinterpret_cast<const uint4*>(row + (f32 ? 64 : 32) * hl.pair_block);
+      const uint4 r0 = p[0], r1 = p[1], r2 = p[f32 ? 2 : 0], r3 = p[f32 ? 3 : 1];
+      const uint32_t* tp = reinterpret_cast<const uint32_t*>(row + (f32 ? 8 : 4) * tl.pair);
+      const uint32_t t0 = tp[0], t1 = tp[f32 ? 1 : 0];
+      if (f32) {
+        const uint4 r[4] = {r0, r1, r2, r3};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          cs[4 * i] = __uint_as_float(r[i].x); cs[4 * i + 1] = __uint_as_float(r[i].y);
+          cs[4 * i + 2] = __uint_as_float(r[i].z); cs[4 * i + 3] = __uint_as_float(r[i].w);
+        }
+        tcs = make_float2(__uint_as_float(t0), __uint_as_float(t1));
+      } else {
+        float lo[8], hi[8];
+        unpack8_16(r0, f16, lo);
+        unpack8_16(r1, f16, hi);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          cs[k] = lo[k];
+          cs[8 + k] = hi[k];
+        }
+        tcs = make_float2(half_of(t0, 0, f16), half_of(t0, 1, f16));
+      }
     }
   }
   uint32_t col = 0, page = 0;
