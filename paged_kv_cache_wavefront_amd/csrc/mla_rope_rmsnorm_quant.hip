@@ -461,9 +461,11 @@ __device__ __forceinline__ void finish_item(const MlaArgs& a, uint32_t t, uint32
 template <int R, int NI, MlaOut MODE, QIO X, bool PLANNED, bool GT>
 __global__ __launch_bounds__(256) void mla_kernel(const MlaArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
-  const uint32_t wave = blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
-  const uint32_t t = uniform(wave / a.chunks);
-  const uint32_t chunk = uniform(wave - t * a.chunks);
+  // wave-uniform item index: the division by the head chunks runs on the
+  // scalar unit (a shift for 1, 2 or 4 chunks) instead of on every lane
+  const uint32_t wave = uniform(blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave));
+  const uint32_t t = uniform(udiv_uniform(wave, a.chunks));
+  const uint32_t chunk = wave - t * a.chunks;
   if (t >= a.total_tokens) return;
   ItemLoads<NI> L;
   issue_item<R, NI, MODE, PLANNED>(a, t, chunk, lane, L);

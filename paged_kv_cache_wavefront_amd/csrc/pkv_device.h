@@ -130,13 +130,14 @@ __device__ __forceinline__ void load_typed(const void* p, int type, float (&f)[N
 // ---- fp32 -> FP8 E4M3FN (OCP), saturating, round-to-nearest-even -----------
 // Values are clamped to +-448 (the largest finite E4M3FN value; infinities
 // saturate too) and then converted by v_cvt_pk_fp8_f32, which rounds to
-// nearest even in the OCP format on gfx950; -0 keeps its sign.  A NaN skips
-// the clamp (min / max would replace it by a bound) and converts to the NaN
-// code, so a NaN in a row stays visible in the cache.
+// nearest even in the OCP format on gfx950; -0 keeps its sign.  The clamp is
+// IEEE 754-2019 maximum / minimum (v_maximum3_f32, v_minimum3_f32 on gfx950),
+// which pass a NaN through where fmaxf / fminf would replace it by a bound,
+// so a NaN converts to the NaN code and stays visible in the cache: two
+// instructions per value.
 
 __device__ __forceinline__ float sat448(float v) {
-  const float c = fminf(fmaxf(v, -448.0f), 448.0f);
-  return v != v ? v : c;
+  return __builtin_elementwise_minimum(__builtin_elementwise_maximum(v, -448.0f), 448.0f);
 }
 
 __device__ __forceinline__ uint32_t pack4_fp8(float a, float b, float c, float d) {
@@ -323,6 +324,15 @@ __device__ __forceinline__ uint32_t uniform(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
 }
 
+// n / d for wave-uniform n and d: a shift when d is a power of two (scalar
+// instructions only: the usual case for page sizes and head-chunk counts),
+// else the general division, whose reciprocal estimate runs on the vector
+// unit.
+__device__ __forceinline__ uint32_t udiv_uniform(uint32_t n, uint32_t d) {
+  if ((d & (d - 1)) == 0) return n >> __builtin_ctz(d);
+  return n / d;
+}
+
 // ---- ragged batch and page table -------------------------------------------
 
 // Request owning token t: the number of offsets[1..B] that are <= t (offsets
@@ -402,7 +412,7 @@ struct PageSlot {
 };
 
 __device__ __forceinline__ uint32_t page_column(uint32_t slot, uint32_t page_size) {
-  return slot / page_size;
+  return udiv_uniform(slot, page_size);
 }
 
 __device__ __forceinline__ bool page_of(const uint32_t* __restrict__ page_table,

@@ -194,10 +194,9 @@ __global__ __launch_bounds__(256) void qk_rope_kernel(const QkArgs a) {
   using Geo = Geometry<D, INTER>;
   constexpr int LP = Geo::kLanesPerHead, HPI = Geo::kHeadsPerInstr;
   const int lane = threadIdx.x & (kWave - 1);
-  const uint32_t wave =
-      blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave);
-  const uint32_t t = uniform(wave / a.chunks);
-  const uint32_t chunk = uniform(wave - t * a.chunks);
+  const uint32_t wave = uniform(blockIdx.x * kWavesPerBlock + (threadIdx.x / kWave));
+  const uint32_t t = uniform(udiv_uniform(wave, a.chunks));
+  const uint32_t chunk = wave - t * a.chunks;
   if (t >= a.total_tokens) return;
   const LaneRole<D, INTER> role(lane);
   const uint32_t hl = (uint32_t)(lane / LP);
