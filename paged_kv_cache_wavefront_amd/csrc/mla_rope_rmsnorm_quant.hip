@@ -437,7 +437,7 @@ __device__ __forceinline__ void finish_item(const MlaArgs& a, uint32_t t, uint32
       for (int k = 0; k < 8; ++k) am = fmaxf(am, fabsf(xg[k]));
       am *= r;
       if (tl.active) am = fmaxf(am, fmaxf(fabsf(tv[0]), fabsf(tv[1])));
-      am = wave_max(am);
+      am = wave_max_abs(am);
       const float st = am / 448.0f;
       inv = st > 0.0f ? rcp_hw(st) : 0.0f;
       if (lane == 0)

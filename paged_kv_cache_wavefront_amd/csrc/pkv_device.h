@@ -294,14 +294,19 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Max of |v| over aligned groups of N lanes, a NaN counting as 0 (as fmaxf
+// drops it).  Non-negative floats order like their bit patterns, so each
+// step is one integer max with the DPP operand folded in; a float max would
+// first canonicalise the DPP result (three instructions per step).
 template <int N>
-__device__ __forceinline__ float group_max(float v) {
-  if constexpr (N >= 2) v = fmaxf(v, dpp<kDppXor1>(v));
-  if constexpr (N >= 4) v = fmaxf(v, dpp<kDppXor2>(v));
-  if constexpr (N >= 8) v = fmaxf(v, dpp<kDppHalfMirror>(v));
-  if constexpr (N >= 16) v = fmaxf(v, dpp<kDppMirror>(v));
-  if constexpr (N >= 32) v = fmaxf(v, swizzle<kSwizzleXor16>(v));
-  return v;
+__device__ __forceinline__ float group_max_abs(float v) {
+  uint32_t u = __float_as_uint(fmaxf(fabsf(v), 0.0f));
+  if constexpr (N >= 2) u = max(u, dpp_u32<kDppXor1>(u));
+  if constexpr (N >= 4) u = max(u, dpp_u32<kDppXor2>(u));
+  if constexpr (N >= 8) u = max(u, dpp_u32<kDppHalfMirror>(u));
+  if constexpr (N >= 16) u = max(u, dpp_u32<kDppMirror>(u));
+  if constexpr (N >= 32) u = max(u, swizzle_u32<kSwizzleXor16>(u));
+  return __uint_as_float(u);
 }
 
 __device__ __forceinline__ float lane_value(float v, int lane) {
@@ -314,10 +319,15 @@ __device__ __forceinline__ float wave_sum(float v) {
   return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-  v = group_max<16>(v);
-  return fmaxf(fmaxf(lane_value(v, 0), lane_value(v, 16)),
-               fmaxf(lane_value(v, 32), lane_value(v, 48)));
+// Wave-uniform max of |v| (a NaN counting as 0), the last step on the
+// scalar unit.
+__device__ __forceinline__ float wave_max_abs(float v) {
+  const uint32_t u = __float_as_uint(group_max_abs<16>(v));
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)u, 0);
+  const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)u, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)u, 32);
+  const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)u, 48);
+  return __uint_as_float(max(max(a, b), max(c, d)));
 }
 
 __device__ __forceinline__ uint32_t uniform(uint32_t v) {

@@ -355,7 +355,7 @@ __global__ __launch_bounds__(256) void qk_rope_kernel(const QkArgs a) {
         float am = 0.0f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(own[j]));
-        am = group_max<LP>(am);
+        am = group_max_abs<LP>(am);
         const float st = am / 448.0f;
         inv = st > 0.0f ? rcp_hw(st) : 0.0f;
         if (valid && role.k == 0) a.k_scales[slot_head0 + h] = st;

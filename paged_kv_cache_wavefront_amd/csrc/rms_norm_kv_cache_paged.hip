@@ -212,7 +212,7 @@ __global__ __launch_bounds__(256) void kv_norm_kernel(const KvNormArgs a) {
           float am = 0.0f;
 #pragma unroll
           for (int k = 0; k < 8; ++k) am = fmaxf(am, fabsf(v[k]));
-          am = group_max<LP>(am);
+          am = group_max_abs<LP>(am);
           const float st = am / 448.0f;
           inv = st > 0.0f ? rcp_hw(st) : 0.0f;
           if (valid && m == 0) a.k_scales[slot_head0 + h] = st;
