@@ -60,20 +60,18 @@ __global__ __launch_bounds__(256) void kv_norm_kernel(const KvNormArgs a) {
   const uint32_t col0 = active ? 8 * m : 0;
   const uint32_t C = a.gamma_len;
 
-  // gamma (+ weight_offset) of this lane's columns, loaded before the chain
-  // (bf16, fp16 or fp32 gamma, widened exactly)
-  float g[8];
+  // gamma of this lane's columns (bf16, fp16 or fp32, widened exactly): a
+  // whole chunk is loaded here, before the chain, and unpacked only before
+  // its first use, so that its wait does not hold up the chain's loads
   const int gamma_type = GT ? a.gamma_type : (int)kBf16;
-  if (col0 + 8 <= C) {
-    const int64_t geb = gamma_type == kF32 ? 4 : 2;
-    load_typed<8>(static_cast<const char*>(a.gamma) + geb * col0, gamma_type, g);
-  } else {
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-      g[k] = (col0 + k < C) ? load_elem(a.gamma, col0 + k, gamma_type) : 0.0f;
+  const bool gamma_chunk = col0 + 8 <= C;
+  uint4 g_lo = make_uint4(0, 0, 0, 0), g_hi = make_uint4(0, 0, 0, 0);
+  if (gamma_chunk) {
+    const uint4* gp = reinterpret_cast<const uint4*>(static_cast<const char*>(a.gamma) +
+                                                     (gamma_type == kF32 ? 4 : 2) * col0);
+    g_lo = load16(gp);
+    if (gamma_type == kF32) g_hi = load16(gp + 1);
   }
-#pragma unroll
-  for (int k = 0; k < 8; ++k) g[k] += a.weight_offset;
 
   const CacheView& cv = a.cache;
   PageSlot ps{};
@@ -135,6 +133,25 @@ __global__ __launch_bounds__(256) void kv_norm_kernel(const KvNormArgs a) {
     }
     r_presum = rsqrt_hw(wave_sum(ss_all) * a.inv_token_cols + a.epsilon);
   }
+  // gamma + weight_offset: the chunk loaded above, or a partial chunk (the
+  // columns past gamma_len take 0) element by element
+  float g[8];
+  if (gamma_chunk) {
+    if (gamma_type == kF32) {
+      const uint32_t w[8] = {g_lo.x, g_lo.y, g_lo.z, g_lo.w, g_hi.x, g_hi.y, g_hi.z, g_hi.w};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) g[k] = __uint_as_float(w[k]);
+    } else {
+      unpack8_16(g_lo, gamma_type == kF16, g);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      g[k] = (col0 + k < C) ? load_elem(a.gamma, col0 + k, gamma_type) : 0.0f;
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) g[k] += a.weight_offset;
+
   for (uint32_t base = 0; base < nit; base += kMaxIter) {
     // phase 1: load the chunk's heads this lane serves, sums of squares
     float x[kMaxIter][8], rh[kMaxIter];
