@@ -102,12 +102,17 @@ __device__ __forceinline__ uint32_t load2_stream(const uint16_t* p) {
   return __builtin_nontemporal_load(p);
 }
 
+// The lane's tail values as loaded: value l in lo, and for rope_dim 128 value
+// l + 64 in hi (joined into one word only where they are used).
 template <int R>
-__device__ __forceinline__ uint32_t load_tail(const uint16_t* tail_row, int lane) {
-  if constexpr (R == 128)
-    return load2_stream(tail_row + lane) | (load2_stream(tail_row + 64 + lane) << 16);
-  else
-    return lane < R ? load2_stream(tail_row + lane) : 0u;
+__device__ __forceinline__ void load_tail(const uint16_t* tail_row, int lane, uint32_t& lo,
+                                          uint32_t& hi) {
+  if constexpr (R == 128) {
+    lo = load2_stream(tail_row + lane);
+    hi = load2_stream(tail_row + 64 + lane);
+  } else {
+    lo = lane < R ? load2_stream(tail_row + lane) : 0u;
+  }
 }
 
 // Rotated tail values of this lane (tv[1] only for rope_dim 128); tcs is the
@@ -238,7 +243,7 @@ template <int NI>
 struct ItemLoads {
   uint4 q[NI];
   uint4 xn;
-  uint32_t tail;
+  uint32_t tail, tail_hi;  // the rope tail as load_tail leaves it
   uint4 pe;
 };
 
@@ -258,12 +263,12 @@ __device__ __forceinline__ void issue_item(const MlaArgs& a, uint32_t t, uint32_
   else
     load_q<NI, HPI, true>(L.q, qsrc, 2 * HPI * a.qi_head, qi_lane, h_lane, a.num_heads);
   L.xn = make_uint4(0, 0, 0, 0);
-  L.tail = 0;
+  L.tail = L.tail_hi = 0;
   if constexpr (MODE != MlaOut::Bf16InPlace) {
     if (chunk == 0) {
       const uint16_t* row = a.latent + (int64_t)t * a.kv_row;
       if ((uint32_t)lane < a.nope_chunks) L.xn = load16_stream(row + 8 * lane);
-      L.tail = load_tail<R>(row + 8 * a.nope_chunks, lane);
+      load_tail<R>(row + 8 * a.nope_chunks, lane, L.tail, L.tail_hi);
     }
   }
   if constexpr (PLANNED) L.pe = *reinterpret_cast<const uint4*>(a.plan + 4 * (uint64_t)t);
@@ -387,7 +392,7 @@ __device__ __forceinline__ void finish_item(const MlaArgs& a, uint32_t t, uint32
     if (latent_wave) {
       const uint16_t* row = static_cast<const uint16_t*>(cv.layer_base) + row_elems;
       if ((uint32_t)lane < a.nope_chunks) L.xn = load16_stream(row + 8 * lane);
-      L.tail = load_tail<R>(row + 8 * a.nope_chunks, lane);
+      load_tail<R>(row + 8 * a.nope_chunks, lane, L.tail, L.tail_hi);
     }
   }
   if (hl.first) {
@@ -411,7 +416,23 @@ __device__ __forceinline__ void finish_item(const MlaArgs& a, uint32_t t, uint32
   // ---- latent row: RMSNorm (non-rope part), RoPE (tail) ---------------------
   if constexpr (INPLACE) r = latent_rms(L.xn, gm, gamma_type, xg, a.inv_dn, a.epsilon);
   float tv[2];
-  rotate_tail<R>(L.tail, tcs, tl, tv);  // meaningful on active tail lanes only
+  // The tail words came with the bulk loads.  Left free, the compiler moves
+  // their widening next to the 2-byte loads, and the wait for them then holds
+  // the chunk-0 wave's address chain back until all of its q and latent loads
+  // are in.  With 32 heads per wave (NI 4: a 128-head token spans 4 waves,
+  // and its chunk-0 wave is the slowest) an empty asm pins the widening here,
+  // which measured faster: 128-head decode batch 4.10 -> 3.80 us, 17108-token
+  // prefill 95.5 -> 94.4 us.  With at most 16 heads (NI 2: every wave owns a
+  // latent row) the compiler's early wait measured faster (16-head mixed
+  // batch 10.96 us against 11.3 us pinned), so it is kept there.
+  uint32_t tail_word = L.tail;
+  if constexpr (R == 128) {
+    if constexpr (NI == 4) asm volatile("" : "+v"(tail_word), "+v"(L.tail_hi));
+    tail_word |= L.tail_hi << 16;
+  } else if constexpr (NI == 4) {
+    asm volatile("" : "+v"(tail_word));
+  }
+  rotate_tail<R>(tail_word, tcs, tl, tv);  // meaningful on active tail lanes only
   const bool nope_lane = (uint32_t)lane < a.nope_chunks;
   const uint32_t tail0 = 8 * a.nope_chunks + lane;  // element of the lane's (first) tail value
 
