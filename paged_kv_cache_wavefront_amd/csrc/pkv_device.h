@@ -206,6 +206,15 @@ __device__ __forceinline__ uint4 load16_stream(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// An empty asm that takes a loaded value in place (one 16-byte register
+// tuple, so the value stays in the registers the load wrote): code that uses
+// the value cannot be moved above it, and the wait for the load lands here.
+__device__ __forceinline__ void pin_vgprs(uint4& v) {
+  u32x4_t t = {v.x, v.y, v.z, v.w};
+  asm volatile("" : "+v"(t));
+  v = make_uint4(t.x, t.y, t.z, t.w);
+}
+
 __device__ __forceinline__ uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
 // 8-byte non-temporal load.

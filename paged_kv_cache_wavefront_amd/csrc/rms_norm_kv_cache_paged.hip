@@ -61,8 +61,8 @@ __global__ __launch_bounds__(256) void kv_norm_kernel(const KvNormArgs a) {
   const uint32_t C = a.gamma_len;
 
   // gamma of this lane's columns (bf16, fp16 or fp32, widened exactly): a
-  // whole chunk is loaded here, before the chain, and unpacked only before
-  // its first use, so that its wait does not hold up the chain's loads
+  // whole chunk is loaded here, before the chain, and widened only before its
+  // first use, so that its wait holds up neither the chain's nor the rows' loads
   const int gamma_type = GT ? a.gamma_type : (int)kBf16;
   const bool gamma_chunk = col0 + 8 <= C;
   uint4 g_lo = make_uint4(0, 0, 0, 0), g_hi = make_uint4(0, 0, 0, 0);
@@ -133,54 +133,61 @@ __global__ __launch_bounds__(256) void kv_norm_kernel(const KvNormArgs a) {
     }
     r_presum = rsqrt_hw(wave_sum(ss_all) * a.inv_token_cols + a.epsilon);
   }
-  // gamma + weight_offset: the chunk loaded above, or a partial chunk (the
-  // columns past gamma_len take 0) element by element
-  float g[8];
-  if (gamma_chunk) {
-    if (gamma_type == kF32) {
-      const uint32_t w[8] = {g_lo.x, g_lo.y, g_lo.z, g_lo.w, g_hi.x, g_hi.y, g_hi.z, g_hi.w};
-#pragma unroll
-      for (int k = 0; k < 8; ++k) g[k] = __uint_as_float(w[k]);
-    } else {
-      unpack8_16(g_lo, gamma_type == kF16, g);
-    }
-  } else {
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-      g[k] = (col0 + k < C) ? load_elem(a.gamma, col0 + k, gamma_type) : 0.0f;
-  }
-#pragma unroll
-  for (int k = 0; k < 8; ++k) g[k] += a.weight_offset;
-
   for (uint32_t base = 0; base < nit; base += kMaxIter) {
-    // phase 1: load the chunk's heads this lane serves, sums of squares
-    float x[kMaxIter][8], rh[kMaxIter];
-    float ss_token = 0.0f;
+    // phase 1: load the chunk's heads this lane serves, then the sums of
+    // squares.  Every load is issued before any value is used: the chunk's
+    // head groups end at a uniform break, which no load may be moved across,
+    // so a use between two loads would make each wait for the one before.
+    // A lane outside the rows skips its load and takes zeros only in the
+    // second loop (a zero written before the load would make the load wait
+    // for everything still in flight).
+    uint4 raw16[kMaxIter];  // bf16 rows
+    uint2 raw8[kMaxIter];   // fp8 codes
+    float ks[kMaxIter];     // their scales
+    bool valid[kMaxIter];
 #pragma unroll
     for (int it = 0; it < kMaxIter; ++it) {
       if (base + it >= nit) break;
       const uint32_t h = (base + it) * HPI + hl;
-      const bool valid = h < cv.num_heads && touches;
+      valid[it] = h < cv.num_heads && touches;
       const char* p = krow + EB * (int64_t)h * cv.head_stride;
-      if constexpr (KM == KMode::Bf16) {
-        uint4 raw = make_uint4(0, 0, 0, 0);
-        if (valid) raw = load16_stream(p);
-        unpack8(raw, x[it]);
-      } else {
-        uint2 raw = make_uint2(0, 0);
-        float ks = 0.0f;
-        if (valid) {
-          raw = load8_stream(p);
-          ks = KM == KMode::Fp8PerTensor ? tensor_scale : a.k_scales[slot_head0 + h];
+      if (valid[it]) {
+        if constexpr (KM == KMode::Bf16) {
+          raw16[it] = load16_stream(p);
+        } else {
+          raw8[it] = load8_stream(p);
+          ks[it] = KM == KMode::Fp8PerTensor ? tensor_scale : a.k_scales[slot_head0 + h];
         }
-        unpack8_fp8(raw.x, raw.y, x[it]);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) x[it][k] *= ks;
       }
+    }
+    // the values of head group it, widened from the packed loads (twice:
+    // for the sums and again for the stores, which keeps the chunk packed in
+    // registers between the two phases)
+    auto widen = [&](int it, float (&y)[8]) {
+      if constexpr (KM == KMode::Bf16) {
+        unpack8(raw16[it], y);
+      } else {
+        unpack8_fp8(raw8[it].x, raw8[it].y, y);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) y[k] *= ks[it];
+      }
+    };
+    float rh[kMaxIter];
+    float ss_token = 0.0f;
+#pragma unroll
+    for (int it = 0; it < kMaxIter; ++it) {
+      if (base + it >= nit) break;
+      if (!valid[it]) {
+        raw16[it] = make_uint4(0, 0, 0, 0);
+        raw8[it] = make_uint2(0, 0);
+        ks[it] = 0.0f;
+      }
+      float y[8];
+      widen(it, y);
       float ss = 0.0f;
 #pragma unroll
       for (int k = 0; k < 8; ++k)
-        if (col0 + k < C) ss = fmaf(x[it][k], x[it][k], ss);
+        if (col0 + k < C) ss = fmaf(y[k], y[k], ss);
       if constexpr (PER_HEAD) {
         ss = group_sum<LP>(ss);
         rh[it] = rsqrt_hw(ss * a.inv_cols + a.epsilon);
@@ -194,15 +201,39 @@ __global__ __launch_bounds__(256) void kv_norm_kernel(const KvNormArgs a) {
         r_token = rsqrt_hw(wave_sum(ss_token) * a.inv_token_cols + a.epsilon);
     }
 
+    // gamma + weight_offset, widened only now that phase 1 has issued its
+    // loads: the chunk loaded above (the empty asm keeps the widening, and
+    // with it the wait for gamma, from being hoisted in front of them), or a
+    // partial chunk (the columns past gamma_len take 0) element by element
+    float g[8];
+    if (gamma_chunk) {
+      pin_vgprs(g_lo);
+      if (gamma_type == kF32) {
+        pin_vgprs(g_hi);
+        const uint32_t w[8] = {g_lo.x, g_lo.y, g_lo.z, g_lo.w, g_hi.x, g_hi.y, g_hi.z, g_hi.w};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) g[k] = __uint_as_float(w[k]);
+      } else {
+        unpack8_16(g_lo, gamma_type == kF16, g);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        g[k] = (col0 + k < C) ? load_elem(a.gamma, col0 + k, gamma_type) : 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) g[k] += a.weight_offset;
+
     // phase 2: normalise, re-encode, store
 #pragma unroll
     for (int it = 0; it < kMaxIter; ++it) {
       if (base + it >= nit) break;
       const uint32_t h = (base + it) * HPI + hl;
-      const bool valid = h < cv.num_heads && touches;
+      const bool lane_valid = valid[it];
       char* p = krow + EB * (int64_t)h * cv.head_stride;
       const float r = PER_HEAD ? rh[it] : r_token;
-      float* v = x[it];
+      float v[8];
+      widen(it, v);
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         if (col0 + k >= C) continue;
@@ -213,9 +244,9 @@ __global__ __launch_bounds__(256) void kv_norm_kernel(const KvNormArgs a) {
         }
       }
       if constexpr (KM == KMode::Bf16) {
-        if (valid) {
+        if (lane_valid) {
           if (col0 + 8 <= C) {
-            store16_stream(p, pack8_bf16(x[it]));
+            store16_stream(p, pack8_bf16(v));
           } else {
             uint16_t* e = reinterpret_cast<uint16_t*>(p);
 #pragma unroll
@@ -232,12 +263,12 @@ __global__ __launch_bounds__(256) void kv_norm_kernel(const KvNormArgs a) {
           am = group_max_abs<LP>(am);
           const float st = am / 448.0f;
           inv = st > 0.0f ? rcp_hw(st) : 0.0f;
-          if (valid && m == 0) a.k_scales[slot_head0 + h] = st;
+          if (lane_valid && m == 0) a.k_scales[slot_head0 + h] = st;
         }
 #pragma unroll
         for (int k = 0; k < 8; ++k) v[k] *= inv;
-        const uint2 codes = pack8_fp8(x[it]);
-        if (valid) {
+        const uint2 codes = pack8_fp8(v);
+        if (lane_valid) {
           if (kWholeHead || col0 + 8 <= C) {
             store8_stream(p, codes);
           } else {
