@@ -159,22 +159,35 @@ __device__ __forceinline__ void rotate_scaled(float (&own)[8], const float (&par
 // Q of one wave: NI instructions of HPI heads.  Base and step are wave-uniform
 // byte addresses; lane_off is the lane's byte offset.  GUARD masks heads past
 // num_heads.  QF16: q and its output are fp16, else bf16.
-template <int D, bool INTER, int NI, bool GUARD, bool QF16>
-__device__ __forceinline__ void q_rope(const char* src, char* dst, int64_t in_step,
-                                       int64_t out_step, uint32_t in_off, uint32_t out_off,
-                                       uint32_t h_lane, uint32_t num_heads, bool active,
-                                       const float* cs) {
+// 16 bytes of zeros: what a lane that holds no Q value loads instead.
+__device__ uint4 kZero16 = {0u, 0u, 0u, 0u};
+
+// Q loads of one item: NI instructions of HPI heads each, issued before the
+// address chain resolves (their addresses need only the token).  A lane of
+// a head past num_heads, or a padding lane, loads kZero16 instead: every
+// path issues the same loads, so the chain's waits can leave them in flight.
+template <int D, bool INTER, int NI>
+__device__ __forceinline__ void q_load(uint4 (&v)[NI], const char* src, int64_t in_step,
+                                       uint32_t in_off, uint32_t h_lane, uint32_t num_heads,
+                                       bool active) {
   using Geo = Geometry<D, INTER>;
-  constexpr int HPI = Geo::kHeadsPerInstr, LP = Geo::kLanesPerHead;
-  uint4 v[NI];
+  constexpr int HPI = Geo::kHeadsPerInstr;
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    if (GUARD || Geo::kPadded) {
-      v[i] = make_uint4(0, 0, 0, 0);
-      if ((GUARD && h_lane + HPI * i >= num_heads) || (Geo::kPadded && !active)) continue;
-    }
-    v[i] = load16_stream(src + i * in_step + in_off);
+    const bool ok = h_lane + HPI * i < num_heads && (!Geo::kPadded || active);
+    v[i] = load16_stream(ok ? src + i * in_step + in_off
+                            : reinterpret_cast<const char*>(&kZero16));
   }
+}
+
+// Rotate the loaded Q values and store them (GUARD: heads past num_heads
+// are not stored).
+template <int D, bool INTER, int NI, bool GUARD, bool QF16>
+__device__ __forceinline__ void q_rope(const uint4 (&v)[NI], char* dst, int64_t out_step,
+                                       uint32_t out_off, uint32_t h_lane, uint32_t num_heads,
+                                       bool active, const float* cs) {
+  using Geo = Geometry<D, INTER>;
+  constexpr int HPI = Geo::kHeadsPerInstr, LP = Geo::kLanesPerHead;
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     float own[8], par[8] = {};
@@ -203,7 +216,12 @@ __global__ __launch_bounds__(256) void qk_rope_kernel(const QkArgs a) {
   const int col = 8 * role.chunk;          // first column this lane owns
   const int pcol = 8 * role.partner_chunk;  // first column of the partner's values
 
-  // ---- Q loads first (addresses need only t) --------------------------------
+  // ---- loads that need only t: the request lookup's first step, then Q ------
+  // (in that order: the load counter is in order, so the lookup can be
+  // resolved while the Q loads are still in flight)
+  const CacheView& cv = a.cache;
+  SlotLoads sl;
+  slot_issue(a.offsets, a.batch, cv.cache_lengths, lane, sl);
   const uint32_t h0 = chunk * (HPI * NI);
   const uint32_t h_lane = h0 + hl;
   const bool all_heads = h0 + HPI * NI <= a.num_q_heads;
@@ -213,10 +231,11 @@ __global__ __launch_bounds__(256) void qk_rope_kernel(const QkArgs a) {
   const uint32_t qi_off = 2 * (hl * (uint32_t)a.qi_head + (uint32_t)col);
   const uint32_t qo_off = 2 * (hl * (uint32_t)a.qo_head + (uint32_t)col);
   const int64_t qi_step = 2 * HPI * a.qi_head, qo_step = 2 * HPI * a.qo_head;
+  uint4 qv[NI];
+  q_load<D, INTER, NI>(qv, qsrc, qi_step, qi_off, h_lane, a.num_q_heads, role.active);
 
   // ---- address chain: step 1 = {position id(s), offsets, prior lengths};
   //      step 2 = {freqs row(s), page-table entry} ----------------------------------
-  const CacheView& cv = a.cache;
   uint32_t pid[3] = {0, 0, 0};
   if (a.position_ids != nullptr) {
     pid[0] = uniform(a.position_ids[t]);
@@ -225,7 +244,7 @@ __global__ __launch_bounds__(256) void qk_rope_kernel(const QkArgs a) {
       pid[2] = uniform(a.position_ids[2 * (uint64_t)a.total_tokens + t]);
     }
   }
-  const TokenSlot ts = find_slot(a.offsets, a.batch, cv.cache_lengths, t, lane);
+  const TokenSlot ts = slot_resolve(sl, a.offsets, a.batch, cv.cache_lengths, t, lane);
   const uint32_t pos = a.position_ids != nullptr ? pid[0] : ts.slot;
   bool pos_ok = ts.ok && pos < a.max_seq_len;
   if (a.mrope) pos_ok = pos_ok && pid[1] < a.max_seq_len && pid[2] < a.max_seq_len;
@@ -267,11 +286,11 @@ __global__ __launch_bounds__(256) void qk_rope_kernel(const QkArgs a) {
 
   // ---- Q ------------------------------------------------------------------------
   if (all_heads)
-    q_rope<D, INTER, NI, false, QF16>(qsrc, qdst, qi_step, qo_step, qi_off, qo_off, h_lane,
-                                a.num_q_heads, role.active, cs);
+    q_rope<D, INTER, NI, false, QF16>(qv, qdst, qo_step, qo_off, h_lane, a.num_q_heads,
+                                      role.active, cs);
   else if (h0 < a.num_q_heads)
-    q_rope<D, INTER, NI, true, QF16>(qsrc, qdst, qi_step, qo_step, qi_off, qo_off, h_lane,
-                               a.num_q_heads, role.active, cs);
+    q_rope<D, INTER, NI, true, QF16>(qv, qdst, qo_step, qo_off, h_lane, a.num_q_heads,
+                                     role.active, cs);
   if (chunk != 0) return;
 
   // ---- K (in place), optional per-head RMSNorm first ------------------------
