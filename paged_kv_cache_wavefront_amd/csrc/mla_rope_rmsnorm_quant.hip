@@ -453,16 +453,20 @@ __device__ __forceinline__ void finish_item(const MlaArgs& a, uint32_t t, uint32
   // their widening next to the 2-byte loads, and the wait for them then holds
   // the chunk-0 wave's address chain back until all of its q and latent loads
   // are in.  With 32 heads per wave (NI 4: a 128-head token spans 4 waves,
-  // and its chunk-0 wave is the slowest) an empty asm pins the widening here,
-  // which measured faster: 128-head decode batch 4.10 -> 3.80 us, 17108-token
-  // prefill 95.5 -> 94.4 us.  With at most 16 heads (NI 2: every wave owns a
-  // latent row) the compiler's early wait measured faster (16-head mixed
-  // batch 10.96 us against 11.3 us pinned), so it is kept there.
+  // and its chunk-0 wave is the slowest), and with a plan entry (a scalar
+  // load, which then arrives without waiting for the vector loads), an empty
+  // asm pins the widening here, which measured faster: 128-head decode batch
+  // 4.10 -> 3.80 us, 17108-token prefill 95.5 -> 94.4 us, planned 16-head
+  // mixed batch 10.64 -> 10.23 us.  With at most 16 heads and the address
+  // chain in the kernel (every wave owns a latent row) the compiler's early
+  // wait measured faster (mixed batch 10.96 us against 11.3 us pinned), so it
+  // is kept there.
+  constexpr bool kPinTail = NI == 4 || PLANNED;
   uint32_t tail_word = L.tail;
   if constexpr (R == 128) {
-    if constexpr (NI == 4) asm volatile("" : "+v"(tail_word), "+v"(L.tail_hi));
+    if constexpr (kPinTail) asm volatile("" : "+v"(tail_word), "+v"(L.tail_hi));
     tail_word |= L.tail_hi << 16;
-  } else if constexpr (NI == 4) {
+  } else if constexpr (kPinTail) {
     asm volatile("" : "+v"(tail_word));
   }
   rotate_tail<R>(tail_word, tcs, tl, tv);  // meaningful on active tail lanes only
