@@ -437,6 +437,22 @@ def test_styles_and_dims(orc, D, interleaved, pos_ids):
     run_qk(orc, case, False)
 
 
+@pytest.mark.parametrize("D,interleaved", [(128, False), (96, True), (64, False)])
+def test_k_only(orc, D, interleaved):
+    """No Q heads (num_q_heads = 0, null Q pointers): one wave per token
+    rotates (and normalises) K alone; its Q lanes load nothing from Q."""
+    rng = workloads.make_rng(5600 + D)
+    new = rng.integers(1, 60, size=5, endpoint=True)
+    prior = rng.integers(0, 100, size=5, endpoint=True)
+    case = workloads.build_qk(f"qk_konly_d{D}", 5600 + D, new, prior, Hq=0, Hkv=3, D=D,
+                              page_size=16, max_seq_len=512, theta=10000.0,
+                              interleaved=interleaved, with_position_ids=True, norm_cols=D,
+                              rng=rng)
+    assert case.q.shape[1] == 0
+    run_qk(orc, case, True)
+    run_qk(orc, case, False)
+
+
 def oracle_kv_norm(orc, case, gamma, w, total, mbc):
     k = case.k_cache.copy()
     orc.rms_norm_kv_cache_paged(k, case.layer_idx, case.row_offsets, case.cache_lengths,
