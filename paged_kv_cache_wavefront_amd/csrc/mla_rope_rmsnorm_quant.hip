@@ -18,10 +18,12 @@
 //   half-row or row mirror): no LDS round trip, and every load and store
 //   covers full 128-byte lines.
 // * q and latent are read and q_rope_output written with non-temporal
-//   accesses (streamed once); all q loads of an item are issued before the
-//   address chain, which takes two dependent steps ({offsets, cache
-//   lengths}, then {freqs row, page-table entry}) and hides behind the bulk
-//   traffic.
+//   accesses (streamed once).  The address chain takes two dependent steps
+//   ({offsets, cache lengths}, then {freqs row, page-table entry}) and hides
+//   behind the bulk traffic: with 32 heads per wave the chunk-0 wave issues
+//   its latent row and the chain's first step ahead of its q loads and
+//   resolves the chain while q is in flight; with at most 16 heads per wave,
+//   or a plan entry, the q loads are issued first (chain_first below).
 // * The 16 cos/sin values a lane needs sit contiguously in the freqs row and
 //   are the same for every head: one 64-byte load per lane per token (32
 //   bytes for a 16-bit table), kept in registers.
