@@ -153,24 +153,27 @@ __device__ __forceinline__ void rotate_own(float (&own)[8], const float (&par)[8
   for (int j = 0; j < 8; ++j) own[j] = sum_of_products(own[j], cs[2 * j], par[j], cs[2 * j + 1]);
 }
 
+// 16 bytes of zeros: what a lane of a head past num_heads loads instead of q
+// (with no heads at all, q may be a null pointer).
+__device__ uint4 kZero16 = {0u, 0u, 0u, 0u};
+
 // q loads / stores of one item: NI instructions of 64/LP heads each.  The
 // token and chunk parts of the address are wave-uniform (scalar registers);
 // each lane adds a 32-bit offset.  A lane of a head past num_heads (last
-// chunk of a token) loads its columns of the item's first head instead,
-// which exists, and its result is not stored (GUARD on the stores).  So the
-// loads take one straight path, the same NI loads for every item, with no
-// zero written ahead of a load (such a write waits for the loads in flight,
-// and paths with different load counts make later waits conservative).
-// (base and step in bytes, wave-uniform; lane_off and first_off in bytes,
-// per lane.)
+// chunk of a token) loads kZero16 instead, and its result is not stored
+// (GUARD on the stores).  So the loads take one straight path, the same NI
+// loads for every item, with no zero written ahead of a load (such a write
+// waits for the loads in flight, and paths with different load counts make
+// later waits conservative).  (base and step in bytes, wave-uniform;
+// lane_off in bytes, per lane.)
 template <int NI, int HPI>
 __device__ __forceinline__ void load_q(uint4 (&q)[NI], const char* base, int64_t step,
-                                       uint32_t lane_off, uint32_t first_off, uint32_t h_lane,
-                                       uint32_t num_heads) {
+                                       uint32_t lane_off, uint32_t h_lane, uint32_t num_heads) {
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const bool ok = h_lane + HPI * i < num_heads;
-    q[i] = load16_stream(base + (ok ? i * step + lane_off : (int64_t)first_off));
+    q[i] = load16_stream(ok ? base + i * step + lane_off
+                            : reinterpret_cast<const char*>(&kZero16));
   }
 }
 
@@ -281,8 +284,7 @@ __device__ __forceinline__ void issue_item(const MlaArgs& a, uint32_t t, uint32_
     const char* qsrc = reinterpret_cast<const char*>(a.q_in + (int64_t)t * a.qi_tok +
                                                       (int64_t)h0 * a.qi_head);
     const uint32_t qi_lane = 2 * ((uint32_t)(lane / LP) * (uint32_t)a.qi_head + 8 * hl.chunk);
-    const uint32_t qi_first = 2 * 8 * hl.chunk;  // the lane's columns of head h0
-    load_q<NI, HPI>(L.q, qsrc, 2 * HPI * a.qi_head, qi_lane, qi_first, h_lane, a.num_heads);
+    load_q<NI, HPI>(L.q, qsrc, 2 * HPI * a.qi_head, qi_lane, h_lane, a.num_heads);
   };
   const auto issue_latent = [&] {
     L.xn = make_uint4(0, 0, 0, 0);

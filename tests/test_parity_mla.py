@@ -422,6 +422,30 @@ def test_zero_rows_per_token(orc):
                 f"token {t}: zero signs"
 
 
+@pytest.mark.parametrize("mode", ["per_tensor", "per_token", "bf16"])
+def test_no_heads(orc, mode):
+    """num_heads = 0 (q tensors [T, 0, R], null pointers): the wave of each
+    token writes its latent row alone, its q lanes read nothing from q; also
+    through the token plan."""
+    case = workloads.build_mla(f"mla_h0_{mode}", 4401, [7, 0, 12], [0, 5, 30], H=0,
+                               page_size=16, max_seq_len=128, spare_pages=2,
+                               scale_mode="per_token" if mode == "per_token" else "per_tensor",
+                               cache_dtype="bf16" if mode == "bf16" else "fp8",
+                               rng=workloads.make_rng(4401))
+    assert case.q.shape[1] == 0
+    _run_and_compare(orc, case)
+    dev = gh.MlaDevice(case)
+    plan = torch.empty((case.T, 4), dtype=torch.int32, device="cuda")
+    import paged_kv_cache_wavefront_amd as pkv
+    pkv.pkv_token_plan(plan, dev.offsets, dev.desc)
+    pkv.mla_rope_rmsnorm_quant_planned(dev.q_out, dev.q_in, dev.latent, plan, dev.freqs,
+                                       dev.gamma, case.epsilon, dev.desc, case.layer_idx)
+    gpu = dev.results()
+    assert gpu[3] == 0
+    stats = gh.compare_mla(case, gpu, gh.oracle_mla(orc, case))
+    _say(f"[mla-h0 planned] {stats}")
+
+
 def test_launch_shape_invariance():
     """The same tokens under different wave mappings give identical bits: a
     32-head launch (32 heads per wave) against two 16-head launches over its
