@@ -128,7 +128,8 @@ __device__ __forceinline__ void rotate_tail(uint32_t raw, const float2& tcs,
     tv[0] = sum_of_products(own, tcs.x, hi, -tcs.y);
     tv[1] = sum_of_products(hi, tcs.x, own, tcs.y);
   } else {
-    const float par = R == 64 ? __shfl_xor(own, 32) : swizzle<kSwizzleXor16>(own);
+    const float par = R == 64 ? __uint_as_float(swap_halves_u32(__float_as_uint(own), tl.first))
+                              : swizzle<kSwizzleXor16>(own);
     tv[0] = sum_of_products(own, tcs.x, par, tl.first ? -tcs.y : tcs.y);
     tv[1] = 0.0f;
   }

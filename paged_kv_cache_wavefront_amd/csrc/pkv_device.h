@@ -273,6 +273,16 @@ __device__ __forceinline__ float swizzle(float v) {
   return __uint_as_float(swizzle_u32<PATTERN>(__float_as_uint(v)));
 }
 
+// Lane l receives lane (l ^ 32)'s value; low_half = (l < 32).
+// v_permlane32_swap exchanges the upper 32 lanes of one register with the
+// lower 32 of another; given the value twice, one result holds the lower
+// half in both halves and the other the upper half, and each lane takes the
+// one that is not its own: two VALU instructions, no LDS round trip.
+__device__ __forceinline__ uint32_t swap_halves_u32(uint32_t x, bool low_half) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return low_half ? r[1] : r[0];
+}
+
 // Lane k of an aligned group of N lanes (N = 4, 8, 16 or 32) receives lane
 // (N-1-k)'s 32-bit value.
 template <int N>
