@@ -154,6 +154,21 @@ __device__ __forceinline__ void rotate_own(float (&own)[8], const float (&par)[8
   for (int j = 0; j < 8; ++j) own[j] = sum_of_products(own[j], cs[2 * j], par[j], cs[2 * j + 1]);
 }
 
+// x c + p s for the value x of this lane and the value p of the mirrored
+// lane of its LP-lane group (the pair partner), by Kahan's algorithm with
+// the rounding error of x c recovered (the same bound as recovering that of
+// p s): p is read once, in the fused multiply-add, so its DPP mirror folds
+// into that instruction and the partner needs no unpacking of its own.  An
+// infinite x c has no error to recover: its error term is clamped as in
+// sum_of_products.
+template <int LP>
+__device__ __forceinline__ float rotate_with_mirror(float x, float c, float s) {
+  const float xc = x * c;
+  const float xc_err = fminf(fmaf(x, c, -xc), 3.402823466e38f);  // x*c - xc, exact
+  const float p = __uint_as_float(mirror_u32<LP>(__float_as_uint(x)));
+  return fmaf(p, s, xc) + xc_err;
+}
+
 // 16 bytes of zeros: what a lane of a head past num_heads loads instead of q
 // (with no heads at all, q may be a null pointer).
 __device__ uint4 kZero16 = {0u, 0u, 0u, 0u};
@@ -187,11 +202,10 @@ __device__ __forceinline__ void rotate_store_q(const uint4 (&q)[NI], const float
   using QT = QTypes<X>;
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    const uint4 partner = mirror16<LP>(q[i]);
-    float own[8], par[8];
-    unpack8_16(q[i], QT::kInF16, own);
-    unpack8_16(partner, QT::kInF16, par);
-    rotate_own(own, par, cs);
+    float in[8], own[8];
+    unpack8_16(q[i], QT::kInF16, in);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) own[j] = rotate_with_mirror<LP>(in[j], cs[2 * j], cs[2 * j + 1]);
     if (GUARD && h_lane + HPI * i >= num_heads) continue;
     char* p = base + i * step + lane_off;
     if constexpr (QT::kOut == kF16) {
