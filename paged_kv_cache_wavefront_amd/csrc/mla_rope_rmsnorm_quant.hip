@@ -144,23 +144,14 @@ struct QTypes {
   static constexpr int64_t kOutBytes = kOut == kF32 ? 4 : 2;
 };
 
-// Rotate the 8 values this lane owns, given its partner's 8 values: first
-// half  out = own*cos - partner*sin;  second half  out = own*cos + partner*sin.
-// cs holds (cos, sin) per pair with the sines already negated on first-half
-// lanes (negation is exact, so the products and roundings are unchanged).
-__device__ __forceinline__ void rotate_own(float (&own)[8], const float (&par)[8],
-                                           const float (&cs)[16]) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) own[j] = sum_of_products(own[j], cs[2 * j], par[j], cs[2 * j + 1]);
-}
-
-// x c + p s for the value x of this lane and the value p of the mirrored
-// lane of its LP-lane group (the pair partner), by Kahan's algorithm with
-// the rounding error of x c recovered (the same bound as recovering that of
-// p s): p is read once, in the fused multiply-add, so its DPP mirror folds
-// into that instruction and the partner needs no unpacking of its own.  An
-// infinite x c has no error to recover: its error term is clamped as in
-// sum_of_products.
+// One rotated value: x c + p s for the value x of this lane and the value p
+// of the mirrored lane of its LP-lane group (the pair partner); first-half
+// lanes pass the sine negated (out = x cos - p sin), second-half lanes as is
+// (out = x cos + p sin).  Kahan's algorithm with the rounding error of x c
+// recovered (the same bound as recovering that of p s): p is needed once, in
+// the fused multiply-add, so it arrives by one DPP mirror of the unpacked
+// value and the partner needs no unpacking of its own.  An infinite x c has
+// no error to recover: its error term is clamped as in sum_of_products.
 template <int LP>
 __device__ __forceinline__ float rotate_with_mirror(float x, float c, float s) {
   const float xc = x * c;
