@@ -230,6 +230,45 @@ def test_codec_every_bf16_value(orc):
         _say(f"[codec] scale={scale}: {stats}")
 
 
+@pytest.mark.parametrize("H", [4, 40])
+def test_non_finite_q_values(orc, H):
+    """+-inf and NaN in q: a rotated value whose pair holds an infinity is
+    +-inf, or NaN where the two products are opposite infinities or an
+    infinity meets a zero cos/sin (position 0: sin 0); a NaN spreads to its
+    pair.  Every q output as the oracle's: NaN where it is NaN, every other
+    value within the usual bar (infinities equal).  16 and 32 heads per wave."""
+    rng = workloads.make_rng(4500 + H)
+    case = workloads.build_mla(f"mla_q_nonfinite_h{H}", 4500 + H, [9, 7], [0, 40], H=H,
+                               page_size=16, max_seq_len=128, spare_pages=2,
+                               scale_mode="per_tensor", tensor_scale=0.05, rng=rng)
+    pinf, ninf, nan = np.uint16(0x7F80), np.uint16(0xFF80), np.uint16(0x7FC0)
+    q = case.q                                  # [T, H, R] bf16 patterns
+    q[0, 0, 3] = pinf                           # token 0 sits at position 0
+    q[1, 1, 5] = ninf
+    q[2, 2, 40] = nan
+    q[3, 3, 0], q[3, 3, 32] = pinf, pinf        # both members of one pair
+    q[4, 0, 10], q[4, 0, 42] = pinf, ninf
+    q[5, H - 1, 63] = nan
+    q[10, 1, 1] = pinf                          # second request, position 40
+    dev = gh.MlaDevice(case)
+    dev.run()
+    gpu = dev.results()
+    assert gpu[3] == 0
+    want = gh.oracle_mla(orc, case)
+    g, w = gpu[0], want[0]
+    gnan = (g & 0x7FFF) > 0x7F80
+    wnan = (w & 0x7FFF) > 0x7F80
+    assert np.array_equal(gnan, wnan), "NaN positions differ"
+    assert wnan.sum() >= 2
+    d = gh.bf16_ulp_diff(g[~wnan], w[~wnan])
+    assert int(d.max(initial=0)) <= gh.BF16_MAX_ULP
+    inf_w = (w[~wnan] & 0x7FFF) == 0x7F80
+    assert inf_w.sum() >= 4 and np.array_equal(g[~wnan][inf_w], w[~wnan][inf_w])
+    # the cache rows are untouched by q: as the oracle's
+    stats = gh.compare_mla(case, (np.where(wnan, w, g), gpu[1], gpu[2], 0), want)
+    _say(f"[q-nonfinite] H={H}: {int(wnan.sum())} NaN, {int(inf_w.sum())} inf; {stats}")
+
+
 @pytest.mark.parametrize("scale_mode", ["per_tensor", "per_token"])
 def test_non_finite_latent_values(orc, scale_mode):
     """A NaN or an infinity in the latent row's non-rope part reaches the
